@@ -1,0 +1,280 @@
+"""Plain CPU oracle for the Sparse-BitLinear hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this module.  It shares no code with the HIP library.
+
+Every function writes out the plain definition of one step, in numpy (float64
+unless noted), so it can be checked by eye against the pages.  The pages are
+five web summaries of the paper "Sparse-BitNet: 1.58-bit LLMs are Naturally
+Friendly to Semi-Structured Sparsity" (arXiv 2603.05168); they are cited as
+
+  [ja]  gist.science, Japanese summary, section "技術概要" (technical overview)
+  [de]  gist.science, German summary, section "Technische Zusammenfassung"
+  [ko]  gist.science, Korean summary, section "기술 요약"
+  [fr]  gist.science, French summary, section "Résumé technique"
+  [abs] fugumt.com paper page, English abstract
+
+followed by the numbered heading inside that section.
+
+The pages give no formulas.  Where they are silent this oracle takes the
+readings below (each is repeated at the function that uses it):
+
+  * groups of M run along K, the input dimension, inside one output row;
+  * the mask keeps exactly N entries per group, the N largest |w| of the
+    master weights; equal magnitudes go to the lower index;
+  * one per-tensor scale s_w = mean|W| over ALL master weights (the pages put
+    quantization before masking), rounded once to fp32, floored at 1e-5;
+  * ternary value = RoundClip(w / s_w, -1, 1), round half to even;
+  * activations: per-token absmax to int8 in [-127, 127], decided in fp32 as
+    rint((127*x) / a) with a = max(absmax, 1e-5), s_x = a/127 in fp32;
+  * Y = s_w * s_x[t] * sum_k Xq[t,k] * Wt[r,k];
+  * dual STE: identity Jacobians through both quantizers and a dense
+    gradient through the mask, so grad_X = dY @ (s_w*Wt) and
+    grad_W = dY^T @ (s_x*Xq) covering every (r, k).
+
+Tensor conventions: bf16 inputs are ``uint16`` bit patterns, row-major.
+W is [R, K] (R output features, K input features), X is [T, K], Y is [T, R].
+
+Packed weight format (the "explicit N:M metadata" the pages ask for):
+
+  meta  plane: per row a K-bit bitstream, bit (g*M + p) set iff position p of
+               group g survives; bit b lives in byte b >> 3 at bit b & 7.
+               Row stride K/8 bytes.  Not stored when N == M.
+  codes plane: per row the survivors' 2-bit codes in increasing k; the j-th
+               survivor occupies bits 2j, 2j+1 (same bit order).  00 = 0,
+               01 = +1, 11 = -1.  Row stride K*N/(4*M) bytes.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+S_FLOOR = np.float32(1e-5)       # floor of the weight scale and of the token absmax
+QMAX = 127                       # symmetric int8 range [-127, 127]
+
+__all__ = [
+    "bf16_to_f64", "bf16_to_f32", "nm_mask", "absmean_exact", "round_to_f32",
+    "weight_scale", "ternary_codes", "quant_then_mask", "packed_bytes",
+    "pack_sbn1", "act_quant", "accumulate", "output", "backward",
+    "forward", "S_FLOOR", "QMAX",
+]
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 values (exact widening)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 values (exact widening)."""
+    return bf16_to_f32(bits).astype(np.float64)
+
+
+def _check_finite(bits: np.ndarray) -> None:
+    if np.any((np.asarray(bits, dtype=np.uint16) & 0x7F80) == 0x7F80):
+        raise ValueError("non-finite bf16 input is outside the operator's contract")
+
+
+# --------------------------------------------------------------------------- mask
+def nm_mask(W_bits: np.ndarray, n: int, m: int) -> np.ndarray:
+    """N:M magnitude mask of the master weights.  Returns bool [R, K].
+
+    [de] §2 / [ko] §2.1 / [fr] §2: in every group of M consecutive weights
+    the N largest magnitudes of the high-precision master weights are kept;
+    [ja] §2.1: the magnitudes are those of the continuous weights before
+    quantization.  Groups run along K inside one row.  Equal magnitudes are
+    ordered by position, lower index first, which makes the selection unique.
+
+    Definition: sort each group by (|w| descending, index ascending) with a
+    stable sort and keep the first N.
+    """
+    _check_finite(W_bits)
+    R, K = W_bits.shape
+    assert K % m == 0 and 1 <= n <= m
+    mag = np.abs(bf16_to_f64(W_bits)).reshape(R, K // m, m)
+    order = np.argsort(-mag, axis=-1, kind="stable")      # stable: ties keep index order
+    keep = np.zeros(mag.shape, dtype=bool)
+    np.put_along_axis(keep, order[..., :n], True, axis=-1)
+    return keep.reshape(R, K)
+
+
+# --------------------------------------------------------------------------- scale
+def absmean_exact(W_bits: np.ndarray) -> Fraction:
+    """Exact mean |w| over every entry of W, as a rational number.
+
+    Scale domain: [ja] §2.1, [de] §2, [ko] §2.1 and [fr] §2 all quantize the
+    master weights first and apply the mask afterwards, so the scale is taken
+    over the whole dense tensor, before masking.  Every bf16 value is an exact
+    binary fraction, so the sum is exact: count each magnitude pattern and add
+    count * value with rational arithmetic.
+    """
+    _check_finite(W_bits)
+    mag = (np.asarray(W_bits, dtype=np.uint16) & 0x7FFF).reshape(-1)
+    counts = np.bincount(mag, minlength=0x8000)
+    nz = np.nonzero(counts)[0]
+    vals = bf16_to_f64(nz.astype(np.uint16))
+    total = sum((Fraction(int(c)) * Fraction(float(v)) for c, v in zip(counts[nz], vals)),
+                Fraction(0))
+    return total / mag.size
+
+
+def round_to_f32(q: Fraction) -> np.float32:
+    """Nearest float32 to the rational q, ties to even (IEEE round-to-nearest).
+
+    Handles zero, subnormals and overflow to infinity.
+    """
+    if q == 0:
+        return np.float32(0.0)
+    neg = q < 0
+    a = -q if neg else q
+    num, den = a.numerator, a.denominator
+    e = num.bit_length() - den.bit_length()          # a in [2^(e-1), 2^(e+1))
+    if (num << max(0, -e)) < (den << max(0, e)):      # a < 2^e
+        e -= 1                                         # now 2^e <= a < 2^(e+1)
+    qe = max(e, -126) - 23                             # exponent of one ulp
+    sn, sd = (num, den << qe) if qe >= 0 else (num << (-qe), den)
+    k, r = divmod(sn, sd)
+    if 2 * r > sd or (2 * r == sd and (k & 1)):
+        k += 1
+    val = Fraction(k) * (Fraction(2) ** qe)
+    fmax = Fraction((1 << 24) - 1) * (Fraction(2) ** (127 - 23))
+    out = np.float32(np.inf) if val > fmax else np.float32(float(val))
+    return -out if neg else out
+
+
+def weight_scale(W_bits: np.ndarray) -> np.float32:
+    """s_w = max(fp32(mean|W|), 1e-5): one per-tensor absmean scale.
+
+    The pages fix only the ternary set {-1, 0, +1} ([ja] §1, [de] §1,
+    [fr] §1); the scale rule is the per-tensor absmean of 1.58-bit BitNet,
+    rounded once to fp32 and floored at 1e-5 so that an all-zero tensor
+    still has a positive scale.
+    """
+    s = round_to_f32(absmean_exact(W_bits))
+    return np.float32(max(s, S_FLOOR))
+
+
+# --------------------------------------------------------------------------- ternary
+def ternary_codes(W_bits: np.ndarray, s_w: np.float32) -> np.ndarray:
+    """RoundClip(w / s_w, -1, 1) with round-half-to-even, over all of W.  int8 [R, K].
+
+    [ja] §1, [de] §1, [ko] §1, [fr] §1: 1.58-bit weights take values in
+    {-1, 0, +1}.  The quotient is formed in float64; a bf16 w and an fp32
+    s_w are far enough apart from the rounding boundary |w/s| = 1/2 that
+    float64 decides it exactly (an exact half rounds to 0).
+    """
+    w = bf16_to_f64(W_bits)
+    t = np.clip(np.rint(w / np.float64(s_w)), -1.0, 1.0)
+    return t.astype(np.int8)
+
+
+def quant_then_mask(W_bits: np.ndarray, n: int, m: int):
+    """Effective ternary weight W_t = mask (.) Q(W), plus the mask and s_w.
+
+    [ja] §2.1 / [de] §2 / [ko] §2.1 / [fr] §2: quantize first, then apply
+    the mask, so the discrete weights used at inference carry the N:M
+    structure.  Returns (codes int8 [R,K] with pruned entries 0, mask bool
+    [R,K], s_w float32).
+    """
+    s_w = weight_scale(W_bits)
+    q = ternary_codes(W_bits, s_w)
+    mask = nm_mask(W_bits, n, m)
+    return np.where(mask, q, 0).astype(np.int8), mask, s_w
+
+
+# --------------------------------------------------------------------------- packing
+def packed_bytes(R: int, K: int, n: int, m: int):
+    """(codes_bytes, meta_bytes) of the packed format for an R x K weight."""
+    codes = R * (K // m) * n * 2 // 8
+    meta = 0 if n == m else R * K // 8
+    return codes, meta
+
+
+def pack_sbn1(codes: np.ndarray, mask: np.ndarray, n: int, m: int):
+    """Pack (mask, ternary codes) into the meta and codes planes.
+
+    [ja] §2.1 / [fr] §2: the quantize-then-mask order yields explicit N:M
+    metadata for inference.  The pages do not print a layout; the one used
+    here is the per-row bitmap plus 2-bit survivor codes described in this
+    module's docstring.
+    """
+    R, K = codes.shape
+    c2 = np.where(codes == 1, 1, np.where(codes == -1, 3, 0)).astype(np.uint8)
+    surv = c2[mask].reshape(R, (K // m) * n)            # row by row, increasing k
+    bits = np.stack([surv & 1, (surv >> 1) & 1], axis=-1).reshape(R, -1)
+    codes_plane = np.packbits(bits, axis=1, bitorder="little")
+    if n == m:
+        meta_plane = np.zeros((R, 0), dtype=np.uint8)
+    else:
+        meta_plane = np.packbits(mask.astype(np.uint8), axis=1, bitorder="little")
+    return codes_plane, meta_plane
+
+
+# --------------------------------------------------------------------------- activations
+def act_quant(X_bits: np.ndarray):
+    """Per-token absmax int8 quantization.  Returns (Xq int8 [T,K], s_x float32 [T]).
+
+    The pages do not describe the activation path.  Reading used: the
+    1.58-bit BitNet convention of per-token absmax scaling into [-127, 127]:
+    a = max(max_k |x|, 1e-5), q = rint((127*x) / a) (round half to even),
+    s_x = a / 127.  The rounding decision is taken in float32, the precision
+    the device kernel works in: 127*x is exact for bf16 x, and the quotient is
+    one IEEE float32 division.
+    """
+    _check_finite(X_bits)
+    x = bf16_to_f32(X_bits)
+    amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    a = np.maximum(amax, S_FLOOR).astype(np.float32)
+    num = np.float32(QMAX) * x                          # float32, exact
+    q = np.rint(num / a[:, None])                       # float32 IEEE division
+    q = np.clip(q, -QMAX, QMAX).astype(np.int8)
+    s_x = (a / np.float32(QMAX)).astype(np.float32)     # float32 IEEE division
+    return q, s_x
+
+
+# --------------------------------------------------------------------------- matmul
+def accumulate(Xq: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """acc[t, r] = sum_k Xq[t, k] * Wt[r, k] as exact integers.  int64 [T, R].
+
+    Sparse ternary matmul of the Sparse-BitLinear forward ([ja] §2.1,
+    [de] §2).  The float64 matmul is exact here: every product and partial
+    sum is an integer of magnitude at most 127*K < 2^53.
+    """
+    assert Xq.shape[1] == codes.shape[1] and Xq.shape[1] * QMAX < 2 ** 53
+    acc = Xq.astype(np.float64) @ codes.astype(np.float64).T
+    return acc.astype(np.int64)
+
+
+def output(acc: np.ndarray, s_w: np.float32, s_x: np.ndarray) -> np.ndarray:
+    """Y[t, r] = s_w * s_x[t] * acc[t, r], in float64."""
+    return acc.astype(np.float64) * (np.float64(s_w) * s_x.astype(np.float64))[:, None]
+
+
+def backward(dY_bits: np.ndarray, Xq: np.ndarray, s_x: np.ndarray,
+             codes: np.ndarray, s_w: np.float32):
+    """Dual-STE backward.  Returns (grad_X [T,K], grad_W [R,K]) in float64.
+
+    [ja] §2.1, [de] §2, [ko] §2.2, [fr] §2: straight-through estimators
+    for the quantizers, and the gradient passes the mask densely so pruned
+    master weights are still updated.  With identity Jacobians:
+      grad_X = dY @ (s_w * Wt)        (through the sparse ternary weight)
+      grad_W = dY^T @ (s_x * Xq)      (every (r, k), masked or not)
+    No term for the derivative of s_w or s_x is taken.
+    """
+    dY = bf16_to_f64(dY_bits)
+    W_eff = np.float64(s_w) * codes.astype(np.float64)
+    X_hat = s_x.astype(np.float64)[:, None] * Xq.astype(np.float64)
+    return dY @ W_eff, dY.T @ X_hat
+
+
+def forward(W_bits: np.ndarray, X_bits: np.ndarray, n: int, m: int) -> dict:
+    """All forward intermediates for one Sparse-BitLinear call."""
+    codes, mask, s_w = quant_then_mask(W_bits, n, m)
+    codes_plane, meta_plane = pack_sbn1(codes, mask, n, m)
+    Xq, s_x = act_quant(X_bits)
+    acc = accumulate(Xq, codes)
+    return dict(codes=codes, mask=mask, s_w=s_w, codes_plane=codes_plane,
+                meta_plane=meta_plane, Xq=Xq, s_x=s_x, acc=acc,
+                y=output(acc, s_w, s_x))

@@ -1,0 +1,209 @@
+"""Independent checks used to pin the oracle (plain loops and exact rationals).
+
+Nothing here calls the oracle's own arithmetic: each check recomputes what it
+verifies another way (brute-force enumeration, exact ``Fraction`` arithmetic,
+bit-by-bit loops, torch autograd) and takes the function under test as an
+argument, so ``test_oracle_mutations.py`` can pass in deliberately broken
+copies and show that the check fails.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+
+
+def _bf16_value(b: int) -> Fraction:
+    """Exact value of a finite bf16 bit pattern, decoded from its fields."""
+    sign = -1 if b & 0x8000 else 1
+    e = (b >> 7) & 0xFF
+    f = b & 0x7F
+    assert e != 0xFF
+    if e == 0:
+        return sign * Fraction(f) * Fraction(2) ** (-126 - 7)
+    return sign * Fraction(128 + f) * Fraction(2) ** (e - 127 - 7)
+
+
+def _f32_value(x) -> Fraction:
+    return Fraction(float(np.float32(x)))
+
+
+# ------------------------------------------------------------------ mask
+def mask_matches_bruteforce(nm_mask, W, n, m) -> bool:
+    """For every group: among all n-subsets of maximal exact sum of |w|, the
+    lexicographically smallest index tuple must be the kept set."""
+    R, K = W.shape
+    got = nm_mask(W, n, m)
+    for r in range(R):
+        for g0 in range(0, K, m):
+            mags = [abs(_bf16_value(int(W[r, g0 + p]))) for p in range(m)]
+            best = None
+            for comb in itertools.combinations(range(m), n):
+                s = sum((mags[p] for p in comb), Fraction(0))
+                if best is None or s > best[0] or (s == best[0] and comb < best[1]):
+                    best = (s, comb)
+            kept = tuple(p for p in range(m) if got[r, g0 + p])
+            if kept != best[1]:
+                return False
+    return True
+
+
+def mask_invariants(nm_mask, W, n, m) -> bool:
+    got = nm_mask(W, n, m)
+    R, K = W.shape
+    mag = (W & 0x7FFF).astype(np.int64).reshape(R, K // m, m)   # |w| order = key order
+    keep = got.reshape(R, K // m, m)
+    if not (keep.sum(-1) == n).all():
+        return False
+    if n == m:
+        return True
+    big = np.where(keep, mag, 1 << 20).min(-1)
+    small = np.where(keep, -1, mag).max(-1)
+    if not (big >= small).all():
+        return False
+    # equal magnitudes across the boundary: survivor index must be lower
+    for r, g in zip(*np.nonzero(big == small)):
+        v = big[r, g]
+        idx_keep = [p for p in range(m) if keep[r, g, p] and mag[r, g, p] == v]
+        idx_drop = [p for p in range(m) if not keep[r, g, p] and mag[r, g, p] == v]
+        if max(idx_keep) > min(idx_drop):
+            return False
+    return True
+
+
+# ------------------------------------------------------------------ scale
+def is_nearest_f32(round_fn, q: Fraction) -> bool:
+    r = round_fn(q)
+    if not np.isfinite(r):
+        return False
+    rf = Fraction(float(r))
+    for nb in (np.nextafter(np.float32(r), np.float32(np.inf)),
+               np.nextafter(np.float32(r), np.float32(-np.inf))):
+        if not np.isfinite(nb):
+            continue
+        d_r, d_nb = abs(q - rf), abs(q - Fraction(float(nb)))
+        if d_r > d_nb:
+            return False
+        if d_r == d_nb and (int(np.float32(r).view(np.uint32)) & 1):
+            return False
+    return True
+
+
+def scale_matches_fsum(weight_scale, W) -> bool:
+    """s_w must be the fp32 nearest to the exact mean |w| (floored at 1e-5).
+
+    The exact sum is rebuilt from the bf16 bit fields with Python integers, and
+    cross-checked against math.fsum of the float64 magnitudes.
+    """
+    flat = [int(b) for b in np.asarray(W, dtype=np.uint16).reshape(-1)]
+    S = sum((abs(_bf16_value(b)) for b in flat), Fraction(0))
+    fs = math.fsum(abs(float(_bf16_value(b))) for b in flat)
+    if abs(Fraction(fs) - S) > S * Fraction(1, 2 ** 52):
+        return False
+    mean = S / len(flat)
+    s = weight_scale(W)
+    floor = _f32_value(np.float32(1e-5))
+    if mean < floor:
+        return Fraction(float(s)) == floor
+    return is_nearest_f32(lambda _q: s, mean)
+
+
+# ------------------------------------------------------------------ ternary
+def ternary_matches_exact(W, s_w, got) -> bool:
+    s = _f32_value(s_w)
+    R, K = W.shape
+    for r in range(R):
+        for k in range(K):
+            ratio = _bf16_value(int(W[r, k])) / s
+            want = 0 if abs(ratio) <= Fraction(1, 2) else (1 if ratio > 0 else -1)
+            if int(got[r, k]) != want:
+                return False
+    return True
+
+
+# ------------------------------------------------------------------ packing
+def pack_by_loops(codes, mask, n, m):
+    R, K = codes.shape
+    enc = {0: (0, 0), 1: (1, 0), -1: (1, 1)}
+    cplanes, mplanes = [], []
+    for r in range(R):
+        cbits, mbits = [], []
+        for k in range(K):
+            mbits.append(1 if mask[r, k] else 0)
+            if mask[r, k]:
+                cbits.extend(enc[int(codes[r, k])])
+        cplanes.append([sum(cbits[8 * i + j] << j for j in range(8)) for i in range(len(cbits) // 8)])
+        mplanes.append([sum(mbits[8 * i + j] << j for j in range(8)) for i in range(K // 8)])
+    cp = np.array(cplanes, dtype=np.uint8).reshape(R, -1)
+    mp = np.array(mplanes, dtype=np.uint8).reshape(R, -1) if n < m else np.zeros((R, 0), np.uint8)
+    return cp, mp
+
+
+def unpack_by_loops(cp, mp, R, K, n, m):
+    out = np.zeros((R, K), dtype=np.int8)
+    dec = {0: 0, 1: 1, 3: -1}
+    for r in range(R):
+        j = 0
+        for k in range(K):
+            keep = True if n == m else bool((int(mp[r, k >> 3]) >> (k & 7)) & 1)
+            if keep:
+                b = 2 * j
+                c = ((int(cp[r, b >> 3]) >> (b & 7)) & 1) | ((((int(cp[r, (b + 1) >> 3]) >> ((b + 1) & 7)) & 1)) << 1)
+                out[r, k] = dec[c]
+                j += 1
+    return out
+
+
+# ------------------------------------------------------------------ activations
+def _round_half_even(q: Fraction) -> int:
+    f = math.floor(q)
+    d = q - f
+    if d > Fraction(1, 2) or (d == Fraction(1, 2) and f % 2 == 1):
+        return f + 1
+    return f
+
+
+def act_quant_matches_exact(X, Xq, s_x) -> bool:
+    """int8 codes equal round-half-even(127*x/a) computed exactly, a = max(absmax, 1e-5);
+    s_x is the fp32 nearest to a/127.  When the 1e-5 floor is active (a has a
+    24-bit significand) the fp32 quotient may sit on the other side of a half
+    step than the exact one, so those rows only need to agree to within 1."""
+    floor = _f32_value(np.float32(1e-5))
+    T, K = X.shape
+    for t in range(T):
+        xs = [_bf16_value(int(b)) for b in X[t]]
+        amax = max((abs(v) for v in xs), default=Fraction(0))
+        a = max(amax, floor)
+        for k in range(K):
+            want = max(-127, min(127, _round_half_even(Fraction(127) * xs[k] / a)))
+            if amax >= floor:
+                if int(Xq[t, k]) != want:
+                    return False
+            elif abs(int(Xq[t, k]) - want) > 1:
+                return False
+        if not is_nearest_f32(lambda _q: s_x[t], a / 127):
+            return False
+    return True
+
+
+# ------------------------------------------------------------------ backward
+def backward_by_autograd(W, X, dY, codes, s_w, Xq, s_x):
+    """torch float64 autograd of the straight-through formulation
+    w_eff = w + (s_w*Wt - w).detach(), x_hat = x + (s_x*Xq - x).detach()."""
+    import torch
+
+    def f64(bits):
+        return torch.from_numpy((np.asarray(bits, np.uint16).astype(np.uint32) << 16)
+                                .view(np.float32).astype(np.float64))
+
+    w = f64(W).requires_grad_(True)
+    x = f64(X).requires_grad_(True)
+    w_q = float(s_w) * torch.from_numpy(codes.astype(np.float64))
+    x_q = torch.from_numpy(s_x.astype(np.float64))[:, None] * torch.from_numpy(Xq.astype(np.float64))
+    w_eff = w + (w_q - w).detach()
+    x_hat = x + (x_q - x).detach()
+    y = x_hat @ w_eff.T
+    y.backward(f64(dY))
+    return x.grad.numpy(), w.grad.numpy()

@@ -1,0 +1,187 @@
+"""Plant plausible mistakes in copies of the oracle and check the pins catch them.
+
+Each mutant is a small rewrite of one oracle step with one error (a wrong
+tie-break, a dropped term, a wrong sign or encoding, the wrong operand).  The
+test asserts that the corresponding pin in ``pins.py`` rejects it, so a pin
+that passes is known to be sensitive to that class of error.  Mutants live
+only here, on the CPU; the oracle itself is never modified.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle as O
+import pins
+from workloads import f32_to_bf16_bits, gaussian_bf16
+
+TIES = np.array([[0x3C00, 0x3C00, 0x3C00, 0x3C00, 0x0000, 0x8000, 0x0000, 0x3C80,
+                  0x3F80, 0xBF80, 0x3F80, 0x3D00, 0x0001, 0x8001, 0x0080, 0x0001]], dtype=np.uint16)
+
+
+def _mask_highest_index_ties(W, n, m):
+    R, K = W.shape
+    mag = np.abs(O.bf16_to_f64(W)).reshape(R, K // m, m)[..., ::-1]
+    order = np.argsort(-mag, axis=-1, kind="stable")[..., :n]
+    keep = np.zeros(mag.shape, bool)
+    np.put_along_axis(keep, order, True, axis=-1)
+    return keep[..., ::-1].reshape(R, K)
+
+
+def _mask_signed_not_abs(W, n, m):
+    R, K = W.shape
+    val = O.bf16_to_f64(W).reshape(R, K // m, m)
+    order = np.argsort(-val, axis=-1, kind="stable")[..., :n]
+    keep = np.zeros(val.shape, bool)
+    np.put_along_axis(keep, order, True, axis=-1)
+    return keep.reshape(R, K)
+
+
+def _mask_smallest(W, n, m):
+    R, K = W.shape
+    mag = np.abs(O.bf16_to_f64(W)).reshape(R, K // m, m)
+    order = np.argsort(mag, axis=-1, kind="stable")[..., :n]
+    keep = np.zeros(mag.shape, bool)
+    np.put_along_axis(keep, order, True, axis=-1)
+    return keep.reshape(R, K)
+
+
+@pytest.mark.parametrize("mutant", [_mask_highest_index_ties, _mask_signed_not_abs, _mask_smallest])
+def test_mask_mutants_are_caught(mutant):
+    W2 = gaussian_bf16((4, 32), 0.02, seed=1, stream=0)
+    caught = (not pins.mask_matches_bruteforce(mutant, TIES, 2, 4)
+              or not pins.mask_matches_bruteforce(mutant, W2, 2, 4)
+              or not pins.mask_invariants(mutant, W2, 2, 4)
+              or not pins.mask_matches_bruteforce(mutant, TIES, 3, 8))
+    assert caught
+
+
+def _scale_survivors_only(W):
+    mask = O.nm_mask(W, 2, 4)
+    vals = np.abs(O.bf16_to_f64(W))[mask]
+    return np.float32(vals.mean())
+
+
+def _scale_float32_sum(W):
+    vals = np.abs(O.bf16_to_f32(W)).reshape(-1)
+    acc = np.float32(0)
+    for v in vals:                 # sequential float32 accumulation: rounding drift
+        acc = np.float32(acc + v)
+    return np.float32(max(acc / np.float32(vals.size), np.float32(1e-5)))
+
+
+def _scale_max_not_mean(W):
+    return np.float32(np.abs(O.bf16_to_f64(W)).max())
+
+
+def _scale_no_floor(W):
+    return O.round_to_f32(O.absmean_exact(W))
+
+
+@pytest.mark.parametrize("mutant", [_scale_survivors_only, _scale_float32_sum, _scale_max_not_mean, _scale_no_floor])
+def test_scale_mutants_are_caught(mutant):
+    W = gaussian_bf16((128, 128), 0.02, seed=0, stream=0)
+    Z = np.zeros((2, 8), np.uint16)
+    assert (not pins.scale_matches_fsum(mutant, W)) or (not pins.scale_matches_fsum(mutant, Z))
+
+
+def _ternary_ge(W, s):
+    w = O.bf16_to_f64(W)
+    h = float(s) / 2
+    return np.where(w >= h, 1, np.where(w <= -h, -1, 0)).astype(np.int8)
+
+
+def _ternary_half_up(W, s):
+    w = O.bf16_to_f64(W) / float(s)
+    return np.clip(np.floor(w + 0.5), -1, 1).astype(np.int8)
+
+
+def _ternary_threshold_s(W, s):
+    w = O.bf16_to_f64(W)
+    return np.where(w > float(s), 1, np.where(w < -float(s), -1, 0)).astype(np.int8)
+
+
+@pytest.mark.parametrize("mutant", [_ternary_ge, _ternary_half_up, _ternary_threshold_s])
+def test_ternary_mutants_are_caught(mutant):
+    s = np.float32(0.25)
+    W = f32_to_bf16_bits(np.array([[0.125, -0.125, 0.1259765625, -0.1259765625, 0.2, 0.3]], np.float32))
+    assert not pins.ternary_matches_exact(W, s, mutant(W, s))
+
+
+def _pack_swapped_code_bits(codes, mask, n, m):
+    cp, mp = O.pack_sbn1(-codes, mask, n, m)     # sign flipped: +1 <-> -1 encodings
+    return cp, mp
+
+
+def _pack_meta_big_endian(codes, mask, n, m):
+    cp, mp = O.pack_sbn1(codes, mask, n, m)
+    if n < m:
+        mp = np.packbits(mask.astype(np.uint8), axis=1, bitorder="big")
+    return cp, mp
+
+
+@pytest.mark.parametrize("mutant", [_pack_swapped_code_bits, _pack_meta_big_endian])
+def test_pack_mutants_are_caught(mutant):
+    W = gaussian_bf16((4, 64), 0.02, seed=4, stream=0)
+    codes, mask, _ = O.quant_then_mask(W, 2, 4)
+    cp, mp = mutant(codes, mask, 2, 4)
+    ecp, emp = pins.pack_by_loops(codes, mask, 2, 4)
+    assert not (cp.tolist() == ecp.tolist() and mp.tolist() == emp.tolist())
+
+
+def _aq_reciprocal(X):
+    x = O.bf16_to_f32(X)
+    a = np.maximum(np.abs(x).max(1), np.float32(1e-5))
+    q = np.clip(np.rint(x * (np.float32(127) / a)[:, None]), -127, 127).astype(np.int8)
+    return q, (a / np.float32(127)).astype(np.float32)
+
+
+def _aq_half_away(X):
+    x = O.bf16_to_f32(X)
+    a = np.maximum(np.abs(x).max(1), np.float32(1e-5))
+    v = (np.float32(127) * x) / a[:, None]
+    q = np.clip(np.sign(v) * np.floor(np.abs(v) + 0.5), -127, 127).astype(np.int8)
+    return q, (a / np.float32(127)).astype(np.float32)
+
+
+def _aq_scale_128(X):
+    x = O.bf16_to_f32(X)
+    a = np.maximum(np.abs(x).max(1), np.float32(1e-5))
+    q = np.clip(np.rint((np.float32(128) * x) / a[:, None]), -128, 127).astype(np.int8)
+    return q, (a / np.float32(128)).astype(np.float32)
+
+
+@pytest.mark.parametrize("mutant", [_aq_reciprocal, _aq_half_away, _aq_scale_128])
+def test_act_quant_mutants_are_caught(mutant):
+    X = f32_to_bf16_bits(np.array([[3.0, 1.5, -1.5, 0.75, 2.0, -1.0, 0.5, 0.25],
+                                   [8.0, 4.0, -4.0, 1.5, 3.0, 0.0, 1.0, 2.0],
+                                   [2.375, 1.1875, -1.1875, 0.5, 1.0, 2.0, 0.0, 0.25],
+                                   [127.0, 62.5, 2.5, -2.5, 0.5, 1.5, -62.5, 0.0]], np.float32))
+    q, s = mutant(X)
+    assert not pins.act_quant_matches_exact(X, q, s)
+
+
+def _bwd_masked_grad_w(dY, Xq, s_x, codes, s_w):
+    gX, gW = O.backward(dY, Xq, s_x, codes, s_w)
+    return gX, np.where(codes != 0, gW, 0.0)
+
+
+def _bwd_raw_codes_no_scale(dY, Xq, s_x, codes, s_w):
+    gX, gW = O.backward(dY, Xq, s_x, codes, s_w)
+    return gX / float(s_w), gW
+
+
+def _bwd_unscaled_activations(dY, Xq, s_x, codes, s_w):
+    gX, _ = O.backward(dY, Xq, s_x, codes, s_w)
+    return gX, O.bf16_to_f64(dY).T @ Xq.astype(np.float64)
+
+
+@pytest.mark.parametrize("mutant", [_bwd_masked_grad_w, _bwd_raw_codes_no_scale, _bwd_unscaled_activations])
+def test_backward_mutants_are_caught(mutant):
+    W = gaussian_bf16((16, 64), 0.02, seed=8, stream=0)
+    X = gaussian_bf16((4, 64), 1.0, seed=8, stream=1)
+    dY = gaussian_bf16((4, 16), 1e-2, seed=8, stream=2)
+    f = O.forward(W, X, 2, 4)
+    gX, gW = mutant(dY, f["Xq"], f["s_x"], f["codes"], f["s_w"])
+    rX, rW = pins.backward_by_autograd(W, X, dY, f["codes"], f["s_w"], f["Xq"], f["s_x"])
+    assert not (np.allclose(gX, rX, rtol=1e-9) and np.allclose(gW, rW, rtol=1e-9))

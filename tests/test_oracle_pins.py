@@ -1,0 +1,288 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each test compares the oracle with a hand-derived worked example, a brute-force
+enumeration, a closed form, an invariant, a library routine or exact rational
+arithmetic.  ``tests/test_oracle_mutations.py`` plants plausible mistakes in
+copies of the oracle functions and shows that these checks catch them.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st, HealthCheck
+
+import oracle as O
+from workloads import f32_to_bf16_bits, gaussian_bf16, bf16_bits_to_f32
+import pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+HSET = settings(max_examples=60, derandomize=True, deadline=None,
+                suppress_health_check=[HealthCheck.too_slow])
+
+
+def f32_bits(x) -> int:
+    return int(np.asarray(x, dtype=np.float32).reshape(1).view(np.uint32)[0])
+
+
+# ----------------------------------------------------------------- worked example
+def test_worked_example_1x8():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example_1x8.json")))
+    n, m = g["n"], g["m"]
+    W = f32_to_bf16_bits(np.array([g["W"]], dtype=np.float32))
+    X = f32_to_bf16_bits(np.array([g["X"]], dtype=np.float32))
+    e = g["expect"]
+    f = O.forward(W, X, n, m)
+    assert f32_bits(f["s_w"]) == int(e["s_w_bits"], 16)
+    assert f["mask"].astype(int).tolist() == [e["mask"]]
+    assert O.ternary_codes(W, f["s_w"]).tolist() == [e["ternary_all"]]
+    assert f["codes"].tolist() == [e["effective"]]
+    assert f["meta_plane"].tolist() == [[int(b, 16) for b in e["meta_bytes"]]]
+    assert f["codes_plane"].tolist() == [[int(b, 16) for b in e["codes_bytes"]]]
+    assert f["Xq"].tolist() == [e["Xq"]]
+    assert f32_bits(f["s_x"][0]) == int(e["s_x_bits"], 16)
+    assert int(f["acc"][0, 0]) == e["acc"]
+    # exact real value -51/127; the oracle applies the fp32 s_x (8/127 rounded),
+    # so the two differ by at most that one fp32 rounding
+    exact = Fraction(e["y_num"], e["y_den"])
+    assert abs(Fraction(float(f["y"][0, 0])) - exact) <= abs(exact) * Fraction(1, 2 ** 23)
+
+
+# ----------------------------------------------------------------- mask
+# small bf16 alphabet: forces ties, +-0, subnormals and all-zero groups
+ALPHABET = [0x0000, 0x8000, 0x0001, 0x8001, 0x3C00, 0xBC00, 0x3C80, 0xBC80,
+            0x3D00, 0x3F80, 0xBF80, 0x3F81, 0x4000, 0x0080]
+
+
+@st.composite
+def small_w(draw, rows=(1, 3), groups=(1, 4)):
+    m = draw(st.sampled_from([4, 8]))
+    n = draw(st.integers(1, m))
+    R = draw(st.integers(*rows))
+    G = draw(st.integers(*groups))
+    vals = draw(st.lists(st.sampled_from(ALPHABET), min_size=R * G * m, max_size=R * G * m))
+    return np.array(vals, dtype=np.uint16).reshape(R, G * m), n, m
+
+
+@HSET
+@given(small_w())
+def test_mask_matches_bruteforce_enumeration(case):
+    W, n, m = case
+    assert pins.mask_matches_bruteforce(O.nm_mask, W, n, m)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (3, 4), (4, 4), (2, 8), (4, 8), (6, 8), (8, 8), (3, 8)])
+def test_mask_invariants_gaussian(n, m):
+    W = gaussian_bf16((64, 512), 0.02, seed=7, stream=0)
+    assert pins.mask_invariants(O.nm_mask, W, n, m)
+
+
+def test_mask_dense_control_is_all_ones():
+    W = gaussian_bf16((8, 64), 0.02, seed=1, stream=0)
+    assert O.nm_mask(W, 8, 8).all() and O.nm_mask(W, 4, 4).all()
+
+
+def test_mask_recovers_support_of_distinct_nonzeros():
+    rng = np.random.default_rng(3)
+    for n, m in [(2, 4), (6, 8), (1, 4), (2, 8)]:
+        R, G = 5, 16
+        vals = np.zeros((R, G, m), dtype=np.float32)
+        support = np.zeros((R, G, m), dtype=bool)
+        for r in range(R):
+            for gi in range(G):
+                pos = rng.choice(m, size=n, replace=False)
+                mags = rng.choice(np.arange(1, 60), size=n, replace=False).astype(np.float32) / 64
+                sgn = rng.choice([-1.0, 1.0], size=n).astype(np.float32)
+                vals[r, gi, pos] = mags * sgn
+                support[r, gi, pos] = True
+        W = f32_to_bf16_bits(vals.reshape(R, G * m))
+        assert (O.nm_mask(W, n, m) == support.reshape(R, G * m)).all()
+
+
+# ----------------------------------------------------------------- scale
+def test_round_to_f32_agrees_with_numpy_cast_on_doubles():
+    rng = np.random.default_rng(11)
+    xs = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-40, 38, 2000),
+                         np.ldexp(rng.integers(1, 2 ** 30, 500).astype(np.float64), -150),
+                         [1e-45, 1.4e-45, 7e-46, 3.4028235e38, 3.4028236e38, 1e39, -2.5e-40]])
+    for x in xs:
+        assert O.round_to_f32(Fraction(float(x))) == np.float32(x) or (
+            np.isinf(np.float32(x)) and np.isinf(O.round_to_f32(Fraction(float(x)))))
+
+
+@HSET
+@given(st.integers(1, 2 ** 80), st.integers(1, 2 ** 60))
+def test_round_to_f32_is_nearest_ties_even(num, den):
+    assert pins.is_nearest_f32(O.round_to_f32, Fraction(num, den))
+
+
+def test_round_to_f32_exact_ties():
+    # 1 + 2^-24 is half-way between 1 and 1 + 2^-23 -> even (1.0)
+    assert O.round_to_f32(Fraction(2 ** 24 + 1, 2 ** 24)) == np.float32(1.0)
+    # 1 + 3*2^-24 is half-way between 1+2^-23 and 1+2^-22 -> even (1+2^-22)
+    assert O.round_to_f32(Fraction(2 ** 24 + 3, 2 ** 24)) == np.float32(1 + 2 ** -22)
+    assert O.round_to_f32(Fraction(-(2 ** 24 + 3), 2 ** 24)) == np.float32(-(1 + 2 ** -22))
+
+
+def test_scale_closed_form_full_tiny_weight():
+    W = gaussian_bf16((256, 256), 0.02, seed=0, stream=0)
+    assert pins.scale_matches_fsum(O.weight_scale, W)
+
+
+@HSET
+@given(small_w(rows=(1, 4), groups=(1, 8)))
+def test_scale_closed_form_small(case):
+    W, _, _ = case
+    assert pins.scale_matches_fsum(O.weight_scale, W)
+
+
+def test_scale_gaussian_statistic():
+    # E|w| for N(0, s^2) is s*sqrt(2/pi) = 0.015957691 at s = 0.02
+    W = gaussian_bf16((1024, 1024), 0.02, seed=5, stream=0)
+    assert abs(float(O.weight_scale(W)) - 0.02 * math.sqrt(2 / math.pi)) < 2e-4
+
+
+def test_scale_floor_for_zero_weights():
+    W = np.zeros((4, 16), dtype=np.uint16)
+    assert O.weight_scale(W) == np.float32(1e-5)
+
+
+# ----------------------------------------------------------------- ternary
+def test_ternary_exact_boundaries():
+    # scale 0.25 exactly: four entries of 0.25 give sum 1, mean over 4 = 0.25.
+    # half scale is 0.125: |w| = 0.125 -> 0 (exact half, rounds to even 0)
+    s = np.float32(0.25)
+    vals = np.array([[0.125, -0.125, 0.1259765625, -0.1259765625, 0.12451171875, 0.375, -0.375, 1.0,
+                      0.0, -0.0, 1e-30, 0.25]], dtype=np.float32)
+    W = f32_to_bf16_bits(vals)
+    got = O.ternary_codes(W, s)
+    assert pins.ternary_matches_exact(W, s, got)
+    assert got.tolist() == [[0, 0, 1, -1, 0, 1, -1, 1, 0, 0, 0, 1]]
+
+
+@HSET
+@given(small_w(rows=(1, 3), groups=(1, 6)))
+def test_ternary_matches_exact_rational(case):
+    W, n, m = case
+    s = O.weight_scale(W)
+    assert pins.ternary_matches_exact(W, s, O.ternary_codes(W, s))
+
+
+def test_ternary_zero_fraction_gaussian_closed_form():
+    # P(|w| <= E|w|/2) for Gaussian w = 2*Phi(sqrt(2/pi)/2) - 1 = 0.31010...
+    W = gaussian_bf16((1024, 2048), 0.02, seed=9, stream=0)
+    q = O.ternary_codes(W, O.weight_scale(W))
+    phi = 0.5 * (1 + math.erf(math.sqrt(2 / math.pi) / 2 / math.sqrt(2)))
+    assert abs((q == 0).mean() - (2 * phi - 1)) < 3e-3
+
+
+def test_quant_then_mask_uses_dense_scale():
+    W = gaussian_bf16((16, 64), 0.02, seed=2, stream=0)
+    codes, mask, s_w = O.quant_then_mask(W, 2, 4)
+    assert s_w == O.weight_scale(W)                      # scale over all of W
+    full = O.ternary_codes(W, s_w)
+    assert (codes == np.where(mask, full, 0)).all()
+    assert (codes[~mask] == 0).all()
+
+
+# ----------------------------------------------------------------- packing
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (3, 4), (4, 4), (2, 8), (4, 8), (6, 8), (8, 8)])
+def test_pack_matches_bitwise_loop(n, m):
+    W = gaussian_bf16((6, 64), 0.02, seed=n * 10 + m, stream=0)
+    codes, mask, _ = O.quant_then_mask(W, n, m)
+    cp, mp = O.pack_sbn1(codes, mask, n, m)
+    ecp, emp = pins.pack_by_loops(codes, mask, n, m)
+    assert cp.tolist() == ecp.tolist() and mp.tolist() == emp.tolist()
+    assert (cp.nbytes, mp.nbytes) == O.packed_bytes(6, 64, n, m)
+    assert (pins.unpack_by_loops(cp, mp, 6, 64, n, m) == codes).all()
+
+
+# ----------------------------------------------------------------- activations
+def test_act_quant_integer_identity():
+    rng = np.random.default_rng(4)
+    X = rng.integers(-127, 128, size=(8, 64)).astype(np.float32)
+    X[:, 5] = 127.0
+    Xq, s_x = O.act_quant(f32_to_bf16_bits(X))
+    assert (Xq == X).all() and (s_x == np.float32(1.0)).all()
+
+
+@HSET
+@given(st.lists(st.sampled_from(ALPHABET + [0x3F40, 0xBF40, 0x4040, 0x42FE, 0x3DFF, 0x0100, 0x3727]),
+                min_size=64, max_size=64), st.integers(1, 4))
+def test_act_quant_decision_equals_exact_rational(vals, rows):
+    X = np.array((vals * rows)[: 64 * rows], dtype=np.uint16).reshape(rows, 64)
+    Xq, s_x = O.act_quant(X)
+    assert pins.act_quant_matches_exact(X, Xq, s_x)
+
+
+def test_act_quant_gaussian_with_outliers_matches_exact():
+    from workloads import gaussian_bf16_with_outliers
+    X = gaussian_bf16_with_outliers((32, 256), 1.0, 0, 1, 0.01, 20.0)
+    Xq, s_x = O.act_quant(X)
+    assert pins.act_quant_matches_exact(X, Xq, s_x)
+
+
+def test_act_quant_half_ties_go_to_even():
+    # a = 8: x*127/8 for x = 4 is 63.5 -> 64; x = 12/... construct 0.5 ties directly
+    X = f32_to_bf16_bits(np.array([[4.0, 8.0, -4.0, 1.5, 3.0]], dtype=np.float32))
+    Xq, _ = O.act_quant(X)
+    # 127*4/8 = 63.5 -> 64 ; -63.5 -> -64 ; 127*1.5/8 = 23.8125 -> 24 ; 127*3/8 = 47.625 -> 48
+    assert Xq.tolist() == [[64, 127, -64, 24, 48]]
+    # a = 3: 1.5*127/3 = 63.5 -> 64 (tie with an inexact reciprocal)
+    Xq, _ = O.act_quant(f32_to_bf16_bits(np.array([[3.0, 1.5, -1.5]], dtype=np.float32)))
+    assert Xq.tolist() == [[127, 64, -64]]
+    # a = 2.375: 127*1.1875/2.375 = 63.5 exactly; multiplying by a rounded
+    # reciprocal of a would land just below the half and give 63
+    Xq, _ = O.act_quant(f32_to_bf16_bits(np.array([[2.375, 1.1875, -1.1875]], dtype=np.float32)))
+    assert Xq.tolist() == [[127, 64, -64]]
+    # a = 127: q = rint(x); halves go to the even neighbour (62.5 -> 62, 2.5 -> 2)
+    Xq, _ = O.act_quant(f32_to_bf16_bits(np.array([[127.0, 62.5, 2.5, -2.5, 0.5, 1.5, -62.5]], dtype=np.float32)))
+    assert Xq.tolist() == [[127, 62, 2, -2, 0, 2, -62]]
+
+
+def test_act_quant_zero_token():
+    Xq, s_x = O.act_quant(np.zeros((2, 64), dtype=np.uint16))
+    assert (Xq == 0).all() and s_x[0] == np.float32(np.float32(1e-5) / np.float32(127))
+
+
+# ----------------------------------------------------------------- matmul + output
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (8, 8), (1, 4)])
+def test_accumulate_matches_int64_matmul_of_unpacked(n, m):
+    W = gaussian_bf16((48, 128), 0.02, seed=3, stream=0)
+    X = gaussian_bf16((9, 128), 1.0, seed=3, stream=1)
+    f = O.forward(W, X, n, m)
+    dense = pins.unpack_by_loops(f["codes_plane"], f["meta_plane"], 48, 128, n, m)
+    ref = f["Xq"].astype(np.int64) @ dense.astype(np.int64).T      # numpy integer matmul
+    assert (f["acc"] == ref).all()
+
+
+def test_output_scaling_exact_rational():
+    W = gaussian_bf16((8, 64), 0.02, seed=6, stream=0)
+    X = gaussian_bf16((3, 64), 1.0, seed=6, stream=1)
+    f = O.forward(W, X, 2, 4)
+    for t in range(3):
+        for r in range(8):
+            exact = Fraction(int(f["acc"][t, r])) * Fraction(float(f["s_w"])) * Fraction(float(f["s_x"][t]))
+            got = Fraction(float(f["y"][t, r]))
+            assert abs(got - exact) <= abs(exact) * Fraction(1, 2 ** 50)
+
+
+# ----------------------------------------------------------------- backward
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
+def test_backward_matches_torch_autograd_ste(n, m):
+    W = gaussian_bf16((24, 64), 0.02, seed=8, stream=0)
+    X = gaussian_bf16((5, 64), 1.0, seed=8, stream=1)
+    dY = gaussian_bf16((5, 24), 1e-2, seed=8, stream=2)
+    f = O.forward(W, X, n, m)
+    gX, gW = O.backward(dY, f["Xq"], f["s_x"], f["codes"], f["s_w"])
+    rX, rW = pins.backward_by_autograd(W, X, dY, f["codes"], f["s_w"], f["Xq"], f["s_x"])
+    assert np.allclose(gX, rX, rtol=1e-12, atol=1e-15)
+    assert np.allclose(gW, rW, rtol=1e-12, atol=1e-15)
+    # dense gradient through the mask: pruned positions receive gradient
+    mask = f["mask"]
+    assert np.abs(gW[~mask]).sum() > 0
