@@ -1,0 +1,212 @@
+/*
+ * sbn.h -- C ABI of the Sparse-BitLinear hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The operator is the Sparse-BitLinear layer of "Sparse-BitNet: 1.58-bit LLMs
+ * are Naturally Friendly to Semi-Structured Sparsity" (arXiv 2603.05168), as
+ * summarised on the gist.science pages (Japanese "技術概要" §2.1, German
+ * "Technische Zusammenfassung" §2, Korean "기술 요약" §2.1-2.2, French
+ * "Résumé technique" §2) and the fugumt.com abstract page.  It replaces a
+ * linear layer: BF16 master weights W [R x K] get an N:M mask from their
+ * magnitudes, are ternarized to {-1, 0, +1} with one per-tensor scale and
+ * masked (quantize, then mask), and multiply int8 activations.  The backward
+ * pass is a straight-through estimator on both quantizers with a dense
+ * gradient through the mask.
+ *
+ * Shapes: T tokens, R output features, K input features.  N:M groups run
+ * along K inside each output row.  Supported ratios: m in {4, 8} and
+ * 1 <= n <= m (n == m is the dense-ternary control).  K must be a multiple
+ * of 64.
+ *
+ * Packed weight format ("SBN-v1", the explicit N:M metadata of the
+ * quantize-then-mask order; the pages do not print a layout):
+ *   meta  : per row a K-bit bitmap, bit (g*m + p) set iff position p of
+ *           group g survives; bit b is bit (b & 7) of byte (b >> 3).
+ *           Row stride K/8 bytes.  Absent (may be NULL, 0 bytes) when n == m.
+ *   codes : per row the 2-bit codes of the survivors in increasing k; the
+ *           j-th survivor uses bits 2j and 2j+1, same bit order.
+ *           00 = 0, 01 = +1, 11 = -1.  Row stride K*n/(4*m) bytes.
+ *   s_w   : one float, the per-tensor scale (device memory).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or keeps them.  bf16 tensors are passed as
+ *     uint16_t bit patterns.  All tensors are row-major; leading dimensions
+ *     (ld*) are in elements.  Device pointers must be 16-byte aligned and
+ *     leading dimensions multiples of 8 elements.
+ *   - Scales s_w and s_x stay on the device; no call synchronises the host.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *   - Scratch memory is the caller's workspace `ws` of at least
+ *     sbn_workspace_bytes() bytes (ws may be NULL when that size is 0).
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     any error nothing is launched, outputs are untouched, and a message is
+ *     available from sbn_last_error() (per thread).  No C++ exception or
+ *     abort crosses the ABI.
+ *   - Inputs with NaN or Inf are outside the contract.  Activations with
+ *     |x| >= 2^120 are outside the contract (127*x must not overflow).
+ *   - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef SBN_H
+#define SBN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SBN_ABI_VERSION 1
+
+typedef enum sbn_status {
+  SBN_OK = 0,
+  SBN_ERR_NULL = 1,            /* a required pointer is NULL */
+  SBN_ERR_SHAPE = 2,           /* T, R, K < 1; K % 64 != 0; ld < row length; T > 16 for the GEMV */
+  SBN_ERR_UNSUPPORTED_NM = 3,  /* m not in {4, 8} or n not in [1, m] */
+  SBN_ERR_ALIGN = 4,           /* pointer not 16-byte aligned or ld not a multiple of 8 */
+  SBN_ERR_WORKSPACE = 5,       /* ws_bytes smaller than sbn_workspace_bytes() */
+  SBN_ERR_DTYPE = 6,           /* output dtype not allowed for this call */
+  SBN_ERR_HIP = 7              /* a HIP launch or runtime call failed */
+} sbn_status;
+
+typedef enum sbn_dtype {
+  SBN_F32 = 0,                 /* float32 */
+  SBN_BF16 = 1,                /* bfloat16, round to nearest even from float32 */
+  SBN_I32_ACC = 2              /* raw int32 accumulator sum_k Xq*Wt, unscaled */
+} sbn_dtype;
+
+typedef enum sbn_op {
+  SBN_OP_PACK = 0,
+  SBN_OP_ACT_QUANT = 1,
+  SBN_OP_GEMM = 2,
+  SBN_OP_GEMV = 3,
+  SBN_OP_BACKWARD = 4
+} sbn_op;
+
+/* ABI version of the loaded library (SBN_ABI_VERSION). */
+int sbn_abi_version(void);
+
+/* Static English text for a status code. */
+const char* sbn_status_string(sbn_status s);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* sbn_last_error(void);
+
+/*
+ * Allocation sizes of the packed planes for an R x K weight at ratio n:m:
+ * codes_bytes = R*K*n/(4*m) and meta_bytes = R*K/8 (0 when n == m), each
+ * rounded up to a multiple of 16 bytes.  The data fill the first
+ * R*K*n/(4*m) and R*K/8 bytes; readers load whole aligned words, so the
+ * buffers must have the rounded sizes.
+ * Host-only; errors: SBN_ERR_NULL, SBN_ERR_SHAPE, SBN_ERR_UNSUPPORTED_NM.
+ */
+sbn_status sbn_packed_bytes(int64_t R, int64_t K, int n, int m,
+                            size_t* codes_bytes, size_t* meta_bytes);
+
+/*
+ * Workspace bytes needed by `op` at these sizes (0 if none).  Host-only.
+ * Arguments that do not apply to `op` are ignored (pass 0).
+ */
+sbn_status sbn_workspace_bytes(sbn_op op, int64_t T, int64_t R, int64_t K,
+                               int n, int m, size_t* bytes);
+
+/*
+ * Mask, ternarize and pack the master weights.
+ *
+ * Mask (gist.science de §2 "Methodik", ko §2.1, fr §2, ja §2.1): in every
+ * group of m consecutive weights along K, keep the n largest |w| of the
+ * BF16 master weights; equal magnitudes go to the lower index.  The mask is
+ * recomputed from W on every call (ja §2.1, ko §2.2: every training step).
+ * Scale: s_w = max(fp32(mean |W|), 1e-5), the mean taken exactly over all
+ * R*K entries before masking (quantize-then-mask order, ja §2.1, fr §2) and
+ * rounded once to fp32.
+ * Ternarize: q = RoundClip(w / s_w, -1, 1), round half to even, i.e.
+ * q = sign(w) if |w| > s_w/2 else 0; pruned positions are 0.
+ *
+ *   W      [R x K] bf16, row stride ldw >= K                         (in)
+ *   codes  [R x K*n/(4m)] bytes                                     (out)
+ *   meta   [R x K/8] bytes; ignored and may be NULL when n == m     (out)
+ *   s_w    1 float                                                  (out)
+ *   ws     workspace of sbn_workspace_bytes(SBN_OP_PACK, 0, R, K, n, m).  Its
+ *          first 2304 bytes hold a completion counter and per-exponent sums
+ *          that must be zero when a call starts: zero-fill the workspace once
+ *          before its first use; every call leaves that header zeroed again.
+ *          Do not reuse the memory for other operations between pack calls.
+ *
+ * Limits: K <= 2^18 and R*K < 2^37.
+ * The result is bit-for-bit independent of launch geometry (the sum of
+ * |w| is formed exactly in integer arithmetic).
+ */
+sbn_status sbn_mask_ternarize_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw,
+                                   int n, int m, uint8_t* codes, uint8_t* meta, float* s_w,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Per-token absmax int8 quantization of the activations (the pages leave
+ * the activation path open; this is the 1.58-bit BitNet convention):
+ *   a = max(max_k |x[t,k]|, 1e-5); Xq = rint((127*x) / a) in float32,
+ *   round half to even, in [-127, 127]; s_x[t] = a / 127 (float32).
+ *
+ *   X   [T x K] bf16, row stride ldx >= K   (in)
+ *   Xq  [T x K] int8, contiguous            (out)
+ *   s_x [T] float                           (out)
+ */
+sbn_status sbn_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx,
+                         int8_t* Xq, float* s_x, void* stream);
+
+/*
+ * Sparse ternary matmul, the forward of Sparse-BitLinear (ja §2.1, de §2;
+ * the pages run it on a custom 6:8 sparse kernel, ja §3.2, de §4):
+ *   acc[t,r] = sum_k Xq[t,k] * Wt[r,k]   (exact int32)
+ *   Y[t,r]   = fl32(fl32(acc) * fl32(s_w * s_x[t]))   for SBN_F32,
+ *              that value rounded to bf16            for SBN_BF16,
+ *              acc                                   for SBN_I32_ACC.
+ *
+ *   Xq [T x K] int8 contiguous, s_x [T] float             (in)
+ *   codes, meta, s_w: packed weight from sbn_mask_ternarize_pack (in)
+ *   Y  [T x R] of dtype ydt, row stride ldy >= R          (out)
+ *   ws workspace of sbn_workspace_bytes(SBN_OP_GEMM, T, R, K, n, m)
+ *
+ * 2:4 runs on the gfx950 structured-sparse int8 matrix instructions; other
+ * ratios expand to dense int8 tiles and run on dense int8 matrix cores.
+ */
+sbn_status sbn_sparse_ternary_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                   const uint8_t* codes, const uint8_t* meta, const float* s_w,
+                                   int64_t R, int n, int m, void* Y, sbn_dtype ydt, int64_t ldy,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Same operation as sbn_sparse_ternary_gemm for decode batches, 1 <= T <= 16:
+ * streams the packed weight once from memory and unpacks it in registers.
+ * ws: sbn_workspace_bytes(SBN_OP_GEMV, ...) (currently 0).
+ */
+sbn_status sbn_sparse_ternary_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                   const uint8_t* codes, const uint8_t* meta, const float* s_w,
+                                   int64_t R, int n, int m, void* Y, sbn_dtype ydt, int64_t ldy,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dual-STE backward of Sparse-BitLinear (ja §2.1, de §2 "Dual STE",
+ * ko §2.2, fr §2): identity Jacobian through both quantizers and a dense
+ * gradient through the mask, so every master weight receives a gradient.
+ *   dX[t,k] = sum_r dY[t,r] * s_w * Wt[r,k]       (through the sparse ternary W)
+ *   dW[r,k] = sum_t dY[t,r] * s_x[t] * Xq[t,k]    (dense, every (r,k))
+ * No derivative of s_w or s_x is taken.  Accumulation is float32.
+ *
+ *   dY [T x R] bf16 contiguous                     (in)
+ *   Xq [T x K] int8 contiguous, s_x [T] float      (in, from sbn_act_quant)
+ *   codes, meta, s_w: packed weight                (in)
+ *   dX [T x K] of dtype dxdt (SBN_F32 or SBN_BF16), contiguous; may be NULL (out)
+ *   dW [R x K] float, contiguous; may be NULL      (out)
+ *   ws workspace of sbn_workspace_bytes(SBN_OP_BACKWARD, T, R, K, n, m)
+ * R must be a multiple of 8 (dY rows are read in 16-byte units).
+ */
+sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
+                        const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
+                        const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,
+                        void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SBN_H */

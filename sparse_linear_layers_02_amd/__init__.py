@@ -1,0 +1,230 @@
+"""Python binding of libsbn, the Sparse-BitLinear hot path for MI355X (gfx950).
+
+Argument marshalling only: every function here checks nothing numerical,
+allocates outputs with PyTorch when the caller did not pass them, and calls
+the C entry point of the same name in ``libsbn.so`` (declared in
+``include/sbn.h``) with raw device pointers on the current HIP stream.  All
+computation happens in the HIP kernels.  If the library is not built, import
+of the binding still works but the first call raises ``SbnError``: there is no
+fallback implementation.
+
+Tensor conventions: bf16 tensors are ``torch.bfloat16`` (passed as bit
+patterns), int8 ``torch.int8``, packed planes ``torch.uint8``, scales
+``torch.float32``; all on the same CUDA (HIP) device, row-major.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libsbn.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "sbn.h")
+
+SBN_F32, SBN_BF16, SBN_I32_ACC = 0, 1, 2
+SBN_OP_PACK, SBN_OP_ACT_QUANT, SBN_OP_GEMM, SBN_OP_GEMV, SBN_OP_BACKWARD = 0, 1, 2, 3, 4
+STATUS = {0: "SBN_OK", 1: "SBN_ERR_NULL", 2: "SBN_ERR_SHAPE", 3: "SBN_ERR_UNSUPPORTED_NM",
+          4: "SBN_ERR_ALIGN", 5: "SBN_ERR_WORKSPACE", 6: "SBN_ERR_DTYPE", 7: "SBN_ERR_HIP"}
+
+
+class SbnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+_i64, _int, _sz, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+_SIGNATURES = {
+    "sbn_abi_version": ([], _int),
+    "sbn_status_string": ([_int], ctypes.c_char_p),
+    "sbn_last_error": ([], ctypes.c_char_p),
+    "sbn_packed_bytes": ([_i64, _i64, _int, _int, ctypes.POINTER(_sz), ctypes.POINTER(_sz)], _int),
+    "sbn_workspace_bytes": ([_int, _i64, _i64, _i64, _int, _int, ctypes.POINTER(_sz)], _int),
+    "sbn_mask_ternarize_pack": ([_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "sbn_act_quant": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], _int),
+    "sbn_sparse_ternary_gemm": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _int, _int, _vp, _int, _i64,
+                                 _vp, _sz, _vp], _int),
+    "sbn_sparse_ternary_gemv": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _int, _int, _vp, _int, _i64,
+                                 _vp, _sz, _vp], _int),
+    "sbn_backward": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _int, _int, _vp, _int, _vp, _vp,
+                      _sz, _vp], _int),
+}
+
+
+def header_symbols() -> list[str]:
+    """Names of the functions declared in include/sbn.h."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"^\s*(?:sbn_status|int|const char\*)\s+(sbn_\w+)\s*\(", text, re.M)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libsbn.so (loaded once, signatures set)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise SbnError("load", 7, f"{LIB_PATH} is not built; run __graft_entry__.build()")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in _SIGNATURES.items():
+                f = getattr(L, name)
+                f.argtypes, f.restype = args, res
+            _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise SbnError(fn, status, lib().sbn_last_error().decode())
+
+
+# ------------------------------------------------------------------ host-only queries
+def sbn_abi_version() -> int:
+    return lib().sbn_abi_version()
+
+
+def sbn_packed_bytes(R: int, K: int, n: int, m: int) -> tuple[int, int]:
+    c, mt = _sz(), _sz()
+    _check("sbn_packed_bytes", lib().sbn_packed_bytes(R, K, n, m, ctypes.byref(c), ctypes.byref(mt)))
+    return c.value, mt.value
+
+
+def sbn_workspace_bytes(op: int, T: int, R: int, K: int, n: int, m: int) -> int:
+    b = _sz()
+    _check("sbn_workspace_bytes", lib().sbn_workspace_bytes(op, T, R, K, n, m, ctypes.byref(b)))
+    return b.value
+
+
+# ------------------------------------------------------------------ device calls
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Workspace:
+    """Grow-only device byte buffer for one operation.  ``zeroed`` buffers are
+    created with zeros (the pack workspace header must start at zero; every
+    pack call leaves it zeroed again)."""
+
+    def __init__(self, zeroed: bool = False):
+        self.buf = None
+        self.zeroed = zeroed
+
+    def get(self, nbytes: int, device):
+        torch = _torch()
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            alloc = torch.zeros if self.zeroed else torch.empty
+            self.buf = alloc(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_WS = {"pack": Workspace(zeroed=True), "gemm": Workspace(), "bwd": Workspace()}
+
+
+def sbn_mask_ternarize_pack(W, n: int, m: int, *, codes=None, meta=None, s_w=None, ws=None, stream=None):
+    """Mask, ternarize and pack bf16 master weights W [R, K].  Returns (codes, meta, s_w)."""
+    torch = _torch()
+    R, K = W.shape
+    cb, mb = sbn_packed_bytes(R, K, n, m)
+    dev = W.device
+    if codes is None:
+        codes = torch.empty(cb, dtype=torch.uint8, device=dev)
+    if meta is None and mb:
+        meta = torch.empty(mb, dtype=torch.uint8, device=dev)
+    if s_w is None:
+        s_w = torch.empty(1, dtype=torch.float32, device=dev)
+    need = sbn_workspace_bytes(SBN_OP_PACK, 0, R, K, n, m)
+    if ws is None:
+        ws = _WS["pack"].get(need, dev)
+    _check("sbn_mask_ternarize_pack",
+           lib().sbn_mask_ternarize_pack(_ptr(W), R, K, W.stride(0), n, m, _ptr(codes), _ptr(meta),
+                                         _ptr(s_w), _ptr(ws), ws.numel() if ws is not None else 0,
+                                         _stream(stream)))
+    return codes, meta, s_w
+
+
+def sbn_act_quant(X, *, Xq=None, s_x=None, stream=None):
+    """Per-token absmax int8 quantization of bf16 X [T, K].  Returns (Xq, s_x)."""
+    torch = _torch()
+    T, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((T, K), dtype=torch.int8, device=X.device)
+    if s_x is None:
+        s_x = torch.empty(T, dtype=torch.float32, device=X.device)
+    _check("sbn_act_quant",
+           lib().sbn_act_quant(_ptr(X), T, K, X.stride(0), _ptr(Xq), _ptr(s_x), _stream(stream)))
+    return Xq, s_x
+
+
+_YT = {SBN_F32: "float32", SBN_BF16: "bfloat16", SBN_I32_ACC: "int32"}
+
+
+def _matmul(name: str, Xq, s_x, codes, meta, s_w, R: int, n: int, m: int, ydt: int, Y, ws, stream):
+    torch = _torch()
+    T, K = Xq.shape
+    if Y is None:
+        Y = torch.empty((T, R), dtype=getattr(torch, _YT[ydt]), device=Xq.device)
+    op = SBN_OP_GEMM if name == "sbn_sparse_ternary_gemm" else SBN_OP_GEMV
+    need = sbn_workspace_bytes(op, T, R, K, n, m)
+    if ws is None:
+        ws = _WS["gemm"].get(need, Xq.device)
+    fn = getattr(lib(), name)
+    _check(name, fn(_ptr(Xq), _ptr(s_x), T, K, _ptr(codes), _ptr(meta), _ptr(s_w), R, n, m, _ptr(Y), ydt,
+                    Y.stride(0), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+    return Y
+
+
+def sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, R: int, n: int, m: int, *, ydt: int = SBN_BF16,
+                            Y=None, ws=None, stream=None):
+    """Y [T, R] = s_w * s_x[t] * (Xq @ Wt^T) from the packed weight."""
+    return _matmul("sbn_sparse_ternary_gemm", Xq, s_x, codes, meta, s_w, R, n, m, ydt, Y, ws, stream)
+
+
+def sbn_sparse_ternary_gemv(Xq, s_x, codes, meta, s_w, R: int, n: int, m: int, *, ydt: int = SBN_BF16,
+                            Y=None, ws=None, stream=None):
+    """Decode form (T <= 16) of sbn_sparse_ternary_gemm."""
+    return _matmul("sbn_sparse_ternary_gemv", Xq, s_x, codes, meta, s_w, R, n, m, ydt, Y, ws, stream)
+
+
+def sbn_backward(dY, Xq, s_x, codes, meta, s_w, n: int, m: int, *, dxdt: int = SBN_F32, want_dX: bool = True,
+                 want_dW: bool = True, dX=None, dW=None, ws=None, stream=None):
+    """Dual-STE backward.  Returns (dX [T, K] or None, dW [R, K] float32 or None)."""
+    torch = _torch()
+    T, R = dY.shape
+    K = Xq.shape[1]
+    if want_dX and dX is None:
+        dX = torch.empty((T, K), dtype=torch.float32 if dxdt == SBN_F32 else torch.bfloat16, device=dY.device)
+    if want_dW and dW is None:
+        dW = torch.empty((R, K), dtype=torch.float32, device=dY.device)
+    need = sbn_workspace_bytes(SBN_OP_BACKWARD, T, R, K, n, m)
+    if ws is None:
+        ws = _WS["bwd"].get(need, dY.device)
+    _check("sbn_backward",
+           lib().sbn_backward(_ptr(dY), T, R, _ptr(Xq), _ptr(s_x), K, _ptr(codes), _ptr(meta), _ptr(s_w), n, m,
+                              _ptr(dX if want_dX else None), dxdt, _ptr(dW if want_dW else None), _ptr(ws),
+                              ws.numel() if ws is not None else 0, _stream(stream)))
+    return (dX if want_dX else None), (dW if want_dW else None)
+
+
+__all__ = [
+    "lib", "header_symbols", "SbnError", "sbn_abi_version", "sbn_packed_bytes", "sbn_workspace_bytes",
+    "sbn_mask_ternarize_pack", "sbn_act_quant", "sbn_sparse_ternary_gemm", "sbn_sparse_ternary_gemv",
+    "sbn_backward", "SBN_F32", "SBN_BF16", "SBN_I32_ACC", "SBN_OP_PACK", "SBN_OP_ACT_QUANT", "SBN_OP_GEMM",
+    "SBN_OP_GEMV", "SBN_OP_BACKWARD",
+]

@@ -1,0 +1,298 @@
+// Host side of the C ABI declared in include/sbn.h: argument validation,
+// workspace sizing, dispatch to the HIP launchers and error reporting.
+// Validation runs entirely on the host before any HIP call, so a rejected
+// call launches nothing and touches no output.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "sbn_internal.h"
+
+using namespace sbn;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+sbn_status fail(sbn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+sbn_status ok() {
+  g_last_error[0] = '\0';
+  return SBN_OK;
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("SBN_DEBUG_SYNC");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+sbn_status hip_result(hipError_t e, hipStream_t st, const char* what) {
+  if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(SBN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int64_t K_MAX = int64_t(1) << 18;
+constexpr int64_t NUMEL_MAX = int64_t(1) << 37;
+
+sbn_status check_nm(int n, int m) {
+  if (!(m == 4 || m == 8) || n < 1 || n > m)
+    return fail(SBN_ERR_UNSUPPORTED_NM, "unsupported N:M ratio %d:%d (m in {4,8}, 1 <= n <= m)", n, m);
+  return SBN_OK;
+}
+
+sbn_status check_k(int64_t K) {
+  if (K < 64 || K % 64 != 0 || K > K_MAX)
+    return fail(SBN_ERR_SHAPE, "K = %lld must be a positive multiple of 64 and <= 2^18", (long long)K);
+  return SBN_OK;
+}
+
+sbn_status check_rows(const char* name, int64_t v) {
+  if (v < 1) return fail(SBN_ERR_SHAPE, "%s = %lld must be >= 1", name, (long long)v);
+  return SBN_OK;
+}
+
+sbn_status check_ld(const char* name, int64_t ld, int64_t len) {
+  if (ld < len) return fail(SBN_ERR_SHAPE, "%s = %lld is smaller than the row length %lld", name, (long long)ld, (long long)len);
+  if (ld % 8 != 0) return fail(SBN_ERR_ALIGN, "%s = %lld is not a multiple of 8", name, (long long)ld);
+  return SBN_OK;
+}
+
+#define SBN_TRY(expr)                 \
+  do {                                \
+    const sbn_status s_ = (expr);     \
+    if (s_ != SBN_OK) return s_;      \
+  } while (0)
+
+#define SBN_NONNULL(p)                                                        \
+  do {                                                                        \
+    if (!(p)) return fail(SBN_ERR_NULL, "%s: argument '%s' is NULL", fn, #p); \
+  } while (0)
+
+#define SBN_ALIGNED(p)                                                                         \
+  do {                                                                                         \
+    if ((p) && !aligned16(p)) return fail(SBN_ERR_ALIGN, "%s: '%s' is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+size_t packed_codes(int64_t R, int64_t K, int n, int m) {
+  return (size_t)round_up(R * K * n / (4 * m), 16);
+}
+size_t packed_meta(int64_t R, int64_t K, int n, int m) {
+  return n == m ? 0 : (size_t)round_up(R * K / 8, 16);
+}
+
+sbn_status check_matmul_args(const char* fn, const int8_t* Xq, const float* s_x, int64_t T,
+                             int64_t K, const uint8_t* codes, const uint8_t* meta,
+                             const float* s_w, int64_t R, int n, int m, void* Y, sbn_dtype ydt,
+                             int64_t ldy) {
+  SBN_NONNULL(Xq);
+  SBN_NONNULL(s_x);
+  SBN_NONNULL(codes);
+  SBN_NONNULL(s_w);
+  SBN_NONNULL(Y);
+  SBN_TRY(check_nm(n, m));
+  if (n < m) SBN_NONNULL(meta);
+  SBN_TRY(check_rows("T", T));
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  SBN_TRY(check_ld("ldy", ldy, R));
+  if (ydt != SBN_F32 && ydt != SBN_BF16 && ydt != SBN_I32_ACC)
+    return fail(SBN_ERR_DTYPE, "%s: unknown output dtype %d", fn, (int)ydt);
+  SBN_ALIGNED(Xq);
+  SBN_ALIGNED(codes);
+  SBN_ALIGNED(meta);
+  SBN_ALIGNED(Y);
+  return SBN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sbn_abi_version(void) { return SBN_ABI_VERSION; }
+
+const char* sbn_status_string(sbn_status s) {
+  switch (s) {
+    case SBN_OK: return "ok";
+    case SBN_ERR_NULL: return "null pointer argument";
+    case SBN_ERR_SHAPE: return "invalid shape";
+    case SBN_ERR_UNSUPPORTED_NM: return "unsupported N:M ratio";
+    case SBN_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case SBN_ERR_WORKSPACE: return "workspace too small";
+    case SBN_ERR_DTYPE: return "unsupported dtype";
+    case SBN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* sbn_last_error(void) { return g_last_error; }
+
+sbn_status sbn_packed_bytes(int64_t R, int64_t K, int n, int m, size_t* codes_bytes,
+                            size_t* meta_bytes) {
+  const char* fn = "sbn_packed_bytes";
+  SBN_NONNULL(codes_bytes);
+  SBN_NONNULL(meta_bytes);
+  SBN_TRY(check_nm(n, m));
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  *codes_bytes = packed_codes(R, K, n, m);
+  *meta_bytes = packed_meta(R, K, n, m);
+  return ok();
+}
+
+sbn_status sbn_workspace_bytes(sbn_op op, int64_t T, int64_t R, int64_t K, int n, int m,
+                               size_t* bytes) {
+  const char* fn = "sbn_workspace_bytes";
+  SBN_NONNULL(bytes);
+  switch (op) {
+    case SBN_OP_ACT_QUANT:
+    case SBN_OP_GEMV:
+      *bytes = 0;
+      return ok();
+    case SBN_OP_PACK:
+      SBN_TRY(check_nm(n, m));
+      SBN_TRY(check_rows("R", R));
+      SBN_TRY(check_k(K));
+      *bytes = pack_plan(R, K).bytes;
+      return ok();
+    case SBN_OP_GEMM:
+      SBN_TRY(check_nm(n, m));
+      SBN_TRY(check_rows("T", T));
+      SBN_TRY(check_rows("R", R));
+      SBN_TRY(check_k(K));
+      *bytes = gemm_ws_bytes(T, R, K, n, m);
+      return ok();
+    case SBN_OP_BACKWARD:
+      SBN_TRY(check_nm(n, m));
+      SBN_TRY(check_rows("T", T));
+      SBN_TRY(check_rows("R", R));
+      SBN_TRY(check_k(K));
+      *bytes = bwd_ws_bytes(T, R, K, n, m);
+      return ok();
+  }
+  return fail(SBN_ERR_SHAPE, "%s: unknown op %d", fn, (int)op);
+}
+
+sbn_status sbn_mask_ternarize_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n,
+                                   int m, uint8_t* codes, uint8_t* meta, float* s_w, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  const char* fn = "sbn_mask_ternarize_pack";
+  SBN_NONNULL(W);
+  SBN_NONNULL(codes);
+  SBN_NONNULL(s_w);
+  SBN_NONNULL(ws);
+  SBN_TRY(check_nm(n, m));
+  if (n < m) SBN_NONNULL(meta);
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  SBN_TRY(check_ld("ldw", ldw, K));
+  SBN_ALIGNED(W);
+  SBN_ALIGNED(codes);
+  if (n < m) SBN_ALIGNED(meta);
+  SBN_ALIGNED(ws);
+  const size_t need = pack_plan(R, K).bytes;
+  if (ws_bytes < need)
+    return fail(SBN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_pack(W, R, K, ldw, n, m, codes, meta, s_w, ws, st), st, fn);
+}
+
+sbn_status sbn_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, int8_t* Xq,
+                         float* s_x, void* stream) {
+  const char* fn = "sbn_act_quant";
+  SBN_NONNULL(X);
+  SBN_NONNULL(Xq);
+  SBN_NONNULL(s_x);
+  SBN_TRY(check_rows("T", T));
+  SBN_TRY(check_k(K));
+  SBN_TRY(check_ld("ldx", ldx, K));
+  SBN_ALIGNED(X);
+  SBN_ALIGNED(Xq);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_act_quant(X, T, K, ldx, Xq, s_x, st), st, fn);
+}
+
+sbn_status sbn_sparse_ternary_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                   const uint8_t* codes, const uint8_t* meta, const float* s_w,
+                                   int64_t R, int n, int m, void* Y, sbn_dtype ydt, int64_t ldy,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "sbn_sparse_ternary_gemm";
+  SBN_TRY(check_matmul_args(fn, Xq, s_x, T, K, codes, meta, s_w, R, n, m, Y, ydt, ldy));
+  SBN_NONNULL(ws);
+  SBN_ALIGNED(ws);
+  const size_t need = gemm_ws_bytes(T, R, K, n, m);
+  if (ws_bytes < need)
+    return fail(SBN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_gemm(Xq, s_x, T, K, codes, n == m ? nullptr : meta, s_w, R, n, m, Y,
+                                ydt, ldy, ws, st),
+                    st, fn);
+}
+
+sbn_status sbn_sparse_ternary_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                   const uint8_t* codes, const uint8_t* meta, const float* s_w,
+                                   int64_t R, int n, int m, void* Y, sbn_dtype ydt, int64_t ldy,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "sbn_sparse_ternary_gemv";
+  (void)ws;
+  (void)ws_bytes;
+  SBN_TRY(check_matmul_args(fn, Xq, s_x, T, K, codes, meta, s_w, R, n, m, Y, ydt, ldy));
+  if (T > 16) return fail(SBN_ERR_SHAPE, "%s: T = %lld exceeds 16; use the GEMM", fn, (long long)T);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_gemv(Xq, s_x, T, K, codes, n == m ? nullptr : meta, s_w, R, n, m, Y,
+                                ydt, ldy, st),
+                    st, fn);
+}
+
+sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
+                        const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
+                        const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,
+                        void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "sbn_backward";
+  SBN_NONNULL(dY);
+  SBN_NONNULL(Xq);
+  SBN_NONNULL(s_x);
+  SBN_NONNULL(codes);
+  SBN_NONNULL(s_w);
+  SBN_NONNULL(ws);
+  SBN_TRY(check_nm(n, m));
+  if (n < m) SBN_NONNULL(meta);
+  SBN_TRY(check_rows("T", T));
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  if (R % 8 != 0) return fail(SBN_ERR_SHAPE, "%s: R = %lld must be a multiple of 8", fn, (long long)R);
+  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  if (dX && dxdt != SBN_F32 && dxdt != SBN_BF16)
+    return fail(SBN_ERR_DTYPE, "%s: dX dtype must be SBN_F32 or SBN_BF16", fn);
+  SBN_ALIGNED(dY);
+  SBN_ALIGNED(Xq);
+  SBN_ALIGNED(codes);
+  if (n < m) SBN_ALIGNED(meta);
+  SBN_ALIGNED(dX);
+  SBN_ALIGNED(dW);
+  SBN_ALIGNED(ws);
+  const size_t need = bwd_ws_bytes(T, R, K, n, m);
+  if (ws_bytes < need)
+    return fail(SBN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_backward(dY, T, R, Xq, s_x, K, codes, n == m ? nullptr : meta, s_w, n,
+                                    m, dX, dxdt, dW, ws, st),
+                    st, fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Internal declarations shared by the HIP translation units of libsbn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sbn.h"
+
+namespace sbn {
+
+// ----------------------------------------------------------------- vector types
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// ----------------------------------------------------------------- small helpers
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+__host__ __device__ inline size_t align256(size_t a) { return (a + 255) & ~size_t(255); }
+
+// float32 -> bf16 bits, round to nearest even (inputs here are finite)
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ inline float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Write-once global stores through the vector path.
+__device__ inline void store_u16x4(uint16_t* p, uint16_t a, uint16_t b, uint16_t c, uint16_t d) {
+  uint2 v;
+  v.x = (uint32_t)a | ((uint32_t)b << 16);
+  v.y = (uint32_t)c | ((uint32_t)d << 16);
+  *(uint2*)p = v;
+}
+
+// ----------------------------------------------------------------- direct-to-LDS loads
+// 16 bytes per lane from `g` into LDS at `lds_base + 16*lane` (wave-uniform base).
+__device__ inline void g2lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+// 4 bytes per lane into LDS at `lds_base + 4*lane`.
+__device__ inline void g2lds4(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+__device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ----------------------------------------------------------------- workspace layouts
+// Pack: [counter + pad: 256 B][bins: 256 x u64][partials: nblocks x i64]
+struct PackPlan {
+  int64_t nblocks;
+  int64_t rows_per_block;
+  size_t bytes;
+};
+PackPlan pack_plan(int64_t R, int64_t K);
+
+// Sparse (smfmac) expansion: values [RB][KB128][64][16 B] + idx [RB][KB128][64][4 B]
+// Dense expansion: [RB][KB64][64][16 B]; RB covers R rounded up to the GEMM row tile.
+constexpr int GEMM_TILE_R = 256;
+constexpr int GEMM_TILE_T = 256;
+bool gemm_uses_smfmac(int n, int m);
+size_t gemm_ws_bytes(int64_t T, int64_t R, int64_t K, int n, int m);
+size_t bwd_ws_bytes(int64_t T, int64_t R, int64_t K, int n, int m);
+
+// ----------------------------------------------------------------- launchers
+hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
+                       uint8_t* codes, uint8_t* meta, float* s_w, void* ws, hipStream_t st);
+hipError_t launch_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, int8_t* Xq,
+                            float* s_x, hipStream_t st);
+hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                       const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
+                       int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, void* ws, hipStream_t st);
+hipError_t launch_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                       const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
+                       int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, hipStream_t st);
+hipError_t launch_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
+                           const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
+                           const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,
+                           void* ws, hipStream_t st);
+
+}  // namespace sbn

@@ -1,0 +1,134 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, reports sizes, and rejects bad arguments on the host before
+any launch (fake, never-dereferenced device addresses are enough for that)."""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+import sparse_linear_layers_02_amd as sbn
+
+OK, NULL, SHAPE, NM, ALIGN, WS, DTYPE, HIP = range(8)
+P = ctypes.c_void_p(0x100000)          # 16-byte aligned fake device address (never touched)
+P2 = ctypes.c_void_p(0x200000)
+MIS = ctypes.c_void_p(0x100004)        # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    return sbn.lib()
+
+
+def test_exports_every_header_symbol(L):
+    names = sbn.header_symbols()
+    assert len(names) == 10
+    for nm in names:
+        assert hasattr(L, nm), nm
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.sbn_abi_version() == 1
+    for s in range(8):
+        assert L.sbn_status_string(s)
+    assert L.sbn_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("R,K,n,m", [(256, 256, 2, 4), (4096, 4096, 6, 8), (7, 64, 1, 4), (3, 192, 8, 8),
+                                     (11008, 4096, 6, 8)])
+def test_packed_bytes(R, K, n, m):
+    c, mt = sbn.sbn_packed_bytes(R, K, n, m)
+    rnd = lambda x: (x + 15) // 16 * 16
+    assert c == rnd(R * K * n // (4 * m))
+    assert mt == (0 if n == m else rnd(R * K // 8))
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 256, 2, 4), SHAPE), ((16, 100, 2, 4), SHAPE), ((16, 0, 2, 4), SHAPE),
+    ((16, 256, 0, 4), NM), ((16, 256, 5, 4), NM), ((16, 256, 2, 6), NM),
+    ((16, 1 << 19, 2, 4), SHAPE), ((1 << 20, 1 << 18, 2, 4), SHAPE),
+])
+def test_packed_bytes_errors(args, status):
+    with pytest.raises(sbn.SbnError) as e:
+        sbn.sbn_packed_bytes(*args)
+    assert e.value.status == status
+
+
+def test_workspace_sizes():
+    assert sbn.sbn_workspace_bytes(sbn.SBN_OP_ACT_QUANT, 16, 0, 256, 2, 4) == 0
+    assert sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMV, 16, 4096, 4096, 2, 4) == 0
+    assert sbn.sbn_workspace_bytes(sbn.SBN_OP_PACK, 0, 256, 256, 2, 4) >= 2304
+    g24 = sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM, 4096, 6912, 2560, 2, 4)
+    assert g24 >= 6912 * 2560 // 2 + 6912 * 2560 // 8      # compressed values + indices
+    g68 = sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM, 8192, 11008, 4096, 6, 8)
+    assert g68 >= 11008 * 4096                               # dense int8 operand
+    b = sbn.sbn_workspace_bytes(sbn.SBN_OP_BACKWARD, 8192, 11008, 4096, 6, 8)
+    assert b >= 2 * 11008 * 4096 + 2 * 4096 * 8192 + 4 * 11008 * 8192
+
+
+def test_pack_validation(L):
+    f = L.sbn_mask_ternarize_pack
+    big = 1 << 20
+    assert f(None, 16, 256, 256, 2, 4, P, P, P, P, big, None) == NULL
+    assert f(P, 16, 256, 256, 2, 4, P, None, P, P, big, None) == NULL        # meta needed for n < m
+    assert f(P, 16, 250, 256, 2, 4, P, P, P, P, big, None) == SHAPE
+    assert f(P, 16, 256, 128, 2, 4, P, P, P, P, big, None) == SHAPE          # ldw < K
+    assert f(P, 16, 256, 260, 2, 4, P, P, P, P, big, None) == ALIGN          # ldw % 8
+    assert f(MIS, 16, 256, 256, 2, 4, P, P, P, P, big, None) == ALIGN
+    assert f(P, 16, 256, 256, 3, 6, P, P, P, P, big, None) == NM
+    assert f(P, 16, 256, 256, 2, 4, P, P, P, P, 16, None) == WS
+    assert b"workspace" in L.sbn_last_error()
+
+
+def test_act_quant_validation(L):
+    f = L.sbn_act_quant
+    assert f(None, 4, 256, 256, P, P, None) == NULL
+    assert f(P, 0, 256, 256, P, P, None) == SHAPE
+    assert f(P, 4, 96, 96, P, P, None) == SHAPE
+    assert f(P, 4, 256, 255, P, P, None) == SHAPE
+    assert f(P, 4, 256, 256, MIS, P, None) == ALIGN
+
+
+@pytest.mark.parametrize("name", ["sbn_sparse_ternary_gemm", "sbn_sparse_ternary_gemv"])
+def test_matmul_validation(L, name):
+    f = getattr(L, name)
+    big = 1 << 30
+    args = dict(Xq=P, s_x=P, T=16, K=256, codes=P, meta=P, s_w=P, R=256, n=2, m=4, Y=P, ydt=1, ldy=256,
+                ws=P2, wsb=big)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["Xq"], a["s_x"], a["T"], a["K"], a["codes"], a["meta"], a["s_w"], a["R"], a["n"], a["m"],
+                 a["Y"], a["ydt"], a["ldy"], a["ws"], a["wsb"], None)
+
+    assert call(Xq=None) == NULL
+    assert call(meta=None) == NULL
+    assert call(T=0) == SHAPE
+    assert call(K=100) == SHAPE
+    assert call(ldy=200) == SHAPE
+    assert call(ldy=260) == ALIGN
+    assert call(Y=MIS) == ALIGN
+    assert call(n=9, m=8) == NM
+    assert call(ydt=7) == DTYPE
+    if name.endswith("gemm"):
+        assert call(wsb=8) == WS
+        assert call(ws=None) == NULL
+    else:
+        assert call(T=17) == SHAPE
+
+
+def test_backward_validation(L):
+    f = L.sbn_backward
+    big = 1 << 34
+
+    def call(dY=P, T=64, R=256, Xq=P, s_x=P, K=256, codes=P, meta=P, s_w=P, n=2, m=4, dX=P, dxdt=0, dW=P, ws=P2,
+             wsb=big):
+        return f(dY, T, R, Xq, s_x, K, codes, meta, s_w, n, m, dX, dxdt, dW, ws, wsb, None)
+
+    assert call(dY=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(R=100) == SHAPE          # R % 8
+    assert call(K=32) == SHAPE
+    assert call(dxdt=2) == DTYPE
+    assert call(dX=MIS) == ALIGN
+    assert call(wsb=64) == WS

@@ -1,0 +1,370 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU oracle.
+
+Bars (see gpu_util.py): meta, codes, s_w, Xq, s_x and int32 accumulators are
+compared bit for bit; float outputs within the stated tolerances.  Shapes
+span several tiles with ragged tails in every dimension, the full workload
+sizes (sampled where the oracle would be slow), all supported N:M ratios,
+and the degenerate cases (zero weights, zero tokens, ties, subnormals,
+magnitudes outside the fast summation window).
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle as O
+import sparse_linear_layers_02_amd as sbn
+from gpu_util import (BF16_REL, assert_abs_product, assert_rel, bf16_bits_to_f64, dev, dev_bf16,
+                      f32_bits, host)
+from workloads import WORKLOADS, f32_to_bf16_bits, gaussian_bf16, gaussian_bf16_with_outliers
+
+pytestmark = pytest.mark.gpu
+
+ALL_NM = [(1, 4), (2, 4), (3, 4), (4, 4), (1, 8), (2, 8), (3, 8), (4, 8), (5, 8), (6, 8), (7, 8), (8, 8)]
+
+
+def gpu_pack(W_bits, n, m, ldw=None):
+    import torch
+    R, K = W_bits.shape
+    if ldw is None:
+        Wd = dev_bf16(W_bits)
+    else:
+        pad = np.full((R, ldw), 0x7F00, dtype=np.uint16)      # huge finite filler beyond K
+        pad[:, :K] = W_bits
+        Wd = dev_bf16(pad)[:, :K]
+    codes, meta, s_w = sbn.sbn_mask_ternarize_pack(Wd, n, m)
+    torch.cuda.synchronize()
+    return codes, meta, s_w
+
+
+def check_pack(W_bits, n, m, ldw=None, ref=None):
+    R, K = W_bits.shape
+    codes, meta, s_w = gpu_pack(W_bits, n, m, ldw)
+    if ref is None:
+        eff, mask, sw = O.quant_then_mask(W_bits, n, m)
+        cp, mp = O.pack_sbn1(eff, mask, n, m)
+    else:
+        cp, mp, sw = ref
+    assert f32_bits(host(s_w))[0] == f32_bits(sw), f"s_w {host(s_w)[0]!r} != {sw!r}"
+    gc = host(codes)[: cp.size].reshape(cp.shape)
+    assert np.array_equal(gc, cp), f"codes differ at {np.argwhere(gc != cp)[:3].tolist()}"
+    if n < m:
+        gm = host(meta)[: mp.size].reshape(mp.shape)
+        assert np.array_equal(gm, mp), f"meta differ at {np.argwhere(gm != mp)[:3].tolist()}"
+    return codes, meta, s_w
+
+
+# ------------------------------------------------------------------ pack
+@pytest.mark.parametrize("n,m", ALL_NM)
+def test_pack_tiny_all_ratios(n, m):
+    W = WORKLOADS["tiny"].weights(seed=0)
+    check_pack(W, n, m)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (8, 8), (1, 4)])
+def test_pack_ragged_rows_and_leading_dim(n, m):
+    W = gaussian_bf16((37, 192), 0.02, seed=3, stream=0)
+    check_pack(W, n, m, ldw=200)
+
+
+def special_weights(R=64, K=512, seed=11):
+    rng = np.random.default_rng(seed)
+    vals = [0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x2F80, 0xAF80,   # zeros, subnormals, 2^-32
+            0x2F7F, 0x3C00, 0xBC00, 0x3C80, 0x4180, 0xC180, 0x4300, 0x7F7F,   # below 2^-32, ties, >= 16, max
+            0xFF7F, 0x3F80, 0xBF80, 0x3F81]
+    W = rng.choice(np.array(vals, dtype=np.uint16), size=(R, K))
+    G = gaussian_bf16((R, K), 0.02, seed=seed, stream=0)
+    take = rng.random((R, K)) < 0.5
+    return np.where(take, W, G).astype(np.uint16)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (3, 8), (4, 4)])
+def test_pack_special_values_ties_and_extremes(n, m):
+    check_pack(special_weights(), n, m)
+
+
+def test_pack_gaussian_with_rare_tiny_weights():
+    W = gaussian_bf16((128, 1024), 0.02, seed=5, stream=0)
+    W[3, 7] = 0x0001          # subnormal
+    W[9, 100] = 0x2000        # 2^-63
+    W[50, 512] = 0x4200       # 32
+    check_pack(W, 2, 4)
+
+
+def test_pack_all_zero_weight():
+    W = np.zeros((32, 128), dtype=np.uint16)
+    codes, meta, s_w = check_pack(W, 2, 4)
+    assert host(s_w)[0] == np.float32(1e-5)
+
+
+def test_pack_exact_scale_ties_round_to_even():
+    # one row of 64: the mean is a power-of-two fraction of the sum, so the sum
+    # 1 + 2^-24 lands exactly half-way between two floats (-> even, down) and
+    # 1 + 3*2^-24 half-way the other way (-> even, up)
+    for extra in ([0x3380], [0x3400, 0x3380]):
+        W = np.zeros((1, 64), dtype=np.uint16)
+        W[0, 0] = 0x3F80
+        W[0, 1:1 + len(extra)] = extra
+        check_pack(W, 2, 4)
+
+
+def test_pack_repeated_calls_reuse_workspace():
+    W1 = gaussian_bf16((96, 256), 0.02, seed=1, stream=0)
+    W2 = special_weights(48, 320, seed=2)
+    for W in (W1, W2, W1):
+        check_pack(W, 2, 4)
+
+
+@functools.lru_cache(maxsize=None)
+def full_ref(name, n, m):
+    W = WORKLOADS[name].weights(seed=0)
+    eff, mask, sw = O.quant_then_mask(W, n, m)
+    cp, mp = O.pack_sbn1(eff, mask, n, m)
+    return W, eff, cp, mp, sw
+
+
+@pytest.mark.parametrize("name,n,m", [("prefill", 2, 4), ("train", 6, 8), ("decode", 2, 4), ("decode", 6, 8)])
+def test_pack_full_size_bit_exact(name, n, m):
+    W, eff, cp, mp, sw = full_ref(name, n, m)
+    check_pack(W, n, m, ref=(cp, mp, sw))
+
+
+# ------------------------------------------------------------------ act quant
+def check_act_quant(X_bits, ldx=None):
+    import torch
+    T, K = X_bits.shape
+    if ldx is None:
+        Xd = dev_bf16(X_bits)
+    else:
+        pad = np.full((T, ldx), 0x7F00, dtype=np.uint16)
+        pad[:, :K] = X_bits
+        Xd = dev_bf16(pad)[:, :K]
+    Xq, s_x = sbn.sbn_act_quant(Xd)
+    torch.cuda.synchronize()
+    rq, rs = O.act_quant(X_bits)
+    gq = host(Xq)
+    assert np.array_equal(gq, rq), f"Xq differ at {np.argwhere(gq != rq)[:3].tolist()}"
+    assert np.array_equal(f32_bits(host(s_x)), f32_bits(rs))
+    return Xq, s_x
+
+
+@pytest.mark.parametrize("T,K", [(16, 256), (5, 64), (33, 2560), (7, 8192), (3, 16384)])
+def test_act_quant_shapes(T, K):
+    check_act_quant(gaussian_bf16((T, K), 1.0, seed=T, stream=1))
+
+
+def test_act_quant_outliers_and_leading_dim():
+    X = gaussian_bf16_with_outliers((40, 640), 1.0, 0, 1, 0.01, 20.0)
+    check_act_quant(X, ldx=648)
+
+
+def test_act_quant_half_ties_zero_and_tiny_rows():
+    rows = [
+        [127.0, 62.5, 2.5, -2.5, 0.5, 1.5, -62.5] + [0.0] * 57,
+        [2.375, 1.1875, -1.1875] + [0.25] * 61,
+        [3.0, 1.5, -1.5] + [1.0] * 61,
+        [0.0] * 64,
+        [1e-7, -3e-6, 2e-8] + [0.0] * 61,        # absmax below the 1e-5 floor
+    ]
+    X = f32_to_bf16_bits(np.array(rows, dtype=np.float32))
+    check_act_quant(X)
+
+
+def test_act_quant_all_near_half_values():
+    # every representable bf16 in [0.5, 1) against absmax 1: many near-half quotients
+    vals = np.arange(0x3F00, 0x3F80, dtype=np.uint16)
+    X = np.zeros((4, 192), dtype=np.uint16)
+    X[:, : vals.size] = vals
+    X[:, vals.size] = 0x3F80
+    X[1] ^= 0x8000
+    check_act_quant(X)
+
+
+@pytest.mark.parametrize("name", ["prefill", "train"])
+def test_act_quant_full_size(name):
+    check_act_quant(WORKLOADS[name].activations(seed=0))
+
+
+# ------------------------------------------------------------------ GEMM / GEMV
+def forward_case(T, R, K, n, m, seed=0):
+    W = gaussian_bf16((R, K), 0.02, seed=seed, stream=0)
+    X = gaussian_bf16((T, K), 1.0, seed=seed, stream=1)
+    f = O.forward(W, X, n, m)
+    codes, meta, s_w = check_pack(W, n, m, ref=(f["codes_plane"], f["meta_plane"], f["s_w"]))
+    Xq = dev(f["Xq"])
+    s_x = dev(f["s_x"])
+    return f, Xq, s_x, codes, meta, s_w
+
+
+def run_matmul(kind, Xq, s_x, codes, meta, s_w, R, n, m, ydt):
+    import torch
+    fn = sbn.sbn_sparse_ternary_gemm if kind == "gemm" else sbn.sbn_sparse_ternary_gemv
+    Y = fn(Xq, s_x, codes, meta, s_w, R, n, m, ydt=ydt)
+    torch.cuda.synchronize()
+    return host(Y)
+
+
+def check_outputs(kind, f, Xq, s_x, codes, meta, s_w, R, n, m):
+    acc = run_matmul(kind, Xq, s_x, codes, meta, s_w, R, n, m, sbn.SBN_I32_ACC)
+    assert np.array_equal(acc.astype(np.int64), f["acc"]), \
+        f"acc differ at {np.argwhere(acc != f['acc'])[:3].tolist()}"
+    y32 = run_matmul(kind, Xq, s_x, codes, meta, s_w, R, n, m, sbn.SBN_F32)
+    assert_rel(y32, f["y"], 1e-3, f"{kind} f32 Y")
+    yb = run_matmul(kind, Xq, s_x, codes, meta, s_w, R, n, m, sbn.SBN_BF16)
+    assert_rel(bf16_bits_to_f64(yb), f["y"], BF16_REL, f"{kind} bf16 Y")
+
+
+def test_gemm_tiny_workload_fp32_output():
+    wl = WORKLOADS["tiny"]
+    W, X = wl.weights(0), wl.activations(0)
+    f = O.forward(W, X, 2, 4)
+    codes, meta, s_w = check_pack(W, 2, 4, ref=(f["codes_plane"], f["meta_plane"], f["s_w"]))
+    check_outputs("gemm", f, dev(f["Xq"]), dev(f["s_x"]), codes, meta, s_w, 256, 2, 4)
+
+
+@pytest.mark.parametrize("n,m", ALL_NM)
+def test_gemm_ragged_all_ratios(n, m):
+    T, R, K = 300, 520, 576          # two token tiles, three row tiles, K not a multiple of 128
+    f, Xq, s_x, codes, meta, s_w = forward_case(T, R, K, n, m, seed=n + 10 * m)
+    check_outputs("gemm", f, Xq, s_x, codes, meta, s_w, R, n, m)
+
+
+@pytest.mark.parametrize("T,R,K", [(1, 16, 64), (17, 33, 128), (257, 257, 640)])
+def test_gemm_small_edges(T, R, K):
+    f, Xq, s_x, codes, meta, s_w = forward_case(T, R, K, 2, 4, seed=T)
+    check_outputs("gemm", f, Xq, s_x, codes, meta, s_w, R, 2, 4)
+
+
+def test_gemm_extreme_activations():
+    # Xq = +-127 everywhere on dense ternary +-1 weights: |acc| = 127*K at the limit of the range
+    T, R, K, n, m = 32, 64, 2048, 8, 8
+    W = f32_to_bf16_bits(np.where(np.random.default_rng(1).random((R, K)) < 0.5, 1.0, -1.0).astype(np.float32))
+    X = f32_to_bf16_bits(np.where(np.random.default_rng(2).random((T, K)) < 0.5, 3.0, -3.0).astype(np.float32))
+    f = O.forward(W, X, n, m)
+    codes, meta, s_w = check_pack(W, n, m, ref=(f["codes_plane"], f["meta_plane"], f["s_w"]))
+    check_outputs("gemm", f, dev(f["Xq"]), dev(f["s_x"]), codes, meta, s_w, R, n, m)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (1, 4), (8, 8), (3, 8)])
+@pytest.mark.parametrize("T", [1, 4, 16, 7])
+def test_gemv_ragged(n, m, T):
+    R, K = 600, 2560                 # K not a multiple of 1024: a short last range
+    f, Xq, s_x, codes, meta, s_w = forward_case(T, R, K, n, m, seed=T + n)
+    check_outputs("gemv", f, Xq, s_x, codes, meta, s_w, R, n, m)
+
+
+@pytest.mark.parametrize("n,m", ALL_NM)
+def test_gemv_all_ratios_short_k(n, m):
+    f, Xq, s_x, codes, meta, s_w = forward_case(3, 40, 576, n, m, seed=7 * n + m)
+    check_outputs("gemv", f, Xq, s_x, codes, meta, s_w, 40, n, m)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
+def test_gemv_decode_full_size(n, m):
+    wl = WORKLOADS["decode"]
+    W, eff, cp, mp, sw = full_ref("decode", n, m)
+    codes, meta, s_w = check_pack(W, n, m, ref=(cp, mp, sw))
+    for T in wl.Ts:
+        X = wl.activations(seed=0, T=T)
+        Xq_h, s_x_h = O.act_quant(X)
+        acc = O.accumulate(Xq_h, eff)
+        got = run_matmul("gemv", dev(Xq_h), dev(s_x_h), codes, meta, s_w, 4096, n, m, sbn.SBN_I32_ACC)
+        assert np.array_equal(got.astype(np.int64), acc)
+        yb = run_matmul("gemv", dev(Xq_h), dev(s_x_h), codes, meta, s_w, 4096, n, m, sbn.SBN_BF16)
+        assert_rel(bf16_bits_to_f64(yb), O.output(acc, sw, s_x_h), BF16_REL, "decode bf16 Y")
+
+
+def sampled_check(Xq_h, s_x_h, eff, sw, got_acc, got_bf16, nsamp=4096, seed=0):
+    rng = np.random.default_rng(seed)
+    T, R = got_acc.shape
+    ts = rng.integers(0, T, nsamp)
+    rs = rng.integers(0, R, nsamp)
+    ref = np.einsum("ik,ik->i", Xq_h[ts].astype(np.int64), eff[rs].astype(np.int64))
+    assert np.array_equal(got_acc[ts, rs].astype(np.int64), ref)
+    y = ref.astype(np.float64) * float(sw) * s_x_h[ts].astype(np.float64)
+    assert_rel(bf16_bits_to_f64(got_bf16[ts, rs]), y, BF16_REL, "sampled bf16 Y")
+    # every output: the bf16 result is the scaled int32 result
+    ysc = got_acc.astype(np.float64) * float(sw) * s_x_h.astype(np.float64)[:, None]
+    assert_rel(bf16_bits_to_f64(got_bf16), ysc, BF16_REL, "bf16 Y vs scaled acc")
+
+
+@pytest.mark.parametrize("name,n,m", [("prefill", 2, 4), ("sweep", 2, 4), ("sweep", 6, 8), ("sweep", 8, 8),
+                                      ("sweep", 4, 8), ("sweep", 2, 8), ("sweep", 1, 4)])
+def test_gemm_full_size_sampled(name, n, m):
+    wl = WORKLOADS[name]
+    W, eff, cp, mp, sw = full_ref(name, n, m)
+    codes, meta, s_w = check_pack(W, n, m, ref=(cp, mp, sw))
+    X = wl.activations(seed=0)
+    Xq_h, s_x_h = O.act_quant(X)
+    Xq, s_x = check_act_quant(X)
+    acc = run_matmul("gemm", Xq, s_x, codes, meta, s_w, wl.R, n, m, sbn.SBN_I32_ACC)
+    yb = run_matmul("gemm", Xq, s_x, codes, meta, s_w, wl.R, n, m, sbn.SBN_BF16)
+    sampled_check(Xq_h, s_x_h, eff, sw, acc, yb)
+
+
+def test_gemm_deterministic_and_matches_gemv():
+    f, Xq, s_x, codes, meta, s_w = forward_case(16, 512, 1024, 2, 4, seed=4)
+    a1 = run_matmul("gemm", Xq, s_x, codes, meta, s_w, 512, 2, 4, sbn.SBN_BF16)
+    a2 = run_matmul("gemm", Xq, s_x, codes, meta, s_w, 512, 2, 4, sbn.SBN_BF16)
+    g1 = run_matmul("gemv", Xq, s_x, codes, meta, s_w, 512, 2, 4, sbn.SBN_BF16)
+    assert np.array_equal(a1, a2) and np.array_equal(a1, g1)
+
+
+# ------------------------------------------------------------------ backward
+def check_backward(T, R, K, n, m, seed=0, dxdt=None):
+    import torch
+    W = gaussian_bf16((R, K), 0.02, seed=seed, stream=0)
+    X = gaussian_bf16((T, K), 1.0, seed=seed, stream=1)
+    dY = gaussian_bf16((T, R), 1e-2, seed=seed, stream=2)
+    f = O.forward(W, X, n, m)
+    codes, meta, s_w = check_pack(W, n, m, ref=(f["codes_plane"], f["meta_plane"], f["s_w"]))
+    dxdt = sbn.SBN_F32 if dxdt is None else dxdt
+    dX, dW = sbn.sbn_backward(dev_bf16(dY), dev(f["Xq"]), dev(f["s_x"]), codes, meta, s_w, n, m, dxdt=dxdt)
+    torch.cuda.synchronize()
+    gX, gW = O.backward(dY, f["Xq"], f["s_x"], f["codes"], f["s_w"])
+    dYf = np.abs(bf16_bits_to_f64(dY))
+    boundX = dYf @ (float(f["s_w"]) * np.abs(f["codes"].astype(np.float64)))
+    boundW = dYf.T @ (f["s_x"].astype(np.float64)[:, None] * np.abs(f["Xq"].astype(np.float64)))
+    hx = host(dX)
+    hx = bf16_bits_to_f64(hx) if dxdt == sbn.SBN_BF16 else hx
+    if dxdt == sbn.SBN_BF16:
+        assert_abs_product(hx, gX, boundX + np.abs(gX) * (2 ** -8 / 1e-3), "dX(bf16)")
+    else:
+        assert_abs_product(hx, gX, boundX, "dX")
+    assert_abs_product(host(dW), gW, boundW, "dW")
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (8, 8), (1, 4)])
+def test_backward_ragged(n, m):
+    check_backward(96, 264, 320, n, m, seed=n + m)
+
+
+def test_backward_multi_tile_and_bf16_dx():
+    check_backward(300, 520, 576, 2, 4, seed=3)
+    check_backward(40, 64, 128, 6, 8, seed=4, dxdt=sbn.SBN_BF16)
+
+
+def test_backward_train_size_sampled():
+    import torch
+    wl = WORKLOADS["train"]
+    n, m = wl.nm[0]
+    W, eff, cp, mp, sw = full_ref("train", n, m)
+    codes, meta, s_w = check_pack(W, n, m, ref=(cp, mp, sw))
+    X = wl.activations(seed=0)
+    dY = wl.upstream_grad(seed=0)
+    Xq_h, s_x_h = O.act_quant(X)
+    dX, dW = sbn.sbn_backward(dev_bf16(dY), dev(Xq_h), dev(s_x_h), codes, meta, s_w, n, m)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    dYf = bf16_bits_to_f64(dY)
+    ts = rng.choice(wl.T, 24, replace=False)
+    gX = dYf[ts] @ (float(sw) * eff.astype(np.float64))
+    bX = np.abs(dYf[ts]) @ (float(sw) * np.abs(eff.astype(np.float64)))
+    assert_abs_product(host(dX[torch.from_numpy(ts).cuda()]), gX, bX, "dX rows")
+    rs = rng.choice(wl.R, 24, replace=False)
+    Xh = s_x_h.astype(np.float64)[:, None] * Xq_h.astype(np.float64)
+    gW = dYf[:, rs].T @ Xh
+    bW = np.abs(dYf[:, rs]).T @ np.abs(Xh)
+    assert_abs_product(host(dW[torch.from_numpy(rs).cuda()]), gW, bW, "dW rows")
