@@ -1,0 +1,315 @@
+"""Throughput of the Sparse-BitLinear hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|train|sweep]
+
+A step is one pass of the hot path over one batch of synthetic input already
+resident in HBM:
+  prefill (default): mask/ternarize/pack W (per call), act_quant X, sparse
+                     ternary GEMM -> bf16 Y.  T=4096, R=6912, K=2560, 2:4,
+                     X with 1% outliers x20.
+  train:             the same plus the dual-STE backward (dX, dW).
+                     T=8192, R=11008, K=4096, 6:8, dY ~ N(0, 1e-2).
+  sweep:             GEMM alone for N:M in {2:4, 4:8, 6:8, 2:8, 1:4, 8:8},
+                     T=2048, R=K=8192 (one line per ratio is not the
+                     contract; the JSON line carries the list).
+`value` is dense-equivalent int8 TOPS of the whole step (2*T*R*K per
+forward product; the train step counts its three products).  One JSON line
+is printed.  The same line carries:
+  roofline      the dominant kernel's algorithmic ops (or bytes) per launch
+                over its average launch time, timed with HIP events that the
+                library records around each launch on its own stream,
+                against MI355X's published peak;
+  decode_gemv   the other half of the metric: GB/s of the decode GEMV
+                (R = K = 4096, T = 1, 2:4) over a pool of distinct packed
+                weights larger than the 256 MB Infinity Cache;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+Multi-GPU runs are not part of this build: --gpus above 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-ternary GEMM dense-equiv int8 TOPS & decode GEMV GB/s, % of MI355X roofline"
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 matrix peak (2:4 structured headline excluded)
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "train", "sweep"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the decode GEMV measurement")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 512 MiB device copy (scales the HBM byte counters)")
+    return ap.parse_args()
+
+
+def bf16_dev(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def kernel_avg_ms(prof, name):
+    cnt, ms = prof.get(name, (0, 0.0))
+    return (ms / cnt if cnt else float("nan")), cnt
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    the current kernel source (the summary records the source hash)."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)\s+source_sha256:\s*([0-9a-f]+)\s+source:\s*(\S+)", text)
+    if not m:
+        return None
+    src = os.path.join(ROOT, m.group(3))
+    if not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(2):
+        return None
+    return float(m.group(1))
+
+
+# ---------------------------------------------------------------------- steps
+def make_forward_step(wl, n, m, with_backward=False):
+    import torch
+    import sparse_linear_layers_02_amd as sbn
+    W = bf16_dev(wl.weights(0))
+    X = bf16_dev(wl.activations(0))
+    cb, mb = sbn.sbn_packed_bytes(wl.R, wl.K, n, m)
+    codes = torch.empty(cb, dtype=torch.uint8, device="cuda")
+    meta = torch.empty(max(mb, 16), dtype=torch.uint8, device="cuda")
+    s_w = torch.empty(1, dtype=torch.float32, device="cuda")
+    Xq = torch.empty((wl.T, wl.K), dtype=torch.int8, device="cuda")
+    s_x = torch.empty(wl.T, dtype=torch.float32, device="cuda")
+    Y = torch.empty((wl.T, wl.R), dtype=torch.bfloat16, device="cuda")
+    ws_pack = torch.zeros(sbn.sbn_workspace_bytes(sbn.SBN_OP_PACK, 0, wl.R, wl.K, n, m), dtype=torch.uint8,
+                          device="cuda")
+    ws_gemm = torch.empty(max(sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM, wl.T, wl.R, wl.K, n, m), 256),
+                          dtype=torch.uint8, device="cuda")
+    extra = {}
+    if with_backward:
+        dY = bf16_dev(wl.upstream_grad(0))
+        dX = torch.empty((wl.T, wl.K), dtype=torch.bfloat16, device="cuda")
+        dW = torch.empty((wl.R, wl.K), dtype=torch.float32, device="cuda")
+        ws_bwd = torch.empty(sbn.sbn_workspace_bytes(sbn.SBN_OP_BACKWARD, wl.T, wl.R, wl.K, n, m),
+                             dtype=torch.uint8, device="cuda")
+        extra = dict(dY=dY, dX=dX, dW=dW, ws_bwd=ws_bwd)
+
+    def step():
+        sbn.sbn_mask_ternarize_pack(W, n, m, codes=codes, meta=meta if mb else None, s_w=s_w, ws=ws_pack)
+        sbn.sbn_act_quant(X, Xq=Xq, s_x=s_x)
+        sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta if mb else None, s_w, wl.R, n, m, ydt=sbn.SBN_BF16, Y=Y,
+                                    ws=ws_gemm)
+        if with_backward:
+            sbn.sbn_backward(extra["dY"], Xq, s_x, codes, meta if mb else None, s_w, n, m, dxdt=sbn.SBN_BF16,
+                             dX=extra["dX"], dW=extra["dW"], ws=extra["ws_bwd"])
+
+    return step
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    import sparse_linear_layers_02_amd as sbn
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    sbn.sbn_profile_reset()
+    sbn.sbn_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()                     # barrier (one rank) + sync on both sides
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sbn.sbn_profile_enable(False)
+    prof = sbn.sbn_profile_dump()
+    return e0.elapsed_time(e1) / steps, wall, prof
+
+
+# ---------------------------------------------------------------------- decode GEMV
+def decode_gemv(n=2, m=4, T=1, reps=3):
+    """Steady-state GEMV over a pool of distinct packed weights bigger than the
+    Infinity Cache, launched back to back on one stream; plus one cold call."""
+    import torch
+    import sparse_linear_layers_02_amd as sbn
+    from workloads import WORKLOADS
+    wl = WORKLOADS["decode"]
+    W = bf16_dev(wl.weights(0))
+    codes0, meta0, s_w = sbn.sbn_mask_ternarize_pack(W, n, m)
+    cb, mb = sbn.sbn_packed_bytes(wl.R, wl.K, n, m)
+    per = cb + mb
+    P = MALL_BYTES * 3 // 2 // per + 1          # pool 1.5x the Infinity Cache
+    codes = [codes0.clone() for _ in range(P)]
+    metas = [meta0.clone() for _ in range(P)]
+    Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0, T=T)))
+    Y = torch.empty((T, wl.R), dtype=torch.bfloat16, device="cuda")
+    algo = per + T * wl.K + 4 * T + 2 * T * wl.R + 4       # packed W + Xq + s_x + Y + s_w
+    for i in range(P):
+        sbn.sbn_sparse_ternary_gemv(Xq, s_x, codes[i], metas[i], s_w, wl.R, n, m, Y=Y)
+    torch.cuda.synchronize()
+    sbn.sbn_profile_reset()
+    sbn.sbn_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for i in range(P):
+            sbn.sbn_sparse_ternary_gemv(Xq, s_x, codes[i], metas[i], s_w, wl.R, n, m, Y=Y)
+    e1.record()
+    torch.cuda.synchronize()
+    sbn.sbn_profile_enable(False)
+    prof = sbn.sbn_profile_dump()
+    per_call_ms = e0.elapsed_time(e1) / (reps * P)
+    kern_ms, _ = kernel_avg_ms(prof, "gemv")
+    return {
+        "workload": f"decode R=K=4096 T={T} {n}:{m}", "pool_MiB": round(P * per / 2 ** 20, 1),
+        "algo_bytes_per_call": algo,
+        "kernel_us": round(kern_ms * 1e3, 3), "kernel_GBps": round(algo / (kern_ms * 1e-3) / 1e9, 1),
+        "stream_us_per_call": round(per_call_ms * 1e3, 3),
+        "stream_GBps": round(algo / (per_call_ms * 1e-3) / 1e9, 1),
+        "frac_hbm_kernel": round(algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+
+
+# ---------------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, n, m, tokens):
+    """The oracle as it stands, on the host: pack the full W, quantize `tokens`
+    tokens, accumulate them against every row.  TOPS = 2*tokens*R*K / time."""
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    W = wl.weights(0)
+    X = wl.activations(0)[:tokens]
+    t0 = time.perf_counter()
+    eff, mask, sw = O.quant_then_mask(W, n, m)
+    O.pack_sbn1(eff, mask, n, m)
+    Xq, s_x = O.act_quant(X)
+    acc = O.accumulate(Xq, eff)
+    O.output(acc, sw, s_x)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(2 * tokens * wl.R * wl.K / dt / 1e12, 6), "unit": "TOPS", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"full W pack ({wl.R}x{wl.K}, {n}:{m}) + {tokens} of {wl.T} tokens through "
+                      f"act_quant and the float64 matmul; ops = 2*{tokens}*R*K"}
+
+
+# ---------------------------------------------------------------------- main
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported in this build "
+              f"(multi-GPU sharding is described in DESIGN.md, not run).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_linear_layers_02_amd as sbn
+    from workloads import WORKLOADS
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    sbn.lib()
+
+    if a.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic"}
+
+    if a.workload in ("prefill", "train"):
+        wl = WORKLOADS[a.workload]
+        n, m = wl.nm[0]
+        step = make_forward_step(wl, n, m, with_backward=(a.workload == "train"))
+        ms, wall, prof = time_steps(step, a.steps, a.warmup)
+        nprod = 3 if a.workload == "train" else 1
+        ops = 2 * wl.T * wl.R * wl.K * nprod
+        out.update(value=round(ops / (ms * 1e-3) / 1e12, 3), unit="TOPS", ms_per_step=round(ms, 4),
+                   wall_s=round(wall, 4))
+        out["config"] = {"workload": a.workload, "T": wl.T, "R": wl.R, "K": wl.K, "nm": f"{n}:{m}",
+                         "step": "pack+act_quant+gemm" + ("+backward" if nprod == 3 else ""),
+                         "y_dtype": "bf16", "seed": 0}
+        gname = "gemm_smfmac" if (n <= 2) else "gemm_mfma"
+        g_ms, g_cnt = kernel_avg_ms(prof, gname)
+        g_ach = 2 * wl.T * wl.R * wl.K / (g_ms * 1e-3) / 1e12
+        traffic = traffic_from_profiles(gname, a.workload)
+        out["roofline"] = {"kernel": gname, "bound": "mfma", "achieved": round(g_ach, 2), "peak": PEAK_INT8_TOPS,
+                           "unit": "TFLOP/s", "frac": round(g_ach / PEAK_INT8_TOPS, 4), "traffic": traffic,
+                           "kernel_us": round(g_ms * 1e3, 3), "launches": g_cnt,
+                           "ops_per_launch": 2 * wl.T * wl.R * wl.K,
+                           "note": "int8 multiply-adds count 2 ops; dense-equivalent (pruned positions "
+                                   "counted); peak is the dense int8 matrix peak"}
+        out["stages_us"] = {k: round(v[1] / v[0] * 1e3, 3) for k, v in sorted(prof.items()) if v[0]}
+        if a.workload == "train":
+            for nm_, kname in (("dx", "gemm_dx"), ("dw", "gemm_dw")):
+                k_ms, _ = kernel_avg_ms(prof, kname)
+                fl = 2 * wl.T * wl.R * wl.K * (2 if kname == "gemm_dw" else 1)
+                out["roofline_" + nm_] = {"kernel": kname, "bound": "mfma", "achieved": round(fl / (k_ms * 1e-3) / 1e12, 2),
+                                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                          "frac": round(fl / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                          "note": "bf16 products executed (dW runs hi and lo halves)"}
+    else:
+        wl = WORKLOADS["sweep"]
+        rows = []
+        tot_ms = 0.0
+        for (n, m) in wl.nm:
+            W = bf16_dev(wl.weights(0))
+            codes, meta, s_w = sbn.sbn_mask_ternarize_pack(W, n, m)
+            Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0)))
+            Y = torch.empty((wl.T, wl.R), dtype=torch.bfloat16, device="cuda")
+            ms, wall, prof = time_steps(lambda: sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, wl.R, n, m, Y=Y),
+                                        a.steps, a.warmup)
+            gname = "gemm_smfmac" if sbn_uses_smfmac(n, m) else "gemm_mfma"
+            g_ms, _ = kernel_avg_ms(prof, gname)
+            ops = 2 * wl.T * wl.R * wl.K
+            rows.append({"nm": f"{n}:{m}", "call_us": round(ms * 1e3, 2), "kernel_us": round(g_ms * 1e3, 2),
+                         "TOPS_call": round(ops / (ms * 1e-3) / 1e12, 1),
+                         "TOPS_kernel": round(ops / (g_ms * 1e-3) / 1e12, 1), "kernel": gname})
+            tot_ms += ms
+            del W, codes, meta
+        ops = 2 * wl.T * wl.R * wl.K * len(rows)
+        out.update(value=round(ops / (tot_ms * 1e-3) / 1e12, 3), unit="TOPS", ms_per_step=round(tot_ms, 4))
+        out["config"] = {"workload": "sweep", "T": wl.T, "R": wl.R, "K": wl.K, "step": "gemm for each N:M"}
+        out["sweep"] = rows
+        best = min(rows, key=lambda r: r["kernel_us"])
+        out["roofline"] = {"kernel": best["kernel"], "bound": "mfma", "achieved": best["TOPS_kernel"],
+                           "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                           "frac": round(best["TOPS_kernel"] / PEAK_INT8_TOPS, 4), "traffic": None}
+
+    if not a.no_extras:
+        out["decode_gemv"] = decode_gemv()
+
+    if not a.no_cpu_baseline:
+        wl = WORKLOADS["prefill" if a.workload == "sweep" else a.workload]
+        n, m = wl.nm[0]
+        out["cpu_baseline"] = cpu_baseline(wl, n, m, tokens=min(wl.T, 4096 if a.workload == "prefill" else 512))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def sbn_uses_smfmac(n, m):
+    return n <= 2
+
+
+if __name__ == "__main__":
+    main()

@@ -205,6 +205,20 @@ sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* 
                         const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,
                         void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Kernel timing (diagnostics; not part of the operator).  While enabled,
+ * every kernel the library launches is bracketed by two HIP events recorded
+ * on the stream it runs on.  sbn_profile_dump waits for the recorded events
+ * and writes one line per kernel name, "name launches total_ms\n", into buf
+ * (NUL-terminated, truncated to buf_bytes); sbn_profile_reset forgets them.
+ * Kernel names: abs_sum, mask_pack, act_quant, expand_sparse, expand_dense,
+ * gemm_smfmac, gemm_mfma, gemv, expand_wt, prep_u, prep_xq, gemm_dx, gemm_dw.
+ * Errors: SBN_ERR_NULL (buf), SBN_ERR_HIP.
+ */
+sbn_status sbn_profile_enable(int on);
+sbn_status sbn_profile_reset(void);
+sbn_status sbn_profile_dump(char* buf, size_t buf_bytes);
+
 #ifdef __cplusplus
 }
 #endif

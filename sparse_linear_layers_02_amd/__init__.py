@@ -53,6 +53,9 @@ _SIGNATURES = {
                                  _vp, _sz, _vp], _int),
     "sbn_backward": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _int, _int, _vp, _int, _vp, _vp,
                       _sz, _vp], _int),
+    "sbn_profile_enable": ([_int], _int),
+    "sbn_profile_reset": ([], _int),
+    "sbn_profile_dump": ([ctypes.c_char_p, _sz], _int),
 }
 
 
@@ -222,9 +225,30 @@ def sbn_backward(dY, Xq, s_x, codes, meta, s_w, n: int, m: int, *, dxdt: int = S
     return (dX if want_dX else None), (dW if want_dW else None)
 
 
+# ------------------------------------------------------------------ kernel timing
+def sbn_profile_enable(on: bool = True) -> None:
+    """Bracket every library kernel launch with HIP events on its stream."""
+    _check("sbn_profile_enable", lib().sbn_profile_enable(1 if on else 0))
+
+
+def sbn_profile_reset() -> None:
+    _check("sbn_profile_reset", lib().sbn_profile_reset())
+
+
+def sbn_profile_dump() -> dict:
+    """{kernel name: (launches, total milliseconds)} since the last reset."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    _check("sbn_profile_dump", lib().sbn_profile_dump(buf, len(buf)))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out
+
+
 __all__ = [
     "lib", "header_symbols", "SbnError", "sbn_abi_version", "sbn_packed_bytes", "sbn_workspace_bytes",
     "sbn_mask_ternarize_pack", "sbn_act_quant", "sbn_sparse_ternary_gemm", "sbn_sparse_ternary_gemv",
     "sbn_backward", "SBN_F32", "SBN_BF16", "SBN_I32_ACC", "SBN_OP_PACK", "SBN_OP_ACT_QUANT", "SBN_OP_GEMM",
-    "SBN_OP_GEMV", "SBN_OP_BACKWARD",
+    "SBN_OP_GEMV", "SBN_OP_BACKWARD", "sbn_profile_enable", "sbn_profile_reset", "sbn_profile_dump",
 ]

@@ -118,13 +118,13 @@ hipError_t launch_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx
   const int64_t kc = K / 8;
   const dim3 grid((unsigned)T), block(AT);
   if (kc <= AT)
-    hipLaunchKernelGGL(act_quant_kernel<1>, grid, block, 0, st, X, K, ldx, Xq, s_x);
+    SBN_LAUNCH("act_quant", act_quant_kernel<1>, grid, block, 0, st, X, K, ldx, Xq, s_x);
   else if (kc <= 2 * AT)
-    hipLaunchKernelGGL(act_quant_kernel<2>, grid, block, 0, st, X, K, ldx, Xq, s_x);
+    SBN_LAUNCH("act_quant", act_quant_kernel<2>, grid, block, 0, st, X, K, ldx, Xq, s_x);
   else if (kc <= 4 * AT)
-    hipLaunchKernelGGL(act_quant_kernel<4>, grid, block, 0, st, X, K, ldx, Xq, s_x);
+    SBN_LAUNCH("act_quant", act_quant_kernel<4>, grid, block, 0, st, X, K, ldx, Xq, s_x);
   else
-    hipLaunchKernelGGL(act_quant_kernel<0>, grid, block, 0, st, X, K, ldx, Xq, s_x);
+    SBN_LAUNCH("act_quant", act_quant_kernel<0>, grid, block, 0, st, X, K, ldx, Xq, s_x);
   return hipGetLastError();
 }
 

@@ -2,10 +2,15 @@
 // workspace sizing, dispatch to the HIP launchers and error reporting.
 // Validation runs entirely on the host before any HIP call, so a rejected
 // call launches nothing and touches no output.
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
 
 #include "sbn_internal.h"
 
@@ -118,9 +123,108 @@ sbn_status check_matmul_args(const char* fn, const int8_t* Xq, const float* s_x,
   return SBN_OK;
 }
 
+// ---------------------------------------------------------------- kernel timing
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::atomic<int> g_prof_on{0};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+std::map<std::string, std::pair<long long, double>> g_prof_totals;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// drain recorded events into the totals (caller holds the lock)
+hipError_t prof_collect() {
+  hipError_t err = hipSuccess;
+  for (ProfRec& r : g_prof_recs) {
+    if (r.stop) {
+      hipError_t e = hipEventSynchronize(r.stop);
+      float ms = 0.f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+      if (e != hipSuccess) err = e;
+      auto& t = g_prof_totals[r.name];
+      t.first += 1;
+      t.second += ms;
+      g_prof_pool.push_back(r.stop);
+    }
+    if (r.start) g_prof_pool.push_back(r.start);
+  }
+  g_prof_recs.clear();
+  return err;
+}
+
 }  // namespace
 
+namespace sbn {
+
+int prof_begin(hipStream_t st, const char* name) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return -1;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec r{name, prof_event(), nullptr};
+  if (!r.start) return -1;
+  hipEventRecord(r.start, st);
+  g_prof_recs.push_back(r);
+  return (int)g_prof_recs.size() - 1;
+}
+
+void prof_end(int slot, hipStream_t st) {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (slot >= (int)g_prof_recs.size()) return;
+  hipEvent_t e = prof_event();
+  if (!e) return;
+  hipEventRecord(e, st);
+  g_prof_recs[slot].stop = e;
+}
+
+}  // namespace sbn
+
 extern "C" {
+
+sbn_status sbn_profile_enable(int on) {
+  g_prof_on.store(on ? 1 : 0);
+  return ok();
+}
+
+sbn_status sbn_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipError_t e = prof_collect();
+  g_prof_totals.clear();
+  if (e != hipSuccess) return fail(SBN_ERR_HIP, "sbn_profile_reset: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sbn_status sbn_profile_dump(char* buf, size_t buf_bytes) {
+  const char* fn = "sbn_profile_dump";
+  SBN_NONNULL(buf);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  hipError_t e = prof_collect();
+  std::string out;
+  for (auto& kv : g_prof_totals) {
+    char line[160];
+    snprintf(line, sizeof(line), "%s %lld %.6f\n", kv.first.c_str(), kv.second.first, kv.second.second);
+    out += line;
+  }
+  if (buf_bytes) {
+    const size_t nb = out.size() < buf_bytes - 1 ? out.size() : buf_bytes - 1;
+    memcpy(buf, out.data(), nb);
+    buf[nb] = '\0';
+  }
+  if (e != hipSuccess) return fail(SBN_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
 
 int sbn_abi_version(void) { return SBN_ABI_VERSION; }
 

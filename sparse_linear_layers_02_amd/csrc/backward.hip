@@ -273,29 +273,29 @@ hipError_t launch_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_
   hipError_t e;
   if (dX) {
     const int64_t thr = L.KB16 * L.RB32 * 64;
-    hipLaunchKernelGGL(expand_wt_kernel, dim3((unsigned)cdiv(thr, 256)), dim3(256), 0, st, codes,
+    SBN_LAUNCH("expand_wt", expand_wt_kernel, dim3((unsigned)cdiv(thr, 256)), dim3(256), 0, st, codes,
                        (n == m) ? nullptr : meta, R, K, n, m, L.KB16, L.RB32, (uint4*)(w + L.wt));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 grid((unsigned)cdiv(T, 256), (unsigned)cdiv(K, 256));
     if (dxdt == SBN_F32)
-      hipLaunchKernelGGL((bf16_gemm_kernel<0, 1>), grid, dim3(256), 0, st, w + L.wt, nullptr, nullptr,
+      SBN_LAUNCH("gemm_dx", (bf16_gemm_kernel<0, 1>), grid, dim3(256), 0, st, w + L.wt, nullptr, nullptr,
                          dY, T, K, L.RB32, R, s_w, dX, K);
     else
-      hipLaunchKernelGGL((bf16_gemm_kernel<0, 2>), grid, dim3(256), 0, st, w + L.wt, nullptr, nullptr,
+      SBN_LAUNCH("gemm_dx", (bf16_gemm_kernel<0, 2>), grid, dim3(256), 0, st, w + L.wt, nullptr, nullptr,
                          dY, T, K, L.RB32, R, s_w, dX, K);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dW) {
     const int64_t tu = L.RB16 * L.TB32 * 64;
-    hipLaunchKernelGGL(prep_u_kernel, dim3((unsigned)cdiv(tu, 256)), dim3(256), 0, st, dY, s_x, T, R,
+    SBN_LAUNCH("prep_u", prep_u_kernel, dim3((unsigned)cdiv(tu, 256)), dim3(256), 0, st, dY, s_x, T, R,
                        L.RB16, L.TB32, (uint4*)(w + L.uhi), (uint4*)(w + L.ulo));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t tx = L.KB16 * L.TB32 * 64;
-    hipLaunchKernelGGL(prep_xq_kernel, dim3((unsigned)cdiv(tx, 256)), dim3(256), 0, st, Xq, T, K,
+    SBN_LAUNCH("prep_xq", prep_xq_kernel, dim3((unsigned)cdiv(tx, 256)), dim3(256), 0, st, Xq, T, K,
                        L.KB16, L.TB32, (uint4*)(w + L.xq));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 grid((unsigned)cdiv(R, 256), (unsigned)cdiv(K, 256));
-    hipLaunchKernelGGL((bf16_gemm_kernel<1, 1>), grid, dim3(256), 0, st, w + L.xq, w + L.uhi,
+    SBN_LAUNCH("gemm_dw", (bf16_gemm_kernel<1, 1>), grid, dim3(256), 0, st, w + L.xq, w + L.uhi,
                        w + L.ulo, nullptr, R, K, L.TB32, (int64_t)0, s_w, (void*)dW, K);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -272,11 +272,11 @@ hipError_t launch_gemm_t(const uint8_t* Aw, const uint32_t* Ai, const int8_t* Xq
                          sbn_dtype ydt, int64_t ldy, hipStream_t st) {
   const dim3 grid((unsigned)cdiv(T, GEMM_TILE_T), (unsigned)cdiv(R, GEMM_TILE_R)), block(GT);
   if (ydt == SBN_I32_ACC)
-    hipLaunchKernelGGL((gemm_kernel<SPARSE, 0>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, KBn, Y, ldy);
+    SBN_LAUNCH(SPARSE ? "gemm_smfmac" : "gemm_mfma", (gemm_kernel<SPARSE, 0>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, KBn, Y, ldy);
   else if (ydt == SBN_F32)
-    hipLaunchKernelGGL((gemm_kernel<SPARSE, 1>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, KBn, Y, ldy);
+    SBN_LAUNCH(SPARSE ? "gemm_smfmac" : "gemm_mfma", (gemm_kernel<SPARSE, 1>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, KBn, Y, ldy);
   else
-    hipLaunchKernelGGL((gemm_kernel<SPARSE, 2>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, KBn, Y, ldy);
+    SBN_LAUNCH(SPARSE ? "gemm_smfmac" : "gemm_mfma", (gemm_kernel<SPARSE, 2>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, KBn, Y, ldy);
   return hipGetLastError();
 }
 
@@ -302,7 +302,7 @@ hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
     uint8_t* vals = w;
     uint32_t* idx = (uint32_t*)(w + align256((size_t)(RB * KBn * 1024)));
     const int64_t threads = RB * KBn * 64;
-    hipLaunchKernelGGL(expand_sparse_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st,
+    SBN_LAUNCH("expand_sparse", expand_sparse_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st,
                        codes, meta, R, K, n, m, RB, KBn, vals, idx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -310,7 +310,7 @@ hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
   }
   const int64_t KD = 2 * KBn;
   const int64_t threads = RB * KD * 64;
-  hipLaunchKernelGGL(expand_dense_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st,
+  SBN_LAUNCH("expand_dense", expand_dense_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st,
                      codes, meta, R, K, n, m, RB, KD, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

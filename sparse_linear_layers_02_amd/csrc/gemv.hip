@@ -177,11 +177,11 @@ hipError_t launch_gemv_nm(const int8_t* Xq, const float* s_x, int64_t T, int64_t
   const dim3 grid((unsigned)cdiv(R, 16)), block(256);
   const uint8_t* mp = (N == M) ? nullptr : meta;
   if (ydt == SBN_I32_ACC)
-    hipLaunchKernelGGL((gemv_kernel<N, M, 0>), grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    SBN_LAUNCH("gemv", (gemv_kernel<N, M, 0>), grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
   else if (ydt == SBN_F32)
-    hipLaunchKernelGGL((gemv_kernel<N, M, 1>), grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    SBN_LAUNCH("gemv", (gemv_kernel<N, M, 1>), grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
   else
-    hipLaunchKernelGGL((gemv_kernel<N, M, 2>), grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    SBN_LAUNCH("gemv", (gemv_kernel<N, M, 2>), grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
   return hipGetLastError();
 }
 

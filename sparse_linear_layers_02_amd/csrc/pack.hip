@@ -329,7 +329,7 @@ PackPlan pack_plan(int64_t R, int64_t K) {
 hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
                        uint8_t* codes, uint8_t* meta, float* s_w, void* ws, hipStream_t st) {
   const PackPlan p = pack_plan(R, K);
-  hipLaunchKernelGGL(abs_sum_kernel, dim3((unsigned)p.nblocks), dim3(PT), 0, st, W, R, K, ldw,
+  SBN_LAUNCH("abs_sum", abs_sum_kernel, dim3((unsigned)p.nblocks), dim3(PT), 0, st, W, R, K, ldw,
                      p.rows_per_block, (unsigned char*)ws, s_w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -341,10 +341,10 @@ hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int
   const int64_t dr = stride / cpr, dch = stride % cpr;
   uint8_t* mp = (n == m) ? nullptr : meta;
   if (m == 4)
-    hipLaunchKernelGGL(mask_pack_kernel<4>, dim3((unsigned)blocks), dim3(PT), 0, st, W, R, K, ldw,
+    SBN_LAUNCH("mask_pack", mask_pack_kernel<4>, dim3((unsigned)blocks), dim3(PT), 0, st, W, R, K, ldw,
                        n, codes, mp, s_w, (unsigned char*)ws, total, dr, dch);
   else
-    hipLaunchKernelGGL(mask_pack_kernel<8>, dim3((unsigned)blocks), dim3(PT), 0, st, W, R, K, ldw,
+    SBN_LAUNCH("mask_pack", mask_pack_kernel<8>, dim3((unsigned)blocks), dim3(PT), 0, st, W, R, K, ldw,
                        n, codes, mp, s_w, (unsigned char*)ws, total, dr, dch);
   return hipGetLastError();
 }

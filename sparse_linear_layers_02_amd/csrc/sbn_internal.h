@@ -66,6 +66,20 @@ bool gemm_uses_smfmac(int n, int m);
 size_t gemm_ws_bytes(int64_t T, int64_t R, int64_t K, int n, int m);
 size_t bwd_ws_bytes(int64_t T, int64_t R, int64_t K, int n, int m);
 
+// ----------------------------------------------------------------- kernel timing
+// prof_begin returns -1 when timing is off (one relaxed load); otherwise it
+// records a start event on `st` and returns a slot closed by prof_end.
+int prof_begin(hipStream_t st, const char* name);
+void prof_end(int slot, hipStream_t st);
+
+// launch `kernel` on `st`, bracketed by timing events when timing is on
+#define SBN_LAUNCH(name, kernel, grid, block, shmem, st, ...)          \
+  do {                                                                 \
+    const int sbn_p_ = ::sbn::prof_begin((st), (name));                \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);   \
+    ::sbn::prof_end(sbn_p_, (st));                                     \
+  } while (0)
+
 // ----------------------------------------------------------------- launchers
 hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
                        uint8_t* codes, uint8_t* meta, float* s_w, void* ws, hipStream_t st);

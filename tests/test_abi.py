@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = sbn.header_symbols()
-    assert len(names) == 10
+    assert len(names) == 13
     for nm in names:
         assert hasattr(L, nm), nm
 
@@ -132,3 +132,12 @@ def test_backward_validation(L):
     assert call(dxdt=2) == DTYPE
     assert call(dX=MIS) == ALIGN
     assert call(wsb=64) == WS
+
+
+def test_profile_calls_without_launches(L):
+    assert L.sbn_profile_enable(1) == OK
+    assert L.sbn_profile_reset() == OK
+    buf = ctypes.create_string_buffer(256)
+    assert L.sbn_profile_dump(buf, 256) == OK and buf.value == b""
+    assert L.sbn_profile_dump(None, 0) == NULL
+    assert L.sbn_profile_enable(0) == OK

@@ -199,11 +199,20 @@ def forward_case(T, R, K, n, m, seed=0):
 
 
 def run_matmul(kind, Xq, s_x, codes, meta, s_w, R, n, m, ydt):
+    """Runs the GEMM/GEMV; the output buffer's row stride is R rounded up to 8
+    (the ABI's leading-dimension rule), and the padding columns must stay untouched."""
     import torch
     fn = sbn.sbn_sparse_ternary_gemm if kind == "gemm" else sbn.sbn_sparse_ternary_gemv
-    Y = fn(Xq, s_x, codes, meta, s_w, R, n, m, ydt=ydt)
+    T = Xq.shape[0]
+    ldy = (R + 7) // 8 * 8
+    dt = {sbn.SBN_F32: torch.float32, sbn.SBN_BF16: torch.bfloat16, sbn.SBN_I32_ACC: torch.int32}[ydt]
+    full = torch.full((T, ldy), 77, dtype=dt, device=Xq.device)
+    Y = full[:, :R]
+    fn(Xq, s_x, codes, meta, s_w, R, n, m, ydt=ydt, Y=Y)
     torch.cuda.synchronize()
-    return host(Y)
+    if ldy > R:
+        assert bool((full[:, R:] == 77).all()), "write past R"
+    return host(Y.contiguous())
 
 
 def check_outputs(kind, f, Xq, s_x, codes, meta, s_w, R, n, m):
@@ -231,10 +240,12 @@ def test_gemm_ragged_all_ratios(n, m):
     check_outputs("gemm", f, Xq, s_x, codes, meta, s_w, R, n, m)
 
 
-@pytest.mark.parametrize("T,R,K", [(1, 16, 64), (17, 33, 128), (257, 257, 640)])
+@pytest.mark.parametrize("T,R,K", [(1, 16, 64), (5, 33, 128), (17, 33, 128), (257, 257, 640)])
 def test_gemm_small_edges(T, R, K):
     f, Xq, s_x, codes, meta, s_w = forward_case(T, R, K, 2, 4, seed=T)
     check_outputs("gemm", f, Xq, s_x, codes, meta, s_w, R, 2, 4)
+    if T <= 16:
+        check_outputs("gemv", f, Xq, s_x, codes, meta, s_w, R, 2, 4)
 
 
 def test_gemm_extreme_activations():
