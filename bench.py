@@ -13,8 +13,10 @@ resident in HBM:
                      T=2048, R=K=8192 (one line per ratio is not the
                      contract; the JSON line carries the list).
 `value` is dense-equivalent int8 TOPS of the whole step (2*T*R*K per
-forward product; the train step counts its three products).  One JSON line
-is printed.  The same line carries:
+forward product; the train step counts its three products), timed over
+--steps replays of the step captured as a HIP graph (the library only
+enqueues kernels on the caller's stream).  One JSON line is printed.  The
+same line carries:
   roofline      the dominant kernel's algorithmic ops (or bytes) per launch
                 over its average launch time, timed with HIP events that the
                 library records around each launch on its own stream,
@@ -100,7 +102,7 @@ def make_forward_step(wl, n, m, with_backward=False):
     Xq = torch.empty((wl.T, wl.K), dtype=torch.int8, device="cuda")
     s_x = torch.empty(wl.T, dtype=torch.float32, device="cuda")
     Y = torch.empty((wl.T, wl.R), dtype=torch.bfloat16, device="cuda")
-    ws_pack = torch.zeros(sbn.sbn_workspace_bytes(sbn.SBN_OP_PACK, 0, wl.R, wl.K, n, m), dtype=torch.uint8,
+    ws_pack = torch.empty(sbn.sbn_workspace_bytes(sbn.SBN_OP_PACK, 0, wl.R, wl.K, n, m), dtype=torch.uint8,
                           device="cuda")
     ws_gemm = torch.empty(max(sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM, wl.T, wl.R, wl.K, n, m), 256),
                           dtype=torch.uint8, device="cuda")
@@ -125,26 +127,60 @@ def make_forward_step(wl, n, m, with_backward=False):
     return step
 
 
-def time_steps(step, steps, warmup):
+def capture_graph(step):
+    """One step captured as a HIP graph (the library only enqueues kernels on
+    the current stream, so it captures cleanly); None if capture fails."""
+    import torch
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        return g
+    except Exception as e:                       # pragma: no cover - reported in the JSON line
+        print(f"graph capture failed, timing eager launches: {e}", file=sys.stderr)
+        return None
+
+
+def time_steps(step, steps, warmup, kernel=None, use_graph=True):
+    """Timed region: `steps` steps between two synchronisations, replayed from
+    a HIP graph when possible.  Then the same number of eager steps with the
+    library's HIP events around `kernel` (all kernels if None) give its
+    average launch duration.  Returns (ms_per_step, wall_s, prof, mode)."""
     import torch
     import sparse_linear_layers_02_amd as sbn
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    sbn.sbn_profile_reset()
-    sbn.sbn_profile_enable(True)
+    g = capture_graph(step) if use_graph else None
+    run = g.replay if g is not None else step
+    for _ in range(2):
+        run()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()                     # barrier (one rank) + sync on both sides
     t0 = time.perf_counter()
     e0.record()
     for _ in range(steps):
-        step()
+        run()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    # per-kernel durations: eager steps, events recorded by the library on its stream
+    sbn.sbn_profile_reset()
+    sbn.sbn_profile_enable(True, kernel)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
     sbn.sbn_profile_enable(False)
     prof = sbn.sbn_profile_dump()
-    return e0.elapsed_time(e1) / steps, wall, prof
+    return ms, wall, prof, ("graph" if g is not None else "eager")
 
 
 # ---------------------------------------------------------------------- decode GEMV
@@ -169,7 +205,7 @@ def decode_gemv(n=2, m=4, T=1, reps=3):
         sbn.sbn_sparse_ternary_gemv(Xq, s_x, codes[i], metas[i], s_w, wl.R, n, m, Y=Y)
     torch.cuda.synchronize()
     sbn.sbn_profile_reset()
-    sbn.sbn_profile_enable(True)
+    sbn.sbn_profile_enable(True, "gemv")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -240,11 +276,11 @@ def main():
         wl = WORKLOADS[a.workload]
         n, m = wl.nm[0]
         step = make_forward_step(wl, n, m, with_backward=(a.workload == "train"))
-        ms, wall, prof = time_steps(step, a.steps, a.warmup)
+        ms, wall, prof, mode = time_steps(step, a.steps, a.warmup)
         nprod = 3 if a.workload == "train" else 1
         ops = 2 * wl.T * wl.R * wl.K * nprod
         out.update(value=round(ops / (ms * 1e-3) / 1e12, 3), unit="TOPS", ms_per_step=round(ms, 4),
-                   wall_s=round(wall, 4))
+                   wall_s=round(wall, 4), launch=mode)
         out["config"] = {"workload": a.workload, "T": wl.T, "R": wl.R, "K": wl.K, "nm": f"{n}:{m}",
                          "step": "pack+act_quant+gemm" + ("+backward" if nprod == 3 else ""),
                          "y_dtype": "bf16", "seed": 0}
@@ -276,8 +312,8 @@ def main():
             codes, meta, s_w = sbn.sbn_mask_ternarize_pack(W, n, m)
             Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0)))
             Y = torch.empty((wl.T, wl.R), dtype=torch.bfloat16, device="cuda")
-            ms, wall, prof = time_steps(lambda: sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, wl.R, n, m, Y=Y),
-                                        a.steps, a.warmup)
+            ms, wall, prof, mode = time_steps(
+                lambda: sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, wl.R, n, m, Y=Y), a.steps, a.warmup)
             gname = "gemm_smfmac" if sbn_uses_smfmac(n, m) else "gemm_mfma"
             g_ms, _ = kernel_avg_ms(prof, gname)
             ops = 2 * wl.T * wl.R * wl.K

@@ -126,11 +126,8 @@ sbn_status sbn_workspace_bytes(sbn_op op, int64_t T, int64_t R, int64_t K,
  *   codes  [R x K*n/(4m)] bytes                                     (out)
  *   meta   [R x K/8] bytes; ignored and may be NULL when n == m     (out)
  *   s_w    1 float                                                  (out)
- *   ws     workspace of sbn_workspace_bytes(SBN_OP_PACK, 0, R, K, n, m).  Its
- *          first 2304 bytes hold a completion counter and per-exponent sums
- *          that must be zero when a call starts: zero-fill the workspace once
- *          before its first use; every call leaves that header zeroed again.
- *          Do not reuse the memory for other operations between pack calls.
+ *   ws     workspace of sbn_workspace_bytes(SBN_OP_PACK, 0, R, K, n, m); needs
+ *          no initialisation (it holds per-block partial sums of |w|).
  *
  * Limits: K <= 2^18 and R*K < 2^37.
  * The result is bit-for-bit independent of launch geometry (the sum of
@@ -207,15 +204,16 @@ sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* 
 
 /*
  * Kernel timing (diagnostics; not part of the operator).  While enabled,
- * every kernel the library launches is bracketed by two HIP events recorded
- * on the stream it runs on.  sbn_profile_dump waits for the recorded events
+ * every kernel the library launches whose name equals `kernel` (or every
+ * kernel, when `kernel` is NULL) is bracketed by two HIP events recorded on
+ * the stream it runs on.  sbn_profile_dump waits for the recorded events
  * and writes one line per kernel name, "name launches total_ms\n", into buf
  * (NUL-terminated, truncated to buf_bytes); sbn_profile_reset forgets them.
  * Kernel names: abs_sum, mask_pack, act_quant, expand_sparse, expand_dense,
  * gemm_smfmac, gemm_mfma, gemv, expand_wt, prep_u, prep_xq, gemm_dx, gemm_dw.
  * Errors: SBN_ERR_NULL (buf), SBN_ERR_HIP.
  */
-sbn_status sbn_profile_enable(int on);
+sbn_status sbn_profile_enable(int on, const char* kernel);
 sbn_status sbn_profile_reset(void);
 sbn_status sbn_profile_dump(char* buf, size_t buf_bytes);
 

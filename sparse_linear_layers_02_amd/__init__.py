@@ -53,7 +53,7 @@ _SIGNATURES = {
                                  _vp, _sz, _vp], _int),
     "sbn_backward": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _int, _int, _vp, _int, _vp, _vp,
                       _sz, _vp], _int),
-    "sbn_profile_enable": ([_int], _int),
+    "sbn_profile_enable": ([_int, ctypes.c_char_p], _int),
     "sbn_profile_reset": ([], _int),
     "sbn_profile_dump": ([ctypes.c_char_p, _sz], _int),
 }
@@ -119,25 +119,21 @@ def _stream(stream):
 
 
 class Workspace:
-    """Grow-only device byte buffer for one operation.  ``zeroed`` buffers are
-    created with zeros (the pack workspace header must start at zero; every
-    pack call leaves it zeroed again)."""
+    """Grow-only device byte buffer for one operation."""
 
-    def __init__(self, zeroed: bool = False):
+    def __init__(self):
         self.buf = None
-        self.zeroed = zeroed
 
     def get(self, nbytes: int, device):
         torch = _torch()
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            alloc = torch.zeros if self.zeroed else torch.empty
-            self.buf = alloc(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         return self.buf
 
 
-_WS = {"pack": Workspace(zeroed=True), "gemm": Workspace(), "bwd": Workspace()}
+_WS = {"pack": Workspace(), "gemm": Workspace(), "bwd": Workspace()}
 
 
 def sbn_mask_ternarize_pack(W, n: int, m: int, *, codes=None, meta=None, s_w=None, ws=None, stream=None):
@@ -226,9 +222,10 @@ def sbn_backward(dY, Xq, s_x, codes, meta, s_w, n: int, m: int, *, dxdt: int = S
 
 
 # ------------------------------------------------------------------ kernel timing
-def sbn_profile_enable(on: bool = True) -> None:
-    """Bracket every library kernel launch with HIP events on its stream."""
-    _check("sbn_profile_enable", lib().sbn_profile_enable(1 if on else 0))
+def sbn_profile_enable(on: bool = True, kernel: str | None = None) -> None:
+    """Bracket library kernel launches (all, or only those named `kernel`) with
+    HIP events on their stream."""
+    _check("sbn_profile_enable", lib().sbn_profile_enable(1 if on else 0, kernel.encode() if kernel else None))
 
 
 def sbn_profile_reset() -> None:

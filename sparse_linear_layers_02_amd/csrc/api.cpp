@@ -129,6 +129,7 @@ struct ProfRec {
   hipEvent_t start, stop;
 };
 std::atomic<int> g_prof_on{0};
+char g_prof_only[64] = "";          // empty: every kernel
 std::mutex g_prof_mu;
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_prof_pool;
@@ -172,9 +173,10 @@ namespace sbn {
 int prof_begin(hipStream_t st, const char* name) {
   if (!g_prof_on.load(std::memory_order_relaxed)) return -1;
   std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (g_prof_only[0] && strcmp(g_prof_only, name) != 0) return -1;
   ProfRec r{name, prof_event(), nullptr};
   if (!r.start) return -1;
-  hipEventRecord(r.start, st);
+  (void)hipEventRecord(r.start, st);
   g_prof_recs.push_back(r);
   return (int)g_prof_recs.size() - 1;
 }
@@ -185,7 +187,7 @@ void prof_end(int slot, hipStream_t st) {
   if (slot >= (int)g_prof_recs.size()) return;
   hipEvent_t e = prof_event();
   if (!e) return;
-  hipEventRecord(e, st);
+  (void)hipEventRecord(e, st);
   g_prof_recs[slot].stop = e;
 }
 
@@ -193,7 +195,11 @@ void prof_end(int slot, hipStream_t st) {
 
 extern "C" {
 
-sbn_status sbn_profile_enable(int on) {
+sbn_status sbn_profile_enable(int on, const char* kernel) {
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    snprintf(g_prof_only, sizeof(g_prof_only), "%s", kernel ? kernel : "");
+  }
   g_prof_on.store(on ? 1 : 0);
   return ok();
 }

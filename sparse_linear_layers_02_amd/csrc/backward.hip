@@ -132,7 +132,8 @@ __global__ __launch_bounds__(256) void prep_xq_kernel(const int8_t* __restrict__
 // MODE 0 (dX): A = Wt fragments (rows k, contraction r), B = dY rows read directly.
 // MODE 1 (dW): A = Xq fragments (rows k, contraction t), B = u_hi and u_lo fragments (rows r).
 // Block tile 256 (A rows) x 256 (B rows), 4 waves 2 x 2, wave tile 128 x 128,
-// one contraction step of 32 per stage (MODE 1 takes two B fragments per step).
+// one contraction step of 32 per stage (MODE 1 takes two B fragments per step),
+// 3-4 stages of direct-to-LDS loads in flight.
 template <int MODE, int OUT>
 __global__ __launch_bounds__(256, 1) void bf16_gemm_kernel(
     const uint8_t* __restrict__ Afr, const uint8_t* __restrict__ Bfr_hi,
@@ -143,7 +144,9 @@ __global__ __launch_bounds__(256, 1) void bf16_gemm_kernel(
   constexpr int A_BYTES = 16 * 1024;
   constexpr int B_BYTES = 16 * 1024 * NBF;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  constexpr int NST = MODE == 1 ? 3 : 4;              // 144 KB / 128 KB of LDS
+  constexpr int LPS = 4 + 4 * NBF;                    // loads per stage per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -182,12 +185,15 @@ __global__ __launch_bounds__(256, 1) void bf16_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  load_stage(0, 0);
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nsteps) load_stage(s, s);
   for (int64_t step = 0; step < nsteps; ++step) {
-    wait_vmem();
-    __syncthreads();
-    if (step + 1 < nsteps) load_stage((int)((step + 1) & 1), step + 1);
-    const uint8_t* base = smem + (step & 1) * STAGE;
+    if (step + NST - 2 < nsteps) wait_vmcnt<(NST - 2) * LPS>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (step + NST - 1 < nsteps) load_stage((int)((step + NST - 1) % NST), step + NST - 1);
+    const uint8_t* base = smem + (step % NST) * STAGE;
     v8bf b[8], b2[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {

@@ -61,7 +61,24 @@ __global__ __launch_bounds__(256) void expand_sparse_kernel(
   const int64_t k0 = kb * 128 + 32 * (l >> 4);
   uint32_t v32[4] = {0, 0, 0, 0};
   uint32_t ix = 0x44444444u;                    // (0,1) in every half: harmless with zero values
-  if (r < R && k0 < K) {
+  if (r < R && k0 < K && n == 2 && m == 4) {
+    // 2:4: meta and codes of these 32 positions are one aligned word each
+    const uint32_t mb = *(const uint32_t*)(meta + r * (K / 8) + k0 / 8);
+    const uint32_t cb = *(const uint32_t*)(codes + r * (K / 8) + k0 / 8);
+    // survivor positions per nibble: p0 = lowest set bit, p1 = highest (SWAR over 8 nibbles)
+    const uint32_t M1 = 0x11111111u;
+    const uint32_t b0 = mb & M1, b1 = (mb >> 1) & M1, b2 = (mb >> 2) & M1, b3 = (mb >> 3) & M1;
+    const uint32_t nb0 = b0 ^ M1, nb1 = b1 ^ M1, nb2 = b2 ^ M1;
+    ix = (nb0 & b1) | ((nb0 & nb1) << 1) | ((b3 | nb2) << 2) | ((b3 | b2) << 3);
+    // values: compressed slot j holds code bits 2j..2j+1; spread each byte's four
+    // codes to four bytes and map 01 -> +1, 11 -> -1
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t y = (cb >> (8 * d)) & 0xFFu;
+      const uint32_t sp = (((y & 0x33u) * 0x1001u) & 0x00030003u) | (((y & 0xCCu) * 0x40040u) & 0x03000300u);
+      v32[d] = sp | ((sp & 0x02020202u) * 0x7Eu);
+    }
+  } else if (r < R && k0 < K) {
     const uint32_t mb = *(const uint32_t*)(meta + r * (K / 8) + k0 / 8);
     const int64_t crow = K * n / (4 * m);
     const int64_t gbase = k0 / m;               // groups before k0 in this row
@@ -136,111 +153,131 @@ __global__ __launch_bounds__(256) void expand_dense_kernel(
 }
 
 // ---------------------------------------------------------------- GEMM
-// OUT: 0 = int32 accumulator, 1 = float32, 2 = bf16
-template <bool SPARSE, int OUT>
-__global__ __launch_bounds__(GT, 1) void gemm_kernel(
+// Tile order: blocks are dealt to the 8 XCDs round-robin; give each XCD a
+// contiguous run of tiles, and walk tiles in groups of 8 row tiles (token
+// tile major inside a group), so the blocks resident on one XCD share row
+// and token operands in that XCD's L2.
+__device__ inline void tile_of_block(int64_t b, int64_t ntR, int64_t ntT, int64_t& rt, int64_t& tt) {
+  const int64_t ntiles = ntR * ntT;
+  const int64_t xcd = b & 7, local = b >> 3;
+  const int64_t base = ntiles / 8, rem = ntiles % 8;
+  const int64_t t = xcd * base + (xcd < rem ? xcd : rem) + local;   // blocks of XCD x come first
+  const int64_t g = t / (8 * ntT);                                  // group of 8 row tiles
+  const int64_t gr = (ntR - 8 * g) < 8 ? (ntR - 8 * g) : 8;
+  const int64_t j = t - g * 8 * ntT;
+  rt = 8 * g + j % gr;
+  tt = j / gr;
+}
+
+// OUT: 0 = int32 accumulator, 1 = float32, 2 = bf16.  WR x WT waves, wave tile
+// (256/WR) rows x (256/WT) tokens.  SPARSE: K step 128 (smfmac), 3 stages;
+// dense: K step 64 (mfma 16x16x64), 4 stages.
+template <bool SPARSE, int OUT, int WR, int WT>
+__global__ __launch_bounds__(64 * WR * WT, 1) void gemm_kernel(
     const uint8_t* __restrict__ Aw, const uint32_t* __restrict__ Ai, const int8_t* __restrict__ Xq,
     const float* __restrict__ s_x, const float* __restrict__ s_w, int64_t T, int64_t K, int64_t R,
-    int64_t KBn, void* __restrict__ Y, int64_t ldy) {
-  constexpr int A_BYTES = SPARSE ? 16 * 1024 : 16 * 2 * 1024;
+    int64_t nks, int64_t fstride, void* __restrict__ Y, int64_t ldy) {
+  constexpr int NW = WR * WT;
+  constexpr int MI = 256 / WR / 16, MJ = 256 / WT / 16;          // fragments per wave
+  constexpr int A_BYTES = 16 * 1024;
   constexpr int I_BYTES = SPARSE ? 16 * 256 : 0;
-  constexpr int B_BYTES = 16 * 2 * 1024;
+  constexpr int BH = SPARSE ? 2 : 1;                              // B 1 KB halves per token block
+  constexpr int B_BYTES = 16 * BH * 1024;
   constexpr int STAGE = A_BYTES + I_BYTES + B_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  constexpr int NST = SPARSE ? 3 : 4;
+  constexpr int KS = SPARSE ? 128 : 64;
+  constexpr int LPS = (16 / NW) * (SPARSE ? 2 : 1) + (16 * BH) / NW;   // loads per stage per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wr = wave >> 1, wt = wave & 1;
-  const int64_t tile_t = (int64_t)blockIdx.x * 256;
-  const int64_t tile_r = (int64_t)blockIdx.y * 256;
+  const int wr = wave / WT, wt = wave % WT;
+  int64_t rtile, ttile;
+  tile_of_block(blockIdx.x, cdiv(R, 256), cdiv(T, 256), rtile, ttile);
+  const int64_t tile_r = rtile * 256, tile_t = ttile * 256;
   const int64_t rb0 = tile_r / 16;
-  const int64_t KD = 2 * KBn;
 
-  auto load_stage = [&](int s, int64_t kb) {
+  auto load_stage = [&](int s, int64_t ks) {
     uint8_t* base = smem + s * STAGE;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = wave + 4 * q;
-      if (SPARSE) {
-        const int64_t frag = (rb0 + i) * KBn + kb;
-        g2lds16(Aw + frag * 1024 + lane * 16, base + i * 1024);
-        g2lds4(Ai + frag * 64 + lane, base + A_BYTES + i * 256);
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int64_t frag = (rb0 + i) * KD + 2 * kb + h;
-          g2lds16(Aw + frag * 1024 + lane * 16, base + (i * 2 + h) * 1024);
-        }
-      }
+    for (int q = 0; q < 16 / NW; ++q) {
+      const int i = wave + NW * q;
+      const int64_t frag = (rb0 + i) * fstride + ks;
+      g2lds16(Aw + frag * 1024 + lane * 16, base + i * 1024);
+      if (SPARSE) g2lds4(Ai + frag * 64 + lane, base + A_BYTES + i * 256);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = wave + 4 * q;
+    for (int q = 0; q < (16 * BH) / NW; ++q) {
+      const int hb = wave + NW * q;                                  // half-block index
+      const int j = hb / BH, h = hb % BH;
       int64_t t = tile_t + 16 * j + (lane & 15);
       t = t < T ? t : T - 1;                      // rows past T are computed and discarded
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int64_t k = kb * 128 + 64 * h + 16 * (lane >> 4);
-        k = k < K ? k : K - 16;                   // W is zero past K, any finite bytes do
-        g2lds16(Xq + t * K + k, base + A_BYTES + I_BYTES + (j * 2 + h) * 1024);
-      }
+      int64_t k = ks * KS + 64 * h + 16 * (lane >> 4);
+      k = k < K ? k : K - 16;                     // W is zero past K, any finite bytes do
+      g2lds16(Xq + t * K + k, base + A_BYTES + I_BYTES + hb * 1024);
     }
   };
 
-  v4i acc[8][8];
+  v4i acc[MI][MJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+    for (int j = 0; j < MJ; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
 
-  load_stage(0, 0);
-  for (int64_t kb = 0; kb < KBn; ++kb) {
-    wait_vmem();
-    __syncthreads();
-    if (kb + 1 < KBn) load_stage((int)((kb + 1) & 1), kb + 1);
-    const uint8_t* base = smem + (kb & 1) * STAGE;
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nks) load_stage(s, s);
+
+  for (int64_t ks = 0; ks < nks; ++ks) {
+    if (ks + NST - 2 < nks) wait_vmcnt<(NST - 2) * LPS>();       // stage ks landed, later ones may fly
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (ks + NST - 1 < nks) load_stage((int)((ks + NST - 1) % NST), ks + NST - 1);
+    const uint8_t* base = smem + (ks % NST) * STAGE;
     const uint8_t* bb = base + A_BYTES + I_BYTES;
-    v4i blo[8], bhi[8];
+    v4i blo[MJ], bhi[MJ];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int jj = 8 * wt + j;
-      blo[j] = *(const v4i*)(bb + (jj * 2 + 0) * 1024 + lane * 16);
-      bhi[j] = *(const v4i*)(bb + (jj * 2 + 1) * 1024 + lane * 16);
+    for (int j = 0; j < MJ; ++j) {
+      const int jj = MJ * wt + j;
+      blo[j] = *(const v4i*)(bb + (jj * BH + 0) * 1024 + lane * 16);
+      if (SPARSE) bhi[j] = *(const v4i*)(bb + (jj * BH + 1) * 1024 + lane * 16);
     }
+    v4i a = *(const v4i*)(base + (MI * wr) * 1024 + lane * 16);
+    int ix = SPARSE ? *(const int*)(base + A_BYTES + (MI * wr) * 256 + lane * 4) : 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ii = 8 * wr + i;
-      if (SPARSE) {
-        const v4i a = *(const v4i*)(base + ii * 1024 + lane * 16);
-        const int ix = *(const int*)(base + A_BYTES + ii * 256 + lane * 4);
+    for (int i = 0; i < MI; ++i) {
+      v4i an = a;
+      int ixn = ix;
+      if (i + 1 < MI) {                           // next A fragment in flight during these products
+        const int ii = MI * wr + i + 1;
+        an = *(const v4i*)(base + ii * 1024 + lane * 16);
+        if (SPARSE) ixn = *(const int*)(base + A_BYTES + ii * 256 + lane * 4);
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < MJ; ++j) {
+        if (SPARSE) {
           const v8i b = (v8i){blo[j][0], blo[j][1], blo[j][2], blo[j][3],
                               bhi[j][0], bhi[j][1], bhi[j][2], bhi[j][3]};
           acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, acc[i][j], ix, 0, 0);
-        }
-      } else {
-        const v4i a0 = *(const v4i*)(base + (ii * 2 + 0) * 1024 + lane * 16);
-        const v4i a1 = *(const v4i*)(base + (ii * 2 + 1) * 1024 + lane * 16);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, blo[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bhi[j], acc[i][j], 0, 0, 0);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, blo[j], acc[i][j], 0, 0, 0);
         }
       }
+      a = an;
+      ix = ixn;
     }
   }
 
   // epilogue: lane holds rows r..r+3 of token t
   const float sw = (OUT != 0) ? *s_w : 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t t = tile_t + 16 * (8 * wt + j) + (lane & 15);
+  for (int j = 0; j < MJ; ++j) {
+    const int64_t t = tile_t + 16 * (MJ * wt + j) + (lane & 15);
     if (t >= T) continue;
     const float sc = (OUT != 0) ? sw * s_x[t] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t r = tile_r + 16 * (8 * wr + i) + 4 * (lane >> 4);
+    for (int i = 0; i < MI; ++i) {
+      const int64_t r = tile_r + 16 * (MI * wr + i) + 4 * (lane >> 4);
       if (r >= R) continue;
       const v4i c = acc[i][j];
       if (OUT == 0) {
@@ -266,17 +303,27 @@ __global__ __launch_bounds__(GT, 1) void gemm_kernel(
   }
 }
 
+// wave layouts: 8 waves of 128 x 64 (default; two waves per SIMD hide LDS latency) or 4 of 128 x 128
+#ifndef SBN_GEMM_WT
+#define SBN_GEMM_WT 4
+#endif
+
 template <bool SPARSE>
 hipError_t launch_gemm_t(const uint8_t* Aw, const uint32_t* Ai, const int8_t* Xq, const float* s_x,
                          const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y,
                          sbn_dtype ydt, int64_t ldy, hipStream_t st) {
-  const dim3 grid((unsigned)cdiv(T, GEMM_TILE_T), (unsigned)cdiv(R, GEMM_TILE_R)), block(GT);
+  constexpr int WR = 2, WT = SBN_GEMM_WT;
+  const int64_t ntiles = cdiv(T, GEMM_TILE_T) * cdiv(R, GEMM_TILE_R);
+  const dim3 grid((unsigned)ntiles), block(64 * WR * WT);
+  const int64_t nks = SPARSE ? KBn : K / 64;
+  const int64_t fstride = SPARSE ? KBn : 2 * KBn;
+  const char* name = SPARSE ? "gemm_smfmac" : "gemm_mfma";
   if (ydt == SBN_I32_ACC)
-    SBN_LAUNCH(SPARSE ? "gemm_smfmac" : "gemm_mfma", (gemm_kernel<SPARSE, 0>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, KBn, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 0, WR, WT>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, nks, fstride, Y, ldy);
   else if (ydt == SBN_F32)
-    SBN_LAUNCH(SPARSE ? "gemm_smfmac" : "gemm_mfma", (gemm_kernel<SPARSE, 1>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, KBn, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 1, WR, WT>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, nks, fstride, Y, ldy);
   else
-    SBN_LAUNCH(SPARSE ? "gemm_smfmac" : "gemm_mfma", (gemm_kernel<SPARSE, 2>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, KBn, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 2, WR, WT>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, nks, fstride, Y, ldy);
   return hipGetLastError();
 }
 

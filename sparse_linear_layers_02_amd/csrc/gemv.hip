@@ -12,12 +12,14 @@
 // bits) to the four int8 weights {-1, 0, +1} of those positions (unused code
 // bits are ignored).  Every group of four positions is one table read.
 //
-// Work split: one block (4 waves) per 16 output rows.  K is cut into ranges of
-// 1024 positions; a wave takes ranges wave, wave+4, ...  Inside a range, lane
+// Work split: one block (8 waves) per 16 output rows.  K is cut into ranges of
+// 512 positions; a wave takes ranges wave, wave+8, ...  Inside a range, lane
 // l (row l%16, part g = l/16) owns a contiguous run of 16*S positions, so its
 // meta and code bits are contiguous; the matrix instruction only needs A lane
 // (r, g) and B lane (t, g) to cover the same positions, which they do.  The
-// four waves' 16x16 partial sums are added in LDS.
+// waves' 16x16 partial sums are added in LDS.  All loads of a wave's first
+// range (packed bits and activations) are issued before the block copies the
+// unpack table and synchronises, so the three fetches overlap.
 #include "sbn_internal.h"
 
 namespace sbn {
@@ -53,75 +55,78 @@ __device__ inline uint32_t bits_at(const uint32_t (&w)[NW], int off, int nb) {
   return nb >= 32 ? v : (v & ((1u << nb) - 1u));
 }
 
-template <int N, int M, int OUT>
-__global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ Xq,
-                                                   const float* __restrict__ s_x, int64_t T,
-                                                   int64_t K, const uint8_t* __restrict__ codes,
-                                                   const uint8_t* __restrict__ meta,
-                                                   const float* __restrict__ s_w, int64_t R,
-                                                   void* __restrict__ Y, int64_t ldy) {
-  __shared__ uint32_t lut[4096];
-  __shared__ int red[4][256];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < 1024; i += 256) ((uint4*)lut)[i] = ((const uint4*)kUnpack.v)[i];
-  __syncthreads();
+constexpr int GV_WAVES = 8;            // waves per block (one block per 16 output rows)
+constexpr int GV_RANGE = 512;          // K positions per wave range: 8 MFMA steps of 64
 
+template <int N, int M, int OUT>
+__global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, const float* __restrict__ s_w,
+    int64_t R, void* __restrict__ Y, int64_t ldy) {
+  constexpr int SMAX = GV_RANGE / 64;                  // MFMA steps per range
+  constexpr int64_t CB_NUM = 2 * N;                    // code bits per group
+  constexpr int NWC = (32 * N * SMAX / M) / 32 + 1;    // normalised code words for a full range
+  __shared__ uint32_t lut[4096];
+  __shared__ int red[GV_WAVES][256];
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, rl = lane & 15;
   const int64_t r = (int64_t)blockIdx.x * 16 + rl;
-  const int64_t rr = r < R ? r : R - 1;            // rows past R: computed on row R-1, discarded
-  const int64_t tt = rl < T ? rl : 0;              // B column of this lane (token)
+  const int64_t rr = r < R ? r : R - 1;               // rows past R: computed on row R-1, discarded
   const bool tvalid = rl < T;
-  constexpr int64_t CB_NUM = 2 * N;                // code bits per group
+  const int64_t tt = tvalid ? rl : 0;                 // B column of this lane (token)
   const int64_t crow = K * N / (4 * M);
   const uint8_t* mrow = meta ? meta + rr * (K / 8) : nullptr;
   const uint8_t* crw = codes + rr * crow;
   const int8_t* xrow = Xq + tt * K;
+  const int64_t nranges = cdiv(K, GV_RANGE);
 
   v4i acc = (v4i){0, 0, 0, 0};
-  const int64_t nranges = cdiv(K, 1024);
-  for (int64_t ri = wave; ri < nranges; ri += 4) {
-    const int64_t kbeg = ri * 1024;
-    int S = (int)((K - kbeg) / 64);
-    S = S < 16 ? S : 16;
-    const int64_t p0 = kbeg + 16 * (int64_t)g * S;
+  bool first = true;
+  for (int64_t ri = wave; ri < nranges || first; ri += GV_WAVES) {
+    const bool active = ri < nranges;
+    const int64_t kbeg = ri * GV_RANGE;
+    int S = active ? (int)((K - kbeg) / 64) : 0;
+    S = S < SMAX ? S : SMAX;
+    const int64_t p0 = kbeg + 16 * (int64_t)g * S;    // this lane's run: 16*S positions
 
-    // meta bits of positions [p0, p0 + 16*S)
-    uint32_t mw[8];
-    if (N < M) {
-      if (S == 16) {
-        const uint4 a = *(const uint4*)(mrow + p0 / 8);
-        const uint4 b = *(const uint4*)(mrow + p0 / 8 + 16);
-        mw[0] = a.x; mw[1] = a.y; mw[2] = a.z; mw[3] = a.w;
-        mw[4] = b.x; mw[5] = b.y; mw[6] = b.z; mw[7] = b.w;
-      } else {
-        const uint16_t* mh = (const uint16_t*)(mrow + p0 / 8);
+    // ---- issue every load of this range before anything waits
+    uint32_t mw[SMAX / 2 + 1];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t lo = (2 * i < S) ? mh[2 * i] : 0u;
-          const uint32_t hi = (2 * i + 1 < S) ? mh[2 * i + 1] : 0u;
-          mw[i] = lo | (hi << 16);
-        }
-      }
+    for (int i = 0; i < SMAX / 2 + 1; ++i) mw[i] = 0;
+    if (N < M && active) {
+      const uint16_t* mh = (const uint16_t*)(mrow + p0 / 8);
+#pragma unroll
+      for (int i = 0; i < SMAX; ++i)
+        if (i < S) mw[i >> 1] |= (uint32_t)mh[i] << (16 * (i & 1));
     }
-    // code bits: start 2N*p0/M, 32*N*S/M of them; aligned dword loads, then shifted down
     const int64_t cbit = CB_NUM * (p0 / M);
-    const uint8_t* cp = crw + (cbit >> 3);
-    const uintptr_t ca = (uintptr_t)cp;
+    const uintptr_t ca = (uintptr_t)(crw + (cbit >> 3));
     const uint32_t* cw4 = (const uint32_t*)(ca & ~(uintptr_t)3);
     const int sh = (int)((ca & 3) * 8 + (cbit & 7));
-    constexpr int NWC = (32 * N * 16 / M) / 32 + 1;  // words for a full range, plus one
     const int nbits = 32 * N * S / M;
-    const int nd = (sh + nbits + 31) >> 5;
+    const int nd = active ? (sh + nbits + 31) >> 5 : 0;
     uint32_t raw[NWC + 1];
 #pragma unroll
     for (int i = 0; i < NWC + 1; ++i) raw[i] = (i < nd) ? cw4[i] : 0u;
+    v4i bx[SMAX];
+#pragma unroll
+    for (int j = 0; j < SMAX; ++j)
+      bx[j] = (tvalid && j < S) ? *(const v4i*)(xrow + kbeg + 16 * ((int64_t)g * S + j)) : (v4i){0, 0, 0, 0};
+
+    if (first) {                                       // unpack table, fetched while the loads above fly
+      for (int i = tid; i < 1024; i += 64 * GV_WAVES) ((uint4*)lut)[i] = ((const uint4*)kUnpack.v)[i];
+      __syncthreads();
+      first = false;
+    }
+    if (!active) break;
+
     uint32_t cw[NWC];
 #pragma unroll
     for (int i = 0; i < NWC; ++i) cw[i] = __builtin_amdgcn_alignbit(raw[i + 1], raw[i], sh);
 
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < SMAX; ++j) {
       if (j < S) {
         uint32_t e[4];
 #pragma unroll
@@ -144,9 +149,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ Xq
           e[k] = lut[nib | (c8 << 4)];
         }
         const v4i a = (v4i){(int)e[0], (int)e[1], (int)e[2], (int)e[3]};
-        v4i b = (v4i){0, 0, 0, 0};
-        if (tvalid) b = *(const v4i*)(xrow + kbeg + 16 * ((int64_t)g * S + j));
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx[j], acc, 0, 0, 0);
       }
     }
   }
@@ -154,18 +157,22 @@ __global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ Xq
 #pragma unroll
   for (int v = 0; v < 4; ++v) red[wave][lane * 4 + v] = acc[v];
   __syncthreads();
-  const int e = tid;
-  const int s = red[0][e] + red[1][e] + red[2][e] + red[3][e];
-  const int L = e >> 2, v = e & 3;
-  const int64_t row = (int64_t)blockIdx.x * 16 + 4 * (L >> 4) + v;
-  const int64_t t = L & 15;
-  if (t < T && row < R) {
-    if (OUT == 0) {
-      ((int*)Y)[t * ldy + row] = s;
-    } else {
-      const float y = (float)s * (*s_w * s_x[t]);
-      if (OUT == 1) ((float*)Y)[t * ldy + row] = y;
-      else ((uint16_t*)Y)[t * ldy + row] = f32_to_bf16_rne(y);
+  if (tid < 256) {
+    const int e = tid;
+    int s = 0;
+#pragma unroll
+    for (int w = 0; w < GV_WAVES; ++w) s += red[w][e];
+    const int L = e >> 2, v = e & 3;
+    const int64_t row = (int64_t)blockIdx.x * 16 + 4 * (L >> 4) + v;
+    const int64_t t = L & 15;
+    if (t < T && row < R) {
+      if (OUT == 0) {
+        ((int*)Y)[t * ldy + row] = s;
+      } else {
+        const float y = (float)s * (*s_w * s_x[t]);
+        if (OUT == 1) ((float*)Y)[t * ldy + row] = y;
+        else ((uint16_t*)Y)[t * ldy + row] = f32_to_bf16_rne(y);
+      }
     }
   }
 }
@@ -174,7 +181,7 @@ template <int N, int M>
 hipError_t launch_gemv_nm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                           const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
                           void* Y, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
-  const dim3 grid((unsigned)cdiv(R, 16)), block(256);
+  const dim3 grid((unsigned)cdiv(R, 16)), block(64 * GV_WAVES);
   const uint8_t* mp = (N == M) ? nullptr : meta;
   if (ydt == SBN_I32_ACC)
     SBN_LAUNCH("gemv", (gemv_kernel<N, M, 0>), grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);

@@ -1,6 +1,6 @@
 // Mask, ternarize and pack: the weight side of Sparse-BitLinear.
 //
-// Pass 1 sums |w| exactly and turns the sum into the per-tensor scale
+// Pass 1 sums |w| exactly; pass 2 turns the sum into the per-tensor scale
 //   s_w = max(fp32(mean |W|), 1e-5)   (correctly rounded, launch-independent).
 // Pass 2 computes, per group of M weights along K, the N largest |w| (ties to
 // the lower index), ternarizes with the exact test |w| > s_w/2, and writes the
@@ -15,13 +15,17 @@
 // 8-bit significand.  Magnitudes with exponent field e in [95, 131), i.e.
 // 2^-32 <= |w| < 16, are multiples of 2^-39 below 2^4; a float64 running sum
 // of at most 1024 of them stays below 2^53 units, so it is exact in any
-// order.  Each thread flushes its float64 sum into an int64 counter of
-// 2^-39 units after every row (K <= 2^18 keeps a row's share per thread at
-// <= 1024 terms).  Everything outside that window (zero, subnormal, tiny
-// or >= 16) goes to 256 per-exponent integer bins with atomics: exact too.
-// The last block to finish (atomic counter) forms the total as a 320-bit
-// integer in units of 2^-133 and rounds total / (R*K) to fp32: a float64
-// estimate, then an exact comparison against the two neighbouring midpoints.
+// order.  Each thread sums at most 64 of them in float64 (eight 16-byte
+// loads in flight) before flushing into an int64 counter of 2^-39 units.
+// Everything outside that window (zero, subnormal, tiny or >= 16) is added
+// to 256 per-exponent integer bins in LDS: exact too.  Each block writes its
+// int64 partial, a flag, and its bins only if it had such values.  Pass 2
+// starts with every block forming the total from those few hundred partials
+// (the kernel boundary makes them visible; no device-scope fence is issued,
+// which on this multi-XCD part would write back and invalidate an L2 per
+// block) as a 320-bit integer in units of 2^-133, and rounds total / (R*K) to
+// fp32: a float64 estimate, then an exact comparison against the two
+// neighbouring midpoints.  The workspace needs no initialisation.
 #include "sbn_internal.h"
 
 namespace sbn {
@@ -31,11 +35,19 @@ constexpr int PT = 256;                  // threads per block, both passes
 constexpr uint32_t E_LO = 95, E_HI = 131;
 constexpr double FAST_SCALE = 549755813888.0;  // 2^39
 
-struct PackHeader {
-  unsigned int counter;
-  unsigned int pad[63];
-  unsigned long long bins[256];
+// workspace: [partials: nb x i64][flags: nb x u32][bins: nb x 256 x u64], each 256-aligned
+struct PackWs {
+  long long* partials;
+  unsigned* flags;
+  unsigned long long* bins;
 };
+__host__ __device__ inline PackWs pack_ws(unsigned char* ws, int64_t nb) {
+  PackWs p;
+  p.partials = (long long*)ws;
+  p.flags = (unsigned*)(ws + align256((size_t)nb * 8));
+  p.bins = (unsigned long long*)(ws + align256((size_t)nb * 8) + align256((size_t)nb * 4));
+  return p;
+}
 
 // ------------------------------------------------------------------ 320-bit integer
 struct Big {
@@ -144,72 +156,134 @@ __device__ inline void slow_add(unsigned long long* bins, uint32_t mag32) {
   atomicAdd(&bins[e], (unsigned long long)sig);
 }
 
-// |w| of the two bf16 halves of u; window members returned in float64,
-// the rest sent to the bins.
-__device__ inline double pair_abs(uint32_t u, unsigned long long* bins) {
-  const uint32_t lo = (u << 16) & 0x7FFF0000u;
-  const uint32_t hi = u & 0x7FFF0000u;
-  const bool lo_in = (lo - (E_LO << 23)) < ((E_HI - E_LO) << 23);
-  const bool hi_in = (hi - (E_LO << 23)) < ((E_HI - E_LO) << 23);
-  double s = (lo_in ? (double)__uint_as_float(lo) : 0.0) + (hi_in ? (double)__uint_as_float(hi) : 0.0);
-  if (!(lo_in && hi_in)) {
-    if (!lo_in && lo) slow_add(bins, lo);
-    if (!hi_in && hi) slow_add(bins, hi);
-  }
-  return s;
+// in-window test of one magnitude given as fp32 bits (low 16 bits zero)
+__device__ inline bool in_window(uint32_t mag32) {
+  return (mag32 - (E_LO << 23)) < ((E_HI - E_LO) << 23);
 }
 
+// |w| of the two bf16 halves of u in float64 if inside the window, else 0;
+// `ok` is cleared when either half is outside it.
+__device__ inline double pair_abs(uint32_t u, bool& ok) {
+  const uint32_t lo = (u << 16) & 0x7FFF0000u;
+  const uint32_t hi = u & 0x7FFF0000u;
+  const bool lo_in = in_window(lo), hi_in = in_window(hi);
+  ok = ok && (lo_in || lo == 0u) && (hi_in || hi == 0u);      // zero adds nothing either way
+  return (lo_in ? (double)__uint_as_float(lo) : 0.0) + (hi_in ? (double)__uint_as_float(hi) : 0.0);
+}
+
+// the rare out-of-window values of u go to the exponent bins
+__device__ inline void pair_slow(uint32_t u, unsigned long long* bins) {
+  const uint32_t lo = (u << 16) & 0x7FFF0000u;
+  const uint32_t hi = u & 0x7FFF0000u;
+  if (!in_window(lo) && lo) slow_add(bins, lo);
+  if (!in_window(hi) && hi) slow_add(bins, hi);
+}
+
+constexpr int U = 8;   // 16-byte chunks in flight per thread in pass 1
+
+template <bool FLAT>
+__device__ inline uint4 chunk_at(const uint16_t* __restrict__ W, int64_t c, int64_t kc, int64_t ldw) {
+  if (FLAT) return ((const uint4*)W)[c];
+  const int64_t r = c / kc;
+  return *(const uint4*)(W + r * ldw + (c - r * kc) * 8);
+}
+
+// Pass 1: block b sums |w| over 16-byte chunks [b*cpb, (b+1)*cpb) of the
+// row-major chunk order (8 weights per chunk).  Each thread keeps U loads in
+// flight and flushes its float64 sum (<= 8U terms, exact) into int64 units;
+// out-of-window values take one rare branch per group into the LDS bins.
+template <bool FLAT>
 __global__ __launch_bounds__(PT) void abs_sum_kernel(const uint16_t* __restrict__ W, int64_t R,
-                                                     int64_t K, int64_t ldw, int64_t rows_per_block,
-                                                     unsigned char* __restrict__ ws,
-                                                     float* __restrict__ s_w) {
-  PackHeader* hdr = (PackHeader*)ws;
-  long long* partials = (long long*)(ws + sizeof(PackHeader));
+                                                     int64_t K, int64_t ldw, int64_t cpb,
+                                                     unsigned char* __restrict__ ws) {
+  const PackWs pw = pack_ws(ws, gridDim.x);
+  __shared__ unsigned long long bins[256];
+  __shared__ unsigned long long red[PT / 64];
+  __shared__ int any_slow;
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
-  const int64_t r1 = min(R, r0 + rows_per_block);
-  const int kc = (int)(K / 8);
+  bins[tid] = 0;
+  if (tid == 0) any_slow = 0;
+  __syncthreads();
+  const int64_t kc = K / 8, total = R * kc;
+  const int64_t c0 = (int64_t)blockIdx.x * cpb;
+  const int64_t c1 = min(total, c0 + cpb);
   unsigned long long acc_i = 0;
-  for (int64_t r = r0; r < r1; ++r) {
-    const uint4* row = (const uint4*)(W + r * ldw);
+  for (int64_t base = c0 + tid; base < c1; base += PT * U) {
+    uint4 v[U];
+    if (base + (int64_t)(U - 1) * PT < c1) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = chunk_at<FLAT>(W, base + (int64_t)u * PT, kc, ldw);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = base + (int64_t)u * PT;
+        v[u] = c < c1 ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
+      }
+    }
     double acc = 0.0;
-    for (int c = tid; c < kc; c += PT) {
-      const uint4 v = row[c];
-      acc += pair_abs(v.x, hdr->bins) + pair_abs(v.y, hdr->bins) + pair_abs(v.z, hdr->bins) +
-             pair_abs(v.w, hdr->bins);
+    bool ok = true;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      acc += pair_abs(v[u].x, ok) + pair_abs(v[u].y, ok) + pair_abs(v[u].z, ok) + pair_abs(v[u].w, ok);
+    if (!ok) {
+      any_slow = 1;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        pair_slow(v[u].x, bins);
+        pair_slow(v[u].y, bins);
+        pair_slow(v[u].z, bins);
+        pair_slow(v[u].w, bins);
+      }
     }
     acc_i += (unsigned long long)(acc * FAST_SCALE);   // exact integer < 2^53
   }
-  __shared__ unsigned long long red[PT / 64];
-  __shared__ int is_last;
-  unsigned long long s = wave_sum_u64(acc_i);
+  const unsigned long long s = wave_sum_u64(acc_i);
   if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
   if (tid == 0) {
     unsigned long long b = 0;
     for (int i = 0; i < PT / 64; ++i) b += red[i];
-    partials[blockIdx.x] = (long long)b;
-    __threadfence();
-    is_last = (atomicAdd(&hdr->counter, 1u) == gridDim.x - 1);
+    pw.partials[blockIdx.x] = (long long)b;
+    pw.flags[blockIdx.x] = any_slow ? 1u : 0u;
   }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+  if (any_slow) pw.bins[(int64_t)blockIdx.x * 256 + tid] = bins[tid];
+}
 
-  // ---- finalize: the last block sums the partials and the bins
-  unsigned __int128 f = 0;
-  for (int64_t i = tid; i < (int64_t)gridDim.x; i += PT)
-    f += (unsigned long long)__atomic_load_n(&partials[i], __ATOMIC_RELAXED);
+// Block-wide (256 threads): total = sum of the pass-1 partials (2^-39 units)
+// + the flagged blocks' bins (sig * 2^(e-134) each), then
+// s_w = max(RN_fp32(total / numel), 1e-5).  Every pass-2 block forms it from
+// the <= a few hundred partials (the kernel boundary after pass 1 makes them
+// visible, so no device-scope fence is needed); block 0 also stores it.
+__device__ float scale_from_partials(const unsigned char* __restrict__ ws, int64_t nb, int64_t numel,
+                                     float* __restrict__ s_w_out) {
+  const PackWs pw = pack_ws((unsigned char*)ws, nb);
+  const int tid = threadIdx.x;
   __shared__ unsigned long long flo[PT], fhi[PT];
-  __shared__ unsigned long long sbins[256];
-  __shared__ unsigned long long nzmask[4];
+  __shared__ unsigned long long ebin[256];
+  __shared__ int nflag;
+  __shared__ int flagged[PT];
+  __shared__ float s_sh;
+  if (tid == 0) nflag = 0;
+  __syncthreads();
+  unsigned __int128 f = 0;
+  for (int64_t i = tid; i < nb; i += PT) {
+    f += (unsigned long long)pw.partials[i];
+    if (pw.flags[i]) {
+      const int slot = atomicAdd(&nflag, 1);
+      if (slot < PT) flagged[slot] = (int)i;
+    }
+  }
   flo[tid] = (unsigned long long)f;
   fhi[tid] = (unsigned long long)(f >> 64);
-  const unsigned long long b = __atomic_load_n(&hdr->bins[tid], __ATOMIC_RELAXED);
-  sbins[tid] = b;
-  const unsigned long long bal = __ballot(b != 0);
-  if ((tid & 63) == 0) nzmask[tid >> 6] = bal;
   __syncthreads();
+  unsigned long long eb = 0;                     // exponent bin `tid` over the flagged blocks (rare)
+  if (nflag > 0 && nflag <= PT) {
+    for (int j = 0; j < nflag; ++j) eb += pw.bins[(int64_t)flagged[j] * 256 + tid];
+  } else if (nflag > PT) {
+    for (int64_t i = 0; i < nb; ++i)
+      if (pw.flags[i]) eb += pw.bins[i * 256 + tid];
+  }
+  ebin[tid] = eb;
   for (int sh = PT / 2; sh > 0; sh >>= 1) {      // tree sum of the 128-bit partial sums
     if (tid < sh) {
       unsigned __int128 a = ((unsigned __int128)fhi[tid] << 64) | flo[tid];
@@ -226,17 +300,15 @@ __global__ __launch_bounds__(PT) void abs_sum_kernel(const uint16_t* __restrict_
     // fast part: F units of 2^-39 = F * 2^94 units of 2^-133
     big_add_shifted(t, (unsigned long long)F, 94);
     big_add_shifted(t, (unsigned long long)(F >> 64), 94 + 64);
-    for (int w = 0; w < 4; ++w) {
-      unsigned long long mk = nzmask[w];
-      while (mk) {
-        const int bit = __ffsll((long long)mk) - 1;
-        mk &= mk - 1;
-        const int e = w * 64 + bit;
-        big_add_shifted(t, sbins[e], (e ? e : 1) - 1);
-      }
-    }
-    *s_w = round_mean(t, (unsigned long long)(R * K));
+    if (nflag)
+      for (int e = 0; e < 256; ++e)
+        if (ebin[e]) big_add_shifted(t, ebin[e], (e ? e : 1) - 1);
+    const float sw = round_mean(t, (unsigned long long)numel);
+    s_sh = sw;
+    if (blockIdx.x == 0) *s_w_out = sw;
   }
+  __syncthreads();
+  return s_sh;
 }
 
 // ------------------------------------------------------------------ pass 2
@@ -244,14 +316,9 @@ __global__ __launch_bounds__(PT) void abs_sum_kernel(const uint16_t* __restrict_
 template <int M>
 __global__ __launch_bounds__(PT) void mask_pack_kernel(
     const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw, int n,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ meta, const float* __restrict__ s_w_ptr,
-    unsigned char* __restrict__ ws, int64_t total_chunks, int64_t dr, int64_t dch) {
-  if (blockIdx.x == 0) {   // leave the pass-1 header zeroed for the next call
-    PackHeader* hdr = (PackHeader*)ws;
-    hdr->bins[threadIdx.x] = 0;
-    if (threadIdx.x == 0) hdr->counter = 0;
-  }
-  const float h = 0.5f * (*s_w_ptr);
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ meta, float* __restrict__ s_w_ptr,
+    const unsigned char* __restrict__ ws, int64_t nb, int64_t total_chunks, int64_t dr, int64_t dch) {
+  const float h = 0.5f * scale_from_partials(ws, nb, R * K, s_w_ptr);
   const uint32_t thr = __float_as_uint(h) >> 16;      // |w| > h  <=>  key > thr
   const int64_t cpr = K / 32;
   const int64_t crow = K * n / (4 * M);               // code bytes per row
@@ -310,27 +377,94 @@ __global__ __launch_bounds__(PT) void mask_pack_kernel(
   }
 }
 
+// Pass 2 for 2:4 (the common case).  A 16-byte chunk of W (8 weights, two
+// groups) yields exactly one meta byte and one codes byte, both at the
+// chunk's flat index, so lanes take consecutive chunks (coalesced loads and
+// stores) with U loads in flight.  Per group the second-largest of four
+// distinct keys (|w| << 2 | 3 - p) is the threshold; the two keys at or above
+// it survive and their codes are picked with find-first-bit.
+__device__ inline void group24(uint32_t w01, uint32_t w23, uint32_t thr, uint32_t& keep4, uint32_t& code4) {
+  const uint32_t w[4] = {w01 & 0xFFFFu, w01 >> 16, w23 & 0xFFFFu, w23 >> 16};
+  uint32_t k[4], code8 = 0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t a = w[p] & 0x7FFFu;
+    k[p] = (a << 2) | (uint32_t)(3 - p);
+    const uint32_t nz = a > thr ? 1u : 0u;
+    code8 |= (nz | ((nz & (w[p] >> 15)) << 1)) << (2 * p);
+  }
+  const uint32_t hi01 = max(k[0], k[1]), lo01 = min(k[0], k[1]);
+  const uint32_t hi23 = max(k[2], k[3]), lo23 = min(k[2], k[3]);
+  const uint32_t second = max(min(hi01, hi23), max(lo01, lo23));
+  keep4 = (k[0] >= second ? 1u : 0u) | (k[1] >= second ? 2u : 0u) | (k[2] >= second ? 4u : 0u) |
+          (k[3] >= second ? 8u : 0u);
+  const uint32_t p0 = __builtin_ctz(keep4), p1 = 31u - __builtin_clz(keep4);
+  code4 = ((code8 >> (2 * p0)) & 3u) | (((code8 >> (2 * p1)) & 3u) << 2);
+}
+
+template <bool FLAT>
+__global__ __launch_bounds__(PT) void mask_pack24_kernel(
+    const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ meta, float* __restrict__ s_w_ptr, const unsigned char* __restrict__ ws,
+    int64_t nb) {
+  const int64_t kc = K / 8, total = R * kc;
+  int64_t base = (int64_t)blockIdx.x * PT * U + threadIdx.x;
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {                  // first loads fly while the scale is formed
+    const int64_t c = base + (int64_t)u * PT;
+    v[u] = c < total ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
+  }
+  const float h = 0.5f * scale_from_partials(ws, nb, R * K, s_w_ptr);
+  const uint32_t thr = __float_as_uint(h) >> 16;
+  while (true) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = base + (int64_t)u * PT;
+      if (c < total) {
+        uint32_t k0, c0, k1, c1;
+        group24(v[u].x, v[u].y, thr, k0, c0);
+        group24(v[u].z, v[u].w, thr, k1, c1);
+        meta[c] = (uint8_t)(k0 | (k1 << 4));
+        codes[c] = (uint8_t)(c0 | (c1 << 4));
+      }
+    }
+    base += (int64_t)gridDim.x * PT * U;
+    if (base >= total) break;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = base + (int64_t)u * PT;
+      v[u] = c < total ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
 }  // namespace
 
 PackPlan pack_plan(int64_t R, int64_t K) {
   PackPlan p;
-  int64_t nb = R < 2048 ? R : 2048;
-  int64_t rpb = cdiv(R, nb);
-  const int64_t max_rows = (int64_t(1) << 20) / K;   // keeps a block's int64 partial < 2^63
-  if (rpb > max_rows) rpb = max_rows;
-  if (rpb < 1) rpb = 1;
-  nb = cdiv(R, rpb);
+  const int64_t total = R * (K / 8);                    // 16-byte chunks
+  int64_t nb = cdiv(total, (int64_t)PT * U);
+  if (nb > 256) nb = 256;                               // pass 2 reduces one partial per thread
+  const int64_t max_cpb = (int64_t(1) << 20) / 8;       // a block's int64 partial stays < 2^63
+  int64_t cpb = cdiv(total, nb);
+  if (cpb > max_cpb) cpb = max_cpb;
+  nb = cdiv(total, cpb);
   p.nblocks = nb;
-  p.rows_per_block = rpb;
-  p.bytes = align256(sizeof(PackHeader) + (size_t)nb * 8);
+  p.chunks_per_block = cpb;
+  p.bytes = align256((size_t)nb * 8) + align256((size_t)nb * 4) + align256((size_t)nb * 256 * 8);
   return p;
 }
 
 hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
                        uint8_t* codes, uint8_t* meta, float* s_w, void* ws, hipStream_t st) {
   const PackPlan p = pack_plan(R, K);
-  SBN_LAUNCH("abs_sum", abs_sum_kernel, dim3((unsigned)p.nblocks), dim3(PT), 0, st, W, R, K, ldw,
-                     p.rows_per_block, (unsigned char*)ws, s_w);
+  if (ldw == K)
+    SBN_LAUNCH("abs_sum", abs_sum_kernel<true>, dim3((unsigned)p.nblocks), dim3(PT), 0, st, W, R, K, ldw,
+               p.chunks_per_block, (unsigned char*)ws);
+  else
+    SBN_LAUNCH("abs_sum", abs_sum_kernel<false>, dim3((unsigned)p.nblocks), dim3(PT), 0, st, W, R, K, ldw,
+               p.chunks_per_block, (unsigned char*)ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = R * (K / 32);
@@ -340,12 +474,22 @@ hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int
   const int64_t cpr = K / 32;
   const int64_t dr = stride / cpr, dch = stride % cpr;
   uint8_t* mp = (n == m) ? nullptr : meta;
-  if (m == 4)
+  if (n == 2 && m == 4) {
+    int64_t b24 = cdiv(R * (K / 8), (int64_t)PT * U);
+    if (b24 > 2048) b24 = 2048;
+    if (ldw == K)
+      SBN_LAUNCH("mask_pack", mask_pack24_kernel<true>, dim3((unsigned)b24), dim3(PT), 0, st, W, R, K, ldw,
+                 codes, mp, s_w, (const unsigned char*)ws, p.nblocks);
+    else
+      SBN_LAUNCH("mask_pack", mask_pack24_kernel<false>, dim3((unsigned)b24), dim3(PT), 0, st, W, R, K, ldw,
+                 codes, mp, s_w, (const unsigned char*)ws, p.nblocks);
+  }
+  else if (m == 4)
     SBN_LAUNCH("mask_pack", mask_pack_kernel<4>, dim3((unsigned)blocks), dim3(PT), 0, st, W, R, K, ldw,
-                       n, codes, mp, s_w, (unsigned char*)ws, total, dr, dch);
+                       n, codes, mp, s_w, (const unsigned char*)ws, p.nblocks, total, dr, dch);
   else
     SBN_LAUNCH("mask_pack", mask_pack_kernel<8>, dim3((unsigned)blocks), dim3(PT), 0, st, W, R, K, ldw,
-                       n, codes, mp, s_w, (unsigned char*)ws, total, dr, dch);
+                       n, codes, mp, s_w, (const unsigned char*)ws, p.nblocks, total, dr, dch);
   return hipGetLastError();
 }
 

@@ -49,11 +49,30 @@ __device__ inline void g2lds4(const void* g, void* lds_base) {
 }
 __device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// s_waitcnt with vmcnt = N (gfx9 encoding; expcnt and lgkmcnt left at "no wait")
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS hand-offs that leaves global loads in flight.
+// __syncthreads() carries a memory fence that waits for every outstanding
+// vector memory operation, which would drain the loads of later pipeline
+// stages; here each wave first waits for exactly the loads it must see
+// (wait_vmcnt) and for its own LDS reads, then meets the others.  The empty
+// asm statements keep the compiler from moving memory operations across.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ----------------------------------------------------------------- workspace layouts
 // Pack: [counter + pad: 256 B][bins: 256 x u64][partials: nblocks x i64]
 struct PackPlan {
   int64_t nblocks;
-  int64_t rows_per_block;
+  int64_t chunks_per_block;   // 16-byte chunks of W summed by one pass-1 block
   size_t bytes;
 };
 PackPlan pack_plan(int64_t R, int64_t K);

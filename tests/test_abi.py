@@ -135,9 +135,10 @@ def test_backward_validation(L):
 
 
 def test_profile_calls_without_launches(L):
-    assert L.sbn_profile_enable(1) == OK
+    assert L.sbn_profile_enable(1, None) == OK
+    assert L.sbn_profile_enable(1, b"gemm_smfmac") == OK
     assert L.sbn_profile_reset() == OK
     buf = ctypes.create_string_buffer(256)
     assert L.sbn_profile_dump(buf, 256) == OK and buf.value == b""
     assert L.sbn_profile_dump(None, 0) == NULL
-    assert L.sbn_profile_enable(0) == OK
+    assert L.sbn_profile_enable(0, None) == OK

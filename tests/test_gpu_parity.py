@@ -379,3 +379,49 @@ def test_backward_train_size_sampled():
     gW = dYf[:, rs].T @ Xh
     bW = np.abs(dYf[:, rs]).T @ np.abs(Xh)
     assert_abs_product(host(dW[torch.from_numpy(rs).cuda()]), gW, bW, "dW rows")
+
+
+# ------------------------------------------------------------------ HIP graph replay
+def test_graph_replays_match_eager():
+    """The forward step (pack, act_quant, GEMM) captured as a HIP graph: every
+    replay, with eager work and synchronisation between replays, reproduces
+    the eager results bit for bit (the bench times such replays)."""
+    import torch
+    T, R, K, n, m = 300, 520, 576, 2, 4
+    W = dev_bf16(gaussian_bf16((R, K), 0.02, seed=21, stream=0))
+    X = dev_bf16(gaussian_bf16((T, K), 1.0, seed=21, stream=1))
+    cb, mb = sbn.sbn_packed_bytes(R, K, n, m)
+    codes = torch.empty(cb, dtype=torch.uint8, device="cuda")
+    meta = torch.empty(mb, dtype=torch.uint8, device="cuda")
+    s_w = torch.empty(1, dtype=torch.float32, device="cuda")
+    Xq = torch.empty((T, K), dtype=torch.int8, device="cuda")
+    s_x = torch.empty(T, dtype=torch.float32, device="cuda")
+    Y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+    wsp = torch.empty(sbn.sbn_workspace_bytes(sbn.SBN_OP_PACK, 0, R, K, n, m), dtype=torch.uint8, device="cuda")
+    wsg = torch.empty(sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM, T, R, K, n, m), dtype=torch.uint8, device="cuda")
+
+    def step():
+        sbn.sbn_mask_ternarize_pack(W, n, m, codes=codes, meta=meta, s_w=s_w, ws=wsp)
+        sbn.sbn_act_quant(X, Xq=Xq, s_x=s_x)
+        sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, R, n, m, ydt=sbn.SBN_BF16, Y=Y, ws=wsg)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (codes, meta, s_w, Xq, s_x, Y)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (codes, meta, s_w, Xq, s_x, Y):
+            t.zero_()                               # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((codes, meta, s_w, Xq, s_x, Y), ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
