@@ -10,15 +10,26 @@
 //   * every other ratio (6:8, 4:8, 3:4, the dense 8:8 control, ...) runs on
 //     dense v_mfma_i32_16x16x64_i8 with W expanded to int8 {-1, 0, +1}.
 //
-// Two kernels per call: an expansion pass turns the packed planes into the
-// matrix-core operand order (one contiguous 1 KB fragment per 16 rows x K
-// block, so each lane later fetches 16 contiguous bytes), then the GEMM.
+// Three kernels per call.  Two layout passes put both operands in matrix-core
+// fragment order (one contiguous 1 KB block per 16 rows x 64 or 128 K, lane l's
+// 16 bytes at offset 16*l), so every load of the GEMM main loop is a
+// contiguous 1 KB global->LDS transfer and every LDS read a contiguous
+// 16-byte read:
+//   expand_sparse / expand_dense : packed codes + meta -> W fragments
+//   tile_x                       : Xq [T][K] row-major -> X fragments, zero padded
+// then the GEMM.
 //
-// GEMM tiling: 256 threads (4 waves in 2 x 2), block tile 256 rows x 256
-// tokens, wave tile 128 x 128 (8 x 8 accumulator tiles of 16 x 16 int32),
-// K step 128, two LDS stages filled with direct global->LDS loads, issued one
-// stage ahead.  The LDS image of every fragment is the lane order the matrix
-// instruction reads, so fragment reads are contiguous 16-byte LDS reads.
+// GEMM: 512 threads (8 waves), block tile 256 rows x 256 tokens, wave tile
+// 128 rows x 64 tokens (8 x 4 accumulator tiles of 16 x 16 int32); K step 128
+// (sparse, 3 LDS stages of 52 KB) or 64 (dense, 4 stages of 32 KB), stages
+// filled with direct global->LDS loads issued two (sparse) or three (dense)
+// steps ahead.  The two waves that share a SIMD (w and w + 4) alternate
+// between a memory phase (LDS reads of one step's fragments into registers,
+// plus the global loads of a later stage) and a compute phase (32 matrix
+// instructions), so one of them keeps the SIMD's matrix core busy while the
+// other waits on LDS.  Each block also prefetches into L2 its share of the
+// lines that the blocks running beside it on the same XCD will request a few
+// steps later.
 //
 // Operand layouts (gfx950, measured with a lane-layout check):
 //   16x16x64 i8 : A lane l -> row l%16, K[16*(l/16) .. +16); B lane l -> col l%16,
@@ -48,7 +59,8 @@ __device__ inline uint32_t read_bits(const uint8_t* p, int64_t off, int nbits) {
 __device__ inline int8_t code_to_i8(uint32_t c) { return c == 1u ? (int8_t)1 : c == 3u ? (int8_t)-1 : (int8_t)0; }
 
 // ---------------------------------------------------------------- expansion: sparse operand
-// one thread = one lane of one (16-row, 128-K) fragment: 16 values + 32 index bits
+// one thread = one lane of one (16-row, 128-K) fragment: 16 values + 32 index bits.
+// vals [RB][KBn][64][16 B]; idx [RB/4][KBn][64][4 x u32] (row fragment 4g+q in word q)
 __global__ __launch_bounds__(256) void expand_sparse_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, int64_t R, int64_t K,
     int n, int m, int64_t RB, int64_t KBn, uint8_t* __restrict__ vals, uint32_t* __restrict__ idx) {
@@ -117,7 +129,8 @@ __global__ __launch_bounds__(256) void expand_sparse_kernel(
   uint4 o;
   o.x = v32[0]; o.y = v32[1]; o.z = v32[2]; o.w = v32[3];
   ((uint4*)vals)[gid] = o;
-  idx[gid] = ix;
+  // index words of four consecutive row fragments share one 16-byte lane slot
+  idx[(((rb >> 2) * KBn + kb) * 64 + l) * 4 + (rb & 3)] = ix;
 }
 
 // ---------------------------------------------------------------- expansion: dense operand
@@ -152,6 +165,24 @@ __global__ __launch_bounds__(256) void expand_dense_kernel(
   ((uint4*)vals)[gid] = o;
 }
 
+// ---------------------------------------------------------------- activation fragments
+// Xt [TBp][KC][64][16 B]: block (tb, kc) holds tokens 16*tb.. and K bytes
+// 64*kc..; lane l carries token 16*tb + l%16, K bytes 64*kc + 16*(l/16) ..+16.
+// Tokens >= T and K >= K are zero.
+__global__ __launch_bounds__(256) void tile_x_kernel(const int8_t* __restrict__ Xq, int64_t T, int64_t K,
+                                                     int64_t TBp, int64_t KC, uint4* __restrict__ Xt) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= TBp * KC * 64) return;
+  const int l = (int)(gid & 63);
+  const int64_t f = gid >> 6;
+  const int64_t tb = f / KC, kc = f - tb * KC;
+  const int64_t t = tb * 16 + (l & 15);
+  const int64_t k = kc * 64 + 16 * (l >> 4);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (t < T && k < K) v = *(const uint4*)(Xq + t * K + k);
+  Xt[gid] = v;
+}
+
 // ---------------------------------------------------------------- GEMM
 // Tile order: blocks are dealt to the 8 XCDs round-robin; give each XCD a
 // contiguous run of tiles, and walk tiles in groups of 8 row tiles (token
@@ -169,53 +200,98 @@ __device__ inline void tile_of_block(int64_t b, int64_t ntR, int64_t ntT, int64_
   tt = j / gr;
 }
 
-// OUT: 0 = int32 accumulator, 1 = float32, 2 = bf16.  WR x WT waves, wave tile
-// (256/WR) rows x (256/WT) tokens.  SPARSE: K step 128 (smfmac), 3 stages;
-// dense: K step 64 (mfma 16x16x64), 4 stages.
-template <bool SPARSE, int OUT, int WR, int WT>
-__global__ __launch_bounds__(64 * WR * WT, 1) void gemm_kernel(
-    const uint8_t* __restrict__ Aw, const uint32_t* __restrict__ Ai, const int8_t* __restrict__ Xq,
-    const float* __restrict__ s_x, const float* __restrict__ s_w, int64_t T, int64_t K, int64_t R,
-    int64_t nks, int64_t fstride, void* __restrict__ Y, int64_t ldy) {
-  constexpr int NW = WR * WT;
-  constexpr int MI = 256 / WR / 16, MJ = 256 / WT / 16;          // fragments per wave
-  constexpr int A_BYTES = 16 * 1024;
-  constexpr int I_BYTES = SPARSE ? 16 * 256 : 0;
-  constexpr int BH = SPARSE ? 2 : 1;                              // B 1 KB halves per token block
+__device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// workgroup barrier kept in program order with the surrounding waits
+__device__ inline void pp_barrier() {
+  sched_fence();
+  asm volatile("s_barrier" ::: "memory");
+  sched_fence();
+}
+
+#ifndef SBN_GEMM_PF
+#define SBN_GEMM_PF 0
+#endif
+
+// OUT: 0 = int32 accumulator, 1 = float32, 2 = bf16.  PF: L2 prefetch distance
+// in steps beyond the stage being loaded (0 = none).
+template <bool SPARSE, int OUT, int PF>
+__global__ __launch_bounds__(512, 1) void gemm_kernel(
+    const uint8_t* __restrict__ Aw, const uint8_t* __restrict__ Ai, const uint8_t* __restrict__ Xt,
+    const float* __restrict__ s_x, const float* __restrict__ s_w, int64_t T, int64_t R,
+    int64_t nks, int64_t fstride, int64_t KC, void* __restrict__ Y, int64_t ldy) {
+  constexpr int NW = 8, MI = 8, MJ = 4;                // 8 waves; wave tile 8 x 4 fragments
+  constexpr int A_BYTES = 16 * 1024;                   // 16 row fragments
+  constexpr int I_BYTES = SPARSE ? 4 * 1024 : 0;       // their index words
+  constexpr int BH = SPARSE ? 2 : 1;                   // 1 KB X blocks per token block per step
   constexpr int B_BYTES = 16 * BH * 1024;
   constexpr int STAGE = A_BYTES + I_BYTES + B_BYTES;
   constexpr int NST = SPARSE ? 3 : 4;
-  constexpr int KS = SPARSE ? 128 : 64;
-  constexpr int LPS = (16 / NW) * (SPARSE ? 2 : 1) + (16 * BH) / NW;   // loads per stage per wave
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
+  // global loads per wave per stage: 2 W fragments, 4 (sparse) or 2 X blocks,
+  // the index block (waves 0..3, sparse), one prefetch
+  constexpr int LPS0 = 2 + (SPARSE ? 1 : 0) + 2 * BH + (PF ? 1 : 0);
+  constexpr int LPS1 = 2 + 2 * BH + (PF ? 1 : 0);
+  constexpr int WAIT0 = (NST - 2) * LPS0, WAIT1 = (NST - 2) * LPS1;
+  // L2 prefetch share of one block per step: a quarter of its row tile's lines
+  // and an eighth of its token tile's lines
+  constexpr int A_LINES = (A_BYTES + I_BYTES) / 128, B_LINES = B_BYTES / 128;
+  constexpr int PA = A_LINES / 4, PB = B_LINES / 8, PL = (PA + PB) / NW;
+  static_assert((PA + PB) % NW == 0, "prefetch share");
+  constexpr int EPI_BYTES = NW * 64 * 272;              // bf16 epilogue staging, 64 x 272 B per wave
+  constexpr int SMEM = (NST * STAGE + 256) > EPI_BYTES ? (NST * STAGE + 256) : EPI_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wr = wave / WT, wt = wave % WT;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int grp = wave >> 2;                           // waves w and w + 4 share a SIMD
+  const int wr = wave & 1, wt = wave >> 1;             // rows 128*wr.., tokens 64*wt..
   int64_t rtile, ttile;
   tile_of_block(blockIdx.x, cdiv(R, 256), cdiv(T, 256), rtile, ttile);
   const int64_t tile_r = rtile * 256, tile_t = ttile * 256;
-  const int64_t rb0 = tile_r / 16;
+  const int64_t rb0 = tile_r / 16, tb0 = tile_t / 16;
+
+  // scales for the epilogue, fetched before the main loop
+  float sw = 0.0f, sxv[MJ];
+#pragma unroll
+  for (int j = 0; j < MJ; ++j) {
+    const int64_t t = tile_t + 16 * (MJ * wt + j) + (lane & 15);
+    sxv[j] = (OUT != 0 && t < T) ? s_x[t] : 0.0f;
+  }
+  if (OUT != 0) sw = *s_w;
+
+  // prefetch line of this lane (lanes past the share repeat it)
+  const int pg = wave * PL + lane % PL;
+  const int pq = (int)(ttile & 3), pe = (int)(rtile & 7);
+  auto prefetch = [&](int64_t sp) {
+    sp = sp < nks ? sp : nks - 1;
+    const uint8_t* p;
+    if (pg < PA) {
+      const int L = pq * PA + pg;                      // line of the row tile's stage
+      if (L < A_BYTES / 128) p = Aw + ((rb0 + (L >> 3)) * fstride + sp) * 1024 + (L & 7) * 128;
+      else p = Ai + ((rb0 / 4 + ((L - A_BYTES / 128) >> 3)) * fstride + sp) * 1024 + (L & 7) * 128;
+    } else {
+      const int L = pe * PB + (pg - PA);               // line of the token tile's stage
+      const int per = BH * 8;                          // lines per token block per step
+      p = Xt + ((tb0 + L / per) * KC + sp * BH) * 1024 + (L % per) * 128;
+    }
+    g2lds4(p, smem + NST * STAGE);                     // lands in a scratch slot nobody reads
+  };
 
   auto load_stage = [&](int s, int64_t ks) {
     uint8_t* base = smem + s * STAGE;
 #pragma unroll
-    for (int q = 0; q < 16 / NW; ++q) {
+    for (int q = 0; q < 2; ++q) {
       const int i = wave + NW * q;
-      const int64_t frag = (rb0 + i) * fstride + ks;
-      g2lds16(Aw + frag * 1024 + lane * 16, base + i * 1024);
-      if (SPARSE) g2lds4(Ai + frag * 64 + lane, base + A_BYTES + i * 256);
+      g2lds16(Aw + ((rb0 + i) * fstride + ks) * 1024 + lane * 16, base + i * 1024);
     }
+    if (SPARSE && grp == 0)
+      g2lds16(Ai + ((rb0 / 4 + wave) * fstride + ks) * 1024 + lane * 16, base + A_BYTES + wave * 1024);
 #pragma unroll
-    for (int q = 0; q < (16 * BH) / NW; ++q) {
-      const int hb = wave + NW * q;                                  // half-block index
-      const int j = hb / BH, h = hb % BH;
-      int64_t t = tile_t + 16 * j + (lane & 15);
-      t = t < T ? t : T - 1;                      // rows past T are computed and discarded
-      int64_t k = ks * KS + 64 * h + 16 * (lane >> 4);
-      k = k < K ? k : K - 16;                     // W is zero past K, any finite bytes do
-      g2lds16(Xq + t * K + k, base + A_BYTES + I_BYTES + hb * 1024);
+    for (int q = 0; q < 2 * BH; ++q) {
+      const int hb = wave + NW * q;                    // 1 KB block: token block hb/BH, half hb%BH
+      g2lds16(Xt + ((tb0 + hb / BH) * KC + ks * BH + hb % BH) * 1024 + lane * 16,
+              base + A_BYTES + I_BYTES + hb * 1024);
     }
+    if (PF) prefetch(ks + PF);
   };
 
   v4i acc[MI][MJ];
@@ -223,58 +299,132 @@ __global__ __launch_bounds__(64 * WR * WT, 1) void gemm_kernel(
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < MJ; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+  v4i a[MI], blo[MJ], bhi[MJ];
+  int ix[MI];
 
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < nks) load_stage(s, s);
-
-  for (int64_t ks = 0; ks < nks; ++ks) {
-    if (ks + NST - 2 < nks) wait_vmcnt<(NST - 2) * LPS>();       // stage ks landed, later ones may fly
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (ks + NST - 1 < nks) load_stage((int)((ks + NST - 1) % NST), ks + NST - 1);
-    const uint8_t* base = smem + (ks % NST) * STAGE;
+  // memory phase of step s: issue the loads of stage s + NST - 1, read step s's fragments
+  auto mem_phase = [&](int64_t s) {
+    if (s + NST - 1 < nks) load_stage((int)((s + NST - 1) % NST), s + NST - 1);
+    const uint8_t* base = smem + (s % NST) * STAGE;
     const uint8_t* bb = base + A_BYTES + I_BYTES;
-    v4i blo[MJ], bhi[MJ];
 #pragma unroll
     for (int j = 0; j < MJ; ++j) {
       const int jj = MJ * wt + j;
       blo[j] = *(const v4i*)(bb + (jj * BH + 0) * 1024 + lane * 16);
       if (SPARSE) bhi[j] = *(const v4i*)(bb + (jj * BH + 1) * 1024 + lane * 16);
     }
-    v4i a = *(const v4i*)(base + (MI * wr) * 1024 + lane * 16);
-    int ix = SPARSE ? *(const int*)(base + A_BYTES + (MI * wr) * 256 + lane * 4) : 0;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      v4i an = a;
-      int ixn = ix;
-      if (i + 1 < MI) {                           // next A fragment in flight during these products
-        const int ii = MI * wr + i + 1;
-        an = *(const v4i*)(base + ii * 1024 + lane * 16);
-        if (SPARSE) ixn = *(const int*)(base + A_BYTES + ii * 256 + lane * 4);
+    for (int i = 0; i < MI; ++i) a[i] = *(const v4i*)(base + (MI * wr + i) * 1024 + lane * 16);
+    if (SPARSE) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const v4i v = *(const v4i*)(base + A_BYTES + (2 * wr + h) * 1024 + lane * 16);
+        ix[4 * h] = v[0]; ix[4 * h + 1] = v[1]; ix[4 * h + 2] = v[2]; ix[4 * h + 3] = v[3];
       }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  auto comp_phase = [&]() {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
         if (SPARSE) {
-          const v8i b = (v8i){blo[j][0], blo[j][1], blo[j][2], blo[j][3],
-                              bhi[j][0], bhi[j][1], bhi[j][2], bhi[j][3]};
-          acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, acc[i][j], ix, 0, 0);
+          const v8i b = (v8i){blo[j][0], blo[j][1], blo[j][2], blo[j][3], bhi[j][0], bhi[j][1], bhi[j][2], bhi[j][3]};
+          acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a[i], b, acc[i][j], ix[i], 0, 0);
         } else {
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, blo[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], blo[j], acc[i][j], 0, 0, 0);
         }
       }
-      a = an;
-      ix = ixn;
+  };
+  // this wave's loads of stage s + 1 have landed (later stages may still fly)
+  auto vm_wait = [&](int64_t s) {
+    sched_fence();
+    if (s + NST - 1 < nks) {
+      if (grp == 0) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(WAIT0) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(WAIT1) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    sched_fence();
+  };
+
+  // Barrier schedule (B0, B1, ... in order; both groups pass the same count):
+  //   group 0: B0 | mem(s) B(2s+1) comp(s) wait B(2s+2) | ...
+  //   group 1: B0 B1 | mem(s) wait B(2s+2) comp(s) B(2s+3) | ... (no barrier after its last comp)
+  // so phase (B(2s+1), B(2s+2)) is comp(s) of group 0 beside mem(s) of group 1,
+  // and phase (B(2s+2), B(2s+3)) is comp(s) of group 1 beside mem(s+1) of group 0.
+  // Stage s is complete before B(2s) and read only between B(2s) and B(2s+2);
+  // its buffer is refilled (stage s + NST) from mem(s+1), after B(2s+2).
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nks) load_stage(s, s);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  pp_barrier();                                        // B0: stages 0 .. NST-2 visible
+  if (grp == 0) {
+    for (int64_t s = 0; s < nks; ++s) {
+      mem_phase(s);
+      pp_barrier();
+      comp_phase();
+      vm_wait(s);
+      pp_barrier();
+    }
+  } else {
+    pp_barrier();
+    for (int64_t s = 0; s < nks; ++s) {
+      mem_phase(s);
+      vm_wait(s);
+      pp_barrier();
+      comp_phase();
+      if (s + 1 < nks) pp_barrier();
     }
   }
 
-  // epilogue: lane holds rows r..r+3 of token t
-  const float sw = (OUT != 0) ? *s_w : 0.0f;
+  if (OUT == 2) {
+    // bf16: stage the wave's 128 x 64 tile through LDS as [token][row] (pitch
+    // 272 B keeps the 8-byte writes of 16 tokens on distinct banks), then store
+    // four token rows of 256 contiguous bytes per instruction, non-temporal so
+    // the output streams past L2 instead of evicting operands other blocks
+    // still read.  All LDS stages are free here: every wave passed its last
+    // stage read before B(2*nks).
+    constexpr int PITCH = 272;
+    static_assert(NW * 64 * PITCH <= SMEM, "epilogue staging fits");
+    uint8_t* st = smem + wave * (64 * PITCH);
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) {
+      const float sc = sw * sxv[j];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const v4i c = acc[i][j];
+        uint2 v;
+        v.x = (uint32_t)f32_to_bf16_rne((float)c[0] * sc) | ((uint32_t)f32_to_bf16_rne((float)c[1] * sc) << 16);
+        v.y = (uint32_t)f32_to_bf16_rne((float)c[2] * sc) | ((uint32_t)f32_to_bf16_rne((float)c[3] * sc) << 16);
+        *(uint2*)(st + (16 * j + (lane & 15)) * PITCH + (16 * i + 4 * (lane >> 4)) * 2) = v;
+      }
+    }
+    const int64_t r0 = tile_r + 128 * wr + 8 * (lane & 15);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int tl = 4 * q + (lane >> 4);
+      const int64_t t = tile_t + 64 * wt + tl;
+      const v4i v = *(const v4i*)(st + tl * PITCH + (lane & 15) * 16);
+      if (t >= T || r0 >= R) continue;
+      uint16_t* y = (uint16_t*)Y + t * ldy + r0;
+      if (r0 + 7 < R) {
+        __builtin_nontemporal_store(v, (v4i*)y);
+      } else {
+        const uint32_t w[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+        for (int e = 0; e < 8 && r0 + e < R; ++e) y[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    return;
+  }
+  // int32 / float32 epilogue: lane holds rows r..r+3 of token t, 16 bytes
 #pragma unroll
   for (int j = 0; j < MJ; ++j) {
     const int64_t t = tile_t + 16 * (MJ * wt + j) + (lane & 15);
     if (t >= T) continue;
-    const float sc = (OUT != 0) ? sw * s_x[t] : 0.0f;
+    const float sc = (OUT != 0) ? sw * sxv[j] : 0.0f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int64_t r = tile_r + 16 * (MI * wr + i) + 4 * (lane >> 4);
@@ -284,46 +434,33 @@ __global__ __launch_bounds__(64 * WR * WT, 1) void gemm_kernel(
         int* y = (int*)Y + t * ldy + r;
         if (r + 3 < R) *(v4i*)y = c;
         else for (int v = 0; v < 4 && r + v < R; ++v) y[v] = c[v];
-      } else if (OUT == 1) {
+      } else {
         float* y = (float*)Y + t * ldy + r;
         const v4f o = (v4f){(float)c[0] * sc, (float)c[1] * sc, (float)c[2] * sc, (float)c[3] * sc};
         if (r + 3 < R) *(v4f*)y = o;
         else for (int v = 0; v < 4 && r + v < R; ++v) y[v] = o[v];
-      } else {
-        uint16_t* y = (uint16_t*)Y + t * ldy + r;
-        const uint16_t o0 = f32_to_bf16_rne((float)c[0] * sc), o1 = f32_to_bf16_rne((float)c[1] * sc);
-        const uint16_t o2 = f32_to_bf16_rne((float)c[2] * sc), o3 = f32_to_bf16_rne((float)c[3] * sc);
-        if (r + 3 < R) store_u16x4(y, o0, o1, o2, o3);
-        else {
-          const uint16_t o[4] = {o0, o1, o2, o3};
-          for (int v = 0; v < 4 && r + v < R; ++v) y[v] = o[v];
-        }
       }
     }
   }
 }
 
-// wave layouts: 8 waves of 128 x 64 (default; two waves per SIMD hide LDS latency) or 4 of 128 x 128
-#ifndef SBN_GEMM_WT
-#define SBN_GEMM_WT 4
-#endif
-
 template <bool SPARSE>
-hipError_t launch_gemm_t(const uint8_t* Aw, const uint32_t* Ai, const int8_t* Xq, const float* s_x,
+hipError_t launch_gemm_t(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
                          const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y,
                          sbn_dtype ydt, int64_t ldy, hipStream_t st) {
-  constexpr int WR = 2, WT = SBN_GEMM_WT;
+  constexpr int PF = SBN_GEMM_PF;
   const int64_t ntiles = cdiv(T, GEMM_TILE_T) * cdiv(R, GEMM_TILE_R);
-  const dim3 grid((unsigned)ntiles), block(64 * WR * WT);
+  const dim3 grid((unsigned)ntiles), block(512);
   const int64_t nks = SPARSE ? KBn : K / 64;
   const int64_t fstride = SPARSE ? KBn : 2 * KBn;
+  const int64_t KC = 2 * KBn;
   const char* name = SPARSE ? "gemm_smfmac" : "gemm_mfma";
   if (ydt == SBN_I32_ACC)
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 0, WR, WT>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, nks, fstride, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 0, PF>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
   else if (ydt == SBN_F32)
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 1, WR, WT>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, nks, fstride, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 1, PF>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
   else
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 2, WR, WT>), grid, block, 0, st, Aw, Ai, Xq, s_x, s_w, T, K, R, nks, fstride, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 2, PF>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
   return hipGetLastError();
 }
 
@@ -332,36 +469,59 @@ hipError_t launch_gemm_t(const uint8_t* Aw, const uint32_t* Ai, const int8_t* Xq
 bool gemm_uses_smfmac(int n, int m) { return n <= 2 && (m == 4 || m == 8); }
 
 static int64_t gemm_rb(int64_t R) { return round_up(R, GEMM_TILE_R) / 16; }
+static int64_t gemm_tbp(int64_t T) { return round_up(T, GEMM_TILE_T) / 16; }
 
-size_t gemm_ws_bytes(int64_t /*T*/, int64_t R, int64_t K, int n, int m) {
+// [W fragments][index blocks (sparse)][X fragments]
+struct GemmWs {
+  size_t w_bytes, i_bytes, x_bytes;
+};
+static GemmWs gemm_ws(int64_t T, int64_t R, int64_t K, int n, int m) {
   const int64_t RB = gemm_rb(R), KBn = cdiv(K, 128);
-  if (gemm_uses_smfmac(n, m))
-    return align256((size_t)(RB * KBn * 1024)) + align256((size_t)(RB * KBn * 256));
-  return align256((size_t)(RB * KBn * 2 * 1024));
+  GemmWs g;
+  g.w_bytes = align256((size_t)(RB * KBn * 2048));                 // sparse: vals use the first half
+  if (gemm_uses_smfmac(n, m)) {
+    g.w_bytes = align256((size_t)(RB * KBn * 1024));
+    g.i_bytes = align256((size_t)(RB * KBn * 256));
+  } else {
+    g.i_bytes = 0;
+  }
+  g.x_bytes = align256((size_t)(gemm_tbp(T) * KBn * 2 * 1024));
+  return g;
+}
+
+size_t gemm_ws_bytes(int64_t T, int64_t R, int64_t K, int n, int m) {
+  const GemmWs g = gemm_ws(T, R, K, n, m);
+  return g.w_bytes + g.i_bytes + g.x_bytes;
 }
 
 hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                        const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
                        int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, void* ws, hipStream_t st) {
-  const int64_t RB = gemm_rb(R), KBn = cdiv(K, 128);
+  const int64_t RB = gemm_rb(R), KBn = cdiv(K, 128), TBp = gemm_tbp(T), KC = 2 * KBn;
+  const GemmWs g = gemm_ws(T, R, K, n, m);
   uint8_t* w = (uint8_t*)ws;
+  uint8_t* xt = w + g.w_bytes + g.i_bytes;
+  SBN_LAUNCH("tile_x", tile_x_kernel, dim3((unsigned)cdiv(TBp * KC * 64, 256)), dim3(256), 0, st,
+             Xq, T, K, TBp, KC, (uint4*)xt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (gemm_uses_smfmac(n, m)) {
     uint8_t* vals = w;
-    uint32_t* idx = (uint32_t*)(w + align256((size_t)(RB * KBn * 1024)));
+    uint32_t* idx = (uint32_t*)(w + g.w_bytes);
     const int64_t threads = RB * KBn * 64;
     SBN_LAUNCH("expand_sparse", expand_sparse_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st,
-                       codes, meta, R, K, n, m, RB, KBn, vals, idx);
-    hipError_t e = hipGetLastError();
+               codes, meta, R, K, n, m, RB, KBn, vals, idx);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_gemm_t<true>(vals, idx, Xq, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+    return launch_gemm_t<true>(vals, (const uint8_t*)idx, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
   }
   const int64_t KD = 2 * KBn;
   const int64_t threads = RB * KD * 64;
   SBN_LAUNCH("expand_dense", expand_dense_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st,
-                     codes, meta, R, K, n, m, RB, KD, w);
-  hipError_t e = hipGetLastError();
+             codes, meta, R, K, n, m, RB, KD, w);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_gemm_t<false>(w, nullptr, Xq, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+  return launch_gemm_t<false>(w, nullptr, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
 }
 
 }  // namespace sbn

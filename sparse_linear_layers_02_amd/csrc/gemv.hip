@@ -3,48 +3,58 @@
 //
 // The pages measure decode on a custom sparse kernel ("Sparse-BitNet",
 // gist.science Japanese "技術概要" §3.2: B200 decode; Korean "기술 요약" §4).
-// Here the sixteen-wide int8 matrix instruction v_mfma_i32_16x16x64_i8 takes
-// 16 weight rows against the (up to) 16 tokens, so the arithmetic is never
-// the limit; the cost is reading the packed planes and turning them into
-// int8 operands.
+// Here a sixteen-wide int8 matrix instruction takes 16 weight rows against
+// the (up to) 16 tokens, so the arithmetic is never the limit; the cost is
+// reading the packed planes and turning them into int8 operands.
 //
-// Unpacking: a 4096-entry table in LDS maps (4 meta bits, the next 8 code
-// bits) to the four int8 weights {-1, 0, +1} of those positions (unused code
-// bits are ignored).  Every group of four positions is one table read.
+// Work split: a block (4 waves) handles groups of 16 output rows, walking the
+// row groups with a grid stride (the decode table below is built once per
+// block).  K is cut into ranges of 1024 positions; a wave takes ranges wave,
+// wave+4, ...  The K order inside a range is free (a dot product does not
+// care), so every lane group g = l/16 owns one contiguous run of the range,
+// which makes its meta and code bits one contiguous read of up to 64 bytes;
+// the matrix instruction only needs A lane (r, g) and B lane (t, g) to name
+// the same positions, and the activation bytes of each B lane are picked to
+// match.  The waves' 16 x 16 partial sums are added in LDS.
 //
-// Work split: one block (8 waves) per 16 output rows.  K is cut into ranges of
-// 512 positions; a wave takes ranges wave, wave+8, ...  Inside a range, lane
-// l (row l%16, part g = l/16) owns a contiguous run of 16*S positions, so its
-// meta and code bits are contiguous; the matrix instruction only needs A lane
-// (r, g) and B lane (t, g) to cover the same positions, which they do.  The
-// waves' 16x16 partial sums are added in LDS.  All loads of a wave's first
-// range (packed bits and activations) are issued before the block copies the
-// unpack table and synchronises, so the three fetches overlap.
+//   2:4   v_smfmac_i32_16x16x128_i8: up to eight steps of 128 positions per
+//         range; lane group g's run is 32 positions per step.  Each 32-bit
+//         meta word (8 groups) and the matching 32-bit code word (2 survivors
+//         x 2 bits per group) become the 16 compressed int8 values and the
+//         2-bit position indices with a few shifts and masks (no table).
+//   other v_mfma_i32_16x16x64_i8: up to sixteen steps of 64 positions per
+//         range, W expanded to int8 {-1, 0, +1} through a 4096-entry table in
+//         LDS that maps (4 meta bits, the next 8 code bits) to the four weights
+//         of those positions (unused code bits are ignored); each block
+//         computes the table while its first loads are in flight.
 #include "sbn_internal.h"
 
 namespace sbn {
 namespace {
 
-struct UnpackTable {
-  uint32_t v[4096];
-  constexpr UnpackTable() : v() {
-    for (int nib = 0; nib < 16; ++nib)
-      for (int c8 = 0; c8 < 256; ++c8) {
-        uint32_t out = 0;
-        int cur = 0;
-        for (int p = 0; p < 4; ++p)
-          if ((nib >> p) & 1) {
-            const int c = (c8 >> (2 * cur)) & 3;
-            ++cur;
-            const uint32_t b = c == 1 ? 0x01u : c == 3 ? 0xFFu : 0u;
-            out |= b << (8 * p);
-          }
-        v[nib | (c8 << 4)] = out;
-      }
-  }
-};
+#ifndef SBN_GV_WAVES
+#define SBN_GV_WAVES 4
+#endif
+constexpr int GV_WAVES = SBN_GV_WAVES;  // waves per block
+constexpr int GV_RANGE = 4096 / GV_WAVES;   // K positions per wave range
+static_assert(GV_RANGE % 128 == 0 && GV_WAVES * 256 <= 4096, "GEMV range");
+constexpr int GV_MAX_BLOCKS = 2048;    // grid-stride cap (8 blocks per CU)
 
-__device__ const UnpackTable kUnpack;
+// Unpack table entry e = nib | (c8 << 4): the four int8 weights of a group of
+// four positions whose meta bits are `nib` and whose survivors' 2-bit codes
+// start at the low end of `c8`.  The codes are spread to one byte each
+// (01 -> +1, 11 -> -1, 00 -> 0), then byte k of the entry takes survivor
+// number popcount(nib & ((1 << k) - 1)) if bit k of nib is set, else 0.
+__device__ inline uint32_t unpack_entry(uint32_t e) {
+  const uint32_t nib = e & 15u, c8 = (e >> 4) & 0xFFu;
+  const uint32_t sp = (((c8 & 0x33u) * 0x1001u) & 0x00030003u) | (((c8 & 0xCCu) * 0x40040u) & 0x03000300u);
+  const uint32_t v = sp | ((sp & 0x02020202u) * 0x7Eu);           // survivors, one per byte, in order
+  const uint32_t t = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);   // byte k = bit k
+  const uint32_t pre = t * 0x01010100u;                            // byte k = set bits below k
+  const uint32_t msk = t * 0xFFu;
+  const uint32_t sel = (pre & msk) | (0x0C0C0C0Cu & ~msk);        // byte select; 0x0C yields 0
+  return __builtin_amdgcn_perm(0u, v, sel);
+}
 
 // bits [off, off+nb) of the normalised word array (off, nb compile-time after unrolling)
 template <int NW>
@@ -55,9 +65,181 @@ __device__ inline uint32_t bits_at(const uint32_t (&w)[NW], int off, int nb) {
   return nb >= 32 ? v : (v & ((1u << nb) - 1u));
 }
 
-constexpr int GV_WAVES = 8;            // waves per block (one block per 16 output rows)
-constexpr int GV_RANGE = 512;          // K positions per wave range: 8 MFMA steps of 64
+// add the waves' 16 x 16 partial sums in LDS and write rows x tokens; thread
+// tid < 256 writes element tid (token (tid/4)%16), whose scale sxo it loaded early
+template <int OUT>
+__device__ inline void gemv_finish(int (*red)[256], v4i acc, int tid, int wave, int lane, int64_t row0,
+                                   int64_t T, int64_t R, float sc, void* Y, int64_t ldy) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[wave][lane * 4 + v] = acc[v];
+  __syncthreads();
+  if (tid < 256) {
+    const int e = tid;
+    int s = 0;
+#pragma unroll
+    for (int w = 0; w < GV_WAVES; ++w) s += red[w][e];
+    const int L = e >> 2, v = e & 3;
+    const int64_t row = row0 + 4 * (L >> 4) + v;
+    const int64_t t = L & 15;
+    if (t < T && row < R) {
+      if (OUT == 0) {
+        ((int*)Y)[t * ldy + row] = s;
+      } else {
+        const float y = (float)s * sc;
+        if (OUT == 1) ((float*)Y)[t * ldy + row] = y;
+        else ((uint16_t*)Y)[t * ldy + row] = f32_to_bf16_rne(y);
+      }
+    }
+  }
+  __syncthreads();                                     // red is reused by the next row group
+}
 
+// s_w * s_x[t] for the output element this thread writes in gemv_finish
+template <int OUT>
+__device__ inline float gemv_out_scale(int tid, int64_t T, const float* s_x, const float* s_w) {
+  const int64_t t = (tid >> 2) & 15;
+  return (OUT != 0 && tid < 256 && t < T) ? *s_w * s_x[t] : 0.0f;
+}
+
+// ----------------------------------------------------------------------------- 2:4
+// One 32-position slice of a row: meta word mb (8 groups of 4 bits, two set)
+// and code word cb (16 survivors x 2 bits, in position order) -> the 16
+// compressed int8 values and the sixteen 2-bit position indices of
+// v_smfmac_i32_16x16x128_i8's A operand.
+__device__ inline void decode24(uint32_t mb, uint32_t cb, v4i& a, int& ix) {
+  // indices, per nibble (m3 m2 m1 m0, two bits set): p0 = lowest set bit,
+  // p1 = highest; p0 = (m1 & ~m0) + 2 (~m1 & ~m0), p1 = (m3 | ~m2) + 2 (m3 | m2),
+  // each bit formed in place from the word shifted by one position
+  const uint32_t L = mb << 1, Rr = mb >> 1, lx = L | mb;
+  ix = (int)((~mb & Rr & 0x11111111u) | (~lx & 0x22222222u) | ((Rr | ~mb) & 0x44444444u) | (lx & 0x88888888u));
+  // values: plane q holds, in byte d, the code of survivor 4d+q, turned into its
+  // int8 weight by a byte permute against the table {00 -> 0, 01 -> +1, 11 -> -1};
+  // words d and d+1 gather byte d and d+1 of the four planes
+  constexpr uint32_t TAB = 0xFF000100u;
+  const uint32_t e0 = __builtin_amdgcn_perm(0u, TAB, cb & 0x03030303u);
+  const uint32_t o1 = __builtin_amdgcn_perm(0u, TAB, (cb >> 2) & 0x03030303u);
+  const uint32_t e2 = __builtin_amdgcn_perm(0u, TAB, (cb >> 4) & 0x03030303u);
+  const uint32_t o3 = __builtin_amdgcn_perm(0u, TAB, (cb >> 6) & 0x03030303u);
+#pragma unroll
+  for (int d = 0; d < 4; d += 2) {
+    const uint32_t sel = ((uint32_t)(d + 5) << 24) | ((uint32_t)(d + 1) << 16) | ((uint32_t)(d + 4) << 8) | (uint32_t)d;
+    const uint32_t lo = __builtin_amdgcn_perm(o1, e0, sel);   // [e0_d, o1_d, e0_d+1, o1_d+1]
+    const uint32_t hi = __builtin_amdgcn_perm(o3, e2, sel);
+    a[d] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    a[d + 1] = (int)__builtin_amdgcn_perm(hi, lo, 0x07060302u);
+  }
+}
+
+// Range of 128*S positions (S <= SMAX steps); lane group g's run is positions
+// kbeg + 32*S*g + [0, 32*S), i.e. one meta word and one code word per step.
+// Step s maps the instruction's logical K index q (0..127) to position
+// kbeg + 32*S*(q/32) + 32*s + q%32.
+template <int OUT>
+__global__ __launch_bounds__(64 * GV_WAVES) void gemv24_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, const float* __restrict__ s_w,
+    int64_t R, void* __restrict__ Y, int64_t ldy) {
+  constexpr int SMAX = GV_RANGE / 128;
+  __shared__ int red[GV_WAVES][256];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, rl = lane & 15;
+  const bool tvalid = rl < T;
+  const int8_t* xrow = Xq + (tvalid ? rl : 0) * K;
+  const int64_t nranges = cdiv(K, GV_RANGE), nrg = cdiv(R, 16);
+  const int gb2 = g >> 1, gb1 = g & 1;
+  const float sc = gemv_out_scale<OUT>(tid, T, s_x, s_w);
+
+  // packed words of the lane group's run in range ri of row group rg (2:4: the
+  // meta and code planes both hold one bit per position)
+  auto load_w = [&](int64_t rg, int64_t ri, int S, uint32_t (&mw)[SMAX], uint32_t (&cw)[SMAX]) {
+    const int64_t r = rg * 16 + rl;
+    const int64_t rr = r < R ? r : R - 1;             // rows past R: computed on row R-1, discarded
+    const uint32_t* mrow = (const uint32_t*)(meta + rr * (K / 8));
+    const uint32_t* crow = (const uint32_t*)(codes + rr * (K / 8));
+    const int64_t w0 = ri * (GV_RANGE / 32) + (int64_t)S * g;
+    if (SMAX % 4 == 0 && S == SMAX) {
+#pragma unroll
+      for (int h = 0; h < SMAX / 4; ++h) {
+        const v4i x = *(const v4i*)(mrow + w0 + 4 * h), y = *(const v4i*)(crow + w0 + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { mw[4 * h + i] = (uint32_t)x[i]; cw[4 * h + i] = (uint32_t)y[i]; }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < SMAX; ++i) {
+        mw[i] = i < S ? mrow[w0 + i] : 0u;
+        cw[i] = i < S ? crow[w0 + i] : 0u;
+      }
+    }
+  };
+  auto load_x = [&](int64_t ri, int S, v4i (&blo)[SMAX], v4i (&bhi)[SMAX]) {
+    const int64_t kbeg = ri * GV_RANGE;
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      const int64_t lo = kbeg + 32 * (int64_t)S * gb2 + 32 * s + 16 * gb1;
+      const bool ok = tvalid && s < S;
+      blo[s] = ok ? *(const v4i*)(xrow + lo) : (v4i){0, 0, 0, 0};
+      bhi[s] = ok ? *(const v4i*)(xrow + lo + 64 * (int64_t)S) : (v4i){0, 0, 0, 0};
+    }
+  };
+  auto steps = [&](int S, const uint32_t (&mw)[SMAX], const uint32_t (&cw)[SMAX], const v4i (&blo)[SMAX],
+                   const v4i (&bhi)[SMAX], v4i acc) {
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      if (s < S) {
+        v4i a;
+        int ix;
+        decode24(mw[s], cw[s], a, ix);
+        const v8i b = (v8i){blo[s][0], blo[s][1], blo[s][2], blo[s][3], bhi[s][0], bhi[s][1], bhi[s][2], bhi[s][3]};
+        acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, acc, ix, 0, 0);
+      }
+    }
+    return acc;
+  };
+  auto range_steps = [&](int64_t ri) {
+    const int S = (int)((K - ri * GV_RANGE) / 128 < SMAX ? (K - ri * GV_RANGE) / 128 : SMAX);
+    return S;
+  };
+
+  if (nranges <= GV_WAVES) {
+    // K fits one range per wave: the activations stay in registers for every
+    // row group, and the next row group's packed words load during this one's math
+    const bool has = wave < nranges;
+    const int S = has ? range_steps(wave) : 0;
+    v4i blo[SMAX], bhi[SMAX];
+    load_x(wave, S, blo, bhi);
+    uint32_t mw[SMAX], cw[SMAX];
+    int64_t rg = blockIdx.x;
+    if (has) load_w(rg, wave, S, mw, cw);
+    for (; rg < nrg; rg += gridDim.x) {
+      uint32_t m0[SMAX], c0[SMAX];
+#pragma unroll
+      for (int i = 0; i < SMAX; ++i) { m0[i] = mw[i]; c0[i] = cw[i]; }
+      if (has && rg + gridDim.x < nrg) load_w(rg + gridDim.x, wave, S, mw, cw);
+      const v4i acc = steps(S, m0, c0, blo, bhi, (v4i){0, 0, 0, 0});
+      gemv_finish<OUT>(red, acc, tid, wave, lane, rg * 16, T, R, sc, Y, ldy);
+    }
+  } else {
+    for (int64_t rg = blockIdx.x; rg < nrg; rg += gridDim.x) {
+      v4i acc = (v4i){0, 0, 0, 0};
+      for (int64_t ri = wave; ri < nranges; ri += GV_WAVES) {
+        const int S = range_steps(ri);
+        uint32_t mw[SMAX], cw[SMAX];
+        v4i blo[SMAX], bhi[SMAX];
+        load_w(rg, ri, S, mw, cw);
+        load_x(ri, S, blo, bhi);
+        acc = steps(S, mw, cw, blo, bhi, acc);
+      }
+      gemv_finish<OUT>(red, acc, tid, wave, lane, rg * 16, T, R, sc, Y, ldy);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- table path
+// Range of 64*S positions (S <= SMAX steps); lane group g's run is positions
+// p0 = kbeg + 16*S*g + [0, 16*S); step j takes positions p0 + 16*j .. +16 as
+// A lane (r, g) and the same activation bytes as B lane (t, g).
 template <int N, int M, int OUT>
 __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K,
@@ -71,60 +253,59 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, rl = lane & 15;
-  const int64_t r = (int64_t)blockIdx.x * 16 + rl;
-  const int64_t rr = r < R ? r : R - 1;               // rows past R: computed on row R-1, discarded
   const bool tvalid = rl < T;
-  const int64_t tt = tvalid ? rl : 0;                 // B column of this lane (token)
-  const int64_t crow = K * N / (4 * M);
-  const uint8_t* mrow = meta ? meta + rr * (K / 8) : nullptr;
-  const uint8_t* crw = codes + rr * crow;
-  const int8_t* xrow = Xq + tt * K;
-  const int64_t nranges = cdiv(K, GV_RANGE);
+  const int8_t* xrow = Xq + (tvalid ? rl : 0) * K;
+  const int64_t crow_bytes = K * N / (4 * M);
+  const int64_t nranges = cdiv(K, GV_RANGE), nrg = cdiv(R, 16);
+  const float sc = gemv_out_scale<OUT>(tid, T, s_x, s_w);
 
-  v4i acc = (v4i){0, 0, 0, 0};
-  bool first = true;
-  for (int64_t ri = wave; ri < nranges || first; ri += GV_WAVES) {
-    const bool active = ri < nranges;
-    const int64_t kbeg = ri * GV_RANGE;
-    int S = active ? (int)((K - kbeg) / 64) : 0;
-    S = S < SMAX ? S : SMAX;
-    const int64_t p0 = kbeg + 16 * (int64_t)g * S;    // this lane's run: 16*S positions
-
-    // ---- issue every load of this range before anything waits
-    uint32_t mw[SMAX / 2 + 1];
+  // packed bits of the lane group's run in range ri of row group rg: meta
+  // words (16 bits per step) and the code words that cover the run, as read
+  // (aligned down to 4 bytes; `sh` is the bit offset of the run in raw[0])
+  struct Packed {
+    uint32_t mw[SMAX / 2];
+    uint32_t raw[NWC + 1];
+    int sh;
+  };
+  auto load_w = [&](int64_t rg, int64_t ri, int S, Packed& P) {
+    const int64_t r = rg * 16 + rl;
+    const int64_t rr = r < R ? r : R - 1;             // rows past R: computed on row R-1, discarded
+    const int64_t p0 = ri * GV_RANGE + 16 * (int64_t)g * S;
 #pragma unroll
-    for (int i = 0; i < SMAX / 2 + 1; ++i) mw[i] = 0;
-    if (N < M && active) {
-      const uint16_t* mh = (const uint16_t*)(mrow + p0 / 8);
+    for (int i = 0; i < SMAX / 2; ++i) P.mw[i] = 0;
+    if (N < M && S > 0) {
+      const uint8_t* mrow = meta + rr * (K / 8);
+      if ((S & 1) == 0) {                              // run starts on a 4-byte boundary
+        const uint32_t* mp = (const uint32_t*)(mrow + p0 / 8);
 #pragma unroll
-      for (int i = 0; i < SMAX; ++i)
-        if (i < S) mw[i >> 1] |= (uint32_t)mh[i] << (16 * (i & 1));
+        for (int i = 0; i < SMAX / 2; ++i)
+          if (2 * i < S) P.mw[i] = mp[i];
+      } else {
+        const uint16_t* mh = (const uint16_t*)(mrow + p0 / 8);
+#pragma unroll
+        for (int i = 0; i < SMAX; ++i)
+          if (i < S) P.mw[i >> 1] |= (uint32_t)mh[i] << (16 * (i & 1));
+      }
     }
     const int64_t cbit = CB_NUM * (p0 / M);
-    const uintptr_t ca = (uintptr_t)(crw + (cbit >> 3));
+    const uintptr_t ca = (uintptr_t)(codes + rr * crow_bytes + (cbit >> 3));
     const uint32_t* cw4 = (const uint32_t*)(ca & ~(uintptr_t)3);
-    const int sh = (int)((ca & 3) * 8 + (cbit & 7));
+    P.sh = (int)((ca & 3) * 8 + (cbit & 7));
     const int nbits = 32 * N * S / M;
-    const int nd = active ? (sh + nbits + 31) >> 5 : 0;
-    uint32_t raw[NWC + 1];
+    const int nd = S > 0 ? (P.sh + nbits + 31) >> 5 : 0;
 #pragma unroll
-    for (int i = 0; i < NWC + 1; ++i) raw[i] = (i < nd) ? cw4[i] : 0u;
-    v4i bx[SMAX];
+    for (int i = 0; i < NWC + 1; ++i) P.raw[i] = (i < nd) ? cw4[i] : 0u;
+  };
+  auto load_x = [&](int64_t ri, int S, v4i (&bx)[SMAX]) {
+    const int64_t p0 = ri * GV_RANGE + 16 * (int64_t)g * S;
 #pragma unroll
     for (int j = 0; j < SMAX; ++j)
-      bx[j] = (tvalid && j < S) ? *(const v4i*)(xrow + kbeg + 16 * ((int64_t)g * S + j)) : (v4i){0, 0, 0, 0};
-
-    if (first) {                                       // unpack table, fetched while the loads above fly
-      for (int i = tid; i < 1024; i += 64 * GV_WAVES) ((uint4*)lut)[i] = ((const uint4*)kUnpack.v)[i];
-      __syncthreads();
-      first = false;
-    }
-    if (!active) break;
-
+      bx[j] = (tvalid && j < S) ? *(const v4i*)(xrow + p0 + 16 * j) : (v4i){0, 0, 0, 0};
+  };
+  auto steps = [&](int S, const Packed& P, const v4i (&bx)[SMAX], v4i acc) {
     uint32_t cw[NWC];
 #pragma unroll
-    for (int i = 0; i < NWC; ++i) cw[i] = __builtin_amdgcn_alignbit(raw[i + 1], raw[i], sh);
-
+    for (int i = 0; i < NWC; ++i) cw[i] = __builtin_amdgcn_alignbit(P.raw[i + 1], P.raw[i], P.sh);
 #pragma unroll
     for (int j = 0; j < SMAX; ++j) {
       if (j < S) {
@@ -132,7 +313,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int pos = 16 * j + 4 * k;                        // position within the run
-          const uint32_t nib = (N < M) ? ((mw[pos >> 5] >> (pos & 31)) & 0xFu) : 0xFu;
+          const uint32_t nib = (N < M) ? ((P.mw[pos >> 5] >> (pos & 31)) & 0xFu) : 0xFu;
           uint32_t c8;
           if (M == 4) {
             c8 = bits_at<NWC>(cw, (int)CB_NUM * (pos / 4), 8);
@@ -142,7 +323,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
             if ((k & 1) == 0) {
               c8 = gb & 0xFFu;
             } else {
-              const uint32_t low = (N < M) ? ((mw[(pos - 4) >> 5] >> ((pos - 4) & 31)) & 0xFu) : 0xFu;
+              const uint32_t low = (N < M) ? ((P.mw[(pos - 4) >> 5] >> ((pos - 4) & 31)) & 0xFu) : 0xFu;
               c8 = (gb >> (2 * __builtin_popcount(low))) & 0xFFu;
             }
           }
@@ -152,27 +333,45 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
         acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx[j], acc, 0, 0, 0);
       }
     }
-  }
+    return acc;
+  };
+  auto range_steps = [&](int64_t ri) {
+    const int64_t left = (K - ri * GV_RANGE) / 64;
+    return (int)(left < SMAX ? left : SMAX);
+  };
 
-#pragma unroll
-  for (int v = 0; v < 4; ++v) red[wave][lane * 4 + v] = acc[v];
-  __syncthreads();
-  if (tid < 256) {
-    const int e = tid;
-    int s = 0;
-#pragma unroll
-    for (int w = 0; w < GV_WAVES; ++w) s += red[w][e];
-    const int L = e >> 2, v = e & 3;
-    const int64_t row = (int64_t)blockIdx.x * 16 + 4 * (L >> 4) + v;
-    const int64_t t = L & 15;
-    if (t < T && row < R) {
-      if (OUT == 0) {
-        ((int*)Y)[t * ldy + row] = s;
-      } else {
-        const float y = (float)s * (*s_w * s_x[t]);
-        if (OUT == 1) ((float*)Y)[t * ldy + row] = y;
-        else ((uint16_t*)Y)[t * ldy + row] = f32_to_bf16_rne(y);
+  if (nranges <= GV_WAVES) {
+    // one range per wave: activations stay in registers for every row group,
+    // and the next row group's packed bits load during this one's math
+    const bool has = wave < nranges;
+    const int S = has ? range_steps(wave) : 0;
+    v4i bx[SMAX];
+    load_x(wave, S, bx);
+    Packed P;
+    int64_t rg = blockIdx.x;
+    load_w(rg, wave, S, P);
+    for (int i = tid; i < 4096; i += 64 * GV_WAVES) lut[i] = unpack_entry((uint32_t)i);   // while loads fly
+    __syncthreads();
+    for (; rg < nrg; rg += gridDim.x) {
+      const Packed cur = P;
+      if (rg + gridDim.x < nrg) load_w(rg + gridDim.x, wave, S, P);
+      const v4i acc = steps(S, cur, bx, (v4i){0, 0, 0, 0});
+      gemv_finish<OUT>(red, acc, tid, wave, lane, rg * 16, T, R, sc, Y, ldy);
+    }
+  } else {
+    for (int i = tid; i < 4096; i += 64 * GV_WAVES) lut[i] = unpack_entry((uint32_t)i);
+    __syncthreads();
+    for (int64_t rg = blockIdx.x; rg < nrg; rg += gridDim.x) {
+      v4i acc = (v4i){0, 0, 0, 0};
+      for (int64_t ri = wave; ri < nranges; ri += GV_WAVES) {
+        const int S = range_steps(ri);
+        Packed P;
+        v4i bx[SMAX];
+        load_w(rg, ri, S, P);
+        load_x(ri, S, bx);
+        acc = steps(S, P, bx, acc);
       }
+      gemv_finish<OUT>(red, acc, tid, wave, lane, rg * 16, T, R, sc, Y, ldy);
     }
   }
 }
@@ -181,8 +380,18 @@ template <int N, int M>
 hipError_t launch_gemv_nm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                           const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
                           void* Y, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
-  const dim3 grid((unsigned)cdiv(R, 16)), block(64 * GV_WAVES);
+  const int64_t nrg = cdiv(R, 16);
+  const dim3 grid((unsigned)(nrg < GV_MAX_BLOCKS ? nrg : GV_MAX_BLOCKS)), block(64 * GV_WAVES);
   const uint8_t* mp = (N == M) ? nullptr : meta;
+  if (N == 2 && M == 4 && K % 128 == 0) {
+    if (ydt == SBN_I32_ACC)
+      SBN_LAUNCH("gemv", gemv24_kernel<0>, grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    else if (ydt == SBN_F32)
+      SBN_LAUNCH("gemv", gemv24_kernel<1>, grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    else
+      SBN_LAUNCH("gemv", gemv24_kernel<2>, grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    return hipGetLastError();
+  }
   if (ydt == SBN_I32_ACC)
     SBN_LAUNCH("gemv", (gemv_kernel<N, M, 0>), grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
   else if (ydt == SBN_F32)

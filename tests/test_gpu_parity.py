@@ -425,3 +425,12 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for a, b in zip((codes, meta, s_w, Xq, s_x, Y), ref):
             assert torch.equal(a, b), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("K", [128, 384, 640, 768, 896, 1600])
+@pytest.mark.parametrize("T", [1, 7, 16])
+def test_gemv_2_4_partial_ranges(K, T):
+    """2:4 decode: K ranges of 512 positions with a short last range of one to
+    three 128-position steps, and K = 64 mod 128 (the table path)."""
+    f, Xq, s_x, codes, meta, s_w = forward_case(T, 40, K, 2, 4, seed=K + T)
+    check_outputs("gemv", f, Xq, s_x, codes, meta, s_w, 40, 2, 4)
