@@ -19,11 +19,15 @@ enqueues kernels on the caller's stream).  One JSON line is printed.  The
 same line carries:
   roofline      the dominant kernel's algorithmic ops (or bytes) per launch
                 over its average launch time, timed with HIP events that the
-                library records around each launch on its own stream,
-                against MI355X's published peak;
+                library records around that kernel alone on its own stream,
+                against MI355X's published dense peak (the fraction of the
+                structured-sparse int8 peak is printed beside it);
   decode_gemv   the other half of the metric: GB/s of the decode GEMV
-                (R = K = 4096, T = 1, 2:4) over a pool of distinct packed
-                weights larger than the 256 MB Infinity Cache;
+                (R = K = 4096, T = 1, 2:4 and 6:8) three ways: (i) one call on
+                a cold packed weight, (ii-a) the steady state over a pool of
+                distinct packed weights larger than the 256 MB Infinity Cache,
+                replayed as four HIP graphs on four streams, (ii-b) one call
+                over 64 such weights stacked along R (268-336 MB);
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 Multi-GPU runs are not part of this build: --gpus above 1 exits.
 """
@@ -42,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse-ternary GEMM dense-equiv int8 TOPS & decode GEMV GB/s, % of MI355X roofline"
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 matrix peak (2:4 structured headline excluded)
+PEAK_INT8_SPARSE_TOPS = 10070.0  # the same with 2:4 structured sparsity, dense-equivalent
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
@@ -172,58 +177,111 @@ def time_steps(step, steps, warmup, kernel=None, use_graph=True):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
-    # per-kernel durations: eager steps, events recorded by the library on its stream
+    return ms, wall, profile_pass(step, steps, kernel), ("graph" if g is not None else "eager")
+
+
+def profile_pass(step, steps, kernel=None):
+    """Eager steps with the library's HIP events around `kernel` (every kernel
+    if None), recorded on the stream each launch goes to.  {name: (n, ms)}."""
+    import torch
+    import sparse_linear_layers_02_amd as sbn
+    torch.cuda.synchronize()
     sbn.sbn_profile_reset()
     sbn.sbn_profile_enable(True, kernel)
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     sbn.sbn_profile_enable(False)
-    prof = sbn.sbn_profile_dump()
-    return ms, wall, prof, ("graph" if g is not None else "eager")
+    return sbn.sbn_profile_dump()
 
 
 # ---------------------------------------------------------------------- decode GEMV
-def decode_gemv(n=2, m=4, T=1, reps=3):
-    """Steady-state GEMV over a pool of distinct packed weights bigger than the
-    Infinity Cache, launched back to back on one stream; plus one cold call."""
+def decode_gemv(n=2, m=4, T=1, reps=5):
+    """Decode GEMV at R = K = 4096 over packed weights that do not fit the
+    Infinity Cache: (i) one call per cold weight, kernel time from the
+    library's events; (ii-a) the pool replayed as four HIP graphs on four
+    streams so launch ramps overlap; (ii-b) 64 weights stacked along R in one
+    call.  GB/s = algorithmic bytes (packed W + Xq + s_x + Y + s_w) / time."""
     import torch
     import sparse_linear_layers_02_amd as sbn
     from workloads import WORKLOADS
     wl = WORKLOADS["decode"]
     W = bf16_dev(wl.weights(0))
     codes0, meta0, s_w = sbn.sbn_mask_ternarize_pack(W, n, m)
+    del W
     cb, mb = sbn.sbn_packed_bytes(wl.R, wl.K, n, m)
     per = cb + mb
-    P = MALL_BYTES * 3 // 2 // per + 1          # pool 1.5x the Infinity Cache
+    P = (MALL_BYTES * 3 // 2 // per + 1 + 3) // 4 * 4      # pool 1.5x the Infinity Cache, 4 | P
     codes = [codes0.clone() for _ in range(P)]
     metas = [meta0.clone() for _ in range(P)]
     Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0, T=T)))
-    Y = torch.empty((T, wl.R), dtype=torch.bfloat16, device="cuda")
-    algo = per + T * wl.K + 4 * T + 2 * T * wl.R + 4       # packed W + Xq + s_x + Y + s_w
+    Ys = [torch.empty((T, wl.R), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    algo = per + T * wl.K + 4 * T + 2 * T * wl.R + 4
+
+    def call(i, y=0):
+        sbn.sbn_sparse_ternary_gemv(Xq, s_x, codes[i], metas[i], s_w, wl.R, n, m, Y=Ys[y])
+
     for i in range(P):
-        sbn.sbn_sparse_ternary_gemv(Xq, s_x, codes[i], metas[i], s_w, wl.R, n, m, Y=Y)
+        call(i)
+    # (i) cold single calls: kernel time from the library's events (gemv only)
+    prof = profile_pass(lambda: [call(i) for i in range(P)], 1, "gemv")
+    kern_ms, kcnt = kernel_avg_ms(prof, "gemv")
+    # (ii-a) four graphs (every 4th pool entry each) replayed on four streams
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    graphs = []
+    for b in range(4):
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(b, P, 4):
+                call(i, b)
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
     torch.cuda.synchronize()
-    sbn.sbn_profile_reset()
-    sbn.sbn_profile_enable(True, "gemv")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
+    for s_ in streams:
+        s_.wait_event(e0)
     for _ in range(reps):
-        for i in range(P):
-            sbn.sbn_sparse_ternary_gemv(Xq, s_x, codes[i], metas[i], s_w, wl.R, n, m, Y=Y)
+        for b in range(4):
+            with torch.cuda.stream(streams[b]):
+                graphs[b].replay()
+    for s_ in streams:
+        torch.cuda.current_stream().wait_stream(s_)
     e1.record()
     torch.cuda.synchronize()
-    sbn.sbn_profile_enable(False)
-    prof = sbn.sbn_profile_dump()
-    per_call_ms = e0.elapsed_time(e1) / (reps * P)
-    kern_ms, _ = kernel_avg_ms(prof, "gemv")
+    ss_ms = e0.elapsed_time(e1) / (reps * P)
+    del graphs
+    # (ii-b) one call over 64 weights stacked along R
+    L = 64
+    assert cb == wl.R * wl.K * n // (4 * m) and mb in (0, wl.R * wl.K // 8)   # planes hold no padding
+    codes_t = torch.cat(codes[:L])
+    meta_t = torch.cat(metas[:L]) if mb else None
+    Rt = L * wl.R
+    Yt = torch.empty((T, Rt), dtype=torch.bfloat16, device="cuda")
+    f = lambda: sbn.sbn_sparse_ternary_gemv(Xq, s_x, codes_t, meta_t, s_w, Rt, n, m, Y=Yt)
+    f()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    st_ms = e0.elapsed_time(e1) / reps
+    algo_t = L * per + T * wl.K + 4 * T + 2 * T * Rt + 4
+    gbps = lambda b_, ms_: round(b_ / (ms_ * 1e-3) / 1e9, 1)
     return {
-        "workload": f"decode R=K=4096 T={T} {n}:{m}", "pool_MiB": round(P * per / 2 ** 20, 1),
-        "algo_bytes_per_call": algo,
-        "kernel_us": round(kern_ms * 1e3, 3), "kernel_GBps": round(algo / (kern_ms * 1e-3) / 1e9, 1),
-        "stream_us_per_call": round(per_call_ms * 1e3, 3),
-        "stream_GBps": round(algo / (per_call_ms * 1e-3) / 1e9, 1),
-        "frac_hbm_kernel": round(algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "workload": f"decode R=K=4096 T={T} {n}:{m}", "algo_bytes_per_call": algo,
+        "pool_MiB": round(P * per / 2 ** 20, 1), "pool_calls": P,
+        "single_call": {"kernel_us": round(kern_ms * 1e3, 3), "GBps": gbps(algo, kern_ms),
+                        "frac_hbm": round(algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "steady_graphs_4streams": {"us_per_call": round(ss_ms * 1e3, 3), "GBps": gbps(algo, ss_ms),
+                                   "frac_hbm": round(algo / (ss_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "stacked_64": {"R": Rt, "algo_bytes": algo_t, "us": round(st_ms * 1e3, 2), "GBps": gbps(algo_t, st_ms),
+                       "frac_hbm": round(algo_t / (st_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
 
 
@@ -276,7 +334,9 @@ def main():
         wl = WORKLOADS[a.workload]
         n, m = wl.nm[0]
         step = make_forward_step(wl, n, m, with_backward=(a.workload == "train"))
-        ms, wall, prof, mode = time_steps(step, a.steps, a.warmup)
+        gname = "gemm_smfmac" if (n <= 2) else "gemm_mfma"
+        ms, wall, prof, mode = time_steps(step, a.steps, a.warmup)          # every stage, for stages_us
+        prof_g = profile_pass(step, a.steps, gname)                          # the roofline kernel alone
         nprod = 3 if a.workload == "train" else 1
         ops = 2 * wl.T * wl.R * wl.K * nprod
         out.update(value=round(ops / (ms * 1e-3) / 1e12, 3), unit="TOPS", ms_per_step=round(ms, 4),
@@ -284,20 +344,21 @@ def main():
         out["config"] = {"workload": a.workload, "T": wl.T, "R": wl.R, "K": wl.K, "nm": f"{n}:{m}",
                          "step": "pack+act_quant+gemm" + ("+backward" if nprod == 3 else ""),
                          "y_dtype": "bf16", "seed": 0}
-        gname = "gemm_smfmac" if (n <= 2) else "gemm_mfma"
-        g_ms, g_cnt = kernel_avg_ms(prof, gname)
+        g_ms, g_cnt = kernel_avg_ms(prof_g, gname)
         g_ach = 2 * wl.T * wl.R * wl.K / (g_ms * 1e-3) / 1e12
         traffic = traffic_from_profiles(gname, a.workload)
         out["roofline"] = {"kernel": gname, "bound": "mfma", "achieved": round(g_ach, 2), "peak": PEAK_INT8_TOPS,
                            "unit": "TFLOP/s", "frac": round(g_ach / PEAK_INT8_TOPS, 4), "traffic": traffic,
                            "kernel_us": round(g_ms * 1e3, 3), "launches": g_cnt,
                            "ops_per_launch": 2 * wl.T * wl.R * wl.K,
+                           "frac_of_sparse_peak": (round(g_ach / PEAK_INT8_SPARSE_TOPS, 4) if n <= 2 else None),
                            "note": "int8 multiply-adds count 2 ops; dense-equivalent (pruned positions "
-                                   "counted); peak is the dense int8 matrix peak"}
+                                   "counted); peak is the dense int8 matrix peak; frac_of_sparse_peak divides "
+                                   "by the 2:4 structured-sparse int8 peak instead"}
         out["stages_us"] = {k: round(v[1] / v[0] * 1e3, 3) for k, v in sorted(prof.items()) if v[0]}
         if a.workload == "train":
             for nm_, kname in (("dx", "gemm_dx"), ("dw", "gemm_dw")):
-                k_ms, _ = kernel_avg_ms(prof, kname)
+                k_ms, _ = kernel_avg_ms(profile_pass(step, max(2, a.steps // 4), kname), kname)
                 fl = 2 * wl.T * wl.R * wl.K * (2 if kname == "gemm_dw" else 1)
                 out["roofline_" + nm_] = {"kernel": kname, "bound": "mfma", "achieved": round(fl / (k_ms * 1e-3) / 1e12, 2),
                                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -312,9 +373,10 @@ def main():
             codes, meta, s_w = sbn.sbn_mask_ternarize_pack(W, n, m)
             Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0)))
             Y = torch.empty((wl.T, wl.R), dtype=torch.bfloat16, device="cuda")
-            ms, wall, prof, mode = time_steps(
-                lambda: sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, wl.R, n, m, Y=Y), a.steps, a.warmup)
             gname = "gemm_smfmac" if sbn_uses_smfmac(n, m) else "gemm_mfma"
+            ms, wall, prof, mode = time_steps(
+                lambda: sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, wl.R, n, m, Y=Y), a.steps, a.warmup,
+                kernel=gname)
             g_ms, _ = kernel_avg_ms(prof, gname)
             ops = 2 * wl.T * wl.R * wl.K
             rows.append({"nm": f"{n}:{m}", "call_us": round(ms * 1e3, 2), "kernel_us": round(g_ms * 1e3, 2),
@@ -332,7 +394,7 @@ def main():
                            "frac": round(best["TOPS_kernel"] / PEAK_INT8_TOPS, 4), "traffic": None}
 
     if not a.no_extras:
-        out["decode_gemv"] = decode_gemv()
+        out["decode_gemv"] = [decode_gemv(2, 4, 1), decode_gemv(6, 8, 1)]
 
     if not a.no_cpu_baseline:
         wl = WORKLOADS["prefill" if a.workload == "sweep" else a.workload]

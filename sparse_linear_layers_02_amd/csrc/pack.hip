@@ -15,8 +15,9 @@
 // 8-bit significand.  Magnitudes with exponent field e in [95, 131), i.e.
 // 2^-32 <= |w| < 16, are multiples of 2^-39 below 2^4; a float64 running sum
 // of at most 1024 of them stays below 2^53 units, so it is exact in any
-// order.  Each thread sums at most 64 of them in float64 (eight 16-byte
-// loads in flight) before flushing into an int64 counter of 2^-39 units.
+// order.  Each thread sums at most 32 of them in float64 (four 16-byte
+// chunks, while the next four load) before flushing into an int64 counter of
+// 2^-39 units.
 // Everything outside that window (zero, subnormal, tiny or >= 16) is added
 // to 256 per-exponent integer bins in LDS: exact too.  Each block writes its
 // int64 partial, a flag, and its bins only if it had such values.  Pass 2
@@ -24,14 +25,15 @@
 // (the kernel boundary makes them visible; no device-scope fence is issued,
 // which on this multi-XCD part would write back and invalidate an L2 per
 // block) as a 320-bit integer in units of 2^-133, and rounds total / (R*K) to
-// fp32: a float64 estimate, then an exact comparison against the two
-// neighbouring midpoints.  The workspace needs no initialisation.
+// fp32: a float64 estimate, and an exact comparison against the two
+// neighbouring midpoints whenever the estimate is too close to one of them
+// to decide.  The workspace needs no initialisation.
 #include "sbn_internal.h"
 
 namespace sbn {
 namespace {
 
-constexpr int PT = 256;                  // threads per block, both passes
+constexpr int PT = 256;                  // threads per block in pass 2
 constexpr uint32_t E_LO = 95, E_HI = 131;
 constexpr double FAST_SCALE = 549755813888.0;  // 2^39
 
@@ -100,7 +102,11 @@ __device__ inline float pick_even(float a, float b) {
   return (__float_as_uint(a) & 1u) ? b : a;
 }
 
-// s_w = max(RN_f32(total * 2^-133 / n), 1e-5)
+// s_w = max(RN_f32(total * 2^-133 / n), 1e-5).  The float64 estimate
+// (top 96 bits of the total, one division) is within 2^-50 of the exact
+// mean relative to it, so it already decides the rounding unless it lies
+// within 2^-46 (relative) of a midpoint between two floats; only then are the
+// exact 320-bit comparisons against those midpoints made.
 __device__ float round_mean(const Big& t, unsigned long long n) {
   int top = -1;
 #pragma unroll
@@ -124,6 +130,9 @@ __device__ float round_mean(const Big& t, unsigned long long n) {
   const float r0 = (float)approx;
   const float rn = __uint_as_float(__float_as_uint(r0) + 1u);
   const float rp = __uint_as_float(__float_as_uint(r0) - 1u);
+  const double m_hi = ((double)r0 + (double)rn) * 0.5, m_lo = ((double)rp + (double)r0) * 0.5;
+  const double tol = approx * 0x1p-46;
+  if (fabs(approx - m_hi) > tol && fabs(approx - m_lo) > tol) return fmaxf(r0, 1e-5f);
   const int c_hi = big_cmp(t, mid_times_n(r0, rn, n));
   const int c_lo = big_cmp(t, mid_times_n(rp, r0, n));
   float r = r0;
@@ -179,7 +188,9 @@ __device__ inline void pair_slow(uint32_t u, unsigned long long* bins) {
   if (!in_window(hi) && hi) slow_add(bins, hi);
 }
 
-constexpr int U = 8;   // 16-byte chunks in flight per thread in pass 1
+constexpr int U = 4;      // 16-byte chunks per thread per step in pass 2 (2:4), plus as many prefetched
+constexpr int U1 = 4;     // the same in pass 1
+constexpr int PT1 = 1024; // pass-1 threads per block: 16 waves keep up to 128 KB of W in flight per CU
 
 template <bool FLAT>
 __device__ inline uint4 chunk_at(const uint16_t* __restrict__ W, int64_t c, int64_t kc, int64_t ldw) {
@@ -189,46 +200,51 @@ __device__ inline uint4 chunk_at(const uint16_t* __restrict__ W, int64_t c, int6
 }
 
 // Pass 1: block b sums |w| over 16-byte chunks [b*cpb, (b+1)*cpb) of the
-// row-major chunk order (8 weights per chunk).  Each thread keeps U loads in
-// flight and flushes its float64 sum (<= 8U terms, exact) into int64 units;
-// out-of-window values take one rare branch per group into the LDS bins.
+// row-major chunk order (8 weights per chunk).  Each thread sums U1 chunks per
+// step while the next U1 load, and flushes its float64 sum (<= 8*U1 terms,
+// exact) into int64 units; out-of-window values take one rare branch per
+// group into the LDS bins.
 template <bool FLAT>
-__global__ __launch_bounds__(PT) void abs_sum_kernel(const uint16_t* __restrict__ W, int64_t R,
+__global__ __launch_bounds__(PT1) void abs_sum_kernel(const uint16_t* __restrict__ W, int64_t R,
                                                      int64_t K, int64_t ldw, int64_t cpb,
                                                      unsigned char* __restrict__ ws) {
   const PackWs pw = pack_ws(ws, gridDim.x);
   __shared__ unsigned long long bins[256];
-  __shared__ unsigned long long red[PT / 64];
+  __shared__ unsigned long long red[PT1 / 64];
   __shared__ int any_slow;
   const int tid = threadIdx.x;
-  bins[tid] = 0;
+  if (tid < 256) bins[tid] = 0;
   if (tid == 0) any_slow = 0;
   __syncthreads();
   const int64_t kc = K / 8, total = R * kc;
   const int64_t c0 = (int64_t)blockIdx.x * cpb;
   const int64_t c1 = min(total, c0 + cpb);
   unsigned long long acc_i = 0;
-  for (int64_t base = c0 + tid; base < c1; base += PT * U) {
-    uint4 v[U];
-    if (base + (int64_t)(U - 1) * PT < c1) {
+  constexpr int64_t STEP = (int64_t)PT1 * U1;
+  uint4 v[U1], nx[U1];
+  int64_t base = c0 + tid;
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = chunk_at<FLAT>(W, base + (int64_t)u * PT, kc, ldw);
-    } else {
+  for (int u = 0; u < U1; ++u) {
+    const int64_t c = base + (int64_t)u * PT1;
+    v[u] = c < c1 ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
+  }
+  for (; base < c1; base += STEP) {
+    if (base + STEP < c1) {                      // next chunks load while these are summed
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t c = base + (int64_t)u * PT;
-        v[u] = c < c1 ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < U1; ++u) {
+        const int64_t c = base + STEP + (int64_t)u * PT1;
+        nx[u] = c < c1 ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
       }
     }
     double acc = 0.0;
     bool ok = true;
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U1; ++u)
       acc += pair_abs(v[u].x, ok) + pair_abs(v[u].y, ok) + pair_abs(v[u].z, ok) + pair_abs(v[u].w, ok);
     if (!ok) {
       any_slow = 1;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U1; ++u) {
         pair_slow(v[u].x, bins);
         pair_slow(v[u].y, bins);
         pair_slow(v[u].z, bins);
@@ -236,17 +252,19 @@ __global__ __launch_bounds__(PT) void abs_sum_kernel(const uint16_t* __restrict_
       }
     }
     acc_i += (unsigned long long)(acc * FAST_SCALE);   // exact integer < 2^53
+#pragma unroll
+    for (int u = 0; u < U1; ++u) v[u] = nx[u];
   }
   const unsigned long long s = wave_sum_u64(acc_i);
   if ((tid & 63) == 0) red[tid >> 6] = s;
   __syncthreads();
   if (tid == 0) {
     unsigned long long b = 0;
-    for (int i = 0; i < PT / 64; ++i) b += red[i];
+    for (int i = 0; i < PT1 / 64; ++i) b += red[i];
     pw.partials[blockIdx.x] = (long long)b;
     pw.flags[blockIdx.x] = any_slow ? 1u : 0u;
   }
-  if (any_slow) pw.bins[(int64_t)blockIdx.x * 256 + tid] = bins[tid];
+  if (any_slow && tid < 256) pw.bins[(int64_t)blockIdx.x * 256 + tid] = bins[tid];
 }
 
 // Block-wide (256 threads): total = sum of the pass-1 partials (2^-39 units)
@@ -258,49 +276,50 @@ __device__ float scale_from_partials(const unsigned char* __restrict__ ws, int64
                                      float* __restrict__ s_w_out) {
   const PackWs pw = pack_ws((unsigned char*)ws, nb);
   const int tid = threadIdx.x;
-  __shared__ unsigned long long flo[PT], fhi[PT];
+  __shared__ unsigned long long wlo[PT / 64], whi[PT / 64];
   __shared__ unsigned long long ebin[256];
   __shared__ int nflag;
   __shared__ int flagged[PT];
   __shared__ float s_sh;
   if (tid == 0) nflag = 0;
   __syncthreads();
-  unsigned __int128 f = 0;
+  // each partial (< 2^63) split into 32-bit halves, summed separately in u64
+  unsigned long long lo = 0, hi = 0;
   for (int64_t i = tid; i < nb; i += PT) {
-    f += (unsigned long long)pw.partials[i];
+    const unsigned long long p = (unsigned long long)pw.partials[i];
+    lo += p & 0xFFFFFFFFull;
+    hi += p >> 32;
     if (pw.flags[i]) {
       const int slot = atomicAdd(&nflag, 1);
       if (slot < PT) flagged[slot] = (int)i;
     }
   }
-  flo[tid] = (unsigned long long)f;
-  fhi[tid] = (unsigned long long)(f >> 64);
+  lo = wave_sum_u64(lo);
+  hi = wave_sum_u64(hi);
+  if ((tid & 63) == 0) {
+    wlo[tid >> 6] = lo;
+    whi[tid >> 6] = hi;
+  }
   __syncthreads();
+  const int nf = nflag;
   unsigned long long eb = 0;                     // exponent bin `tid` over the flagged blocks (rare)
-  if (nflag > 0 && nflag <= PT) {
-    for (int j = 0; j < nflag; ++j) eb += pw.bins[(int64_t)flagged[j] * 256 + tid];
-  } else if (nflag > PT) {
+  if (nf > 0 && nf <= PT) {
+    for (int j = 0; j < nf; ++j) eb += pw.bins[(int64_t)flagged[j] * 256 + tid];
+  } else if (nf > PT) {
     for (int64_t i = 0; i < nb; ++i)
       if (pw.flags[i]) eb += pw.bins[i * 256 + tid];
   }
-  ebin[tid] = eb;
-  for (int sh = PT / 2; sh > 0; sh >>= 1) {      // tree sum of the 128-bit partial sums
-    if (tid < sh) {
-      unsigned __int128 a = ((unsigned __int128)fhi[tid] << 64) | flo[tid];
-      a += ((unsigned __int128)fhi[tid + sh] << 64) | flo[tid + sh];
-      flo[tid] = (unsigned long long)a;
-      fhi[tid] = (unsigned long long)(a >> 64);
-    }
-    __syncthreads();
-  }
+  if (nf) ebin[tid] = eb;
+  __syncthreads();
   if (tid == 0) {
-    const unsigned __int128 F = ((unsigned __int128)fhi[0] << 64) | flo[0];
+    unsigned __int128 F = 0;
+    for (int w = 0; w < PT / 64; ++w) F += (unsigned __int128)wlo[w] + ((unsigned __int128)whi[w] << 32);
     Big t;
     big_zero(t);
     // fast part: F units of 2^-39 = F * 2^94 units of 2^-133
     big_add_shifted(t, (unsigned long long)F, 94);
     big_add_shifted(t, (unsigned long long)(F >> 64), 94 + 64);
-    if (nflag)
+    if (nf)
       for (int e = 0; e < 256; ++e)
         if (ebin[e]) big_add_shifted(t, ebin[e], (e ? e : 1) - 1);
     const float sw = round_mean(t, (unsigned long long)numel);
@@ -408,8 +427,9 @@ __global__ __launch_bounds__(PT) void mask_pack24_kernel(
     uint8_t* __restrict__ meta, float* __restrict__ s_w_ptr, const unsigned char* __restrict__ ws,
     int64_t nb) {
   const int64_t kc = K / 8, total = R * kc;
+  const int64_t step = (int64_t)gridDim.x * PT * U;
   int64_t base = (int64_t)blockIdx.x * PT * U + threadIdx.x;
-  uint4 v[U];
+  uint4 v[U], nx[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {                  // first loads fly while the scale is formed
     const int64_t c = base + (int64_t)u * PT;
@@ -417,7 +437,14 @@ __global__ __launch_bounds__(PT) void mask_pack24_kernel(
   }
   const float h = 0.5f * scale_from_partials(ws, nb, R * K, s_w_ptr);
   const uint32_t thr = __float_as_uint(h) >> 16;
-  while (true) {
+  for (; base < total; base += step) {
+    if (base + step < total) {                   // next chunks load while these are packed
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = base + step + (int64_t)u * PT;
+        nx[u] = c < total ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t c = base + (int64_t)u * PT;
@@ -429,13 +456,8 @@ __global__ __launch_bounds__(PT) void mask_pack24_kernel(
         codes[c] = (uint8_t)(c0 | (c1 << 4));
       }
     }
-    base += (int64_t)gridDim.x * PT * U;
-    if (base >= total) break;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = base + (int64_t)u * PT;
-      v[u] = c < total ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < U; ++u) v[u] = nx[u];
   }
 }
 
@@ -444,7 +466,7 @@ __global__ __launch_bounds__(PT) void mask_pack24_kernel(
 PackPlan pack_plan(int64_t R, int64_t K) {
   PackPlan p;
   const int64_t total = R * (K / 8);                    // 16-byte chunks
-  int64_t nb = cdiv(total, (int64_t)PT * U);
+  int64_t nb = cdiv(total, (int64_t)PT1 * U1);
   if (nb > 256) nb = 256;                               // pass 2 reduces one partial per thread
   const int64_t max_cpb = (int64_t(1) << 20) / 8;       // a block's int64 partial stays < 2^63
   int64_t cpb = cdiv(total, nb);
@@ -460,10 +482,10 @@ hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int
                        uint8_t* codes, uint8_t* meta, float* s_w, void* ws, hipStream_t st) {
   const PackPlan p = pack_plan(R, K);
   if (ldw == K)
-    SBN_LAUNCH("abs_sum", abs_sum_kernel<true>, dim3((unsigned)p.nblocks), dim3(PT), 0, st, W, R, K, ldw,
+    SBN_LAUNCH("abs_sum", abs_sum_kernel<true>, dim3((unsigned)p.nblocks), dim3(PT1), 0, st, W, R, K, ldw,
                p.chunks_per_block, (unsigned char*)ws);
   else
-    SBN_LAUNCH("abs_sum", abs_sum_kernel<false>, dim3((unsigned)p.nblocks), dim3(PT), 0, st, W, R, K, ldw,
+    SBN_LAUNCH("abs_sum", abs_sum_kernel<false>, dim3((unsigned)p.nblocks), dim3(PT1), 0, st, W, R, K, ldw,
                p.chunks_per_block, (unsigned char*)ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -476,7 +498,7 @@ hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int
   uint8_t* mp = (n == m) ? nullptr : meta;
   if (n == 2 && m == 4) {
     int64_t b24 = cdiv(R * (K / 8), (int64_t)PT * U);
-    if (b24 > 2048) b24 = 2048;
+    if (b24 > 1024) b24 = 1024;                         // four blocks per CU, looping
     if (ldw == K)
       SBN_LAUNCH("mask_pack", mask_pack24_kernel<true>, dim3((unsigned)b24), dim3(PT), 0, st, W, R, K, ldw,
                  codes, mp, s_w, (const unsigned char*)ws, p.nblocks);

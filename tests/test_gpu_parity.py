@@ -434,3 +434,28 @@ def test_gemv_2_4_partial_ranges(K, T):
     three 128-position steps, and K = 64 mod 128 (the table path)."""
     f, Xq, s_x, codes, meta, s_w = forward_case(T, 40, K, 2, 4, seed=K + T)
     check_outputs("gemv", f, Xq, s_x, codes, meta, s_w, 40, 2, 4)
+
+
+def _midpoint_weights(extra_bits=None):
+    """256 x 256 bf16 weights whose exact mean |w| is 1 - 2^-15 + 2^-25: the
+    midpoint between two adjacent fp32 values (65534 ones, one 2^-9, one 0);
+    `extra_bits` replaces the zero to move the mean off the midpoint."""
+    W = np.full((256, 256), 0x3F80, dtype=np.uint16)          # 1.0
+    W[0, 0] = 0x3B00                                           # 2^-9
+    W[0, 1] = 0x0000 if extra_bits is None else extra_bits
+    return W
+
+
+@pytest.mark.parametrize("extra", [None, 0x0001, 0x8001, 0x2F80])
+def test_pack_scale_rounding_near_midpoint(extra):
+    """s_w when mean |W| is exactly a midpoint between two floats (ties to
+    even), a subnormal 2^-133 above it (rounds up, decided only by the exact
+    comparison), and 2^-32 above it; against the oracle's exact rounding."""
+    W = _midpoint_weights(extra)
+    for n, m in [(2, 4), (6, 8)]:
+        check_pack(W, n, m)
+    sw = O.weight_scale(W)
+    if extra is None:
+        assert f32_bits(sw) == 0x3F7FFE00                      # the even neighbour
+    elif extra in (0x0001, 0x8001):
+        assert f32_bits(sw) == 0x3F7FFE01
