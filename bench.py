@@ -188,7 +188,8 @@ def profile_pass(step, steps, kernel=None):
     torch.cuda.synchronize()
     sbn.sbn_profile_reset()
     sbn.sbn_profile_enable(True, kernel)
-    for _ in range(steps):
+    torch.cuda._sleep(5_000_000)     # keep the GPU busy while the host queues the steps, so no
+    for _ in range(steps):           # host submission delay falls between a kernel and its events
         step()
     torch.cuda.synchronize()
     sbn.sbn_profile_enable(False)

@@ -38,7 +38,7 @@
 //                 32*(l/16) + 4*(j/2) + idx_j (idx_j = bits 2j..2j+1 of the index
 //                 register); B lane l -> col l%16, bytes 0..15 = K[16*(l/16)..),
 //                 bytes 16..31 = K[64 + 16*(l/16)..); C as above.
-#include "sbn_internal.h"
+#include "sbn_decode.h"
 
 namespace sbn {
 namespace {
@@ -59,110 +59,112 @@ __device__ inline uint32_t read_bits(const uint8_t* p, int64_t off, int nbits) {
 __device__ inline int8_t code_to_i8(uint32_t c) { return c == 1u ? (int8_t)1 : c == 3u ? (int8_t)-1 : (int8_t)0; }
 
 // ---------------------------------------------------------------- expansion: sparse operand
-// one thread = one lane of one (16-row, 128-K) fragment: 16 values + 32 index bits.
-// vals [RB][KBn][64][16 B]; idx [RB/4][KBn][64][4 x u32] (row fragment 4g+q in word q)
+// One thread = one lane of four row-consecutive (16-row, 128-K) fragments: per
+// fragment 16 compressed values + 32 index bits.
+// vals [RB][KBn][64][16 B]; idx [RB/4][KBn][64][4 x u32] (row fragment 4g+q in
+// word q, so a thread's four index words are one 16-byte store)
 __global__ __launch_bounds__(256) void expand_sparse_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, int64_t R, int64_t K,
     int n, int m, int64_t RB, int64_t KBn, uint8_t* __restrict__ vals, uint32_t* __restrict__ idx) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= RB * KBn * 64) return;
+  if (gid >= (RB / 4) * KBn * 64) return;
   const int l = (int)(gid & 63);
-  const int64_t f = gid >> 6;                   // fragment = rb * KBn + kb
-  const int64_t rb = f / KBn, kb = f - rb * KBn;
-  const int64_t r = rb * 16 + (l & 15);
+  const int64_t f = gid >> 6;                   // = g * KBn + kb
+  const int64_t g = f / KBn, kb = f - g * KBn;
   const int64_t k0 = kb * 128 + 32 * (l >> 4);
-  uint32_t v32[4] = {0, 0, 0, 0};
-  uint32_t ix = 0x44444444u;                    // (0,1) in every half: harmless with zero values
-  if (r < R && k0 < K && n == 2 && m == 4) {
-    // 2:4: meta and codes of these 32 positions are one aligned word each
-    const uint32_t mb = *(const uint32_t*)(meta + r * (K / 8) + k0 / 8);
-    const uint32_t cb = *(const uint32_t*)(codes + r * (K / 8) + k0 / 8);
-    // survivor positions per nibble: p0 = lowest set bit, p1 = highest (SWAR over 8 nibbles)
-    const uint32_t M1 = 0x11111111u;
-    const uint32_t b0 = mb & M1, b1 = (mb >> 1) & M1, b2 = (mb >> 2) & M1, b3 = (mb >> 3) & M1;
-    const uint32_t nb0 = b0 ^ M1, nb1 = b1 ^ M1, nb2 = b2 ^ M1;
-    ix = (nb0 & b1) | ((nb0 & nb1) << 1) | ((b3 | nb2) << 2) | ((b3 | b2) << 3);
-    // values: compressed slot j holds code bits 2j..2j+1; spread each byte's four
-    // codes to four bytes and map 01 -> +1, 11 -> -1
+  uint32_t ixs[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t y = (cb >> (8 * d)) & 0xFFu;
-      const uint32_t sp = (((y & 0x33u) * 0x1001u) & 0x00030003u) | (((y & 0xCCu) * 0x40040u) & 0x03000300u);
-      v32[d] = sp | ((sp & 0x02020202u) * 0x7Eu);
-    }
-  } else if (r < R && k0 < K) {
-    const uint32_t mb = *(const uint32_t*)(meta + r * (K / 8) + k0 / 8);
-    const int64_t crow = K * n / (4 * m);
-    const int64_t gbase = k0 / m;               // groups before k0 in this row
-    const int ngroups = 32 / m;
-    const uint32_t cb = read_bits(codes + r * crow, 2 * n * gbase, 2 * n * ngroups);
-    ix = 0;
-    int cur = 0;                                // codes consumed so far in this range
+  for (int q = 0; q < 4; ++q) {
+    const int64_t rb = 4 * g + q;
+    const int64_t r = rb * 16 + (l & 15);
+    v4i a = (v4i){0, 0, 0, 0};
+    uint32_t ix = 0x44444444u;                  // (0,1) in every half: harmless with zero values
+    if (r < R && k0 < K && n == 2 && m == 4) {
+      // 2:4: meta and codes of these 32 positions are one aligned word each
+      const uint32_t mb = *(const uint32_t*)(meta + r * (K / 8) + k0 / 8);
+      const uint32_t cb = *(const uint32_t*)(codes + r * (K / 8) + k0 / 8);
+      int ixi;
+      decode24(mb, cb, a, ixi);
+      ix = (uint32_t)ixi;
+    } else if (r < R && k0 < K) {
+      const uint32_t mb = *(const uint32_t*)(meta + r * (K / 8) + k0 / 8);
+      const int64_t crow = K * n / (4 * m);
+      const int64_t gbase = k0 / m;             // groups before k0 in this row
+      const int ngroups = 32 / m;
+      const uint32_t cb = read_bits(codes + r * crow, 2 * n * gbase, 2 * n * ngroups);
+      uint32_t v32[4] = {0, 0, 0, 0};
+      ix = 0;
+      int cur = 0;                              // codes consumed so far in this range
 #pragma unroll
-    for (int h = 0; h < 8; ++h) {               // eight halves of four positions
-      int cnt = 0;
-      uint32_t pos[2] = {0, 1};
-      int8_t val[2] = {0, 0};
+      for (int h = 0; h < 8; ++h) {             // eight halves of four positions
+        int cnt = 0;
+        uint32_t pos[2] = {0, 1};
+        int8_t val[2] = {0, 0};
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int pp = 4 * h + p;
-        if ((mb >> pp) & 1u) {
-          const uint32_t c = (cb >> (2 * cur)) & 3u;
-          ++cur;
-          if (cnt < 2) {
-            pos[cnt] = (uint32_t)p;
-            val[cnt] = code_to_i8(c);
+        for (int p = 0; p < 4; ++p) {
+          const int pp = 4 * h + p;
+          if ((mb >> pp) & 1u) {
+            const uint32_t c = (cb >> (2 * cur)) & 3u;
+            ++cur;
+            if (cnt < 2) {
+              pos[cnt] = (uint32_t)p;
+              val[cnt] = code_to_i8(c);
+            }
+            ++cnt;
           }
-          ++cnt;
         }
+        if (cnt == 1) {                         // keep the two indices distinct and ordered
+          if (pos[0] == 3) { pos[1] = 3; val[1] = val[0]; pos[0] = 0; val[0] = 0; }
+          else { pos[1] = 3; val[1] = 0; }
+        }
+        ix |= (pos[0] | (pos[1] << 2)) << (4 * h);
+        const int j0 = 2 * h;
+        v32[j0 >> 2] |= (uint32_t)(uint8_t)val[0] << (8 * (j0 & 3));
+        v32[(j0 + 1) >> 2] |= (uint32_t)(uint8_t)val[1] << (8 * ((j0 + 1) & 3));
       }
-      if (cnt == 1) {                           // keep the two indices distinct and ordered
-        if (pos[0] == 3) { pos[1] = 3; val[1] = val[0]; pos[0] = 0; val[0] = 0; }
-        else { pos[1] = 3; val[1] = 0; }
-      }
-      ix |= (pos[0] | (pos[1] << 2)) << (4 * h);
-      const int j0 = 2 * h;
-      v32[j0 >> 2] |= (uint32_t)(uint8_t)val[0] << (8 * (j0 & 3));
-      v32[(j0 + 1) >> 2] |= (uint32_t)(uint8_t)val[1] << (8 * ((j0 + 1) & 3));
+      a = (v4i){(int)v32[0], (int)v32[1], (int)v32[2], (int)v32[3]};
     }
+    *(v4i*)(vals + ((rb * KBn + kb) * 64 + l) * 16) = a;
+    ixs[q] = ix;
   }
-  uint4 o;
-  o.x = v32[0]; o.y = v32[1]; o.z = v32[2]; o.w = v32[3];
-  ((uint4*)vals)[gid] = o;
-  // index words of four consecutive row fragments share one 16-byte lane slot
-  idx[(((rb >> 2) * KBn + kb) * 64 + l) * 4 + (rb & 3)] = ix;
+  *(uint4*)(idx + ((g * KBn + kb) * 64 + l) * 4) = make_uint4(ixs[0], ixs[1], ixs[2], ixs[3]);
 }
 
 // ---------------------------------------------------------------- expansion: dense operand
-// one thread = one lane of one (16-row, 64-K) fragment: 16 int8 values
+// One thread = one lane of one (16-row, 64-K) fragment: 16 int8 weights,
+// through the unpack table in LDS (built once per block; blocks walk the
+// fragments with a grid stride).  vals [RB][KD][64][16 B].
+template <int M>
 __global__ __launch_bounds__(256) void expand_dense_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, int64_t R, int64_t K,
-    int n, int m, int64_t RB, int64_t KD, uint8_t* __restrict__ vals) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= RB * KD * 64) return;
-  const int l = (int)(gid & 63);
-  const int64_t f = gid >> 6;
-  const int64_t rb = f / KD, kd = f - rb * KD;
-  const int64_t r = rb * 16 + (l & 15);
-  const int64_t k0 = kd * 64 + 16 * (l >> 4);
-  uint32_t v32[4] = {0, 0, 0, 0};
-  if (r < R && k0 < K) {
-    const uint32_t mb = (n == m) ? 0xFFFFu : (uint32_t)*(const uint16_t*)(meta + r * (K / 8) + k0 / 8);
-    const int64_t crow = K * n / (4 * m);
-    const uint32_t cb = read_bits(codes + r * crow, 2 * n * (k0 / m), 2 * n * (16 / m));
-    int cur = 0;
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      if ((mb >> p) & 1u) {
-        const uint32_t c = (cb >> (2 * cur)) & 3u;
-        ++cur;
-        v32[p >> 2] |= (uint32_t)(uint8_t)code_to_i8(c) << (8 * (p & 3));
-      }
+    int n, int64_t RB, int64_t KD, int64_t cplane, uint8_t* __restrict__ vals) {
+  __shared__ uint32_t lut[4096];
+  for (int i = threadIdx.x; i < 4096; i += 256) lut[i] = unpack_entry((uint32_t)i);
+  __syncthreads();
+  const int64_t total = RB * KD * 64;
+  const int64_t crow = K * n / (4 * M);          // code bytes per row
+  const int64_t lastw = (cplane - 4) & ~(int64_t)3;
+  const bool dense = meta == nullptr;
+  for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total; gid += (int64_t)gridDim.x * 256) {
+    const int l = (int)(gid & 63);
+    const int64_t f = gid >> 6;
+    const int64_t rb = f / KD, kd = f - rb * KD;
+    const int64_t r = rb * 16 + (l & 15);
+    const int64_t k0 = kd * 64 + 16 * (l >> 4);
+    v4i a = (v4i){0, 0, 0, 0};
+    if (r < R && k0 < K) {
+      const uint32_t mw16 = dense ? 0xFFFFu : (uint32_t)*(const uint16_t*)(meta + r * (K / 8) + k0 / 8);
+      // the 16 positions' codes start at bit cbit of the plane (a group boundary)
+      const int64_t cbit = r * crow * 8 + k0 * 2 * n / M;
+      const int64_t a0 = (cbit >> 3) & ~(int64_t)3;
+      const int sh = (int)(cbit - a0 * 8);                        // < 32; sh + 32 bits <= 64
+      const uint32_t w0 = *(const uint32_t*)(codes + (a0 < lastw ? a0 : lastw));
+      const uint32_t w1 = *(const uint32_t*)(codes + (a0 + 4 < lastw ? a0 + 4 : lastw));
+      const unsigned long long c = (((unsigned long long)w1 << 32) | w0) >> sh;
+      a = unpack16<M>(lut, mw16, dense, n, c, 0);
     }
+    *(v4i*)(vals + gid * 16) = a;
   }
-  uint4 o;
-  o.x = v32[0]; o.y = v32[1]; o.z = v32[2]; o.w = v32[3];
-  ((uint4*)vals)[gid] = o;
 }
 
 // ---------------------------------------------------------------- activation fragments
@@ -508,7 +510,7 @@ hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
   if (gemm_uses_smfmac(n, m)) {
     uint8_t* vals = w;
     uint32_t* idx = (uint32_t*)(w + g.w_bytes);
-    const int64_t threads = RB * KBn * 64;
+    const int64_t threads = (RB / 4) * KBn * 64;
     SBN_LAUNCH("expand_sparse", expand_sparse_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st,
                codes, meta, R, K, n, m, RB, KBn, vals, idx);
     e = hipGetLastError();
@@ -517,8 +519,16 @@ hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
   }
   const int64_t KD = 2 * KBn;
   const int64_t threads = RB * KD * 64;
-  SBN_LAUNCH("expand_dense", expand_dense_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st,
-             codes, meta, R, K, n, m, RB, KD, w);
+  const int64_t cplane = round_up(R * (K * n / (4 * m)), 16);    // readable bytes of the codes plane
+  int64_t blocks = cdiv(threads, 256);
+  if (blocks > 1024) blocks = 1024;                        // four blocks per CU, each table built once
+  const uint8_t* mp = (n == m) ? nullptr : meta;
+  if (m == 4)
+    SBN_LAUNCH("expand_dense", expand_dense_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st,
+               codes, mp, R, K, n, RB, KD, cplane, w);
+  else
+    SBN_LAUNCH("expand_dense", expand_dense_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, st,
+               codes, mp, R, K, n, RB, KD, cplane, w);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_gemm_t<false>(w, nullptr, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);

@@ -27,7 +27,7 @@
 //         LDS that maps (4 meta bits, the next 8 code bits) to the four weights
 //         of those positions (unused code bits are ignored); each block
 //         computes the table while its first loads are in flight.
-#include "sbn_internal.h"
+#include "sbn_decode.h"
 
 namespace sbn {
 namespace {
@@ -39,31 +39,6 @@ constexpr int GV_WAVES = SBN_GV_WAVES;  // waves per block
 constexpr int GV_RANGE = 4096 / GV_WAVES;   // K positions per wave range
 static_assert(GV_RANGE % 128 == 0 && GV_WAVES * 256 <= 4096, "GEMV range");
 constexpr int GV_MAX_BLOCKS = 2048;    // grid-stride cap (8 blocks per CU)
-
-// Unpack table entry e = nib | (c8 << 4): the four int8 weights of a group of
-// four positions whose meta bits are `nib` and whose survivors' 2-bit codes
-// start at the low end of `c8`.  The codes are spread to one byte each
-// (01 -> +1, 11 -> -1, 00 -> 0), then byte k of the entry takes survivor
-// number popcount(nib & ((1 << k) - 1)) if bit k of nib is set, else 0.
-__device__ inline uint32_t unpack_entry(uint32_t e) {
-  const uint32_t nib = e & 15u, c8 = (e >> 4) & 0xFFu;
-  const uint32_t sp = (((c8 & 0x33u) * 0x1001u) & 0x00030003u) | (((c8 & 0xCCu) * 0x40040u) & 0x03000300u);
-  const uint32_t v = sp | ((sp & 0x02020202u) * 0x7Eu);           // survivors, one per byte, in order
-  const uint32_t t = (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);   // byte k = bit k
-  const uint32_t pre = t * 0x01010100u;                            // byte k = set bits below k
-  const uint32_t msk = t * 0xFFu;
-  const uint32_t sel = (pre & msk) | (0x0C0C0C0Cu & ~msk);        // byte select; 0x0C yields 0
-  return __builtin_amdgcn_perm(0u, v, sel);
-}
-
-// bits [off, off+nb) of the normalised word array (off, nb compile-time after unrolling)
-template <int NW>
-__device__ inline uint32_t bits_at(const uint32_t (&w)[NW], int off, int nb) {
-  const int i = off >> 5, s = off & 31;
-  uint32_t v = w[i] >> s;
-  if (s + nb > 32 && i + 1 < NW) v = __builtin_amdgcn_alignbit(w[i + 1], w[i], s);
-  return nb >= 32 ? v : (v & ((1u << nb) - 1u));
-}
 
 // add the waves' 16 x 16 partial sums in LDS and write rows x tokens; thread
 // tid < 256 writes element tid (token (tid/4)%16), whose scale sxo it loaded early
@@ -102,34 +77,6 @@ __device__ inline float gemv_out_scale(int tid, int64_t T, const float* s_x, con
 }
 
 // ----------------------------------------------------------------------------- 2:4
-// One 32-position slice of a row: meta word mb (8 groups of 4 bits, two set)
-// and code word cb (16 survivors x 2 bits, in position order) -> the 16
-// compressed int8 values and the sixteen 2-bit position indices of
-// v_smfmac_i32_16x16x128_i8's A operand.
-__device__ inline void decode24(uint32_t mb, uint32_t cb, v4i& a, int& ix) {
-  // indices, per nibble (m3 m2 m1 m0, two bits set): p0 = lowest set bit,
-  // p1 = highest; p0 = (m1 & ~m0) + 2 (~m1 & ~m0), p1 = (m3 | ~m2) + 2 (m3 | m2),
-  // each bit formed in place from the word shifted by one position
-  const uint32_t L = mb << 1, Rr = mb >> 1, lx = L | mb;
-  ix = (int)((~mb & Rr & 0x11111111u) | (~lx & 0x22222222u) | ((Rr | ~mb) & 0x44444444u) | (lx & 0x88888888u));
-  // values: plane q holds, in byte d, the code of survivor 4d+q, turned into its
-  // int8 weight by a byte permute against the table {00 -> 0, 01 -> +1, 11 -> -1};
-  // words d and d+1 gather byte d and d+1 of the four planes
-  constexpr uint32_t TAB = 0xFF000100u;
-  const uint32_t e0 = __builtin_amdgcn_perm(0u, TAB, cb & 0x03030303u);
-  const uint32_t o1 = __builtin_amdgcn_perm(0u, TAB, (cb >> 2) & 0x03030303u);
-  const uint32_t e2 = __builtin_amdgcn_perm(0u, TAB, (cb >> 4) & 0x03030303u);
-  const uint32_t o3 = __builtin_amdgcn_perm(0u, TAB, (cb >> 6) & 0x03030303u);
-#pragma unroll
-  for (int d = 0; d < 4; d += 2) {
-    const uint32_t sel = ((uint32_t)(d + 5) << 24) | ((uint32_t)(d + 1) << 16) | ((uint32_t)(d + 4) << 8) | (uint32_t)d;
-    const uint32_t lo = __builtin_amdgcn_perm(o1, e0, sel);   // [e0_d, o1_d, e0_d+1, o1_d+1]
-    const uint32_t hi = __builtin_amdgcn_perm(o3, e2, sel);
-    a[d] = (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    a[d + 1] = (int)__builtin_amdgcn_perm(hi, lo, 0x07060302u);
-  }
-}
-
 // Range of 128*S positions (S <= SMAX steps); lane group g's run is positions
 // kbeg + 32*S*g + [0, 32*S), i.e. one meta word and one code word per step.
 // Step s maps the instruction's logical K index q (0..127) to position

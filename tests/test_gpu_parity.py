@@ -459,3 +459,13 @@ def test_pack_scale_rounding_near_midpoint(extra):
         assert f32_bits(sw) == 0x3F7FFE00                      # the even neighbour
     elif extra in (0x0001, 0x8001):
         assert f32_bits(sw) == 0x3F7FFE01
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 512, 1152])
+def test_gemm_2_4_k_steps(K):
+    """2:4 GEMM with one to nine K steps of 128, i.e. fewer steps than
+    pipeline stages, exactly as many, and more; two token tiles and three row
+    tiles with ragged tails."""
+    T, R = 300, 520
+    f, Xq, s_x, codes, meta, s_w = forward_case(T, R, K, 2, 4, seed=K)
+    check_outputs("gemm", f, Xq, s_x, codes, meta, s_w, R, 2, 4)
