@@ -141,8 +141,10 @@ hipEvent_t prof_event() {
     g_prof_pool.pop_back();
     return e;
   }
+  // timing-only events: no system-scope fence, so recording them does not add
+  // an L2 write-back and invalidate to the bracketed kernel's interval
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 

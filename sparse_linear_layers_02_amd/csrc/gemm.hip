@@ -27,9 +27,8 @@
 // between a memory phase (LDS reads of one step's fragments into registers,
 // plus the global loads of a later stage) and a compute phase (32 matrix
 // instructions), so one of them keeps the SIMD's matrix core busy while the
-// other waits on LDS.  Each block also prefetches into L2 its share of the
-// lines that the blocks running beside it on the same XCD will request a few
-// steps later.
+// other waits on LDS.  Consecutive blocks take tiles that share row and token
+// tiles on the same XCD (tile_of_block), so most operand lines come from L2.
 //
 // Operand layouts (gfx950, measured with a lane-layout check):
 //   16x16x64 i8 : A lane l -> row l%16, K[16*(l/16) .. +16); B lane l -> col l%16,
@@ -210,13 +209,8 @@ __device__ inline void pp_barrier() {
   sched_fence();
 }
 
-#ifndef SBN_GEMM_PF
-#define SBN_GEMM_PF 0
-#endif
-
-// OUT: 0 = int32 accumulator, 1 = float32, 2 = bf16.  PF: L2 prefetch distance
-// in steps beyond the stage being loaded (0 = none).
-template <bool SPARSE, int OUT, int PF>
+// OUT: 0 = int32 accumulator, 1 = float32, 2 = bf16.
+template <bool SPARSE, int OUT>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(
     const uint8_t* __restrict__ Aw, const uint8_t* __restrict__ Ai, const uint8_t* __restrict__ Xt,
     const float* __restrict__ s_x, const float* __restrict__ s_w, int64_t T, int64_t R,
@@ -229,17 +223,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   constexpr int STAGE = A_BYTES + I_BYTES + B_BYTES;
   constexpr int NST = SPARSE ? 3 : 4;
   // global loads per wave per stage: 2 W fragments, 4 (sparse) or 2 X blocks,
-  // the index block (waves 0..3, sparse), one prefetch
-  constexpr int LPS0 = 2 + (SPARSE ? 1 : 0) + 2 * BH + (PF ? 1 : 0);
-  constexpr int LPS1 = 2 + 2 * BH + (PF ? 1 : 0);
+  // the index block (waves 0..3, sparse)
+  constexpr int LPS0 = 2 + (SPARSE ? 1 : 0) + 2 * BH;
+  constexpr int LPS1 = 2 + 2 * BH;
   constexpr int WAIT0 = (NST - 2) * LPS0, WAIT1 = (NST - 2) * LPS1;
-  // L2 prefetch share of one block per step: a quarter of its row tile's lines
-  // and an eighth of its token tile's lines
-  constexpr int A_LINES = (A_BYTES + I_BYTES) / 128, B_LINES = B_BYTES / 128;
-  constexpr int PA = A_LINES / 4, PB = B_LINES / 8, PL = (PA + PB) / NW;
-  static_assert((PA + PB) % NW == 0, "prefetch share");
   constexpr int EPI_BYTES = NW * 64 * 272;              // bf16 epilogue staging, 64 x 272 B per wave
-  constexpr int SMEM = (NST * STAGE + 256) > EPI_BYTES ? (NST * STAGE + 256) : EPI_BYTES;
+  constexpr int SMEM = NST * STAGE > EPI_BYTES ? NST * STAGE : EPI_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x;
@@ -260,24 +249,6 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   }
   if (OUT != 0) sw = *s_w;
 
-  // prefetch line of this lane (lanes past the share repeat it)
-  const int pg = wave * PL + lane % PL;
-  const int pq = (int)(ttile & 3), pe = (int)(rtile & 7);
-  auto prefetch = [&](int64_t sp) {
-    sp = sp < nks ? sp : nks - 1;
-    const uint8_t* p;
-    if (pg < PA) {
-      const int L = pq * PA + pg;                      // line of the row tile's stage
-      if (L < A_BYTES / 128) p = Aw + ((rb0 + (L >> 3)) * fstride + sp) * 1024 + (L & 7) * 128;
-      else p = Ai + ((rb0 / 4 + ((L - A_BYTES / 128) >> 3)) * fstride + sp) * 1024 + (L & 7) * 128;
-    } else {
-      const int L = pe * PB + (pg - PA);               // line of the token tile's stage
-      const int per = BH * 8;                          // lines per token block per step
-      p = Xt + ((tb0 + L / per) * KC + sp * BH) * 1024 + (L % per) * 128;
-    }
-    g2lds4(p, smem + NST * STAGE);                     // lands in a scratch slot nobody reads
-  };
-
   auto load_stage = [&](int s, int64_t ks) {
     uint8_t* base = smem + s * STAGE;
 #pragma unroll
@@ -293,7 +264,6 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
       g2lds16(Xt + ((tb0 + hb / BH) * KC + ks * BH + hb % BH) * 1024 + lane * 16,
               base + A_BYTES + I_BYTES + hb * 1024);
     }
-    if (PF) prefetch(ks + PF);
   };
 
   v4i acc[MI][MJ];
@@ -450,7 +420,6 @@ template <bool SPARSE>
 hipError_t launch_gemm_t(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
                          const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y,
                          sbn_dtype ydt, int64_t ldy, hipStream_t st) {
-  constexpr int PF = SBN_GEMM_PF;
   const int64_t ntiles = cdiv(T, GEMM_TILE_T) * cdiv(R, GEMM_TILE_R);
   const dim3 grid((unsigned)ntiles), block(512);
   const int64_t nks = SPARSE ? KBn : K / 64;
@@ -458,11 +427,11 @@ hipError_t launch_gemm_t(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt
   const int64_t KC = 2 * KBn;
   const char* name = SPARSE ? "gemm_smfmac" : "gemm_mfma";
   if (ydt == SBN_I32_ACC)
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 0, PF>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 0>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
   else if (ydt == SBN_F32)
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 1, PF>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 1>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
   else
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 2, PF>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 2>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
   return hipGetLastError();
 }
 

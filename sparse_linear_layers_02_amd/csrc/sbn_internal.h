@@ -42,11 +42,6 @@ __device__ inline void g2lds16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
-// 4 bytes per lane into LDS at `lds_base + 4*lane`.
-__device__ inline void g2lds4(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
-}
 __device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // s_waitcnt with vmcnt = N (gfx9 encoding; expcnt and lgkmcnt left at "no wait")
