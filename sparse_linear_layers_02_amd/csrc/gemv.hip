@@ -183,6 +183,141 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv24_kernel(
   }
 }
 
+// ----------------------------------------------------------------------------- 2:4, streamed
+// K a multiple of 1024, at most 4096: wave w owns positions [1024w, 1024w + 1024)
+// of every row (eight steps of 128, lane group g's run = meta and code words
+// 8g .. 8g + 7 of the range) and walks the block's row groups.  The packed
+// words of the next GV_RING - 1 row groups stream into a ring in LDS that only
+// this wave uses, by direct global->LDS loads: several row groups are in
+// flight per wave without holding registers, and no load waits behind the math.
+// Ring slot: 16 rows x 128 B of meta, then the same of codes; 16-byte chunk c
+// of row r sits at chunk position c ^ (r & 7), so the eight lanes that read one
+// chunk position of eight rows touch eight different banks, and each 1 KB load
+// instruction still reads whole 128-byte row segments.  Survivor values are
+// decoded as 64 * w, so the partial sums are 64 times the accumulator.
+#ifndef SBN_GV_RING
+#define SBN_GV_RING 3
+#endif
+constexpr int GV_RING = SBN_GV_RING;
+#ifndef SBN_GV_STREAM
+#define SBN_GV_STREAM 1
+#endif
+constexpr int GV_STREAM_BLOCKS = 512;  // two blocks per CU
+
+template <int OUT>
+__global__ __launch_bounds__(256, 2) void gemv24s_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, const float* __restrict__ s_w,
+    int64_t R, void* __restrict__ Y, int64_t ldy) {
+  // one LDS array: [4 waves][GV_RING slots][4096 B] ring, then red[2][4][256] ints
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * GV_RING * 4096 + 2 * 4 * 256 * 4];
+  uint8_t (*ring)[GV_RING][4096] = (uint8_t (*)[GV_RING][4096])lds;
+  int (*red)[4][256] = (int (*)[4][256])(lds + 4 * GV_RING * 4096);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 4, rl = lane & 15;
+  const int64_t nrg = cdiv(R, 16), rowb = K / 8;
+  const bool has = wave < K / 1024;                    // wave-uniform
+  // scales of the output element this thread writes (token (tid / 4) % 16); the
+  // loads are unconditional so nothing waits for them before the loop
+  const int64_t tq = (tid >> 2) & 15;
+  const float sxv = OUT != 0 ? s_x[tq < T ? tq : 0] : 0.0f;
+  const float swv = OUT != 0 ? *s_w : 0.0f;
+  uint8_t* myring = &ring[wave][0][0];
+
+  // direct loads of one row group into ring slot `slot`: instruction q of a
+  // plane fills chunk positions 64q + lane (row (64q + lane) / 8)
+  auto issue = [&](int64_t rg, int slot) {
+    uint8_t* dst = myring + slot * 4096;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int sp = 64 * q + lane, rr = sp >> 3, ch = (sp & 7) ^ (rr & 7);
+      int64_t r = rg * 16 + rr;
+      r = r < R ? r : R - 1;                           // rows past R: row R-1, discarded
+      const int64_t off = r * rowb + 128 * wave + 16 * ch;
+      g2lds16(meta + off, dst + 1024 * q);
+      g2lds16(codes + off, dst + 2048 + 1024 * q);
+    }
+  };
+
+  int64_t rg = blockIdx.x;
+  const int64_t gs = gridDim.x;
+  if (has) {
+#pragma unroll
+    for (int i = 0; i < GV_RING - 1; ++i)
+      if (rg + i * gs < nrg) issue(rg + i * gs, i);
+  }
+  // activations of this wave's range, kept in registers (as gemv24 with S = 8)
+  const bool tvalid = rl < T;
+  const int8_t* xrow = Xq + (tvalid ? rl : 0) * K;
+  v4i blo[8], bhi[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int64_t lo = 1024 * wave + 256 * (g >> 1) + 32 * s + 16 * (g & 1);
+    const bool ok = has && tvalid;
+    blo[s] = ok ? *(const v4i*)(xrow + lo) : (v4i){0, 0, 0, 0};
+    bhi[s] = ok ? *(const v4i*)(xrow + lo + 512) : (v4i){0, 0, 0, 0};
+  }
+  // make the activations (and with them the first ring slots) resident before
+  // the loop, whose only global loads are the counted ring loads
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(blo[s]), "v"(bhi[s]));
+
+  // row groups of this block: rg = blockIdx.x + i * gs, i < nit
+  const int nit = rg < nrg ? (int)((nrg - 1 - rg) / gs) + 1 : 0;
+  int slot = 0, par = 0;
+  for (int it = 0; it < nit; ++it, rg += gs) {
+    v4i acc = (v4i){0, 0, 0, 0};
+    if (has) {
+      if (it + GV_RING - 1 < nit) issue(rg + (GV_RING - 1) * gs, (slot + GV_RING - 1) % GV_RING);
+      // this slot's loads are done once at most 4 per later row group remain
+      const int later = nit - 1 - it;
+      if (later >= GV_RING - 1) wait_vmcnt<4 * (GV_RING - 1)>();
+      else if (GV_RING > 3 && later == 2) wait_vmcnt<8>();
+      else if (later == 1) wait_vmcnt<4>();
+      else wait_vmcnt<0>();
+      const uint8_t* sl = myring + slot * 4096 + rl * 128;
+      const int c0 = (2 * g) ^ (rl & 7), c1 = (2 * g + 1) ^ (rl & 7);
+      const v4i m0 = *(const v4i*)(sl + 16 * c0), m1 = *(const v4i*)(sl + 16 * c1);
+      const v4i k0 = *(const v4i*)(sl + 2048 + 16 * c0), k1 = *(const v4i*)(sl + 2048 + 16 * c1);
+      const uint32_t mw[8] = {(uint32_t)m0[0], (uint32_t)m0[1], (uint32_t)m0[2], (uint32_t)m0[3],
+                              (uint32_t)m1[0], (uint32_t)m1[1], (uint32_t)m1[2], (uint32_t)m1[3]};
+      const uint32_t cw[8] = {(uint32_t)k0[0], (uint32_t)k0[1], (uint32_t)k0[2], (uint32_t)k0[3],
+                              (uint32_t)k1[0], (uint32_t)k1[1], (uint32_t)k1[2], (uint32_t)k1[3]};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        v4i a;
+        int ix;
+        decode24_x64(mw[s], cw[s], a, ix);
+        const v8i b = (v8i){blo[s][0], blo[s][1], blo[s][2], blo[s][3], bhi[s][0], bhi[s][1], bhi[s][2], bhi[s][3]};
+        acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, acc, ix, 0, 0);
+      }
+      slot = slot + 1 == GV_RING ? 0 : slot + 1;
+    }
+    // partial sums of the four waves, double-buffered so one barrier per row group suffices
+    *(v4i*)&red[par][wave][lane * 4] = acc;
+    lds_barrier();
+    {
+      const int e = tid;
+      const int s64 = red[par][0][e] + red[par][1][e] + red[par][2][e] + red[par][3][e];
+      const int sum = s64 >> 6;                        // exact: every partial is a multiple of 64
+      const int L = e >> 2, v = e & 3;
+      const int64_t row = rg * 16 + 4 * (L >> 4) + v;
+      const int64_t t = L & 15;
+      if (t < T && row < R) {
+        if (OUT == 0) {
+          ((int*)Y)[t * ldy + row] = sum;
+        } else {
+          const float y = (float)sum * (swv * sxv);
+          if (OUT == 1) ((float*)Y)[t * ldy + row] = y;
+          else ((uint16_t*)Y)[t * ldy + row] = f32_to_bf16_rne(y);
+        }
+      }
+    }
+    par ^= 1;
+  }
+}
+
 // ----------------------------------------------------------------------------- table path
 // Range of 64*S positions (S <= SMAX steps); lane group g's run is positions
 // p0 = kbeg + 16*S*g + [0, 16*S); step j takes positions p0 + 16*j .. +16 as
@@ -330,6 +465,16 @@ hipError_t launch_gemv_nm(const int8_t* Xq, const float* s_x, int64_t T, int64_t
   const int64_t nrg = cdiv(R, 16);
   const dim3 grid((unsigned)(nrg < GV_MAX_BLOCKS ? nrg : GV_MAX_BLOCKS)), block(64 * GV_WAVES);
   const uint8_t* mp = (N == M) ? nullptr : meta;
+  if (SBN_GV_STREAM && N == 2 && M == 4 && K % 1024 == 0 && K <= 4096) {
+    const dim3 sgrid((unsigned)(nrg < GV_STREAM_BLOCKS ? nrg : GV_STREAM_BLOCKS)), sblock(256);
+    if (ydt == SBN_I32_ACC)
+      SBN_LAUNCH("gemv", gemv24s_kernel<0>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    else if (ydt == SBN_F32)
+      SBN_LAUNCH("gemv", gemv24s_kernel<1>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    else
+      SBN_LAUNCH("gemv", gemv24s_kernel<2>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    return hipGetLastError();
+  }
   if (N == 2 && M == 4 && K % 128 == 0) {
     if (ydt == SBN_I32_ACC)
       SBN_LAUNCH("gemv", gemv24_kernel<0>, grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);

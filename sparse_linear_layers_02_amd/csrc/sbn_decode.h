@@ -91,4 +91,24 @@ __device__ inline void decode24(uint32_t mb, uint32_t cb, v4i& a, int& ix) {
   }
 }
 
+// decode24 with the values as 64 * w: each survivor's code in the top two bits
+// of its byte (0x40 = +64, 0xC0 = -64, 0 = 0), so the products sum to 64 times
+// the accumulator.  Plane q = (cb << (6 - 2q)) & 0xC0C0C0C0 holds in byte d the
+// code of survivor 4d + q; two rounds of byte permutes transpose the four
+// planes into survivor order.
+__device__ inline void decode24_x64(uint32_t mb, uint32_t cb, v4i& a, int& ix) {
+  const uint32_t L = mb << 1, Rr = mb >> 1, lx = L | mb;
+  ix = (int)((~mb & Rr & 0x11111111u) | (~lx & 0x22222222u) | ((Rr | ~mb) & 0x44444444u) | (lx & 0x88888888u));
+  const uint32_t p0 = (cb << 6) & 0xC0C0C0C0u, p1 = (cb << 4) & 0xC0C0C0C0u;
+  const uint32_t p2 = (cb << 2) & 0xC0C0C0C0u, p3 = cb & 0xC0C0C0C0u;
+  const uint32_t q01l = __builtin_amdgcn_perm(p1, p0, 0x05010400u);   // [p0.0, p1.0, p0.1, p1.1]
+  const uint32_t q01h = __builtin_amdgcn_perm(p1, p0, 0x07030602u);   // [p0.2, p1.2, p0.3, p1.3]
+  const uint32_t q23l = __builtin_amdgcn_perm(p3, p2, 0x05010400u);
+  const uint32_t q23h = __builtin_amdgcn_perm(p3, p2, 0x07030602u);
+  a[0] = (int)__builtin_amdgcn_perm(q23l, q01l, 0x05040100u);         // survivors 0..3
+  a[1] = (int)__builtin_amdgcn_perm(q23l, q01l, 0x07060302u);         // 4..7
+  a[2] = (int)__builtin_amdgcn_perm(q23h, q01h, 0x05040100u);         // 8..11
+  a[3] = (int)__builtin_amdgcn_perm(q23h, q01h, 0x07060302u);         // 12..15
+}
+
 }  // namespace sbn
