@@ -196,16 +196,92 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv24_kernel(
 // instruction still reads whole 128-byte row segments.  Survivor values are
 // decoded as 64 * w, so the partial sums are 64 times the accumulator.
 #ifndef SBN_GV_RING
-#define SBN_GV_RING 3
+#define SBN_GV_RING 2
 #endif
 constexpr int GV_RING = SBN_GV_RING;
 #ifndef SBN_GV_STREAM
 #define SBN_GV_STREAM 1
 #endif
-constexpr int GV_STREAM_BLOCKS = 512;  // two blocks per CU
+#ifndef SBN_GV_BPC
+#define SBN_GV_BPC 3
+#endif
+constexpr int GV_BPC = SBN_GV_BPC;                   // resident blocks per CU
+constexpr int GV_STREAM_BLOCKS = 256 * GV_BPC;
+
+// Streamed kernels: a block walks consecutive row groups, and row groups 4k ..
+// 4k + 3 (64 rows) form one output group.  Per row group the four waves' 16 x 16
+// partial sums (64 times the accumulator) go through red (one of two buffers,
+// alternating per row group, so one barrier per row group suffices).  Lane
+// (t = tid / 16, r = tid % 16) owns rows 4r .. 4r + 3 of its output group for
+// token t: it sums them (16 contiguous bytes of each wave's partials) after row
+// group r / 4 of the group and keeps them in registers; once the group is
+// complete they are stored together, so each token's 64 outputs leave as one
+// contiguous 128- or 256-byte run instead of four 32-byte pieces.
+template <int OUT>
+struct StreamOut {
+  v4i v;                                               // this lane's four outputs (bf16: v[0..1] packed)
+  int64_t prow = -1;                                   // first row of a pending store (-1: none)
+  // j: place of this row group in its output group (row group index mod 4); j0:
+  // the first place this block fills in that group; last: the block's last row group.
+  // A completed group's stores are only recorded here and issued by commit(),
+  // which the kernel calls right after its next wait for ring loads: a store
+  // counts in the same vmcnt as the ring loads, so a store issued just before
+  // such a wait would make the wait cover the store's latency too.
+  __device__ inline void row_group(int (*red)[256], v4i acc, int tid, int wave, int lane, int j, int j0, bool last,
+                                   int64_t grp_row0, int64_t T, float swv, float sxv) {
+    *(v4i*)&red[wave][lane * 4] = acc;
+    lds_barrier();
+    const int t = tid >> 4, r = tid & 15;
+    if ((r >> 2) == j && t < T) {
+      // rows 4 (r % 4) .. +3 of this row group: entries 64 (r % 4) + 4 t + 0..3 of every wave's partials
+      const int e = 64 * (r & 3) + 4 * t;
+      const v4i a = *(const v4i*)&red[0][e] + *(const v4i*)&red[1][e] + *(const v4i*)&red[2][e] + *(const v4i*)&red[3][e];
+      const v4i sum = a >> 6;                          // exact: every partial is a multiple of 64
+      if (OUT == 0) {
+        v = sum;
+      } else {
+        const float sc = swv * sxv;
+        float y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y[q] = (float)sum[q] * sc;
+        if (OUT == 1) {
+          v = (v4i){(int)__float_as_uint(y[0]), (int)__float_as_uint(y[1]), (int)__float_as_uint(y[2]), (int)__float_as_uint(y[3])};
+        } else {
+          v[0] = (int)((uint32_t)f32_to_bf16_rne(y[0]) | ((uint32_t)f32_to_bf16_rne(y[1]) << 16));
+          v[1] = (int)((uint32_t)f32_to_bf16_rne(y[2]) | ((uint32_t)f32_to_bf16_rne(y[3]) << 16));
+        }
+      }
+    }
+    if ((j == 3 || last) && (r >> 2) >= j0 && (r >> 2) <= j && t < T) prow = grp_row0 + 4 * r;
+  }
+  __device__ inline void commit(int tid, int64_t R, void* Y, int64_t ldy) {
+    if (prow < 0) return;
+    const int64_t row = prow, t = tid >> 4;
+    prow = -1;
+    if (OUT == 2) {
+      uint16_t* y = (uint16_t*)Y + t * ldy + row;
+      if (row + 4 <= R) {
+        *(uint2*)y = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (row + q < R) y[q] = (uint16_t)((uint32_t)v[q >> 1] >> (16 * (q & 1)));
+      }
+    } else {
+      int* y = (int*)Y + t * ldy + row;
+      if (row + 4 <= R) {
+        *(v4i*)y = v;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (row + q < R) y[q] = v[q];
+      }
+    }
+  }
+};
 
 template <int OUT>
-__global__ __launch_bounds__(256, 2) void gemv24s_kernel(
+__global__ __launch_bounds__(256, GV_BPC) void gemv24s_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K,
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, const float* __restrict__ s_w,
     int64_t R, void* __restrict__ Y, int64_t ldy) {
@@ -218,34 +294,45 @@ __global__ __launch_bounds__(256, 2) void gemv24s_kernel(
   const int g = lane >> 4, rl = lane & 15;
   const int64_t nrg = cdiv(R, 16), rowb = K / 8;
   const bool has = wave < K / 1024;                    // wave-uniform
-  // scales of the output element this thread writes (token (tid / 4) % 16); the
+  // scales of the output element this thread writes (token tid / 16); the
   // loads are unconditional so nothing waits for them before the loop
-  const int64_t tq = (tid >> 2) & 15;
+  const int64_t tq = tid >> 4;
   const float sxv = OUT != 0 ? s_x[tq < T ? tq : 0] : 0.0f;
   const float swv = OUT != 0 ? *s_w : 0.0f;
   uint8_t* myring = &ring[wave][0][0];
 
   // direct loads of one row group into ring slot `slot`: instruction q of a
   // plane fills chunk positions 64q + lane (row (64q + lane) / 8)
+  int rowq[2], colq[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int sp = 64 * q + lane, rr = sp >> 3;
+    rowq[q] = rr;
+    colq[q] = 128 * wave + 16 * ((sp & 7) ^ (rr & 7));
+  }
   auto issue = [&](int64_t rg, int slot) {
     uint8_t* dst = myring + slot * 4096;
+    const int64_t base = rg * 16 * rowb;               // wave-uniform
+    const bool full = rg * 16 + 16 <= R;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int sp = 64 * q + lane, rr = sp >> 3, ch = (sp & 7) ^ (rr & 7);
-      int64_t r = rg * 16 + rr;
-      r = r < R ? r : R - 1;                           // rows past R: row R-1, discarded
-      const int64_t off = r * rowb + 128 * wave + 16 * ch;
-      g2lds16(meta + off, dst + 1024 * q);
-      g2lds16(codes + off, dst + 2048 + 1024 * q);
+      int off = rowq[q] * (int)rowb + colq[q];
+      if (!full) {                                     // rows past R: row R-1, discarded
+        const int64_t r = rg * 16 + rowq[q] < R ? rowq[q] : R - 1 - rg * 16;
+        off = (int)r * (int)rowb + colq[q];
+      }
+      g2lds16(meta + base + off, dst + 1024 * q);
+      g2lds16(codes + base + off, dst + 2048 + 1024 * q);
     }
   };
 
-  int64_t rg = blockIdx.x;
-  const int64_t gs = gridDim.x;
+  // this block's row groups: [rg0, rg0 + nit), consecutive
+  const int64_t rg0 = (int64_t)blockIdx.x * nrg / gridDim.x;
+  const int nit = (int)(((int64_t)blockIdx.x + 1) * nrg / gridDim.x - rg0);
   if (has) {
 #pragma unroll
     for (int i = 0; i < GV_RING - 1; ++i)
-      if (rg + i * gs < nrg) issue(rg + i * gs, i);
+      if (i < nit) issue(rg0 + i, i);
   }
   // activations of this wave's range, kept in registers (as gemv24 with S = 8)
   const bool tvalid = rl < T;
@@ -263,19 +350,19 @@ __global__ __launch_bounds__(256, 2) void gemv24s_kernel(
 #pragma unroll
   for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(blo[s]), "v"(bhi[s]));
 
-  // row groups of this block: rg = blockIdx.x + i * gs, i < nit
-  const int nit = rg < nrg ? (int)((nrg - 1 - rg) / gs) + 1 : 0;
+  StreamOut<OUT> out;
   int slot = 0, par = 0;
-  for (int it = 0; it < nit; ++it, rg += gs) {
+  for (int it = 0; it < nit; ++it) {
     v4i acc = (v4i){0, 0, 0, 0};
     if (has) {
-      if (it + GV_RING - 1 < nit) issue(rg + (GV_RING - 1) * gs, (slot + GV_RING - 1) % GV_RING);
+      if (it + GV_RING - 1 < nit) issue(rg0 + it + GV_RING - 1, (slot + GV_RING - 1) % GV_RING);
       // this slot's loads are done once at most 4 per later row group remain
       const int later = nit - 1 - it;
       if (later >= GV_RING - 1) wait_vmcnt<4 * (GV_RING - 1)>();
       else if (GV_RING > 3 && later == 2) wait_vmcnt<8>();
       else if (later == 1) wait_vmcnt<4>();
       else wait_vmcnt<0>();
+      out.commit(tid, R, Y, ldy);
       const uint8_t* sl = myring + slot * 4096 + rl * 128;
       const int c0 = (2 * g) ^ (rl & 7), c1 = (2 * g + 1) ^ (rl & 7);
       const v4i m0 = *(const v4i*)(sl + 16 * c0), m1 = *(const v4i*)(sl + 16 * c1);
@@ -294,28 +381,176 @@ __global__ __launch_bounds__(256, 2) void gemv24s_kernel(
       }
       slot = slot + 1 == GV_RING ? 0 : slot + 1;
     }
-    // partial sums of the four waves, double-buffered so one barrier per row group suffices
-    *(v4i*)&red[par][wave][lane * 4] = acc;
-    lds_barrier();
     {
-      const int e = tid;
-      const int s64 = red[par][0][e] + red[par][1][e] + red[par][2][e] + red[par][3][e];
-      const int sum = s64 >> 6;                        // exact: every partial is a multiple of 64
-      const int L = e >> 2, v = e & 3;
-      const int64_t row = rg * 16 + 4 * (L >> 4) + v;
-      const int64_t t = L & 15;
-      if (t < T && row < R) {
-        if (OUT == 0) {
-          ((int*)Y)[t * ldy + row] = sum;
-        } else {
-          const float y = (float)sum * (swv * sxv);
-          if (OUT == 1) ((float*)Y)[t * ldy + row] = y;
-          else ((uint16_t*)Y)[t * ldy + row] = f32_to_bf16_rne(y);
-        }
-      }
+      const int64_t rgi = rg0 + it;                    // output groups: row groups 4k .. 4k + 3
+      const int j0 = it < 4 - (int)(rg0 & 3) ? (int)(rg0 & 3) : 0;
+      out.row_group(red[par], acc, tid, wave, lane, (int)(rgi & 3), j0, it == nit - 1, (rgi & ~(int64_t)3) * 16,
+                    T, swv, sxv);
     }
     par ^= 1;
+    if (!has) out.commit(tid, R, Y, ldy);
   }
+  out.commit(tid, R, Y, ldy);
+}
+
+
+// ----------------------------------------------------------------------------- 6:8, streamed
+// Same walk as gemv24s with the dense v_mfma_i32_16x16x64_i8: wave w owns
+// positions [1024w, 1024w + 1024) of every row, sixteen steps of 64; lane group
+// g's run is positions 256g .. 256g + 255 of the range (meta words 8g .. 8g+7,
+// code words 12g .. 12g+11), step s takes positions 256g + 16s .. +16 as A lane
+// (r, g) and the same activation bytes as B lane (t, g).  Ring slot: 16 rows x
+// 128 B of meta (chunk c of row r at chunk position c ^ (r & 7)), then 16 rows x
+// 192 B of codes (chunk c at position (c + (r & 7)) mod 12).
+// Decode of one step (two groups: 16 meta bits, twelve 2-bit codes f0..f11):
+// planes P_q = (codes << (6 - 2q)) & 0xC0C0C0C0 hold f_{4b+q} in byte b as
+// 64 * w; one round of byte permutes gives
+//   A = [f0 f1 f4 f5]  B = [f2 f3 f6 f7]  C = [f8 f9 . .]  D = [f10 f11 . .]
+// and each output word (four positions) is one permute of a pair of those,
+// with a selector taken from a 256-entry table indexed by the group's meta
+// byte (0x0C selects a zero byte at a pruned position).
+__device__ inline v4i lut68_entry(uint32_t mb) {
+  // survivor rank -> byte of the permute window, per output word
+  constexpr uint32_t M0[6] = {0, 1, 4, 5, 2, 3};            // words 0, 1: window (lo A, hi B)
+  constexpr uint32_t M2[6] = {2, 3, 4, 5, 12, 12};          // word 2: window (lo B, hi C)
+  constexpr uint32_t M3[6] = {12, 12, 0, 1, 4, 5};          // word 3: window (lo C, hi D)
+  uint32_t w[4] = {0, 0, 0, 0};
+  uint32_t r = 0;
+  for (int p = 0; p < 8; ++p) {
+    const bool on = (mb >> p) & 1u;
+    const uint32_t rr = r < 6 ? r : 5;
+    const uint32_t a = on ? M0[rr] : 12u, b = on ? (p < 4 ? M2[rr] : M3[rr]) : 12u;
+    w[p >> 2] |= a << (8 * (p & 3));
+    w[2 + (p >> 2)] |= b << (8 * (p & 3));
+    r += on ? 1u : 0u;
+  }
+  return (v4i){(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+}
+
+template <int OUT>
+__global__ __launch_bounds__(256, GV_BPC) void gemv68s_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K,
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, const float* __restrict__ s_w,
+    int64_t R, void* __restrict__ Y, int64_t ldy) {
+  constexpr int SLOT = 2048 + 3072;
+  // one LDS array: [4 waves][GV_RING][SLOT] ring, the 256 x 16 B table, red[2][4][256]
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * GV_RING * SLOT + 4096 + 2 * 4 * 256 * 4];
+  uint8_t* ring = lds;
+  uint8_t* lut = lds + 4 * GV_RING * SLOT;
+  int (*red)[4][256] = (int (*)[4][256])(lut + 4096);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 4, rl = lane & 15;
+  const int64_t nrg = cdiv(R, 16), rowm = K / 8, rowc = K * 3 / 16;
+  const bool has = wave < K / 1024;
+  const int64_t tq = tid >> 4;
+  const float sxv = OUT != 0 ? s_x[tq < T ? tq : 0] : 0.0f;
+  const float swv = OUT != 0 ? *s_w : 0.0f;
+  uint8_t* myring = ring + wave * GV_RING * SLOT;
+
+  // per-lane sources of the five 1 KB loads of a row group (row offset, column offset)
+  int rowA[5], colA[5];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {                          // meta: chunk positions 64q + lane
+    const int sp = 64 * q + lane, rr = sp >> 3;
+    rowA[q] = rr;
+    colA[q] = 128 * wave + 16 * ((sp & 7) ^ (rr & 7));
+  }
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {                          // codes: chunk positions 64q + lane
+    const int sp = 64 * q + lane, rr = sp / 12, pos = sp - 12 * rr;
+    const int c = pos - (rr & 7) < 0 ? pos - (rr & 7) + 12 : pos - (rr & 7);
+    rowA[2 + q] = rr;
+    colA[2 + q] = 192 * wave + 16 * c;
+  }
+  auto issue = [&](int64_t rg, int slot) {
+    uint8_t* dst = myring + slot * SLOT;
+    const uint8_t* mb = meta + rg * 16 * rowm;         // wave-uniform row-group bases
+    const uint8_t* cb = codes + rg * 16 * rowc;
+    const bool full = rg * 16 + 16 <= R;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      int r = rowA[q];
+      if (!full && rg * 16 + r >= R) r = (int)(R - 1 - rg * 16);   // rows past R: row R-1, discarded
+      if (q < 2) g2lds16(mb + r * (int)rowm + colA[q], dst + 1024 * q);
+      else g2lds16(cb + r * (int)rowc + colA[q], dst + 2048 + 1024 * (q - 2));
+    }
+  };
+
+  // this block's row groups: [rg0, rg0 + nit), consecutive
+  const int64_t rg0 = (int64_t)blockIdx.x * nrg / gridDim.x;
+  const int nit = (int)(((int64_t)blockIdx.x + 1) * nrg / gridDim.x - rg0);
+  if (has) {
+#pragma unroll
+    for (int i = 0; i < GV_RING - 1; ++i)
+      if (i < nit) issue(rg0 + i, i);
+  }
+  *(v4i*)(lut + 16 * tid) = lut68_entry((uint32_t)tid);
+  const bool tvalid = rl < T;
+  const int8_t* xrow = Xq + (tvalid ? rl : 0) * K;
+  v4i bx[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+    bx[s] = (has && tvalid) ? *(const v4i*)(xrow + 1024 * wave + 256 * g + 16 * s) : (v4i){0, 0, 0, 0};
+#pragma unroll
+  for (int s = 0; s < 16; ++s) asm volatile("" ::"v"(bx[s]));
+  lds_barrier();                                       // table complete
+
+  StreamOut<OUT> out;
+  int slot = 0, par = 0;
+  for (int it = 0; it < nit; ++it) {
+    v4i acc = (v4i){0, 0, 0, 0};
+    if (has) {
+      if (it + GV_RING - 1 < nit) issue(rg0 + it + GV_RING - 1, (slot + GV_RING - 1) % GV_RING);
+      const int later = nit - 1 - it;
+      if (later >= GV_RING - 1) wait_vmcnt<5 * (GV_RING - 1)>();
+      else if (GV_RING > 3 && later == 2) wait_vmcnt<10>();
+      else if (later == 1) wait_vmcnt<5>();
+      else wait_vmcnt<0>();
+      out.commit(tid, R, Y, ldy);
+      const uint8_t* sl = myring + slot * SLOT;
+      const uint8_t* sm = sl + rl * 128;
+      const uint8_t* sc = sl + 2048 + rl * 192;
+      const int r7 = rl & 7;
+      const v4i m0 = *(const v4i*)(sm + 16 * ((2 * g) ^ r7)), m1 = *(const v4i*)(sm + 16 * ((2 * g + 1) ^ r7));
+      uint32_t cw[12];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int c = 3 * g + i + r7;
+        const v4i v = *(const v4i*)(sc + 16 * (c < 12 ? c : c - 12));
+        cw[4 * i] = (uint32_t)v[0]; cw[4 * i + 1] = (uint32_t)v[1]; cw[4 * i + 2] = (uint32_t)v[2]; cw[4 * i + 3] = (uint32_t)v[3];
+      }
+      const uint32_t mw[8] = {(uint32_t)m0[0], (uint32_t)m0[1], (uint32_t)m0[2], (uint32_t)m0[3],
+                              (uint32_t)m1[0], (uint32_t)m1[1], (uint32_t)m1[2], (uint32_t)m1[3]};
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const uint32_t m16 = mw[s >> 1] >> (16 * (s & 1));
+        const int bo = 24 * s, wi = bo >> 5, sh = bo & 31;
+        const uint32_t c = sh == 0 ? cw[wi] : __builtin_amdgcn_alignbit(cw[wi + 1 < 12 ? wi + 1 : 11], cw[wi], sh);
+        const uint32_t p0 = (c << 6) & 0xC0C0C0C0u, p1 = (c << 4) & 0xC0C0C0C0u;
+        const uint32_t p2 = (c << 2) & 0xC0C0C0C0u, p3 = c & 0xC0C0C0C0u;
+        const uint32_t A = __builtin_amdgcn_perm(p1, p0, 0x05010400u);   // [f0 f1 f4 f5]
+        const uint32_t B = __builtin_amdgcn_perm(p3, p2, 0x05010400u);   // [f2 f3 f6 f7]
+        const uint32_t C = __builtin_amdgcn_perm(p1, p0, 0x07030602u);   // [f8 f9 . .]
+        const uint32_t D = __builtin_amdgcn_perm(p3, p2, 0x07030602u);   // [f10 f11 . .]
+        const uint2 s01 = *(const uint2*)(lut + 16 * (m16 & 0xFFu));
+        const uint2 s23 = *(const uint2*)(lut + 16 * ((m16 >> 8) & 0xFFu) + 8);
+        const v4i a = (v4i){(int)__builtin_amdgcn_perm(B, A, s01.x), (int)__builtin_amdgcn_perm(B, A, s01.y),
+                            (int)__builtin_amdgcn_perm(C, B, s23.x), (int)__builtin_amdgcn_perm(D, C, s23.y)};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx[s], acc, 0, 0, 0);
+      }
+      slot = slot + 1 == GV_RING ? 0 : slot + 1;
+    }
+    {
+      const int64_t rgi = rg0 + it;                    // output groups: row groups 4k .. 4k + 3
+      const int j0 = it < 4 - (int)(rg0 & 3) ? (int)(rg0 & 3) : 0;
+      out.row_group(red[par], acc, tid, wave, lane, (int)(rgi & 3), j0, it == nit - 1, (rgi & ~(int64_t)3) * 16,
+                    T, swv, sxv);
+    }
+    par ^= 1;
+    if (!has) out.commit(tid, R, Y, ldy);
+  }
+  out.commit(tid, R, Y, ldy);
 }
 
 // ----------------------------------------------------------------------------- table path
@@ -473,6 +708,16 @@ hipError_t launch_gemv_nm(const int8_t* Xq, const float* s_x, int64_t T, int64_t
       SBN_LAUNCH("gemv", gemv24s_kernel<1>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
     else
       SBN_LAUNCH("gemv", gemv24s_kernel<2>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    return hipGetLastError();
+  }
+  if (SBN_GV_STREAM && N == 6 && M == 8 && K % 1024 == 0 && K <= 4096) {
+    const dim3 sgrid((unsigned)(nrg < GV_STREAM_BLOCKS ? nrg : GV_STREAM_BLOCKS)), sblock(256);
+    if (ydt == SBN_I32_ACC)
+      SBN_LAUNCH("gemv", gemv68s_kernel<0>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    else if (ydt == SBN_F32)
+      SBN_LAUNCH("gemv", gemv68s_kernel<1>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
+    else
+      SBN_LAUNCH("gemv", gemv68s_kernel<2>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
     return hipGetLastError();
   }
   if (N == 2 && M == 4 && K % 128 == 0) {

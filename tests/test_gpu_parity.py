@@ -273,6 +273,27 @@ def test_gemv_all_ratios_short_k(n, m):
 
 
 @pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
+@pytest.mark.parametrize("K", [1024, 2048, 3072, 4096])
+@pytest.mark.parametrize("T,R", [(1, 37), (5, 1000), (16, 203)])
+def test_gemv_streamed_shapes(n, m, K, T, R):
+    """The streamed decode kernels (K a multiple of 1024 up to 4096): one to four
+    waves with a range, ragged R (rows past R read row R-1 and are dropped)."""
+    f, Xq, s_x, codes, meta, s_w = forward_case(T, R, K, n, m, seed=K + T + R)
+    check_outputs("gemv", f, Xq, s_x, codes, meta, s_w, R, n, m)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
+def test_gemv_streamed_ring_tail(n, m):
+    """Many more row groups than blocks (at most 1024 blocks): each block walks
+    five or more consecutive row groups through its ring, so the loads-in-flight
+    count drains at the tail, outputs leave in one full group of four row groups
+    and one partial group, and the last row group is ragged."""
+    R, K, T = 1024 * 16 * 5 + 40, 1024, 3
+    f, Xq, s_x, codes, meta, s_w = forward_case(T, R, K, n, m, seed=5)
+    check_outputs("gemv", f, Xq, s_x, codes, meta, s_w, R, n, m)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
 def test_gemv_decode_full_size(n, m):
     wl = WORKLOADS["decode"]
     W, eff, cp, mp, sw = full_ref("decode", n, m)
