@@ -23,11 +23,12 @@ same line carries:
                 against MI355X's published dense peak (the fraction of the
                 structured-sparse int8 peak is printed beside it);
   decode_gemv   the other half of the metric: GB/s of the decode GEMV
-                (R = K = 4096, T = 1, 2:4 and 6:8) three ways: (i) one call on
-                a cold packed weight, (ii-a) the steady state over a pool of
-                distinct packed weights larger than the 256 MB Infinity Cache,
-                replayed as four HIP graphs on four streams, (ii-b) one call
-                over 64 such weights stacked along R (268-336 MB);
+                (R = K = 4096, T = 1, 2:4 and 6:8) over a pool of 128 distinct
+                packed weights (twice the 256 MB Infinity Cache or more), three
+                ways: (i) one call on a cold weight, (ii-a) the pool as
+                separate calls replayed as four HIP graphs on four streams,
+                (ii-b) the pool as batched calls of 64 weights sharing the
+                activations (one launch each), replayed from a HIP graph;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 Multi-GPU runs are not part of this build: --gpus above 1 exits.
 """
@@ -198,11 +199,14 @@ def profile_pass(step, steps, kernel=None):
 
 # ---------------------------------------------------------------------- decode GEMV
 def decode_gemv(n=2, m=4, T=1, reps=5):
-    """Decode GEMV at R = K = 4096 over packed weights that do not fit the
-    Infinity Cache: (i) one call per cold weight, kernel time from the
-    library's events; (ii-a) the pool replayed as four HIP graphs on four
-    streams so launch ramps overlap; (ii-b) 64 weights stacked along R in one
-    call.  GB/s = algorithmic bytes (packed W + Xq + s_x + Y + s_w) / time."""
+    """Decode GEMV at R = K = 4096 over a pool of 128 distinct packed weights
+    (537 MB at 2:4, 671 MB at 6:8: at least twice the 256 MB Infinity Cache, so
+    every weight comes from HBM): (i) one call per cold weight, kernel time
+    from the library's events; (ii-a) the pool as separate calls, replayed as
+    four HIP graphs on four streams so launch ramps overlap; (ii-b) the pool
+    as batched calls of 64 weights that share the activations (one launch
+    each), replayed from a HIP graph.  GB/s = algorithmic bytes (packed W +
+    Xq + s_x + Y + s_w per weight) / time."""
     import torch
     import sparse_linear_layers_02_amd as sbn
     from workloads import WORKLOADS
@@ -212,77 +216,74 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
     del W
     cb, mb = sbn.sbn_packed_bytes(wl.R, wl.K, n, m)
     per = cb + mb
-    P = (MALL_BYTES * 3 // 2 // per + 1 + 3) // 4 * 4      # pool 1.5x the Infinity Cache, 4 | P
+    P, B = 128, 64
+    assert P * per >= 2 * MALL_BYTES
     codes = [codes0.clone() for _ in range(P)]
     metas = [meta0.clone() for _ in range(P)]
+    s_ws = [s_w.clone() for _ in range(P)]
     Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0, T=T)))
-    Ys = [torch.empty((T, wl.R), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    Ys = [torch.empty((T, wl.R), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
     algo = per + T * wl.K + 4 * T + 2 * T * wl.R + 4
 
-    def call(i, y=0):
-        sbn.sbn_sparse_ternary_gemv(Xq, s_x, codes[i], metas[i], s_w, wl.R, n, m, Y=Ys[y])
+    def call(i):
+        sbn.sbn_sparse_ternary_gemv(Xq, s_x, codes[i], metas[i], s_ws[i], wl.R, n, m, Y=Ys[i])
+
+    def batched(b0):
+        sbn.sbn_sparse_ternary_gemv_batched(Xq, s_x, codes[b0:b0 + B], metas[b0:b0 + B], s_ws[b0:b0 + B], wl.R, n, m,
+                                            Ys=Ys[b0:b0 + B])
 
     for i in range(P):
         call(i)
     # (i) cold single calls: kernel time from the library's events (gemv only)
     prof = profile_pass(lambda: [call(i) for i in range(P)], 1, "gemv")
     kern_ms, kcnt = kernel_avg_ms(prof, "gemv")
-    # (ii-a) four graphs (every 4th pool entry each) replayed on four streams
-    streams = [torch.cuda.Stream() for _ in range(4)]
-    graphs = []
-    for b in range(4):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def replay_ms(graphs, streams, calls):
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for s_ in streams:
+            s_.wait_event(e0)
+        for _ in range(reps):
+            for g, s_ in zip(graphs, streams):
+                with torch.cuda.stream(s_):
+                    g.replay()
+        for s_ in streams:
+            torch.cuda.current_stream().wait_stream(s_)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * calls)
+
+    def capture(fn):
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=cap):
-            for i in range(b, P, 4):
-                call(i, b)
-        graphs.append(g)
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for s_ in streams:
-        s_.wait_event(e0)
-    for _ in range(reps):
-        for b in range(4):
-            with torch.cuda.stream(streams[b]):
-                graphs[b].replay()
-    for s_ in streams:
-        torch.cuda.current_stream().wait_stream(s_)
-    e1.record()
-    torch.cuda.synchronize()
-    ss_ms = e0.elapsed_time(e1) / (reps * P)
+            fn()
+        return g
+
+    # (ii-a) separate calls: four graphs (every 4th pool entry each) on four streams
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    graphs = [capture(lambda b=b: [call(i) for i in range(b, P, 4)]) for b in range(4)]
+    ss_ms = replay_ms(graphs, streams, P)
     del graphs
-    # (ii-b) one call over 64 weights stacked along R
-    L = 64
-    assert cb == wl.R * wl.K * n // (4 * m) and mb in (0, wl.R * wl.K // 8)   # planes hold no padding
-    codes_t = torch.cat(codes[:L])
-    meta_t = torch.cat(metas[:L]) if mb else None
-    Rt = L * wl.R
-    Yt = torch.empty((T, Rt), dtype=torch.bfloat16, device="cuda")
-    f = lambda: sbn.sbn_sparse_ternary_gemv(Xq, s_x, codes_t, meta_t, s_w, Rt, n, m, Y=Yt)
-    f()
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        f()
-    e1.record()
-    torch.cuda.synchronize()
-    st_ms = e0.elapsed_time(e1) / reps
-    algo_t = L * per + T * wl.K + 4 * T + 2 * T * Rt + 4
-    gbps = lambda b_, ms_: round(b_ / (ms_ * 1e-3) / 1e9, 1)
+    # (ii-b) batched calls of B weights, one graph on one stream
+    gb = capture(lambda: [batched(b0) for b0 in range(0, P, B)])
+    bt_ms = replay_ms([gb], [streams[0]], P)
+    del gb
+    frac = lambda ms_: round(algo / (ms_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    gbps = lambda ms_: round(algo / (ms_ * 1e-3) / 1e9, 1)
     return {
-        "workload": f"decode R=K=4096 T={T} {n}:{m}", "algo_bytes_per_call": algo,
-        "pool_MiB": round(P * per / 2 ** 20, 1), "pool_calls": P,
-        "single_call": {"kernel_us": round(kern_ms * 1e3, 3), "GBps": gbps(algo, kern_ms),
-                        "frac_hbm": round(algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        "steady_graphs_4streams": {"us_per_call": round(ss_ms * 1e3, 3), "GBps": gbps(algo, ss_ms),
-                                   "frac_hbm": round(algo / (ss_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        "stacked_64": {"R": Rt, "algo_bytes": algo_t, "us": round(st_ms * 1e3, 2), "GBps": gbps(algo_t, st_ms),
-                       "frac_hbm": round(algo_t / (st_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "workload": f"decode R=K=4096 T={T} {n}:{m}", "algo_bytes_per_weight": algo,
+        "pool_MiB": round(P * per / 2 ** 20, 1), "pool_weights": P,
+        "single_call": {"kernel_us": round(kern_ms * 1e3, 3), "GBps": gbps(kern_ms), "frac_hbm": frac(kern_ms)},
+        "steady_separate_calls_4streams": {"us_per_weight": round(ss_ms * 1e3, 3), "GBps": gbps(ss_ms),
+                                           "frac_hbm": frac(ss_ms)},
+        f"steady_batched_{B}": {"us_per_weight": round(bt_ms * 1e3, 3), "GBps": gbps(bt_ms), "frac_hbm": frac(bt_ms),
+                                "launches_per_pool": P // B},
     }
 
 

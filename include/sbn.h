@@ -182,6 +182,26 @@ sbn_status sbn_sparse_ternary_gemv(const int8_t* Xq, const float* s_x, int64_t T
                                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sbn_sparse_ternary_gemv over `count` weights that share the activations
+ * (e.g. the projections of one layer that read the same tokens), in one
+ * launch where the shapes allow (2:4 and 6:8 with K a multiple of 1024 up to
+ * 4096; otherwise one launch per weight):
+ *   Y_b = that call's result for (Xq, s_x, codes[b], meta[b], s_w[b])
+ * for b < count.  codes, meta, s_w and Y are HOST arrays of `count` device
+ * pointers (meta may be NULL, or hold NULLs, when n == m); every weight is
+ * R x K at ratio n:m, every Y_b is [T x R] of dtype ydt with row stride ldy.
+ * The pointer arrays are read during the call and not kept.
+ * Errors: as sbn_sparse_ternary_gemv, and SBN_ERR_SHAPE for count < 1 or
+ * count > SBN_GEMV_MAX_BATCH.
+ */
+#define SBN_GEMV_MAX_BATCH 64
+sbn_status sbn_sparse_ternary_gemv_batched(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                           const uint8_t* const* codes, const uint8_t* const* meta,
+                                           const float* const* s_w, int64_t R, int n, int m,
+                                           void* const* Y, sbn_dtype ydt, int64_t ldy, int64_t count,
+                                           void* stream);
+
+/*
  * Dual-STE backward of Sparse-BitLinear (ja §2.1, de §2 "Dual STE",
  * ko §2.2, fr §2): identity Jacobian through both quantizers and a dense
  * gradient through the mask, so every master weight receives a gradient.

@@ -51,6 +51,9 @@ _SIGNATURES = {
                                  _vp, _sz, _vp], _int),
     "sbn_sparse_ternary_gemv": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _int, _int, _vp, _int, _i64,
                                  _vp, _sz, _vp], _int),
+    "sbn_sparse_ternary_gemv_batched": ([_vp, _vp, _i64, _i64, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                         ctypes.POINTER(_vp), _i64, _int, _int, ctypes.POINTER(_vp), _int,
+                                         _i64, _i64, _vp], _int),
     "sbn_backward": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _int, _int, _vp, _int, _vp, _vp,
                       _sz, _vp], _int),
     "sbn_profile_enable": ([_int, ctypes.c_char_p], _int),
@@ -177,8 +180,8 @@ _YT = {SBN_F32: "float32", SBN_BF16: "bfloat16", SBN_I32_ACC: "int32"}
 def _matmul(name: str, Xq, s_x, codes, meta, s_w, R: int, n: int, m: int, ydt: int, Y, ws, stream):
     torch = _torch()
     T, K = Xq.shape
-    if Y is None:
-        Y = torch.empty((T, R), dtype=getattr(torch, _YT[ydt]), device=Xq.device)
+    if Y is None:                                    # row stride rounded up to 8 elements (the ABI's rule)
+        Y = torch.empty((T, (R + 7) // 8 * 8), dtype=getattr(torch, _YT[ydt]), device=Xq.device)[:, :R]
     op = SBN_OP_GEMM if name == "sbn_sparse_ternary_gemm" else SBN_OP_GEMV
     need = sbn_workspace_bytes(op, T, R, K, n, m)
     if ws is None:
@@ -199,6 +202,25 @@ def sbn_sparse_ternary_gemv(Xq, s_x, codes, meta, s_w, R: int, n: int, m: int, *
                             Y=None, ws=None, stream=None):
     """Decode form (T <= 16) of sbn_sparse_ternary_gemm."""
     return _matmul("sbn_sparse_ternary_gemv", Xq, s_x, codes, meta, s_w, R, n, m, ydt, Y, ws, stream)
+
+
+def sbn_sparse_ternary_gemv_batched(Xq, s_x, codes, metas, s_ws, R: int, n: int, m: int, *,
+                                    ydt: int = SBN_BF16, Ys=None, stream=None):
+    """sbn_sparse_ternary_gemv for several weights sharing Xq: codes, metas, s_ws
+    (and Ys) are lists of tensors, one per weight.  Returns the list of Y."""
+    torch = _torch()
+    T, K = Xq.shape
+    count = len(codes)
+    if Ys is None:                                   # row stride rounded up to 8 elements (the ABI's rule)
+        ld = (R + 7) // 8 * 8
+        Ys = [torch.empty((T, ld), dtype=getattr(torch, _YT[ydt]), device=Xq.device)[:, :R] for _ in range(count)]
+    arr = lambda ts: (_vp * max(count, 1))(*[None if t is None else t.data_ptr() for t in ts])
+    metas_a = None if metas is None else arr(metas)
+    _check("sbn_sparse_ternary_gemv_batched",
+           lib().sbn_sparse_ternary_gemv_batched(_ptr(Xq), _ptr(s_x), T, K, arr(codes), metas_a, arr(s_ws), R, n, m,
+                                                 arr(Ys), ydt, Ys[0].stride(0) if count else R, count,
+                                                 _stream(stream)))
+    return Ys
 
 
 def sbn_backward(dY, Xq, s_x, codes, meta, s_w, n: int, m: int, *, dxdt: int = SBN_F32, want_dX: bool = True,

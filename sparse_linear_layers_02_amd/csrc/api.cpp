@@ -371,6 +371,35 @@ sbn_status sbn_sparse_ternary_gemv(const int8_t* Xq, const float* s_x, int64_t T
                     st, fn);
 }
 
+sbn_status sbn_sparse_ternary_gemv_batched(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                           const uint8_t* const* codes, const uint8_t* const* meta,
+                                           const float* const* s_w, int64_t R, int n, int m,
+                                           void* const* Y, sbn_dtype ydt, int64_t ldy, int64_t count,
+                                           void* stream) {
+  const char* fn = "sbn_sparse_ternary_gemv_batched";
+  SBN_NONNULL(codes);
+  SBN_NONNULL(s_w);
+  SBN_NONNULL(Y);
+  if (count < 1 || count > SBN_GEMV_MAX_BATCH)
+    return fail(SBN_ERR_SHAPE, "%s: count = %lld must be in [1, %d]", fn, (long long)count, SBN_GEMV_MAX_BATCH);
+  SBN_TRY(check_nm(n, m));
+  if (n < m) SBN_NONNULL(meta);
+  const uint8_t* metas[SBN_GEMV_MAX_BATCH];
+  for (int64_t b = 0; b < count; ++b) {
+    metas[b] = n < m ? meta[b] : nullptr;
+    const sbn_status st_b = check_matmul_args(fn, Xq, s_x, T, K, codes[b], metas[b], s_w[b], R, n, m, Y[b], ydt, ldy);
+    if (st_b != SBN_OK) {
+      char msg[512];
+      snprintf(msg, sizeof(msg), "%s (weight %lld)", sbn_last_error(), (long long)b);
+      return fail(st_b, "%s", msg);
+    }
+  }
+  if (T > 16) return fail(SBN_ERR_SHAPE, "%s: T = %lld exceeds 16; use the GEMM", fn, (long long)T);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_gemv_batched(Xq, s_x, T, K, codes, metas, s_w, R, n, m, Y, ydt, ldy, (int)count, st),
+                    st, fn);
+}
+
 sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
                         const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
                         const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,

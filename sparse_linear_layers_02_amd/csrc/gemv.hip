@@ -183,18 +183,16 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv24_kernel(
   }
 }
 
-// ----------------------------------------------------------------------------- 2:4, streamed
-// K a multiple of 1024, at most 4096: wave w owns positions [1024w, 1024w + 1024)
-// of every row (eight steps of 128, lane group g's run = meta and code words
-// 8g .. 8g + 7 of the range) and walks the block's row groups.  The packed
-// words of the next GV_RING - 1 row groups stream into a ring in LDS that only
-// this wave uses, by direct global->LDS loads: several row groups are in
-// flight per wave without holding registers, and no load waits behind the math.
-// Ring slot: 16 rows x 128 B of meta, then the same of codes; 16-byte chunk c
-// of row r sits at chunk position c ^ (r & 7), so the eight lanes that read one
-// chunk position of eight rows touch eight different banks, and each 1 KB load
-// instruction still reads whole 128-byte row segments.  Survivor values are
-// decoded as 64 * w, so the partial sums are 64 times the accumulator.
+// ----------------------------------------------------------------------------- streamed decode
+// For 2:4 and 6:8 with K a multiple of 1024, at most 4096.  Wave w of a block
+// owns positions [1024w, 1024w + 1024) of every row and keeps the activations
+// of that range in registers; a block walks consecutive row groups (16 rows)
+// of one or more weights that share the activations.  The packed words of the
+// next GV_RING - 1 row groups stream into a ring in LDS that only this wave
+// uses, by direct global->LDS loads: several row groups are in flight per wave
+// without holding registers, and no load waits behind the math.  Survivor
+// values are decoded as 64 * w (the code in the top two bits of its byte), so
+// the partial sums are 64 times the accumulator.
 #ifndef SBN_GV_RING
 #define SBN_GV_RING 2
 #endif
@@ -208,27 +206,34 @@ constexpr int GV_RING = SBN_GV_RING;
 constexpr int GV_BPC = SBN_GV_BPC;                   // resident blocks per CU
 constexpr int GV_STREAM_BLOCKS = 256 * GV_BPC;
 
-// Streamed kernels: a block walks consecutive row groups, and row groups 4k ..
-// 4k + 3 (64 rows) form one output group.  Per row group the four waves' 16 x 16
-// partial sums (64 times the accumulator) go through red (one of two buffers,
-// alternating per row group, so one barrier per row group suffices).  Lane
-// (t = tid / 16, r = tid % 16) owns rows 4r .. 4r + 3 of its output group for
-// token t: it sums them (16 contiguous bytes of each wave's partials) after row
-// group r / 4 of the group and keeps them in registers; once the group is
-// complete they are stored together, so each token's 64 outputs leave as one
-// contiguous 128- or 256-byte run instead of four 32-byte pieces.
+// The weights of one streamed launch (kernel argument, by value).
+struct GemvBatch {
+  const uint8_t* codes[GV_MAX_BATCH];
+  const uint8_t* meta[GV_MAX_BATCH];
+  const float* s_w[GV_MAX_BATCH];
+  void* Y[GV_MAX_BATCH];
+};
+
+// Output side.  Row groups 4k .. 4k + 3 of a weight (64 rows) form one output
+// group.  Per row group the four waves' 16 x 16 partial sums go through red
+// (one of two buffers, alternating per row group, so one barrier per row group
+// suffices).  Lane (t = tid / 16, r = tid % 16) owns rows 4r .. 4r + 3 of its
+// output group for token t: it sums them (16 contiguous bytes of each wave's
+// partials) after row group r / 4 of the group and keeps them in registers;
+// once the group is complete they are stored together, so each token's 64
+// outputs leave as one contiguous 128- or 256-byte run.
 template <int OUT>
 struct StreamOut {
   v4i v;                                               // this lane's four outputs (bf16: v[0..1] packed)
   int64_t prow = -1;                                   // first row of a pending store (-1: none)
-  // j: place of this row group in its output group (row group index mod 4); j0:
-  // the first place this block fills in that group; last: the block's last row group.
-  // A completed group's stores are only recorded here and issued by commit(),
-  // which the kernel calls right after its next wait for ring loads: a store
-  // counts in the same vmcnt as the ring loads, so a store issued just before
-  // such a wait would make the wait cover the store's latency too.
-  __device__ inline void row_group(int (*red)[256], v4i acc, int tid, int wave, int lane, int j, int j0, bool last,
-                                   int64_t grp_row0, int64_t T, float swv, float sxv) {
+  void* pY = nullptr;
+  // j: place of the row group in its output group; j0: the first place this
+  // block fills in that group; done: the group is complete for this block.
+  // The stores are only recorded here and issued by commit(), which the kernel
+  // calls right after its next wait for ring loads (stores count in the same
+  // vmcnt as the ring loads).
+  __device__ inline void row_group(int (*red)[256], v4i acc, int tid, int wave, int lane, int j, int j0, bool done,
+                                   int64_t grp_row0, int64_t T, float swv, float sxv, void* Y) {
     *(v4i*)&red[wave][lane * 4] = acc;
     lds_barrier();
     const int t = tid >> 4, r = tid & 15;
@@ -252,14 +257,17 @@ struct StreamOut {
         }
       }
     }
-    if ((j == 3 || last) && (r >> 2) >= j0 && (r >> 2) <= j && t < T) prow = grp_row0 + 4 * r;
+    if (done && (r >> 2) >= j0 && (r >> 2) <= j && t < T) {
+      prow = grp_row0 + 4 * r;
+      pY = Y;
+    }
   }
-  __device__ inline void commit(int tid, int64_t R, void* Y, int64_t ldy) {
+  __device__ inline void commit(int tid, int64_t R, int64_t ldy) {
     if (prow < 0) return;
     const int64_t row = prow, t = tid >> 4;
     prow = -1;
     if (OUT == 2) {
-      uint16_t* y = (uint16_t*)Y + t * ldy + row;
+      uint16_t* y = (uint16_t*)pY + t * ldy + row;
       if (row + 4 <= R) {
         *(uint2*)y = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
       } else {
@@ -268,7 +276,7 @@ struct StreamOut {
           if (row + q < R) y[q] = (uint16_t)((uint32_t)v[q >> 1] >> (16 * (q & 1)));
       }
     } else {
-      int* y = (int*)Y + t * ldy + row;
+      int* y = (int*)pY + t * ldy + row;
       if (row + 4 <= R) {
         *(v4i*)y = v;
       } else {
@@ -280,123 +288,71 @@ struct StreamOut {
   }
 };
 
-template <int OUT>
-__global__ __launch_bounds__(256, GV_BPC) void gemv24s_kernel(
-    const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K,
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, const float* __restrict__ s_w,
-    int64_t R, void* __restrict__ Y, int64_t ldy) {
-  // one LDS array: [4 waves][GV_RING slots][4096 B] ring, then red[2][4][256] ints
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * GV_RING * 4096 + 2 * 4 * 256 * 4];
-  uint8_t (*ring)[GV_RING][4096] = (uint8_t (*)[GV_RING][4096])lds;
-  int (*red)[4][256] = (int (*)[4][256])(lds + 4 * GV_RING * 4096);
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int g = lane >> 4, rl = lane & 15;
-  const int64_t nrg = cdiv(R, 16), rowb = K / 8;
-  const bool has = wave < K / 1024;                    // wave-uniform
-  // scales of the output element this thread writes (token tid / 16); the
-  // loads are unconditional so nothing waits for them before the loop
-  const int64_t tq = tid >> 4;
-  const float sxv = OUT != 0 ? s_x[tq < T ? tq : 0] : 0.0f;
-  const float swv = OUT != 0 ? *s_w : 0.0f;
-  uint8_t* myring = &ring[wave][0][0];
-
-  // direct loads of one row group into ring slot `slot`: instruction q of a
-  // plane fills chunk positions 64q + lane (row (64q + lane) / 8)
+// 2:4 decoder.  Range of 1024 positions = eight steps of v_smfmac_i32_16x16x128_i8;
+// lane group g's run is meta and code words 8g .. 8g + 7 of the range; step s
+// maps the instruction's logical K index q (0..127) to position
+// 256 (q / 32) + 32 s + q % 32 of the range.  Ring slot: 16 rows x 128 B of
+// meta, then the same of codes; 16-byte chunk c of row r sits at chunk
+// position c ^ (r & 7), so the eight lanes that read one chunk position of
+// eight rows touch eight different banks, and each 1 KB load instruction
+// still reads whole 128-byte row segments.
+struct Dec24 {
+  static constexpr int SLOT = 4096, NDMA = 4, LUT = 0;
   int rowq[2], colq[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int sp = 64 * q + lane, rr = sp >> 3;
-    rowq[q] = rr;
-    colq[q] = 128 * wave + 16 * ((sp & 7) ^ (rr & 7));
-  }
-  auto issue = [&](int64_t rg, int slot) {
-    uint8_t* dst = myring + slot * 4096;
-    const int64_t base = rg * 16 * rowb;               // wave-uniform
-    const bool full = rg * 16 + 16 <= R;
+  v4i blo[8], bhi[8];
+  __device__ inline void init(int wave, int lane) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      int off = rowq[q] * (int)rowb + colq[q];
-      if (!full) {                                     // rows past R: row R-1, discarded
-        const int64_t r = rg * 16 + rowq[q] < R ? rowq[q] : R - 1 - rg * 16;
-        off = (int)r * (int)rowb + colq[q];
-      }
-      g2lds16(meta + base + off, dst + 1024 * q);
-      g2lds16(codes + base + off, dst + 2048 + 1024 * q);
+      const int sp = 64 * q + lane, rr = sp >> 3;
+      rowq[q] = rr;
+      colq[q] = 128 * wave + 16 * ((sp & 7) ^ (rr & 7));
     }
-  };
-
-  // this block's row groups: [rg0, rg0 + nit), consecutive
-  const int64_t rg0 = (int64_t)blockIdx.x * nrg / gridDim.x;
-  const int nit = (int)(((int64_t)blockIdx.x + 1) * nrg / gridDim.x - rg0);
-  if (has) {
-#pragma unroll
-    for (int i = 0; i < GV_RING - 1; ++i)
-      if (i < nit) issue(rg0 + i, i);
   }
-  // activations of this wave's range, kept in registers (as gemv24 with S = 8)
-  const bool tvalid = rl < T;
-  const int8_t* xrow = Xq + (tvalid ? rl : 0) * K;
-  v4i blo[8], bhi[8];
+  // row group at planes (m, c); rows of the group from `valid` on read row valid - 1
+  __device__ inline void issue(uint8_t* dst, const uint8_t* m, const uint8_t* c, int valid, int64_t K) {
+    const int rowb = (int)(K / 8);
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int64_t lo = 1024 * wave + 256 * (g >> 1) + 32 * s + 16 * (g & 1);
-    const bool ok = has && tvalid;
-    blo[s] = ok ? *(const v4i*)(xrow + lo) : (v4i){0, 0, 0, 0};
-    bhi[s] = ok ? *(const v4i*)(xrow + lo + 512) : (v4i){0, 0, 0, 0};
+    for (int q = 0; q < 2; ++q) {
+      const int r = rowq[q] < valid ? rowq[q] : valid - 1;
+      const int off = r * rowb + colq[q];
+      g2lds16(m + off, dst + 1024 * q);
+      g2lds16(c + off, dst + 2048 + 1024 * q);
+    }
   }
-  // make the activations (and with them the first ring slots) resident before
-  // the loop, whose only global loads are the counted ring loads
+  __device__ inline void load_x(const int8_t* xrow, bool ok, int wave, int g) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(blo[s]), "v"(bhi[s]));
-
-  StreamOut<OUT> out;
-  int slot = 0, par = 0;
-  for (int it = 0; it < nit; ++it) {
+    for (int s = 0; s < 8; ++s) {
+      const int64_t lo = 1024 * wave + 256 * (g >> 1) + 32 * s + 16 * (g & 1);
+      blo[s] = ok ? *(const v4i*)(xrow + lo) : (v4i){0, 0, 0, 0};
+      bhi[s] = ok ? *(const v4i*)(xrow + lo + 512) : (v4i){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(blo[s]), "v"(bhi[s]));
+  }
+  __device__ inline void build_lut(uint8_t*, int) {}
+  __device__ inline v4i compute(const uint8_t* slot, const uint8_t*, int rl, int g) {
+    const uint8_t* sl = slot + rl * 128;
+    const int c0 = (2 * g) ^ (rl & 7), c1 = (2 * g + 1) ^ (rl & 7);
+    const v4i m0 = *(const v4i*)(sl + 16 * c0), m1 = *(const v4i*)(sl + 16 * c1);
+    const v4i k0 = *(const v4i*)(sl + 2048 + 16 * c0), k1 = *(const v4i*)(sl + 2048 + 16 * c1);
+    const uint32_t mw[8] = {(uint32_t)m0[0], (uint32_t)m0[1], (uint32_t)m0[2], (uint32_t)m0[3],
+                            (uint32_t)m1[0], (uint32_t)m1[1], (uint32_t)m1[2], (uint32_t)m1[3]};
+    const uint32_t cw[8] = {(uint32_t)k0[0], (uint32_t)k0[1], (uint32_t)k0[2], (uint32_t)k0[3],
+                            (uint32_t)k1[0], (uint32_t)k1[1], (uint32_t)k1[2], (uint32_t)k1[3]};
     v4i acc = (v4i){0, 0, 0, 0};
-    if (has) {
-      if (it + GV_RING - 1 < nit) issue(rg0 + it + GV_RING - 1, (slot + GV_RING - 1) % GV_RING);
-      // this slot's loads are done once at most 4 per later row group remain
-      const int later = nit - 1 - it;
-      if (later >= GV_RING - 1) wait_vmcnt<4 * (GV_RING - 1)>();
-      else if (GV_RING > 3 && later == 2) wait_vmcnt<8>();
-      else if (later == 1) wait_vmcnt<4>();
-      else wait_vmcnt<0>();
-      out.commit(tid, R, Y, ldy);
-      const uint8_t* sl = myring + slot * 4096 + rl * 128;
-      const int c0 = (2 * g) ^ (rl & 7), c1 = (2 * g + 1) ^ (rl & 7);
-      const v4i m0 = *(const v4i*)(sl + 16 * c0), m1 = *(const v4i*)(sl + 16 * c1);
-      const v4i k0 = *(const v4i*)(sl + 2048 + 16 * c0), k1 = *(const v4i*)(sl + 2048 + 16 * c1);
-      const uint32_t mw[8] = {(uint32_t)m0[0], (uint32_t)m0[1], (uint32_t)m0[2], (uint32_t)m0[3],
-                              (uint32_t)m1[0], (uint32_t)m1[1], (uint32_t)m1[2], (uint32_t)m1[3]};
-      const uint32_t cw[8] = {(uint32_t)k0[0], (uint32_t)k0[1], (uint32_t)k0[2], (uint32_t)k0[3],
-                              (uint32_t)k1[0], (uint32_t)k1[1], (uint32_t)k1[2], (uint32_t)k1[3]};
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        v4i a;
-        int ix;
-        decode24_x64(mw[s], cw[s], a, ix);
-        const v8i b = (v8i){blo[s][0], blo[s][1], blo[s][2], blo[s][3], bhi[s][0], bhi[s][1], bhi[s][2], bhi[s][3]};
-        acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, acc, ix, 0, 0);
-      }
-      slot = slot + 1 == GV_RING ? 0 : slot + 1;
+    for (int s = 0; s < 8; ++s) {
+      v4i a;
+      int ix;
+      decode24_x64(mw[s], cw[s], a, ix);
+      const v8i b = (v8i){blo[s][0], blo[s][1], blo[s][2], blo[s][3], bhi[s][0], bhi[s][1], bhi[s][2], bhi[s][3]};
+      acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, acc, ix, 0, 0);
     }
-    {
-      const int64_t rgi = rg0 + it;                    // output groups: row groups 4k .. 4k + 3
-      const int j0 = it < 4 - (int)(rg0 & 3) ? (int)(rg0 & 3) : 0;
-      out.row_group(red[par], acc, tid, wave, lane, (int)(rgi & 3), j0, it == nit - 1, (rgi & ~(int64_t)3) * 16,
-                    T, swv, sxv);
-    }
-    par ^= 1;
-    if (!has) out.commit(tid, R, Y, ldy);
+    return acc;
   }
-  out.commit(tid, R, Y, ldy);
-}
+};
 
-
-// ----------------------------------------------------------------------------- 6:8, streamed
-// Same walk as gemv24s with the dense v_mfma_i32_16x16x64_i8: wave w owns
-// positions [1024w, 1024w + 1024) of every row, sixteen steps of 64; lane group
+// 6:8 decoder, dense v_mfma_i32_16x16x64_i8: sixteen steps of 64; lane group
 // g's run is positions 256g .. 256g + 255 of the range (meta words 8g .. 8g+7,
 // code words 12g .. 12g+11), step s takes positions 256g + 16s .. +16 as A lane
 // (r, g) and the same activation bytes as B lane (t, g).  Ring slot: 16 rows x
@@ -427,130 +383,151 @@ __device__ inline v4i lut68_entry(uint32_t mb) {
   return (v4i){(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
 }
 
-template <int OUT>
-__global__ __launch_bounds__(256, GV_BPC) void gemv68s_kernel(
-    const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K,
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, const float* __restrict__ s_w,
-    int64_t R, void* __restrict__ Y, int64_t ldy) {
-  constexpr int SLOT = 2048 + 3072;
-  // one LDS array: [4 waves][GV_RING][SLOT] ring, the 256 x 16 B table, red[2][4][256]
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * GV_RING * SLOT + 4096 + 2 * 4 * 256 * 4];
-  uint8_t* ring = lds;
-  uint8_t* lut = lds + 4 * GV_RING * SLOT;
-  int (*red)[4][256] = (int (*)[4][256])(lut + 4096);
+struct Dec68 {
+  static constexpr int SLOT = 2048 + 3072, NDMA = 5, LUT = 4096;
+  int rowA[5], colA[5];
+  v4i bx[16];
+  __device__ inline void init(int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {                        // meta: chunk positions 64q + lane
+      const int sp = 64 * q + lane, rr = sp >> 3;
+      rowA[q] = rr;
+      colA[q] = 128 * wave + 16 * ((sp & 7) ^ (rr & 7));
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {                        // codes: chunk positions 64q + lane
+      const int sp = 64 * q + lane, rr = sp / 12, pos = sp - 12 * rr;
+      const int c = pos - (rr & 7) < 0 ? pos - (rr & 7) + 12 : pos - (rr & 7);
+      rowA[2 + q] = rr;
+      colA[2 + q] = 192 * wave + 16 * c;
+    }
+  }
+  __device__ inline void issue(uint8_t* dst, const uint8_t* m, const uint8_t* c, int valid, int64_t K) {
+    const int rowm = (int)(K / 8), rowc = (int)(K * 3 / 16);
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int r = rowA[q] < valid ? rowA[q] : valid - 1;
+      if (q < 2) g2lds16(m + r * rowm + colA[q], dst + 1024 * q);
+      else g2lds16(c + r * rowc + colA[q], dst + 2048 + 1024 * (q - 2));
+    }
+  }
+  __device__ inline void load_x(const int8_t* xrow, bool ok, int wave, int g) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      bx[s] = ok ? *(const v4i*)(xrow + 1024 * wave + 256 * g + 16 * s) : (v4i){0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) asm volatile("" ::"v"(bx[s]));
+  }
+  __device__ inline void build_lut(uint8_t* lut, int tid) { *(v4i*)(lut + 16 * tid) = lut68_entry((uint32_t)tid); }
+  __device__ inline v4i compute(const uint8_t* slot, const uint8_t* lut, int rl, int g) {
+    const uint8_t* sm = slot + rl * 128;
+    const uint8_t* sc = slot + 2048 + rl * 192;
+    const int r7 = rl & 7;
+    const v4i m0 = *(const v4i*)(sm + 16 * ((2 * g) ^ r7)), m1 = *(const v4i*)(sm + 16 * ((2 * g + 1) ^ r7));
+    uint32_t cw[12];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int c = 3 * g + i + r7;
+      const v4i v = *(const v4i*)(sc + 16 * (c < 12 ? c : c - 12));
+      cw[4 * i] = (uint32_t)v[0]; cw[4 * i + 1] = (uint32_t)v[1]; cw[4 * i + 2] = (uint32_t)v[2]; cw[4 * i + 3] = (uint32_t)v[3];
+    }
+    const uint32_t mw[8] = {(uint32_t)m0[0], (uint32_t)m0[1], (uint32_t)m0[2], (uint32_t)m0[3],
+                            (uint32_t)m1[0], (uint32_t)m1[1], (uint32_t)m1[2], (uint32_t)m1[3]};
+    v4i acc = (v4i){0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const uint32_t m16 = mw[s >> 1] >> (16 * (s & 1));
+      const int bo = 24 * s, wi = bo >> 5, sh = bo & 31;
+      const uint32_t c = sh == 0 ? cw[wi] : __builtin_amdgcn_alignbit(cw[wi + 1 < 12 ? wi + 1 : 11], cw[wi], sh);
+      const uint32_t p0 = (c << 6) & 0xC0C0C0C0u, p1 = (c << 4) & 0xC0C0C0C0u;
+      const uint32_t p2 = (c << 2) & 0xC0C0C0C0u, p3 = c & 0xC0C0C0C0u;
+      const uint32_t A = __builtin_amdgcn_perm(p1, p0, 0x05010400u);   // [f0 f1 f4 f5]
+      const uint32_t B = __builtin_amdgcn_perm(p3, p2, 0x05010400u);   // [f2 f3 f6 f7]
+      const uint32_t C = __builtin_amdgcn_perm(p1, p0, 0x07030602u);   // [f8 f9 . .]
+      const uint32_t D = __builtin_amdgcn_perm(p3, p2, 0x07030602u);   // [f10 f11 . .]
+      const uint2 s01 = *(const uint2*)(lut + 16 * (m16 & 0xFFu));
+      const uint2 s23 = *(const uint2*)(lut + 16 * ((m16 >> 8) & 0xFFu) + 8);
+      const v4i a = (v4i){(int)__builtin_amdgcn_perm(B, A, s01.x), (int)__builtin_amdgcn_perm(B, A, s01.y),
+                          (int)__builtin_amdgcn_perm(C, B, s23.x), (int)__builtin_amdgcn_perm(D, C, s23.y)};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx[s], acc, 0, 0, 0);
+    }
+    return acc;
+  }
+};
+
+// One launch over `count` weights of R rows each: global row group q = w * nrg + lr.
+template <int OUT, typename Dec>
+__global__ __launch_bounds__(256, GV_BPC) void gemv_stream_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K, const GemvBatch P,
+    int count, int64_t R, int64_t ldy) {
+  // one LDS array: [4 waves][GV_RING][SLOT] ring, the decode table, red[2][4][256]
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * GV_RING * Dec::SLOT + Dec::LUT + 2 * 4 * 256 * 4];
+  uint8_t* lut = lds + 4 * GV_RING * Dec::SLOT;
+  int (*red)[4][256] = (int (*)[4][256])(lut + Dec::LUT);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, rl = lane & 15;
-  const int64_t nrg = cdiv(R, 16), rowm = K / 8, rowc = K * 3 / 16;
-  const bool has = wave < K / 1024;
-  const int64_t tq = tid >> 4;
+  const int64_t nrg = cdiv(R, 16);
+  const int64_t rowm = K / 8, rowc = K * (Dec::NDMA == 4 ? 2 : 3) / 16;   // plane bytes per row
+  const bool has = wave < K / 1024;                    // wave-uniform
+  const int64_t tq = tid >> 4;                         // token of the outputs this thread writes
   const float sxv = OUT != 0 ? s_x[tq < T ? tq : 0] : 0.0f;
-  const float swv = OUT != 0 ? *s_w : 0.0f;
-  uint8_t* myring = ring + wave * GV_RING * SLOT;
+  uint8_t* myring = lds + wave * GV_RING * Dec::SLOT;
+  Dec dec;
+  dec.init(wave, lane);
 
-  // per-lane sources of the five 1 KB loads of a row group (row offset, column offset)
-  int rowA[5], colA[5];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {                          // meta: chunk positions 64q + lane
-    const int sp = 64 * q + lane, rr = sp >> 3;
-    rowA[q] = rr;
-    colA[q] = 128 * wave + 16 * ((sp & 7) ^ (rr & 7));
-  }
-#pragma unroll
-  for (int q = 0; q < 3; ++q) {                          // codes: chunk positions 64q + lane
-    const int sp = 64 * q + lane, rr = sp / 12, pos = sp - 12 * rr;
-    const int c = pos - (rr & 7) < 0 ? pos - (rr & 7) + 12 : pos - (rr & 7);
-    rowA[2 + q] = rr;
-    colA[2 + q] = 192 * wave + 16 * c;
-  }
-  auto issue = [&](int64_t rg, int slot) {
-    uint8_t* dst = myring + slot * SLOT;
-    const uint8_t* mb = meta + rg * 16 * rowm;         // wave-uniform row-group bases
-    const uint8_t* cb = codes + rg * 16 * rowc;
-    const bool full = rg * 16 + 16 <= R;
-#pragma unroll
-    for (int q = 0; q < 5; ++q) {
-      int r = rowA[q];
-      if (!full && rg * 16 + r >= R) r = (int)(R - 1 - rg * 16);   // rows past R: row R-1, discarded
-      if (q < 2) g2lds16(mb + r * (int)rowm + colA[q], dst + 1024 * q);
-      else g2lds16(cb + r * (int)rowc + colA[q], dst + 2048 + 1024 * (q - 2));
-    }
+  // this block's row groups: [q0, q0 + nit) of the count * nrg, consecutive
+  const int64_t total = nrg * count;
+  const int64_t q0 = (int64_t)blockIdx.x * total / gridDim.x;
+  const int nit = (int)(((int64_t)blockIdx.x + 1) * total / gridDim.x - q0);
+  // position (weight, row group) of the next row group to load
+  int iw = (int)(q0 / nrg);
+  int64_t ilr = q0 - (int64_t)iw * nrg;
+  auto issue_next = [&](int slot) {
+    const int valid = (int)(R - ilr * 16 < 16 ? R - ilr * 16 : 16);
+    dec.issue(myring + slot * Dec::SLOT, P.meta[iw] + ilr * 16 * rowm, P.codes[iw] + ilr * 16 * rowc, valid, K);
+    if (++ilr == nrg) { ilr = 0; ++iw; }
   };
-
-  // this block's row groups: [rg0, rg0 + nit), consecutive
-  const int64_t rg0 = (int64_t)blockIdx.x * nrg / gridDim.x;
-  const int nit = (int)(((int64_t)blockIdx.x + 1) * nrg / gridDim.x - rg0);
   if (has) {
 #pragma unroll
     for (int i = 0; i < GV_RING - 1; ++i)
-      if (i < nit) issue(rg0 + i, i);
+      if (i < nit) issue_next(i);
   }
-  *(v4i*)(lut + 16 * tid) = lut68_entry((uint32_t)tid);
+  dec.build_lut(lut, tid);
   const bool tvalid = rl < T;
-  const int8_t* xrow = Xq + (tvalid ? rl : 0) * K;
-  v4i bx[16];
-#pragma unroll
-  for (int s = 0; s < 16; ++s)
-    bx[s] = (has && tvalid) ? *(const v4i*)(xrow + 1024 * wave + 256 * g + 16 * s) : (v4i){0, 0, 0, 0};
-#pragma unroll
-  for (int s = 0; s < 16; ++s) asm volatile("" ::"v"(bx[s]));
-  lds_barrier();                                       // table complete
+  dec.load_x(Xq + (tvalid ? rl : 0) * K, has && tvalid, wave, g);
+  lds_barrier();                                       // decode table complete
 
   StreamOut<OUT> out;
+  int cw = (int)(q0 / nrg);                            // position of the row group being computed
+  int64_t clr = q0 - (int64_t)cw * nrg;
+  int j0 = (int)(clr & 3);
   int slot = 0, par = 0;
   for (int it = 0; it < nit; ++it) {
     v4i acc = (v4i){0, 0, 0, 0};
+    float swv = 0.0f;
+    if (OUT != 0) swv = *P.s_w[cw];
     if (has) {
-      if (it + GV_RING - 1 < nit) issue(rg0 + it + GV_RING - 1, (slot + GV_RING - 1) % GV_RING);
+      if (it + GV_RING - 1 < nit) issue_next((slot + GV_RING - 1) % GV_RING);
+      // this slot's loads are done once at most NDMA per later row group remain
       const int later = nit - 1 - it;
-      if (later >= GV_RING - 1) wait_vmcnt<5 * (GV_RING - 1)>();
-      else if (GV_RING > 3 && later == 2) wait_vmcnt<10>();
-      else if (later == 1) wait_vmcnt<5>();
+      if (later >= GV_RING - 1) wait_vmcnt<Dec::NDMA * (GV_RING - 1)>();
+      else if (GV_RING > 3 && later == 2) wait_vmcnt<Dec::NDMA * 2>();
+      else if (later == 1) wait_vmcnt<Dec::NDMA>();
       else wait_vmcnt<0>();
-      out.commit(tid, R, Y, ldy);
-      const uint8_t* sl = myring + slot * SLOT;
-      const uint8_t* sm = sl + rl * 128;
-      const uint8_t* sc = sl + 2048 + rl * 192;
-      const int r7 = rl & 7;
-      const v4i m0 = *(const v4i*)(sm + 16 * ((2 * g) ^ r7)), m1 = *(const v4i*)(sm + 16 * ((2 * g + 1) ^ r7));
-      uint32_t cw[12];
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int c = 3 * g + i + r7;
-        const v4i v = *(const v4i*)(sc + 16 * (c < 12 ? c : c - 12));
-        cw[4 * i] = (uint32_t)v[0]; cw[4 * i + 1] = (uint32_t)v[1]; cw[4 * i + 2] = (uint32_t)v[2]; cw[4 * i + 3] = (uint32_t)v[3];
-      }
-      const uint32_t mw[8] = {(uint32_t)m0[0], (uint32_t)m0[1], (uint32_t)m0[2], (uint32_t)m0[3],
-                              (uint32_t)m1[0], (uint32_t)m1[1], (uint32_t)m1[2], (uint32_t)m1[3]};
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const uint32_t m16 = mw[s >> 1] >> (16 * (s & 1));
-        const int bo = 24 * s, wi = bo >> 5, sh = bo & 31;
-        const uint32_t c = sh == 0 ? cw[wi] : __builtin_amdgcn_alignbit(cw[wi + 1 < 12 ? wi + 1 : 11], cw[wi], sh);
-        const uint32_t p0 = (c << 6) & 0xC0C0C0C0u, p1 = (c << 4) & 0xC0C0C0C0u;
-        const uint32_t p2 = (c << 2) & 0xC0C0C0C0u, p3 = c & 0xC0C0C0C0u;
-        const uint32_t A = __builtin_amdgcn_perm(p1, p0, 0x05010400u);   // [f0 f1 f4 f5]
-        const uint32_t B = __builtin_amdgcn_perm(p3, p2, 0x05010400u);   // [f2 f3 f6 f7]
-        const uint32_t C = __builtin_amdgcn_perm(p1, p0, 0x07030602u);   // [f8 f9 . .]
-        const uint32_t D = __builtin_amdgcn_perm(p3, p2, 0x07030602u);   // [f10 f11 . .]
-        const uint2 s01 = *(const uint2*)(lut + 16 * (m16 & 0xFFu));
-        const uint2 s23 = *(const uint2*)(lut + 16 * ((m16 >> 8) & 0xFFu) + 8);
-        const v4i a = (v4i){(int)__builtin_amdgcn_perm(B, A, s01.x), (int)__builtin_amdgcn_perm(B, A, s01.y),
-                            (int)__builtin_amdgcn_perm(C, B, s23.x), (int)__builtin_amdgcn_perm(D, C, s23.y)};
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx[s], acc, 0, 0, 0);
-      }
+      out.commit(tid, R, ldy);
+      acc = dec.compute(myring + slot * Dec::SLOT, lut, rl, g);
       slot = slot + 1 == GV_RING ? 0 : slot + 1;
     }
-    {
-      const int64_t rgi = rg0 + it;                    // output groups: row groups 4k .. 4k + 3
-      const int j0 = it < 4 - (int)(rg0 & 3) ? (int)(rg0 & 3) : 0;
-      out.row_group(red[par], acc, tid, wave, lane, (int)(rgi & 3), j0, it == nit - 1, (rgi & ~(int64_t)3) * 16,
-                    T, swv, sxv);
-    }
+    const int j = (int)(clr & 3);
+    if (j == 0) j0 = 0;
+    const bool done = j == 3 || clr == nrg - 1 || it == nit - 1;
+    out.row_group(red[par], acc, tid, wave, lane, j, j0, done, (clr & ~(int64_t)3) * 16, T, swv, sxv, P.Y[cw]);
     par ^= 1;
-    if (!has) out.commit(tid, R, Y, ldy);
+    if (!has) out.commit(tid, R, ldy);
+    if (++clr == nrg) { clr = 0; ++cw; }
   }
-  out.commit(tid, R, Y, ldy);
+  out.commit(tid, R, ldy);
 }
 
 // ----------------------------------------------------------------------------- table path
@@ -700,26 +677,6 @@ hipError_t launch_gemv_nm(const int8_t* Xq, const float* s_x, int64_t T, int64_t
   const int64_t nrg = cdiv(R, 16);
   const dim3 grid((unsigned)(nrg < GV_MAX_BLOCKS ? nrg : GV_MAX_BLOCKS)), block(64 * GV_WAVES);
   const uint8_t* mp = (N == M) ? nullptr : meta;
-  if (SBN_GV_STREAM && N == 2 && M == 4 && K % 1024 == 0 && K <= 4096) {
-    const dim3 sgrid((unsigned)(nrg < GV_STREAM_BLOCKS ? nrg : GV_STREAM_BLOCKS)), sblock(256);
-    if (ydt == SBN_I32_ACC)
-      SBN_LAUNCH("gemv", gemv24s_kernel<0>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
-    else if (ydt == SBN_F32)
-      SBN_LAUNCH("gemv", gemv24s_kernel<1>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
-    else
-      SBN_LAUNCH("gemv", gemv24s_kernel<2>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
-    return hipGetLastError();
-  }
-  if (SBN_GV_STREAM && N == 6 && M == 8 && K % 1024 == 0 && K <= 4096) {
-    const dim3 sgrid((unsigned)(nrg < GV_STREAM_BLOCKS ? nrg : GV_STREAM_BLOCKS)), sblock(256);
-    if (ydt == SBN_I32_ACC)
-      SBN_LAUNCH("gemv", gemv68s_kernel<0>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
-    else if (ydt == SBN_F32)
-      SBN_LAUNCH("gemv", gemv68s_kernel<1>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
-    else
-      SBN_LAUNCH("gemv", gemv68s_kernel<2>, sgrid, sblock, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
-    return hipGetLastError();
-  }
   if (N == 2 && M == 4 && K % 128 == 0) {
     if (ydt == SBN_I32_ACC)
       SBN_LAUNCH("gemv", gemv24_kernel<0>, grid, block, 0, st, Xq, s_x, T, K, codes, mp, s_w, R, Y, ldy);
@@ -738,11 +695,23 @@ hipError_t launch_gemv_nm(const int8_t* Xq, const float* s_x, int64_t T, int64_t
   return hipGetLastError();
 }
 
-}  // namespace
+template <typename Dec>
+hipError_t launch_stream(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const GemvBatch& P,
+                         int count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
+  const int64_t total = cdiv(R, 16) * count;
+  const dim3 grid((unsigned)(total < GV_STREAM_BLOCKS ? total : GV_STREAM_BLOCKS)), block(256);
+  if (ydt == SBN_I32_ACC)
+    SBN_LAUNCH("gemv", (gemv_stream_kernel<0, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
+  else if (ydt == SBN_F32)
+    SBN_LAUNCH("gemv", (gemv_stream_kernel<1, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
+  else
+    SBN_LAUNCH("gemv", (gemv_stream_kernel<2, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
+  return hipGetLastError();
+}
 
-hipError_t launch_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
-                       const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
-                       int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
+hipError_t launch_gemv_one(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                           const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
+                           int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
 #define SBN_GEMV_CASE(NN, MM) \
   if (n == NN && m == MM) return launch_gemv_nm<NN, MM>(Xq, s_x, T, K, codes, meta, s_w, R, Y, ydt, ldy, st);
   SBN_GEMV_CASE(1, 4) SBN_GEMV_CASE(2, 4) SBN_GEMV_CASE(3, 4) SBN_GEMV_CASE(4, 4)
@@ -750,6 +719,44 @@ hipError_t launch_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
   SBN_GEMV_CASE(5, 8) SBN_GEMV_CASE(6, 8) SBN_GEMV_CASE(7, 8) SBN_GEMV_CASE(8, 8)
 #undef SBN_GEMV_CASE
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemv_batched(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                               const uint8_t* const* codes, const uint8_t* const* meta,
+                               const float* const* s_w, int64_t R, int n, int m, void* const* Y,
+                               sbn_dtype ydt, int64_t ldy, int count, hipStream_t st) {
+  const bool stream_ok = SBN_GV_STREAM && K % 1024 == 0 && K <= 4096 && ((n == 2 && m == 4) || (n == 6 && m == 8));
+  if (stream_ok) {
+    GemvBatch P;
+    for (int b = 0; b < count; ++b) {
+      P.codes[b] = codes[b];
+      P.meta[b] = meta[b];
+      P.s_w[b] = s_w[b];
+      P.Y[b] = Y[b];
+    }
+    for (int b = count; b < GV_MAX_BATCH; ++b) {
+      P.codes[b] = nullptr;
+      P.meta[b] = nullptr;
+      P.s_w[b] = nullptr;
+      P.Y[b] = nullptr;
+    }
+    if (n == 2) return launch_stream<Dec24>(Xq, s_x, T, K, P, count, R, ydt, ldy, st);
+    return launch_stream<Dec68>(Xq, s_x, T, K, P, count, R, ydt, ldy, st);
+  }
+  for (int b = 0; b < count; ++b) {
+    const hipError_t e = launch_gemv_one(Xq, s_x, T, K, codes[b], meta ? meta[b] : nullptr, s_w[b], R, n, m, Y[b],
+                                         ydt, ldy, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                       const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
+                       int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
+  return launch_gemv_batched(Xq, s_x, T, K, &codes, &meta, &s_w, R, n, m, &Y, ydt, ldy, 1, st);
 }
 
 }  // namespace sbn

@@ -102,6 +102,12 @@ hipError_t launch_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx
 hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                        const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
                        int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, void* ws, hipStream_t st);
+// Decode GEMV over `count` (<= GV_MAX_BATCH) weights sharing Xq; host arrays of device pointers.
+constexpr int GV_MAX_BATCH = SBN_GEMV_MAX_BATCH;
+hipError_t launch_gemv_batched(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                               const uint8_t* const* codes, const uint8_t* const* meta,
+                               const float* const* s_w, int64_t R, int n, int m, void* const* Y,
+                               sbn_dtype ydt, int64_t ldy, int count, hipStream_t st);
 hipError_t launch_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                        const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
                        int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, hipStream_t st);

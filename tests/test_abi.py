@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = sbn.header_symbols()
-    assert len(names) == 13
+    assert len(names) == 14
     for nm in names:
         assert hasattr(L, nm), nm
 
@@ -115,6 +115,29 @@ def test_matmul_validation(L, name):
         assert call(ws=None) == NULL
     else:
         assert call(T=17) == SHAPE
+
+
+def test_gemv_batched_validation(L):
+    """Host arrays of device pointers; each weight is checked like a single call (error paths only)."""
+    f = L.sbn_sparse_ternary_gemv_batched
+    arr = lambda *ps: (ctypes.c_void_p * len(ps))(*ps)
+    three = lambda: arr(P, P, P)
+
+    def call(codes=None, meta=None, s_w=None, Y=None, count=3, T=4, K=4096, n=2, m=4, ldy=256, ydt=1):
+        return f(P, P, T, K, codes if codes is not None else three(), meta if meta is not None else three(),
+                 s_w if s_w is not None else three(), 256, n, m, Y if Y is not None else three(), ydt, ldy, count, None)
+
+    assert f(P, P, 4, 4096, None, three(), three(), 256, 2, 4, three(), 1, 256, 3, None) == NULL
+    assert call(count=0) == SHAPE
+    assert call(count=65) == SHAPE
+    assert call(codes=arr(P, None, P)) == NULL                          # a NULL weight pointer
+    assert call(meta=arr(P, P, MIS)) == ALIGN                           # a misaligned plane
+    assert call(Y=arr(MIS, P, P)) == ALIGN
+    assert call(T=17) == SHAPE
+    assert call(K=100) == SHAPE
+    assert call(n=5, m=4) == NM
+    assert call(ydt=7) == DTYPE
+    assert call(meta=arr(P, P, MIS)) == ALIGN and b"weight 2" in L.sbn_last_error()
 
 
 def test_backward_validation(L):

@@ -293,6 +293,34 @@ def test_gemv_streamed_ring_tail(n, m):
     check_outputs("gemv", f, Xq, s_x, codes, meta, s_w, R, n, m)
 
 
+@pytest.mark.parametrize("n,m,K", [(2, 4, 4096), (6, 8, 2048), (1, 4, 1024), (6, 8, 640)])
+@pytest.mark.parametrize("count,R,T", [(3, 203, 5), (64, 48, 1)])
+def test_gemv_batched_matches_oracle(n, m, K, count, R, T):
+    """Several weights sharing the activations in one call (one launch for
+    2:4 and 6:8 at K a multiple of 1024; otherwise one launch per weight):
+    every output equals the oracle's for its own weight."""
+    import torch
+    X = gaussian_bf16((T, K), 1.0, seed=count + K, stream=1)
+    Xq_h, s_x_h = O.act_quant(X)
+    Xq, s_x = dev(Xq_h), dev(s_x_h)
+    Ws = [gaussian_bf16((R, K), 0.02 * (1 + b % 3), seed=100 + b, stream=0) for b in range(count)]
+    packed = [sbn.sbn_mask_ternarize_pack(dev_bf16(W), n, m) for W in Ws]
+    codes = [p[0] for p in packed]
+    metas = None if n == m else [p[1] for p in packed]
+    s_ws = [p[2] for p in packed]
+    for ydt in (sbn.SBN_I32_ACC, sbn.SBN_F32):
+        Ys = sbn.sbn_sparse_ternary_gemv_batched(Xq, s_x, codes, metas, s_ws, R, n, m, ydt=ydt)
+        torch.cuda.synchronize()
+        for b in range(0, count, max(1, count // 8)):
+            eff, _, sw = O.quant_then_mask(Ws[b], n, m)
+            acc = O.accumulate(Xq_h, eff)
+            got = host(Ys[b])
+            if ydt == sbn.SBN_I32_ACC:
+                assert np.array_equal(got.astype(np.int64), acc), f"weight {b}"
+            else:
+                assert_rel(got, O.output(acc, sw, s_x_h), 1e-3, f"weight {b} f32 Y")
+
+
 @pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
 def test_gemv_decode_full_size(n, m):
     wl = WORKLOADS["decode"]
