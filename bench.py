@@ -1,6 +1,6 @@
 """Throughput of the Sparse-BitLinear hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|train|sweep]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|train|sweep|decode]
 
 A step is one pass of the hot path over one batch of synthetic input already
 resident in HBM:
@@ -12,6 +12,9 @@ resident in HBM:
   sweep:             GEMM alone for N:M in {2:4, 4:8, 6:8, 2:8, 1:4, 8:8},
                      T=2048, R=K=8192 (one line per ratio is not the
                      contract; the JSON line carries the list).
+  decode:            decode GEMV (T=1, R=K=4096) over pools of 128 distinct
+                     packed weights per ratio (2:4 and 6:8), as batched calls
+                     of 64 weights; `value` is GB/s of algorithmic bytes.
 `value` is dense-equivalent int8 TOPS of the whole step (2*T*R*K per
 forward product; the train step counts its three products), timed over
 --steps replays of the step captured as a HIP graph (the library only
@@ -58,7 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "train", "sweep"])
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "train", "sweep", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode GEMV measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -235,8 +238,9 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
     for i in range(P):
         call(i)
     # (i) cold single calls: kernel time from the library's events (gemv only)
-    prof = profile_pass(lambda: [call(i) for i in range(P)], 1, "gemv")
-    kern_ms, kcnt = kernel_avg_ms(prof, "gemv")
+    kname = f"gemv_stream_{n}{m}"
+    prof = profile_pass(lambda: [call(i) for i in range(P)], 1, kname)
+    kern_ms, kcnt = kernel_avg_ms(prof, kname)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def replay_ms(graphs, streams, calls):
@@ -310,6 +314,72 @@ def cpu_baseline(wl, n, m, tokens):
                       f"act_quant and the float64 matmul; ops = 2*{tokens}*R*K"}
 
 
+# ---------------------------------------------------------------------- decode step
+POOL, BATCH = 128, 64
+
+
+def make_decode_step(T=1):
+    """Decode step: every weight of two pools of POOL distinct R = K = 4096
+    packed weights (2:4 and 6:8; 537 MB and 671 MB, each at least twice the
+    Infinity Cache) multiplied by the same T activations, as batched calls of
+    BATCH weights (one launch each).  Returns (step, bytes per step, per-launch
+    bytes by kernel name)."""
+    import torch
+    import sparse_linear_layers_02_amd as sbn
+    from workloads import WORKLOADS
+    wl = WORKLOADS["decode"]
+    W = bf16_dev(wl.weights(0))
+    Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0, T=T)))
+    pools, total, per_launch = [], 0, {}
+    for n, m in wl.nm:
+        codes0, meta0, s_w0 = sbn.sbn_mask_ternarize_pack(W, n, m)
+        cb, mb = sbn.sbn_packed_bytes(wl.R, wl.K, n, m)
+        per = cb + mb + T * wl.K + 4 * T + 2 * T * wl.R + 4
+        pool = dict(n=n, m=m, codes=[codes0.clone() for _ in range(POOL)], metas=[meta0.clone() for _ in range(POOL)],
+                    s_ws=[s_w0.clone() for _ in range(POOL)],
+                    Ys=[torch.empty((T, wl.R), dtype=torch.bfloat16, device="cuda") for _ in range(POOL)])
+        pools.append(pool)
+        total += POOL * per
+        per_launch[f"gemv_stream_{n}{m}"] = BATCH * per
+    del W
+
+    def step():
+        for p in pools:
+            for b0 in range(0, POOL, BATCH):
+                sl = slice(b0, b0 + BATCH)
+                sbn.sbn_sparse_ternary_gemv_batched(Xq, s_x, p["codes"][sl], p["metas"][sl], p["s_ws"][sl], wl.R,
+                                                    p["n"], p["m"], Ys=p["Ys"][sl])
+
+    return step, total, per_launch, wl
+
+
+def cpu_baseline_decode(wl, weights=POOL):
+    """The oracle's GEMV (float64 accumulate and output scaling) for one token
+    against `weights` distinct R x K ternary weights per ratio, the effective
+    weights prepared outside the timed region.  GB/s = the decode step's
+    algorithmic bytes for those weights / time."""
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    X = wl.activations(0, T=1)
+    Xq, s_x = O.act_quant(X)
+    effs, nbytes = [], 0
+    for n, m in wl.nm:
+        eff, mask, sw = O.quant_then_mask(wl.weights(0), n, m)
+        cb, mb = O.packed_bytes(wl.R, wl.K, n, m)
+        effs += [(eff, sw)] * weights
+        nbytes += weights * (cb + mb + wl.K + 4 + 2 * wl.R + 4)
+    t0 = time.perf_counter()
+    for eff, sw in effs:
+        O.output(O.accumulate(Xq, eff), sw, s_x)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{weights} weights per ratio ({', '.join(f'{n}:{m}' for n, m in wl.nm)}) of {wl.R}x{wl.K}, "
+                      f"one token, oracle accumulate + output; bytes = the packed-weight step's algorithmic bytes"}
+
+
 # ---------------------------------------------------------------------- main
 def main():
     a = parse()
@@ -366,6 +436,24 @@ def main():
                                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                           "frac": round(fl / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                           "note": "bf16 products executed (dW runs hi and lo halves)"}
+    elif a.workload == "decode":
+        step, nbytes, per_launch, wl = make_decode_step(T=1)
+        ms, wall, prof, mode = time_steps(step, a.steps, a.warmup)
+        out.update(value=round(nbytes / (ms * 1e-3) / 1e9, 1), unit="GB/s", ms_per_step=round(ms, 4),
+                   wall_s=round(wall, 4), launch=mode)
+        out["config"] = {"workload": "decode", "T": 1, "R": wl.R, "K": wl.K, "nm": "2:4+6:8",
+                         "pool_weights_per_ratio": POOL, "weights_per_launch": BATCH,
+                         "step": "batched decode GEMV over both pools", "y_dtype": "bf16", "seed": 0}
+        for key, kname in (("roofline", "gemv_stream_24"), ("roofline_68", "gemv_stream_68")):
+            k_ms, k_cnt = kernel_avg_ms(profile_pass(step, a.steps, kname), kname)
+            ach = per_launch[kname] / (k_ms * 1e-3) / 1e9
+            out[key] = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                        "traffic": traffic_from_profiles(kname, "decode"), "kernel_us": round(k_ms * 1e3, 3),
+                        "launches": k_cnt, "bytes_per_launch": per_launch[kname],
+                        "note": "algorithmic bytes: packed planes + activations + scales + bf16 outputs of the "
+                                f"{BATCH} weights of one launch"}
+        out["stages_us"] = {k: round(v[1] / v[0] * 1e3, 3) for k, v in sorted(prof.items()) if v[0]}
     else:
         wl = WORKLOADS["sweep"]
         rows = []
@@ -390,20 +478,24 @@ def main():
         out.update(value=round(ops / (tot_ms * 1e-3) / 1e12, 3), unit="TOPS", ms_per_step=round(tot_ms, 4))
         out["config"] = {"workload": "sweep", "T": wl.T, "R": wl.R, "K": wl.K, "step": "gemm for each N:M"}
         out["sweep"] = rows
-        best = min(rows, key=lambda r: r["kernel_us"])
-        out["roofline"] = {"kernel": best["kernel"], "bound": "mfma", "achieved": best["TOPS_kernel"],
+        r24 = next(r for r in rows if r["nm"] == "2:4")
+        out["roofline"] = {"kernel": r24["kernel"], "bound": "mfma", "achieved": r24["TOPS_kernel"],
                            "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                           "frac": round(best["TOPS_kernel"] / PEAK_INT8_TOPS, 4), "traffic": None}
+                           "frac": round(r24["TOPS_kernel"] / PEAK_INT8_TOPS, 4), "traffic": None,
+                           "frac_of_sparse_peak": round(r24["TOPS_kernel"] / PEAK_INT8_SPARSE_TOPS, 4),
+                           "note": "the 2:4 row"}
 
-    if not a.no_extras:
+    if not a.no_extras and a.workload != "decode":
         out["decode_gemv"] = [decode_gemv(2, 4, 1), decode_gemv(6, 8, 1)]
 
-    if not a.no_cpu_baseline:
+    if a.no_cpu_baseline:
+        out["cpu_baseline"] = None
+    elif a.workload == "decode":
+        out["cpu_baseline"] = cpu_baseline_decode(WORKLOADS["decode"], weights=POOL)
+    else:
         wl = WORKLOADS["prefill" if a.workload == "sweep" else a.workload]
         n, m = wl.nm[0]
         out["cpu_baseline"] = cpu_baseline(wl, n, m, tokens=min(wl.T, 4096 if a.workload == "prefill" else 512))
-    else:
-        out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
 
 

@@ -230,7 +230,8 @@ sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* 
  * and writes one line per kernel name, "name launches total_ms\n", into buf
  * (NUL-terminated, truncated to buf_bytes); sbn_profile_reset forgets them.
  * Kernel names: abs_sum, mask_pack, act_quant, expand_sparse, expand_dense,
- * gemm_smfmac, gemm_mfma, gemv, expand_wt, prep_u, prep_xq, gemm_dx, gemm_dw.
+ * gemm_smfmac, gemm_mfma, gemv, gemv_stream_24, gemv_stream_68, expand_wt,
+ * prep_u, prep_xq, gemm_dx, gemm_dw.
  * Errors: SBN_ERR_NULL (buf), SBN_ERR_HIP.
  */
 sbn_status sbn_profile_enable(int on, const char* kernel);

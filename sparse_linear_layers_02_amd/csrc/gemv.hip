@@ -696,16 +696,16 @@ hipError_t launch_gemv_nm(const int8_t* Xq, const float* s_x, int64_t T, int64_t
 }
 
 template <typename Dec>
-hipError_t launch_stream(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const GemvBatch& P,
-                         int count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
+hipError_t launch_stream(const char* name, const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                         const GemvBatch& P, int count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
   const int64_t total = cdiv(R, 16) * count;
   const dim3 grid((unsigned)(total < GV_STREAM_BLOCKS ? total : GV_STREAM_BLOCKS)), block(256);
   if (ydt == SBN_I32_ACC)
-    SBN_LAUNCH("gemv", (gemv_stream_kernel<0, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
+    SBN_LAUNCH(name, (gemv_stream_kernel<0, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
   else if (ydt == SBN_F32)
-    SBN_LAUNCH("gemv", (gemv_stream_kernel<1, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
+    SBN_LAUNCH(name, (gemv_stream_kernel<1, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
   else
-    SBN_LAUNCH("gemv", (gemv_stream_kernel<2, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
+    SBN_LAUNCH(name, (gemv_stream_kernel<2, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
   return hipGetLastError();
 }
 
@@ -742,8 +742,8 @@ hipError_t launch_gemv_batched(const int8_t* Xq, const float* s_x, int64_t T, in
       P.s_w[b] = nullptr;
       P.Y[b] = nullptr;
     }
-    if (n == 2) return launch_stream<Dec24>(Xq, s_x, T, K, P, count, R, ydt, ldy, st);
-    return launch_stream<Dec68>(Xq, s_x, T, K, P, count, R, ydt, ldy, st);
+    if (n == 2) return launch_stream<Dec24>("gemv_stream_24", Xq, s_x, T, K, P, count, R, ydt, ldy, st);
+    return launch_stream<Dec68>("gemv_stream_68", Xq, s_x, T, K, P, count, R, ydt, ldy, st);
   }
   for (int b = 0; b < count; ++b) {
     const hipError_t e = launch_gemv_one(Xq, s_x, T, K, codes[b], meta ? meta[b] : nullptr, s_w[b], R, n, m, Y[b],
