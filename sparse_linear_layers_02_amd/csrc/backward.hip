@@ -185,16 +185,14 @@ __global__ __launch_bounds__(256, 1) void bf16_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < nsteps) load_stage(s, s);
-  for (int64_t step = 0; step < nsteps; ++step) {
-    if (step + NST - 2 < nsteps) wait_vmcnt<(NST - 2) * LPS>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (step + NST - 1 < nsteps) load_stage((int)((step + NST - 1) % NST), step + NST - 1);
-    const uint8_t* base = smem + (step % NST) * STAGE;
-    v8bf b[8], b2[8];
+  // Software pipeline: the fragments of step s are read from LDS into one set
+  // of registers while the matrix instructions of step s - 1 run on the other
+  // set, so no step starts by waiting for LDS.  Stage s + 1 is waited for and
+  // published (barrier) at the top of step s; the barrier also shows that every
+  // wave holds stage s in registers, so its buffer is refilled with stage
+  // s + NST right then (NST - 1 steps of load latency hidden).
+  auto read_stage = [&](int64_t st, v8bf (&a)[8], v8bf (&b)[8], v8bf (&b2)[8]) {
+    const uint8_t* base = smem + (st % NST) * STAGE;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int jj = 8 * wb + j;
@@ -203,15 +201,52 @@ __global__ __launch_bounds__(256, 1) void bf16_gemm_kernel(
         b2[j] = __builtin_bit_cast(v8bf, *(const v4i*)(base + A_BYTES + 16 * 1024 + jj * 1024 + lane * 16));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ii = 8 * wa + i;
-      const v8bf a = __builtin_bit_cast(v8bf, *(const v4i*)(base + ii * 1024 + lane * 16));
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_bit_cast(v8bf, *(const v4i*)(base + (8 * wa + i) * 1024 + lane * 16));
+  };
+  auto mma = [&](const v8bf (&a)[8], const v8bf (&b)[8], const v8bf (&b2)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
-        if (MODE == 1) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b2[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        if (MODE == 1) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b2[j], acc[i][j], 0, 0, 0);
       }
-    }
+  };
+  // top of step s: this wave's loads of stage s + 1 have landed (at most the
+  // stages after it still fly), every wave's have (barrier), stage s's buffer is free
+  auto advance = [&](int64_t s) {
+    const int64_t last = (s + NST - 1 < nsteps - 1 ? s + NST - 1 : nsteps - 1);   // last stage issued
+    const int64_t later = last - (s + 1);
+    if (later >= NST - 2) wait_vmcnt<(NST - 2) * LPS>();
+    else if (later == 1) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (s + NST < nsteps) load_stage((int)(s % NST), s + NST);
+  };
+
+#pragma unroll
+  for (int q = 0; q < NST; ++q)
+    if (q < nsteps) load_stage(q, q);
+  if (nsteps >= NST) wait_vmcnt<(NST - 1) * LPS>();
+  else wait_vmcnt<0>();
+  lds_barrier();                                       // stage 0 visible
+  v8bf a0[8], b0[8], c0[8], a1[8], b1[8], c1[8];
+  read_stage(0, a0, b0, c0);
+  // scheduling fences keep each step's reads ahead of its matrix instructions
+  // and stop the next step's reads from being hoisted over them (which would
+  // keep three register sets alive)
+  for (int64_t s = 0; s < nsteps; s += 2) {
+    advance(s);
+    if (s + 1 < nsteps) read_stage(s + 1, a1, b1, c1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0, c0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 >= nsteps) break;
+    advance(s + 1);
+    if (s + 2 < nsteps) read_stage(s + 2, a0, b0, c0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a1, b1, c1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // lane holds A rows (k) a..a+3 of B row (t or r) b

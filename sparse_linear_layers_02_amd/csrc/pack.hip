@@ -15,8 +15,8 @@
 // 8-bit significand.  Magnitudes with exponent field e in [95, 131), i.e.
 // 2^-32 <= |w| < 16, are multiples of 2^-39 below 2^4; a float64 running sum
 // of at most 1024 of them stays below 2^53 units, so it is exact in any
-// order.  Each thread sums at most 32 of them in float64 (four 16-byte
-// chunks, while the next four load) before flushing into an int64 counter of
+// order.  Each thread sums at most 8 * U1 of them in float64 (U1 16-byte
+// chunks, while the next U1 load) before flushing into an int64 counter of
 // 2^-39 units.
 // Everything outside that window (zero, subnormal, tiny or >= 16) is added
 // to 256 per-exponent integer bins in LDS: exact too.  Each block writes its
@@ -188,9 +188,15 @@ __device__ inline void pair_slow(uint32_t u, unsigned long long* bins) {
   if (!in_window(hi) && hi) slow_add(bins, hi);
 }
 
-constexpr int U = 4;      // 16-byte chunks per thread per step in pass 2 (2:4), plus as many prefetched
-constexpr int U1 = 4;     // the same in pass 1
-constexpr int PT1 = 1024; // pass-1 threads per block: 16 waves keep up to 128 KB of W in flight per CU
+#ifndef SBN_PACK_U
+#define SBN_PACK_U 2
+#endif
+#ifndef SBN_PACK_U1
+#define SBN_PACK_U1 2
+#endif
+constexpr int U = SBN_PACK_U;    // 16-byte chunks per thread per step in pass 2 (2:4), plus as many prefetched
+constexpr int U1 = SBN_PACK_U1;  // the same in pass 1
+constexpr int PT1 = 1024; // pass-1 threads per block: 16 waves keep 64 KB of W in flight per CU
 
 template <bool FLAT>
 __device__ inline uint4 chunk_at(const uint16_t* __restrict__ W, int64_t c, int64_t kc, int64_t ldw) {
