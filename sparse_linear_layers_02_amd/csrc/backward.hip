@@ -131,26 +131,33 @@ __global__ __launch_bounds__(256) void prep_xq_kernel(const int8_t* __restrict__
 // ---------------------------------------------------------------- bf16 GEMM on fragments
 // MODE 0 (dX): A = Wt fragments (rows k, contraction r), B = dY rows read directly.
 // MODE 1 (dW): A = Xq fragments (rows k, contraction t), B = u_hi and u_lo fragments (rows r).
-// Block tile 256 (A rows) x 256 (B rows), 4 waves 2 x 2, wave tile 128 x 128,
-// one contraction step of 32 per stage (MODE 1 takes two B fragments per step),
-// 3-4 stages of direct-to-LDS loads in flight.
+// Block tile 256 (A rows) x 256 (B rows), 8 waves, wave tile 128 x 64 (8 x 4
+// accumulator tiles of 16 x 16), one contraction step of 32 per LDS stage
+// (MODE 1 takes two B fragments per step), stages filled by direct
+// global->LDS loads issued NST - 1 steps ahead.  Ping-pong: waves w and w + 4
+// share a SIMD and alternate a memory phase (LDS reads of one step, plus the
+// loads of a later stage) with a compute phase (32 or 64 matrix instructions),
+// so one of them keeps the matrix core busy while the other waits on LDS.
 template <int MODE, int OUT>
-__global__ __launch_bounds__(256, 1) void bf16_gemm_kernel(
+__global__ __launch_bounds__(512, 1) void bf16_gemm_kernel(
     const uint8_t* __restrict__ Afr, const uint8_t* __restrict__ Bfr_hi,
     const uint8_t* __restrict__ Bfr_lo, const uint16_t* __restrict__ dY, int64_t nB /*B rows*/,
     int64_t nA /*A rows*/, int64_t nsteps, int64_t Rc /*dY cols (MODE 0)*/,
     const float* __restrict__ s_w, void* __restrict__ Out, int64_t ldo) {
+  constexpr int NW = 8, MI = 8, MJ = 4;
   constexpr int NBF = MODE == 1 ? 2 : 1;
   constexpr int A_BYTES = 16 * 1024;
   constexpr int B_BYTES = 16 * 1024 * NBF;
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int NST = MODE == 1 ? 3 : 4;              // 144 KB / 128 KB of LDS
-  constexpr int LPS = 4 + 4 * NBF;                    // loads per stage per wave
+  constexpr int LPS = 2 + 2 * NBF;                    // loads per stage per wave
+  constexpr int WAIT = (NST - 2) * LPS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wa = wave >> 1, wb = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int grp = wave >> 2;                           // waves w and w + 4 share a SIMD
+  const int wa = wave & 1, wb = wave >> 1;             // A rows 128*wa.., B rows 64*wb..
   const int64_t tile_b = (int64_t)blockIdx.x * 256;
   const int64_t tile_a = (int64_t)blockIdx.y * 256;
   const int64_t ab0 = tile_a / 16, bb0 = tile_b / 16;
@@ -158,13 +165,13 @@ __global__ __launch_bounds__(256, 1) void bf16_gemm_kernel(
   auto load_stage = [&](int s, int64_t step) {
     uint8_t* base = smem + s * STAGE;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = wave + 4 * q;
+    for (int q = 0; q < 2; ++q) {
+      const int i = wave + NW * q;
       g2lds16(Afr + ((ab0 + i) * nsteps + step) * 1024 + lane * 16, base + i * 1024);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = wave + 4 * q;
+    for (int q = 0; q < 2; ++q) {
+      const int j = wave + NW * q;
       if (MODE == 0) {
         int64_t t = tile_b + 16 * j + (lane & 15);
         t = t < nB ? t : nB - 1;
@@ -179,85 +186,91 @@ __global__ __launch_bounds__(256, 1) void bf16_gemm_kernel(
     }
   };
 
-  v4f acc[8][8];
+  v4f acc[MI][MJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  v8bf a[MI], b[MJ], b2[MJ];
 
-  // Software pipeline: the fragments of step s are read from LDS into one set
-  // of registers while the matrix instructions of step s - 1 run on the other
-  // set, so no step starts by waiting for LDS.  Stage s + 1 is waited for and
-  // published (barrier) at the top of step s; the barrier also shows that every
-  // wave holds stage s in registers, so its buffer is refilled with stage
-  // s + NST right then (NST - 1 steps of load latency hidden).
-  auto read_stage = [&](int64_t st, v8bf (&a)[8], v8bf (&b)[8], v8bf (&b2)[8]) {
-    const uint8_t* base = smem + (st % NST) * STAGE;
+  // memory phase of step s: issue the loads of stage s + NST - 1, read step s's fragments
+  auto mem_phase = [&](int64_t s) {
+    if (s + NST - 1 < nsteps) load_stage((int)((s + NST - 1) % NST), s + NST - 1);
+    const uint8_t* base = smem + (s % NST) * STAGE;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int jj = 8 * wb + j;
+    for (int j = 0; j < MJ; ++j) {
+      const int jj = MJ * wb + j;
       b[j] = __builtin_bit_cast(v8bf, *(const v4i*)(base + A_BYTES + jj * 1024 + lane * 16));
       if (MODE == 1)
         b2[j] = __builtin_bit_cast(v8bf, *(const v4i*)(base + A_BYTES + 16 * 1024 + jj * 1024 + lane * 16));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = __builtin_bit_cast(v8bf, *(const v4i*)(base + (8 * wa + i) * 1024 + lane * 16));
+    for (int i = 0; i < MI; ++i)
+      a[i] = __builtin_bit_cast(v8bf, *(const v4i*)(base + (MI * wa + i) * 1024 + lane * 16));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  auto mma = [&](const v8bf (&a)[8], const v8bf (&b)[8], const v8bf (&b2)[8]) {
+  auto comp_phase = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < MJ; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         if (MODE == 1) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b2[j], acc[i][j], 0, 0, 0);
       }
   };
-  // top of step s: this wave's loads of stage s + 1 have landed (at most the
-  // stages after it still fly), every wave's have (barrier), stage s's buffer is free
-  auto advance = [&](int64_t s) {
-    const int64_t last = (s + NST - 1 < nsteps - 1 ? s + NST - 1 : nsteps - 1);   // last stage issued
-    const int64_t later = last - (s + 1);
-    if (later >= NST - 2) wait_vmcnt<(NST - 2) * LPS>();
-    else if (later == 1) wait_vmcnt<LPS>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (s + NST < nsteps) load_stage((int)(s % NST), s + NST);
+  // this wave's loads of stage s + 1 have landed (later stages may still fly)
+  auto vm_wait = [&](int64_t s) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + NST - 1 < nsteps) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(WAIT) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Barrier schedule (B0, B1, ... in order; both groups pass the same count):
+  //   group 0: B0 | mem(s) B(2s+1) comp(s) wait B(2s+2) | ...
+  //   group 1: B0 B1 | mem(s) wait B(2s+2) comp(s) B(2s+3) | ... (no barrier after its last comp)
+  // so phase (B(2s+1), B(2s+2)) is comp(s) of group 0 beside mem(s) of group 1,
+  // and phase (B(2s+2), B(2s+3)) is comp(s) of group 1 beside mem(s+1) of group 0.
+  // Stage s is complete before B(2s) and read only between B(2s) and B(2s+2);
+  // its buffer is refilled (stage s + NST) from mem(s+1), after B(2s+2).
 #pragma unroll
-  for (int q = 0; q < NST; ++q)
-    if (q < nsteps) load_stage(q, q);
-  if (nsteps >= NST) wait_vmcnt<(NST - 1) * LPS>();
-  else wait_vmcnt<0>();
-  lds_barrier();                                       // stage 0 visible
-  v8bf a0[8], b0[8], c0[8], a1[8], b1[8], c1[8];
-  read_stage(0, a0, b0, c0);
-  // scheduling fences keep each step's reads ahead of its matrix instructions
-  // and stop the next step's reads from being hoisted over them (which would
-  // keep three register sets alive)
-  for (int64_t s = 0; s < nsteps; s += 2) {
-    advance(s);
-    if (s + 1 < nsteps) read_stage(s + 1, a1, b1, c1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0, c0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 >= nsteps) break;
-    advance(s + 1);
-    if (s + 2 < nsteps) read_stage(s + 2, a0, b0, c0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1, c1);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nsteps) load_stage(s, s);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  barrier();                                           // B0: stages 0 .. NST-2 visible
+  if (grp == 0) {
+    for (int64_t s = 0; s < nsteps; ++s) {
+      mem_phase(s);
+      barrier();
+      comp_phase();
+      vm_wait(s);
+      barrier();
+    }
+  } else {
+    barrier();
+    for (int64_t s = 0; s < nsteps; ++s) {
+      mem_phase(s);
+      vm_wait(s);
+      barrier();
+      comp_phase();
+      if (s + 1 < nsteps) barrier();
+    }
   }
 
   // lane holds A rows (k) a..a+3 of B row (t or r) b
   const float scale = MODE == 0 ? *s_w : 1.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t brow = tile_b + 16 * (8 * wb + j) + (lane & 15);
+  for (int j = 0; j < MJ; ++j) {
+    const int64_t brow = tile_b + 16 * (MJ * wb + j) + (lane & 15);
     if (brow >= nB) continue;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t arow = tile_a + 16 * (8 * wa + i) + 4 * (lane >> 4);
+    for (int i = 0; i < MI; ++i) {
+      const int64_t arow = tile_a + 16 * (MI * wa + i) + 4 * (lane >> 4);
       if (arow >= nA) continue;
       const v4f c = acc[i][j] * scale;
       if (OUT == 1) {
@@ -319,10 +332,10 @@ hipError_t launch_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 grid((unsigned)cdiv(T, 256), (unsigned)cdiv(K, 256));
     if (dxdt == SBN_F32)
-      SBN_LAUNCH("gemm_dx", (bf16_gemm_kernel<0, 1>), grid, dim3(256), 0, st, w + L.wt, nullptr, nullptr,
+      SBN_LAUNCH("gemm_dx", (bf16_gemm_kernel<0, 1>), grid, dim3(512), 0, st, w + L.wt, nullptr, nullptr,
                          dY, T, K, L.RB32, R, s_w, dX, K);
     else
-      SBN_LAUNCH("gemm_dx", (bf16_gemm_kernel<0, 2>), grid, dim3(256), 0, st, w + L.wt, nullptr, nullptr,
+      SBN_LAUNCH("gemm_dx", (bf16_gemm_kernel<0, 2>), grid, dim3(512), 0, st, w + L.wt, nullptr, nullptr,
                          dY, T, K, L.RB32, R, s_w, dX, K);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
@@ -336,7 +349,7 @@ hipError_t launch_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_
                        L.KB16, L.TB32, (uint4*)(w + L.xq));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 grid((unsigned)cdiv(R, 256), (unsigned)cdiv(K, 256));
-    SBN_LAUNCH("gemm_dw", (bf16_gemm_kernel<1, 1>), grid, dim3(256), 0, st, w + L.xq, w + L.uhi,
+    SBN_LAUNCH("gemm_dw", (bf16_gemm_kernel<1, 1>), grid, dim3(512), 0, st, w + L.xq, w + L.uhi,
                        w + L.ulo, nullptr, R, K, L.TB32, (int64_t)0, s_w, (void*)dW, K);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
