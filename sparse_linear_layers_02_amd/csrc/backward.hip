@@ -15,117 +15,143 @@
 //
 // Passes:
 //   expand_wt      packed planes -> bf16 Wt fragments, rows k, contraction r
-//   prep_gradw     dY, s_x, Xq -> bf16 fragments (u_hi, u_lo rows r; Xq rows k),
-//                  contraction t
+//   prep_u         dY, s_x -> bf16 u_hi, u_lo fragments, rows r, contraction t
+//   prep_xq        Xq -> bf16 fragments, rows k, contraction t
 //   bf16 GEMM x2   dX^T tile = Wt^T dY^T   and   dW^T tile = Xq^T (u_hi + u_lo)
 // Fragment = 16 rows x 32 contraction, lane l holds row l%16 and contraction
 // entries 8*(l/16) .. +8 (the lane order of v_mfma_f32_16x16x32_bf16).
-#include "sbn_internal.h"
+#include "sbn_decode.h"
 
 namespace sbn {
 namespace {
 
 constexpr uint16_t BF16_ONE = 0x3F80, BF16_MONE = 0xBF80;
 
-__device__ inline uint32_t read_bits_b(const uint8_t* p, int64_t off, int nbits) {
-  const uint8_t* q = p + (off >> 3);
-  const int s = (int)(off & 7);
-  uint32_t v = 0;
-  const int nb = (s + nbits + 7) >> 3;
-  for (int i = 0; i < nb; ++i) v |= (uint32_t)q[i] << (8 * i);
-  return (v >> s) & ((1u << nbits) - 1u);
-}
+// ---------------------------------------------------------------- fragment transposes
+// The three operand passes below are transposes: their sources are row-major
+// with the contraction index (r or t) as the row, and a fragment wants 8
+// consecutive contraction entries of one output row (k or r) per lane.  A block
+// takes a tile of 32 contraction entries x 128 rows: it reads the tile's source
+// rows with coalesced 16-byte loads, writes them transposed into LDS as bf16
+// ([row][contraction], pitch TP entries), and stores the tile's eight 1 KB
+// fragments with one 16-byte store per lane.  Entries past the real sizes are 0.
+constexpr int TP = 40;                               // LDS pitch in bf16 (80 B: 16-byte aligned rows)
 
-// ternary weight at (r, k) from the packed planes, as bf16 bits
-__device__ inline uint16_t w_at(const uint8_t* codes, const uint8_t* meta, int64_t K, int n, int m,
-                                int64_t r, int64_t k) {
-  const int64_t g = k / m;
-  const int p = (int)(k - g * m);
-  int slot = p;
-  if (n < m) {
-    const uint32_t gm = read_bits_b(meta + r * (K / 8), g * m, m);
-    if (!((gm >> p) & 1u)) return 0;
-    slot = __builtin_popcount(gm & ((1u << p) - 1u));
-  }
-  const int64_t crow = K * n / (4 * m);
-  const uint32_t c = read_bits_b(codes + r * crow, 2 * (n * g + slot), 2);
-  return c == 1u ? BF16_ONE : c == 3u ? BF16_MONE : (uint16_t)0;
-}
-
-// one thread = one lane of fragment (kb, rb): rows k, contraction r
-__global__ __launch_bounds__(256) void expand_wt_kernel(const uint8_t* __restrict__ codes,
-                                                        const uint8_t* __restrict__ meta, int64_t R,
-                                                        int64_t K, int n, int m, int64_t KB16,
-                                                        int64_t RB32, uint4* __restrict__ out) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= KB16 * RB32 * 64) return;
-  const int l = (int)(gid & 63);
-  const int64_t f = gid >> 6;
-  const int64_t kb = f / RB32, rb = f - kb * RB32;
-  const int64_t k = kb * 16 + (l & 15);
-  const int64_t r0 = rb * 32 + 8 * (l >> 4);
-  uint16_t v[8];
+// the eight fragments (rows row0 .. row0 + 127, contraction block cb) of an LDS
+// tile [128][TP] into out[(rowblock * CB + cb) * 64 + lane]
+__device__ inline void store_tile(const uint16_t* tile, uint4* __restrict__ out, int64_t rb0, int64_t cb,
+                                  int64_t CB) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (k < K && r0 + j < R) ? w_at(codes, meta, K, n, m, r0 + j, k) : (uint16_t)0;
-  uint4 o;
-  o.x = v[0] | ((uint32_t)v[1] << 16);
-  o.y = v[2] | ((uint32_t)v[3] << 16);
-  o.z = v[4] | ((uint32_t)v[5] << 16);
-  o.w = v[6] | ((uint32_t)v[7] << 16);
-  out[gid] = o;
+  for (int h = 0; h < 2; ++h) {
+    const int q = threadIdx.x + 256 * h;               // fragment q / 64, lane q % 64
+    const int f = q >> 6, l = q & 63;
+    const int row = 16 * f + (l & 15), c0 = 8 * (l >> 4);
+    out[((rb0 + f) * CB + cb) * 64 + l] = *(const uint4*)(tile + row * TP + c0);
+  }
 }
 
-// fragments for dW: u = dY*s_x split hi/lo (rows r), Xq as bf16 (rows k); contraction t
+// one bf16 into tile[row][c]
+__device__ inline void tile_put(uint16_t* tile, int row, int c, uint16_t v) { tile[row * TP + c] = v; }
+
+// Wt fragments (rows k, contraction r) from the packed planes.  Thread (r, seg)
+// decodes positions 16 seg .. +16 of the tile's 128 k for row r through the
+// unpack table; blocks walk the tiles with a grid stride.
+template <int M>
+__global__ __launch_bounds__(256) void expand_wt_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+                                                        int n, int64_t KB16, int64_t RB32, int64_t cplane,
+                                                        uint4* __restrict__ out) {
+  __shared__ uint32_t lut[4096];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * TP];
+  for (int i = threadIdx.x; i < 4096; i += 256) lut[i] = unpack_entry((uint32_t)i);
+  const bool dense = meta == nullptr;
+  const int64_t crow = K * n / (4 * M);                // code bytes per row
+  const int64_t lastw = (cplane - 4) & ~(int64_t)3;
+  const int64_t ntk = KB16 / 8, ntiles = ntk * RB32;
+  // lanes of a wave take 32 consecutive rows r of two segments, so each LDS
+  // write instruction fills contiguous bf16 entries of two tile rows
+  const int rl = threadIdx.x & 31, seg = threadIdx.x >> 5;
+  for (int64_t tt = blockIdx.x; tt < ntiles; tt += gridDim.x) {
+    const int64_t kt = tt / RB32, rb = tt - kt * RB32;
+    const int64_t r = rb * 32 + rl, k0 = kt * 128 + 16 * seg;
+    v4i a = (v4i){0, 0, 0, 0};
+    __syncthreads();                                   // lut built / previous tile stored
+    if (r < R && k0 < K) {
+      const uint32_t mw16 = dense ? 0xFFFFu : (uint32_t)*(const uint16_t*)(meta + r * (K / 8) + k0 / 8);
+      const int64_t cbit = r * crow * 8 + k0 * 2 * n / M;   // the 16 positions start on a group boundary
+      const int64_t a0 = (cbit >> 3) & ~(int64_t)3;
+      const int sh = (int)(cbit - a0 * 8);
+      const uint32_t w0 = *(const uint32_t*)(codes + (a0 < lastw ? a0 : lastw));
+      const uint32_t w1 = *(const uint32_t*)(codes + (a0 + 4 < lastw ? a0 + 4 : lastw));
+      const unsigned long long c = (((unsigned long long)w1 << 32) | w0) >> sh;
+      a = unpack16<M>(lut, mw16, dense, n, c, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int8_t v = (int8_t)((uint32_t)a[i >> 2] >> (8 * (i & 3)));
+      tile_put(tile, 16 * seg + i, rl, v == 1 ? BF16_ONE : v == -1 ? BF16_MONE : (uint16_t)0);
+    }
+    __syncthreads();
+    store_tile(tile, out, kt * 8, rb, RB32);
+  }
+}
+
+// u = dY * s_x split into bf16 hi and lo fragments (rows r, contraction t)
 __global__ __launch_bounds__(256) void prep_u_kernel(const uint16_t* __restrict__ dY,
                                                      const float* __restrict__ s_x, int64_t T,
                                                      int64_t R, int64_t RB16, int64_t TB32,
                                                      uint4* __restrict__ uhi, uint4* __restrict__ ulo) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= RB16 * TB32 * 64) return;
-  const int l = (int)(gid & 63);
-  const int64_t f = gid >> 6;
-  const int64_t rb = f / TB32, tb = f - rb * TB32;
-  const int64_t r = rb * 16 + (l & 15);
-  const int64_t t0 = tb * 32 + 8 * (l >> 4);
-  uint16_t h[8], lo[8];
+  __shared__ __attribute__((aligned(16))) uint16_t th[128 * TP], tl[128 * TP];
+  const int64_t rt = blockIdx.x / TB32, tb = blockIdx.x - rt * TB32;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t t = t0 + j;
-    float u = 0.0f;
-    if (r < R && t < T) u = bf16_to_f32(dY[t * R + r]) * s_x[t];
-    h[j] = f32_to_bf16_rne(u);
-    lo[j] = f32_to_bf16_rne(u - bf16_to_f32(h[j]));
+  for (int h = 0; h < 2; ++h) {                        // 32 t x 16 chunks of 8 r; lanes run over t
+    const int q = threadIdx.x + 256 * h;
+    const int tl_ = q & 31, ch = q >> 5;
+    const int64_t t = tb * 32 + tl_, r0 = rt * 128 + 8 * ch;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    float sx = 0.0f;
+    if (t < T && r0 < R) {
+      sx = s_x[t];
+      if (r0 + 8 <= R && R % 8 == 0) v = *(const uint4*)(dY + t * R + r0);
+      else {
+        uint16_t e[8];
+        for (int i = 0; i < 8; ++i) e[i] = r0 + i < R ? dY[t * R + r0 + i] : (uint16_t)0;
+        v = make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
+                       e[6] | ((uint32_t)e[7] << 16));
+      }
+    }
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float u = bf16_to_f32((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) * sx;
+      const uint16_t hi = f32_to_bf16_rne(u);
+      tile_put(th, 8 * ch + i, tl_, hi);
+      tile_put(tl, 8 * ch + i, tl_, f32_to_bf16_rne(u - bf16_to_f32(hi)));
+    }
   }
-  uint4 a, b;
-  a.x = h[0] | ((uint32_t)h[1] << 16); a.y = h[2] | ((uint32_t)h[3] << 16);
-  a.z = h[4] | ((uint32_t)h[5] << 16); a.w = h[6] | ((uint32_t)h[7] << 16);
-  b.x = lo[0] | ((uint32_t)lo[1] << 16); b.y = lo[2] | ((uint32_t)lo[3] << 16);
-  b.z = lo[4] | ((uint32_t)lo[5] << 16); b.w = lo[6] | ((uint32_t)lo[7] << 16);
-  uhi[gid] = a;
-  ulo[gid] = b;
+  __syncthreads();
+  store_tile(th, uhi, rt * 8, tb, TB32);
+  store_tile(tl, ulo, rt * 8, tb, TB32);
 }
 
+// Xq as bf16 fragments (rows k, contraction t); |q| <= 127 is exact in bf16
 __global__ __launch_bounds__(256) void prep_xq_kernel(const int8_t* __restrict__ Xq, int64_t T,
                                                       int64_t K, int64_t KB16, int64_t TB32,
                                                       uint4* __restrict__ out) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= KB16 * TB32 * 64) return;
-  const int l = (int)(gid & 63);
-  const int64_t f = gid >> 6;
-  const int64_t kb = f / TB32, tb = f - kb * TB32;
-  const int64_t k = kb * 16 + (l & 15);
-  const int64_t t0 = tb * 32 + 8 * (l >> 4);
-  uint16_t h[8];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * TP];
+  const int64_t kt = blockIdx.x / TB32, tb = blockIdx.x - kt * TB32;
+  const int tl_ = threadIdx.x & 31, ch = threadIdx.x >> 5;  // 32 t x 8 chunks of 16 k; lanes run over t
+  const int64_t t = tb * 32 + tl_, k0 = kt * 128 + 16 * ch;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (t < T && k0 < K) v = *(const uint4*)(Xq + t * K + k0);   // K % 64 == 0
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t t = t0 + j;
-    const float x = (k < K && t < T) ? (float)Xq[t * K + k] : 0.0f;
-    h[j] = (uint16_t)(__float_as_uint(x) >> 16);     // |q| <= 127: exact in bf16
+  for (int i = 0; i < 16; ++i) {
+    const float x = (float)(int8_t)(w[i >> 2] >> (8 * (i & 3)));
+    tile_put(tile, 16 * ch + i, tl_, (uint16_t)(__float_as_uint(x) >> 16));
   }
-  uint4 a;
-  a.x = h[0] | ((uint32_t)h[1] << 16); a.y = h[2] | ((uint32_t)h[3] << 16);
-  a.z = h[4] | ((uint32_t)h[5] << 16); a.w = h[6] | ((uint32_t)h[7] << 16);
-  out[gid] = a;
+  __syncthreads();
+  store_tile(tile, out, kt * 8, tb, TB32);
 }
 
 // ---------------------------------------------------------------- bf16 GEMM on fragments
@@ -326,9 +352,15 @@ hipError_t launch_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_
   uint8_t* w = (uint8_t*)ws;
   hipError_t e;
   if (dX) {
-    const int64_t thr = L.KB16 * L.RB32 * 64;
-    SBN_LAUNCH("expand_wt", expand_wt_kernel, dim3((unsigned)cdiv(thr, 256)), dim3(256), 0, st, codes,
-                       (n == m) ? nullptr : meta, R, K, n, m, L.KB16, L.RB32, (uint4*)(w + L.wt));
+    int64_t tiles = (L.KB16 / 8) * L.RB32;
+    if (tiles > 2048) tiles = 2048;                     // grid stride: the unpack table is built per block
+    const int64_t cplane = round_up(R * K * n / (4 * m), 16);
+    if (m == 4)
+      SBN_LAUNCH("expand_wt", expand_wt_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, st, codes,
+                 (n == m) ? nullptr : meta, R, K, n, L.KB16, L.RB32, cplane, (uint4*)(w + L.wt));
+    else
+      SBN_LAUNCH("expand_wt", expand_wt_kernel<8>, dim3((unsigned)tiles), dim3(256), 0, st, codes,
+                 (n == m) ? nullptr : meta, R, K, n, L.KB16, L.RB32, cplane, (uint4*)(w + L.wt));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 grid((unsigned)cdiv(T, 256), (unsigned)cdiv(K, 256));
     if (dxdt == SBN_F32)
@@ -340,13 +372,11 @@ hipError_t launch_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dW) {
-    const int64_t tu = L.RB16 * L.TB32 * 64;
-    SBN_LAUNCH("prep_u", prep_u_kernel, dim3((unsigned)cdiv(tu, 256)), dim3(256), 0, st, dY, s_x, T, R,
-                       L.RB16, L.TB32, (uint4*)(w + L.uhi), (uint4*)(w + L.ulo));
+    SBN_LAUNCH("prep_u", prep_u_kernel, dim3((unsigned)((L.RB16 / 8) * L.TB32)), dim3(256), 0, st, dY, s_x, T, R,
+               L.RB16, L.TB32, (uint4*)(w + L.uhi), (uint4*)(w + L.ulo));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t tx = L.KB16 * L.TB32 * 64;
-    SBN_LAUNCH("prep_xq", prep_xq_kernel, dim3((unsigned)cdiv(tx, 256)), dim3(256), 0, st, Xq, T, K,
-                       L.KB16, L.TB32, (uint4*)(w + L.xq));
+    SBN_LAUNCH("prep_xq", prep_xq_kernel, dim3((unsigned)((L.KB16 / 8) * L.TB32)), dim3(256), 0, st, Xq, T, K,
+               L.KB16, L.TB32, (uint4*)(w + L.xq));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 grid((unsigned)cdiv(R, 256), (unsigned)cdiv(K, 256));
     SBN_LAUNCH("gemm_dw", (bf16_gemm_kernel<1, 1>), grid, dim3(512), 0, st, w + L.xq, w + L.uhi,
