@@ -44,17 +44,6 @@ namespace {
 
 constexpr int GT = 256;
 
-// read nbits (<= 32) of a little-endian bitstream starting at bit `off`
-__device__ inline uint32_t read_bits(const uint8_t* p, int64_t off, int nbits) {
-  const uint8_t* q = p + (off >> 3);
-  const int s = (int)(off & 7);
-  unsigned long long v = 0;
-  const int nb = (s + nbits + 7) >> 3;
-  for (int i = 0; i < nb; ++i) v |= (unsigned long long)q[i] << (8 * i);
-  v >>= s;
-  return nbits == 32 ? (uint32_t)v : (uint32_t)(v & ((1ull << nbits) - 1));
-}
-
 __device__ inline int8_t code_to_i8(uint32_t c) { return c == 1u ? (int8_t)1 : c == 3u ? (int8_t)-1 : (int8_t)0; }
 
 // ---------------------------------------------------------------- expansion: sparse operand
@@ -64,7 +53,8 @@ __device__ inline int8_t code_to_i8(uint32_t c) { return c == 1u ? (int8_t)1 : c
 // word q, so a thread's four index words are one 16-byte store)
 __global__ __launch_bounds__(256) void expand_sparse_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, int64_t R, int64_t K,
-    int n, int m, int64_t RB, int64_t KBn, uint8_t* __restrict__ vals, uint32_t* __restrict__ idx) {
+    int n, int m, int64_t RB, int64_t KBn, int64_t cplane, uint8_t* __restrict__ vals,
+    uint32_t* __restrict__ idx) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= (RB / 4) * KBn * 64) return;
   const int l = (int)(gid & 63);
@@ -86,40 +76,37 @@ __global__ __launch_bounds__(256) void expand_sparse_kernel(
       decode24(mb, cb, a, ixi);
       ix = (uint32_t)ixi;
     } else if (r < R && k0 < K) {
+      // 1:4, 1:8, 2:8: at most two survivors per half-group of four positions.
+      // The 32 meta bits and the (<= 16) code bits of these positions come from
+      // aligned words; each half-group's survivors take the next codes in order.
       const uint32_t mb = *(const uint32_t*)(meta + r * (K / 8) + k0 / 8);
-      const int64_t crow = K * n / (4 * m);
-      const int64_t gbase = k0 / m;             // groups before k0 in this row
-      const int ngroups = 32 / m;
-      const uint32_t cb = read_bits(codes + r * crow, 2 * n * gbase, 2 * n * ngroups);
+      const int64_t crow = K * n / (4 * m);                 // code bytes per row
+      const int64_t cbit = r * crow * 8 + (k0 / m) * 2 * n; // first code bit of these positions
+      const int64_t a0 = (cbit >> 3) & ~(int64_t)3;
+      const int sh = (int)(cbit - a0 * 8);
+      const int64_t lastw = cplane - 4;
+      const uint32_t w0 = *(const uint32_t*)(codes + (a0 < lastw ? a0 : lastw));
+      const uint32_t w1 = *(const uint32_t*)(codes + (a0 + 4 < lastw ? a0 + 4 : lastw));
+      uint32_t cb = (uint32_t)((((unsigned long long)w1 << 32) | w0) >> sh);
       uint32_t v32[4] = {0, 0, 0, 0};
       ix = 0;
-      int cur = 0;                              // codes consumed so far in this range
 #pragma unroll
       for (int h = 0; h < 8; ++h) {             // eight halves of four positions
-        int cnt = 0;
-        uint32_t pos[2] = {0, 1};
-        int8_t val[2] = {0, 0};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int pp = 4 * h + p;
-          if ((mb >> pp) & 1u) {
-            const uint32_t c = (cb >> (2 * cur)) & 3u;
-            ++cur;
-            if (cnt < 2) {
-              pos[cnt] = (uint32_t)p;
-              val[cnt] = code_to_i8(c);
-            }
-            ++cnt;
-          }
+        const uint32_t nib = (mb >> (4 * h)) & 15u;
+        const int cnt = __builtin_popcount(nib);
+        const uint32_t p0 = nib ? (uint32_t)__builtin_ctz(nib) : 0u, p1 = nib ? 31u - (uint32_t)__builtin_clz(nib) : 1u;
+        const uint32_t v0 = cnt >= 1 ? (uint32_t)(uint8_t)code_to_i8(cb & 3u) : 0u;
+        const uint32_t v1 = cnt == 2 ? (uint32_t)(uint8_t)code_to_i8((cb >> 2) & 3u) : 0u;
+        cb >>= 2 * cnt;
+        // slots (2h, 2h + 1): distinct, ordered positions; a lone survivor at 3 goes second
+        uint32_t i0 = p0, i1 = p1, b0 = v0, b1 = v1;
+        if (cnt == 0) { i0 = 0; i1 = 1; }
+        if (cnt == 1) {
+          if (p0 == 3) { i0 = 0; i1 = 3; b0 = 0; b1 = v0; }
+          else { i1 = 3; b1 = 0; }
         }
-        if (cnt == 1) {                         // keep the two indices distinct and ordered
-          if (pos[0] == 3) { pos[1] = 3; val[1] = val[0]; pos[0] = 0; val[0] = 0; }
-          else { pos[1] = 3; val[1] = 0; }
-        }
-        ix |= (pos[0] | (pos[1] << 2)) << (4 * h);
-        const int j0 = 2 * h;
-        v32[j0 >> 2] |= (uint32_t)(uint8_t)val[0] << (8 * (j0 & 3));
-        v32[(j0 + 1) >> 2] |= (uint32_t)(uint8_t)val[1] << (8 * ((j0 + 1) & 3));
+        ix |= (i0 | (i1 << 2)) << (4 * h);
+        v32[h >> 1] |= (b0 | (b1 << 8)) << (16 * (h & 1));
       }
       a = (v4i){(int)v32[0], (int)v32[1], (int)v32[2], (int)v32[3]};
     }
@@ -480,8 +467,9 @@ hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
     uint8_t* vals = w;
     uint32_t* idx = (uint32_t*)(w + g.w_bytes);
     const int64_t threads = (RB / 4) * KBn * 64;
+    const int64_t cplane = round_up(R * (K * n / (4 * m)), 16);  // readable bytes of the codes plane
     SBN_LAUNCH("expand_sparse", expand_sparse_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st,
-               codes, meta, R, K, n, m, RB, KBn, vals, idx);
+               codes, meta, R, K, n, m, RB, KBn, cplane, vals, idx);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_gemm_t<true>(vals, (const uint8_t*)idx, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
