@@ -200,11 +200,6 @@ constexpr int GV_RING = SBN_GV_RING;
 #ifndef SBN_GV_STREAM
 #define SBN_GV_STREAM 1
 #endif
-#ifndef SBN_GV_BPC
-#define SBN_GV_BPC 3
-#endif
-constexpr int GV_BPC = SBN_GV_BPC;                   // resident blocks per CU
-constexpr int GV_STREAM_BLOCKS = 256 * GV_BPC;
 
 // The weights of one streamed launch (kernel argument, by value).
 struct GemvBatch {
@@ -297,7 +292,7 @@ struct StreamOut {
 // eight rows touch eight different banks, and each 1 KB load instruction
 // still reads whole 128-byte row segments.
 struct Dec24 {
-  static constexpr int SLOT = 4096, NDMA = 4, LUT = 0;
+  static constexpr int SLOT = 4096, NDMA = 4, LUT = 0, BPC = 4;   // BPC: resident blocks per CU (40 KB LDS each)
   int rowq[2], colq[2];
   v4i blo[8], bhi[8];
   __device__ inline void init(int wave, int lane) {
@@ -384,7 +379,7 @@ __device__ inline v4i lut68_entry(uint32_t mb) {
 }
 
 struct Dec68 {
-  static constexpr int SLOT = 2048 + 3072, NDMA = 5, LUT = 4096;
+  static constexpr int SLOT = 2048 + 3072, NDMA = 5, LUT = 4096, BPC = 3;   // 52 KB LDS per block
   int rowA[5], colA[5];
   v4i bx[16];
   __device__ inline void init(int wave, int lane) {
@@ -457,7 +452,7 @@ struct Dec68 {
 
 // One launch over `count` weights of R rows each: global row group q = w * nrg + lr.
 template <int OUT, typename Dec>
-__global__ __launch_bounds__(256, GV_BPC) void gemv_stream_kernel(
+__global__ __launch_bounds__(256, Dec::BPC) void gemv_stream_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K, const GemvBatch P,
     int count, int64_t R, int64_t ldy) {
   // one LDS array: [4 waves][GV_RING][SLOT] ring, the decode table, red[2][4][256]
@@ -699,7 +694,8 @@ template <typename Dec>
 hipError_t launch_stream(const char* name, const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                          const GemvBatch& P, int count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
   const int64_t total = cdiv(R, 16) * count;
-  const dim3 grid((unsigned)(total < GV_STREAM_BLOCKS ? total : GV_STREAM_BLOCKS)), block(256);
+  const int64_t blocks = 256 * Dec::BPC;   // one wave of resident blocks over the 256 CUs
+  const dim3 grid((unsigned)(total < blocks ? total : blocks)), block(256);
   if (ydt == SBN_I32_ACC)
     SBN_LAUNCH(name, (gemv_stream_kernel<0, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
   else if (ydt == SBN_F32)
