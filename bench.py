@@ -1,6 +1,6 @@
 """Throughput of the Sparse-BitLinear hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|train|sweep|decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|train|sweep|decode|speedup]
 
 A step is one pass of the hot path over one batch of synthetic input already
 resident in HBM:
@@ -15,6 +15,13 @@ resident in HBM:
   decode:            decode GEMV (T=1, R=K=4096) over pools of 128 distinct
                      packed weights per ratio (2:4 and 6:8), as batched calls
                      of 64 weights; `value` is GB/s of algorithmic bytes.
+  speedup:           sparse against dense at several token counts: the
+                     library's 2:4 and 6:8 calls against its own dense
+                     ternary (8:8) call and the vendor library's dense bf16
+                     and int8 GEMMs (hipBLASLt through torch), prefill shape
+                     R=6912, K=2560 at T = 512..8192 and decode shape
+                     R=K=4096 at T = 1, 4, 16 (pools above the Infinity
+                     Cache); `value` is the 2:4 call's TOPS at T=4096.
 `value` is dense-equivalent int8 TOPS of the whole step (2*T*R*K per
 forward product; the train step counts its three products), timed over
 --steps replays of the step captured as a HIP graph (the library only
@@ -61,7 +68,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "train", "sweep", "decode"])
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "train", "sweep", "decode", "speedup"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode GEMV measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -291,6 +298,149 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
     }
 
 
+# ---------------------------------------------------------------------- sparse vs dense
+SPEEDUP_T_PREFILL = (512, 1024, 2048, 4096, 8192)
+SPEEDUP_T_DECODE = (1, 4, 16)
+
+
+def graph_ms(fn, reps):
+    """Milliseconds per execution of fn (which only enqueues GPU work),
+    replayed from a HIP graph (eager launches if capture fails)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = capture_graph(fn)
+    run = g.replay if g is not None else fn
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def ternary_int8(W):
+    """Dense ternary int8 copy of bf16 W [R, K] (absmean scale, no mask): the
+    operand of the vendor int8 GEMM that the sparse calls are compared with."""
+    import torch
+    Wf = W.float()
+    s = Wf.abs().mean().clamp_min(1e-5)
+    return torch.clamp(torch.round(Wf / s), -1, 1).to(torch.int8)
+
+
+def speedup_tables(reps):
+    """Per-call times of the sparse 2:4 and 6:8 products against dense ones
+    over the same activations: the library's dense ternary 8:8 call, and
+    torch's bf16 matmul and int8 _int_mm (hipBLASLt).  Prefill: the prefill
+    shape at several T, one call per timing.  Decode: R = K = 4096 at T = 1, 4,
+    16, every weight of a pool of distinct weights at least twice the Infinity
+    Cache, as separate calls in one graph (the library's calls also batched, 64
+    weights per launch).  A product the vendor library refuses is null, with
+    its error."""
+    import torch
+    import sparse_linear_layers_02_amd as sbn
+    from workloads import WORKLOADS
+    out = {"prefill": [], "decode": []}
+    # prefill shape
+    wl = WORKLOADS["prefill"]
+    R, K = wl.R, wl.K
+    W = bf16_dev(wl.weights(0))
+    Xall = bf16_dev(wl.activations(0, T=max(SPEEDUP_T_PREFILL)))
+    packs = {(n, m): sbn.sbn_mask_ternarize_pack(W, n, m) for n, m in ((2, 4), (6, 8), (8, 8))}
+    Wq = ternary_int8(W)
+    WqT = Wq.t()
+
+    def vendor(fn):
+        try:
+            return graph_ms(fn, reps), None
+        except Exception as e:          # reported in the row
+            return None, f"{type(e).__name__}: {str(e).splitlines()[0][:160]}"
+
+    for T in SPEEDUP_T_PREFILL:
+        X = Xall[:T]
+        Xq, s_x = sbn.sbn_act_quant(X)
+        row = {"T": T, "R": R, "K": K}
+        ops = 2 * T * R * K
+        for (n, m), (codes, meta, s_w) in packs.items():
+            Y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty(max(sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM, T, R, K, n, m), 256), dtype=torch.uint8,
+                             device="cuda")
+            ms = graph_ms(lambda: sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, R, n, m, Y=Y, ws=ws), reps)
+            row[f"sbn_{n}{m}_us"] = round(ms * 1e3, 2)
+            del Y, ws
+        Yb = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
+        ms, err = vendor(lambda: torch.matmul(X, W.t(), out=Yb))
+        row["bf16_us"], row["bf16_error"] = (round(ms * 1e3, 2) if ms else None), err
+        Yi = torch.empty((T, R), dtype=torch.int32, device="cuda")
+        ms, err = vendor(lambda: torch._int_mm(Xq, WqT, out=Yi))
+        row["int8_us"], row["int8_error"] = (round(ms * 1e3, 2) if ms else None), err
+        del Yb, Yi
+        for key in ("sbn_24", "sbn_68"):
+            t = row[key + "_us"]
+            row[key + "_TOPS"] = round(ops / (t * 1e-6) / 1e12, 1)
+            row[key + "_vs_dense_ternary"] = round(row["sbn_88_us"] / t, 3)
+            row[key + "_vs_bf16"] = round(row["bf16_us"] / t, 3) if row["bf16_us"] else None
+            row[key + "_vs_int8"] = round(row["int8_us"] / t, 3) if row["int8_us"] else None
+        out["prefill"].append({k: v for k, v in row.items() if v is not None or not k.endswith("_error")})
+    del W, Xall, packs, Wq, WqT
+    torch.cuda.empty_cache()
+
+    # decode shape, pools above the Infinity Cache
+    wl = WORKLOADS["decode"]
+    R, K = wl.R, wl.K
+    W = bf16_dev(wl.weights(0))
+    pools = {}
+    for n, m in ((2, 4), (6, 8), (8, 8)):
+        codes0, meta0, s_w0 = sbn.sbn_mask_ternarize_pack(W, n, m)
+        cb, mb = sbn.sbn_packed_bytes(R, K, n, m)
+        P = -(-2 * MALL_BYTES // (cb + mb))
+        pools[(n, m)] = dict(P=P, codes=[codes0.clone() for _ in range(P)],
+                             metas=[(meta0.clone() if meta0 is not None else None) for _ in range(P)],
+                             s_ws=[s_w0.clone() for _ in range(P)])
+        del codes0, meta0
+    Pb = -(-2 * MALL_BYTES // (2 * R * K))
+    Wb = [W.clone() for _ in range(Pb)]
+    Pi = -(-2 * MALL_BYTES // (R * K))
+    Wi = [ternary_int8(W).t() for _ in range(Pi)]
+    del W
+    for T in SPEEDUP_T_DECODE:
+        X = bf16_dev(wl.activations(0, T=T))
+        Xq, s_x = sbn.sbn_act_quant(X)
+        row = {"T": T, "R": R, "K": K}
+        for (n, m), p in pools.items():
+            P = p["P"]
+            Ys = [torch.empty((T, R), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+            ws = torch.empty(max(sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMV, T, R, K, n, m), 256), dtype=torch.uint8,
+                             device="cuda")
+            ms = graph_ms(lambda: [sbn.sbn_sparse_ternary_gemv(Xq, s_x, p["codes"][i], p["metas"][i], p["s_ws"][i],
+                                                                R, n, m, Y=Ys[i], ws=ws) for i in range(P)], reps)
+            row[f"sbn_{n}{m}_us"] = round(ms * 1e3 / P, 3)
+            if (n, m) != (8, 8):
+                ms = graph_ms(lambda: [sbn.sbn_sparse_ternary_gemv_batched(
+                    Xq, s_x, p["codes"][b:b + BATCH], p["metas"][b:b + BATCH], p["s_ws"][b:b + BATCH], R, n, m,
+                    Ys=Ys[b:b + BATCH]) for b in range(0, P, BATCH)], reps)
+                row[f"sbn_{n}{m}_batched_us"] = round(ms * 1e3 / P, 3)
+            del Ys, ws
+        Yb = [torch.empty((T, R), dtype=torch.bfloat16, device="cuda") for _ in range(Pb)]
+        ms, err = vendor(lambda: [torch.matmul(X, Wb[i].t(), out=Yb[i]) for i in range(Pb)])
+        row["bf16_us"], row["bf16_error"] = (round(ms * 1e3 / Pb, 3) if ms else None), err
+        Yi = [torch.empty((T, R), dtype=torch.int32, device="cuda") for _ in range(Pi)]
+        ms, err = vendor(lambda: [torch._int_mm(Xq, Wi[i], out=Yi[i]) for i in range(Pi)])
+        row["int8_us"], row["int8_error"] = (round(ms * 1e3 / Pi, 3) if ms else None), err
+        del Yb, Yi
+        for key in ("sbn_24", "sbn_68", "sbn_24_batched", "sbn_68_batched"):
+            t = row[key + "_us"]
+            row[key + "_vs_dense_ternary"] = round(row["sbn_88_us"] / t, 3)
+            row[key + "_vs_bf16"] = round(row["bf16_us"] / t, 3) if row["bf16_us"] else None
+            row[key + "_vs_int8"] = round(row["int8_us"] / t, 3) if row["int8_us"] else None
+        row["pool_weights"] = {f"{n}:{m}": p["P"] for (n, m), p in pools.items()} | {"bf16": Pb, "int8": Pi}
+        out["decode"].append({k: v for k, v in row.items() if v is not None or not k.endswith("_error")})
+    return out
+
+
 # ---------------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl, n, m, tokens):
     """The oracle as it stands, on the host: pack the full W, quantize `tokens`
@@ -454,6 +604,16 @@ def main():
                         "note": "algorithmic bytes: packed planes + activations + scales + bf16 outputs of the "
                                 f"{BATCH} weights of one launch"}
         out["stages_us"] = {k: round(v[1] / v[0] * 1e3, 3) for k, v in sorted(prof.items()) if v[0]}
+    elif a.workload == "speedup":
+        tab = speedup_tables(a.steps)
+        r = next(r for r in tab["prefill"] if r["T"] == 4096)
+        out.update(value=r["sbn_24_TOPS"], unit="TOPS", ms_per_step=round(r["sbn_24_us"] * 1e-3, 4))
+        out["config"] = {"workload": "speedup", "prefill": {"R": 6912, "K": 2560, "T": list(SPEEDUP_T_PREFILL)},
+                         "decode": {"R": 4096, "K": 4096, "T": list(SPEEDUP_T_DECODE)},
+                         "step": "one library call per product (sparse 2:4, 6:8; dense ternary 8:8) against "
+                                 "torch bf16 matmul and int8 _int_mm"}
+        out["speedup"] = tab
+        out["roofline"] = None
     else:
         wl = WORKLOADS["sweep"]
         rows = []
@@ -485,10 +645,10 @@ def main():
                            "frac_of_sparse_peak": round(r24["TOPS_kernel"] / PEAK_INT8_SPARSE_TOPS, 4),
                            "note": "the 2:4 row"}
 
-    if not a.no_extras and a.workload != "decode":
+    if not a.no_extras and a.workload not in ("decode", "speedup"):
         out["decode_gemv"] = [decode_gemv(2, 4, 1), decode_gemv(6, 8, 1)]
 
-    if a.no_cpu_baseline:
+    if a.no_cpu_baseline or a.workload == "speedup":
         out["cpu_baseline"] = None
     elif a.workload == "decode":
         out["cpu_baseline"] = cpu_baseline_decode(WORKLOADS["decode"], weights=POOL)
