@@ -30,7 +30,14 @@ readings below (each is repeated at the function that uses it):
   * Y = s_w * s_x[t] * sum_k Xq[t,k] * Wt[r,k];
   * dual STE: identity Jacobians through both quantizers and a dense
     gradient through the mask, so grad_X = dY @ (s_w*Wt) and
-    grad_W = dY^T @ (s_x*Xq) covering every (r, k).
+    grad_W = dY^T @ (s_x*Xq) covering every (r, k);
+  * the two ablation variants ([de] §4 "Ablationsstudien", [fr] §5): the
+    mask taken from |q| of the ternary weights (ties to the lower index),
+    and grad_W blocked at pruned positions (grad_W * mask);
+  * the master-weight optimizer step ([ja] §2.1: BF16 master weights are
+    kept and receive the gradients; no optimizer is named): plain SGD,
+    w' = bf16(fl32(w - lr*g)) with fl32 one rounding of the exact value
+    (a float32 fused multiply-add) and bf16 round-half-to-even.
 
 Tensor conventions: bf16 inputs are ``uint16`` bit patterns, row-major.
 W is [R, K] (R output features, K input features), X is [T, K], Y is [T, R].
@@ -57,7 +64,8 @@ __all__ = [
     "bf16_to_f64", "bf16_to_f32", "nm_mask", "absmean_exact", "round_to_f32",
     "weight_scale", "ternary_codes", "quant_then_mask", "packed_bytes",
     "pack_sbn1", "act_quant", "accumulate", "output", "backward",
-    "forward", "S_FLOOR", "QMAX",
+    "forward", "S_FLOOR", "QMAX", "nm_mask_ternary", "fma_f32", "f32_to_bf16_rne",
+    "sgd_update",
 ]
 
 
@@ -96,6 +104,28 @@ def nm_mask(W_bits: np.ndarray, n: int, m: int) -> np.ndarray:
     mag = np.abs(bf16_to_f64(W_bits)).reshape(R, K // m, m)
     order = np.argsort(-mag, axis=-1, kind="stable")      # stable: ties keep index order
     keep = np.zeros(mag.shape, dtype=bool)
+    np.put_along_axis(keep, order[..., :n], True, axis=-1)
+    return keep.reshape(R, K)
+
+
+def nm_mask_ternary(W_bits: np.ndarray, s_w: np.float32, n: int, m: int) -> np.ndarray:
+    """Ablation variant of the mask: the N largest |q| of the TERNARY weights.
+
+    [de] §4 ("Ablationsstudien") and [fr] §5 report that building the mask
+    from the quantized ternary weights instead of the master weights makes
+    training unstable; this is that variant, kept for the comparison.
+    |q| is 0 or 1, so most groups hold ties; as in nm_mask, equal keys go
+    to the lower index.  q = RoundClip(w / s_w, -1, 1) with the tensor's
+    scale s_w (ternary_codes).
+
+    Definition: stable sort each group by |q| descending and keep the first N.
+    """
+    _check_finite(W_bits)
+    R, K = W_bits.shape
+    assert K % m == 0 and 1 <= n <= m
+    key = np.abs(ternary_codes(W_bits, s_w).astype(np.int64)).reshape(R, K // m, m)
+    order = np.argsort(-key, axis=-1, kind="stable")
+    keep = np.zeros(key.shape, dtype=bool)
     np.put_along_axis(keep, order[..., :n], True, axis=-1)
     return keep.reshape(R, K)
 
@@ -170,17 +200,23 @@ def ternary_codes(W_bits: np.ndarray, s_w: np.float32) -> np.ndarray:
     return t.astype(np.int8)
 
 
-def quant_then_mask(W_bits: np.ndarray, n: int, m: int):
+def quant_then_mask(W_bits: np.ndarray, n: int, m: int, mask_from: str = "master"):
     """Effective ternary weight W_t = mask (.) Q(W), plus the mask and s_w.
 
     [ja] §2.1 / [de] §2 / [ko] §2.1 / [fr] §2: quantize first, then apply
     the mask, so the discrete weights used at inference carry the N:M
-    structure.  Returns (codes int8 [R,K] with pruned entries 0, mask bool
-    [R,K], s_w float32).
+    structure.  mask_from = "master" (the method) or "ternary" (the ablation
+    variant, nm_mask_ternary).  Returns (codes int8 [R,K] with pruned
+    entries 0, mask bool [R,K], s_w float32).
     """
     s_w = weight_scale(W_bits)
     q = ternary_codes(W_bits, s_w)
-    mask = nm_mask(W_bits, n, m)
+    if mask_from == "master":
+        mask = nm_mask(W_bits, n, m)
+    elif mask_from == "ternary":
+        mask = nm_mask_ternary(W_bits, s_w, n, m)
+    else:
+        raise ValueError(mask_from)
     return np.where(mask, q, 0).astype(np.int8), mask, s_w
 
 
@@ -253,7 +289,7 @@ def output(acc: np.ndarray, s_w: np.float32, s_x: np.ndarray) -> np.ndarray:
 
 
 def backward(dY_bits: np.ndarray, Xq: np.ndarray, s_x: np.ndarray,
-             codes: np.ndarray, s_w: np.float32):
+             codes: np.ndarray, s_w: np.float32, grad_mask: np.ndarray | None = None):
     """Dual-STE backward.  Returns (grad_X [T,K], grad_W [R,K]) in float64.
 
     [ja] §2.1, [de] §2, [ko] §2.2, [fr] §2: straight-through estimators
@@ -262,11 +298,80 @@ def backward(dY_bits: np.ndarray, Xq: np.ndarray, s_x: np.ndarray,
       grad_X = dY @ (s_w * Wt)        (through the sparse ternary weight)
       grad_W = dY^T @ (s_x * Xq)      (every (r, k), masked or not)
     No term for the derivative of s_w or s_x is taken.
+
+    grad_mask (bool [R,K]) selects the ablation variant of [de] §4
+    ("Ablationsstudien") and [fr] §5, gradients blocked for pruned weights:
+    grad_W is multiplied by the mask.
     """
     dY = bf16_to_f64(dY_bits)
     W_eff = np.float64(s_w) * codes.astype(np.float64)
     X_hat = s_x.astype(np.float64)[:, None] * Xq.astype(np.float64)
-    return dY @ W_eff, dY.T @ X_hat
+    gW = dY.T @ X_hat
+    if grad_mask is not None:
+        gW = np.where(grad_mask, gW, 0.0)
+    return dY @ W_eff, gW
+
+
+# --------------------------------------------------------------------------- optimizer step
+def fma_f32(a, b, c) -> np.ndarray:
+    """fl32(a*b + c) for float32 inputs: the exact value rounded ONCE to
+    float32, nearest, ties to even (an IEEE fused multiply-add).
+
+    The product of two float32 values is exact in float64; the sum is formed
+    in float64 together with its exact rounding error (Knuth's two-sum), so
+    the float64 sum s and error e satisfy s + e = a*b + c exactly.  Rounding
+    s to float32 is then the correct result unless s lies exactly halfway
+    between two float32 values while e is not zero; in that case the exact
+    value is on the side of e.  Results outside the float32 range are an
+    error (the operator's inputs are finite).
+    """
+    a64 = np.asarray(a, dtype=np.float32).astype(np.float64)
+    b64 = np.asarray(b, dtype=np.float32).astype(np.float64)
+    c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
+    p = a64 * b64                                   # exact: 48 significant bits
+    s = p + c64
+    bv = s - p
+    e = (p - (s - bv)) + (c64 - bv)                 # s + e == p + c exactly
+    with np.errstate(over="ignore"):
+        f = s.astype(np.float32)
+    if not np.all(np.isfinite(f)):
+        raise ValueError("float32 overflow in the update")
+    # the float32 neighbour of f on the side of s, and the midpoint between them
+    toward = np.where(s > f.astype(np.float64), np.float32(np.inf), np.float32(-np.inf)).astype(np.float32)
+    nb = np.nextafter(f, toward)
+    mid = (f.astype(np.float64) + nb.astype(np.float64)) * 0.5   # exact in float64
+    fix = (s != f.astype(np.float64)) & (s == mid) & (e != 0)
+    up = np.maximum(f, nb)
+    lo = np.minimum(f, nb)
+    return np.where(fix, np.where(e > 0, up, lo), f).astype(np.float32)
+
+
+def f32_to_bf16_rne(x) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest, ties to even."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    if np.any((r & 0x7F80) == 0x7F80):
+        raise ValueError("bf16 overflow in the update")
+    return r
+
+
+def sgd_update(W_bits: np.ndarray, G: np.ndarray, lr) -> np.ndarray:
+    """One SGD step on the BF16 master weights.  Returns the new bf16 bits.
+
+    [ja] §2.1: BF16 master weights are kept during optimization and receive
+    the (dense, dual-STE) gradients; [ja] §2.1 and [ko] §2.2: the mask is
+    recomputed from the updated master weights at every step.  The pages
+    name no optimizer; plain SGD is taken:
+        w' = bf16(fl32(w - lr * g))
+    with lr and g in float32, fl32 one rounding of the exact value (a fused
+    multiply-add) and bf16 round-half-to-even.
+    """
+    _check_finite(W_bits)
+    w = bf16_to_f32(W_bits)
+    g = np.asarray(G, dtype=np.float32)
+    assert g.shape == w.shape and np.all(np.isfinite(g))
+    return f32_to_bf16_rne(fma_f32(-np.float32(lr), g, w))
 
 
 def forward(W_bits: np.ndarray, X_bits: np.ndarray, n: int, m: int) -> dict:

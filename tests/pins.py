@@ -189,9 +189,11 @@ def act_quant_matches_exact(X, Xq, s_x) -> bool:
 
 
 # ------------------------------------------------------------------ backward
-def backward_by_autograd(W, X, dY, codes, s_w, Xq, s_x):
+def backward_by_autograd(W, X, dY, codes, s_w, Xq, s_x, block_mask=None):
     """torch float64 autograd of the straight-through formulation
-    w_eff = w + (s_w*Wt - w).detach(), x_hat = x + (s_x*Xq - x).detach()."""
+    w_eff = w + (s_w*Wt - w).detach(), x_hat = x + (s_x*Xq - x).detach().
+    With block_mask (the blocked-gradient ablation) the weight path is
+    w_eff = M * (w + (s_w*Wt - w).detach()): pruned weights get no gradient."""
     import torch
 
     def f64(bits):
@@ -203,7 +205,78 @@ def backward_by_autograd(W, X, dY, codes, s_w, Xq, s_x):
     w_q = float(s_w) * torch.from_numpy(codes.astype(np.float64))
     x_q = torch.from_numpy(s_x.astype(np.float64))[:, None] * torch.from_numpy(Xq.astype(np.float64))
     w_eff = w + (w_q - w).detach()
+    if block_mask is not None:
+        w_eff = torch.from_numpy(np.asarray(block_mask, dtype=np.float64)) * w_eff
     x_hat = x + (x_q - x).detach()
     y = x_hat @ w_eff.T
     y.backward(f64(dY))
     return x.grad.numpy(), w.grad.numpy()
+
+
+# ------------------------------------------------------------------ ablation: mask from ternary weights
+def mask_ternary_matches_bruteforce(mask_fn, W, s_w, n, m) -> bool:
+    """Kept set per group = the lexicographically smallest n-subset among
+    those of maximal sum of |q|, q the exact RoundClip(w / s_w) (|q| = 1 iff
+    |w| / s_w > 1/2, computed with rationals)."""
+    R, K = W.shape
+    got = mask_fn(W, s_w, n, m)
+    s = _f32_value(s_w)
+    for r in range(R):
+        for g0 in range(0, K, m):
+            qs = [1 if abs(_bf16_value(int(W[r, g0 + p])) / s) > Fraction(1, 2) else 0 for p in range(m)]
+            best = None
+            for comb in itertools.combinations(range(m), n):
+                t = sum(qs[p] for p in comb)
+                if best is None or t > best[0] or (t == best[0] and comb < best[1]):
+                    best = (t, comb)
+            kept = tuple(p for p in range(m) if got[r, g0 + p])
+            if kept != best[1]:
+                return False
+    return True
+
+
+# ------------------------------------------------------------------ optimizer step
+def round_binary(q: Fraction, p: int, emin: int = -126) -> Fraction:
+    """Nearest number with a p-bit significand (ties to even significand),
+    gradual underflow below 2^emin, for the rational q (no overflow check)."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    ulp = Fraction(2) ** (max(e, emin) - (p - 1))
+    k = a / ulp
+    f = k.numerator // k.denominator
+    rem = k - f
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and f % 2 == 1):
+        f += 1
+    return sign * f * ulp
+
+
+def fma_matches_exact(fma_fn, a, b, c) -> bool:
+    """fma_fn(a, b, c) equals the float32 nearest (ties to even) to the exact a*b + c."""
+    got = np.asarray(fma_fn(a, b, c), dtype=np.float32).reshape(-1)
+    A, B, C = (np.asarray(v, dtype=np.float32).reshape(-1) for v in (a, b, c))
+    A, B, C = np.broadcast_arrays(A, B, C)
+    for i in range(got.size):
+        exact = _f32_value(A[i]) * _f32_value(B[i]) + _f32_value(C[i])
+        if Fraction(float(got[i])) != round_binary(exact, 24):
+            return False
+    return True
+
+
+def sgd_matches_exact(sgd_fn, W, G, lr) -> bool:
+    """New weight = bf16 nearest (ties even) of the float32 nearest (ties even)
+    of the exact w - lr * g, compared as exact values."""
+    got = np.asarray(sgd_fn(W, G, lr), dtype=np.uint16)
+    lrv = _f32_value(lr)
+    for idx in np.ndindex(W.shape):
+        exact = _bf16_value(int(W[idx])) - lrv * _f32_value(G[idx])
+        want = round_binary(round_binary(exact, 24), 8)
+        if _bf16_value(int(got[idx])) != want:
+            return False
+    return True

@@ -185,3 +185,99 @@ def test_backward_mutants_are_caught(mutant):
     gX, gW = mutant(dY, f["Xq"], f["s_x"], f["codes"], f["s_w"])
     rX, rW = pins.backward_by_autograd(W, X, dY, f["codes"], f["s_w"], f["Xq"], f["s_x"])
     assert not (np.allclose(gX, rX, rtol=1e-9) and np.allclose(gW, rW, rtol=1e-9))
+
+
+# ----------------------------------------------------------------- ablation variants
+def _mask_ternary_highest_index_ties(W, s_w, n, m):
+    R, K = W.shape
+    key = np.abs(O.ternary_codes(W, s_w).astype(np.int64)).reshape(R, K // m, m)[..., ::-1]
+    order = np.argsort(-key, axis=-1, kind="stable")[..., :n]
+    keep = np.zeros(key.shape, bool)
+    np.put_along_axis(keep, order, True, axis=-1)
+    return keep[..., ::-1].reshape(R, K)
+
+
+def _mask_ternary_uses_master(W, s_w, n, m):
+    return O.nm_mask(W, n, m)
+
+
+def _mask_ternary_half_scale(W, s_w, n, m):
+    return O.nm_mask_ternary(W, np.float32(s_w * 2), n, m)
+
+
+@pytest.mark.parametrize("mutant", [_mask_ternary_highest_index_ties, _mask_ternary_uses_master,
+                                    _mask_ternary_half_scale])
+def test_mask_ternary_mutants_are_caught(mutant):
+    W = gaussian_bf16((6, 64), 0.02, seed=11, stream=0)
+    s_w = O.weight_scale(W)
+    assert not all(pins.mask_ternary_matches_bruteforce(mutant, W, s_w, n, m) for n, m in ((2, 4), (6, 8)))
+
+
+def _bwd_blocked_by_codes(dY, Xq, s_x, codes, s_w, mask):
+    return O.backward(dY, Xq, s_x, codes, s_w, grad_mask=(codes != 0))
+
+
+def _bwd_blocked_not_applied(dY, Xq, s_x, codes, s_w, mask):
+    return O.backward(dY, Xq, s_x, codes, s_w)
+
+
+def _bwd_blocked_inverted(dY, Xq, s_x, codes, s_w, mask):
+    return O.backward(dY, Xq, s_x, codes, s_w, grad_mask=~mask)
+
+
+@pytest.mark.parametrize("mutant", [_bwd_blocked_by_codes, _bwd_blocked_not_applied, _bwd_blocked_inverted])
+def test_backward_blocked_mutants_are_caught(mutant):
+    W = gaussian_bf16((16, 64), 0.02, seed=13, stream=0)
+    X = gaussian_bf16((4, 64), 1.0, seed=13, stream=1)
+    dY = gaussian_bf16((4, 16), 1e-2, seed=13, stream=2)
+    f = O.forward(W, X, 6, 8)
+    gX, gW = mutant(dY, f["Xq"], f["s_x"], f["codes"], f["s_w"], f["mask"])
+    rX, rW = pins.backward_by_autograd(W, X, dY, f["codes"], f["s_w"], f["Xq"], f["s_x"], block_mask=f["mask"])
+    assert not (np.allclose(gX, rX, rtol=1e-9) and np.allclose(gW, rW, rtol=1e-9))
+
+
+# ----------------------------------------------------------------- optimizer step
+def _fma_double_rounding(a, b, c):
+    return (np.asarray(a, np.float32).astype(np.float64) * np.asarray(b, np.float32).astype(np.float64)
+            + np.asarray(c, np.float32).astype(np.float64)).astype(np.float32)
+
+
+def _fma_product_rounded(a, b, c):
+    p = (np.asarray(a, np.float32) * np.asarray(b, np.float32)).astype(np.float32)
+    return (p + np.asarray(c, np.float32)).astype(np.float32)
+
+
+@pytest.mark.parametrize("mutant", [_fma_double_rounding, _fma_product_rounded])
+def test_fma_mutants_are_caught(mutant):
+    lr = np.float32(2.0 ** -24 * (1 + 2896 * 2.0 ** -23))
+    g = np.float32(-(1 - 2895 * 2.0 ** -23))
+    cases = [(-lr, g, np.float32(1.0))]
+    # the float32 product rounds away information a fused operation keeps
+    # (1 + 2^-12)^2 - 1 = 2^-11 + 2^-24 is a float32; the float32 product loses the 2^-24
+    cases.append((np.float32(1 + 2.0 ** -12), np.float32(1 + 2.0 ** -12), np.float32(-1.0)))
+    assert not all(pins.fma_matches_exact(mutant, a, b, c) for a, b, c in cases)
+    assert all(pins.fma_matches_exact(O.fma_f32, a, b, c) for a, b, c in cases)
+
+
+def _sgd_plus(W, G, lr):
+    return O.f32_to_bf16_rne(O.fma_f32(np.float32(lr), G, O.bf16_to_f32(W)))
+
+
+def _sgd_truncate(W, G, lr):
+    v = O.fma_f32(-np.float32(lr), G, O.bf16_to_f32(W))
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _sgd_round_half_up(W, G, lr):
+    v = O.fma_f32(-np.float32(lr), G, O.bf16_to_f32(W)).view(np.uint32).astype(np.uint64)
+    return ((v + 0x8000) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("mutant", [_sgd_plus, _sgd_truncate, _sgd_round_half_up])
+def test_sgd_mutants_are_caught(mutant):
+    W = gaussian_bf16((8, 40), 0.02, seed=14, stream=0)
+    G = np.random.default_rng([14, 5]).standard_normal((8, 40)).astype(np.float32) * np.float32(1e-2)
+    # plus an exact tie in the bf16 rounding: 1 + 2^-8 lands halfway between bf16 neighbours
+    W = np.concatenate([W, f32_to_bf16_bits(np.full((1, 40), 1.0, np.float32))], axis=0)
+    G = np.concatenate([G, np.full((1, 40), -2.0 ** -8, np.float32)], axis=0)
+    assert not pins.sgd_matches_exact(mutant, W, G, np.float32(1.0))

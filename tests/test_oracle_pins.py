@@ -286,3 +286,100 @@ def test_backward_matches_torch_autograd_ste(n, m):
     # dense gradient through the mask: pruned positions receive gradient
     mask = f["mask"]
     assert np.abs(gW[~mask]).sum() > 0
+
+
+# ----------------------------------------------------------------- ablation: mask from ternary weights
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (3, 4), (2, 8), (4, 8), (6, 8)])
+def test_mask_ternary_matches_bruteforce(n, m):
+    W = gaussian_bf16((6, 64), 0.02, seed=11, stream=0)
+    s_w = O.weight_scale(W)
+    assert pins.mask_ternary_matches_bruteforce(O.nm_mask_ternary, W, s_w, n, m)
+
+
+def test_mask_ternary_worked_group():
+    # s_w = 1: |q| = 1 iff |w| > 0.5.  Group [0.25, -0.75, 0.5, 1.0, 0.125, -2, 0, 0.75]
+    # has |q| = [0, 1, 0, 1, 0, 1, 0, 1]: 2:8 keeps positions 1 and 3 (first two
+    # nonzeros), 6:8 keeps the four nonzeros and the two lowest zeros (0, 2).
+    W = f32_to_bf16_bits(np.array([[0.25, -0.75, 0.5, 1.0, 0.125, -2.0, 0.0, 0.75]], dtype=np.float32))
+    one = np.float32(1.0)
+    assert np.nonzero(O.nm_mask_ternary(W, one, 2, 8)[0])[0].tolist() == [1, 3]
+    assert np.nonzero(O.nm_mask_ternary(W, one, 6, 8)[0])[0].tolist() == [0, 1, 2, 3, 5, 7]
+    # the master-weight mask of the same group differs: 2:8 keeps -2 and 1.0
+    assert np.nonzero(O.nm_mask(W, 2, 8)[0])[0].tolist() == [3, 5]
+
+
+def test_quant_then_mask_ternary_variant_keeps_every_nonzero_when_room():
+    # at 6:8 a group with at most six nonzero |q| keeps all of them
+    W = gaussian_bf16((8, 64), 0.02, seed=12, stream=0)
+    codes, mask, s_w = O.quant_then_mask(W, 6, 8, mask_from="ternary")
+    q = O.ternary_codes(W, s_w)
+    nz = (q != 0).reshape(8, 8, 8).sum(-1)
+    lost = ((q != 0) & ~mask).reshape(8, 8, 8).sum(-1)
+    assert (lost[nz <= 6] == 0).all() and (mask.reshape(8, 8, 8).sum(-1) == 6).all()
+    assert np.array_equal(codes, np.where(mask, q, 0))
+
+
+# ----------------------------------------------------------------- ablation: blocked gradient
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
+def test_backward_blocked_matches_torch_autograd(n, m):
+    W = gaussian_bf16((24, 64), 0.02, seed=13, stream=0)
+    X = gaussian_bf16((5, 64), 1.0, seed=13, stream=1)
+    dY = gaussian_bf16((5, 24), 1e-2, seed=13, stream=2)
+    f = O.forward(W, X, n, m)
+    gX, gW = O.backward(dY, f["Xq"], f["s_x"], f["codes"], f["s_w"], grad_mask=f["mask"])
+    rX, rW = pins.backward_by_autograd(W, X, dY, f["codes"], f["s_w"], f["Xq"], f["s_x"], block_mask=f["mask"])
+    assert np.allclose(gX, rX, rtol=1e-12, atol=1e-15)
+    assert np.allclose(gW, rW, rtol=1e-12, atol=1e-15)
+    assert (gW[~f["mask"]] == 0).all() and np.abs(gW[f["mask"]]).sum() > 0
+
+
+# ----------------------------------------------------------------- optimizer step
+def test_fma_f32_single_rounding_case():
+    # w - lr*g = 1 + 2^-24 + 4688 * 2^-70: float64 rounds the sum onto the
+    # float32 midpoint 1 + 2^-24 (a tie that goes to 1.0); the exact value is
+    # above it, so the fused result is 1 + 2^-23.
+    lr = np.float32(2.0 ** -24 * (1 + 2896 * 2.0 ** -23))
+    g = np.float32(-(1 - 2895 * 2.0 ** -23))
+    got = O.fma_f32(-lr, g, np.float32(1.0))
+    assert float(got) == 1 + 2.0 ** -23
+    assert pins.fma_matches_exact(O.fma_f32, -lr, g, np.float32(1.0))
+
+
+def test_fma_f32_random_and_special():
+    r = np.random.default_rng([21, 0])
+    a = r.standard_normal(400).astype(np.float32) * np.float32(1e-3)
+    b = r.standard_normal(400).astype(np.float32)
+    c = f32_to_bf16_bits(r.standard_normal(400).astype(np.float32) * np.float32(0.02))
+    c = bf16_bits_to_f32(c)
+    assert pins.fma_matches_exact(O.fma_f32, a, b, c)
+    # exact cases, zeros, and a subnormal result
+    sa = np.array([0.5, 0.0, 1.0, 2.0 ** -70, -3.0], dtype=np.float32)
+    sb = np.array([2.0, 5.0, -1.0, 2.0 ** -70, 0.0], dtype=np.float32)
+    sc = np.array([0.0, -7.0, 1.0, 0.0, 0.0], dtype=np.float32)
+    assert pins.fma_matches_exact(O.fma_f32, sa, sb, sc)
+    assert O.fma_f32(sa, sb, sc).tolist()[:3] == [1.0, -7.0, 0.0]
+
+
+def test_f32_to_bf16_rne_ties_and_examples():
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, -1.5, 0.0], dtype=np.float32)
+    got = O.f32_to_bf16_rne(x)
+    # 1 + 2^-8 is a tie -> even (1.0); 1 + 3*2^-8 is a tie -> even (1 + 2^-6); just above a tie rounds up
+    assert got.tolist() == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xBFC0, 0x0000]
+
+
+def test_sgd_update_matches_exact():
+    W = gaussian_bf16((8, 40), 0.02, seed=14, stream=0)
+    G = np.random.default_rng([14, 5]).standard_normal((8, 40)).astype(np.float32) * np.float32(1e-2)
+    for lr in (np.float32(0.1), np.float32(3e-4), np.float32(1.0)):
+        assert pins.sgd_matches_exact(O.sgd_update, W, G, lr)
+
+
+def test_sgd_update_identities():
+    W = gaussian_bf16((4, 64), 0.02, seed=15, stream=0)
+    G = np.random.default_rng([15, 5]).standard_normal((4, 64)).astype(np.float32)
+    assert np.array_equal(O.sgd_update(W, G, np.float32(0.0)), W)           # lr = 0
+    assert np.array_equal(O.sgd_update(W, np.zeros_like(G), np.float32(0.5)), W)
+    # w = 1, lr = 0.5, g = 1 -> 0.5 exactly; g = -2 -> 2.0
+    one = f32_to_bf16_bits(np.array([[1.0, 1.0]], dtype=np.float32))
+    out = O.sgd_update(one, np.array([[1.0, -2.0]], dtype=np.float32), np.float32(0.5))
+    assert bf16_bits_to_f32(out).tolist() == [[0.5, 2.0]]
