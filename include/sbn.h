@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SBN_ABI_VERSION 1
+#define SBN_ABI_VERSION 2
 
 typedef enum sbn_status {
   SBN_OK = 0,
@@ -65,7 +65,9 @@ typedef enum sbn_status {
   SBN_ERR_ALIGN = 4,           /* pointer not 16-byte aligned or ld not a multiple of 8 */
   SBN_ERR_WORKSPACE = 5,       /* ws_bytes smaller than sbn_workspace_bytes() */
   SBN_ERR_DTYPE = 6,           /* output dtype not allowed for this call */
-  SBN_ERR_HIP = 7              /* a HIP launch or runtime call failed */
+  SBN_ERR_HIP = 7,             /* a HIP launch or runtime call failed */
+  SBN_ERR_FLAGS = 8,           /* a flag bit this call does not accept */
+  SBN_ERR_VALUE = 9            /* a scalar argument out of range (e.g. a non-finite lr) */
 } sbn_status;
 
 typedef enum sbn_dtype {
@@ -73,6 +75,25 @@ typedef enum sbn_dtype {
   SBN_BF16 = 1,                /* bfloat16, round to nearest even from float32 */
   SBN_I32_ACC = 2              /* raw int32 accumulator sum_k Xq*Wt, unscaled */
 } sbn_dtype;
+
+/*
+ * Variant flags.  The two ablations the pages report (gist.science de §4
+ * "Ablationsstudien", fr §5 "Importance de la Stratégie d'Optimisation": both
+ * make training worse) are kept as switches of the method's own calls, for
+ * that comparison:
+ *   SBN_MASK_FROM_TERNARY  pack: the mask keeps, per group, the n largest |q|
+ *                          of the ternary weights q = RoundClip(w / s_w)
+ *                          (0 or 1) instead of the n largest |w| of the master
+ *                          weights; ties go to the lower index as before.
+ *   SBN_GRAD_W_MASKED      backward: dW is 0 wherever the meta bit of (r, k)
+ *                          is clear (gradients blocked for pruned weights)
+ *                          instead of the dense gradient.  No effect at n == m.
+ */
+typedef enum sbn_flags {
+  SBN_FLAGS_NONE = 0,
+  SBN_MASK_FROM_TERNARY = 1,
+  SBN_GRAD_W_MASKED = 2
+} sbn_flags;
 
 typedef enum sbn_op {
   SBN_OP_PACK = 0,
@@ -136,6 +157,39 @@ sbn_status sbn_workspace_bytes(sbn_op op, int64_t T, int64_t R, int64_t K,
 sbn_status sbn_mask_ternarize_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw,
                                    int n, int m, uint8_t* codes, uint8_t* meta, float* s_w,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sbn_mask_ternarize_pack with variant flags: 0 or SBN_MASK_FROM_TERNARY.
+ * Other flag bits: SBN_ERR_FLAGS.  Arguments and limits as above.
+ */
+sbn_status sbn_mask_ternarize_pack_ex(const uint16_t* W, int64_t R, int64_t K, int64_t ldw,
+                                      int n, int m, uint32_t flags, uint8_t* codes, uint8_t* meta,
+                                      float* s_w, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One optimizer step on the BF16 master weights followed by the next
+ * step's mask/ternarize/pack of the updated weights, in two passes over W.
+ * The pages keep BF16 master weights that receive the gradients and
+ * recompute the mask from them at every step (ja §2.1, ko §2.2) but name no
+ * optimizer; this is plain SGD:
+ *   W[r,k] <- bf16(fma(-lr, G[r,k], W[r,k]))   (one float32 rounding of the
+ *             exact value, then round half to even to bf16), in place;
+ * then exactly sbn_mask_ternarize_pack_ex(W, ...) of the new W.  Pass 1
+ * updates W and sums |W| from the values it writes; pass 2 masks and packs,
+ * so W is read twice and written once (an update followed by a separate
+ * pack reads it three times).
+ *
+ *   W      [R x K] bf16, row stride ldw >= K        (in/out, updated in place)
+ *   G      [R x K] float32, row stride ldg >= K     (in, e.g. dW of sbn_backward)
+ *   lr     learning rate, finite (else SBN_ERR_VALUE)
+ *   flags  0 or SBN_MASK_FROM_TERNARY
+ *   codes, meta, s_w, ws: as sbn_mask_ternarize_pack (workspace of
+ *          sbn_workspace_bytes(SBN_OP_PACK, 0, R, K, n, m))
+ * An update that overflows bf16 is outside the contract.
+ */
+sbn_status sbn_sgd_update_pack(uint16_t* W, int64_t R, int64_t K, int64_t ldw, const float* G,
+                               int64_t ldg, float lr, int n, int m, uint32_t flags, uint8_t* codes,
+                               uint8_t* meta, float* s_w, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Per-token absmax int8 quantization of the activations (the pages leave
@@ -223,13 +277,23 @@ sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* 
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sbn_backward with variant flags: 0 or SBN_GRAD_W_MASKED (then meta is
+ * required when n < m, and dW at pruned positions is written as 0).
+ * Other flag bits: SBN_ERR_FLAGS.  Arguments as sbn_backward.
+ */
+sbn_status sbn_backward_ex(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
+                           const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
+                           const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,
+                           uint32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Kernel timing (diagnostics; not part of the operator).  While enabled,
  * every kernel the library launches whose name equals `kernel` (or every
  * kernel, when `kernel` is NULL) is bracketed by two HIP events recorded on
  * the stream it runs on.  sbn_profile_dump waits for the recorded events
  * and writes one line per kernel name, "name launches total_ms\n", into buf
  * (NUL-terminated, truncated to buf_bytes); sbn_profile_reset forgets them.
- * Kernel names: abs_sum, mask_pack, act_quant, expand_sparse, expand_dense,
+ * Kernel names: abs_sum, sgd_abs_sum, mask_pack, act_quant, expand_sparse, expand_dense,
  * gemm_smfmac, gemm_mfma, gemv, gemv_stream_24, gemv_stream_68, expand_wt,
  * prep_u, prep_xq, gemm_dx, gemm_dw.
  * Errors: SBN_ERR_NULL (buf), SBN_ERR_HIP.

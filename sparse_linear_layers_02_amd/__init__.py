@@ -25,8 +25,10 @@ HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "sbn.h")
 
 SBN_F32, SBN_BF16, SBN_I32_ACC = 0, 1, 2
 SBN_OP_PACK, SBN_OP_ACT_QUANT, SBN_OP_GEMM, SBN_OP_GEMV, SBN_OP_BACKWARD = 0, 1, 2, 3, 4
+SBN_FLAGS_NONE, SBN_MASK_FROM_TERNARY, SBN_GRAD_W_MASKED = 0, 1, 2
 STATUS = {0: "SBN_OK", 1: "SBN_ERR_NULL", 2: "SBN_ERR_SHAPE", 3: "SBN_ERR_UNSUPPORTED_NM",
-          4: "SBN_ERR_ALIGN", 5: "SBN_ERR_WORKSPACE", 6: "SBN_ERR_DTYPE", 7: "SBN_ERR_HIP"}
+          4: "SBN_ERR_ALIGN", 5: "SBN_ERR_WORKSPACE", 6: "SBN_ERR_DTYPE", 7: "SBN_ERR_HIP",
+          8: "SBN_ERR_FLAGS", 9: "SBN_ERR_VALUE"}
 
 
 class SbnError(RuntimeError):
@@ -38,7 +40,7 @@ class SbnError(RuntimeError):
 _lib = None
 _lock = threading.Lock()
 
-_i64, _int, _sz, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+_i64, _int, _sz, _vp, _u32 = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_uint32
 _SIGNATURES = {
     "sbn_abi_version": ([], _int),
     "sbn_status_string": ([_int], ctypes.c_char_p),
@@ -46,6 +48,9 @@ _SIGNATURES = {
     "sbn_packed_bytes": ([_i64, _i64, _int, _int, ctypes.POINTER(_sz), ctypes.POINTER(_sz)], _int),
     "sbn_workspace_bytes": ([_int, _i64, _i64, _i64, _int, _int, ctypes.POINTER(_sz)], _int),
     "sbn_mask_ternarize_pack": ([_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "sbn_mask_ternarize_pack_ex": ([_vp, _i64, _i64, _i64, _int, _int, _u32, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "sbn_sgd_update_pack": ([_vp, _i64, _i64, _i64, _vp, _i64, ctypes.c_float, _int, _int, _u32, _vp, _vp, _vp,
+                             _vp, _sz, _vp], _int),
     "sbn_act_quant": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], _int),
     "sbn_sparse_ternary_gemm": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _int, _int, _vp, _int, _i64,
                                  _vp, _sz, _vp], _int),
@@ -56,6 +61,8 @@ _SIGNATURES = {
                                          _i64, _i64, _vp], _int),
     "sbn_backward": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _int, _int, _vp, _int, _vp, _vp,
                       _sz, _vp], _int),
+    "sbn_backward_ex": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _int, _int, _vp, _int, _vp, _u32, _vp,
+                         _sz, _vp], _int),
     "sbn_profile_enable": ([_int, ctypes.c_char_p], _int),
     "sbn_profile_reset": ([], _int),
     "sbn_profile_dump": ([ctypes.c_char_p, _sz], _int),
@@ -139,8 +146,7 @@ class Workspace:
 _WS = {"pack": Workspace(), "gemm": Workspace(), "bwd": Workspace()}
 
 
-def sbn_mask_ternarize_pack(W, n: int, m: int, *, codes=None, meta=None, s_w=None, ws=None, stream=None):
-    """Mask, ternarize and pack bf16 master weights W [R, K].  Returns (codes, meta, s_w)."""
+def _pack_outputs(W, n: int, m: int, codes, meta, s_w, ws):
     torch = _torch()
     R, K = W.shape
     cb, mb = sbn_packed_bytes(R, K, n, m)
@@ -154,10 +160,42 @@ def sbn_mask_ternarize_pack(W, n: int, m: int, *, codes=None, meta=None, s_w=Non
     need = sbn_workspace_bytes(SBN_OP_PACK, 0, R, K, n, m)
     if ws is None:
         ws = _WS["pack"].get(need, dev)
+    return codes, meta, s_w, ws
+
+
+def sbn_mask_ternarize_pack(W, n: int, m: int, *, codes=None, meta=None, s_w=None, ws=None, stream=None):
+    """Mask, ternarize and pack bf16 master weights W [R, K].  Returns (codes, meta, s_w)."""
+    R, K = W.shape
+    codes, meta, s_w, ws = _pack_outputs(W, n, m, codes, meta, s_w, ws)
     _check("sbn_mask_ternarize_pack",
            lib().sbn_mask_ternarize_pack(_ptr(W), R, K, W.stride(0), n, m, _ptr(codes), _ptr(meta),
                                          _ptr(s_w), _ptr(ws), ws.numel() if ws is not None else 0,
                                          _stream(stream)))
+    return codes, meta, s_w
+
+
+def sbn_mask_ternarize_pack_ex(W, n: int, m: int, flags: int, *, codes=None, meta=None, s_w=None, ws=None,
+                               stream=None):
+    """sbn_mask_ternarize_pack with variant flags (SBN_MASK_FROM_TERNARY).  Returns (codes, meta, s_w)."""
+    R, K = W.shape
+    codes, meta, s_w, ws = _pack_outputs(W, n, m, codes, meta, s_w, ws)
+    _check("sbn_mask_ternarize_pack_ex",
+           lib().sbn_mask_ternarize_pack_ex(_ptr(W), R, K, W.stride(0), n, m, flags, _ptr(codes), _ptr(meta),
+                                            _ptr(s_w), _ptr(ws), ws.numel() if ws is not None else 0,
+                                            _stream(stream)))
+    return codes, meta, s_w
+
+
+def sbn_sgd_update_pack(W, G, lr: float, n: int, m: int, flags: int = 0, *, codes=None, meta=None, s_w=None,
+                        ws=None, stream=None):
+    """One SGD step W <- bf16(fma(-lr, G, W)) on bf16 W [R, K] (in place) with
+    float32 G [R, K], then mask/ternarize/pack of the new W.  Returns (codes, meta, s_w)."""
+    R, K = W.shape
+    codes, meta, s_w, ws = _pack_outputs(W, n, m, codes, meta, s_w, ws)
+    _check("sbn_sgd_update_pack",
+           lib().sbn_sgd_update_pack(_ptr(W), R, K, W.stride(0), _ptr(G), G.stride(0), float(lr), n, m, flags,
+                                     _ptr(codes), _ptr(meta), _ptr(s_w), _ptr(ws),
+                                     ws.numel() if ws is not None else 0, _stream(stream)))
     return codes, meta, s_w
 
 
@@ -223,9 +261,7 @@ def sbn_sparse_ternary_gemv_batched(Xq, s_x, codes, metas, s_ws, R: int, n: int,
     return Ys
 
 
-def sbn_backward(dY, Xq, s_x, codes, meta, s_w, n: int, m: int, *, dxdt: int = SBN_F32, want_dX: bool = True,
-                 want_dW: bool = True, dX=None, dW=None, ws=None, stream=None):
-    """Dual-STE backward.  Returns (dX [T, K] or None, dW [R, K] float32 or None)."""
+def _backward(name, flags, dY, Xq, s_x, codes, meta, s_w, n, m, dxdt, want_dX, want_dW, dX, dW, ws, stream):
     torch = _torch()
     T, R = dY.shape
     K = Xq.shape[1]
@@ -236,11 +272,27 @@ def sbn_backward(dY, Xq, s_x, codes, meta, s_w, n: int, m: int, *, dxdt: int = S
     need = sbn_workspace_bytes(SBN_OP_BACKWARD, T, R, K, n, m)
     if ws is None:
         ws = _WS["bwd"].get(need, dY.device)
-    _check("sbn_backward",
-           lib().sbn_backward(_ptr(dY), T, R, _ptr(Xq), _ptr(s_x), K, _ptr(codes), _ptr(meta), _ptr(s_w), n, m,
-                              _ptr(dX if want_dX else None), dxdt, _ptr(dW if want_dW else None), _ptr(ws),
-                              ws.numel() if ws is not None else 0, _stream(stream)))
+    args = [_ptr(dY), T, R, _ptr(Xq), _ptr(s_x), K, _ptr(codes), _ptr(meta), _ptr(s_w), n, m,
+            _ptr(dX if want_dX else None), dxdt, _ptr(dW if want_dW else None)]
+    if flags is not None:
+        args.append(flags)
+    args += [_ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)]
+    _check(name, getattr(lib(), name)(*args))
     return (dX if want_dX else None), (dW if want_dW else None)
+
+
+def sbn_backward(dY, Xq, s_x, codes, meta, s_w, n: int, m: int, *, dxdt: int = SBN_F32, want_dX: bool = True,
+                 want_dW: bool = True, dX=None, dW=None, ws=None, stream=None):
+    """Dual-STE backward.  Returns (dX [T, K] or None, dW [R, K] float32 or None)."""
+    return _backward("sbn_backward", None, dY, Xq, s_x, codes, meta, s_w, n, m, dxdt, want_dX, want_dW, dX, dW,
+                     ws, stream)
+
+
+def sbn_backward_ex(dY, Xq, s_x, codes, meta, s_w, n: int, m: int, flags: int, *, dxdt: int = SBN_F32,
+                    want_dX: bool = True, want_dW: bool = True, dX=None, dW=None, ws=None, stream=None):
+    """sbn_backward with variant flags (SBN_GRAD_W_MASKED).  Returns (dX or None, dW or None)."""
+    return _backward("sbn_backward_ex", flags, dY, Xq, s_x, codes, meta, s_w, n, m, dxdt, want_dX, want_dW, dX,
+                     dW, ws, stream)
 
 
 # ------------------------------------------------------------------ kernel timing
@@ -268,6 +320,8 @@ def sbn_profile_dump() -> dict:
 __all__ = [
     "lib", "header_symbols", "SbnError", "sbn_abi_version", "sbn_packed_bytes", "sbn_workspace_bytes",
     "sbn_mask_ternarize_pack", "sbn_act_quant", "sbn_sparse_ternary_gemm", "sbn_sparse_ternary_gemv",
-    "sbn_backward", "SBN_F32", "SBN_BF16", "SBN_I32_ACC", "SBN_OP_PACK", "SBN_OP_ACT_QUANT", "SBN_OP_GEMM",
+    "sbn_backward", "sbn_backward_ex", "sbn_mask_ternarize_pack_ex", "sbn_sgd_update_pack",
+    "SBN_FLAGS_NONE", "SBN_MASK_FROM_TERNARY", "SBN_GRAD_W_MASKED",
+    "SBN_F32", "SBN_BF16", "SBN_I32_ACC", "SBN_OP_PACK", "SBN_OP_ACT_QUANT", "SBN_OP_GEMM",
     "SBN_OP_GEMV", "SBN_OP_BACKWARD", "sbn_profile_enable", "sbn_profile_reset", "sbn_profile_dump",
 ]

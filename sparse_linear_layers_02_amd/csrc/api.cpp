@@ -3,6 +3,7 @@
 // Validation runs entirely on the host before any HIP call, so a rejected
 // call launches nothing and touches no output.
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -246,6 +247,8 @@ const char* sbn_status_string(sbn_status s) {
     case SBN_ERR_WORKSPACE: return "workspace too small";
     case SBN_ERR_DTYPE: return "unsupported dtype";
     case SBN_ERR_HIP: return "HIP runtime error";
+    case SBN_ERR_FLAGS: return "flag not accepted by this call";
+    case SBN_ERR_VALUE: return "scalar argument out of range";
   }
   return "unknown status";
 }
@@ -299,10 +302,9 @@ sbn_status sbn_workspace_bytes(sbn_op op, int64_t T, int64_t R, int64_t K, int n
   return fail(SBN_ERR_SHAPE, "%s: unknown op %d", fn, (int)op);
 }
 
-sbn_status sbn_mask_ternarize_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n,
-                                   int m, uint8_t* codes, uint8_t* meta, float* s_w, void* ws,
-                                   size_t ws_bytes, void* stream) {
-  const char* fn = "sbn_mask_ternarize_pack";
+static sbn_status pack_common(const char* fn, const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
+                              uint32_t flags, uint8_t* codes, uint8_t* meta, float* s_w, void* ws,
+                              size_t ws_bytes, const float* G, int64_t ldg, float lr, void* stream) {
   SBN_NONNULL(W);
   SBN_NONNULL(codes);
   SBN_NONNULL(s_w);
@@ -313,6 +315,8 @@ sbn_status sbn_mask_ternarize_pack(const uint16_t* W, int64_t R, int64_t K, int6
   SBN_TRY(check_k(K));
   if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
   SBN_TRY(check_ld("ldw", ldw, K));
+  if (flags & ~(uint32_t)SBN_MASK_FROM_TERNARY)
+    return fail(SBN_ERR_FLAGS, "%s: flags 0x%x: only SBN_MASK_FROM_TERNARY is accepted", fn, (unsigned)flags);
   SBN_ALIGNED(W);
   SBN_ALIGNED(codes);
   if (n < m) SBN_ALIGNED(meta);
@@ -321,7 +325,32 @@ sbn_status sbn_mask_ternarize_pack(const uint16_t* W, int64_t R, int64_t K, int6
   if (ws_bytes < need)
     return fail(SBN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
-  return hip_result(launch_pack(W, R, K, ldw, n, m, codes, meta, s_w, ws, st), st, fn);
+  return hip_result(launch_pack(W, R, K, ldw, n, m, codes, meta, s_w, ws, flags, G, ldg, lr, st), st, fn);
+}
+
+sbn_status sbn_mask_ternarize_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n,
+                                   int m, uint8_t* codes, uint8_t* meta, float* s_w, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return pack_common("sbn_mask_ternarize_pack", W, R, K, ldw, n, m, 0u, codes, meta, s_w, ws, ws_bytes,
+                     nullptr, 0, 0.0f, stream);
+}
+
+sbn_status sbn_mask_ternarize_pack_ex(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
+                                      uint32_t flags, uint8_t* codes, uint8_t* meta, float* s_w, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  return pack_common("sbn_mask_ternarize_pack_ex", W, R, K, ldw, n, m, flags, codes, meta, s_w, ws, ws_bytes,
+                     nullptr, 0, 0.0f, stream);
+}
+
+sbn_status sbn_sgd_update_pack(uint16_t* W, int64_t R, int64_t K, int64_t ldw, const float* G, int64_t ldg,
+                               float lr, int n, int m, uint32_t flags, uint8_t* codes, uint8_t* meta,
+                               float* s_w, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "sbn_sgd_update_pack";
+  SBN_NONNULL(G);
+  SBN_ALIGNED(G);
+  SBN_TRY(check_ld("ldg", ldg, K));
+  if (!std::isfinite(lr)) return fail(SBN_ERR_VALUE, "%s: lr must be finite", fn);
+  return pack_common(fn, W, R, K, ldw, n, m, flags, codes, meta, s_w, ws, ws_bytes, G, ldg, lr, stream);
 }
 
 sbn_status sbn_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, int8_t* Xq,
@@ -400,11 +429,10 @@ sbn_status sbn_sparse_ternary_gemv_batched(const int8_t* Xq, const float* s_x, i
                     st, fn);
 }
 
-sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
-                        const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
-                        const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,
-                        void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "sbn_backward";
+static sbn_status backward_common(const char* fn, const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
+                                  const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
+                                  const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,
+                                  uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
   SBN_NONNULL(dY);
   SBN_NONNULL(Xq);
   SBN_NONNULL(s_x);
@@ -420,6 +448,8 @@ sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* 
   if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
   if (dX && dxdt != SBN_F32 && dxdt != SBN_BF16)
     return fail(SBN_ERR_DTYPE, "%s: dX dtype must be SBN_F32 or SBN_BF16", fn);
+  if (flags & ~(uint32_t)SBN_GRAD_W_MASKED)
+    return fail(SBN_ERR_FLAGS, "%s: flags 0x%x: only SBN_GRAD_W_MASKED is accepted", fn, (unsigned)flags);
   SBN_ALIGNED(dY);
   SBN_ALIGNED(Xq);
   SBN_ALIGNED(codes);
@@ -432,8 +462,24 @@ sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* 
     return fail(SBN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
   return hip_result(launch_backward(dY, T, R, Xq, s_x, K, codes, n == m ? nullptr : meta, s_w, n,
-                                    m, dX, dxdt, dW, ws, st),
+                                    m, dX, dxdt, dW, ws, flags, st),
                     st, fn);
+}
+
+sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
+                        const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
+                        const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return backward_common("sbn_backward", dY, T, R, Xq, s_x, K, codes, meta, s_w, n, m, dX, dxdt, dW, 0u, ws,
+                         ws_bytes, stream);
+}
+
+sbn_status sbn_backward_ex(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
+                           const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
+                           const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,
+                           uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  return backward_common("sbn_backward_ex", dY, T, R, Xq, s_x, K, codes, meta, s_w, n, m, dX, dxdt, dW, flags, ws,
+                         ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -7,6 +7,9 @@
 // receiving updates.  With identity Jacobians:
 //   dX[t,k] = s_w * sum_r dY[t,r] * Wt[r,k]         (sparse ternary weight)
 //   dW[r,k] = sum_t (dY[t,r] * s_x[t]) * Xq[t,k]     (every (r,k))
+// The ablation of German §4 ("Ablationsstudien") / French §5 that blocks the
+// gradient of pruned weights is a flag: dW is then 0 wherever the meta bit of
+// (r, k) is clear (applied in the dW epilogue).
 //
 // Numerics.  dY (bf16) times a ternary weight is exact in bf16 operands;
 // Xq (|q| <= 127) is exact in bf16.  u = dY * s_x is not, so it is split
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(512, 1) void bf16_gemm_kernel(
     const uint8_t* __restrict__ Afr, const uint8_t* __restrict__ Bfr_hi,
     const uint8_t* __restrict__ Bfr_lo, const uint16_t* __restrict__ dY, int64_t nB /*B rows*/,
     int64_t nA /*A rows*/, int64_t nsteps, int64_t Rc /*dY cols (MODE 0)*/,
-    const float* __restrict__ s_w, void* __restrict__ Out, int64_t ldo) {
+    const float* __restrict__ s_w, void* __restrict__ Out, int64_t ldo, const uint8_t* __restrict__ gmask) {
   constexpr int NW = 8, MI = 8, MJ = 4;
   constexpr int NBF = MODE == 1 ? 2 : 1;
   constexpr int A_BYTES = 16 * 1024;
@@ -298,7 +301,13 @@ __global__ __launch_bounds__(512, 1) void bf16_gemm_kernel(
     for (int i = 0; i < MI; ++i) {
       const int64_t arow = tile_a + 16 * (MI * wa + i) + 4 * (lane >> 4);
       if (arow >= nA) continue;
-      const v4f c = acc[i][j] * scale;
+      v4f c = acc[i][j] * scale;
+      if (MODE == 1 && gmask) {                        // blocked-gradient variant: dW at pruned (r, k) is 0
+        const uint32_t nib = (uint32_t)(gmask[brow * (nA / 8) + (arow >> 3)] >> (arow & 7)) & 15u;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (!((nib >> v) & 1u)) c[v] = 0.0f;
+      }
       if (OUT == 1) {
         float* y = (float*)Out + brow * ldo + arow;
         if (arow + 3 < nA) *(v4f*)y = c;
@@ -347,7 +356,7 @@ size_t bwd_ws_bytes(int64_t T, int64_t R, int64_t K, int /*n*/, int /*m*/) {
 hipError_t launch_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
                            const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
                            const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,
-                           void* ws, hipStream_t st) {
+                           void* ws, uint32_t flags, hipStream_t st) {
   const BwdLayout L = bwd_layout(T, R, K);
   uint8_t* w = (uint8_t*)ws;
   hipError_t e;
@@ -365,10 +374,10 @@ hipError_t launch_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_
     const dim3 grid((unsigned)cdiv(T, 256), (unsigned)cdiv(K, 256));
     if (dxdt == SBN_F32)
       SBN_LAUNCH("gemm_dx", (bf16_gemm_kernel<0, 1>), grid, dim3(512), 0, st, w + L.wt, nullptr, nullptr,
-                         dY, T, K, L.RB32, R, s_w, dX, K);
+                         dY, T, K, L.RB32, R, s_w, dX, K, nullptr);
     else
       SBN_LAUNCH("gemm_dx", (bf16_gemm_kernel<0, 2>), grid, dim3(512), 0, st, w + L.wt, nullptr, nullptr,
-                         dY, T, K, L.RB32, R, s_w, dX, K);
+                         dY, T, K, L.RB32, R, s_w, dX, K, nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (dW) {
@@ -379,8 +388,9 @@ hipError_t launch_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_
                L.KB16, L.TB32, (uint4*)(w + L.xq));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 grid((unsigned)cdiv(R, 256), (unsigned)cdiv(K, 256));
+    const uint8_t* gmask = (flags & SBN_GRAD_W_MASKED) && n < m ? meta : nullptr;
     SBN_LAUNCH("gemm_dw", (bf16_gemm_kernel<1, 1>), grid, dim3(512), 0, st, w + L.xq, w + L.uhi,
-                       w + L.ulo, nullptr, R, K, L.TB32, (int64_t)0, s_w, (void*)dW, K);
+                       w + L.ulo, nullptr, R, K, L.TB32, (int64_t)0, s_w, (void*)dW, K, gmask);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -11,6 +11,16 @@
 // block of M; quantize, then mask), Japanese "技術概要" §2.1 (mask from the
 // continuous weights, recomputed every step), French "Résumé technique" §2.
 //
+// Variants.  The ablation of German §4 ("Ablationsstudien") / French §5 takes
+// the mask from the ternary weights instead: the key of a position becomes
+// |q| in {0, 1} (q = RoundClip(w / s_w)), ties still to the lower index.  The
+// optimizer step (Japanese §2.1: BF16 master weights receive the gradients;
+// no optimizer is named, plain SGD is used) replaces pass 1: each chunk of W
+// is updated in place, w' = bf16(fma(-lr, g, w)) (one float32 rounding, then
+// round-half-to-even to bf16), and the exact sum of |w'| is formed from the
+// values just written, so the step and the next pack read W once less than
+// an update followed by a separate pack.
+//
 // Exactness of the sum.  Every bf16 magnitude is sig * 2^(e-134) with an
 // 8-bit significand.  Magnitudes with exponent field e in [95, 131), i.e.
 // 2^-32 <= |w| < 16, are multiples of 2^-39 below 2^4; a float64 running sum
@@ -210,10 +220,41 @@ __device__ inline uint4 chunk_at(const uint16_t* __restrict__ W, int64_t c, int6
 // step while the next U1 load, and flushes its float64 sum (<= 8*U1 terms,
 // exact) into int64 units; out-of-window values take one rare branch per
 // group into the LDS bins.
+// The SGD step on one chunk of 8 bf16 weights and their 8 float32 gradients.
+__device__ inline uint4 sgd_chunk(uint4 w, float4 g0, float4 g1, float nlr) {
+  const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+  const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = f32_to_bf16_rne(__builtin_fmaf(nlr, g[2 * j], __uint_as_float(in[j] << 16)));
+    const uint32_t hi = f32_to_bf16_rne(__builtin_fmaf(nlr, g[2 * j + 1], __uint_as_float(in[j] & 0xFFFF0000u)));
+    out[j] = lo | (hi << 16);
+  }
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
 template <bool FLAT>
+__device__ inline void grad_at(const float* __restrict__ G, int64_t c, int64_t kc, int64_t ldg, float4& g0,
+                               float4& g1) {
+  const float4* p;
+  if (FLAT) {
+    p = (const float4*)G + 2 * c;
+  } else {
+    const int64_t r = c / kc;
+    p = (const float4*)(G + r * ldg + (c - r * kc) * 8);
+  }
+  g0 = p[0];
+  g1 = p[1];
+}
+
+// UPD: the optimizer step -- chunk c of W is first updated in place with the
+// gradient chunk of G (row stride ldg), nlr = -lr; the sum is of the new values.
+template <bool FLAT, bool UPD>
 __global__ __launch_bounds__(PT1) void abs_sum_kernel(const uint16_t* __restrict__ W, int64_t R,
                                                      int64_t K, int64_t ldw, int64_t cpb,
-                                                     unsigned char* __restrict__ ws) {
+                                                     unsigned char* __restrict__ ws,
+                                                     const float* __restrict__ G, int64_t ldg, float nlr) {
   const PackWs pw = pack_ws(ws, gridDim.x);
   __shared__ unsigned long long bins[256];
   __shared__ unsigned long long red[PT1 / 64];
@@ -228,11 +269,17 @@ __global__ __launch_bounds__(PT1) void abs_sum_kernel(const uint16_t* __restrict
   unsigned long long acc_i = 0;
   constexpr int64_t STEP = (int64_t)PT1 * U1;
   uint4 v[U1], nx[U1];
+  float4 g[U1][2], ng[U1][2];
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
   int64_t base = c0 + tid;
 #pragma unroll
   for (int u = 0; u < U1; ++u) {
     const int64_t c = base + (int64_t)u * PT1;
     v[u] = c < c1 ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
+    if (UPD) {
+      g[u][0] = g[u][1] = z4;
+      if (c < c1) grad_at<FLAT>(G, c, kc, ldg, g[u][0], g[u][1]);
+    }
   }
   for (; base < c1; base += STEP) {
     if (base + STEP < c1) {                      // next chunks load while these are summed
@@ -240,6 +287,29 @@ __global__ __launch_bounds__(PT1) void abs_sum_kernel(const uint16_t* __restrict
       for (int u = 0; u < U1; ++u) {
         const int64_t c = base + STEP + (int64_t)u * PT1;
         nx[u] = c < c1 ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
+        if (UPD) {
+          ng[u][0] = ng[u][1] = z4;
+          if (c < c1) grad_at<FLAT>(G, c, kc, ldg, ng[u][0], ng[u][1]);
+        }
+      }
+    }
+    if (UPD) {
+#pragma unroll
+      for (int u = 0; u < U1; ++u) {
+        const int64_t c = base + (int64_t)u * PT1;
+        if (c < c1) {
+          v[u] = sgd_chunk(v[u], g[u][0], g[u][1], nlr);
+          uint16_t* dst;
+          if (FLAT) {
+            dst = (uint16_t*)W + c * 8;
+          } else {
+            const int64_t r = c / kc;
+            dst = (uint16_t*)W + r * ldw + (c - r * kc) * 8;
+          }
+          *(uint4*)dst = v[u];
+        } else {
+          v[u] = make_uint4(0, 0, 0, 0);
+        }
       }
     }
     double acc = 0.0;
@@ -259,7 +329,13 @@ __global__ __launch_bounds__(PT1) void abs_sum_kernel(const uint16_t* __restrict
     }
     acc_i += (unsigned long long)(acc * FAST_SCALE);   // exact integer < 2^53
 #pragma unroll
-    for (int u = 0; u < U1; ++u) v[u] = nx[u];
+    for (int u = 0; u < U1; ++u) {
+      v[u] = nx[u];
+      if (UPD) {
+        g[u][0] = ng[u][0];
+        g[u][1] = ng[u][1];
+      }
+    }
   }
   const unsigned long long s = wave_sum_u64(acc_i);
   if ((tid & 63) == 0) red[tid >> 6] = s;
@@ -342,7 +418,8 @@ template <int M>
 __global__ __launch_bounds__(PT) void mask_pack_kernel(
     const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw, int n,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ meta, float* __restrict__ s_w_ptr,
-    const unsigned char* __restrict__ ws, int64_t nb, int64_t total_chunks, int64_t dr, int64_t dch) {
+    const unsigned char* __restrict__ ws, int64_t nb, int64_t total_chunks, int64_t dr, int64_t dch,
+    int tmask) {
   const float h = 0.5f * scale_from_partials(ws, nb, R * K, s_w_ptr);
   const uint32_t thr = __float_as_uint(h) >> 16;      // |w| > h  <=>  key > thr
   const int64_t cpr = K / 32;
@@ -365,8 +442,8 @@ __global__ __launch_bounds__(PT) void mask_pack_kernel(
         const int i = g * M + p;
         const uint32_t w = (u[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
         const uint32_t a = w & 0x7FFFu;
-        key[p] = (a << 3) | (uint32_t)(7 - p);          // distinct; lower index wins ties
         const uint32_t nz = a > thr ? 1u : 0u;
+        key[p] = ((tmask ? nz : a) << 3) | (uint32_t)(7 - p);   // distinct; lower index wins ties
         code[p] = nz | ((nz & (w >> 15)) << 1);          // 00 = 0, 01 = +1, 11 = -1
       }
       int slot = 0;
@@ -408,14 +485,15 @@ __global__ __launch_bounds__(PT) void mask_pack_kernel(
 // stores) with U loads in flight.  Per group the second-largest of four
 // distinct keys (|w| << 2 | 3 - p) is the threshold; the two keys at or above
 // it survive and their codes are picked with find-first-bit.
-__device__ inline void group24(uint32_t w01, uint32_t w23, uint32_t thr, uint32_t& keep4, uint32_t& code4) {
+__device__ inline void group24(uint32_t w01, uint32_t w23, uint32_t thr, int tmask, uint32_t& keep4,
+                               uint32_t& code4) {
   const uint32_t w[4] = {w01 & 0xFFFFu, w01 >> 16, w23 & 0xFFFFu, w23 >> 16};
   uint32_t k[4], code8 = 0;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const uint32_t a = w[p] & 0x7FFFu;
-    k[p] = (a << 2) | (uint32_t)(3 - p);
     const uint32_t nz = a > thr ? 1u : 0u;
+    k[p] = ((tmask ? nz : a) << 2) | (uint32_t)(3 - p);
     code8 |= (nz | ((nz & (w[p] >> 15)) << 1)) << (2 * p);
   }
   const uint32_t hi01 = max(k[0], k[1]), lo01 = min(k[0], k[1]);
@@ -431,7 +509,7 @@ template <bool FLAT>
 __global__ __launch_bounds__(PT) void mask_pack24_kernel(
     const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ meta, float* __restrict__ s_w_ptr, const unsigned char* __restrict__ ws,
-    int64_t nb) {
+    int64_t nb, int tmask) {
   const int64_t kc = K / 8, total = R * kc;
   const int64_t step = (int64_t)gridDim.x * PT * U;
   int64_t base = (int64_t)blockIdx.x * PT * U + threadIdx.x;
@@ -456,8 +534,8 @@ __global__ __launch_bounds__(PT) void mask_pack24_kernel(
       const int64_t c = base + (int64_t)u * PT;
       if (c < total) {
         uint32_t k0, c0, k1, c1;
-        group24(v[u].x, v[u].y, thr, k0, c0);
-        group24(v[u].z, v[u].w, thr, k1, c1);
+        group24(v[u].x, v[u].y, thr, tmask, k0, c0);
+        group24(v[u].z, v[u].w, thr, tmask, k1, c1);
         meta[c] = (uint8_t)(k0 | (k1 << 4));
         codes[c] = (uint8_t)(c0 | (c1 << 4));
       }
@@ -485,16 +563,27 @@ PackPlan pack_plan(int64_t R, int64_t K) {
 }
 
 hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
-                       uint8_t* codes, uint8_t* meta, float* s_w, void* ws, hipStream_t st) {
+                       uint8_t* codes, uint8_t* meta, float* s_w, void* ws, uint32_t flags,
+                       const float* G, int64_t ldg, float lr, hipStream_t st) {
   const PackPlan p = pack_plan(R, K);
-  if (ldw == K)
-    SBN_LAUNCH("abs_sum", abs_sum_kernel<true>, dim3((unsigned)p.nblocks), dim3(PT1), 0, st, W, R, K, ldw,
-               p.chunks_per_block, (unsigned char*)ws);
+  const bool flat = ldw == K && (G == nullptr || ldg == K);
+  const dim3 g1((unsigned)p.nblocks), b1(PT1);
+  const float nlr = -lr;
+  if (G == nullptr && flat)
+    SBN_LAUNCH("abs_sum", (abs_sum_kernel<true, false>), g1, b1, 0, st, W, R, K, ldw, p.chunks_per_block,
+               (unsigned char*)ws, G, ldg, nlr);
+  else if (G == nullptr)
+    SBN_LAUNCH("abs_sum", (abs_sum_kernel<false, false>), g1, b1, 0, st, W, R, K, ldw, p.chunks_per_block,
+               (unsigned char*)ws, G, ldg, nlr);
+  else if (flat)
+    SBN_LAUNCH("sgd_abs_sum", (abs_sum_kernel<true, true>), g1, b1, 0, st, W, R, K, ldw, p.chunks_per_block,
+               (unsigned char*)ws, G, ldg, nlr);
   else
-    SBN_LAUNCH("abs_sum", abs_sum_kernel<false>, dim3((unsigned)p.nblocks), dim3(PT1), 0, st, W, R, K, ldw,
-               p.chunks_per_block, (unsigned char*)ws);
+    SBN_LAUNCH("sgd_abs_sum", (abs_sum_kernel<false, true>), g1, b1, 0, st, W, R, K, ldw, p.chunks_per_block,
+               (unsigned char*)ws, G, ldg, nlr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const int tmask = (flags & SBN_MASK_FROM_TERNARY) ? 1 : 0;
   const int64_t total = R * (K / 32);
   int64_t blocks = cdiv(total, PT);
   if (blocks > 8192) blocks = 8192;
@@ -507,17 +596,17 @@ hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int
     if (b24 > 1024) b24 = 1024;                         // four blocks per CU, looping
     if (ldw == K)
       SBN_LAUNCH("mask_pack", mask_pack24_kernel<true>, dim3((unsigned)b24), dim3(PT), 0, st, W, R, K, ldw,
-                 codes, mp, s_w, (const unsigned char*)ws, p.nblocks);
+                 codes, mp, s_w, (const unsigned char*)ws, p.nblocks, tmask);
     else
       SBN_LAUNCH("mask_pack", mask_pack24_kernel<false>, dim3((unsigned)b24), dim3(PT), 0, st, W, R, K, ldw,
-                 codes, mp, s_w, (const unsigned char*)ws, p.nblocks);
+                 codes, mp, s_w, (const unsigned char*)ws, p.nblocks, tmask);
   }
   else if (m == 4)
     SBN_LAUNCH("mask_pack", mask_pack_kernel<4>, dim3((unsigned)blocks), dim3(PT), 0, st, W, R, K, ldw,
-                       n, codes, mp, s_w, (const unsigned char*)ws, p.nblocks, total, dr, dch);
+                       n, codes, mp, s_w, (const unsigned char*)ws, p.nblocks, total, dr, dch, tmask);
   else
     SBN_LAUNCH("mask_pack", mask_pack_kernel<8>, dim3((unsigned)blocks), dim3(PT), 0, st, W, R, K, ldw,
-                       n, codes, mp, s_w, (const unsigned char*)ws, p.nblocks, total, dr, dch);
+                       n, codes, mp, s_w, (const unsigned char*)ws, p.nblocks, total, dr, dch, tmask);
   return hipGetLastError();
 }
 

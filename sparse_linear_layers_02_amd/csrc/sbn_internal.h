@@ -95,8 +95,10 @@ void prof_end(int slot, hipStream_t st);
   } while (0)
 
 // ----------------------------------------------------------------- launchers
+// G != nullptr: the optimizer step W <- bf16(fma(-lr, G, W)) runs first, in place.
 hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
-                       uint8_t* codes, uint8_t* meta, float* s_w, void* ws, hipStream_t st);
+                       uint8_t* codes, uint8_t* meta, float* s_w, void* ws, uint32_t flags,
+                       const float* G, int64_t ldg, float lr, hipStream_t st);
 hipError_t launch_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, int8_t* Xq,
                             float* s_x, hipStream_t st);
 hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
@@ -114,6 +116,6 @@ hipError_t launch_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
 hipError_t launch_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
                            const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
                            const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,
-                           void* ws, hipStream_t st);
+                           void* ws, uint32_t flags, hipStream_t st);
 
 }  // namespace sbn

@@ -9,7 +9,7 @@ import pytest
 
 import sparse_linear_layers_02_amd as sbn
 
-OK, NULL, SHAPE, NM, ALIGN, WS, DTYPE, HIP = range(8)
+OK, NULL, SHAPE, NM, ALIGN, WS, DTYPE, HIP, FLAGS, VALUE = range(10)
 P = ctypes.c_void_p(0x100000)          # 16-byte aligned fake device address (never touched)
 P2 = ctypes.c_void_p(0x200000)
 MIS = ctypes.c_void_p(0x100004)        # misaligned
@@ -22,15 +22,15 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = sbn.header_symbols()
-    assert len(names) == 14
+    assert len(names) == 17
     for nm in names:
         assert hasattr(L, nm), nm
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.sbn_abi_version() == 1
-    for s in range(8):
-        assert L.sbn_status_string(s)
+    assert L.sbn_abi_version() == 2
+    for s in range(10):
+        assert L.sbn_status_string(s) != b"unknown status"
     assert L.sbn_status_string(99) == b"unknown status"
 
 
@@ -165,3 +165,30 @@ def test_profile_calls_without_launches(L):
     assert L.sbn_profile_dump(buf, 256) == OK and buf.value == b""
     assert L.sbn_profile_dump(None, 0) == NULL
     assert L.sbn_profile_enable(0, None) == OK
+
+
+def test_pack_ex_and_sgd_validation(L):
+    big = 1 << 20
+    f = L.sbn_mask_ternarize_pack_ex
+    assert f(P, 16, 256, 256, 2, 4, 4, P, P, P, P, big, None) == FLAGS          # unknown flag bit
+    assert f(P, 16, 256, 256, 2, 4, 2, P, P, P, P, big, None) == FLAGS          # a backward flag
+    assert f(None, 16, 256, 256, 2, 4, 1, P, P, P, P, big, None) == NULL
+    g = L.sbn_sgd_update_pack
+    nan = float("nan")
+    assert g(P, 16, 256, 256, None, 256, 0.1, 2, 4, 0, P, P, P, P, big, None) == NULL     # no gradient
+    assert g(P, 16, 256, 256, MIS, 256, 0.1, 2, 4, 0, P, P, P, P, big, None) == ALIGN
+    assert g(P, 16, 256, 256, P2, 128, 0.1, 2, 4, 0, P, P, P, P, big, None) == SHAPE      # ldg < K
+    assert g(P, 16, 256, 256, P2, 260, 0.1, 2, 4, 0, P, P, P, P, big, None) == ALIGN      # ldg % 8
+    assert g(P, 16, 256, 256, P2, 256, nan, 2, 4, 0, P, P, P, P, big, None) == VALUE
+    assert g(P, 16, 256, 256, P2, 256, float("inf"), 2, 4, 0, P, P, P, P, big, None) == VALUE
+    assert g(P, 16, 256, 256, P2, 256, 0.1, 2, 4, 8, P, P, P, P, big, None) == FLAGS
+    assert g(P, 16, 256, 256, P2, 256, 0.1, 2, 4, 0, P, P, P, P, 16, None) == WS
+    assert b"workspace" in L.sbn_last_error()
+
+
+def test_backward_ex_validation(L):
+    f = L.sbn_backward_ex
+    big = 1 << 30
+    assert f(P, 16, 256, P, P, 256, P, P, P, 2, 4, P, 0, P, 1, P, big, None) == FLAGS      # a pack flag
+    assert f(P, 16, 256, P, P, 256, P, None, P, 2, 4, P, 0, P, 2, P, big, None) == NULL    # meta needed
+    assert f(P, 16, 250, P, P, 256, P, P, P, 2, 4, P, 0, P, 2, P, big, None) == SHAPE      # R % 8
