@@ -39,6 +39,9 @@ same line carries:
                 separate calls replayed as four HIP graphs on four streams,
                 (ii-b) the pool as batched calls of 64 weights sharing the
                 activations (one launch each), replayed from a HIP graph;
+  variants      (train) the SGD step fused with the next pack, and the two
+                ablation switches (mask from the ternary weights; dW blocked
+                at pruned positions), per kernel;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload.
 Multi-GPU runs are not part of this build: --gpus above 1 exits.
 """
@@ -441,6 +444,70 @@ def speedup_tables(reps):
     return out
 
 
+# ---------------------------------------------------------------------- variants beside the path
+def variants_extras(wl, reps=10):
+    """The SGD step fused with the next pack, and the two ablation switches, at
+    the train shape, timed per kernel with the library's events:
+      sgd_update_pack   sgd_abs_sum (W, G read, W written in place, exact sum
+                        of the new |W|) + mask_pack, against the plain pack
+                        (abs_sum + mask_pack); HBM roofline of the fused call
+                        from its algorithmic bytes (W read twice and written
+                        once, G read once, planes written);
+      mask_from_ternary the pack with the mask from |q|;
+      grad_w_masked     gemm_dw with dW blocked at pruned positions, against
+                        the dense-gradient gemm_dw."""
+    import torch
+    import sparse_linear_layers_02_amd as sbn
+    n, m = wl.nm[0]
+    R, K = wl.R, wl.K
+    W = bf16_dev(wl.weights(0))
+    G = torch.randn((R, K), dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(0))
+    G.mul_(1e-2)
+    cb, mb = sbn.sbn_packed_bytes(R, K, n, m)
+    codes = torch.empty(cb, dtype=torch.uint8, device="cuda")
+    meta = torch.empty(mb, dtype=torch.uint8, device="cuda")
+    s_w = torch.empty(1, dtype=torch.float32, device="cuda")
+
+    def kernels(fn_):
+        fn_()
+        torch.cuda.synchronize()
+        prof = profile_pass(fn_, reps)
+        return {k: v[1] / v[0] * 1e3 for k, v in prof.items() if v[0]}
+
+    plain = kernels(lambda: sbn.sbn_mask_ternarize_pack(W, n, m, codes=codes, meta=meta, s_w=s_w))
+    tern = kernels(lambda: sbn.sbn_mask_ternarize_pack_ex(W, n, m, sbn.SBN_MASK_FROM_TERNARY, codes=codes,
+                                                          meta=meta, s_w=s_w))
+    fused = kernels(lambda: sbn.sbn_sgd_update_pack(W, G, 1e-6, n, m, codes=codes, meta=meta, s_w=s_w))
+    numel = R * K
+    planes = cb + mb
+    fused_bytes = numel * (2 + 4 + 2) + numel * 2 + planes
+    f_us = fused["sgd_abs_sum"] + fused["mask_pack"]
+    p_us = plain["abs_sum"] + plain["mask_pack"]
+    # backward: the dW GEMM with and without the blocked-gradient flag
+    X = bf16_dev(wl.activations(0))
+    dY = bf16_dev(wl.upstream_grad(0))
+    Xq, s_x = sbn.sbn_act_quant(X)
+    sbn.sbn_mask_ternarize_pack(W, n, m, codes=codes, meta=meta, s_w=s_w)
+    dW = torch.empty((R, K), dtype=torch.float32, device="cuda")
+    dense = kernels(lambda: sbn.sbn_backward(dY, Xq, s_x, codes, meta, s_w, n, m, want_dX=False, dW=dW))
+    blocked = kernels(lambda: sbn.sbn_backward_ex(dY, Xq, s_x, codes, meta, s_w, n, m, sbn.SBN_GRAD_W_MASKED,
+                                                  want_dX=False, dW=dW))
+    r = lambda x: round(x, 2)
+    return {
+        "shape": f"R={R} K={K} {n}:{m}",
+        "sgd_update_pack": {"sgd_abs_sum_us": r(fused["sgd_abs_sum"]), "mask_pack_us": r(fused["mask_pack"]),
+                            "total_us": r(f_us), "algo_bytes": fused_bytes,
+                            "GBps": round(fused_bytes / (f_us * 1e-6) / 1e9, 1),
+                            "frac_hbm": round(fused_bytes / (f_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                            "plain_pack_us": r(p_us),
+                            "note": "W read twice and written once, G (float32) read once; an update followed "
+                                    "by a separate pack reads W once more (2 bytes per weight)"},
+        "mask_from_ternary": {"abs_sum_us": r(tern["abs_sum"]), "mask_pack_us": r(tern["mask_pack"]),
+                              "plain_mask_pack_us": r(plain["mask_pack"])},
+        "grad_w_masked": {"gemm_dw_us": r(blocked["gemm_dw"]), "dense_gemm_dw_us": r(dense["gemm_dw"])},
+    }
+
+
 # ---------------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl, n, m, tokens):
     """The oracle as it stands, on the host: pack the full W, quantize `tokens`
@@ -647,6 +714,8 @@ def main():
 
     if not a.no_extras and a.workload not in ("decode", "speedup"):
         out["decode_gemv"] = [decode_gemv(2, 4, 1), decode_gemv(6, 8, 1)]
+    if not a.no_extras and a.workload == "train":
+        out["variants"] = variants_extras(WORKLOADS["train"])
 
     if a.no_cpu_baseline or a.workload == "speedup":
         out["cpu_baseline"] = None
