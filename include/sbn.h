@@ -293,7 +293,7 @@ sbn_status sbn_backward_ex(const uint16_t* dY, int64_t T, int64_t R, const int8_
  * the stream it runs on.  sbn_profile_dump waits for the recorded events
  * and writes one line per kernel name, "name launches total_ms\n", into buf
  * (NUL-terminated, truncated to buf_bytes); sbn_profile_reset forgets them.
- * Kernel names: abs_sum, sgd_abs_sum, mask_pack, act_quant, expand_sparse, expand_dense,
+ * Kernel names: abs_sum, sgd_abs_sum, mask_pack, act_quant, layout_sparse, layout_dense,
  * gemm_smfmac, gemm_mfma, gemv, gemv_stream_24, gemv_stream_68, expand_wt,
  * prep_u, prep_xq, gemm_dx, gemm_dw.
  * Errors: SBN_ERR_NULL (buf), SBN_ERR_HIP.

@@ -10,13 +10,13 @@
 //   * every other ratio (6:8, 4:8, 3:4, the dense 8:8 control, ...) runs on
 //     dense v_mfma_i32_16x16x64_i8 with W expanded to int8 {-1, 0, +1}.
 //
-// Three kernels per call.  Two layout passes put both operands in matrix-core
-// fragment order (one contiguous 1 KB block per 16 rows x 64 or 128 K, lane l's
-// 16 bytes at offset 16*l), so every load of the GEMM main loop is a
-// contiguous 1 KB global->LDS transfer and every LDS read a contiguous
-// 16-byte read:
-//   expand_sparse / expand_dense : packed codes + meta -> W fragments
-//   tile_x                       : Xq [T][K] row-major -> X fragments, zero padded
+// Two kernels per call.  Two layout passes, run side by side in one launch
+// (layout_sparse / layout_dense), put both operands in matrix-core fragment
+// order (one contiguous 1 KB block per 16 rows x 64 or 128 K, lane l's 16
+// bytes at offset 16*l), so every load of the GEMM main loop is a contiguous
+// 1 KB global->LDS transfer and every LDS read a contiguous 16-byte read:
+//   expand (sparse or dense) : packed codes + meta -> W fragments
+//   tile_x                   : Xq [T][K] row-major -> X fragments, zero padded
 // then the GEMM.
 //
 // GEMM: 512 threads (8 waves), block tile 256 rows x 256 tokens, wave tile
@@ -51,11 +51,11 @@ __device__ inline int8_t code_to_i8(uint32_t c) { return c == 1u ? (int8_t)1 : c
 // fragment 16 compressed values + 32 index bits.
 // vals [RB][KBn][64][16 B]; idx [RB/4][KBn][64][4 x u32] (row fragment 4g+q in
 // word q, so a thread's four index words are one 16-byte store)
-__global__ __launch_bounds__(256) void expand_sparse_kernel(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+__device__ inline void expand_sparse_block(
+    int64_t blk, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, int64_t R, int64_t K,
     int n, int m, int64_t RB, int64_t KBn, int64_t cplane, uint8_t* __restrict__ vals,
     uint32_t* __restrict__ idx) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t gid = blk * 256 + threadIdx.x;
   if (gid >= (RB / 4) * KBn * 64) return;
   const int l = (int)(gid & 63);
   const int64_t f = gid >> 6;                   // = g * KBn + kb
@@ -121,17 +121,16 @@ __global__ __launch_bounds__(256) void expand_sparse_kernel(
 // through the unpack table in LDS (built once per block; blocks walk the
 // fragments with a grid stride).  vals [RB][KD][64][16 B].
 template <int M>
-__global__ __launch_bounds__(256) void expand_dense_kernel(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, int64_t R, int64_t K,
-    int n, int64_t RB, int64_t KD, int64_t cplane, uint8_t* __restrict__ vals) {
-  __shared__ uint32_t lut[4096];
+__device__ inline void expand_dense_blocks(
+    int64_t blk, int64_t nblk, uint32_t* lut, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
+    int64_t R, int64_t K, int n, int64_t RB, int64_t KD, int64_t cplane, uint8_t* __restrict__ vals) {
   for (int i = threadIdx.x; i < 4096; i += 256) lut[i] = unpack_entry((uint32_t)i);
   __syncthreads();
   const int64_t total = RB * KD * 64;
   const int64_t crow = K * n / (4 * M);          // code bytes per row
   const int64_t lastw = (cplane - 4) & ~(int64_t)3;
   const bool dense = meta == nullptr;
-  for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total; gid += (int64_t)gridDim.x * 256) {
+  for (int64_t gid = blk * 256 + threadIdx.x; gid < total; gid += nblk * 256) {
     const int l = (int)(gid & 63);
     const int64_t f = gid >> 6;
     const int64_t rb = f / KD, kd = f - rb * KD;
@@ -157,9 +156,9 @@ __global__ __launch_bounds__(256) void expand_dense_kernel(
 // Xt [TBp][KC][64][16 B]: block (tb, kc) holds tokens 16*tb.. and K bytes
 // 64*kc..; lane l carries token 16*tb + l%16, K bytes 64*kc + 16*(l/16) ..+16.
 // Tokens >= T and K >= K are zero.
-__global__ __launch_bounds__(256) void tile_x_kernel(const int8_t* __restrict__ Xq, int64_t T, int64_t K,
-                                                     int64_t TBp, int64_t KC, uint4* __restrict__ Xt) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ inline void tile_x_block(int64_t blk, const int8_t* __restrict__ Xq, int64_t T, int64_t K,
+                                    int64_t TBp, int64_t KC, uint4* __restrict__ Xt) {
+  const int64_t gid = blk * 256 + threadIdx.x;
   if (gid >= TBp * KC * 64) return;
   const int l = (int)(gid & 63);
   const int64_t f = gid >> 6;
@@ -169,6 +168,39 @@ __global__ __launch_bounds__(256) void tile_x_kernel(const int8_t* __restrict__ 
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (t < T && k < K) v = *(const uint4*)(Xq + t * K + k);
   Xt[gid] = v;
+}
+
+// ---------------------------------------------------------------- the two layout passes in one launch
+// Blocks [0, nbw) expand W, blocks [nbw, nbw + nbx) tile X: the two passes are
+// independent, so one grid runs them side by side (one launch ramp, and the
+// short X pass fills the compute units the W pass leaves idle).
+struct XTileArgs {
+  const int8_t* Xq;
+  int64_t T, K, TBp, KC;
+  uint4* Xt;
+};
+
+__global__ __launch_bounds__(256) void layout_sparse_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+    int n, int m, int64_t RB, int64_t KBn, int64_t cplane, uint8_t* __restrict__ vals,
+    uint32_t* __restrict__ idx, int64_t nbw, const XTileArgs xa) {
+  const int64_t b = blockIdx.x;
+  if (b < nbw)
+    expand_sparse_block(b, codes, meta, R, K, n, m, RB, KBn, cplane, vals, idx);
+  else
+    tile_x_block(b - nbw, xa.Xq, xa.T, xa.K, xa.TBp, xa.KC, xa.Xt);
+}
+
+template <int M>
+__global__ __launch_bounds__(256) void layout_dense_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+    int n, int64_t RB, int64_t KD, int64_t cplane, uint8_t* __restrict__ vals, int64_t nbw, const XTileArgs xa) {
+  __shared__ uint32_t lut[4096];
+  const int64_t b = blockIdx.x;
+  if (b < nbw)                                       // uniform per block: the table barrier is safe
+    expand_dense_blocks<M>(b, nbw, lut, codes, meta, R, K, n, RB, KD, cplane, vals);
+  else
+    tile_x_block(b - nbw, xa.Xq, xa.T, xa.K, xa.TBp, xa.KC, xa.Xt);
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -459,33 +491,30 @@ hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
   const GemmWs g = gemm_ws(T, R, K, n, m);
   uint8_t* w = (uint8_t*)ws;
   uint8_t* xt = w + g.w_bytes + g.i_bytes;
-  SBN_LAUNCH("tile_x", tile_x_kernel, dim3((unsigned)cdiv(TBp * KC * 64, 256)), dim3(256), 0, st,
-             Xq, T, K, TBp, KC, (uint4*)xt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const XTileArgs xa{Xq, T, K, TBp, KC, (uint4*)xt};
+  const int64_t nbx = cdiv(TBp * KC * 64, 256);                // X tiling blocks
+  const int64_t cplane = round_up(R * (K * n / (4 * m)), 16);  // readable bytes of the codes plane
+  hipError_t e;
   if (gemm_uses_smfmac(n, m)) {
     uint8_t* vals = w;
     uint32_t* idx = (uint32_t*)(w + g.w_bytes);
-    const int64_t threads = (RB / 4) * KBn * 64;
-    const int64_t cplane = round_up(R * (K * n / (4 * m)), 16);  // readable bytes of the codes plane
-    SBN_LAUNCH("expand_sparse", expand_sparse_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, st,
-               codes, meta, R, K, n, m, RB, KBn, cplane, vals, idx);
+    const int64_t nbw = cdiv((RB / 4) * KBn * 64, 256);
+    SBN_LAUNCH("layout_sparse", layout_sparse_kernel, dim3((unsigned)(nbw + nbx)), dim3(256), 0, st,
+               codes, meta, R, K, n, m, RB, KBn, cplane, vals, idx, nbw, xa);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_gemm_t<true>(vals, (const uint8_t*)idx, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
   }
   const int64_t KD = 2 * KBn;
-  const int64_t threads = RB * KD * 64;
-  const int64_t cplane = round_up(R * (K * n / (4 * m)), 16);    // readable bytes of the codes plane
-  int64_t blocks = cdiv(threads, 256);
-  if (blocks > 1024) blocks = 1024;                        // four blocks per CU, each table built once
+  int64_t nbw = cdiv(RB * KD * 64, 256);
+  if (nbw > 1024) nbw = 1024;                              // four blocks per CU, each table built once
   const uint8_t* mp = (n == m) ? nullptr : meta;
   if (m == 4)
-    SBN_LAUNCH("expand_dense", expand_dense_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st,
-               codes, mp, R, K, n, RB, KD, cplane, w);
+    SBN_LAUNCH("layout_dense", layout_dense_kernel<4>, dim3((unsigned)(nbw + nbx)), dim3(256), 0, st,
+               codes, mp, R, K, n, RB, KD, cplane, w, nbw, xa);
   else
-    SBN_LAUNCH("expand_dense", expand_dense_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, st,
-               codes, mp, R, K, n, RB, KD, cplane, w);
+    SBN_LAUNCH("layout_dense", layout_dense_kernel<8>, dim3((unsigned)(nbw + nbx)), dim3(256), 0, st,
+               codes, mp, R, K, n, RB, KD, cplane, w, nbw, xa);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_gemm_t<false>(w, nullptr, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
