@@ -20,7 +20,9 @@
 // then the GEMM.
 //
 // GEMM: 512 threads (8 waves), block tile 256 rows x 256 tokens, wave tile
-// 128 rows x 64 tokens (8 x 4 accumulator tiles of 16 x 16 int32); K step 128
+// 128 rows x 64 tokens (8 x 4 accumulator tiles of 16 x 16 int32) -- or 128 /
+// 64 tokens per block (8 x 2 / 8 x 1 per wave) when the token count gives the
+// 256 x 256 grid fewer than 192 tiles for the 256 compute units; K step 128
 // (sparse, 3 LDS stages of 52 KB) or 64 (dense, 4 stages of 32 KB), stages
 // filled with direct global->LDS loads issued two (sparse) or three (dense)
 // steps ahead.  The two waves that share a SIMD (w and w + 4) alternate
@@ -229,34 +231,39 @@ __device__ inline void pp_barrier() {
 }
 
 // OUT: 0 = int32 accumulator, 1 = float32, 2 = bf16.
-template <bool SPARSE, int OUT>
+// MJ: token fragments per wave (4: 256-token block tile; 2 and 1: 128 and 64
+// tokens, for token counts whose 256 x 256 grid would leave compute units idle).
+template <bool SPARSE, int OUT, int MJ>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(
     const uint8_t* __restrict__ Aw, const uint8_t* __restrict__ Ai, const uint8_t* __restrict__ Xt,
     const float* __restrict__ s_x, const float* __restrict__ s_w, int64_t T, int64_t R,
     int64_t nks, int64_t fstride, int64_t KC, void* __restrict__ Y, int64_t ldy) {
-  constexpr int NW = 8, MI = 8, MJ = 4;                // 8 waves; wave tile 8 x 4 fragments
+  constexpr int NW = 8, MI = 8;                        // 8 waves; wave tile 8 x MJ fragments
+  constexpr int TT = 64 * MJ;                          // tokens per block tile
   constexpr int A_BYTES = 16 * 1024;                   // 16 row fragments
   constexpr int I_BYTES = SPARSE ? 4 * 1024 : 0;       // their index words
   constexpr int BH = SPARSE ? 2 : 1;                   // 1 KB X blocks per token block per step
-  constexpr int B_BYTES = 16 * BH * 1024;
+  constexpr int NXB = 4 * MJ * BH;                     // 1 KB X blocks per stage
+  static_assert(NXB % NW == 0, "every wave loads the same number of X blocks");
+  constexpr int B_BYTES = NXB * 1024;
   constexpr int STAGE = A_BYTES + I_BYTES + B_BYTES;
   constexpr int NST = SPARSE ? 3 : 4;
-  // global loads per wave per stage: 2 W fragments, 4 (sparse) or 2 X blocks,
-  // the index block (waves 0..3, sparse)
-  constexpr int LPS0 = 2 + (SPARSE ? 1 : 0) + 2 * BH;
-  constexpr int LPS1 = 2 + 2 * BH;
+  // global loads per wave per stage: 2 W fragments, NXB / 8 X blocks, the
+  // index block (waves 0..3, sparse)
+  constexpr int LPS0 = 2 + (SPARSE ? 1 : 0) + NXB / NW;
+  constexpr int LPS1 = 2 + NXB / NW;
   constexpr int WAIT0 = (NST - 2) * LPS0, WAIT1 = (NST - 2) * LPS1;
-  constexpr int EPI_BYTES = NW * 64 * 272;              // bf16 epilogue staging, 64 x 272 B per wave
+  constexpr int EPI_BYTES = NW * 16 * MJ * 272;         // bf16 epilogue staging, 16*MJ x 272 B per wave
   constexpr int SMEM = NST * STAGE > EPI_BYTES ? NST * STAGE : EPI_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int grp = wave >> 2;                           // waves w and w + 4 share a SIMD
-  const int wr = wave & 1, wt = wave >> 1;             // rows 128*wr.., tokens 64*wt..
+  const int wr = wave & 1, wt = wave >> 1;             // rows 128*wr.., tokens 16*MJ*wt..
   int64_t rtile, ttile;
-  tile_of_block(blockIdx.x, cdiv(R, 256), cdiv(T, 256), rtile, ttile);
-  const int64_t tile_r = rtile * 256, tile_t = ttile * 256;
+  tile_of_block(blockIdx.x, cdiv(R, 256), cdiv(T, TT), rtile, ttile);
+  const int64_t tile_r = rtile * 256, tile_t = ttile * TT;
   const int64_t rb0 = tile_r / 16, tb0 = tile_t / 16;
 
   // scales for the epilogue, fetched before the main loop
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
     if (SPARSE && grp == 0)
       g2lds16(Ai + ((rb0 / 4 + wave) * fstride + ks) * 1024 + lane * 16, base + A_BYTES + wave * 1024);
 #pragma unroll
-    for (int q = 0; q < 2 * BH; ++q) {
+    for (int q = 0; q < NXB / NW; ++q) {
       const int hb = wave + NW * q;                    // 1 KB block: token block hb/BH, half hb%BH
       g2lds16(Xt + ((tb0 + hb / BH) * KC + ks * BH + hb % BH) * 1024 + lane * 16,
               base + A_BYTES + I_BYTES + hb * 1024);
@@ -372,15 +379,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   }
 
   if (OUT == 2) {
-    // bf16: stage the wave's 128 x 64 tile through LDS as [token][row] (pitch
+    // bf16: stage the wave's 128 x 16*MJ tile through LDS as [token][row] (pitch
     // 272 B keeps the 8-byte writes of 16 tokens on distinct banks), then store
     // four token rows of 256 contiguous bytes per instruction, non-temporal so
     // the output streams past L2 instead of evicting operands other blocks
     // still read.  All LDS stages are free here: every wave passed its last
     // stage read before B(2*nks).
     constexpr int PITCH = 272;
-    static_assert(NW * 64 * PITCH <= SMEM, "epilogue staging fits");
-    uint8_t* st = smem + wave * (64 * PITCH);
+    static_assert(NW * 16 * MJ * PITCH <= SMEM, "epilogue staging fits");
+    uint8_t* st = smem + wave * (16 * MJ * PITCH);
 #pragma unroll
     for (int j = 0; j < MJ; ++j) {
       const float sc = sw * sxv[j];
@@ -395,9 +402,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
     }
     const int64_t r0 = tile_r + 128 * wr + 8 * (lane & 15);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < 4 * MJ; ++q) {
       const int tl = 4 * q + (lane >> 4);
-      const int64_t t = tile_t + 64 * wt + tl;
+      const int64_t t = tile_t + 16 * MJ * wt + tl;
       const v4i v = *(const v4i*)(st + tl * PITCH + (lane & 15) * 16);
       if (t >= T || r0 >= R) continue;
       uint16_t* y = (uint16_t*)Y + t * ldy + r0;
@@ -435,23 +442,46 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   }
 }
 
-template <bool SPARSE>
-hipError_t launch_gemm_t(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
-                         const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y,
-                         sbn_dtype ydt, int64_t ldy, hipStream_t st) {
-  const int64_t ntiles = cdiv(T, GEMM_TILE_T) * cdiv(R, GEMM_TILE_R);
+template <bool SPARSE, int MJ>
+hipError_t launch_gemm_mj(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
+                          const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y,
+                          sbn_dtype ydt, int64_t ldy, hipStream_t st) {
+  const int64_t ntiles = cdiv(T, 64 * MJ) * cdiv(R, GEMM_TILE_R);
   const dim3 grid((unsigned)ntiles), block(512);
   const int64_t nks = SPARSE ? KBn : K / 64;
   const int64_t fstride = SPARSE ? KBn : 2 * KBn;
   const int64_t KC = 2 * KBn;
   const char* name = SPARSE ? "gemm_smfmac" : "gemm_mfma";
   if (ydt == SBN_I32_ACC)
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 0>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 0, MJ>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC,
+               Y, ldy);
   else if (ydt == SBN_F32)
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 1>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 1, MJ>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC,
+               Y, ldy);
   else
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 2>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC, Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 2, MJ>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC,
+               Y, ldy);
   return hipGetLastError();
+}
+
+// Token fragments per wave: the 256-token tile unless its grid leaves more
+// than a quarter of the 256 compute units idle; then 128 or (sparse) 64 tokens.
+int gemm_mj(bool sparse, int64_t T, int64_t R) {
+  const int64_t rt = cdiv(R, GEMM_TILE_R);
+  if (cdiv(T, 256) * rt >= 192) return 4;
+  if (!sparse || cdiv(T, 128) * rt >= 192) return 2;
+  return 1;
+}
+
+template <bool SPARSE>
+hipError_t launch_gemm_t(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
+                         const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y,
+                         sbn_dtype ydt, int64_t ldy, hipStream_t st) {
+  const int mj = gemm_mj(SPARSE, T, R);
+  if (mj == 4) return launch_gemm_mj<SPARSE, 4>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+  if (mj == 2) return launch_gemm_mj<SPARSE, 2>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+  if (SPARSE) return launch_gemm_mj<SPARSE, SPARSE ? 1 : 2>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -248,6 +248,17 @@ def test_gemm_small_edges(T, R, K):
         check_outputs("gemv", f, Xq, s_x, codes, meta, s_w, R, 2, 4)
 
 
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
+@pytest.mark.parametrize("T", [100, 200, 497])
+def test_gemm_token_tile_variants(T, n, m):
+    # R = 96 row tiles - 37 rows: T = 497 keeps the 256-token block tile (192
+    # tiles), T = 200 takes the 128-token tile and T = 100 the 64-token tile
+    # (sparse; dense stops at 128), each with ragged rows and tokens
+    R, K = 96 * 256 - 37, 256
+    f, Xq, s_x, codes, meta, s_w = forward_case(T, R, K, n, m, seed=T + n)
+    check_outputs("gemm", f, Xq, s_x, codes, meta, s_w, R, n, m)
+
+
 def test_gemm_extreme_activations():
     # Xq = +-127 everywhere on dense ternary +-1 weights: |acc| = 127*K at the limit of the range
     T, R, K, n, m = 32, 64, 2048, 8, 8
