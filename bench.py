@@ -5,7 +5,7 @@
 A step is one pass of the hot path over one batch of synthetic input already
 resident in HBM:
   prefill (default): mask/ternarize/pack W (per call), act_quant X, sparse
-                     ternary GEMM -> bf16 Y.  T=4096, R=6912, K=2560, 2:4,
+                     ternary GEMM -> bf16 Y (the one-call forward, sbn_forward).  T=4096, R=6912, K=2560, 2:4,
                      X with 1% outliers x20.
   train:             the same plus the dual-STE backward (dX, dW).
                      T=8192, R=11008, K=4096, 6:8, dY ~ N(0, 1e-2).
@@ -121,10 +121,8 @@ def make_forward_step(wl, n, m, with_backward=False):
     Xq = torch.empty((wl.T, wl.K), dtype=torch.int8, device="cuda")
     s_x = torch.empty(wl.T, dtype=torch.float32, device="cuda")
     Y = torch.empty((wl.T, wl.R), dtype=torch.bfloat16, device="cuda")
-    ws_pack = torch.empty(sbn.sbn_workspace_bytes(sbn.SBN_OP_PACK, 0, wl.R, wl.K, n, m), dtype=torch.uint8,
-                          device="cuda")
-    ws_gemm = torch.empty(max(sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM, wl.T, wl.R, wl.K, n, m), 256),
-                          dtype=torch.uint8, device="cuda")
+    ws_fwd = torch.empty(sbn.sbn_workspace_bytes(sbn.SBN_OP_FORWARD, wl.T, wl.R, wl.K, n, m), dtype=torch.uint8,
+                         device="cuda")
     extra = {}
     if with_backward:
         dY = bf16_dev(wl.upstream_grad(0))
@@ -135,10 +133,9 @@ def make_forward_step(wl, n, m, with_backward=False):
         extra = dict(dY=dY, dX=dX, dW=dW, ws_bwd=ws_bwd)
 
     def step():
-        sbn.sbn_mask_ternarize_pack(W, n, m, codes=codes, meta=meta if mb else None, s_w=s_w, ws=ws_pack)
-        sbn.sbn_act_quant(X, Xq=Xq, s_x=s_x)
-        sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta if mb else None, s_w, wl.R, n, m, ydt=sbn.SBN_BF16, Y=Y,
-                                    ws=ws_gemm)
+        # pack of W, quantization of X and the GEMM, as the one-call forward
+        sbn.sbn_forward(W, X, n, m, ydt=sbn.SBN_BF16, codes=codes, meta=meta if mb else None, s_w=s_w, Xq=Xq,
+                        s_x=s_x, Y=Y, ws=ws_fwd)
         if with_backward:
             sbn.sbn_backward(extra["dY"], Xq, s_x, codes, meta if mb else None, s_w, n, m, dxdt=sbn.SBN_BF16,
                              dX=extra["dX"], dW=extra["dW"], ws=extra["ws_bwd"])

@@ -100,7 +100,8 @@ typedef enum sbn_op {
   SBN_OP_ACT_QUANT = 1,
   SBN_OP_GEMM = 2,
   SBN_OP_GEMV = 3,
-  SBN_OP_BACKWARD = 4
+  SBN_OP_BACKWARD = 4,
+  SBN_OP_FORWARD = 5
 } sbn_op;
 
 /* ABI version of the loaded library (SBN_ABI_VERSION). */
@@ -226,6 +227,29 @@ sbn_status sbn_sparse_ternary_gemm(const int8_t* Xq, const float* s_x, int64_t T
                                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The whole forward of one Sparse-BitLinear call in one entry point:
+ *   sbn_mask_ternarize_pack_ex(W, ..., flags) ; sbn_act_quant(X, ...) ;
+ *   sbn_sparse_ternary_gemm(Xq, s_x, ..., Y)
+ * with the same results, bit for bit.  The activation quantizer does not
+ * depend on the weight pack; at 2:4 it runs in the same launch as the pack's
+ * second pass, side by side, which saves a launch and overlaps their memory
+ * traffic.
+ *
+ *   W      [R x K] bf16, row stride ldw >= K                    (in)
+ *   X      [T x K] bf16, row stride ldx >= K                    (in)
+ *   flags  0 or SBN_MASK_FROM_TERNARY
+ *   codes, meta, s_w                                            (out, as the pack)
+ *   Xq [T x K] int8 contiguous, s_x [T] float                   (out, as act_quant)
+ *   Y  [T x R] of dtype ydt, row stride ldy >= R                (out, as the GEMM)
+ *   ws workspace of sbn_workspace_bytes(SBN_OP_FORWARD, T, R, K, n, m)
+ * Limits and errors: those of the three calls.
+ */
+sbn_status sbn_forward(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, const uint16_t* X, int64_t T,
+                       int64_t ldx, int n, int m, uint32_t flags, uint8_t* codes, uint8_t* meta, float* s_w,
+                       int8_t* Xq, float* s_x, void* Y, sbn_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/*
  * Same operation as sbn_sparse_ternary_gemm for decode batches, 1 <= T <= 16:
  * streams the packed weight once from memory and unpacks it in registers.
  * ws: sbn_workspace_bytes(SBN_OP_GEMV, ...) (currently 0).
@@ -293,7 +317,7 @@ sbn_status sbn_backward_ex(const uint16_t* dY, int64_t T, int64_t R, const int8_
  * the stream it runs on.  sbn_profile_dump waits for the recorded events
  * and writes one line per kernel name, "name launches total_ms\n", into buf
  * (NUL-terminated, truncated to buf_bytes); sbn_profile_reset forgets them.
- * Kernel names: abs_sum, sgd_abs_sum, mask_pack, act_quant, layout_sparse, layout_dense,
+ * Kernel names: abs_sum, sgd_abs_sum, mask_pack, mask_pack_quant, act_quant, layout_sparse, layout_dense,
  * gemm_smfmac, gemm_mfma, gemv, gemv_stream_24, gemv_stream_68, expand_wt,
  * prep_u, prep_xq, gemm_dx, gemm_dw.
  * Errors: SBN_ERR_NULL (buf), SBN_ERR_HIP.

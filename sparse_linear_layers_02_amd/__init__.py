@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libsbn.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "sbn.h")
 
 SBN_F32, SBN_BF16, SBN_I32_ACC = 0, 1, 2
-SBN_OP_PACK, SBN_OP_ACT_QUANT, SBN_OP_GEMM, SBN_OP_GEMV, SBN_OP_BACKWARD = 0, 1, 2, 3, 4
+SBN_OP_PACK, SBN_OP_ACT_QUANT, SBN_OP_GEMM, SBN_OP_GEMV, SBN_OP_BACKWARD, SBN_OP_FORWARD = 0, 1, 2, 3, 4, 5
 SBN_FLAGS_NONE, SBN_MASK_FROM_TERNARY, SBN_GRAD_W_MASKED = 0, 1, 2
 STATUS = {0: "SBN_OK", 1: "SBN_ERR_NULL", 2: "SBN_ERR_SHAPE", 3: "SBN_ERR_UNSUPPORTED_NM",
           4: "SBN_ERR_ALIGN", 5: "SBN_ERR_WORKSPACE", 6: "SBN_ERR_DTYPE", 7: "SBN_ERR_HIP",
@@ -56,6 +56,8 @@ _SIGNATURES = {
                                  _vp, _sz, _vp], _int),
     "sbn_sparse_ternary_gemv": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _int, _int, _vp, _int, _i64,
                                  _vp, _sz, _vp], _int),
+    "sbn_forward": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _int, _int, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _int,
+                     _i64, _vp, _sz, _vp], _int),
     "sbn_sparse_ternary_gemv_batched": ([_vp, _vp, _i64, _i64, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                          ctypes.POINTER(_vp), _i64, _int, _int, ctypes.POINTER(_vp), _int,
                                          _i64, _i64, _vp], _int),
@@ -143,7 +145,7 @@ class Workspace:
         return self.buf
 
 
-_WS = {"pack": Workspace(), "gemm": Workspace(), "bwd": Workspace()}
+_WS = {"pack": Workspace(), "gemm": Workspace(), "bwd": Workspace(), "fwd": Workspace()}
 
 
 def _pack_outputs(W, n: int, m: int, codes, meta, s_w, ws):
@@ -242,6 +244,37 @@ def sbn_sparse_ternary_gemv(Xq, s_x, codes, meta, s_w, R: int, n: int, m: int, *
     return _matmul("sbn_sparse_ternary_gemv", Xq, s_x, codes, meta, s_w, R, n, m, ydt, Y, ws, stream)
 
 
+def sbn_forward(W, X, n: int, m: int, flags: int = 0, *, ydt: int = SBN_BF16, codes=None, meta=None, s_w=None,
+                Xq=None, s_x=None, Y=None, ws=None, stream=None):
+    """The whole forward (pack of W, quantization of X, sparse ternary GEMM) in
+    one call.  Returns (codes, meta, s_w, Xq, s_x, Y)."""
+    torch = _torch()
+    R, K = W.shape
+    T = X.shape[0]
+    cb, mb = sbn_packed_bytes(R, K, n, m)
+    dev = W.device
+    if codes is None:
+        codes = torch.empty(cb, dtype=torch.uint8, device=dev)
+    if meta is None and mb:
+        meta = torch.empty(mb, dtype=torch.uint8, device=dev)
+    if s_w is None:
+        s_w = torch.empty(1, dtype=torch.float32, device=dev)
+    if Xq is None:
+        Xq = torch.empty((T, K), dtype=torch.int8, device=dev)
+    if s_x is None:
+        s_x = torch.empty(T, dtype=torch.float32, device=dev)
+    if Y is None:                                    # row stride rounded up to 8 elements (the ABI's rule)
+        Y = torch.empty((T, (R + 7) // 8 * 8), dtype=getattr(torch, _YT[ydt]), device=dev)[:, :R]
+    need = sbn_workspace_bytes(SBN_OP_FORWARD, T, R, K, n, m)
+    if ws is None:
+        ws = _WS["fwd"].get(need, dev)
+    _check("sbn_forward",
+           lib().sbn_forward(_ptr(W), R, K, W.stride(0), _ptr(X), T, X.stride(0), n, m, flags, _ptr(codes),
+                             _ptr(meta), _ptr(s_w), _ptr(Xq), _ptr(s_x), _ptr(Y), ydt, Y.stride(0), _ptr(ws),
+                             ws.numel(), _stream(stream)))
+    return codes, meta, s_w, Xq, s_x, Y
+
+
 def sbn_sparse_ternary_gemv_batched(Xq, s_x, codes, metas, s_ws, R: int, n: int, m: int, *,
                                     ydt: int = SBN_BF16, Ys=None, stream=None):
     """sbn_sparse_ternary_gemv for several weights sharing Xq: codes, metas, s_ws
@@ -320,8 +353,8 @@ def sbn_profile_dump() -> dict:
 __all__ = [
     "lib", "header_symbols", "SbnError", "sbn_abi_version", "sbn_packed_bytes", "sbn_workspace_bytes",
     "sbn_mask_ternarize_pack", "sbn_act_quant", "sbn_sparse_ternary_gemm", "sbn_sparse_ternary_gemv",
-    "sbn_backward", "sbn_backward_ex", "sbn_mask_ternarize_pack_ex", "sbn_sgd_update_pack",
+    "sbn_backward", "sbn_backward_ex", "sbn_mask_ternarize_pack_ex", "sbn_sgd_update_pack", "sbn_forward",
     "SBN_FLAGS_NONE", "SBN_MASK_FROM_TERNARY", "SBN_GRAD_W_MASKED",
     "SBN_F32", "SBN_BF16", "SBN_I32_ACC", "SBN_OP_PACK", "SBN_OP_ACT_QUANT", "SBN_OP_GEMM",
-    "SBN_OP_GEMV", "SBN_OP_BACKWARD", "sbn_profile_enable", "sbn_profile_reset", "sbn_profile_dump",
+    "SBN_OP_GEMV", "SBN_OP_BACKWARD", "SBN_OP_FORWARD", "sbn_profile_enable", "sbn_profile_reset", "sbn_profile_dump",
 ]

@@ -291,6 +291,13 @@ sbn_status sbn_workspace_bytes(sbn_op op, int64_t T, int64_t R, int64_t K, int n
       SBN_TRY(check_k(K));
       *bytes = gemm_ws_bytes(T, R, K, n, m);
       return ok();
+    case SBN_OP_FORWARD:
+      SBN_TRY(check_nm(n, m));
+      SBN_TRY(check_rows("T", T));
+      SBN_TRY(check_rows("R", R));
+      SBN_TRY(check_k(K));
+      *bytes = align256(pack_plan(R, K).bytes) + gemm_ws_bytes(T, R, K, n, m);
+      return ok();
     case SBN_OP_BACKWARD:
       SBN_TRY(check_nm(n, m));
       SBN_TRY(check_rows("T", T));
@@ -383,6 +390,34 @@ sbn_status sbn_sparse_ternary_gemm(const int8_t* Xq, const float* s_x, int64_t T
   return hip_result(launch_gemm(Xq, s_x, T, K, codes, n == m ? nullptr : meta, s_w, R, n, m, Y,
                                 ydt, ldy, ws, st),
                     st, fn);
+}
+
+sbn_status sbn_forward(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, const uint16_t* X, int64_t T,
+                       int64_t ldx, int n, int m, uint32_t flags, uint8_t* codes, uint8_t* meta, float* s_w,
+                       int8_t* Xq, float* s_x, void* Y, sbn_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                       void* stream) {
+  const char* fn = "sbn_forward";
+  SBN_NONNULL(W);
+  SBN_NONNULL(X);
+  SBN_NONNULL(ws);
+  SBN_TRY(check_matmul_args(fn, Xq, s_x, T, K, codes, meta, s_w, R, n, m, Y, ydt, ldy));
+  SBN_TRY(check_ld("ldw", ldw, K));
+  SBN_TRY(check_ld("ldx", ldx, K));
+  if (flags & ~(uint32_t)SBN_MASK_FROM_TERNARY)
+    return fail(SBN_ERR_FLAGS, "%s: flags 0x%x: only SBN_MASK_FROM_TERNARY is accepted", fn, (unsigned)flags);
+  SBN_ALIGNED(W);
+  SBN_ALIGNED(X);
+  SBN_ALIGNED(ws);
+  const size_t pack_b = align256(pack_plan(R, K).bytes);
+  const size_t need = pack_b + gemm_ws_bytes(T, R, K, n, m);
+  if (ws_bytes < need)
+    return fail(SBN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* mp = n == m ? nullptr : meta;
+  hipError_t e = launch_pack_quant(W, R, K, ldw, n, m, codes, mp, s_w, ws, flags, X, T, ldx, Xq, s_x, st);
+  if (e == hipSuccess)
+    e = launch_gemm(Xq, s_x, T, K, codes, mp, s_w, R, n, m, Y, ydt, ldy, (uint8_t*)ws + pack_b, st);
+  return hip_result(e, st, fn);
 }
 
 sbn_status sbn_sparse_ternary_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,

@@ -38,7 +38,7 @@
 // fp32: a float64 estimate, and an exact comparison against the two
 // neighbouring midpoints whenever the estimate is too close to one of them
 // to decide.  The workspace needs no initialisation.
-#include "sbn_internal.h"
+#include "act_quant.h"
 
 namespace sbn {
 namespace {
@@ -250,12 +250,13 @@ __device__ inline void grad_at(const float* __restrict__ G, int64_t c, int64_t k
 
 // UPD: the optimizer step -- chunk c of W is first updated in place with the
 // gradient chunk of G (row stride ldg), nlr = -lr; the sum is of the new values.
+// Pass 1 as block `blk` of `nb` (the body of abs_sum_kernel and of the fused
+// pass-1 + activation-quantizer kernel).
 template <bool FLAT, bool UPD>
-__global__ __launch_bounds__(PT1) void abs_sum_kernel(const uint16_t* __restrict__ W, int64_t R,
-                                                     int64_t K, int64_t ldw, int64_t cpb,
-                                                     unsigned char* __restrict__ ws,
-                                                     const float* __restrict__ G, int64_t ldg, float nlr) {
-  const PackWs pw = pack_ws(ws, gridDim.x);
+__device__ inline void abs_sum_body(int64_t blk, int64_t nb, const uint16_t* __restrict__ W, int64_t R,
+                                    int64_t K, int64_t ldw, int64_t cpb, unsigned char* __restrict__ ws,
+                                    const float* __restrict__ G, int64_t ldg, float nlr) {
+  const PackWs pw = pack_ws(ws, nb);
   __shared__ unsigned long long bins[256];
   __shared__ unsigned long long red[PT1 / 64];
   __shared__ int any_slow;
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(PT1) void abs_sum_kernel(const uint16_t* __restrict
   if (tid == 0) any_slow = 0;
   __syncthreads();
   const int64_t kc = K / 8, total = R * kc;
-  const int64_t c0 = (int64_t)blockIdx.x * cpb;
+  const int64_t c0 = blk * cpb;
   const int64_t c1 = min(total, c0 + cpb);
   unsigned long long acc_i = 0;
   constexpr int64_t STEP = (int64_t)PT1 * U1;
@@ -343,11 +344,20 @@ __global__ __launch_bounds__(PT1) void abs_sum_kernel(const uint16_t* __restrict
   if (tid == 0) {
     unsigned long long b = 0;
     for (int i = 0; i < PT1 / 64; ++i) b += red[i];
-    pw.partials[blockIdx.x] = (long long)b;
-    pw.flags[blockIdx.x] = any_slow ? 1u : 0u;
+    pw.partials[blk] = (long long)b;
+    pw.flags[blk] = any_slow ? 1u : 0u;
   }
-  if (any_slow && tid < 256) pw.bins[(int64_t)blockIdx.x * 256 + tid] = bins[tid];
+  if (any_slow && tid < 256) pw.bins[blk * 256 + tid] = bins[tid];
 }
+
+template <bool FLAT, bool UPD>
+__global__ __launch_bounds__(PT1) void abs_sum_kernel(const uint16_t* __restrict__ W, int64_t R,
+                                                     int64_t K, int64_t ldw, int64_t cpb,
+                                                     unsigned char* __restrict__ ws,
+                                                     const float* __restrict__ G, int64_t ldg, float nlr) {
+  abs_sum_body<FLAT, UPD>(blockIdx.x, gridDim.x, W, R, K, ldw, cpb, ws, G, ldg, nlr);
+}
+
 
 // Block-wide (256 threads): total = sum of the pass-1 partials (2^-39 units)
 // + the flagged blocks' bins (sig * 2^(e-134) each), then
@@ -355,7 +365,7 @@ __global__ __launch_bounds__(PT1) void abs_sum_kernel(const uint16_t* __restrict
 // the <= a few hundred partials (the kernel boundary after pass 1 makes them
 // visible, so no device-scope fence is needed); block 0 also stores it.
 __device__ float scale_from_partials(const unsigned char* __restrict__ ws, int64_t nb, int64_t numel,
-                                     float* __restrict__ s_w_out) {
+                                     float* __restrict__ s_w_out, bool store) {
   const PackWs pw = pack_ws((unsigned char*)ws, nb);
   const int tid = threadIdx.x;
   __shared__ unsigned long long wlo[PT / 64], whi[PT / 64];
@@ -406,7 +416,7 @@ __device__ float scale_from_partials(const unsigned char* __restrict__ ws, int64
         if (ebin[e]) big_add_shifted(t, ebin[e], (e ? e : 1) - 1);
     const float sw = round_mean(t, (unsigned long long)numel);
     s_sh = sw;
-    if (blockIdx.x == 0) *s_w_out = sw;
+    if (store) *s_w_out = sw;
   }
   __syncthreads();
   return s_sh;
@@ -415,19 +425,19 @@ __device__ float scale_from_partials(const unsigned char* __restrict__ ws, int64
 // ------------------------------------------------------------------ pass 2
 // One thread = 32 consecutive weights of one row (32/M whole groups).
 template <int M>
-__global__ __launch_bounds__(PT) void mask_pack_kernel(
-    const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw, int n,
+__device__ inline void mask_pack_body(
+    int64_t blk, int64_t nblk, const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw, int n,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ meta, float* __restrict__ s_w_ptr,
     const unsigned char* __restrict__ ws, int64_t nb, int64_t total_chunks, int64_t dr, int64_t dch,
     int tmask) {
-  const float h = 0.5f * scale_from_partials(ws, nb, R * K, s_w_ptr);
+  const float h = 0.5f * scale_from_partials(ws, nb, R * K, s_w_ptr, blk == 0);
   const uint32_t thr = __float_as_uint(h) >> 16;      // |w| > h  <=>  key > thr
   const int64_t cpr = K / 32;
   const int64_t crow = K * n / (4 * M);               // code bytes per row
   const int cbc = 8 * n / M;                          // code bytes per chunk (M=8: n, M=4: 2n)
-  int64_t c = (int64_t)blockIdx.x * PT + threadIdx.x;
+  int64_t c = blk * PT + threadIdx.x;
   int64_t r = c / cpr, ch = c - r * cpr;
-  for (; c < total_chunks; c += (int64_t)gridDim.x * PT) {
+  for (; c < total_chunks; c += nblk * PT) {
     const uint4* src = (const uint4*)(W + r * ldw + ch * 32);
     const uint4 q0 = src[0], q1 = src[1], q2 = src[2], q3 = src[3];
     const uint32_t u[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
@@ -506,20 +516,20 @@ __device__ inline void group24(uint32_t w01, uint32_t w23, uint32_t thr, int tma
 }
 
 template <bool FLAT>
-__global__ __launch_bounds__(PT) void mask_pack24_kernel(
-    const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ meta, float* __restrict__ s_w_ptr, const unsigned char* __restrict__ ws,
-    int64_t nb, int tmask) {
+__device__ inline void mask_pack24_body(
+    int64_t blk, int64_t nblk, const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ meta, float* __restrict__ s_w_ptr,
+    const unsigned char* __restrict__ ws, int64_t nb, int tmask) {
   const int64_t kc = K / 8, total = R * kc;
-  const int64_t step = (int64_t)gridDim.x * PT * U;
-  int64_t base = (int64_t)blockIdx.x * PT * U + threadIdx.x;
+  const int64_t step = nblk * PT * U;
+  int64_t base = blk * PT * U + threadIdx.x;
   uint4 v[U], nx[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {                  // first loads fly while the scale is formed
     const int64_t c = base + (int64_t)u * PT;
     v[u] = c < total ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
   }
-  const float h = 0.5f * scale_from_partials(ws, nb, R * K, s_w_ptr);
+  const float h = 0.5f * scale_from_partials(ws, nb, R * K, s_w_ptr, blk == 0);
   const uint32_t thr = __float_as_uint(h) >> 16;
   for (; base < total; base += step) {
     if (base + step < total) {                   // next chunks load while these are packed
@@ -545,6 +555,57 @@ __global__ __launch_bounds__(PT) void mask_pack24_kernel(
   }
 }
 
+struct MaskPackArgs {
+  const uint16_t* W;
+  int64_t R, K, ldw;
+  int n;
+  uint8_t* codes;
+  uint8_t* meta;
+  float* s_w;
+  const unsigned char* ws;
+  int64_t nb, total_chunks, dr, dch;
+  int tmask;
+};
+
+// KIND: 0 = 2:4 with ldw == K, 1 = 2:4, 4 / 8 = any n of a group of 4 / 8.
+template <int KIND>
+__device__ inline void mask_pack_dispatch(int64_t blk, int64_t nblk, const MaskPackArgs& a) {
+  if constexpr (KIND == 0)
+    mask_pack24_body<true>(blk, nblk, a.W, a.R, a.K, a.ldw, a.codes, a.meta, a.s_w, a.ws, a.nb, a.tmask);
+  else if constexpr (KIND == 1)
+    mask_pack24_body<false>(blk, nblk, a.W, a.R, a.K, a.ldw, a.codes, a.meta, a.s_w, a.ws, a.nb, a.tmask);
+  else
+    mask_pack_body<KIND>(blk, nblk, a.W, a.R, a.K, a.ldw, a.n, a.codes, a.meta, a.s_w, a.ws, a.nb, a.total_chunks,
+                         a.dr, a.dch, a.tmask);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(PT) void mask_pack_kernel(const MaskPackArgs a) {
+  mask_pack_dispatch<KIND>(blockIdx.x, gridDim.x, a);
+}
+
+// The forward's pass 2: blocks [0, nblk) mask and pack W, blocks [nblk, nblk + T)
+// quantize one token each.  The quantizer does not depend on the pack, so one
+// grid runs them side by side (one launch, and the short token blocks fill the
+// compute units beside the pack's loop).
+struct QuantArgs {
+  const uint16_t* X;
+  int64_t T, K, ldx;
+  int8_t* Xq;
+  float* s_x;
+};
+
+template <int KIND, int CH>
+__global__ __launch_bounds__(PT) void mask_pack_quant_kernel(const MaskPackArgs a, int64_t nblk, const QuantArgs q) {
+  const int64_t b = blockIdx.x;
+  if (b < nblk) {
+    mask_pack_dispatch<KIND>(b, nblk, a);
+  } else {
+    __shared__ uint32_t qred[PT / 64];
+    act_quant_token<CH>(true, b - nblk, threadIdx.x, qred, q.X, q.K, q.ldx, q.Xq, q.s_x);
+  }
+}
+
 }  // namespace
 
 PackPlan pack_plan(int64_t R, int64_t K) {
@@ -560,6 +621,45 @@ PackPlan pack_plan(int64_t R, int64_t K) {
   p.chunks_per_block = cpb;
   p.bytes = align256((size_t)nb * 8) + align256((size_t)nb * 4) + align256((size_t)nb * 256 * 8);
   return p;
+}
+
+static MaskPackArgs mask_pack_args(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
+                                   uint8_t* codes, uint8_t* meta, float* s_w, const void* ws, uint32_t flags,
+                                   int64_t nb, int64_t& nblk, int& kind) {
+  MaskPackArgs a;
+  a.W = W; a.R = R; a.K = K; a.ldw = ldw; a.n = n;
+  a.codes = codes; a.meta = (n == m) ? nullptr : meta; a.s_w = s_w;
+  a.ws = (const unsigned char*)ws; a.nb = nb;
+  a.tmask = (flags & SBN_MASK_FROM_TERNARY) ? 1 : 0;
+  a.total_chunks = R * (K / 32);
+  if (n == 2 && m == 4) {
+    nblk = cdiv(R * (K / 8), (int64_t)PT * U);
+    if (nblk > 1024) nblk = 1024;                       // four blocks per CU, looping
+    kind = ldw == K ? 0 : 1;
+    a.dr = a.dch = 0;
+  } else {
+    nblk = cdiv(a.total_chunks, PT);
+    if (nblk > 8192) nblk = 8192;
+    const int64_t stride = nblk * PT, cpr = K / 32;
+    a.dr = stride / cpr;
+    a.dch = stride % cpr;
+    kind = m;
+  }
+  return a;
+}
+
+static hipError_t launch_mask_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
+                                   uint8_t* codes, uint8_t* meta, float* s_w, void* ws, uint32_t flags,
+                                   int64_t nb, hipStream_t st) {
+  int64_t nblk;
+  int kind;
+  const MaskPackArgs a = mask_pack_args(W, R, K, ldw, n, m, codes, meta, s_w, ws, flags, nb, nblk, kind);
+  const dim3 grid((unsigned)nblk), block(PT);
+  if (kind == 0) SBN_LAUNCH("mask_pack", mask_pack_kernel<0>, grid, block, 0, st, a);
+  else if (kind == 1) SBN_LAUNCH("mask_pack", mask_pack_kernel<1>, grid, block, 0, st, a);
+  else if (kind == 4) SBN_LAUNCH("mask_pack", mask_pack_kernel<4>, grid, block, 0, st, a);
+  else SBN_LAUNCH("mask_pack", mask_pack_kernel<8>, grid, block, 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
@@ -583,30 +683,43 @@ hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int
                (unsigned char*)ws, G, ldg, nlr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int tmask = (flags & SBN_MASK_FROM_TERNARY) ? 1 : 0;
-  const int64_t total = R * (K / 32);
-  int64_t blocks = cdiv(total, PT);
-  if (blocks > 8192) blocks = 8192;
-  const int64_t stride = blocks * PT;
-  const int64_t cpr = K / 32;
-  const int64_t dr = stride / cpr, dch = stride % cpr;
-  uint8_t* mp = (n == m) ? nullptr : meta;
-  if (n == 2 && m == 4) {
-    int64_t b24 = cdiv(R * (K / 8), (int64_t)PT * U);
-    if (b24 > 1024) b24 = 1024;                         // four blocks per CU, looping
-    if (ldw == K)
-      SBN_LAUNCH("mask_pack", mask_pack24_kernel<true>, dim3((unsigned)b24), dim3(PT), 0, st, W, R, K, ldw,
-                 codes, mp, s_w, (const unsigned char*)ws, p.nblocks, tmask);
-    else
-      SBN_LAUNCH("mask_pack", mask_pack24_kernel<false>, dim3((unsigned)b24), dim3(PT), 0, st, W, R, K, ldw,
-                 codes, mp, s_w, (const unsigned char*)ws, p.nblocks, tmask);
-  }
-  else if (m == 4)
-    SBN_LAUNCH("mask_pack", mask_pack_kernel<4>, dim3((unsigned)blocks), dim3(PT), 0, st, W, R, K, ldw,
-                       n, codes, mp, s_w, (const unsigned char*)ws, p.nblocks, total, dr, dch, tmask);
+  return launch_mask_pack(W, R, K, ldw, n, m, codes, meta, s_w, ws, flags, p.nblocks, st);
+}
+
+hipError_t launch_pack_quant(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
+                             uint8_t* codes, uint8_t* meta, float* s_w, void* ws, uint32_t flags,
+                             const uint16_t* X, int64_t T, int64_t ldx, int8_t* Xq, float* s_x, hipStream_t st) {
+  const PackPlan p = pack_plan(R, K);
+  if (ldw == K)
+    SBN_LAUNCH("abs_sum", (abs_sum_kernel<true, false>), dim3((unsigned)p.nblocks), dim3(PT1), 0, st, W, R, K, ldw,
+               p.chunks_per_block, (unsigned char*)ws, nullptr, 0, 0.0f);
   else
-    SBN_LAUNCH("mask_pack", mask_pack_kernel<8>, dim3((unsigned)blocks), dim3(PT), 0, st, W, R, K, ldw,
-                       n, codes, mp, s_w, (const unsigned char*)ws, p.nblocks, total, dr, dch, tmask);
+    SBN_LAUNCH("abs_sum", (abs_sum_kernel<false, false>), dim3((unsigned)p.nblocks), dim3(PT1), 0, st, W, R, K, ldw,
+               p.chunks_per_block, (unsigned char*)ws, nullptr, 0, 0.0f);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t nblk;
+  int kind;
+  const MaskPackArgs a = mask_pack_args(W, R, K, ldw, n, m, codes, meta, s_w, ws, flags, p.nblocks, nblk, kind);
+  if (kind > 1) {
+    // the rank-count pass of other ratios fills the chip by itself (up to 8192
+    // blocks): the quantizer gains nothing beside it and runs after it
+    e = launch_mask_pack(W, R, K, ldw, n, m, codes, meta, s_w, ws, flags, p.nblocks, st);
+    return e != hipSuccess ? e : launch_act_quant(X, T, K, ldx, Xq, s_x, st);
+  }
+  const QuantArgs q{X, T, K, ldx, Xq, s_x};
+  const dim3 grid((unsigned)(nblk + T)), block(PT);
+  const int ch = act_quant_ch(K);
+#define SBN_MPQ(KIND)                                                                                          \
+  do {                                                                                                         \
+    if (ch == 1) SBN_LAUNCH("mask_pack_quant", (mask_pack_quant_kernel<KIND, 1>), grid, block, 0, st, a, nblk, q); \
+    else if (ch == 2) SBN_LAUNCH("mask_pack_quant", (mask_pack_quant_kernel<KIND, 2>), grid, block, 0, st, a, nblk, q); \
+    else if (ch == 4) SBN_LAUNCH("mask_pack_quant", (mask_pack_quant_kernel<KIND, 4>), grid, block, 0, st, a, nblk, q); \
+    else SBN_LAUNCH("mask_pack_quant", (mask_pack_quant_kernel<KIND, 0>), grid, block, 0, st, a, nblk, q);  \
+  } while (0)
+  if (kind == 0) SBN_MPQ(0);
+  else SBN_MPQ(1);
+#undef SBN_MPQ
   return hipGetLastError();
 }
 

@@ -101,6 +101,11 @@ hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int
                        const float* G, int64_t ldg, float lr, hipStream_t st);
 hipError_t launch_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, int8_t* Xq,
                             float* s_x, hipStream_t st);
+// The pack and the activation quantizer of one forward, with pass 1 of the pack
+// and the quantizer in one launch (same results as launch_pack + launch_act_quant).
+hipError_t launch_pack_quant(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
+                             uint8_t* codes, uint8_t* meta, float* s_w, void* ws, uint32_t flags,
+                             const uint16_t* X, int64_t T, int64_t ldx, int8_t* Xq, float* s_x, hipStream_t st);
 hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                        const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
                        int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, void* ws, hipStream_t st);

@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = sbn.header_symbols()
-    assert len(names) == 17
+    assert len(names) == 18
     for nm in names:
         assert hasattr(L, nm), nm
 
@@ -192,3 +192,20 @@ def test_backward_ex_validation(L):
     assert f(P, 16, 256, P, P, 256, P, P, P, 2, 4, P, 0, P, 1, P, big, None) == FLAGS      # a pack flag
     assert f(P, 16, 256, P, P, 256, P, None, P, 2, 4, P, 0, P, 2, P, big, None) == NULL    # meta needed
     assert f(P, 16, 250, P, P, 256, P, P, P, 2, 4, P, 0, P, 2, P, big, None) == SHAPE      # R % 8
+
+
+def test_forward_validation(L):
+    f = L.sbn_forward
+    big = 1 << 30
+    # W, R, K, ldw, X, T, ldx, n, m, flags, codes, meta, s_w, Xq, s_x, Y, ydt, ldy, ws, ws_bytes, stream
+    assert f(None, 64, 256, 256, P, 16, 256, 2, 4, 0, P, P, P, P, P, P, 1, 64, P, big, None) == NULL
+    assert f(P, 64, 256, 256, None, 16, 256, 2, 4, 0, P, P, P, P, P, P, 1, 64, P, big, None) == NULL
+    assert f(P, 64, 256, 256, P, 16, 256, 2, 4, 0, P, None, P, P, P, P, 1, 64, P, big, None) == NULL
+    assert f(P, 64, 256, 128, P, 16, 256, 2, 4, 0, P, P, P, P, P, P, 1, 64, P, big, None) == SHAPE   # ldw
+    assert f(P, 64, 256, 256, P, 16, 260, 2, 4, 0, P, P, P, P, P, P, 1, 64, P, big, None) == ALIGN   # ldx
+    assert f(P, 64, 256, 256, P, 16, 256, 2, 4, 2, P, P, P, P, P, P, 1, 64, P, big, None) == FLAGS
+    assert f(P, 64, 256, 256, P, 16, 256, 2, 4, 0, P, P, P, P, P, P, 9, 64, P, big, None) == DTYPE
+    assert f(P, 64, 256, 256, P, 16, 256, 2, 4, 0, P, P, P, P, P, P, 1, 64, P, 64, None) == WS
+    need = sbn.sbn_workspace_bytes(sbn.SBN_OP_FORWARD, 16, 64, 256, 2, 4)
+    assert need >= sbn.sbn_workspace_bytes(sbn.SBN_OP_PACK, 0, 64, 256, 2, 4) + \
+        sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM, 16, 64, 256, 2, 4)

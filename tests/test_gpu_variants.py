@@ -1,7 +1,7 @@
 """GPU parity of the variants beside the path, through the C ABI, against the
 CPU oracle: the two ablations (mask from the ternary weights; gradient
-blocked at pruned positions) and the SGD master-weight step fused with the
-next pack.  Bars as in test_gpu_parity.py: packed planes, scales and updated
+blocked at pruned positions), the SGD master-weight step fused with the
+next pack, and the one-call forward.  Bars as in test_gpu_parity.py: packed planes, scales and updated
 bf16 weights bit for bit; gradients within the float32 accumulation bound.
 """
 from __future__ import annotations
@@ -173,3 +173,60 @@ def test_sgd_update_pack_train_size():
     W = wl.weights(seed=0)
     G = np.random.default_rng([0, 9]).standard_normal(W.shape).astype(np.float32) * np.float32(1e-2)
     check_sgd(W, G, 1e-2, n, m)
+
+
+# ------------------------------------------------------------------ the one-call forward
+def check_forward(T, R, K, n, m, flags=0, ldw=None, ldx=None, seed=0, ydt=None):
+    import torch
+    W = gaussian_bf16((R, K), 0.02, seed=seed, stream=0)
+    X = gaussian_bf16((T, K), 1.0, seed=seed, stream=1)
+    Wd = padded(W, ldw, np.uint16(0x7F00))
+    Xd = padded(X, ldx, np.uint16(0x7F00))
+    ydt = sbn.SBN_I32_ACC if ydt is None else ydt
+    codes, meta, s_w, Xq, s_x, Y = sbn.sbn_forward(Wd, Xd, n, m, flags, ydt=ydt)
+    torch.cuda.synchronize()
+    mask_from = "ternary" if flags & sbn.SBN_MASK_FROM_TERNARY else "master"
+    eff, mask, sw = compare_planes(codes, meta, s_w, W, n, m, mask_from)
+    xq, sx = O.act_quant(X)
+    assert np.array_equal(host(Xq), xq)
+    assert np.array_equal(f32_bits(host(s_x)), f32_bits(sx))
+    acc = O.accumulate(xq, eff)
+    if ydt == sbn.SBN_I32_ACC:
+        assert np.array_equal(host(Y).astype(np.int64), acc)
+    else:
+        y = O.output(acc, sw, sx)
+        got = host(Y)
+        got = bf16_bits_to_f64(got) if ydt == sbn.SBN_BF16 else got
+        rel = 2.0 ** -8 + 2.0 ** -20 if ydt == sbn.SBN_BF16 else 1e-3
+        assert (np.abs(got - y) <= rel * np.abs(y)).all()
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (1, 8), (8, 8)])
+def test_forward_matches_oracle(n, m):
+    check_forward(37, 264, 320, n, m, seed=n + m)                 # T not a multiple of the 4 tokens per block
+
+
+@pytest.mark.parametrize("K", [64, 2560, 8192, 16384])
+def test_forward_token_lengths(K):
+    # one, two and four 16-byte chunks per thread, and the two-pass quantizer beyond K = 8192
+    check_forward(6, 40, K, 2, 4, seed=K)
+
+
+def test_forward_leading_dims_flags_and_outputs():
+    check_forward(21, 96, 256, 6, 8, ldw=264, ldx=272, seed=3)
+    check_forward(21, 96, 256, 2, 4, flags=sbn.SBN_MASK_FROM_TERNARY, seed=4)
+    check_forward(50, 520, 576, 2, 4, seed=5, ydt=sbn.SBN_BF16)
+    check_forward(50, 520, 576, 6, 8, seed=6, ydt=sbn.SBN_F32)
+
+
+def test_forward_prefill_size_equals_separate_calls():
+    import torch
+    wl = WORKLOADS["prefill"]
+    W, X = dev_bf16(wl.weights(0)), dev_bf16(wl.activations(0))
+    a = sbn.sbn_forward(W, X, 2, 4)
+    codes, meta, s_w = sbn.sbn_mask_ternarize_pack(W, 2, 4)
+    Xq, s_x = sbn.sbn_act_quant(X)
+    Y = sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, wl.R, 2, 4)
+    torch.cuda.synchronize()
+    for x, y in zip(a, (codes, meta, s_w, Xq, s_x, Y)):
+        assert torch.equal(x, y)
