@@ -34,6 +34,8 @@ readings below (each is repeated at the function that uses it):
   * the two ablation variants ([de] §4 "Ablationsstudien", [fr] §5): the
     mask taken from |q| of the ternary weights (ties to the lower index),
     and grad_W blocked at pruned positions (grad_W * mask);
+  * a decode plane (pack_d2, not on the pages): the effective ternary
+    weights as one 2-bit code per position, for memory-bound decode;
   * the master-weight optimizer step ([ja] §2.1: BF16 master weights are
     kept and receive the gradients; no optimizer is named): plain SGD,
     w' = bf16(fl32(w - lr*g)) with fl32 one rounding of the exact value
@@ -65,7 +67,7 @@ __all__ = [
     "weight_scale", "ternary_codes", "quant_then_mask", "packed_bytes",
     "pack_sbn1", "act_quant", "accumulate", "output", "backward",
     "forward", "S_FLOOR", "QMAX", "nm_mask_ternary", "fma_f32", "f32_to_bf16_rne",
-    "sgd_update",
+    "sgd_update", "pack_d2", "unpack_d2",
 ]
 
 
@@ -246,6 +248,37 @@ def pack_sbn1(codes: np.ndarray, mask: np.ndarray, n: int, m: int):
     else:
         meta_plane = np.packbits(mask.astype(np.uint8), axis=1, bitorder="little")
     return codes_plane, meta_plane
+
+
+# --------------------------------------------------------------------------- decode plane
+def pack_d2(codes: np.ndarray) -> np.ndarray:
+    """Decode plane of an effective ternary weight (any N:M; pruned entries 0).
+
+    Not a format of the pages: a byte-lean form for memory-bound decode (at
+    6:8 the packed planes hold 2.5 bits per weight, a dense 2-bit ternary
+    code 2).  Codes as in pack_sbn1 (00 = 0, 01 = +1, 11 = -1), one per
+    position, no bitmap.  Row r is K/16 little-endian 32-bit words; word w
+    holds positions 16w .. 16w + 15, position 16w + 4k + b (k, b in 0..3) in
+    bits 8b + 6 - 2k (low) and 8b + 7 - 2k (high) -- so that shifting the word
+    left by 2k and masking 0xC0C0C0C0 leaves positions 4k .. 4k + 3 as 64 * w,
+    one per byte, in order.  Returns uint8 [R, K/4].
+    """
+    R, K = codes.shape
+    assert K % 16 == 0
+    c2 = np.where(codes == 1, 1, np.where(codes == -1, 3, 0)).astype(np.uint32)
+    c = c2.reshape(R, K // 16, 4, 4)                    # [r, w, k, b]
+    shift = 8 * np.arange(4)[None, None, None, :] + 6 - 2 * np.arange(4)[None, None, :, None]
+    words = (c << shift.astype(np.uint32)).sum(axis=(2, 3)).astype(np.uint32)   # disjoint bit fields
+    return words.astype("<u4").view(np.uint8).reshape(R, K // 4)
+
+
+def unpack_d2(plane: np.ndarray, R: int, K: int) -> np.ndarray:
+    """Inverse of pack_d2: int8 [R, K] ternary weights."""
+    words = np.ascontiguousarray(plane[:, : K // 4]).view("<u4").reshape(R, K // 16, 1, 1)
+    shift = 8 * np.arange(4)[None, None, None, :] + 6 - 2 * np.arange(4)[None, None, :, None]
+    c = (words >> shift.astype(np.uint32)) & 3
+    w = np.where(c == 1, 1, np.where(c == 3, -1, 0)).astype(np.int8)
+    return w.reshape(R, K)
 
 
 # --------------------------------------------------------------------------- activations

@@ -280,3 +280,38 @@ def sgd_matches_exact(sgd_fn, W, G, lr) -> bool:
         if _bf16_value(int(got[idx])) != want:
             return False
     return True
+
+
+# ------------------------------------------------------------------ decode plane
+def d2_by_loops(codes):
+    """Bit-by-bit construction of the decode plane: position 16w + 4k + b of a
+    row goes to bits 8b + 6 - 2k (low) and 8b + 7 - 2k (high) of word w."""
+    R, K = codes.shape
+    enc = {0: 0, 1: 1, -1: 3}
+    out = np.zeros((R, K // 4), dtype=np.uint8)
+    for r in range(R):
+        for w in range(K // 16):
+            word = 0
+            for k in range(4):
+                for b in range(4):
+                    word |= enc[int(codes[r, 16 * w + 4 * k + b])] << (8 * b + 6 - 2 * k)
+            for i in range(4):
+                out[r, 4 * w + i] = (word >> (8 * i)) & 0xFF
+    return out
+
+
+def d2_decode_matches(plane, codes) -> bool:
+    """The decode the kernels use: (word << 2k) & 0xC0C0C0C0 holds positions
+    4k .. 4k + 3 of the word as 64 * w, one signed byte each, in order."""
+    R, K = codes.shape
+    for r in range(R):
+        for w in range(K // 16):
+            word = int.from_bytes(bytes(plane[r, 4 * w: 4 * w + 4]), "little")
+            for k in range(4):
+                v = ((word << (2 * k)) & 0xC0C0C0C0) & 0xFFFFFFFF
+                for b in range(4):
+                    byte = (v >> (8 * b)) & 0xFF
+                    sv = byte - 256 if byte >= 128 else byte
+                    if sv != 64 * int(codes[r, 16 * w + 4 * k + b]):
+                        return False
+    return True

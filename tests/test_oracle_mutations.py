@@ -281,3 +281,23 @@ def test_sgd_mutants_are_caught(mutant):
     W = np.concatenate([W, f32_to_bf16_bits(np.full((1, 40), 1.0, np.float32))], axis=0)
     G = np.concatenate([G, np.full((1, 40), -2.0 ** -8, np.float32)], axis=0)
     assert not pins.sgd_matches_exact(mutant, W, G, np.float32(1.0))
+
+
+# ----------------------------------------------------------------- decode plane
+def _d2_position_major(codes):
+    R, K = codes.shape
+    c2 = np.where(codes == 1, 1, np.where(codes == -1, 3, 0)).astype(np.uint8)
+    bits = np.stack([c2 & 1, (c2 >> 1) & 1], axis=-1).reshape(R, -1)
+    return np.packbits(bits, axis=1, bitorder="little")          # the packed-plane order, not the decode order
+
+
+def _d2_swapped_code(codes):
+    return O.pack_d2(-codes)
+
+
+@pytest.mark.parametrize("mutant", [_d2_position_major, _d2_swapped_code])
+def test_d2_mutants_are_caught(mutant):
+    W = gaussian_bf16((4, 64), 0.02, seed=17, stream=0)
+    codes, _, _ = O.quant_then_mask(W, 6, 8)
+    plane = mutant(codes)
+    assert not (np.array_equal(plane, pins.d2_by_loops(codes)) and pins.d2_decode_matches(plane, codes))

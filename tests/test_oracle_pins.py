@@ -383,3 +383,26 @@ def test_sgd_update_identities():
     one = f32_to_bf16_bits(np.array([[1.0, 1.0]], dtype=np.float32))
     out = O.sgd_update(one, np.array([[1.0, -2.0]], dtype=np.float32), np.float32(0.5))
     assert bf16_bits_to_f32(out).tolist() == [[0.5, 2.0]]
+
+
+# ----------------------------------------------------------------- decode plane
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (8, 8), (1, 8)])
+def test_d2_matches_bit_loops_and_decode(n, m):
+    W = gaussian_bf16((5, 64), 0.02, seed=17, stream=0)
+    codes, mask, sw = O.quant_then_mask(W, n, m)
+    plane = O.pack_d2(codes)
+    assert np.array_equal(plane, pins.d2_by_loops(codes))
+    assert pins.d2_decode_matches(plane, codes)
+    assert np.array_equal(O.unpack_d2(plane, 5, 64), codes)
+    # the 2:4 bytes equal those of the packed planes; 6:8 is smaller
+    cb, mb = O.packed_bytes(5, 64, n, m)
+    assert plane.size == 5 * 64 // 4 and (plane.size < cb + mb if (n, m) == (6, 8) else True)
+
+
+def test_d2_worked_word():
+    # one row of 16: +1 at position 0, -1 at position 5 (k=1, b=1), +1 at 15 (k=3, b=3)
+    codes = np.zeros((1, 16), np.int8)
+    codes[0, 0], codes[0, 5], codes[0, 15] = 1, -1, 1
+    # position 0 -> bits 6,7 of byte 0 (code 01 -> 0x40); position 5 -> bits 4,5 of byte 1
+    # (code 11 -> 0x30); position 15 -> bits 0,1 of byte 3 (code 01 -> 0x01)
+    assert O.pack_d2(codes).tolist() == [[0x40, 0x30, 0x00, 0x01]]
