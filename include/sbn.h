@@ -280,6 +280,35 @@ sbn_status sbn_sparse_ternary_gemv_batched(const int8_t* Xq, const float* s_x, i
                                            void* stream);
 
 /*
+ * Decode plane: a byte-lean form of a packed weight for memory-bound decode
+ * (not a format of the pages; at 6:8 the packed planes hold 2.5 bits per
+ * weight, the decode plane 2).  It holds the effective ternary weights (pruned
+ * positions 0) at one 2-bit code per position (00 = 0, 01 = +1, 11 = -1), no
+ * bitmap: row r is K/16 little-endian 32-bit words, word w holds positions
+ * 16w .. 16w+15, position 16w + 4k + b (k, b in 0..3) in bits 8b + 6 - 2k
+ * (low) and 8b + 7 - 2k (high).  Row stride K/4 bytes.
+ *
+ * sbn_decode_plane_bytes: R*K/4 rounded up to 16 (host-only).
+ * sbn_repack_d2: packed planes (codes, meta of an n:m weight; meta NULL when
+ *   n == m) -> decode plane d2 of sbn_decode_plane_bytes(R, K) bytes.
+ * sbn_ternary_gemv_d2: the decode GEMV of sbn_sparse_ternary_gemv on a decode
+ *   plane, 1 <= T <= 16, same results (Y as there; s_w the weight's scale).
+ * sbn_ternary_gemv_d2_batched: the same over `count` planes sharing the
+ *   activations, one launch (K a multiple of 1024 up to 4096; else one launch
+ *   per plane); d2, s_w and Y are HOST arrays of device pointers.
+ * Errors: as the packed-weight calls; SBN_ERR_SHAPE for count outside
+ * [1, SBN_GEMV_MAX_BATCH].
+ */
+sbn_status sbn_decode_plane_bytes(int64_t R, int64_t K, size_t* bytes);
+sbn_status sbn_repack_d2(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, int n, int m,
+                         uint8_t* d2, void* stream);
+sbn_status sbn_ternary_gemv_d2(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const uint8_t* d2,
+                               const float* s_w, int64_t R, void* Y, sbn_dtype ydt, int64_t ldy, void* stream);
+sbn_status sbn_ternary_gemv_d2_batched(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                       const uint8_t* const* d2, const float* const* s_w, int64_t R,
+                                       void* const* Y, sbn_dtype ydt, int64_t ldy, int64_t count, void* stream);
+
+/*
  * Dual-STE backward of Sparse-BitLinear (ja §2.1, de §2 "Dual STE",
  * ko §2.2, fr §2): identity Jacobian through both quantizers and a dense
  * gradient through the mask, so every master weight receives a gradient.
@@ -318,7 +347,7 @@ sbn_status sbn_backward_ex(const uint16_t* dY, int64_t T, int64_t R, const int8_
  * and writes one line per kernel name, "name launches total_ms\n", into buf
  * (NUL-terminated, truncated to buf_bytes); sbn_profile_reset forgets them.
  * Kernel names: abs_sum, sgd_abs_sum, mask_pack, mask_pack_quant, act_quant, layout_sparse, layout_dense,
- * gemm_smfmac, gemm_mfma, gemv, gemv_stream_24, gemv_stream_68, expand_wt,
+ * gemm_smfmac, gemm_mfma, gemv, gemv_stream_24, gemv_stream_68, repack_d2, gemv_stream_d2, gemv_d2, expand_wt,
  * prep_u, prep_xq, gemm_dx, gemm_dw.
  * Errors: SBN_ERR_NULL (buf), SBN_ERR_HIP.
  */

@@ -56,6 +56,11 @@ _SIGNATURES = {
                                  _vp, _sz, _vp], _int),
     "sbn_sparse_ternary_gemv": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _int, _int, _vp, _int, _i64,
                                  _vp, _sz, _vp], _int),
+    "sbn_decode_plane_bytes": ([_i64, _i64, ctypes.POINTER(_sz)], _int),
+    "sbn_repack_d2": ([_vp, _vp, _i64, _i64, _int, _int, _vp, _vp], _int),
+    "sbn_ternary_gemv_d2": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _int, _i64, _vp], _int),
+    "sbn_ternary_gemv_d2_batched": ([_vp, _vp, _i64, _i64, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64,
+                                     ctypes.POINTER(_vp), _int, _i64, _i64, _vp], _int),
     "sbn_forward": ([_vp, _i64, _i64, _i64, _vp, _i64, _i64, _int, _int, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _int,
                      _i64, _vp, _sz, _vp], _int),
     "sbn_sparse_ternary_gemv_batched": ([_vp, _vp, _i64, _i64, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
@@ -275,6 +280,47 @@ def sbn_forward(W, X, n: int, m: int, flags: int = 0, *, ydt: int = SBN_BF16, co
     return codes, meta, s_w, Xq, s_x, Y
 
 
+def sbn_decode_plane_bytes(R: int, K: int) -> int:
+    b = _sz()
+    _check("sbn_decode_plane_bytes", lib().sbn_decode_plane_bytes(R, K, ctypes.byref(b)))
+    return b.value
+
+
+def sbn_repack_d2(codes, meta, R: int, K: int, n: int, m: int, *, d2=None, stream=None):
+    """Decode plane (uint8, sbn_decode_plane_bytes(R, K)) of a packed n:m weight."""
+    torch = _torch()
+    if d2 is None:
+        d2 = torch.empty(sbn_decode_plane_bytes(R, K), dtype=torch.uint8, device=codes.device)
+    _check("sbn_repack_d2", lib().sbn_repack_d2(_ptr(codes), _ptr(meta), R, K, n, m, _ptr(d2), _stream(stream)))
+    return d2
+
+
+def sbn_ternary_gemv_d2(Xq, s_x, d2, s_w, R: int, *, ydt: int = SBN_BF16, Y=None, stream=None):
+    """Decode GEMV (T <= 16) on a decode plane.  Returns Y [T, R]."""
+    torch = _torch()
+    T, K = Xq.shape
+    if Y is None:                                    # row stride rounded up to 8 elements (the ABI's rule)
+        Y = torch.empty((T, (R + 7) // 8 * 8), dtype=getattr(torch, _YT[ydt]), device=Xq.device)[:, :R]
+    _check("sbn_ternary_gemv_d2", lib().sbn_ternary_gemv_d2(_ptr(Xq), _ptr(s_x), T, K, _ptr(d2), _ptr(s_w), R, _ptr(Y),
+                                                          ydt, Y.stride(0), _stream(stream)))
+    return Y
+
+
+def sbn_ternary_gemv_d2_batched(Xq, s_x, d2s, s_ws, R: int, *, ydt: int = SBN_BF16, Ys=None, stream=None):
+    """sbn_ternary_gemv_d2 over several planes sharing Xq (lists of tensors).  Returns the list of Y."""
+    torch = _torch()
+    T, K = Xq.shape
+    count = len(d2s)
+    if Ys is None:
+        ld = (R + 7) // 8 * 8
+        Ys = [torch.empty((T, ld), dtype=getattr(torch, _YT[ydt]), device=Xq.device)[:, :R] for _ in range(count)]
+    arr = lambda ts: (_vp * max(count, 1))(*[t.data_ptr() for t in ts])
+    _check("sbn_ternary_gemv_d2_batched",
+           lib().sbn_ternary_gemv_d2_batched(_ptr(Xq), _ptr(s_x), T, K, arr(d2s), arr(s_ws), R, arr(Ys), ydt,
+                                             Ys[0].stride(0) if count else R, count, _stream(stream)))
+    return Ys
+
+
 def sbn_sparse_ternary_gemv_batched(Xq, s_x, codes, metas, s_ws, R: int, n: int, m: int, *,
                                     ydt: int = SBN_BF16, Ys=None, stream=None):
     """sbn_sparse_ternary_gemv for several weights sharing Xq: codes, metas, s_ws
@@ -354,6 +400,7 @@ __all__ = [
     "lib", "header_symbols", "SbnError", "sbn_abi_version", "sbn_packed_bytes", "sbn_workspace_bytes",
     "sbn_mask_ternarize_pack", "sbn_act_quant", "sbn_sparse_ternary_gemm", "sbn_sparse_ternary_gemv",
     "sbn_backward", "sbn_backward_ex", "sbn_mask_ternarize_pack_ex", "sbn_sgd_update_pack", "sbn_forward",
+    "sbn_decode_plane_bytes", "sbn_repack_d2", "sbn_ternary_gemv_d2", "sbn_ternary_gemv_d2_batched",
     "SBN_FLAGS_NONE", "SBN_MASK_FROM_TERNARY", "SBN_GRAD_W_MASKED",
     "SBN_F32", "SBN_BF16", "SBN_I32_ACC", "SBN_OP_PACK", "SBN_OP_ACT_QUANT", "SBN_OP_GEMM",
     "SBN_OP_GEMV", "SBN_OP_BACKWARD", "SBN_OP_FORWARD", "sbn_profile_enable", "sbn_profile_reset", "sbn_profile_dump",

@@ -509,6 +509,84 @@ sbn_status sbn_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_t* 
                          ws_bytes, stream);
 }
 
+sbn_status sbn_decode_plane_bytes(int64_t R, int64_t K, size_t* bytes) {
+  const char* fn = "sbn_decode_plane_bytes";
+  SBN_NONNULL(bytes);
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  *bytes = (size_t)round_up(R * K / 4, 16);
+  return ok();
+}
+
+sbn_status sbn_repack_d2(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, int n, int m,
+                         uint8_t* d2, void* stream) {
+  const char* fn = "sbn_repack_d2";
+  SBN_NONNULL(codes);
+  SBN_NONNULL(d2);
+  SBN_TRY(check_nm(n, m));
+  if (n < m) SBN_NONNULL(meta);
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  SBN_ALIGNED(codes);
+  if (n < m) SBN_ALIGNED(meta);
+  SBN_ALIGNED(d2);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_repack_d2(codes, n == m ? nullptr : meta, R, K, n, m, d2, st), st, fn);
+}
+
+static sbn_status check_d2_args(const char* fn, const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                const uint8_t* d2, const float* s_w, int64_t R, void* Y, sbn_dtype ydt,
+                                int64_t ldy) {
+  SBN_NONNULL(Xq);
+  SBN_NONNULL(s_x);
+  SBN_NONNULL(d2);
+  SBN_NONNULL(s_w);
+  SBN_NONNULL(Y);
+  SBN_TRY(check_rows("T", T));
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  if (T > 16) return fail(SBN_ERR_SHAPE, "%s: T = %lld exceeds 16", fn, (long long)T);
+  SBN_TRY(check_ld("ldy", ldy, R));
+  if (ydt != SBN_F32 && ydt != SBN_BF16 && ydt != SBN_I32_ACC)
+    return fail(SBN_ERR_DTYPE, "%s: unknown output dtype %d", fn, (int)ydt);
+  SBN_ALIGNED(Xq);
+  SBN_ALIGNED(d2);
+  SBN_ALIGNED(Y);
+  return SBN_OK;
+}
+
+sbn_status sbn_ternary_gemv_d2(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const uint8_t* d2,
+                               const float* s_w, int64_t R, void* Y, sbn_dtype ydt, int64_t ldy, void* stream) {
+  const char* fn = "sbn_ternary_gemv_d2";
+  SBN_TRY(check_d2_args(fn, Xq, s_x, T, K, d2, s_w, R, Y, ydt, ldy));
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_gemv_d2_batched(Xq, s_x, T, K, &d2, &s_w, R, &Y, ydt, ldy, 1, st), st, fn);
+}
+
+sbn_status sbn_ternary_gemv_d2_batched(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                       const uint8_t* const* d2, const float* const* s_w, int64_t R,
+                                       void* const* Y, sbn_dtype ydt, int64_t ldy, int64_t count, void* stream) {
+  const char* fn = "sbn_ternary_gemv_d2_batched";
+  SBN_NONNULL(d2);
+  SBN_NONNULL(s_w);
+  SBN_NONNULL(Y);
+  if (count < 1 || count > SBN_GEMV_MAX_BATCH)
+    return fail(SBN_ERR_SHAPE, "%s: count = %lld must be in [1, %d]", fn, (long long)count, SBN_GEMV_MAX_BATCH);
+  for (int64_t b = 0; b < count; ++b) {
+    const sbn_status st_b = check_d2_args(fn, Xq, s_x, T, K, d2[b], s_w[b], R, Y[b], ydt, ldy);
+    if (st_b != SBN_OK) {
+      char msg[512];
+      snprintf(msg, sizeof(msg), "%s (weight %lld)", sbn_last_error(), (long long)b);
+      return fail(st_b, "%s", msg);
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_gemv_d2_batched(Xq, s_x, T, K, d2, s_w, R, Y, ydt, ldy, (int)count, st), st, fn);
+}
+
 sbn_status sbn_backward_ex(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
                            const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
                            const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,

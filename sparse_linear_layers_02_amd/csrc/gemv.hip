@@ -293,6 +293,8 @@ struct StreamOut {
 // still reads whole 128-byte row segments.
 struct Dec24 {
   static constexpr int SLOT = 4096, NDMA = 4, LUT = 0, BPC = 4;   // BPC: resident blocks per CU (40 KB LDS each)
+  __host__ __device__ static int64_t meta_row(int64_t K) { return K / 8; }
+  __host__ __device__ static int64_t code_row(int64_t K) { return K / 8; }
   int rowq[2], colq[2];
   v4i blo[8], bhi[8];
   __device__ inline void init(int wave, int lane) {
@@ -380,6 +382,8 @@ __device__ inline v4i lut68_entry(uint32_t mb) {
 
 struct Dec68 {
   static constexpr int SLOT = 2048 + 3072, NDMA = 5, LUT = 4096, BPC = 3;   // 52 KB LDS per block
+  __host__ __device__ static int64_t meta_row(int64_t K) { return K / 8; }
+  __host__ __device__ static int64_t code_row(int64_t K) { return K * 3 / 16; }
   int rowA[5], colA[5];
   v4i bx[16];
   __device__ inline void init(int wave, int lane) {
@@ -450,6 +454,64 @@ struct Dec68 {
   }
 };
 
+// Decode-plane decoder (any ratio, the effective ternary weights at one 2-bit
+// code per position), dense v_mfma_i32_16x16x64_i8: sixteen steps of 64 as in
+// the 6:8 decoder; lane group g's run is the 64 plane bytes of positions
+// 256g .. 256g + 255 (plane words 16g .. 16g + 15 of the range), step s takes
+// word 16g + s.  The plane's bit order makes the decode four shift-and-masks:
+// (word << 2k) & 0xC0C0C0C0 are positions 4k .. 4k + 3 of the word as 64 * w.
+// Ring slot: 16 rows x 256 B; chunk c of row r sits at chunk position
+// c ^ (r & 15), so the 16 lanes that read one chunk of 16 rows touch 16
+// different 16-byte bank groups.
+struct Dec2 {
+  static constexpr int SLOT = 4096, NDMA = 4, LUT = 0, BPC = 4;   // 40 KB LDS per block
+  __host__ __device__ static int64_t meta_row(int64_t) { return 0; }
+  __host__ __device__ static int64_t code_row(int64_t K) { return K / 4; }
+  int rowq[4], colq[4];
+  v4i bx[16];
+  __device__ inline void init(int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {                        // LDS chunk position 64q + lane
+      const int sp = 64 * q + lane, rr = sp >> 4;
+      rowq[q] = rr;
+      colq[q] = 256 * wave + 16 * ((sp & 15) ^ (rr & 15));
+    }
+  }
+  __device__ inline void issue(uint8_t* dst, const uint8_t*, const uint8_t* c, int valid, int64_t K) {
+    const int64_t rowc = K / 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = rowq[q] < valid ? rowq[q] : valid - 1;
+      g2lds16(c + r * rowc + colq[q], dst + 1024 * q);
+    }
+  }
+  __device__ inline void load_x(const int8_t* xrow, bool ok, int wave, int g) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      bx[s] = ok ? *(const v4i*)(xrow + 1024 * wave + 256 * g + 16 * s) : (v4i){0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) asm volatile("" ::"v"(bx[s]));
+  }
+  __device__ inline void build_lut(uint8_t*, int) {}
+  __device__ inline v4i compute(const uint8_t* slot, const uint8_t*, int rl, int g) {
+    const uint8_t* sr = slot + rl * 256;
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v4i v = *(const v4i*)(sr + 16 * ((4 * g + i) ^ rl));
+      w[4 * i] = (uint32_t)v[0]; w[4 * i + 1] = (uint32_t)v[1]; w[4 * i + 2] = (uint32_t)v[2]; w[4 * i + 3] = (uint32_t)v[3];
+    }
+    constexpr uint32_t MK = 0xC0C0C0C0u;
+    v4i acc = (v4i){0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const v4i a = (v4i){(int)(w[s] & MK), (int)((w[s] << 2) & MK), (int)((w[s] << 4) & MK), (int)((w[s] << 6) & MK)};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx[s], acc, 0, 0, 0);
+    }
+    return acc;
+  }
+};
+
 // One launch over `count` weights of R rows each: global row group q = w * nrg + lr.
 template <int OUT, typename Dec>
 __global__ __launch_bounds__(256, Dec::BPC) void gemv_stream_kernel(
@@ -463,7 +525,7 @@ __global__ __launch_bounds__(256, Dec::BPC) void gemv_stream_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, rl = lane & 15;
   const int64_t nrg = cdiv(R, 16);
-  const int64_t rowm = K / 8, rowc = K * (Dec::NDMA == 4 ? 2 : 3) / 16;   // plane bytes per row
+  const int64_t rowm = Dec::meta_row(K), rowc = Dec::code_row(K);      // plane bytes per row
   const bool has = wave < K / 1024;                    // wave-uniform
   const int64_t tq = tid >> 4;                         // token of the outputs this thread writes
   const float sxv = OUT != 0 ? s_x[tq < T ? tq : 0] : 0.0f;
@@ -480,7 +542,8 @@ __global__ __launch_bounds__(256, Dec::BPC) void gemv_stream_kernel(
   int64_t ilr = q0 - (int64_t)iw * nrg;
   auto issue_next = [&](int slot) {
     const int valid = (int)(R - ilr * 16 < 16 ? R - ilr * 16 : 16);
-    dec.issue(myring + slot * Dec::SLOT, P.meta[iw] + ilr * 16 * rowm, P.codes[iw] + ilr * 16 * rowc, valid, K);
+    const uint8_t* mp = rowm ? P.meta[iw] + ilr * 16 * rowm : nullptr;
+    dec.issue(myring + slot * Dec::SLOT, mp, P.codes[iw] + ilr * 16 * rowc, valid, K);
     if (++ilr == nrg) { ilr = 0; ++iw; }
   };
   if (has) {
@@ -753,6 +816,113 @@ hipError_t launch_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                        const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
                        int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
   return launch_gemv_batched(Xq, s_x, T, K, &codes, &meta, &s_w, R, n, m, &Y, ydt, ldy, 1, st);
+}
+
+// ----------------------------------------------------------------------------- decode plane
+namespace {
+
+// Packed planes -> decode plane: one thread per plane word (16 positions),
+// through the unpack table (blocks walk the words with a grid stride).
+template <int M>
+__global__ __launch_bounds__(256) void repack_d2_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+                                                        int n, int64_t cplane, uint32_t* __restrict__ d2) {
+  __shared__ uint32_t lut[4096];
+  for (int i = threadIdx.x; i < 4096; i += 256) lut[i] = unpack_entry((uint32_t)i);
+  __syncthreads();
+  const int64_t wpr = K / 16, total = R * wpr;
+  const int64_t crow = K * n / (4 * M);                // code bytes per row
+  const int64_t lastw = (cplane - 4) & ~(int64_t)3;
+  const bool dense = meta == nullptr;
+  for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total; gid += (int64_t)gridDim.x * 256) {
+    const int64_t r = gid / wpr, k0 = (gid - r * wpr) * 16;
+    const uint32_t mw16 = dense ? 0xFFFFu : (uint32_t)*(const uint16_t*)(meta + r * (K / 8) + k0 / 8);
+    const int64_t cbit = r * crow * 8 + k0 * 2 * n / M;
+    const int64_t a0 = (cbit >> 3) & ~(int64_t)3;
+    const int sh = (int)(cbit - a0 * 8);
+    const uint32_t w0 = *(const uint32_t*)(codes + (a0 < lastw ? a0 : lastw));
+    const uint32_t w1 = *(const uint32_t*)(codes + (a0 + 4 < lastw ? a0 + 4 : lastw));
+    const unsigned long long c = (((unsigned long long)w1 << 32) | w0) >> sh;
+    const v4i a = unpack16<M>(lut, mw16, dense, n, c, 0);   // positions 4k .. 4k + 3 in word k, int8
+    uint32_t out = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out |= ((uint32_t)a[k] & 0x03030303u) << (6 - 2 * k);   // +1 -> 01, -1 -> 11
+    d2[gid] = out;
+  }
+}
+
+// Decode-plane GEMV for any K (a multiple of 64): one thread per (row, token),
+// four sdot4 per plane word.
+template <int OUT>
+__global__ __launch_bounds__(256) void gemv_d2_kernel(const int8_t* __restrict__ Xq, const float* __restrict__ s_x,
+                                                      int64_t T, int64_t K, const uint32_t* __restrict__ d2,
+                                                      const float* __restrict__ s_w, int64_t R, void* __restrict__ Y,
+                                                      int64_t ldy) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int t = threadIdx.x & 15;
+  if (row >= R || t >= T) return;
+  const uint32_t* wr = d2 + row * (K / 16);
+  const int* xr = (const int*)(Xq + t * K);
+  int acc = 0;
+  for (int64_t w = 0; w < K / 16; ++w) {
+    const uint32_t word = wr[w];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      acc = __builtin_amdgcn_sdot4((int)((word << (2 * k)) & 0xC0C0C0C0u), xr[4 * w + k], acc, false);
+  }
+  const int sum = acc >> 6;                           // exact: every product is a multiple of 64
+  if (OUT == 0) {
+    ((int*)Y)[t * ldy + row] = sum;
+  } else {
+    const float y = (float)sum * (*s_w * s_x[t]);
+    if (OUT == 1) ((float*)Y)[t * ldy + row] = y;
+    else ((uint16_t*)Y)[t * ldy + row] = f32_to_bf16_rne(y);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_repack_d2(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, int n, int m,
+                            uint8_t* d2, hipStream_t st) {
+  int64_t blocks = cdiv(R * (K / 16), 256);
+  if (blocks > 1024) blocks = 1024;
+  const int64_t cplane = round_up(R * (K * n / (4 * m)), 16);
+  const uint8_t* mp = (n == m) ? nullptr : meta;
+  if (m == 4)
+    SBN_LAUNCH("repack_d2", repack_d2_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, st, codes, mp, R, K, n, cplane,
+               (uint32_t*)d2);
+  else
+    SBN_LAUNCH("repack_d2", repack_d2_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, st, codes, mp, R, K, n, cplane,
+               (uint32_t*)d2);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_d2_batched(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                  const uint8_t* const* d2, const float* const* s_w, int64_t R, void* const* Y,
+                                  sbn_dtype ydt, int64_t ldy, int count, hipStream_t st) {
+  if (SBN_GV_STREAM && K % 1024 == 0 && K <= 4096) {
+    GemvBatch P;
+    for (int b = 0; b < GV_MAX_BATCH; ++b) {
+      P.codes[b] = b < count ? d2[b] : nullptr;
+      P.meta[b] = nullptr;
+      P.s_w[b] = b < count ? s_w[b] : nullptr;
+      P.Y[b] = b < count ? Y[b] : nullptr;
+    }
+    return launch_stream<Dec2>("gemv_stream_d2", Xq, s_x, T, K, P, count, R, ydt, ldy, st);
+  }
+  const dim3 grid((unsigned)cdiv(R, 16)), block(256);
+  for (int b = 0; b < count; ++b) {
+    const uint32_t* p = (const uint32_t*)d2[b];
+    if (ydt == SBN_I32_ACC)
+      SBN_LAUNCH("gemv_d2", gemv_d2_kernel<0>, grid, block, 0, st, Xq, s_x, T, K, p, s_w[b], R, Y[b], ldy);
+    else if (ydt == SBN_F32)
+      SBN_LAUNCH("gemv_d2", gemv_d2_kernel<1>, grid, block, 0, st, Xq, s_x, T, K, p, s_w[b], R, Y[b], ldy);
+    else
+      SBN_LAUNCH("gemv_d2", gemv_d2_kernel<2>, grid, block, 0, st, Xq, s_x, T, K, p, s_w[b], R, Y[b], ldy);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace sbn

@@ -115,6 +115,12 @@ hipError_t launch_gemv_batched(const int8_t* Xq, const float* s_x, int64_t T, in
                                const uint8_t* const* codes, const uint8_t* const* meta,
                                const float* const* s_w, int64_t R, int n, int m, void* const* Y,
                                sbn_dtype ydt, int64_t ldy, int count, hipStream_t st);
+// Decode plane: repack of the packed planes, and the GEMV over up to GV_MAX_BATCH planes.
+hipError_t launch_repack_d2(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, int n, int m,
+                            uint8_t* d2, hipStream_t st);
+hipError_t launch_gemv_d2_batched(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                  const uint8_t* const* d2, const float* const* s_w, int64_t R, void* const* Y,
+                                  sbn_dtype ydt, int64_t ldy, int count, hipStream_t st);
 hipError_t launch_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                        const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
                        int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, hipStream_t st);

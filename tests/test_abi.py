@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = sbn.header_symbols()
-    assert len(names) == 18
+    assert len(names) == 22
     for nm in names:
         assert hasattr(L, nm), nm
 
@@ -209,3 +209,19 @@ def test_forward_validation(L):
     need = sbn.sbn_workspace_bytes(sbn.SBN_OP_FORWARD, 16, 64, 256, 2, 4)
     assert need >= sbn.sbn_workspace_bytes(sbn.SBN_OP_PACK, 0, 64, 256, 2, 4) + \
         sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM, 16, 64, 256, 2, 4)
+
+
+def test_decode_plane_validation(L):
+    big = 1 << 20
+    assert sbn.sbn_decode_plane_bytes(4096, 4096) == 4096 * 4096 // 4
+    assert sbn.sbn_decode_plane_bytes(7, 64) == 112
+    f = L.sbn_repack_d2
+    assert f(P, None, 16, 256, 6, 8, P2, None) == NULL            # meta needed below n == m
+    assert f(P, None, 16, 250, 8, 8, P2, None) == SHAPE
+    assert f(P, P, 16, 256, 3, 6, P2, None) == NM
+    assert f(P, P, 16, 256, 6, 8, MIS, None) == ALIGN
+    g = L.sbn_ternary_gemv_d2
+    assert g(P, P, 17, 256, P, P, 64, P, 1, 64, None) == SHAPE     # T > 16
+    assert g(P, P, 4, 256, None, P, 64, P, 1, 64, None) == NULL
+    assert g(P, P, 4, 256, P, P, 64, P, 1, 60, None) == SHAPE      # ldy < R
+    assert g(P, P, 4, 256, P, P, 64, P, 7, 64, None) == DTYPE
