@@ -14,7 +14,9 @@ resident in HBM:
                      contract; the JSON line carries the list).
   decode:            decode GEMV (T=1, R=K=4096) over pools of 128 distinct
                      packed weights per ratio (2:4 and 6:8), as batched calls
-                     of 64 weights; `value` is GB/s of algorithmic bytes.
+                     of 64 weights; `value` is GB/s of algorithmic bytes.  The
+                     line also carries the same step on decode planes
+                     (`decode_d2`: the weights repacked into dense 2-bit codes).
   speedup:           sparse against dense at several token counts: the
                      library's 2:4 and 6:8 calls against its own dense
                      ternary (8:8) call and the vendor library's dense bf16
@@ -567,6 +569,37 @@ def make_decode_step(T=1):
     return step, total, per_launch, wl
 
 
+def make_decode_step_d2(T=1):
+    """The decode step on decode planes: the same two pools (2:4 and 6:8 weights,
+    POOL each) repacked once, outside the timed region, into the dense 2-bit
+    decode plane (4.19 MB per weight for both ratios), as batched calls of
+    BATCH planes.  Returns (step, bytes per step, bytes per launch)."""
+    import torch
+    import sparse_linear_layers_02_amd as sbn
+    from workloads import WORKLOADS
+    wl = WORKLOADS["decode"]
+    W = bf16_dev(wl.weights(0))
+    Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0, T=T)))
+    pools, total = [], 0
+    per = wl.R * wl.K // 4 + T * wl.K + 4 * T + 2 * T * wl.R + 4
+    for n, m in wl.nm:
+        codes0, meta0, s_w0 = sbn.sbn_mask_ternarize_pack(W, n, m)
+        d20 = sbn.sbn_repack_d2(codes0, meta0, wl.R, wl.K, n, m)
+        pools.append(dict(d2s=[d20.clone() for _ in range(POOL)], s_ws=[s_w0.clone() for _ in range(POOL)],
+                          Ys=[torch.empty((T, wl.R), dtype=torch.bfloat16, device="cuda") for _ in range(POOL)]))
+        total += POOL * per
+        del codes0, meta0, d20
+    del W
+
+    def step():
+        for p in pools:
+            for b0 in range(0, POOL, BATCH):
+                sl = slice(b0, b0 + BATCH)
+                sbn.sbn_ternary_gemv_d2_batched(Xq, s_x, p["d2s"][sl], p["s_ws"][sl], wl.R, Ys=p["Ys"][sl])
+
+    return step, total, BATCH * per
+
+
 def cpu_baseline_decode(wl, weights=POOL):
     """The oracle's GEMV (float64 accumulate and output scaling) for one token
     against `weights` distinct R x K ternary weights per ratio, the effective
@@ -668,6 +701,25 @@ def main():
                         "note": "algorithmic bytes: packed planes + activations + scales + bf16 outputs of the "
                                 f"{BATCH} weights of one launch"}
         out["stages_us"] = {k: round(v[1] / v[0] * 1e3, 3) for k, v in sorted(prof.items()) if v[0]}
+        if not a.no_extras:
+            del step
+            torch.cuda.empty_cache()
+            step2, nbytes2, per_launch2 = make_decode_step_d2(T=1)
+            ms2, _, _, mode2 = time_steps(step2, a.steps, a.warmup, kernel="gemv_stream_d2")
+            k_ms, k_cnt = kernel_avg_ms(profile_pass(step2, a.steps, "gemv_stream_d2"), "gemv_stream_d2")
+            ach = per_launch2 / (k_ms * 1e-3) / 1e9
+            out["decode_d2"] = {
+                "note": "the same step on decode planes (the pools' weights repacked once into dense 2-bit "
+                        "ternary codes, 4.19 MB per weight for both ratios, against 4.19 / 5.24 MB packed); "
+                        "value stays on the packed weights",
+                "ms_per_step": round(ms2, 4), "GBps": round(nbytes2 / (ms2 * 1e-3) / 1e9, 1),
+                "frac_hbm": round(nbytes2 / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "speedup_vs_packed": round(ms / ms2, 3), "launch": mode2,
+                "roofline": {"kernel": "gemv_stream_d2", "bound": "hbm", "achieved": round(ach, 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                             "traffic": traffic_from_profiles("gemv_stream_d2", "decode"),
+                             "kernel_us": round(k_ms * 1e3, 3), "launches": k_cnt, "bytes_per_launch": per_launch2}}
+            del step2
     elif a.workload == "speedup":
         tab = speedup_tables(a.steps)
         r = next(r for r in tab["prefill"] if r["T"] == 4096)

@@ -463,8 +463,11 @@ struct Dec68 {
 // Ring slot: 16 rows x 256 B; chunk c of row r sits at chunk position
 // c ^ (r & 15), so the 16 lanes that read one chunk of 16 rows touch 16
 // different 16-byte bank groups.
+#ifndef SBN_GV_D2_BPC
+#define SBN_GV_D2_BPC 4
+#endif
 struct Dec2 {
-  static constexpr int SLOT = 4096, NDMA = 4, LUT = 0, BPC = 4;   // 40 KB LDS per block
+  static constexpr int SLOT = 4096, NDMA = 4, LUT = 0, BPC = SBN_GV_D2_BPC;   // 40 KB LDS per block (ring of 2)
   __host__ __device__ static int64_t meta_row(int64_t) { return 0; }
   __host__ __device__ static int64_t code_row(int64_t K) { return K / 4; }
   int rowq[4], colq[4];
