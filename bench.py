@@ -425,6 +425,16 @@ def speedup_tables(reps):
                     Xq, s_x, p["codes"][b:b + BATCH], p["metas"][b:b + BATCH], p["s_ws"][b:b + BATCH], R, n, m,
                     Ys=Ys[b:b + BATCH]) for b in range(0, P, BATCH)], reps)
                 row[f"sbn_{n}{m}_batched_us"] = round(ms * 1e3 / P, 3)
+            if (n, m) == (6, 8):                       # the same weights as decode planes (2 bits per weight)
+                Pd = -(-2 * MALL_BYTES // (R * K // 4))
+                d2s = [sbn.sbn_repack_d2(p["codes"][i % P], p["metas"][i % P], R, K, n, m) for i in range(Pd)]
+                sds = [p["s_ws"][i % P] for i in range(Pd)]
+                Yd = [torch.empty((T, R), dtype=torch.bfloat16, device="cuda") for _ in range(Pd)]
+                ms = graph_ms(lambda: [sbn.sbn_ternary_gemv_d2_batched(
+                    Xq, s_x, d2s[b:b + BATCH], sds[b:b + BATCH], R, Ys=Yd[b:b + BATCH])
+                    for b in range(0, Pd, BATCH)], reps)
+                row["sbn_68_d2_batched_us"] = round(ms * 1e3 / Pd, 3)
+                del d2s, sds, Yd
             del Ys, ws
         Yb = [torch.empty((T, R), dtype=torch.bfloat16, device="cuda") for _ in range(Pb)]
         ms, err = vendor(lambda: [torch.matmul(X, Wb[i].t(), out=Yb[i]) for i in range(Pb)])
@@ -433,7 +443,7 @@ def speedup_tables(reps):
         ms, err = vendor(lambda: [torch._int_mm(Xq, Wi[i], out=Yi[i]) for i in range(Pi)])
         row["int8_us"], row["int8_error"] = (round(ms * 1e3 / Pi, 3) if ms else None), err
         del Yb, Yi
-        for key in ("sbn_24", "sbn_68", "sbn_24_batched", "sbn_68_batched"):
+        for key in ("sbn_24", "sbn_68", "sbn_24_batched", "sbn_68_batched", "sbn_68_d2_batched"):
             t = row[key + "_us"]
             row[key + "_vs_dense_ternary"] = round(row["sbn_88_us"] / t, 3)
             row[key + "_vs_bf16"] = round(row["bf16_us"] / t, 3) if row["bf16_us"] else None
