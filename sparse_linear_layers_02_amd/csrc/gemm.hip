@@ -21,8 +21,8 @@
 //
 // GEMM: 512 threads (8 waves), block tile 256 rows x 256 tokens, wave tile
 // 128 rows x 64 tokens (8 x 4 accumulator tiles of 16 x 16 int32) -- or 128 /
-// 64 tokens per block (8 x 2 / 8 x 1 per wave) when the token count gives the
-// 256 x 256 grid fewer than 192 tiles for the 256 compute units; K step 128
+// 64 tokens per block (8 x 2 / 8 x 1 per wave) when the token count leaves
+// the 256 x 256 grid too few tiles for the 256 compute units; K step 128
 // (sparse, 3 LDS stages of 52 KB) or 64 (dense, 4 stages of 32 KB), stages
 // filled with direct global->LDS loads issued two (sparse) or three (dense)
 // steps ahead.  The two waves that share a SIMD (w and w + 4) alternate
@@ -464,13 +464,25 @@ hipError_t launch_gemm_mj(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* X
   return hipGetLastError();
 }
 
-// Token fragments per wave: the 256-token tile unless its grid leaves more
-// than a quarter of the 256 compute units idle; then 128 or (sparse) 64 tokens.
+// Token fragments per wave: the tile width whose grid finishes first, with one
+// block per compute unit -- rounds of 256 tiles times a tile's time, measured
+// at about 1 : 1.25 : 1.8 for the 64-, 128- and 256-token tiles (a 256-token
+// tile does four times the work of a 64-token one in 1.8 times the time, so
+// wide tiles win once the grid fills the chip).  64 tokens: sparse only.
 int gemm_mj(bool sparse, int64_t T, int64_t R) {
   const int64_t rt = cdiv(R, GEMM_TILE_R);
-  if (cdiv(T, 256) * rt >= 192) return 4;
-  if (!sparse || cdiv(T, 128) * rt >= 192) return 2;
-  return 1;
+  const double cost[3] = {1.0, 1.25, 1.8};            // MJ = 1, 2, 4
+  int best = 4;
+  double best_t = 1e300;
+  for (int i = 2; i >= (sparse ? 0 : 1); --i) {
+    const int mj = 1 << i;
+    const double t = (double)cdiv(cdiv(T, 64 * mj) * rt, 256) * cost[i];
+    if (t < best_t) {
+      best_t = t;
+      best = mj;
+    }
+  }
+  return best;
 }
 
 template <bool SPARSE>
