@@ -456,14 +456,49 @@ __device__ inline void mask_pack_body(
         key[p] = ((tmask ? nz : a) << 3) | (uint32_t)(7 - p);   // distinct; lower index wins ties
         code[p] = nz | ((nz & (w >> 15)) << 1);          // 00 = 0, 01 = +1, 11 = -1
       }
+      // Survivors: the n largest of M distinct keys.  n = 1, 2, M - 2, M - 1 take
+      // a threshold from a min/max network (the largest two or the smallest two:
+      // from sorted pairs, the two extremes of a union of two sorted pairs are
+      // min(x1, y1) and min(max(x1, y1), min(x2, y2)), and likewise with max);
+      // other n count each key's rank.
+      const int mode = (n == 1 || n == 2) ? 1 : (n == M - 1 || n == M - 2) ? 2 : 0;
+      uint32_t thk = 0;
+      if (mode != 0) {
+        const bool big = mode == 1;                      // keep the largest (else drop the smallest)
+        const bool two = big ? n == 2 : n == M - 2;
+        uint32_t e1[M / 2], e2[M / 2];                   // per pair: extreme, other
+#pragma unroll
+        for (int i = 0; i < M / 2; ++i) {
+          const uint32_t x = key[2 * i], y = key[2 * i + 1];
+          e1[i] = big ? max(x, y) : min(x, y);
+          e2[i] = big ? min(x, y) : max(x, y);
+        }
+#pragma unroll
+        for (int w2 = M / 2; w2 > 1; w2 >>= 1) {        // merge pairs of (first, second) extremes
+#pragma unroll
+          for (int i = 0; i < w2 / 2; ++i) {
+            const uint32_t x1 = e1[2 * i], x2 = e2[2 * i], y1 = e1[2 * i + 1], y2 = e2[2 * i + 1];
+            e1[i] = big ? max(x1, y1) : min(x1, y1);
+            e2[i] = big ? max(min(x1, y1), max(x2, y2)) : min(max(x1, y1), min(x2, y2));
+          }
+        }
+        thk = two ? e2[0] : e1[0];                       // n-th largest (big) / (M-n)-th smallest
+      }
       int slot = 0;
 #pragma unroll
       for (int p = 0; p < M; ++p) {
-        int rank = 0;
+        bool kp;
+        if (mode == 1) {
+          kp = key[p] >= thk;
+        } else if (mode == 2) {
+          kp = key[p] > thk;
+        } else {
+          int rank = 0;
 #pragma unroll
-        for (int q = 0; q < M; ++q)
-          if (q != p) rank += key[q] > key[p] ? 1 : 0;
-        const bool kp = rank < n;
+          for (int q = 0; q < M; ++q)
+            if (q != p) rank += key[q] > key[p] ? 1 : 0;
+          kp = rank < n;
+        }
         keep |= (kp ? 1u : 0u) << (g * M + p);
         cw |= (unsigned long long)(kp ? code[p] : 0u) << (2 * (n * g + slot));
         slot += kp ? 1 : 0;
@@ -639,7 +674,7 @@ static MaskPackArgs mask_pack_args(const uint16_t* W, int64_t R, int64_t K, int6
     a.dr = a.dch = 0;
   } else {
     nblk = cdiv(a.total_chunks, PT);
-    if (nblk > 8192) nblk = 8192;
+    if (nblk > 1024) nblk = 1024;                       // four blocks per CU, looping: each block forms the scale once
     const int64_t stride = nblk * PT, cpr = K / 32;
     a.dr = stride / cpr;
     a.dch = stride % cpr;
