@@ -424,9 +424,9 @@ __device__ float scale_from_partials(const unsigned char* __restrict__ ws, int64
 
 // ------------------------------------------------------------------ pass 2
 // One thread = 32 consecutive weights of one row (32/M whole groups).
-template <int M>
+template <int M, int n>
 __device__ inline void mask_pack_body(
-    int64_t blk, int64_t nblk, const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw, int n,
+    int64_t blk, int64_t nblk, const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ meta, float* __restrict__ s_w_ptr,
     const unsigned char* __restrict__ ws, int64_t nb, int64_t total_chunks, int64_t dr, int64_t dch,
     int tmask) {
@@ -461,7 +461,7 @@ __device__ inline void mask_pack_body(
       // from sorted pairs, the two extremes of a union of two sorted pairs are
       // min(x1, y1) and min(max(x1, y1), min(x2, y2)), and likewise with max);
       // other n count each key's rank.
-      const int mode = (n == 1 || n == 2) ? 1 : (n == M - 1 || n == M - 2) ? 2 : 0;
+      constexpr int mode = (n == 1 || n == 2) ? 1 : (n == M - 1 || n == M - 2) ? 2 : 0;
       uint32_t thk = 0;
       if (mode != 0) {
         const bool big = mode == 1;                      // keep the largest (else drop the smallest)
@@ -602,7 +602,7 @@ struct MaskPackArgs {
   int tmask;
 };
 
-// KIND: 0 = 2:4 with ldw == K, 1 = 2:4, 4 / 8 = any n of a group of 4 / 8.
+// KIND: 0 = 2:4 with ldw == K, 1 = 2:4, 16 m + n = n of a group of m (4 or 8).
 template <int KIND>
 __device__ inline void mask_pack_dispatch(int64_t blk, int64_t nblk, const MaskPackArgs& a) {
   if constexpr (KIND == 0)
@@ -610,7 +610,7 @@ __device__ inline void mask_pack_dispatch(int64_t blk, int64_t nblk, const MaskP
   else if constexpr (KIND == 1)
     mask_pack24_body<false>(blk, nblk, a.W, a.R, a.K, a.ldw, a.codes, a.meta, a.s_w, a.ws, a.nb, a.tmask);
   else
-    mask_pack_body<KIND>(blk, nblk, a.W, a.R, a.K, a.ldw, a.n, a.codes, a.meta, a.s_w, a.ws, a.nb, a.total_chunks,
+    mask_pack_body<KIND / 16, KIND % 16>(blk, nblk, a.W, a.R, a.K, a.ldw, a.codes, a.meta, a.s_w, a.ws, a.nb, a.total_chunks,
                          a.dr, a.dch, a.tmask);
 }
 
@@ -678,7 +678,7 @@ static MaskPackArgs mask_pack_args(const uint16_t* W, int64_t R, int64_t K, int6
     const int64_t stride = nblk * PT, cpr = K / 32;
     a.dr = stride / cpr;
     a.dch = stride % cpr;
-    kind = m;
+    kind = 16 * m + n;
   }
   return a;
 }
@@ -692,8 +692,13 @@ static hipError_t launch_mask_pack(const uint16_t* W, int64_t R, int64_t K, int6
   const dim3 grid((unsigned)nblk), block(PT);
   if (kind == 0) SBN_LAUNCH("mask_pack", mask_pack_kernel<0>, grid, block, 0, st, a);
   else if (kind == 1) SBN_LAUNCH("mask_pack", mask_pack_kernel<1>, grid, block, 0, st, a);
-  else if (kind == 4) SBN_LAUNCH("mask_pack", mask_pack_kernel<4>, grid, block, 0, st, a);
-  else SBN_LAUNCH("mask_pack", mask_pack_kernel<8>, grid, block, 0, st, a);
+#define SBN_MP_CASE(KD) \
+  else if (kind == KD) SBN_LAUNCH("mask_pack", mask_pack_kernel<KD>, grid, block, 0, st, a);
+  SBN_MP_CASE(65) SBN_MP_CASE(67) SBN_MP_CASE(68)                  // 1:4, 3:4, 4:4
+  SBN_MP_CASE(129) SBN_MP_CASE(130) SBN_MP_CASE(131) SBN_MP_CASE(132)   // 1:8 .. 8:8
+  SBN_MP_CASE(133) SBN_MP_CASE(134) SBN_MP_CASE(135) SBN_MP_CASE(136)
+#undef SBN_MP_CASE
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
