@@ -59,10 +59,10 @@ __device__ inline void tile_put(uint16_t* tile, int row, int c, uint16_t v) { ti
 // Wt fragments (rows k, contraction r) from the packed planes.  Thread (r, seg)
 // decodes positions 16 seg .. +16 of the tile's 128 k for row r through the
 // unpack table; blocks walk the tiles with a grid stride.
-template <int M>
+template <int M, int n>                                  // n: survivors per group (straight-line decode)
 __global__ __launch_bounds__(256) void expand_wt_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ meta, int64_t R, int64_t K,
-                                                        int n, int64_t KB16, int64_t RB32, int64_t cplane,
+                                                        int64_t KB16, int64_t RB32, int64_t cplane,
                                                         uint4* __restrict__ out) {
   __shared__ uint32_t lut[4096];
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * TP];
@@ -364,12 +364,18 @@ hipError_t launch_backward(const uint16_t* dY, int64_t T, int64_t R, const int8_
     int64_t tiles = (L.KB16 / 8) * L.RB32;
     if (tiles > 2048) tiles = 2048;                     // grid stride: the unpack table is built per block
     const int64_t cplane = round_up(R * K * n / (4 * m), 16);
-    if (m == 4)
-      SBN_LAUNCH("expand_wt", expand_wt_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, st, codes,
-                 (n == m) ? nullptr : meta, R, K, n, L.KB16, L.RB32, cplane, (uint4*)(w + L.wt));
-    else
-      SBN_LAUNCH("expand_wt", expand_wt_kernel<8>, dim3((unsigned)tiles), dim3(256), 0, st, codes,
-                 (n == m) ? nullptr : meta, R, K, n, L.KB16, L.RB32, cplane, (uint4*)(w + L.wt));
+    const uint8_t* mp = (n == m) ? nullptr : meta;
+    const dim3 eg((unsigned)tiles), eb(256);
+#define SBN_EW_CASE(MM, NN)                                                                                        \
+    else if (m == MM && n == NN) SBN_LAUNCH("expand_wt", (expand_wt_kernel<MM, NN>), eg, eb, 0, st, codes, mp, R, K, \
+                                            L.KB16, L.RB32, cplane, (uint4*)(w + L.wt));
+    if (false) {
+    }
+    SBN_EW_CASE(4, 1) SBN_EW_CASE(4, 2) SBN_EW_CASE(4, 3) SBN_EW_CASE(4, 4)
+    SBN_EW_CASE(8, 1) SBN_EW_CASE(8, 2) SBN_EW_CASE(8, 3) SBN_EW_CASE(8, 4)
+    SBN_EW_CASE(8, 5) SBN_EW_CASE(8, 6) SBN_EW_CASE(8, 7) SBN_EW_CASE(8, 8)
+#undef SBN_EW_CASE
+    else return hipErrorInvalidValue;
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 grid((unsigned)cdiv(T, 256), (unsigned)cdiv(K, 256));
     if (dxdt == SBN_F32)

@@ -193,14 +193,15 @@ __global__ __launch_bounds__(256) void layout_sparse_kernel(
     tile_x_block(b - nbw, xa.Xq, xa.T, xa.K, xa.TBp, xa.KC, xa.Xt);
 }
 
-template <int M>
+// N: survivors per group, a template argument so each ratio's decode is straight-line code.
+template <int M, int N>
 __global__ __launch_bounds__(256) void layout_dense_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, int64_t R, int64_t K,
-    int n, int64_t RB, int64_t KD, int64_t cplane, uint8_t* __restrict__ vals, int64_t nbw, const XTileArgs xa) {
+    int64_t RB, int64_t KD, int64_t cplane, uint8_t* __restrict__ vals, int64_t nbw, const XTileArgs xa) {
   __shared__ uint32_t lut[4096];
   const int64_t b = blockIdx.x;
   if (b < nbw)                                       // uniform per block: the table barrier is safe
-    expand_dense_blocks<M>(b, nbw, lut, codes, meta, R, K, n, RB, KD, cplane, vals);
+    expand_dense_blocks<M>(b, nbw, lut, codes, meta, R, K, N, RB, KD, cplane, vals);
   else
     tile_x_block(b - nbw, xa.Xq, xa.T, xa.K, xa.TBp, xa.KC, xa.Xt);
 }
@@ -551,12 +552,16 @@ hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
   int64_t nbw = cdiv(RB * KD * 64, 256);
   if (nbw > 1024) nbw = 1024;                              // four blocks per CU, each table built once
   const uint8_t* mp = (n == m) ? nullptr : meta;
-  if (m == 4)
-    SBN_LAUNCH("layout_dense", layout_dense_kernel<4>, dim3((unsigned)(nbw + nbx)), dim3(256), 0, st,
-               codes, mp, R, K, n, RB, KD, cplane, w, nbw, xa);
-  else
-    SBN_LAUNCH("layout_dense", layout_dense_kernel<8>, dim3((unsigned)(nbw + nbx)), dim3(256), 0, st,
-               codes, mp, R, K, n, RB, KD, cplane, w, nbw, xa);
+  const dim3 lgrid((unsigned)(nbw + nbx)), lblock(256);
+#define SBN_LD_CASE(MM, NN)                                                                                  \
+  else if (m == MM && n == NN) SBN_LAUNCH("layout_dense", (layout_dense_kernel<MM, NN>), lgrid, lblock, 0, st, \
+                                          codes, mp, R, K, RB, KD, cplane, w, nbw, xa);
+  if (false) {
+  }
+  SBN_LD_CASE(4, 3) SBN_LD_CASE(4, 4)
+  SBN_LD_CASE(8, 3) SBN_LD_CASE(8, 4) SBN_LD_CASE(8, 5) SBN_LD_CASE(8, 6) SBN_LD_CASE(8, 7) SBN_LD_CASE(8, 8)
+#undef SBN_LD_CASE
+  else return hipErrorInvalidValue;
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_gemm_t<false>(w, nullptr, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
