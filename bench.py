@@ -303,16 +303,19 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
 # ---------------------------------------------------------------------- sparse vs dense
 SPEEDUP_T_PREFILL = (512, 1024, 2048, 4096, 8192)
 SPEEDUP_T_DECODE = (1, 4, 16)
+PER_GRAPH = 8                  # prefill calls per replayed graph in the speedup tables
 
 
-def graph_ms(fn, reps):
+def graph_ms(fn, reps, per=1):
     """Milliseconds per execution of fn (which only enqueues GPU work),
-    replayed from a HIP graph (eager launches if capture fails)."""
+    replayed from a HIP graph of per executions back to back (eager launches
+    if capture fails), so that the host's cost of one replay is spread."""
     import torch
     fn()
     torch.cuda.synchronize()
-    g = capture_graph(fn)
-    run = g.replay if g is not None else fn
+    body = fn if per == 1 else (lambda: [fn() for _ in range(per)])
+    g = capture_graph(body)
+    run = g.replay if g is not None else body
     run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -321,7 +324,7 @@ def graph_ms(fn, reps):
         run()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    return e0.elapsed_time(e1) / (reps * per)
 
 
 def ternary_int8(W):
@@ -337,7 +340,8 @@ def speedup_tables(reps):
     """Per-call times of the sparse 2:4 and 6:8 products against dense ones
     over the same activations: the library's dense ternary 8:8 call, and
     torch's bf16 matmul and int8 _int_mm (hipBLASLt).  Prefill: the prefill
-    shape at several T, one call per timing.  Decode: R = K = 4096 at T = 1, 4,
+    shape at several T, one call per timing, each library ratio both from the
+    packed planes and on a weight operand prepared once.  Decode: R = K = 4096 at T = 1, 4,
     16, every weight of a pool of distinct weights at least twice the Infinity
     Cache, as separate calls in one graph (the library's calls also batched, 64
     weights per launch).  A product the vendor library refuses is null, with
@@ -352,12 +356,13 @@ def speedup_tables(reps):
     W = bf16_dev(wl.weights(0))
     Xall = bf16_dev(wl.activations(0, T=max(SPEEDUP_T_PREFILL)))
     packs = {(n, m): sbn.sbn_mask_ternarize_pack(W, n, m) for n, m in ((2, 4), (6, 8), (8, 8))}
+    prepared = {nm: sbn.sbn_prepare_gemm_weight(c, mt, R, K, *nm) for nm, (c, mt, _) in packs.items()}
     Wq = ternary_int8(W)
     WqT = Wq.t()
 
     def vendor(fn):
         try:
-            return graph_ms(fn, reps), None
+            return graph_ms(fn, reps, PER_GRAPH), None
         except Exception as e:          # reported in the row
             return None, f"{type(e).__name__}: {str(e).splitlines()[0][:160]}"
 
@@ -370,8 +375,15 @@ def speedup_tables(reps):
             Y = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
             ws = torch.empty(max(sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM, T, R, K, n, m), 256), dtype=torch.uint8,
                              device="cuda")
-            ms = graph_ms(lambda: sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, R, n, m, Y=Y, ws=ws), reps)
+            ms = graph_ms(lambda: sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, R, n, m, Y=Y, ws=ws),
+                          reps, PER_GRAPH)
             row[f"sbn_{n}{m}_us"] = round(ms * 1e3, 2)
+            ws = torch.empty(max(sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM_PREPARED, T, R, K, n, m), 256),
+                             dtype=torch.uint8, device="cuda")
+            pw = prepared[(n, m)]
+            ms = graph_ms(lambda: sbn.sbn_sparse_ternary_gemm_prepared(Xq, s_x, pw, s_w, R, n, m, Y=Y, ws=ws),
+                          reps, PER_GRAPH)
+            row[f"sbn_{n}{m}_prepared_us"] = round(ms * 1e3, 2)
             del Y, ws
         Yb = torch.empty((T, R), dtype=torch.bfloat16, device="cuda")
         ms, err = vendor(lambda: torch.matmul(X, W.t(), out=Yb))
@@ -380,14 +392,15 @@ def speedup_tables(reps):
         ms, err = vendor(lambda: torch._int_mm(Xq, WqT, out=Yi))
         row["int8_us"], row["int8_error"] = (round(ms * 1e3, 2) if ms else None), err
         del Yb, Yi
-        for key in ("sbn_24", "sbn_68"):
+        for key in ("sbn_24", "sbn_68", "sbn_24_prepared", "sbn_68_prepared"):
             t = row[key + "_us"]
+            dense = row["sbn_88_prepared_us" if key.endswith("prepared") else "sbn_88_us"]
             row[key + "_TOPS"] = round(ops / (t * 1e-6) / 1e12, 1)
-            row[key + "_vs_dense_ternary"] = round(row["sbn_88_us"] / t, 3)
+            row[key + "_vs_dense_ternary"] = round(dense / t, 3)
             row[key + "_vs_bf16"] = round(row["bf16_us"] / t, 3) if row["bf16_us"] else None
             row[key + "_vs_int8"] = round(row["int8_us"] / t, 3) if row["int8_us"] else None
         out["prefill"].append({k: v for k, v in row.items() if v is not None or not k.endswith("_error")})
-    del W, Xall, packs, Wq, WqT
+    del W, Xall, packs, prepared, Wq, WqT
     torch.cuda.empty_cache()
 
     # decode shape, pools above the Infinity Cache

@@ -101,7 +101,8 @@ typedef enum sbn_op {
   SBN_OP_GEMM = 2,
   SBN_OP_GEMV = 3,
   SBN_OP_BACKWARD = 4,
-  SBN_OP_FORWARD = 5
+  SBN_OP_FORWARD = 5,
+  SBN_OP_GEMM_PREPARED = 6
 } sbn_op;
 
 /* ABI version of the loaded library (SBN_ABI_VERSION). */
@@ -225,6 +226,26 @@ sbn_status sbn_sparse_ternary_gemm(const int8_t* Xq, const float* s_x, int64_t T
                                    const uint8_t* codes, const uint8_t* meta, const float* s_w,
                                    int64_t R, int n, int m, void* Y, sbn_dtype ydt, int64_t ldy,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * For weights that serve many GEMM calls (inference): the weight operand the
+ * GEMM builds from the packed planes on every call, built once.
+ * sbn_gemm_weight_bytes: its size (host-only).
+ * sbn_prepare_gemm_weight: packed planes (meta NULL when n == m) -> prepared
+ *   operand (device, sbn_gemm_weight_bytes(R, K, n, m) bytes, opaque layout).
+ * sbn_sparse_ternary_gemm_prepared: the sparse_ternary_gemm on it, same
+ *   results bit for bit; ws of sbn_workspace_bytes(SBN_OP_GEMM_PREPARED, T, R,
+ *   K, n, m) bytes (0 for every ratio in this version: the activations are
+ *   read in place; ws may then be NULL).
+ * Errors: as sbn_sparse_ternary_gemm.
+ */
+sbn_status sbn_gemm_weight_bytes(int64_t R, int64_t K, int n, int m, size_t* bytes);
+sbn_status sbn_prepare_gemm_weight(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, int n, int m,
+                                   uint8_t* prepared, void* stream);
+sbn_status sbn_sparse_ternary_gemm_prepared(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                            const uint8_t* prepared, const float* s_w, int64_t R, int n, int m,
+                                            void* Y, sbn_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                                            void* stream);
 
 /*
  * The whole forward of one Sparse-BitLinear call in one entry point:

@@ -25,6 +25,7 @@ HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "sbn.h")
 
 SBN_F32, SBN_BF16, SBN_I32_ACC = 0, 1, 2
 SBN_OP_PACK, SBN_OP_ACT_QUANT, SBN_OP_GEMM, SBN_OP_GEMV, SBN_OP_BACKWARD, SBN_OP_FORWARD = 0, 1, 2, 3, 4, 5
+SBN_OP_GEMM_PREPARED = 6
 SBN_FLAGS_NONE, SBN_MASK_FROM_TERNARY, SBN_GRAD_W_MASKED = 0, 1, 2
 STATUS = {0: "SBN_OK", 1: "SBN_ERR_NULL", 2: "SBN_ERR_SHAPE", 3: "SBN_ERR_UNSUPPORTED_NM",
           4: "SBN_ERR_ALIGN", 5: "SBN_ERR_WORKSPACE", 6: "SBN_ERR_DTYPE", 7: "SBN_ERR_HIP",
@@ -56,6 +57,10 @@ _SIGNATURES = {
                                  _vp, _sz, _vp], _int),
     "sbn_sparse_ternary_gemv": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _int, _int, _vp, _int, _i64,
                                  _vp, _sz, _vp], _int),
+    "sbn_gemm_weight_bytes": ([_i64, _i64, _int, _int, ctypes.POINTER(_sz)], _int),
+    "sbn_prepare_gemm_weight": ([_vp, _vp, _i64, _i64, _int, _int, _vp, _vp], _int),
+    "sbn_sparse_ternary_gemm_prepared": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, _int, _int, _vp, _int, _i64, _vp, _sz,
+                                          _vp], _int),
     "sbn_decode_plane_bytes": ([_i64, _i64, ctypes.POINTER(_sz)], _int),
     "sbn_repack_d2": ([_vp, _vp, _i64, _i64, _int, _int, _vp, _vp], _int),
     "sbn_ternary_gemv_d2": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _int, _i64, _vp], _int),
@@ -280,6 +285,39 @@ def sbn_forward(W, X, n: int, m: int, flags: int = 0, *, ydt: int = SBN_BF16, co
     return codes, meta, s_w, Xq, s_x, Y
 
 
+def sbn_gemm_weight_bytes(R: int, K: int, n: int, m: int) -> int:
+    b = _sz()
+    _check("sbn_gemm_weight_bytes", lib().sbn_gemm_weight_bytes(R, K, n, m, ctypes.byref(b)))
+    return b.value
+
+
+def sbn_prepare_gemm_weight(codes, meta, R: int, K: int, n: int, m: int, *, prepared=None, stream=None):
+    """The GEMM's weight operand, built once from the packed planes (uint8, opaque)."""
+    torch = _torch()
+    if prepared is None:
+        prepared = torch.empty(sbn_gemm_weight_bytes(R, K, n, m), dtype=torch.uint8, device=codes.device)
+    _check("sbn_prepare_gemm_weight",
+           lib().sbn_prepare_gemm_weight(_ptr(codes), _ptr(meta), R, K, n, m, _ptr(prepared), _stream(stream)))
+    return prepared
+
+
+def sbn_sparse_ternary_gemm_prepared(Xq, s_x, prepared, s_w, R: int, n: int, m: int, *, ydt: int = SBN_BF16, Y=None,
+                                     ws=None, stream=None):
+    """sbn_sparse_ternary_gemm on a prepared weight operand.  Returns Y [T, R]."""
+    torch = _torch()
+    T, K = Xq.shape
+    if Y is None:                                    # row stride rounded up to 8 elements (the ABI's rule)
+        Y = torch.empty((T, (R + 7) // 8 * 8), dtype=getattr(torch, _YT[ydt]), device=Xq.device)[:, :R]
+    need = sbn_workspace_bytes(SBN_OP_GEMM_PREPARED, T, R, K, n, m)
+    if ws is None:
+        ws = _WS["gemm"].get(need, Xq.device)
+    _check("sbn_sparse_ternary_gemm_prepared",
+           lib().sbn_sparse_ternary_gemm_prepared(_ptr(Xq), _ptr(s_x), T, K, _ptr(prepared), _ptr(s_w), R, n, m,
+                                                  _ptr(Y), ydt, Y.stride(0), _ptr(ws), ws.numel() if ws is not None else 0,
+                                                  _stream(stream)))
+    return Y
+
+
 def sbn_decode_plane_bytes(R: int, K: int) -> int:
     b = _sz()
     _check("sbn_decode_plane_bytes", lib().sbn_decode_plane_bytes(R, K, ctypes.byref(b)))
@@ -401,6 +439,7 @@ __all__ = [
     "sbn_mask_ternarize_pack", "sbn_act_quant", "sbn_sparse_ternary_gemm", "sbn_sparse_ternary_gemv",
     "sbn_backward", "sbn_backward_ex", "sbn_mask_ternarize_pack_ex", "sbn_sgd_update_pack", "sbn_forward",
     "sbn_decode_plane_bytes", "sbn_repack_d2", "sbn_ternary_gemv_d2", "sbn_ternary_gemv_d2_batched",
+    "sbn_gemm_weight_bytes", "sbn_prepare_gemm_weight", "sbn_sparse_ternary_gemm_prepared", "SBN_OP_GEMM_PREPARED",
     "SBN_FLAGS_NONE", "SBN_MASK_FROM_TERNARY", "SBN_GRAD_W_MASKED",
     "SBN_F32", "SBN_BF16", "SBN_I32_ACC", "SBN_OP_PACK", "SBN_OP_ACT_QUANT", "SBN_OP_GEMM",
     "SBN_OP_GEMV", "SBN_OP_BACKWARD", "SBN_OP_FORWARD", "sbn_profile_enable", "sbn_profile_reset", "sbn_profile_dump",

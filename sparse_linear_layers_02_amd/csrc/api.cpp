@@ -291,6 +291,12 @@ sbn_status sbn_workspace_bytes(sbn_op op, int64_t T, int64_t R, int64_t K, int n
       SBN_TRY(check_k(K));
       *bytes = gemm_ws_bytes(T, R, K, n, m);
       return ok();
+    case SBN_OP_GEMM_PREPARED:
+      SBN_TRY(check_rows("T", T));
+      SBN_TRY(check_k(K));
+      SBN_TRY(check_nm(n, m));
+      *bytes = gemm_x_bytes(T, K, n, m);
+      return ok();
     case SBN_OP_FORWARD:
       SBN_TRY(check_nm(n, m));
       SBN_TRY(check_rows("T", T));
@@ -390,6 +396,53 @@ sbn_status sbn_sparse_ternary_gemm(const int8_t* Xq, const float* s_x, int64_t T
   return hip_result(launch_gemm(Xq, s_x, T, K, codes, n == m ? nullptr : meta, s_w, R, n, m, Y,
                                 ydt, ldy, ws, st),
                     st, fn);
+}
+
+sbn_status sbn_gemm_weight_bytes(int64_t R, int64_t K, int n, int m, size_t* bytes) {
+  const char* fn = "sbn_gemm_weight_bytes";
+  SBN_NONNULL(bytes);
+  SBN_TRY(check_nm(n, m));
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  *bytes = gemm_weight_bytes(R, K, n, m);
+  return ok();
+}
+
+sbn_status sbn_prepare_gemm_weight(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, int n, int m,
+                                   uint8_t* prepared, void* stream) {
+  const char* fn = "sbn_prepare_gemm_weight";
+  SBN_NONNULL(codes);
+  SBN_NONNULL(prepared);
+  SBN_TRY(check_nm(n, m));
+  if (n < m) SBN_NONNULL(meta);
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  SBN_ALIGNED(codes);
+  if (n < m) SBN_ALIGNED(meta);
+  SBN_ALIGNED(prepared);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_prepare_gemm_weight(codes, n == m ? nullptr : meta, R, K, n, m, prepared, st), st, fn);
+}
+
+sbn_status sbn_sparse_ternary_gemm_prepared(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                            const uint8_t* prepared, const float* s_w, int64_t R, int n, int m,
+                                            void* Y, sbn_dtype ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  const char* fn = "sbn_sparse_ternary_gemm_prepared";
+  SBN_NONNULL(prepared);
+  // the packed-weight checks with the prepared operand standing in for both planes
+  SBN_TRY(check_matmul_args(fn, Xq, s_x, T, K, prepared, prepared, s_w, R, n, m, Y, ydt, ldy));
+  const size_t need = gemm_x_bytes(T, K, n, m);
+  if (need > 0) {
+    SBN_NONNULL(ws);
+    SBN_ALIGNED(ws);
+    if (ws_bytes < need)
+      return fail(SBN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_gemm_prepared(Xq, s_x, T, K, prepared, s_w, R, n, m, Y, ydt, ldy, ws, st), st, fn);
 }
 
 sbn_status sbn_forward(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, const uint16_t* X, int64_t T,

@@ -17,7 +17,9 @@
 // 1 KB global->LDS transfer and every LDS read a contiguous 16-byte read:
 //   expand (sparse or dense) : packed codes + meta -> W fragments
 //   tile_x                   : Xq [T][K] row-major -> X fragments, zero padded
-// then the GEMM.
+// then the GEMM.  A weight prepared once (sbn_prepare_gemm_weight: the
+// expansion alone, into a caller buffer) serves later calls with no layout
+// launch: the GEMM then loads the X fragments straight from row-major Xq.
 //
 // GEMM: 512 threads (8 waves), block tile 256 rows x 256 tokens, wave tile
 // 128 rows x 64 tokens (8 x 4 accumulator tiles of 16 x 16 int32) -- or 128 /
@@ -223,6 +225,7 @@ __device__ inline void tile_of_block(int64_t b, int64_t ntR, int64_t ntT, int64_
   tt = j / gr;
 }
 
+
 __device__ inline void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 // workgroup barrier kept in program order with the surrounding waits
 __device__ inline void pp_barrier() {
@@ -234,11 +237,11 @@ __device__ inline void pp_barrier() {
 // OUT: 0 = int32 accumulator, 1 = float32, 2 = bf16.
 // MJ: token fragments per wave (4: 256-token block tile; 2 and 1: 128 and 64
 // tokens, for token counts whose 256 x 256 grid would leave compute units idle).
-template <bool SPARSE, int OUT, int MJ>
+template <bool SPARSE, int OUT, int MJ, bool DX>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(
     const uint8_t* __restrict__ Aw, const uint8_t* __restrict__ Ai, const uint8_t* __restrict__ Xt,
     const float* __restrict__ s_x, const float* __restrict__ s_w, int64_t T, int64_t R,
-    int64_t nks, int64_t fstride, int64_t KC, void* __restrict__ Y, int64_t ldy) {
+    int64_t nks, int64_t fstride, int64_t KC, int64_t ldx, void* __restrict__ Y, int64_t ldy) {
   constexpr int NW = 8, MI = 8;                        // 8 waves; wave tile 8 x MJ fragments
   constexpr int TT = 64 * MJ;                          // tokens per block tile
   constexpr int A_BYTES = 16 * 1024;                   // 16 row fragments
@@ -276,6 +279,23 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   }
   if (OUT != 0) sw = *s_w;
 
+  // DX: X straight from Xq [T][ldx] instead of the tiled copy, into the same
+  // LDS layout: lane l of 1 KB block hb reads token 16*(hb/BH) + l%16 of the
+  // tile, bytes 16*(l/16).. of 64-byte chunk step*BH + hb%BH of its row.
+  // Tokens past T re-read token T - 1 (they feed only outputs never stored);
+  // a chunk past K (the upper half of a last 128-K step) re-reads chunk KC - 1
+  // (KC = K / 64 here), whose weights are zero.
+  const int8_t* xbase = (const int8_t*)Xt + tile_t * ldx;
+  uint32_t xoff[NXB / NW];
+  if constexpr (DX) {
+#pragma unroll
+    for (int q = 0; q < NXB / NW; ++q) {
+      const int hb = wave + NW * q;
+      const int64_t t = tile_t + 16 * (hb / BH) + (lane & 15);
+      xoff[q] = (uint32_t)(((t < T ? t : T - 1) - tile_t) * ldx + 16 * (lane >> 4));
+    }
+  }
+
   auto load_stage = [&](int s, int64_t ks) {
     uint8_t* base = smem + s * STAGE;
 #pragma unroll
@@ -288,8 +308,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
 #pragma unroll
     for (int q = 0; q < NXB / NW; ++q) {
       const int hb = wave + NW * q;                    // 1 KB block: token block hb/BH, half hb%BH
-      g2lds16(Xt + ((tb0 + hb / BH) * KC + ks * BH + hb % BH) * 1024 + lane * 16,
-              base + A_BYTES + I_BYTES + hb * 1024);
+      if constexpr (DX) {
+        int64_t kc = ks * BH + hb % BH;
+        kc = kc < KC ? kc : KC - 1;
+        g2lds16(xbase + kc * 64 + xoff[q], base + A_BYTES + I_BYTES + hb * 1024);
+      } else {
+        g2lds16(Xt + ((tb0 + hb / BH) * KC + ks * BH + hb % BH) * 1024 + lane * 16,
+                base + A_BYTES + I_BYTES + hb * 1024);
+      }
     }
   };
 
@@ -443,7 +469,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   }
 }
 
-template <bool SPARSE, int MJ>
+template <bool SPARSE, int MJ, bool DX>
 hipError_t launch_gemm_mj(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
                           const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y,
                           sbn_dtype ydt, int64_t ldy, hipStream_t st) {
@@ -451,17 +477,17 @@ hipError_t launch_gemm_mj(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* X
   const dim3 grid((unsigned)ntiles), block(512);
   const int64_t nks = SPARSE ? KBn : K / 64;
   const int64_t fstride = SPARSE ? KBn : 2 * KBn;
-  const int64_t KC = 2 * KBn;
+  const int64_t KC = DX ? K / 64 : 2 * KBn, ldx = K;  // 64-byte chunks of an X row (direct) or a tiled row
   const char* name = SPARSE ? "gemm_smfmac" : "gemm_mfma";
   if (ydt == SBN_I32_ACC)
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 0, MJ>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC,
-               Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 0, MJ, DX>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC,
+               ldx, Y, ldy);
   else if (ydt == SBN_F32)
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 1, MJ>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC,
-               Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 1, MJ, DX>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC,
+               ldx, Y, ldy);
   else
-    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 2, MJ>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC,
-               Y, ldy);
+    SBN_LAUNCH(name, (gemm_kernel<SPARSE, 2, MJ, DX>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, nks, fstride, KC,
+               ldx, Y, ldy);
   return hipGetLastError();
 }
 
@@ -486,20 +512,21 @@ int gemm_mj(bool sparse, int64_t T, int64_t R) {
   return best;
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool DX>
 hipError_t launch_gemm_t(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
                          const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y,
                          sbn_dtype ydt, int64_t ldy, hipStream_t st) {
   const int mj = gemm_mj(SPARSE, T, R);
-  if (mj == 4) return launch_gemm_mj<SPARSE, 4>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
-  if (mj == 2) return launch_gemm_mj<SPARSE, 2>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
-  if (SPARSE) return launch_gemm_mj<SPARSE, SPARSE ? 1 : 2>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+  if (mj == 4) return launch_gemm_mj<SPARSE, 4, DX>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+  if (mj == 2) return launch_gemm_mj<SPARSE, 2, DX>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+  if (SPARSE) return launch_gemm_mj<SPARSE, SPARSE ? 1 : 2, DX>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 bool gemm_uses_smfmac(int n, int m) { return n <= 2 && (m == 4 || m == 8); }
+
 
 static int64_t gemm_rb(int64_t R) { return round_up(R, GEMM_TILE_R) / 16; }
 static int64_t gemm_tbp(int64_t T) { return round_up(T, GEMM_TILE_T) / 16; }
@@ -527,44 +554,87 @@ size_t gemm_ws_bytes(int64_t T, int64_t R, int64_t K, int n, int m) {
   return g.w_bytes + g.i_bytes + g.x_bytes;
 }
 
-hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
-                       const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
-                       int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, void* ws, hipStream_t st) {
-  const int64_t RB = gemm_rb(R), KBn = cdiv(K, 128), TBp = gemm_tbp(T), KC = 2 * KBn;
+// The GEMM call in parts: the layout launch expands W into `w` (expand_w),
+// beside it tiles X into `xt` when the GEMM follows (run_gemm); without the
+// expansion (a prepared weight in `w`) the GEMM reads X straight from Xq: no
+// layout launch runs then, while the main loop is 5-10% faster on the tiled
+// copy, which otherwise rides beside the expansion almost for free.
+static hipError_t gemm_parts(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const uint8_t* codes,
+                             const uint8_t* meta, const float* s_w, int64_t R, int n, int m, void* Y, sbn_dtype ydt,
+                             int64_t ldy, uint8_t* w, uint8_t* xt, bool expand_w, bool run_gemm, hipStream_t st) {
+  const bool dx = !expand_w, tile_x = expand_w && run_gemm;
+  if (dx) xt = (uint8_t*)Xq;
+  const int64_t RB = gemm_rb(R), KBn = cdiv(K, 128), TBp = tile_x ? gemm_tbp(T) : 0, KC = 2 * KBn;
   const GemmWs g = gemm_ws(T, R, K, n, m);
-  uint8_t* w = (uint8_t*)ws;
-  uint8_t* xt = w + g.w_bytes + g.i_bytes;
   const XTileArgs xa{Xq, T, K, TBp, KC, (uint4*)xt};
-  const int64_t nbx = cdiv(TBp * KC * 64, 256);                // X tiling blocks
+  const int64_t nbx = tile_x ? cdiv(TBp * KC * 64, 256) : 0;   // X tiling blocks
   const int64_t cplane = round_up(R * (K * n / (4 * m)), 16);  // readable bytes of the codes plane
   hipError_t e;
   if (gemm_uses_smfmac(n, m)) {
     uint8_t* vals = w;
     uint32_t* idx = (uint32_t*)(w + g.w_bytes);
-    const int64_t nbw = cdiv((RB / 4) * KBn * 64, 256);
-    SBN_LAUNCH("layout_sparse", layout_sparse_kernel, dim3((unsigned)(nbw + nbx)), dim3(256), 0, st,
-               codes, meta, R, K, n, m, RB, KBn, cplane, vals, idx, nbw, xa);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_gemm_t<true>(vals, (const uint8_t*)idx, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+    const int64_t nbw = expand_w ? cdiv((RB / 4) * KBn * 64, 256) : 0;
+    if (nbw + nbx > 0) {
+      SBN_LAUNCH("layout_sparse", layout_sparse_kernel, dim3((unsigned)(nbw + nbx)), dim3(256), 0, st,
+                 codes, meta, R, K, n, m, RB, KBn, cplane, vals, idx, nbw, xa);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (!run_gemm) return hipSuccess;
+    return dx ? launch_gemm_t<true, true>(vals, (const uint8_t*)idx, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st)
+              : launch_gemm_t<true, false>(vals, (const uint8_t*)idx, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
   }
   const int64_t KD = 2 * KBn;
-  int64_t nbw = cdiv(RB * KD * 64, 256);
+  int64_t nbw = expand_w ? cdiv(RB * KD * 64, 256) : 0;
   if (nbw > 1024) nbw = 1024;                              // four blocks per CU, each table built once
   const uint8_t* mp = (n == m) ? nullptr : meta;
-  const dim3 lgrid((unsigned)(nbw + nbx)), lblock(256);
+  if (nbw + nbx > 0) {
+    const dim3 lgrid((unsigned)(nbw + nbx)), lblock(256);
 #define SBN_LD_CASE(MM, NN)                                                                                  \
   else if (m == MM && n == NN) SBN_LAUNCH("layout_dense", (layout_dense_kernel<MM, NN>), lgrid, lblock, 0, st, \
                                           codes, mp, R, K, RB, KD, cplane, w, nbw, xa);
-  if (false) {
-  }
-  SBN_LD_CASE(4, 3) SBN_LD_CASE(4, 4)
-  SBN_LD_CASE(8, 3) SBN_LD_CASE(8, 4) SBN_LD_CASE(8, 5) SBN_LD_CASE(8, 6) SBN_LD_CASE(8, 7) SBN_LD_CASE(8, 8)
+    if (false) {
+    }
+    SBN_LD_CASE(4, 3) SBN_LD_CASE(4, 4)
+    SBN_LD_CASE(8, 3) SBN_LD_CASE(8, 4) SBN_LD_CASE(8, 5) SBN_LD_CASE(8, 6) SBN_LD_CASE(8, 7) SBN_LD_CASE(8, 8)
 #undef SBN_LD_CASE
-  else return hipErrorInvalidValue;
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_gemm_t<false>(w, nullptr, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+    else return hipErrorInvalidValue;
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!run_gemm) return hipSuccess;
+  return dx ? launch_gemm_t<false, true>(w, nullptr, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st)
+            : launch_gemm_t<false, false>(w, nullptr, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+}
+
+size_t gemm_weight_bytes(int64_t R, int64_t K, int n, int m) {
+  const GemmWs g = gemm_ws(1, R, K, n, m);
+  return g.w_bytes + g.i_bytes;
+}
+
+// the GEMM on a prepared weight reads the activations in place
+size_t gemm_x_bytes(int64_t, int64_t, int, int) { return 0; }
+
+hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                       const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
+                       int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, void* ws, hipStream_t st) {
+  const GemmWs g = gemm_ws(T, R, K, n, m);
+  uint8_t* w = (uint8_t*)ws;
+  return gemm_parts(Xq, s_x, T, K, codes, meta, s_w, R, n, m, Y, ydt, ldy, w, w + g.w_bytes + g.i_bytes, true, true,
+                    st);
+}
+
+hipError_t launch_prepare_gemm_weight(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, int n, int m,
+                                      uint8_t* prepared, hipStream_t st) {
+  return gemm_parts(nullptr, nullptr, 0, K, codes, meta, nullptr, R, n, m, nullptr, SBN_BF16, 0, prepared, nullptr,
+                    true, false, st);
+}
+
+hipError_t launch_gemm_prepared(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const uint8_t* prepared,
+                                const float* s_w, int64_t R, int n, int m, void* Y, sbn_dtype ydt, int64_t ldy,
+                                void* ws, hipStream_t st) {
+  return gemm_parts(Xq, s_x, T, K, nullptr, nullptr, s_w, R, n, m, Y, ydt, ldy, (uint8_t*)prepared, nullptr,
+                    false, true, st);
 }
 
 }  // namespace sbn

@@ -78,6 +78,8 @@ constexpr int GEMM_TILE_R = 256;
 constexpr int GEMM_TILE_T = 256;
 bool gemm_uses_smfmac(int n, int m);
 size_t gemm_ws_bytes(int64_t T, int64_t R, int64_t K, int n, int m);
+size_t gemm_weight_bytes(int64_t R, int64_t K, int n, int m);   // the prepared (expanded) weight operand
+size_t gemm_x_bytes(int64_t T, int64_t K, int n, int m);         // tiled activations of a prepared-weight GEMM
 size_t bwd_ws_bytes(int64_t T, int64_t R, int64_t K, int n, int m);
 
 // ----------------------------------------------------------------- kernel timing
@@ -106,6 +108,13 @@ hipError_t launch_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx
 hipError_t launch_pack_quant(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
                              uint8_t* codes, uint8_t* meta, float* s_w, void* ws, uint32_t flags,
                              const uint16_t* X, int64_t T, int64_t ldx, int8_t* Xq, float* s_x, hipStream_t st);
+// The weight operand of the GEMM expanded once (for weights used by many calls),
+// and the GEMM on it (the activations are tiled into ws, gemm_x_bytes).
+hipError_t launch_prepare_gemm_weight(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, int n, int m,
+                                      uint8_t* prepared, hipStream_t st);
+hipError_t launch_gemm_prepared(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const uint8_t* prepared,
+                                const float* s_w, int64_t R, int n, int m, void* Y, sbn_dtype ydt, int64_t ldy,
+                                void* ws, hipStream_t st);
 hipError_t launch_gemm(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                        const uint8_t* codes, const uint8_t* meta, const float* s_w, int64_t R,
                        int n, int m, void* Y, sbn_dtype ydt, int64_t ldy, void* ws, hipStream_t st);

@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = sbn.header_symbols()
-    assert len(names) == 22
+    assert len(names) == 25
     for nm in names:
         assert hasattr(L, nm), nm
 
@@ -225,3 +225,20 @@ def test_decode_plane_validation(L):
     assert g(P, P, 4, 256, None, P, 64, P, 1, 64, None) == NULL
     assert g(P, P, 4, 256, P, P, 64, P, 1, 60, None) == SHAPE      # ldy < R
     assert g(P, P, 4, 256, P, P, 64, P, 7, 64, None) == DTYPE
+
+
+def test_prepared_weight_validation(L):
+    assert sbn.sbn_gemm_weight_bytes(6912, 2560, 2, 4) >= 6912 * 2560 // 2
+    assert sbn.sbn_gemm_weight_bytes(4096, 4096, 6, 8) >= 4096 * 4096
+    # the GEMM on a prepared weight reads the activations in place: no workspace
+    for n, m in ((2, 4), (1, 8), (6, 8), (8, 8)):
+        assert sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM_PREPARED, 300, 0, 576, n, m) == 0
+    # the GEMM from packed planes holds the expanded weight and the tiled activations
+    assert sbn.sbn_workspace_bytes(sbn.SBN_OP_GEMM, 4096, 6912, 2560, 2, 4) == \
+        sbn.sbn_gemm_weight_bytes(6912, 2560, 2, 4) + 4096 * 2560
+    f = L.sbn_prepare_gemm_weight
+    assert f(P, None, 16, 256, 2, 4, P2, None) == NULL
+    assert f(P, P, 16, 250, 2, 4, P2, None) == SHAPE
+    g = L.sbn_sparse_ternary_gemm_prepared
+    assert g(P, P, 16, 256, None, P, 64, 2, 4, P2, 1, 64, P, 1 << 20, None) == NULL
+    assert g(P, P, 16, 256, P, P, 64, 2, 4, P2, 1, 60, P, 1 << 20, None) == SHAPE
