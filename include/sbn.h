@@ -43,6 +43,11 @@
  *     abort crosses the ABI.
  *   - Inputs with NaN or Inf are outside the contract.  Activations with
  *     |x| >= 2^120 are outside the contract (127*x must not overflow).
+ *     With the environment variable SBN_CHECK_FINITE=1 (read on every call),
+ *     the calls that take bf16 or fp32 inputs (W, G, X, dY) scan them first
+ *     and return SBN_ERR_VALUE, launching nothing else, if one holds a NaN or
+ *     Inf.  The scan synchronises the stream (a diagnostic mode) and is
+ *     skipped while the stream is being captured into a graph.
  *   - Calls that share a workspace must be ordered on one stream.
  */
 #ifndef SBN_H
@@ -67,7 +72,8 @@ typedef enum sbn_status {
   SBN_ERR_DTYPE = 6,           /* output dtype not allowed for this call */
   SBN_ERR_HIP = 7,             /* a HIP launch or runtime call failed */
   SBN_ERR_FLAGS = 8,           /* a flag bit this call does not accept */
-  SBN_ERR_VALUE = 9            /* a scalar argument out of range (e.g. a non-finite lr) */
+  SBN_ERR_VALUE = 9            /* a scalar argument out of range (e.g. a non-finite lr), or a
+                                  non-finite input under SBN_CHECK_FINITE=1 */
 } sbn_status;
 
 typedef enum sbn_dtype {

@@ -30,6 +30,7 @@ SBN_FLAGS_NONE, SBN_MASK_FROM_TERNARY, SBN_GRAD_W_MASKED = 0, 1, 2
 STATUS = {0: "SBN_OK", 1: "SBN_ERR_NULL", 2: "SBN_ERR_SHAPE", 3: "SBN_ERR_UNSUPPORTED_NM",
           4: "SBN_ERR_ALIGN", 5: "SBN_ERR_WORKSPACE", 6: "SBN_ERR_DTYPE", 7: "SBN_ERR_HIP",
           8: "SBN_ERR_FLAGS", 9: "SBN_ERR_VALUE"}
+SBN_ERR_VALUE = 9
 
 
 class SbnError(RuntimeError):
@@ -440,6 +441,7 @@ __all__ = [
     "sbn_backward", "sbn_backward_ex", "sbn_mask_ternarize_pack_ex", "sbn_sgd_update_pack", "sbn_forward",
     "sbn_decode_plane_bytes", "sbn_repack_d2", "sbn_ternary_gemv_d2", "sbn_ternary_gemv_d2_batched",
     "sbn_gemm_weight_bytes", "sbn_prepare_gemm_weight", "sbn_sparse_ternary_gemm_prepared", "SBN_OP_GEMM_PREPARED",
+    "SBN_ERR_VALUE",
     "SBN_FLAGS_NONE", "SBN_MASK_FROM_TERNARY", "SBN_GRAD_W_MASKED",
     "SBN_F32", "SBN_BF16", "SBN_I32_ACC", "SBN_OP_PACK", "SBN_OP_ACT_QUANT", "SBN_OP_GEMM",
     "SBN_OP_GEMV", "SBN_OP_BACKWARD", "SBN_OP_FORWARD", "sbn_profile_enable", "sbn_profile_reset", "sbn_profile_dump",

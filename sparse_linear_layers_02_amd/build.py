@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "libsbn")
 LIB = os.path.join(PKG, "libsbn.so")
 
-SOURCES = ["api.cpp", "pack.hip", "act_quant.hip", "gemm.hip", "gemv.hip", "backward.hip"]
+SOURCES = ["api.cpp", "pack.hip", "act_quant.hip", "gemm.hip", "gemv.hip", "backward.hip", "finite.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -42,6 +42,22 @@ bool debug_sync() {
   return on;
 }
 
+// SBN_CHECK_FINITE=1: entry points scan their floating-point inputs for
+// NaN / Inf first (read on every call, so a process can switch it).  Skipped
+// while the stream is being captured: the scan reads a flag back to the host.
+sbn_status check_finite(const char* fn, const char* what, const void* x, int64_t rows, int64_t cols, int64_t ld,
+                        int elem_bytes, hipStream_t st) {
+  const char* env = std::getenv("SBN_CHECK_FINITE");
+  if (!(env && env[0] == '1')) return SBN_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return SBN_OK;
+  bool found = false;
+  const hipError_t e = scan_nonfinite(x, rows, cols, ld, elem_bytes, st, &found);
+  if (e != hipSuccess) return fail(SBN_ERR_HIP, "%s: finite check of %s: %s", fn, what, hipGetErrorString(e));
+  if (found) return fail(SBN_ERR_VALUE, "%s: %s holds a NaN or Inf (SBN_CHECK_FINITE)", fn, what);
+  return SBN_OK;
+}
+
 sbn_status hip_result(hipError_t e, hipStream_t st, const char* what) {
   if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(SBN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -338,6 +354,8 @@ static sbn_status pack_common(const char* fn, const uint16_t* W, int64_t R, int6
   if (ws_bytes < need)
     return fail(SBN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
+  SBN_TRY(check_finite(fn, "W", W, R, K, ldw, 2, st));
+  if (G) SBN_TRY(check_finite(fn, "G", G, R, K, ldg, 4, st));
   return hip_result(launch_pack(W, R, K, ldw, n, m, codes, meta, s_w, ws, flags, G, ldg, lr, st), st, fn);
 }
 
@@ -378,6 +396,7 @@ sbn_status sbn_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, i
   SBN_ALIGNED(X);
   SBN_ALIGNED(Xq);
   hipStream_t st = (hipStream_t)stream;
+  SBN_TRY(check_finite(fn, "X", X, T, K, ldx, 2, st));
   return hip_result(launch_act_quant(X, T, K, ldx, Xq, s_x, st), st, fn);
 }
 
@@ -466,6 +485,8 @@ sbn_status sbn_forward(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, con
   if (ws_bytes < need)
     return fail(SBN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
+  SBN_TRY(check_finite(fn, "W", W, R, K, ldw, 2, st));
+  SBN_TRY(check_finite(fn, "X", X, T, K, ldx, 2, st));
   uint8_t* mp = n == m ? nullptr : meta;
   hipError_t e = launch_pack_quant(W, R, K, ldw, n, m, codes, mp, s_w, ws, flags, X, T, ldx, Xq, s_x, st);
   if (e == hipSuccess)
@@ -549,6 +570,7 @@ static sbn_status backward_common(const char* fn, const uint16_t* dY, int64_t T,
   if (ws_bytes < need)
     return fail(SBN_ERR_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn, ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
+  SBN_TRY(check_finite(fn, "dY", dY, T, R, R, 2, st));
   return hip_result(launch_backward(dY, T, R, Xq, s_x, K, codes, n == m ? nullptr : meta, s_w, n,
                                     m, dX, dxdt, dW, ws, flags, st),
                     st, fn);

@@ -77,6 +77,11 @@ PackPlan pack_plan(int64_t R, int64_t K);
 constexpr int GEMM_TILE_R = 256;
 constexpr int GEMM_TILE_T = 256;
 bool gemm_uses_smfmac(int n, int m);
+// The optional input check: *found = any NaN / Inf among the first `cols`
+// elements (2- or 4-byte floats) of `rows` rows at stride `ld` elements.
+// Synchronizes `st`.
+hipError_t scan_nonfinite(const void* x, int64_t rows, int64_t cols, int64_t ld, int elem_bytes, hipStream_t st,
+                          bool* found);
 size_t gemm_ws_bytes(int64_t T, int64_t R, int64_t K, int n, int m);
 size_t gemm_weight_bytes(int64_t R, int64_t K, int n, int m);   // the prepared (expanded) weight operand
 size_t gemm_x_bytes(int64_t T, int64_t K, int n, int m);         // tiled activations of a prepared-weight GEMM

@@ -230,3 +230,49 @@ def test_forward_prefill_size_equals_separate_calls():
     torch.cuda.synchronize()
     for x, y in zip(a, (codes, meta, s_w, Xq, s_x, Y)):
         assert torch.equal(x, y)
+
+
+# ------------------------------------------------------------------ optional non-finite input check
+def test_check_finite_rejects_nonfinite_inputs(monkeypatch):
+    """SBN_CHECK_FINITE=1: a NaN or Inf in W, G, X or dY is rejected with
+    SBN_ERR_VALUE before anything launches (outputs untouched); finite inputs
+    give the unchecked results; without the variable nothing is scanned."""
+    import torch
+    R, K, T = 64, 256, 24
+    W = gaussian_bf16((R, K), 0.02, seed=5, stream=0)
+    X = gaussian_bf16((T, K), 1.0, seed=5, stream=1)
+    dY = gaussian_bf16((T, R), 1e-2, seed=5, stream=2)
+    ref = sbn.sbn_mask_ternarize_pack(dev_bf16(W), 2, 4)
+    monkeypatch.setenv("SBN_CHECK_FINITE", "1")
+    got = sbn.sbn_mask_ternarize_pack(dev_bf16(W), 2, 4)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(ref, got))
+    Xq, s_x = sbn.sbn_act_quant(dev_bf16(X))
+    codes, meta, s_w = got
+
+    def rejected(call):
+        with pytest.raises(sbn.SbnError) as ei:
+            call()
+        assert ei.value.status == sbn.SBN_ERR_VALUE, str(ei.value)
+
+    for bits, where in ((0x7FC0, (3, 100)), (0x7F80, (63, 255)), (0xFF80, (0, 0))):   # NaN, +Inf, -Inf
+        Wb = W.copy(); Wb[where] = bits
+        codes2 = torch.full_like(codes, 0x5A)
+        rejected(lambda: sbn.sbn_mask_ternarize_pack(dev_bf16(Wb), 2, 4, codes=codes2))
+        assert bool((codes2 == 0x5A).all()), "output touched"
+        Xb = X.copy(); Xb[min(where[0], T - 1), where[1]] = bits
+        rejected(lambda: sbn.sbn_act_quant(dev_bf16(Xb)))
+        rejected(lambda: sbn.sbn_forward(dev_bf16(W), dev_bf16(Xb), 2, 4))
+        dYb = dY.copy(); dYb[min(where[0], T - 1), min(where[1], R - 1)] = bits
+        rejected(lambda: sbn.sbn_backward(dev_bf16(dYb), Xq, s_x, codes, meta, s_w, 2, 4))
+    G = np.zeros((R, K), dtype=np.float32); G[7, 9] = np.inf
+    rejected(lambda: sbn.sbn_sgd_update_pack(dev_bf16(W), dev(G), 0.1, 2, 4))
+    # padding columns past K are not scanned
+    Wp = np.full((R, K + 64), 0x7FC0, dtype=np.uint16); Wp[:, :K] = W
+    got = sbn.sbn_mask_ternarize_pack(dev_bf16(Wp)[:, :K], 2, 4)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(ref, got))
+    monkeypatch.delenv("SBN_CHECK_FINITE")
+    Wb = W.copy(); Wb[3, 100] = 0x7FC0
+    sbn.sbn_mask_ternarize_pack(dev_bf16(Wb), 2, 4)        # outside the contract, but not rejected
+    torch.cuda.synchronize()
