@@ -51,8 +51,9 @@ constexpr int GT = 256;
 __device__ inline int8_t code_to_i8(uint32_t c) { return c == 1u ? (int8_t)1 : c == 3u ? (int8_t)-1 : (int8_t)0; }
 
 // ---------------------------------------------------------------- expansion: sparse operand
-// One thread = one lane of four row-consecutive (16-row, 128-K) fragments: per
-// fragment 16 compressed values + 32 index bits.
+// 1:4, 1:8, 2:8 (2:4 has its own mapping below): one thread = one lane of
+// four row-consecutive (16-row, 128-K) fragments: per fragment 16 compressed
+// values + 32 index bits.
 // vals [RB][KBn][64][16 B]; idx [RB/4][KBn][64][4 x u32] (row fragment 4g+q in
 // word q, so a thread's four index words are one 16-byte store)
 __device__ inline void expand_sparse_block(
@@ -72,14 +73,7 @@ __device__ inline void expand_sparse_block(
     const int64_t r = rb * 16 + (l & 15);
     v4i a = (v4i){0, 0, 0, 0};
     uint32_t ix = 0x44444444u;                  // (0,1) in every half: harmless with zero values
-    if (r < R && k0 < K && n == 2 && m == 4) {
-      // 2:4: meta and codes of these 32 positions are one aligned word each
-      const uint32_t mb = *(const uint32_t*)(meta + r * (K / 8) + k0 / 8);
-      const uint32_t cb = *(const uint32_t*)(codes + r * (K / 8) + k0 / 8);
-      int ixi;
-      decode24(mb, cb, a, ixi);
-      ix = (uint32_t)ixi;
-    } else if (r < R && k0 < K) {
+    if (r < R && k0 < K) {
       // 1:4, 1:8, 2:8: at most two survivors per half-group of four positions.
       // The 32 meta bits and the (<= 16) code bits of these positions come from
       // aligned words; each half-group's survivors take the next codes in order.
@@ -118,6 +112,51 @@ __device__ inline void expand_sparse_block(
     ixs[q] = ix;
   }
   *(uint4*)(idx + ((g * KBn + kb) * 64 + l) * 4) = make_uint4(ixs[0], ixs[1], ixs[2], ixs[3]);
+}
+
+// 2:4: one thread = one row of one 128-K step, i.e. the lanes r%16 + 16*j
+// (j = 0..3) of row fragment r/16: the row's 16 meta and 16 code bytes of the
+// step (positions in order, so four aligned 32-bit words each) come in two
+// wide loads, and the 64 threads of a wave (16 rows x 4 row fragments of one
+// index block) write whole 256-byte runs of values and of index words.
+__device__ inline void expand_sparse24_block(
+    int64_t blk, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+    int64_t RB, int64_t KBn, uint8_t* __restrict__ vals, uint32_t* __restrict__ idx) {
+  const int64_t gid = blk * 256 + threadIdx.x;
+  if (gid >= (RB / 4) * KBn * 64) return;
+  const int t = (int)(gid & 63), r16 = t & 15, q = t >> 4;
+  const int64_t f = gid >> 6;                   // = g * KBn + kb
+  const int64_t g = f / KBn, kb = f - g * KBn;
+  const int64_t rb = 4 * g + q, r = rb * 16 + r16;
+  const int64_t rowb = K / 8;                   // meta (and 2:4 code) bytes per row
+  uint32_t mw[4] = {0, 0, 0, 0}, cw[4] = {0, 0, 0, 0};
+  if (r < R) {
+    const uint8_t* mp = meta + r * rowb + kb * 16;
+    const uint8_t* cp = codes + r * rowb + kb * 16;
+    if (kb * 128 + 128 <= K && (rowb & 15) == 0) {
+      const uint4 m4 = *(const uint4*)mp, c4 = *(const uint4*)cp;
+      mw[0] = m4.x; mw[1] = m4.y; mw[2] = m4.z; mw[3] = m4.w;
+      cw[0] = c4.x; cw[1] = c4.y; cw[2] = c4.z; cw[3] = c4.w;
+    } else {                                    // rows 8-byte aligned; a last step may hold 64 positions
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (kb * 128 + 64 * h < K) {
+          const uint2 m2 = *(const uint2*)(mp + 8 * h), c2 = *(const uint2*)(cp + 8 * h);
+          mw[2 * h] = m2.x; mw[2 * h + 1] = m2.y;
+          cw[2 * h] = c2.x; cw[2 * h + 1] = c2.y;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int l = r16 + 16 * j;
+    v4i a = (v4i){0, 0, 0, 0};
+    int ix = 0x44444444;                        // (0,1) in every half: harmless with zero values
+    if (r < R && kb * 128 + 32 * j < K) decode24(mw[j], cw[j], a, ix);
+    *(v4i*)(vals + ((rb * KBn + kb) * 64 + l) * 16) = a;
+    idx[((g * KBn + kb) * 64 + l) * 4 + q] = (uint32_t)ix;
+  }
 }
 
 // ---------------------------------------------------------------- expansion: dense operand
@@ -159,19 +198,24 @@ __device__ inline void expand_dense_blocks(
 // ---------------------------------------------------------------- activation fragments
 // Xt [TBp][KC][64][16 B]: block (tb, kc) holds tokens 16*tb.. and K bytes
 // 64*kc..; lane l carries token 16*tb + l%16, K bytes 64*kc + 16*(l/16) ..+16.
-// Tokens >= T and K >= K are zero.
+// Tokens >= T and K >= K are zero.  One 256-thread block covers 16 tokens x
+// 256 K bytes (four Xt blocks): thread i reads 16 bytes of token i/16 (so a
+// wave reads four 256-byte row runs) and writes them to lane
+// i/16 + 16*((i%16)%4) of Xt block (i%16)/4 -- the four blocks are whole
+// within the workgroup, so their lines fill in one L2.
 __device__ inline void tile_x_block(int64_t blk, const int8_t* __restrict__ Xq, int64_t T, int64_t K,
                                     int64_t TBp, int64_t KC, uint4* __restrict__ Xt) {
-  const int64_t gid = blk * 256 + threadIdx.x;
-  if (gid >= TBp * KC * 64) return;
-  const int l = (int)(gid & 63);
-  const int64_t f = gid >> 6;
-  const int64_t tb = f / KC, kc = f - tb * KC;
-  const int64_t t = tb * 16 + (l & 15);
-  const int64_t k = kc * 64 + 16 * (l >> 4);
+  const int64_t spans = (KC + 3) / 4;
+  if (blk >= TBp * spans) return;
+  const int64_t tb = blk / spans, sp = blk - tb * spans;
+  const int i = threadIdx.x, tok = i >> 4, piece = i & 15;
+  const int64_t kc = sp * 4 + (piece >> 2);
+  if (kc >= KC) return;
+  const int64_t t = tb * 16 + tok;
+  const int64_t k = sp * 256 + 16 * piece;
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (t < T && k < K) v = *(const uint4*)(Xq + t * K + k);
-  Xt[gid] = v;
+  Xt[(tb * KC + kc) * 64 + tok + 16 * (piece & 3)] = v;
 }
 
 // ---------------------------------------------------------------- the two layout passes in one launch
@@ -189,9 +233,12 @@ __global__ __launch_bounds__(256) void layout_sparse_kernel(
     int n, int m, int64_t RB, int64_t KBn, int64_t cplane, uint8_t* __restrict__ vals,
     uint32_t* __restrict__ idx, int64_t nbw, const XTileArgs xa) {
   const int64_t b = blockIdx.x;
-  if (b < nbw)
-    expand_sparse_block(b, codes, meta, R, K, n, m, RB, KBn, cplane, vals, idx);
-  else
+  if (b < nbw) {
+    if (n == 2 && m == 4)
+      expand_sparse24_block(b, codes, meta, R, K, RB, KBn, vals, idx);
+    else
+      expand_sparse_block(b, codes, meta, R, K, n, m, RB, KBn, cplane, vals, idx);
+  } else
     tile_x_block(b - nbw, xa.Xq, xa.T, xa.K, xa.TBp, xa.KC, xa.Xt);
 }
 
@@ -567,7 +614,7 @@ static hipError_t gemm_parts(const int8_t* Xq, const float* s_x, int64_t T, int6
   const int64_t RB = gemm_rb(R), KBn = cdiv(K, 128), TBp = tile_x ? gemm_tbp(T) : 0, KC = 2 * KBn;
   const GemmWs g = gemm_ws(T, R, K, n, m);
   const XTileArgs xa{Xq, T, K, TBp, KC, (uint4*)xt};
-  const int64_t nbx = tile_x ? cdiv(TBp * KC * 64, 256) : 0;   // X tiling blocks
+  const int64_t nbx = tile_x ? TBp * cdiv(KC, 4) : 0;          // X tiling blocks (16 tokens x 256 K bytes)
   const int64_t cplane = round_up(R * (K * n / (4 * m)), 16);  // readable bytes of the codes plane
   hipError_t e;
   if (gemm_uses_smfmac(n, m)) {
