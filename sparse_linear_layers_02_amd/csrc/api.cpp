@@ -58,7 +58,13 @@ sbn_status check_finite(const char* fn, const char* what, const void* x, int64_t
   return SBN_OK;
 }
 
+thread_local bool g_injected = false;
+
 sbn_status hip_result(hipError_t e, hipStream_t st, const char* what) {
+  if (g_injected) {
+    g_injected = false;
+    return fail(SBN_ERR_HIP, "%s: launch failed (injected by SBN_TEST_INJECT_LAUNCH_FAILURE)", what);
+  }
   if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return fail(SBN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -188,6 +194,16 @@ hipError_t prof_collect() {
 }  // namespace
 
 namespace sbn {
+
+bool inject_launch_failure() {
+  static const bool on = [] {
+    const char* e = std::getenv("SBN_TEST_INJECT_LAUNCH_FAILURE");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+void note_injected_failure() { g_injected = true; }
 
 int prof_begin(hipStream_t st, const char* name) {
   if (!g_prof_on.load(std::memory_order_relaxed)) return -1;

@@ -94,11 +94,21 @@ int prof_begin(hipStream_t st, const char* name);
 void prof_end(int slot, hipStream_t st);
 
 // launch `kernel` on `st`, bracketed by timing events when timing is on
-#define SBN_LAUNCH(name, kernel, grid, block, shmem, st, ...)          \
-  do {                                                                 \
-    const int sbn_p_ = ::sbn::prof_begin((st), (name));                \
-    hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);   \
-    ::sbn::prof_end(sbn_p_, (st));                                     \
+// Test hook: with SBN_TEST_INJECT_LAUNCH_FAILURE=1 in the environment at the
+// first launch, no kernel is launched and the entry point reports SBN_ERR_HIP
+// (so the error path is testable on any machine, without touching memory).
+bool inject_launch_failure();
+void note_injected_failure();
+
+#define SBN_LAUNCH(name, kernel, grid, block, shmem, st, ...)            \
+  do {                                                                   \
+    if (::sbn::inject_launch_failure()) {                                \
+      ::sbn::note_injected_failure();                                    \
+    } else {                                                             \
+      const int sbn_p_ = ::sbn::prof_begin((st), (name));                \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, st, __VA_ARGS__);   \
+      ::sbn::prof_end(sbn_p_, (st));                                     \
+    }                                                                    \
   } while (0)
 
 // ----------------------------------------------------------------- launchers

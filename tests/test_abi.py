@@ -242,3 +242,51 @@ def test_prepared_weight_validation(L):
     g = L.sbn_sparse_ternary_gemm_prepared
     assert g(P, P, 16, 256, None, P, 64, 2, 4, P2, 1, 64, P, 1 << 20, None) == NULL
     assert g(P, P, 16, 256, P, P, 64, 2, 4, P2, 1, 60, P, 1 << 20, None) == SHAPE
+
+
+INJECT_SCRIPT = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+import sparse_linear_layers_02_amd as sbn
+L = sbn.lib()
+P, P2 = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+big = 1 << 30
+calls = {
+    "sbn_act_quant": lambda: L.sbn_act_quant(P, 16, 256, 256, P2, P2, None),
+    "sbn_mask_ternarize_pack": lambda: L.sbn_mask_ternarize_pack(P, 16, 256, 256, 2, 4, P2, P2, P2, P2, big, None),
+    "sbn_sparse_ternary_gemm": lambda: L.sbn_sparse_ternary_gemm(P, P, 16, 256, P, P, P, 64, 2, 4, P2, 1, 64, P2,
+                                                                 big, None),
+    "sbn_sparse_ternary_gemv": lambda: L.sbn_sparse_ternary_gemv(P, P, 4, 256, P, P, P, 64, 6, 8, P2, 1, 64, P2,
+                                                                 big, None),
+    "sbn_prepare_gemm_weight": lambda: L.sbn_prepare_gemm_weight(P, P, 64, 256, 2, 4, P2, None),
+    "sbn_backward": lambda: L.sbn_backward(P, 16, 64, P, P, 256, P, P, P, 2, 4, P2, 1, P2, P2, big, None),
+    "sbn_repack_d2": lambda: L.sbn_repack_d2(P, P, 64, 256, 2, 4, P2, None),
+}
+for name, call in calls.items():
+    st = call()
+    print(name, st, L.sbn_last_error().decode())
+# validation still runs first
+print("null", L.sbn_act_quant(None, 16, 256, 256, P2, P2, None))
+"""
+
+
+def test_injected_launch_failure_reports_hip_error(tmp_path):
+    """SBN_TEST_INJECT_LAUNCH_FAILURE=1: every launch is replaced by a failure
+    (nothing is launched), and each entry point returns SBN_ERR_HIP naming
+    itself; a validation error still wins.  Runs in a child process (the
+    variable is read once per process)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, SBN_TEST_INJECT_LAUNCH_FAILURE="1", HIP_VISIBLE_DEVICES="")
+    out = subprocess.run([sys.executable, "-c", INJECT_SCRIPT, root], env=env, capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 0, out.stderr
+    lines = out.stdout.strip().splitlines()
+    assert len(lines) == 8, out.stdout
+    for line in lines[:-1]:
+        name, st, msg = line.split(" ", 2)
+        assert int(st) == HIP, line
+        assert msg.startswith(name + ":") and "injected" in msg, line
+    assert lines[-1] == f"null {NULL}"
