@@ -1,5 +1,5 @@
 """HIP-graph replays of the one-call forward with the backward, of the fused
-SGD step, and of the decode-plane GEMV: every replay, with eager work and
+SGD step, of the decode-plane GEMV and of the prepared-weight GEMM: every replay, with eager work and
 synchronisation between replays, reproduces the eager results bit for bit
 (the bench times such replays)."""
 from __future__ import annotations
@@ -106,3 +106,23 @@ def test_graph_decode_plane_batched():
         sbn.sbn_ternary_gemv_d2_batched(Xq, s_x, d2s, sws, R, Ys=Ys)
 
     replay_matches(step, Ys)
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
+def test_graph_prepare_and_prepared_gemm(n, m):
+    """The weight preparation and two prepared GEMMs of different token counts
+    in one graph."""
+    import torch
+    R, K = 520, 576
+    W = dev_bf16(gaussian_bf16((R, K), 0.02, seed=34, stream=0))
+    codes, meta, s_w = sbn.sbn_mask_ternarize_pack(W, n, m)
+    pw = torch.empty(sbn.sbn_gemm_weight_bytes(R, K, n, m), dtype=torch.uint8, device="cuda")
+    xs = [sbn.sbn_act_quant(dev_bf16(gaussian_bf16((T, K), 1.0, seed=T, stream=1))) for T in (300, 7)]
+    Ys = [torch.empty((Xq.shape[0], R), dtype=torch.bfloat16, device="cuda") for Xq, _ in xs]
+
+    def step():
+        sbn.sbn_prepare_gemm_weight(codes, meta, R, K, n, m, prepared=pw)
+        for (Xq, s_x), Y in zip(xs, Ys):
+            sbn.sbn_sparse_ternary_gemm_prepared(Xq, s_x, pw, s_w, R, n, m, Y=Y)
+
+    replay_matches(step, [pw] + Ys, before=lambda: pw.zero_())
