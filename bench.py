@@ -654,8 +654,8 @@ def cpu_baseline_decode(wl, weights=POOL):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported in this build "
-              f"(multi-GPU sharding is described in DESIGN.md, not run).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              f"(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     import torch
     import sparse_linear_layers_02_amd as sbn
