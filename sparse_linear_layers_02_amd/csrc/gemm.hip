@@ -25,7 +25,8 @@
 // 128 rows x 64 tokens (8 x 4 accumulator tiles of 16 x 16 int32) -- or 128 /
 // 64 tokens per block (8 x 2 / 8 x 1 per wave) when the token count leaves
 // the 256 x 256 grid too few tiles for the 256 compute units; K step 128
-// (sparse, 3 LDS stages of 52 KB) or 64 (dense, 4 stages of 32 KB), stages
+// (sparse, 3 LDS stages of 52 KB; the 64-token tile 2 stages of two steps)
+// or 64 (dense, 4 stages of 32 KB), stages
 // filled with direct global->LDS loads issued two (sparse) or three (dense)
 // steps ahead.  The two waves that share a SIMD (w and w + 4) alternate
 // between a memory phase (LDS reads of one step's fragments into registers,
@@ -297,12 +298,17 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   constexpr int NXB = 4 * MJ * BH;                     // 1 KB X blocks per stage
   static_assert(NXB % NW == 0, "every wave loads the same number of X blocks");
   constexpr int B_BYTES = NXB * 1024;
-  constexpr int STAGE = A_BYTES + I_BYTES + B_BYTES;
-  constexpr int NST = SPARSE ? 3 : 4;
+  // KS K steps per stage: the 64-token sparse tile takes two per stage (two
+  // stages of 56 KB), so each ping-pong phase holds 16 matrix instructions
+  // per wave instead of 8 and the barriers per step halve.
+  constexpr int KS = (SPARSE && MJ == 1) ? 2 : 1;
+  constexpr int SUB = A_BYTES + I_BYTES + B_BYTES;     // one K step
+  constexpr int STAGE = KS * SUB;
+  constexpr int NST = KS == 2 ? 2 : SPARSE ? 3 : 4;
   // global loads per wave per stage: 2 W fragments, NXB / 8 X blocks, the
-  // index block (waves 0..3, sparse)
-  constexpr int LPS0 = 2 + (SPARSE ? 1 : 0) + NXB / NW;
-  constexpr int LPS1 = 2 + NXB / NW;
+  // index block (waves 0..3, sparse), per K step
+  constexpr int LPS0 = KS * (2 + (SPARSE ? 1 : 0) + NXB / NW);
+  constexpr int LPS1 = KS * (2 + NXB / NW);
   constexpr int WAIT0 = (NST - 2) * LPS0, WAIT1 = (NST - 2) * LPS1;
   constexpr int EPI_BYTES = NW * 16 * MJ * 272;         // bf16 epilogue staging, 16*MJ x 272 B per wave
   constexpr int SMEM = NST * STAGE > EPI_BYTES ? NST * STAGE : EPI_BYTES;
@@ -343,8 +349,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
     }
   }
 
-  auto load_stage = [&](int s, int64_t ks) {
-    uint8_t* base = smem + s * STAGE;
+  const int64_t nss = cdiv(nks, KS);                   // stages (the last may hold one K step)
+  auto load_stage = [&](int s, int64_t ss) {
+#pragma unroll
+  for (int u = 0; u < KS; ++u) {
+    const int64_t ks = ss * KS + u;
+    if (KS > 1 && ks >= nks) break;
+    uint8_t* base = smem + s * STAGE + u * SUB;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int i = wave + NW * q;
@@ -364,6 +375,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
                 base + A_BYTES + I_BYTES + hb * 1024);
       }
     }
+  }
   };
 
   v4i acc[MI][MJ];
@@ -371,48 +383,56 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < MJ; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
-  v4i a[MI], blo[MJ], bhi[MJ];
-  int ix[MI];
+  v4i a[KS][MI], blo[KS][MJ], bhi[KS][MJ];
+  int ix[KS][MI];
 
-  // memory phase of step s: issue the loads of stage s + NST - 1, read step s's fragments
+  // memory phase of stage s: issue the loads of stage s + NST - 1, read stage s's fragments
   auto mem_phase = [&](int64_t s) {
-    if (s + NST - 1 < nks) load_stage((int)((s + NST - 1) % NST), s + NST - 1);
-    const uint8_t* base = smem + (s % NST) * STAGE;
-    const uint8_t* bb = base + A_BYTES + I_BYTES;
+    if (s + NST - 1 < nss) load_stage((int)((s + NST - 1) % NST), s + NST - 1);
 #pragma unroll
-    for (int j = 0; j < MJ; ++j) {
-      const int jj = MJ * wt + j;
-      blo[j] = *(const v4i*)(bb + (jj * BH + 0) * 1024 + lane * 16);
-      if (SPARSE) bhi[j] = *(const v4i*)(bb + (jj * BH + 1) * 1024 + lane * 16);
-    }
+    for (int u = 0; u < KS; ++u) {
+      const uint8_t* base = smem + (s % NST) * STAGE + u * SUB;
+      const uint8_t* bb = base + A_BYTES + I_BYTES;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) a[i] = *(const v4i*)(base + (MI * wr + i) * 1024 + lane * 16);
-    if (SPARSE) {
+      for (int j = 0; j < MJ; ++j) {
+        const int jj = MJ * wt + j;
+        blo[u][j] = *(const v4i*)(bb + (jj * BH + 0) * 1024 + lane * 16);
+        if (SPARSE) bhi[u][j] = *(const v4i*)(bb + (jj * BH + 1) * 1024 + lane * 16);
+      }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const v4i v = *(const v4i*)(base + A_BYTES + (2 * wr + h) * 1024 + lane * 16);
-        ix[4 * h] = v[0]; ix[4 * h + 1] = v[1]; ix[4 * h + 2] = v[2]; ix[4 * h + 3] = v[3];
+      for (int i = 0; i < MI; ++i) a[u][i] = *(const v4i*)(base + (MI * wr + i) * 1024 + lane * 16);
+      if (SPARSE) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const v4i v = *(const v4i*)(base + A_BYTES + (2 * wr + h) * 1024 + lane * 16);
+          ix[u][4 * h] = v[0]; ix[u][4 * h + 1] = v[1]; ix[u][4 * h + 2] = v[2]; ix[u][4 * h + 3] = v[3];
+        }
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  auto comp_phase = [&]() {
+  auto comp_phase = [&](int64_t s) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int u = 0; u < KS; ++u) {
+      if (KS > 1 && s * KS + u >= nks) break;          // a last stage with one K step
 #pragma unroll
-      for (int j = 0; j < MJ; ++j) {
-        if (SPARSE) {
-          const v8i b = (v8i){blo[j][0], blo[j][1], blo[j][2], blo[j][3], bhi[j][0], bhi[j][1], bhi[j][2], bhi[j][3]};
-          acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a[i], b, acc[i][j], ix[i], 0, 0);
-        } else {
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], blo[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < MJ; ++j) {
+          if (SPARSE) {
+            const v8i b = (v8i){blo[u][j][0], blo[u][j][1], blo[u][j][2], blo[u][j][3],
+                                bhi[u][j][0], bhi[u][j][1], bhi[u][j][2], bhi[u][j][3]};
+            acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a[u][i], b, acc[i][j], ix[u][i], 0, 0);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][i], blo[u][j], acc[i][j], 0, 0, 0);
+          }
         }
-      }
+    }
   };
   // this wave's loads of stage s + 1 have landed (later stages may still fly)
   auto vm_wait = [&](int64_t s) {
     sched_fence();
-    if (s + NST - 1 < nks) {
+    if (s + NST - 1 < nss) {
       if (grp == 0) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(WAIT0) : "memory");
       else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(WAIT1) : "memory");
     } else {
@@ -430,25 +450,25 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   // its buffer is refilled (stage s + NST) from mem(s+1), after B(2s+2).
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < nks) load_stage(s, s);
+    if (s < nss) load_stage(s, s);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   pp_barrier();                                        // B0: stages 0 .. NST-2 visible
   if (grp == 0) {
-    for (int64_t s = 0; s < nks; ++s) {
+    for (int64_t s = 0; s < nss; ++s) {
       mem_phase(s);
       pp_barrier();
-      comp_phase();
+      comp_phase(s);
       vm_wait(s);
       pp_barrier();
     }
   } else {
     pp_barrier();
-    for (int64_t s = 0; s < nks; ++s) {
+    for (int64_t s = 0; s < nss; ++s) {
       mem_phase(s);
       vm_wait(s);
       pp_barrier();
-      comp_phase();
-      if (s + 1 < nks) pp_barrier();
+      comp_phase(s);
+      if (s + 1 < nss) pp_barrier();
     }
   }
 
