@@ -25,7 +25,7 @@
 // 128 rows x 64 tokens (8 x 4 accumulator tiles of 16 x 16 int32) -- or 128 /
 // 64 tokens per block (8 x 2 / 8 x 1 per wave) when the token count leaves
 // the 256 x 256 grid too few tiles for the 256 compute units; K step 128
-// (sparse, 3 LDS stages of 52 KB; the 64-token tile 2 stages of two steps)
+// (sparse, 3 LDS stages of 52 KB; the 64- and 128-token tiles 2 stages of two steps)
 // or 64 (dense, 4 stages of 32 KB), stages
 // filled with direct global->LDS loads issued two (sparse) or three (dense)
 // steps ahead.  The two waves that share a SIMD (w and w + 4) alternate
@@ -298,13 +298,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   constexpr int NXB = 4 * MJ * BH;                     // 1 KB X blocks per stage
   static_assert(NXB % NW == 0, "every wave loads the same number of X blocks");
   constexpr int B_BYTES = NXB * 1024;
-  // KS K steps per stage: the 64-token sparse tile takes two per stage (two
-  // stages of 56 KB), so each ping-pong phase holds 16 matrix instructions
-  // per wave instead of 8 and the barriers per step halve.
-  constexpr int KS = (SPARSE && MJ == 1) ? 2 : 1;
+  // KS K steps per stage: the 64- and 128-token sparse tiles take two per
+  // stage (two stages of 56 / 72 KB), so each ping-pong phase holds 16 / 32
+  // matrix instructions per wave instead of 8 / 16 and the barriers per step
+  // halve (the dense tiles measured no gain from it).
+  constexpr int KS = (SPARSE && MJ <= 2) ? 2 : 1;
   constexpr int SUB = A_BYTES + I_BYTES + B_BYTES;     // one K step
   constexpr int STAGE = KS * SUB;
   constexpr int NST = KS == 2 ? 2 : SPARSE ? 3 : 4;
+  static_assert(NST * STAGE <= 160 * 1024, "LDS");
   // global loads per wave per stage: 2 W fragments, NXB / 8 X blocks, the
   // index block (waves 0..3, sparse), per K step
   constexpr int LPS0 = KS * (2 + (SPARSE ? 1 : 0) + NXB / NW);
