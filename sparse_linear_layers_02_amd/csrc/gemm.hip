@@ -298,11 +298,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   constexpr int NXB = 4 * MJ * BH;                     // 1 KB X blocks per stage
   static_assert(NXB % NW == 0, "every wave loads the same number of X blocks");
   constexpr int B_BYTES = NXB * 1024;
-  // KS K steps per stage: the 64- and 128-token sparse tiles take two per
-  // stage (two stages of 56 / 72 KB), so each ping-pong phase holds 16 / 32
-  // matrix instructions per wave instead of 8 / 16 and the barriers per step
-  // halve (the dense tiles measured no gain from it).
-  constexpr int KS = (SPARSE && MJ <= 2) ? 2 : 1;
+  // KS K steps per stage: the 64- and 128-token sparse tiles on the tiled X
+  // copy take two per stage (two stages of 56 / 72 KB), so each ping-pong
+  // phase holds 16 / 32 matrix instructions per wave instead of 8 / 16 and
+  // the barriers per step halve (the dense tiles measured no gain from it,
+  // and the direct-X tiles lose 0-11%).
+  constexpr int KS = (SPARSE && !DX && MJ <= 2) ? 2 : 1;
   constexpr int SUB = A_BYTES + I_BYTES + B_BYTES;     // one K step
   constexpr int STAGE = KS * SUB;
   constexpr int NST = KS == 2 ? 2 : SPARSE ? 3 : 4;
