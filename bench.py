@@ -11,8 +11,9 @@ resident in HBM:
   train:             the same plus the dual-STE backward (dX, dW).
                      T=8192, R=11008, K=4096, 6:8, dY ~ N(0, 1e-2).
   sweep:             GEMM alone for N:M in {2:4, 4:8, 6:8, 2:8, 1:4, 8:8},
-                     T=2048, R=K=8192 (one line per ratio is not the
-                     contract; the JSON line carries the list).
+                     T=2048, R=K=8192, and the pack of W for each ratio
+                     (one line per ratio is not the contract; the JSON line
+                     carries the list).
   decode:            decode GEMV (T=1, R=K=4096) over pools of 128 distinct
                      packed weights per ratio (2:4 and 6:8), as batched calls
                      of 64 weights; `value` is GB/s of algorithmic bytes.  The
@@ -35,9 +36,14 @@ same line carries:
   roofline      the dominant kernel's algorithmic ops (or bytes) per launch
                 over its average launch time, timed with HIP events that the
                 library records around that kernel alone on its own stream,
-                against MI355X's published dense peak (the fraction of the
-                structured-sparse int8 peak is printed beside it);
-  decode_gemv   the other half of the metric: GB/s of the decode GEMV
+                against MI355X's published dense peak.  For the GEMM the ops
+                are the products the method performs, 2*T*R*K*n/m (pruned
+                positions are not work); the dense-equivalent rate and its
+                fractions of the dense and 2:4-sparse int8 peaks sit beside it;
+  decode_step   the other half of the metric, measured like `--workload
+                decode`: GB/s of the batched decode GEMV step over both pools
+                with the HBM roofline of each streamed kernel;
+  decode_gemv   GB/s of the decode GEMV
                 (R = K = 4096, T = 1, 2:4 and 6:8) over a pool of 128 distinct
                 packed weights (twice the 256 MB Infinity Cache or more), three
                 ways: (i) one call on a cold weight, (ii-a) the pool as
@@ -47,7 +53,8 @@ same line carries:
   variants      (train) the SGD step fused with the next pack, and the two
                 ablation switches (mask from the ternary weights; dW blocked
                 at pruned positions), per kernel;
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload, with
+                all of its BLAS threads and with one (median of 3 each).
 Multi-GPU runs are not part of this build: --gpus above 1 exits.
 """
 from __future__ import annotations
@@ -114,6 +121,27 @@ def traffic_from_profiles(kernel, workload):
     if hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(2):
         return None
     return float(m.group(1))
+
+
+def gemm_roofline(gname, T, R, K, n, m, k_ms, launches, traffic):
+    """Roofline of the forward GEMM: `achieved` counts the products the method
+    performs, 2*T*R*K*n/m int8 ops (pruned positions are not work), against
+    the dense int8 matrix peak.  For 2:4 on the structured-sparse instruction
+    that fraction equals the dense-equivalent rate over the 2:4 instruction's
+    dense-equivalent peak.  The dense-equivalent rate (2*T*R*K, pruned
+    positions counted) and its fractions of both peaks are printed beside it."""
+    dense_eq = 2 * T * R * K
+    ops = dense_eq * n // m
+    ach = ops / (k_ms * 1e-3) / 1e12
+    de = dense_eq / (k_ms * 1e-3) / 1e12
+    return {"kernel": gname, "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_INT8_TOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_INT8_TOPS, 4), "traffic": traffic,
+            "kernel_us": round(k_ms * 1e3, 3), "launches": launches, "ops_per_launch": ops,
+            "dense_equivalent": {"TOPS": round(de, 2), "ops_per_launch": dense_eq,
+                                 "frac_of_dense_int8_peak": round(de / PEAK_INT8_TOPS, 4),
+                                 "frac_of_2_4_sparse_peak": round(de / PEAK_INT8_SPARSE_TOPS, 4)},
+            "note": f"int8 multiply-adds count 2 ops; achieved = 2*T*R*K*{n}/{m} (the products the method "
+                    "performs) per second over the dense int8 matrix peak"}
 
 
 # ---------------------------------------------------------------------- steps
@@ -554,26 +582,45 @@ def variants_extras(wl, reps=10):
 
 
 # ---------------------------------------------------------------------- CPU baseline
-def cpu_baseline(wl, n, m, tokens):
-    """The oracle as it stands, on the host: pack the full W, quantize `tokens`
-    tokens, accumulate them against every row.  TOPS = 2*tokens*R*K / time."""
-    import numpy as np
-    import oracle as O
+def _median_runs(fn, runs=3):
+    ts = sorted(fn() for _ in range(runs))
+    return ts[len(ts) // 2]
+
+
+def _oracle_threads():
     from threadpoolctl import threadpool_info
+    return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+
+
+def cpu_baseline(wl, n, m, tokens, runs=3):
+    """The oracle as it stands, on the host: pack the full W, quantize `tokens`
+    tokens, accumulate them against every row, round the bf16 outputs.  Timed
+    with all of the BLAS threads and with one (median of `runs` each).
+    TOPS = 2*tokens*R*K / time."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
     W = wl.weights(0)
     X = wl.activations(0)[:tokens]
-    t0 = time.perf_counter()
-    eff, mask, sw = O.quant_then_mask(W, n, m)
-    O.pack_sbn1(eff, mask, n, m)
-    Xq, s_x = O.act_quant(X)
-    acc = O.accumulate(Xq, eff)
-    O.output(acc, sw, s_x)
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": round(2 * tokens * wl.R * wl.K / dt / 1e12, 6), "unit": "TOPS", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"full W pack ({wl.R}x{wl.K}, {n}:{m}) + {tokens} of {wl.T} tokens through "
-                      f"act_quant and the float64 matmul; ops = 2*{tokens}*R*K"}
+
+    def once():
+        t0 = time.perf_counter()
+        eff, mask, sw = O.quant_then_mask(W, n, m)
+        O.pack_sbn1(eff, mask, n, m)
+        Xq, s_x = O.act_quant(X)
+        O.output_bf16(O.accumulate(Xq, eff), sw, s_x)
+        return time.perf_counter() - t0
+
+    threads = _oracle_threads()
+    dt = _median_runs(once, runs)
+    with threadpool_limits(1):
+        dt1 = _median_runs(once, runs)
+    ops = 2 * tokens * wl.R * wl.K
+    return {"value": round(ops / dt / 1e12, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3), "runs": runs, "statistic": "median",
+            "single_thread": {"value": round(ops / dt1 / 1e12, 6), "cores": 1, "seconds": round(dt1, 3)},
+            "nproc": os.cpu_count(),
+            "sample": f"full W pack ({wl.R}x{wl.K}, {n}:{m}) + {tokens} of {wl.T} tokens through act_quant, "
+                      f"the float64 matmul and the bf16 output rounding; ops = 2*{tokens}*R*K"}
 
 
 # ---------------------------------------------------------------------- decode step
@@ -646,14 +693,60 @@ def make_decode_step_d2(T=1):
     return step, total, BATCH * per
 
 
-def cpu_baseline_decode(wl, weights=POOL):
-    """The oracle's GEMV (float64 accumulate and output scaling) for one token
-    against `weights` distinct R x K ternary weights per ratio, the effective
-    weights prepared outside the timed region.  GB/s = the decode step's
-    algorithmic bytes for those weights / time."""
-    import numpy as np
+def measure_decode_step(a, with_d2=True):
+    """The decode half of the metric as one step: batched decode GEMVs over
+    both pools (make_decode_step), timed like every step, with the HBM
+    roofline of each streamed kernel (`roofline` 2:4, `roofline_68` 6:8) and,
+    when asked, the same step on decode planes (`decode_d2`)."""
+    import torch
+    step, nbytes, per_launch, wl = make_decode_step(T=1)
+    ms, wall, prof, mode = time_steps(step, a.steps, a.warmup)
+    out = {"GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms, 4), "wall_s": round(wall, 4),
+           "launch": mode, "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "config": {"workload": "decode", "T": 1, "R": wl.R, "K": wl.K, "nm": "2:4+6:8",
+                      "pool_weights_per_ratio": POOL, "weights_per_launch": BATCH,
+                      "step": "batched decode GEMV over both pools", "y_dtype": "bf16", "seed": 0}}
+    for key, kname in (("roofline", "gemv_stream_24"), ("roofline_68", "gemv_stream_68")):
+        k_ms, k_cnt = kernel_avg_ms(profile_pass(step, a.steps, kname), kname)
+        ach = per_launch[kname] / (k_ms * 1e-3) / 1e9
+        out[key] = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                    "traffic": traffic_from_profiles(kname, "decode"), "kernel_us": round(k_ms * 1e3, 3),
+                    "launches": k_cnt, "bytes_per_launch": per_launch[kname],
+                    "note": "algorithmic bytes: packed planes + activations + scales + bf16 outputs of the "
+                            "weights of one launch"}
+    out["stages_us"] = {k: round(v[1] / v[0] * 1e3, 3) for k, v in sorted(prof.items()) if v[0]}
+    del step
+    torch.cuda.empty_cache()
+    if with_d2:
+        step2, nbytes2, per_launch2 = make_decode_step_d2(T=1)
+        ms2, _, _, mode2 = time_steps(step2, a.steps, a.warmup, kernel="gemv_stream_d2")
+        k_ms, k_cnt = kernel_avg_ms(profile_pass(step2, a.steps, "gemv_stream_d2"), "gemv_stream_d2")
+        ach = per_launch2 / (k_ms * 1e-3) / 1e9
+        out["decode_d2"] = {
+            "note": "the same step on decode planes (the pools' weights repacked once into dense 2-bit "
+                    "ternary codes, 4.19 MB per weight for both ratios, against 4.19 / 5.24 MB packed); "
+                    "the step's GB/s stays on the packed weights",
+            "ms_per_step": round(ms2, 4), "GBps": round(nbytes2 / (ms2 * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes2 / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "speedup_vs_packed": round(ms / ms2, 3), "launch": mode2,
+            "roofline": {"kernel": "gemv_stream_d2", "bound": "hbm", "achieved": round(ach, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_from_profiles("gemv_stream_d2", "decode"),
+                         "kernel_us": round(k_ms * 1e3, 3), "launches": k_cnt, "bytes_per_launch": per_launch2}}
+        del step2
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline_decode(wl, weights=POOL, runs=3):
+    """The oracle's GEMV (float64 accumulate and bf16 output rounding) for one
+    token against `weights` distinct R x K ternary weights per ratio, the
+    effective weights prepared outside the timed region; all BLAS threads and
+    one thread, median of `runs` each.  GB/s = the decode step's algorithmic
+    bytes for those weights / time."""
     import oracle as O
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
     X = wl.activations(0, T=1)
     Xq, s_x = O.act_quant(X)
     effs, nbytes = [], 0
@@ -662,15 +755,24 @@ def cpu_baseline_decode(wl, weights=POOL):
         cb, mb = O.packed_bytes(wl.R, wl.K, n, m)
         effs += [(eff, sw)] * weights
         nbytes += weights * (cb + mb + wl.K + 4 + 2 * wl.R + 4)
-    t0 = time.perf_counter()
-    for eff, sw in effs:
-        O.output(O.accumulate(Xq, eff), sw, s_x)
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+
+    def once():
+        t0 = time.perf_counter()
+        for eff, sw in effs:
+            O.output_bf16(O.accumulate(Xq, eff), sw, s_x)
+        return time.perf_counter() - t0
+
+    threads = _oracle_threads()
+    dt = _median_runs(once, runs)
+    with threadpool_limits(1):
+        dt1 = _median_runs(once, runs)
     return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 2),
+            "seconds": round(dt, 3), "runs": runs, "statistic": "median",
+            "single_thread": {"value": round(nbytes / dt1 / 1e9, 3), "cores": 1, "seconds": round(dt1, 3)},
+            "nproc": os.cpu_count(),
             "sample": f"{weights} weights per ratio ({', '.join(f'{n}:{m}' for n, m in wl.nm)}) of {wl.R}x{wl.K}, "
-                      f"one token, oracle accumulate + output; bytes = the packed-weight step's algorithmic bytes"}
+                      f"one token, oracle accumulate + bf16 output; bytes = the packed-weight step's algorithmic "
+                      f"bytes"}
 
 
 # ---------------------------------------------------------------------- main
@@ -713,62 +815,29 @@ def main():
                          "step": "pack+act_quant+gemm" + ("+backward" if nprod == 3 else ""),
                          "y_dtype": "bf16", "seed": 0}
         g_ms, g_cnt = kernel_avg_ms(prof_g, gname)
-        g_ach = 2 * wl.T * wl.R * wl.K / (g_ms * 1e-3) / 1e12
-        traffic = traffic_from_profiles(gname, a.workload)
-        out["roofline"] = {"kernel": gname, "bound": "mfma", "achieved": round(g_ach, 2), "peak": PEAK_INT8_TOPS,
-                           "unit": "TFLOP/s", "frac": round(g_ach / PEAK_INT8_TOPS, 4), "traffic": traffic,
-                           "kernel_us": round(g_ms * 1e3, 3), "launches": g_cnt,
-                           "ops_per_launch": 2 * wl.T * wl.R * wl.K,
-                           "frac_of_sparse_peak": (round(g_ach / PEAK_INT8_SPARSE_TOPS, 4) if n <= 2 else None),
-                           "note": "int8 multiply-adds count 2 ops; dense-equivalent (pruned positions "
-                                   "counted); peak is the dense int8 matrix peak; frac_of_sparse_peak divides "
-                                   "by the 2:4 structured-sparse int8 peak instead"}
+        out["roofline"] = gemm_roofline(gname, wl.T, wl.R, wl.K, n, m, g_ms, g_cnt,
+                                        traffic_from_profiles(gname, a.workload))
         out["stages_us"] = {k: round(v[1] / v[0] * 1e3, 3) for k, v in sorted(prof.items()) if v[0]}
         if a.workload == "train":
             for nm_, kname in (("dx", "gemm_dx"), ("dw", "gemm_dw")):
                 k_ms, _ = kernel_avg_ms(profile_pass(step, max(2, a.steps // 4), kname), kname)
-                fl = 2 * wl.T * wl.R * wl.K * (2 if kname == "gemm_dw" else 1)
+                fl = 2 * wl.T * wl.R * wl.K                     # the product the method computes
+                ex = fl * (2 if kname == "gemm_dw" else 1)      # bf16 products executed (dW: hi and lo halves)
                 out["roofline_" + nm_] = {"kernel": kname, "bound": "mfma", "achieved": round(fl / (k_ms * 1e-3) / 1e12, 2),
                                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                           "frac": round(fl / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                                          "note": "bf16 products executed (dW runs hi and lo halves)"}
+                                          "kernel_us": round(k_ms * 1e3, 3),
+                                          "executed_TFLOPs": round(ex / (k_ms * 1e-3) / 1e12, 2),
+                                          "executed_frac": round(ex / (k_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                          "note": "achieved = 2*T*R*K (the method's product) per second; "
+                                                  "executed counts the bf16 products run (dW runs hi and lo "
+                                                  "halves of dY*s_x)"}
     elif a.workload == "decode":
-        step, nbytes, per_launch, wl = make_decode_step(T=1)
-        ms, wall, prof, mode = time_steps(step, a.steps, a.warmup)
-        out.update(value=round(nbytes / (ms * 1e-3) / 1e9, 1), unit="GB/s", ms_per_step=round(ms, 4),
-                   wall_s=round(wall, 4), launch=mode)
-        out["config"] = {"workload": "decode", "T": 1, "R": wl.R, "K": wl.K, "nm": "2:4+6:8",
-                         "pool_weights_per_ratio": POOL, "weights_per_launch": BATCH,
-                         "step": "batched decode GEMV over both pools", "y_dtype": "bf16", "seed": 0}
-        for key, kname in (("roofline", "gemv_stream_24"), ("roofline_68", "gemv_stream_68")):
-            k_ms, k_cnt = kernel_avg_ms(profile_pass(step, a.steps, kname), kname)
-            ach = per_launch[kname] / (k_ms * 1e-3) / 1e9
-            out[key] = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                        "traffic": traffic_from_profiles(kname, "decode"), "kernel_us": round(k_ms * 1e3, 3),
-                        "launches": k_cnt, "bytes_per_launch": per_launch[kname],
-                        "note": "algorithmic bytes: packed planes + activations + scales + bf16 outputs of the "
-                                f"{BATCH} weights of one launch"}
-        out["stages_us"] = {k: round(v[1] / v[0] * 1e3, 3) for k, v in sorted(prof.items()) if v[0]}
-        if not a.no_extras:
-            del step
-            torch.cuda.empty_cache()
-            step2, nbytes2, per_launch2 = make_decode_step_d2(T=1)
-            ms2, _, _, mode2 = time_steps(step2, a.steps, a.warmup, kernel="gemv_stream_d2")
-            k_ms, k_cnt = kernel_avg_ms(profile_pass(step2, a.steps, "gemv_stream_d2"), "gemv_stream_d2")
-            ach = per_launch2 / (k_ms * 1e-3) / 1e9
-            out["decode_d2"] = {
-                "note": "the same step on decode planes (the pools' weights repacked once into dense 2-bit "
-                        "ternary codes, 4.19 MB per weight for both ratios, against 4.19 / 5.24 MB packed); "
-                        "value stays on the packed weights",
-                "ms_per_step": round(ms2, 4), "GBps": round(nbytes2 / (ms2 * 1e-3) / 1e9, 1),
-                "frac_hbm": round(nbytes2 / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                "speedup_vs_packed": round(ms / ms2, 3), "launch": mode2,
-                "roofline": {"kernel": "gemv_stream_d2", "bound": "hbm", "achieved": round(ach, 1),
-                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                             "traffic": traffic_from_profiles("gemv_stream_d2", "decode"),
-                             "kernel_us": round(k_ms * 1e3, 3), "launches": k_cnt, "bytes_per_launch": per_launch2}}
-            del step2
+        d = measure_decode_step(a, with_d2=not a.no_extras)
+        out.update(value=d.pop("GBps"), unit="GB/s", ms_per_step=d.pop("ms_per_step"), wall_s=d.pop("wall_s"),
+                   launch=d.pop("launch"))
+        out["config"] = d.pop("config")
+        out.update(d)
     elif a.workload == "speedup":
         tab = speedup_tables(a.steps)
         r = next(r for r in tab["prefill"] if r["T"] == 4096)
@@ -792,25 +861,37 @@ def main():
             ms, wall, prof, mode = time_steps(
                 lambda: sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, wl.R, n, m, Y=Y), a.steps, a.warmup,
                 kernel=gname)
-            g_ms, _ = kernel_avg_ms(prof, gname)
+            g_ms, g_cnt = kernel_avg_ms(prof, gname)
             ops = 2 * wl.T * wl.R * wl.K
+            ws_p = torch.empty(max(sbn.sbn_workspace_bytes(sbn.SBN_OP_PACK, 0, wl.R, wl.K, n, m), 256),
+                               dtype=torch.uint8, device="cuda")
+            pk_ms, _, pk_prof, _ = time_steps(
+                lambda: sbn.sbn_mask_ternarize_pack(W, n, m, codes=codes, meta=meta, s_w=s_w, ws=ws_p), a.steps,
+                a.warmup)
+            pk_bytes = 2 * wl.R * wl.K + sum(sbn.sbn_packed_bytes(wl.R, wl.K, n, m))
             rows.append({"nm": f"{n}:{m}", "call_us": round(ms * 1e3, 2), "kernel_us": round(g_ms * 1e3, 2),
                          "TOPS_call": round(ops / (ms * 1e-3) / 1e12, 1),
-                         "TOPS_kernel": round(ops / (g_ms * 1e-3) / 1e12, 1), "kernel": gname})
+                         "TOPS_kernel": round(ops / (g_ms * 1e-3) / 1e12, 1), "kernel": gname,
+                         "roofline": gemm_roofline(gname, wl.T, wl.R, wl.K, n, m, g_ms, g_cnt, None),
+                         "pack_us": round(pk_ms * 1e3, 2),
+                         "pack_kernels_us": {k: round(v[1] / v[0] * 1e3, 2) for k, v in sorted(pk_prof.items())
+                                             if v[0]},
+                         "pack_GBps": round(pk_bytes / (pk_ms * 1e-3) / 1e9, 1),
+                         "pack_frac_hbm": round(pk_bytes / (pk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
             tot_ms += ms
-            del W, codes, meta
+            del W, codes, meta, ws_p
         ops = 2 * wl.T * wl.R * wl.K * len(rows)
         out.update(value=round(ops / (tot_ms * 1e-3) / 1e12, 3), unit="TOPS", ms_per_step=round(tot_ms, 4))
         out["config"] = {"workload": "sweep", "T": wl.T, "R": wl.R, "K": wl.K, "step": "gemm for each N:M"}
         out["sweep"] = rows
-        r24 = next(r for r in rows if r["nm"] == "2:4")
-        out["roofline"] = {"kernel": r24["kernel"], "bound": "mfma", "achieved": r24["TOPS_kernel"],
-                           "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                           "frac": round(r24["TOPS_kernel"] / PEAK_INT8_TOPS, 4), "traffic": None,
-                           "frac_of_sparse_peak": round(r24["TOPS_kernel"] / PEAK_INT8_SPARSE_TOPS, 4),
-                           "note": "the 2:4 row"}
+        out["roofline"] = dict(next(r for r in rows if r["nm"] == "2:4")["roofline"], row="2:4")
 
     if not a.no_extras and a.workload not in ("decode", "speedup"):
+        # the decode half of the metric beside the prefill / train / sweep line
+        d = measure_decode_step(a, with_d2=False)
+        out["decode_step"] = {k: d[k] for k in ("GBps", "frac_hbm", "ms_per_step", "launch", "config", "roofline",
+                                                "roofline_68")}
+        torch.cuda.empty_cache()
         out["decode_gemv"] = [decode_gemv(2, 4, 1), decode_gemv(6, 8, 1)]
     if not a.no_extras and a.workload == "train":
         out["variants"] = variants_extras(WORKLOADS["train"])
@@ -818,7 +899,7 @@ def main():
     if a.no_cpu_baseline or a.workload == "speedup":
         out["cpu_baseline"] = None
     elif a.workload == "decode":
-        out["cpu_baseline"] = cpu_baseline_decode(WORKLOADS["decode"], weights=POOL)
+        out["cpu_baseline"] = cpu_baseline_decode(WORKLOADS["decode"], weights=16)
     else:
         wl = WORKLOADS["prefill" if a.workload == "sweep" else a.workload]
         n, m = wl.nm[0]

@@ -27,7 +27,10 @@ readings below (each is repeated at the function that uses it):
   * ternary value = RoundClip(w / s_w, -1, 1), round half to even;
   * activations: per-token absmax to int8 in [-127, 127], decided in fp32 as
     rint((127*x) / a) with a = max(absmax, 1e-5), s_x = a/127 in fp32;
-  * Y = s_w * s_x[t] * sum_k Xq[t,k] * Wt[r,k];
+  * Y = s_w * s_x[t] * sum_k Xq[t,k] * Wt[r,k]; as float32, the token's
+    scale is rounded once, fl32(s_w * s_x[t]), and each output is one float32
+    product of the exact accumulator with it (bf16: that value rounded to
+    nearest even);
   * dual STE: identity Jacobians through both quantizers and a dense
     gradient through the mask, so grad_X = dY @ (s_w*Wt) and
     grad_W = dY^T @ (s_x*Xq) covering every (r, k);
@@ -67,7 +70,7 @@ __all__ = [
     "weight_scale", "ternary_codes", "quant_then_mask", "packed_bytes",
     "pack_sbn1", "act_quant", "accumulate", "output", "backward",
     "forward", "S_FLOOR", "QMAX", "nm_mask_ternary", "fma_f32", "f32_to_bf16_rne",
-    "sgd_update", "pack_d2", "unpack_d2",
+    "sgd_update", "pack_d2", "unpack_d2", "output_f32", "output_bf16",
 ]
 
 
@@ -317,8 +320,30 @@ def accumulate(Xq: np.ndarray, codes: np.ndarray) -> np.ndarray:
 
 
 def output(acc: np.ndarray, s_w: np.float32, s_x: np.ndarray) -> np.ndarray:
-    """Y[t, r] = s_w * s_x[t] * acc[t, r], in float64."""
+    """Y[t, r] = s_w * s_x[t] * acc[t, r], in float64 (the real value the
+    float outputs approximate; tolerances are stated against it)."""
     return acc.astype(np.float64) * (np.float64(s_w) * s_x.astype(np.float64))[:, None]
+
+
+def output_f32(acc: np.ndarray, s_w: np.float32, s_x: np.ndarray) -> np.ndarray:
+    """The float32 output as the operator defines its rounding.  float32 [T, R].
+
+    The pages fix no output precision.  Reading used: the dequantization
+    scale of a token is formed once in float32, c[t] = fl32(s_w * s_x[t]),
+    and each output is one float32 product y = fl32(fl32(acc) * c[t]).
+    fl32(acc) is exact (|acc| <= 127*K < 2^24 for K <= 2^17), so y is fixed
+    bit for bit by acc, s_w and s_x: every IEEE float32 multiplication
+    rounds to nearest, ties to even.
+    """
+    assert np.abs(acc).max(initial=0) < 2 ** 24
+    c = (np.float32(s_w) * np.asarray(s_x, dtype=np.float32)).astype(np.float32)   # float32 IEEE product
+    return (acc.astype(np.float32) * c[:, None]).astype(np.float32)               # float32 IEEE product
+
+
+def output_bf16(acc: np.ndarray, s_w: np.float32, s_x: np.ndarray) -> np.ndarray:
+    """The bf16 output: output_f32 rounded to bf16, nearest, ties to even.
+    uint16 bit patterns [T, R]."""
+    return f32_to_bf16_rne(output_f32(acc, s_w, s_x))
 
 
 def backward(dY_bits: np.ndarray, Xq: np.ndarray, s_x: np.ndarray,
@@ -380,12 +405,13 @@ def fma_f32(a, b, c) -> np.ndarray:
 
 
 def f32_to_bf16_rne(x) -> np.ndarray:
-    """float32 -> bf16 bit patterns, round to nearest, ties to even."""
+    """float32 -> bf16 bit patterns, round to nearest, ties to even (an
+    overflow to infinity is an error: every caller's inputs are finite)."""
     u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     lsb = (u >> 16) & 1
     r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
     if np.any((r & 0x7F80) == 0x7F80):
-        raise ValueError("bf16 overflow in the update")
+        raise ValueError("bf16 overflow")
     return r
 
 

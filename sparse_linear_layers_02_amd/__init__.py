@@ -1,7 +1,9 @@
 """Python binding of libsbn, the Sparse-BitLinear hot path for MI355X (gfx950).
 
-Argument marshalling only: every function here checks nothing numerical,
-allocates outputs with PyTorch when the caller did not pass them, and calls
+Argument marshalling only: every function here checks nothing numerical
+(only the tensor layouts the C ABI cannot see: dtypes, unit column strides,
+contiguity where the ABI takes no leading dimension), allocates outputs
+with PyTorch when the caller did not pass them, and calls
 the C entry point of the same name in ``libsbn.so`` (declared in
 ``include/sbn.h``) with raw device pointers on the current HIP stream.  All
 computation happens in the HIP kernels.  If the library is not built, import
@@ -141,27 +143,52 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-class Workspace:
-    """Grow-only device byte buffer for one operation."""
-
-    def __init__(self):
-        self.buf = None
-
-    def get(self, nbytes: int, device):
-        torch = _torch()
-        if nbytes == 0:
-            return None
-        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        return self.buf
+# Grow-only workspaces, one per (operation, device, stream): calls that share a
+# workspace must be ordered on one stream (the ABI's rule), and a buffer is
+# allocated while its stream is current, so the caching allocator hands its
+# memory to later work on that stream only once this work is done.
+_WS = {}
 
 
-_WS = {"pack": Workspace(), "gemm": Workspace(), "bwd": Workspace(), "fwd": Workspace()}
+def _workspace(kind: str, nbytes: int, device, stream):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    key = (kind, str(device), s.cuda_stream)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        with torch.cuda.stream(s):
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
 
 
-def _pack_outputs(W, n: int, m: int, codes, meta, s_w, ws):
+# Layout the C ABI assumes but cannot see: element types, unit column strides
+# (row-major with a leading dimension), and fully contiguous tensors where the
+# ABI takes no leading dimension.
+_DT = {"bf16": "bfloat16", "i8": "int8", "u8": "uint8", "f32": "float32", "i32": "int32"}
+
+
+def _req(t, name: str, dt: str, contiguous: bool = False, fn: str = "sbn") -> None:
+    if t is None:
+        return
+    torch = _torch()
+    if t.dtype != getattr(torch, _DT[dt]):
+        raise SbnError(fn, 6, f"{name} must be {_DT[dt]}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise SbnError(fn, 2, f"{name} must be contiguous")
+    if t.dim() == 2 and t.shape[1] > 1 and t.stride(1) != 1:
+        raise SbnError(fn, 2, f"{name} must have unit column stride (row-major)")
+
+
+def _pack_outputs(W, n: int, m: int, codes, meta, s_w, ws, stream=None):
     torch = _torch()
     R, K = W.shape
+    _req(W, "W", "bf16")
+    for t, nm in ((codes, "codes"), (meta, "meta")):
+        _req(t, nm, "u8", True)
+    _req(s_w, "s_w", "f32", True)
     cb, mb = sbn_packed_bytes(R, K, n, m)
     dev = W.device
     if codes is None:
@@ -172,14 +199,14 @@ def _pack_outputs(W, n: int, m: int, codes, meta, s_w, ws):
         s_w = torch.empty(1, dtype=torch.float32, device=dev)
     need = sbn_workspace_bytes(SBN_OP_PACK, 0, R, K, n, m)
     if ws is None:
-        ws = _WS["pack"].get(need, dev)
+        ws = _workspace("pack", need, dev, stream)
     return codes, meta, s_w, ws
 
 
 def sbn_mask_ternarize_pack(W, n: int, m: int, *, codes=None, meta=None, s_w=None, ws=None, stream=None):
     """Mask, ternarize and pack bf16 master weights W [R, K].  Returns (codes, meta, s_w)."""
     R, K = W.shape
-    codes, meta, s_w, ws = _pack_outputs(W, n, m, codes, meta, s_w, ws)
+    codes, meta, s_w, ws = _pack_outputs(W, n, m, codes, meta, s_w, ws, stream)
     _check("sbn_mask_ternarize_pack",
            lib().sbn_mask_ternarize_pack(_ptr(W), R, K, W.stride(0), n, m, _ptr(codes), _ptr(meta),
                                          _ptr(s_w), _ptr(ws), ws.numel() if ws is not None else 0,
@@ -191,7 +218,7 @@ def sbn_mask_ternarize_pack_ex(W, n: int, m: int, flags: int, *, codes=None, met
                                stream=None):
     """sbn_mask_ternarize_pack with variant flags (SBN_MASK_FROM_TERNARY).  Returns (codes, meta, s_w)."""
     R, K = W.shape
-    codes, meta, s_w, ws = _pack_outputs(W, n, m, codes, meta, s_w, ws)
+    codes, meta, s_w, ws = _pack_outputs(W, n, m, codes, meta, s_w, ws, stream)
     _check("sbn_mask_ternarize_pack_ex",
            lib().sbn_mask_ternarize_pack_ex(_ptr(W), R, K, W.stride(0), n, m, flags, _ptr(codes), _ptr(meta),
                                             _ptr(s_w), _ptr(ws), ws.numel() if ws is not None else 0,
@@ -204,7 +231,8 @@ def sbn_sgd_update_pack(W, G, lr: float, n: int, m: int, flags: int = 0, *, code
     """One SGD step W <- bf16(fma(-lr, G, W)) on bf16 W [R, K] (in place) with
     float32 G [R, K], then mask/ternarize/pack of the new W.  Returns (codes, meta, s_w)."""
     R, K = W.shape
-    codes, meta, s_w, ws = _pack_outputs(W, n, m, codes, meta, s_w, ws)
+    _req(G, "G", "f32")
+    codes, meta, s_w, ws = _pack_outputs(W, n, m, codes, meta, s_w, ws, stream)
     _check("sbn_sgd_update_pack",
            lib().sbn_sgd_update_pack(_ptr(W), R, K, W.stride(0), _ptr(G), G.stride(0), float(lr), n, m, flags,
                                      _ptr(codes), _ptr(meta), _ptr(s_w), _ptr(ws),
@@ -216,6 +244,9 @@ def sbn_act_quant(X, *, Xq=None, s_x=None, stream=None):
     """Per-token absmax int8 quantization of bf16 X [T, K].  Returns (Xq, s_x)."""
     torch = _torch()
     T, K = X.shape
+    _req(X, "X", "bf16")
+    _req(Xq, "Xq", "i8", True)
+    _req(s_x, "s_x", "f32", True)
     if Xq is None:
         Xq = torch.empty((T, K), dtype=torch.int8, device=X.device)
     if s_x is None:
@@ -226,17 +257,29 @@ def sbn_act_quant(X, *, Xq=None, s_x=None, stream=None):
 
 
 _YT = {SBN_F32: "float32", SBN_BF16: "bfloat16", SBN_I32_ACC: "int32"}
+_YD = {SBN_F32: "f32", SBN_BF16: "bf16", SBN_I32_ACC: "i32"}
+
+
+def _req_matmul(fn, Xq, s_x, s_w, ydt, Y):
+    _req(Xq, "Xq", "i8", True, fn)
+    _req(s_x, "s_x", "f32", True, fn)
+    _req(s_w, "s_w", "f32", True, fn)
+    if ydt in _YD:
+        _req(Y, "Y", _YD[ydt], False, fn)
 
 
 def _matmul(name: str, Xq, s_x, codes, meta, s_w, R: int, n: int, m: int, ydt: int, Y, ws, stream):
     torch = _torch()
     T, K = Xq.shape
+    _req_matmul(name, Xq, s_x, s_w, ydt, Y)
+    _req(codes, "codes", "u8", True, name)
+    _req(meta, "meta", "u8", True, name)
     if Y is None:                                    # row stride rounded up to 8 elements (the ABI's rule)
         Y = torch.empty((T, (R + 7) // 8 * 8), dtype=getattr(torch, _YT[ydt]), device=Xq.device)[:, :R]
     op = SBN_OP_GEMM if name == "sbn_sparse_ternary_gemm" else SBN_OP_GEMV
     need = sbn_workspace_bytes(op, T, R, K, n, m)
     if ws is None:
-        ws = _WS["gemm"].get(need, Xq.device)
+        ws = _workspace("gemm", need, Xq.device, stream)
     fn = getattr(lib(), name)
     _check(name, fn(_ptr(Xq), _ptr(s_x), T, K, _ptr(codes), _ptr(meta), _ptr(s_w), R, n, m, _ptr(Y), ydt,
                     Y.stride(0), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
@@ -262,6 +305,11 @@ def sbn_forward(W, X, n: int, m: int, flags: int = 0, *, ydt: int = SBN_BF16, co
     torch = _torch()
     R, K = W.shape
     T = X.shape[0]
+    _req(W, "W", "bf16", False, "sbn_forward")
+    _req(X, "X", "bf16", False, "sbn_forward")
+    _req_matmul("sbn_forward", Xq, s_x, s_w, ydt, Y)
+    for t, nm in ((codes, "codes"), (meta, "meta")):
+        _req(t, nm, "u8", True, "sbn_forward")
     cb, mb = sbn_packed_bytes(R, K, n, m)
     dev = W.device
     if codes is None:
@@ -278,7 +326,7 @@ def sbn_forward(W, X, n: int, m: int, flags: int = 0, *, ydt: int = SBN_BF16, co
         Y = torch.empty((T, (R + 7) // 8 * 8), dtype=getattr(torch, _YT[ydt]), device=dev)[:, :R]
     need = sbn_workspace_bytes(SBN_OP_FORWARD, T, R, K, n, m)
     if ws is None:
-        ws = _WS["fwd"].get(need, dev)
+        ws = _workspace("fwd", need, dev, stream)
     _check("sbn_forward",
            lib().sbn_forward(_ptr(W), R, K, W.stride(0), _ptr(X), T, X.stride(0), n, m, flags, _ptr(codes),
                              _ptr(meta), _ptr(s_w), _ptr(Xq), _ptr(s_x), _ptr(Y), ydt, Y.stride(0), _ptr(ws),
@@ -295,6 +343,9 @@ def sbn_gemm_weight_bytes(R: int, K: int, n: int, m: int) -> int:
 def sbn_prepare_gemm_weight(codes, meta, R: int, K: int, n: int, m: int, *, prepared=None, stream=None):
     """The GEMM's weight operand, built once from the packed planes (uint8, opaque)."""
     torch = _torch()
+    _req(codes, "codes", "u8", True, "sbn_prepare_gemm_weight")
+    _req(meta, "meta", "u8", True, "sbn_prepare_gemm_weight")
+    _req(prepared, "prepared", "u8", True, "sbn_prepare_gemm_weight")
     if prepared is None:
         prepared = torch.empty(sbn_gemm_weight_bytes(R, K, n, m), dtype=torch.uint8, device=codes.device)
     _check("sbn_prepare_gemm_weight",
@@ -307,11 +358,13 @@ def sbn_sparse_ternary_gemm_prepared(Xq, s_x, prepared, s_w, R: int, n: int, m: 
     """sbn_sparse_ternary_gemm on a prepared weight operand.  Returns Y [T, R]."""
     torch = _torch()
     T, K = Xq.shape
+    _req_matmul("sbn_sparse_ternary_gemm_prepared", Xq, s_x, s_w, ydt, Y)
+    _req(prepared, "prepared", "u8", True, "sbn_sparse_ternary_gemm_prepared")
     if Y is None:                                    # row stride rounded up to 8 elements (the ABI's rule)
         Y = torch.empty((T, (R + 7) // 8 * 8), dtype=getattr(torch, _YT[ydt]), device=Xq.device)[:, :R]
     need = sbn_workspace_bytes(SBN_OP_GEMM_PREPARED, T, R, K, n, m)
     if ws is None:
-        ws = _WS["gemm"].get(need, Xq.device)
+        ws = _workspace("gemm", need, Xq.device, stream)
     _check("sbn_sparse_ternary_gemm_prepared",
            lib().sbn_sparse_ternary_gemm_prepared(_ptr(Xq), _ptr(s_x), T, K, _ptr(prepared), _ptr(s_w), R, n, m,
                                                   _ptr(Y), ydt, Y.stride(0), _ptr(ws), ws.numel() if ws is not None else 0,
@@ -328,6 +381,9 @@ def sbn_decode_plane_bytes(R: int, K: int) -> int:
 def sbn_repack_d2(codes, meta, R: int, K: int, n: int, m: int, *, d2=None, stream=None):
     """Decode plane (uint8, sbn_decode_plane_bytes(R, K)) of a packed n:m weight."""
     torch = _torch()
+    _req(codes, "codes", "u8", True, "sbn_repack_d2")
+    _req(meta, "meta", "u8", True, "sbn_repack_d2")
+    _req(d2, "d2", "u8", True, "sbn_repack_d2")
     if d2 is None:
         d2 = torch.empty(sbn_decode_plane_bytes(R, K), dtype=torch.uint8, device=codes.device)
     _check("sbn_repack_d2", lib().sbn_repack_d2(_ptr(codes), _ptr(meta), R, K, n, m, _ptr(d2), _stream(stream)))
@@ -338,6 +394,8 @@ def sbn_ternary_gemv_d2(Xq, s_x, d2, s_w, R: int, *, ydt: int = SBN_BF16, Y=None
     """Decode GEMV (T <= 16) on a decode plane.  Returns Y [T, R]."""
     torch = _torch()
     T, K = Xq.shape
+    _req_matmul("sbn_ternary_gemv_d2", Xq, s_x, s_w, ydt, Y)
+    _req(d2, "d2", "u8", True, "sbn_ternary_gemv_d2")
     if Y is None:                                    # row stride rounded up to 8 elements (the ABI's rule)
         Y = torch.empty((T, (R + 7) // 8 * 8), dtype=getattr(torch, _YT[ydt]), device=Xq.device)[:, :R]
     _check("sbn_ternary_gemv_d2", lib().sbn_ternary_gemv_d2(_ptr(Xq), _ptr(s_x), T, K, _ptr(d2), _ptr(s_w), R, _ptr(Y),
@@ -350,6 +408,9 @@ def sbn_ternary_gemv_d2_batched(Xq, s_x, d2s, s_ws, R: int, *, ydt: int = SBN_BF
     torch = _torch()
     T, K = Xq.shape
     count = len(d2s)
+    for b in range(count):
+        _req_matmul("sbn_ternary_gemv_d2_batched", Xq, s_x, s_ws[b], ydt, Ys[b] if Ys is not None else None)
+        _req(d2s[b], "d2", "u8", True, "sbn_ternary_gemv_d2_batched")
     if Ys is None:
         ld = (R + 7) // 8 * 8
         Ys = [torch.empty((T, ld), dtype=getattr(torch, _YT[ydt]), device=Xq.device)[:, :R] for _ in range(count)]
@@ -367,6 +428,10 @@ def sbn_sparse_ternary_gemv_batched(Xq, s_x, codes, metas, s_ws, R: int, n: int,
     torch = _torch()
     T, K = Xq.shape
     count = len(codes)
+    for b in range(count):
+        _req_matmul("sbn_sparse_ternary_gemv_batched", Xq, s_x, s_ws[b], ydt, Ys[b] if Ys is not None else None)
+        _req(codes[b], "codes", "u8", True, "sbn_sparse_ternary_gemv_batched")
+        _req(metas[b] if metas is not None else None, "meta", "u8", True, "sbn_sparse_ternary_gemv_batched")
     if Ys is None:                                   # row stride rounded up to 8 elements (the ABI's rule)
         ld = (R + 7) // 8 * 8
         Ys = [torch.empty((T, ld), dtype=getattr(torch, _YT[ydt]), device=Xq.device)[:, :R] for _ in range(count)]
@@ -383,13 +448,21 @@ def _backward(name, flags, dY, Xq, s_x, codes, meta, s_w, n, m, dxdt, want_dX, w
     torch = _torch()
     T, R = dY.shape
     K = Xq.shape[1]
+    _req(dY, "dY", "bf16", True, name)
+    _req(Xq, "Xq", "i8", True, name)
+    _req(s_x, "s_x", "f32", True, name)
+    _req(s_w, "s_w", "f32", True, name)
+    _req(codes, "codes", "u8", True, name)
+    _req(meta, "meta", "u8", True, name)
+    _req(dX, "dX", "f32" if dxdt == SBN_F32 else "bf16", True, name)
+    _req(dW, "dW", "f32", True, name)
     if want_dX and dX is None:
         dX = torch.empty((T, K), dtype=torch.float32 if dxdt == SBN_F32 else torch.bfloat16, device=dY.device)
     if want_dW and dW is None:
         dW = torch.empty((R, K), dtype=torch.float32, device=dY.device)
     need = sbn_workspace_bytes(SBN_OP_BACKWARD, T, R, K, n, m)
     if ws is None:
-        ws = _WS["bwd"].get(need, dY.device)
+        ws = _workspace("bwd", need, dY.device, stream)
     args = [_ptr(dY), T, R, _ptr(Xq), _ptr(s_x), K, _ptr(codes), _ptr(meta), _ptr(s_w), n, m,
             _ptr(dX if want_dX else None), dxdt, _ptr(dW if want_dW else None)]
     if flags is not None:

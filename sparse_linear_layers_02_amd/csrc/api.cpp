@@ -73,7 +73,12 @@ sbn_status hip_result(hipError_t e, hipStream_t st, const char* what) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int64_t K_MAX = int64_t(1) << 18;
-constexpr int64_t NUMEL_MAX = int64_t(1) << 37;
+constexpr int64_t NUMEL_MAX = int64_t(1) << 37;   // elements of W, Xq, dX, dW
+constexpr int64_t ROWS_MAX = int64_t(1) << 40;    // any T or R (so that R*K, T*K fit in int64)
+constexpr int64_t SPAN_MAX = int64_t(1) << 40;    // rows times a leading dimension (Y, X, W, dY)
+
+// a * b < limit for 1 <= a, b, decided without forming the product
+bool prod_below(int64_t a, int64_t b, int64_t limit) { return a <= (limit - 1) / b; }
 
 sbn_status check_nm(int n, int m) {
   if (!(m == 4 || m == 8) || n < 1 || n > m)
@@ -89,12 +94,22 @@ sbn_status check_k(int64_t K) {
 
 sbn_status check_rows(const char* name, int64_t v) {
   if (v < 1) return fail(SBN_ERR_SHAPE, "%s = %lld must be >= 1", name, (long long)v);
+  if (v > ROWS_MAX) return fail(SBN_ERR_SHAPE, "%s = %lld exceeds 2^40", name, (long long)v);
   return SBN_OK;
 }
 
-sbn_status check_ld(const char* name, int64_t ld, int64_t len) {
+// rows x K elements (rows and K already checked): below NUMEL_MAX
+sbn_status check_numel(const char* fn, const char* what, int64_t rows, int64_t K) {
+  if (!prod_below(rows, K, NUMEL_MAX)) return fail(SBN_ERR_SHAPE, "%s: %s has 2^37 elements or more", fn, what);
+  return SBN_OK;
+}
+
+// a leading dimension of `len` elements per row, for `rows` rows (rows already checked)
+sbn_status check_ld(const char* name, int64_t ld, int64_t len, int64_t rows = 1) {
   if (ld < len) return fail(SBN_ERR_SHAPE, "%s = %lld is smaller than the row length %lld", name, (long long)ld, (long long)len);
   if (ld % 8 != 0) return fail(SBN_ERR_ALIGN, "%s = %lld is not a multiple of 8", name, (long long)ld);
+  if (!prod_below(rows, ld, SPAN_MAX))
+    return fail(SBN_ERR_SHAPE, "%s = %lld times %lld rows reaches 2^40 elements", name, (long long)ld, (long long)rows);
   return SBN_OK;
 }
 
@@ -135,8 +150,9 @@ sbn_status check_matmul_args(const char* fn, const int8_t* Xq, const float* s_x,
   SBN_TRY(check_rows("T", T));
   SBN_TRY(check_rows("R", R));
   SBN_TRY(check_k(K));
-  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
-  SBN_TRY(check_ld("ldy", ldy, R));
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
+  SBN_TRY(check_numel(fn, "Xq (T*K)", T, K));
+  SBN_TRY(check_ld("ldy", ldy, R, T));
   if (ydt != SBN_F32 && ydt != SBN_BF16 && ydt != SBN_I32_ACC)
     return fail(SBN_ERR_DTYPE, "%s: unknown output dtype %d", fn, (int)ydt);
   SBN_ALIGNED(Xq);
@@ -295,7 +311,7 @@ sbn_status sbn_packed_bytes(int64_t R, int64_t K, int n, int m, size_t* codes_by
   SBN_TRY(check_nm(n, m));
   SBN_TRY(check_rows("R", R));
   SBN_TRY(check_k(K));
-  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
   *codes_bytes = packed_codes(R, K, n, m);
   *meta_bytes = packed_meta(R, K, n, m);
   return ok();
@@ -314,6 +330,7 @@ sbn_status sbn_workspace_bytes(sbn_op op, int64_t T, int64_t R, int64_t K, int n
       SBN_TRY(check_nm(n, m));
       SBN_TRY(check_rows("R", R));
       SBN_TRY(check_k(K));
+      SBN_TRY(check_numel(fn, "W (R*K)", R, K));
       *bytes = pack_plan(R, K).bytes;
       return ok();
     case SBN_OP_GEMM:
@@ -321,12 +338,15 @@ sbn_status sbn_workspace_bytes(sbn_op op, int64_t T, int64_t R, int64_t K, int n
       SBN_TRY(check_rows("T", T));
       SBN_TRY(check_rows("R", R));
       SBN_TRY(check_k(K));
+      SBN_TRY(check_numel(fn, "W (R*K)", R, K));
+      SBN_TRY(check_numel(fn, "Xq (T*K)", T, K));
       *bytes = gemm_ws_bytes(T, R, K, n, m);
       return ok();
     case SBN_OP_GEMM_PREPARED:
       SBN_TRY(check_rows("T", T));
       SBN_TRY(check_k(K));
       SBN_TRY(check_nm(n, m));
+      SBN_TRY(check_numel(fn, "Xq (T*K)", T, K));
       *bytes = gemm_x_bytes(T, K, n, m);
       return ok();
     case SBN_OP_FORWARD:
@@ -334,6 +354,8 @@ sbn_status sbn_workspace_bytes(sbn_op op, int64_t T, int64_t R, int64_t K, int n
       SBN_TRY(check_rows("T", T));
       SBN_TRY(check_rows("R", R));
       SBN_TRY(check_k(K));
+      SBN_TRY(check_numel(fn, "W (R*K)", R, K));
+      SBN_TRY(check_numel(fn, "Xq (T*K)", T, K));
       *bytes = align256(pack_plan(R, K).bytes) + gemm_ws_bytes(T, R, K, n, m);
       return ok();
     case SBN_OP_BACKWARD:
@@ -341,6 +363,9 @@ sbn_status sbn_workspace_bytes(sbn_op op, int64_t T, int64_t R, int64_t K, int n
       SBN_TRY(check_rows("T", T));
       SBN_TRY(check_rows("R", R));
       SBN_TRY(check_k(K));
+      SBN_TRY(check_numel(fn, "W (R*K)", R, K));
+      SBN_TRY(check_numel(fn, "Xq (T*K)", T, K));
+      SBN_TRY(check_numel(fn, "dY (T*R)", T, R));
       *bytes = bwd_ws_bytes(T, R, K, n, m);
       return ok();
   }
@@ -358,8 +383,8 @@ static sbn_status pack_common(const char* fn, const uint16_t* W, int64_t R, int6
   if (n < m) SBN_NONNULL(meta);
   SBN_TRY(check_rows("R", R));
   SBN_TRY(check_k(K));
-  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
-  SBN_TRY(check_ld("ldw", ldw, K));
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
+  SBN_TRY(check_ld("ldw", ldw, K, R));
   if (flags & ~(uint32_t)SBN_MASK_FROM_TERNARY)
     return fail(SBN_ERR_FLAGS, "%s: flags 0x%x: only SBN_MASK_FROM_TERNARY is accepted", fn, (unsigned)flags);
   SBN_ALIGNED(W);
@@ -395,7 +420,8 @@ sbn_status sbn_sgd_update_pack(uint16_t* W, int64_t R, int64_t K, int64_t ldw, c
   const char* fn = "sbn_sgd_update_pack";
   SBN_NONNULL(G);
   SBN_ALIGNED(G);
-  SBN_TRY(check_ld("ldg", ldg, K));
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_ld("ldg", ldg, K, R));
   if (!std::isfinite(lr)) return fail(SBN_ERR_VALUE, "%s: lr must be finite", fn);
   return pack_common(fn, W, R, K, ldw, n, m, flags, codes, meta, s_w, ws, ws_bytes, G, ldg, lr, stream);
 }
@@ -408,7 +434,8 @@ sbn_status sbn_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx, i
   SBN_NONNULL(s_x);
   SBN_TRY(check_rows("T", T));
   SBN_TRY(check_k(K));
-  SBN_TRY(check_ld("ldx", ldx, K));
+  SBN_TRY(check_numel(fn, "Xq (T*K)", T, K));
+  SBN_TRY(check_ld("ldx", ldx, K, T));
   SBN_ALIGNED(X);
   SBN_ALIGNED(Xq);
   hipStream_t st = (hipStream_t)stream;
@@ -439,7 +466,7 @@ sbn_status sbn_gemm_weight_bytes(int64_t R, int64_t K, int n, int m, size_t* byt
   SBN_TRY(check_nm(n, m));
   SBN_TRY(check_rows("R", R));
   SBN_TRY(check_k(K));
-  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
   *bytes = gemm_weight_bytes(R, K, n, m);
   return ok();
 }
@@ -453,7 +480,7 @@ sbn_status sbn_prepare_gemm_weight(const uint8_t* codes, const uint8_t* meta, in
   if (n < m) SBN_NONNULL(meta);
   SBN_TRY(check_rows("R", R));
   SBN_TRY(check_k(K));
-  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
   SBN_ALIGNED(codes);
   if (n < m) SBN_ALIGNED(meta);
   SBN_ALIGNED(prepared);
@@ -489,8 +516,8 @@ sbn_status sbn_forward(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, con
   SBN_NONNULL(X);
   SBN_NONNULL(ws);
   SBN_TRY(check_matmul_args(fn, Xq, s_x, T, K, codes, meta, s_w, R, n, m, Y, ydt, ldy));
-  SBN_TRY(check_ld("ldw", ldw, K));
-  SBN_TRY(check_ld("ldx", ldx, K));
+  SBN_TRY(check_ld("ldw", ldw, K, R));
+  SBN_TRY(check_ld("ldx", ldx, K, T));
   if (flags & ~(uint32_t)SBN_MASK_FROM_TERNARY)
     return fail(SBN_ERR_FLAGS, "%s: flags 0x%x: only SBN_MASK_FROM_TERNARY is accepted", fn, (unsigned)flags);
   SBN_ALIGNED(W);
@@ -570,7 +597,9 @@ static sbn_status backward_common(const char* fn, const uint16_t* dY, int64_t T,
   SBN_TRY(check_rows("R", R));
   SBN_TRY(check_k(K));
   if (R % 8 != 0) return fail(SBN_ERR_SHAPE, "%s: R = %lld must be a multiple of 8", fn, (long long)R);
-  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
+  SBN_TRY(check_numel(fn, "Xq (T*K)", T, K));
+  SBN_TRY(check_numel(fn, "dY (T*R)", T, R));
   if (dX && dxdt != SBN_F32 && dxdt != SBN_BF16)
     return fail(SBN_ERR_DTYPE, "%s: dX dtype must be SBN_F32 or SBN_BF16", fn);
   if (flags & ~(uint32_t)SBN_GRAD_W_MASKED)
@@ -605,7 +634,7 @@ sbn_status sbn_decode_plane_bytes(int64_t R, int64_t K, size_t* bytes) {
   SBN_NONNULL(bytes);
   SBN_TRY(check_rows("R", R));
   SBN_TRY(check_k(K));
-  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
   *bytes = (size_t)round_up(R * K / 4, 16);
   return ok();
 }
@@ -619,7 +648,7 @@ sbn_status sbn_repack_d2(const uint8_t* codes, const uint8_t* meta, int64_t R, i
   if (n < m) SBN_NONNULL(meta);
   SBN_TRY(check_rows("R", R));
   SBN_TRY(check_k(K));
-  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
   SBN_ALIGNED(codes);
   if (n < m) SBN_ALIGNED(meta);
   SBN_ALIGNED(d2);
@@ -638,9 +667,9 @@ static sbn_status check_d2_args(const char* fn, const int8_t* Xq, const float* s
   SBN_TRY(check_rows("T", T));
   SBN_TRY(check_rows("R", R));
   SBN_TRY(check_k(K));
-  if (R * K >= NUMEL_MAX) return fail(SBN_ERR_SHAPE, "%s: R*K too large", fn);
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
   if (T > 16) return fail(SBN_ERR_SHAPE, "%s: T = %lld exceeds 16", fn, (long long)T);
-  SBN_TRY(check_ld("ldy", ldy, R));
+  SBN_TRY(check_ld("ldy", ldy, R, T));
   if (ydt != SBN_F32 && ydt != SBN_BF16 && ydt != SBN_I32_ACC)
     return fail(SBN_ERR_DTYPE, "%s: unknown output dtype %d", fn, (int)ydt);
   SBN_ALIGNED(Xq);

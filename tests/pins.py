@@ -282,6 +282,26 @@ def sgd_matches_exact(sgd_fn, W, G, lr) -> bool:
     return True
 
 
+# ------------------------------------------------------------------ float outputs
+def output_matches_exact(out_f32_fn, out_bf16_fn, acc, s_w, s_x) -> bool:
+    """The float32 output is the float32 nearest (ties even) to the exact
+    acc * c, where c is the float32 nearest to the exact s_w * s_x[t]; the
+    bf16 output is the bf16 nearest (ties even) to that float32 value.  All
+    compared as exact rational values."""
+    got32 = np.asarray(out_f32_fn(acc, s_w, s_x), dtype=np.float32)
+    got16 = np.asarray(out_bf16_fn(acc, s_w, s_x), dtype=np.uint16)
+    sw = _f32_value(s_w)
+    for t in range(acc.shape[0]):
+        c = round_binary(sw * _f32_value(s_x[t]), 24)
+        for r in range(acc.shape[1]):
+            y = round_binary(Fraction(int(acc[t, r])) * c, 24)
+            if Fraction(float(got32[t, r])) != y:
+                return False
+            if _bf16_value(int(got16[t, r])) != round_binary(y, 8):
+                return False
+    return True
+
+
 # ------------------------------------------------------------------ decode plane
 def d2_by_loops(codes):
     """Bit-by-bit construction of the decode plane: position 16w + 4k + b of a

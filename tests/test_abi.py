@@ -290,3 +290,69 @@ def test_injected_launch_failure_reports_hip_error(tmp_path):
         assert int(st) == HIP, line
         assert msg.startswith(name + ":") and "injected" in msg, line
     assert lines[-1] == f"null {NULL}"
+
+
+def test_huge_shapes_rejected_before_any_product(L):
+    """Counts near the int64 range are rejected on the host: every product of
+    two sizes is bounded by a division first (no signed overflow)."""
+    huge = 1 << 50
+    big = 1 << 62
+    i64 = ctypes.c_int64
+    sz = ctypes.c_size_t()
+    assert L.sbn_packed_bytes(i64(huge), 256, 2, 4, ctypes.byref(sz), ctypes.byref(sz)) == SHAPE
+    assert L.sbn_packed_bytes(i64(1 << 30), 1 << 18, 2, 4, ctypes.byref(sz), ctypes.byref(sz)) == SHAPE
+    for op in (sbn.SBN_OP_PACK, sbn.SBN_OP_GEMM, sbn.SBN_OP_FORWARD, sbn.SBN_OP_BACKWARD):
+        assert L.sbn_workspace_bytes(op, i64(16), i64(huge), 256, 2, 4, ctypes.byref(sz)) == SHAPE
+    for op in (sbn.SBN_OP_GEMM, sbn.SBN_OP_GEMM_PREPARED, sbn.SBN_OP_FORWARD, sbn.SBN_OP_BACKWARD):
+        assert L.sbn_workspace_bytes(op, i64(huge), i64(256), 256, 2, 4, ctypes.byref(sz)) == SHAPE
+        assert L.sbn_workspace_bytes(op, i64(1 << 31), i64(256), 1 << 10, 2, 4, ctypes.byref(sz)) == SHAPE
+    assert L.sbn_workspace_bytes(sbn.SBN_OP_BACKWARD, i64(1 << 30), i64(1 << 12), 64, 2, 4,
+                                 ctypes.byref(sz)) == SHAPE                       # dY = T*R too large
+    gemm = L.sbn_sparse_ternary_gemm
+    call = lambda T, R, ldy: gemm(P, P, i64(T), 256, P, P, P, i64(R), 2, 4, P, 1, i64(ldy), P2, ctypes.c_size_t(big),
+                                  None)
+    assert call(16, huge, huge) == SHAPE
+    assert call(huge, 256, 256) == SHAPE
+    assert call(1 << 30, 256, 1 << 20) == SHAPE                                   # T*ldy reaches 2^40
+    assert call(16, 256, 1 << 62) == SHAPE
+    pack = L.sbn_mask_ternarize_pack
+    assert pack(P, i64(huge), 256, 256, 2, 4, P, P, P, P, ctypes.c_size_t(big), None) == SHAPE
+    assert pack(P, i64(1 << 24), 256, i64(1 << 20), 2, 4, P, P, P, P, ctypes.c_size_t(big), None) == SHAPE
+    aq = L.sbn_act_quant
+    assert aq(P, i64(huge), 256, 256, P, P, None) == SHAPE
+    assert aq(P, i64(1 << 30), 256, i64(1 << 12), P, P, None) == SHAPE
+    bwd = L.sbn_backward
+    assert bwd(P, i64(huge), 256, P, P, 256, P, P, P, 2, 4, P, 0, P, P2, ctypes.c_size_t(big), None) == SHAPE
+    assert bwd(P, 64, i64(huge), P, P, 256, P, P, P, 2, 4, P, 0, P, P2, ctypes.c_size_t(big), None) == SHAPE
+    assert b"2^40" in L.sbn_last_error() or b"2^37" in L.sbn_last_error()
+
+
+def test_binding_rejects_layouts_the_abi_cannot_see():
+    """The binding checks what the C ABI has no argument for (element types,
+    unit column strides, contiguity where no leading dimension is passed)
+    before calling it: these fail on the host, with no device involved."""
+    import torch
+    X32 = torch.zeros((4, 256), dtype=torch.float32)
+    with pytest.raises(sbn.SbnError) as e:
+        sbn.sbn_act_quant(X32)
+    assert e.value.status == DTYPE
+    Xq = torch.zeros((256, 4), dtype=torch.int8).t()               # non-contiguous, no ldx in the ABI
+    s_x = torch.zeros(4, dtype=torch.float32)
+    codes = torch.zeros(64, dtype=torch.uint8)
+    s_w = torch.zeros(1, dtype=torch.float32)
+    with pytest.raises(sbn.SbnError) as e:
+        sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, codes, s_w, 16, 2, 4)
+    assert e.value.status == SHAPE
+    Xq = torch.zeros((4, 256), dtype=torch.int8)
+    Ybad = torch.zeros((4, 16), dtype=torch.float32)               # bf16 requested
+    with pytest.raises(sbn.SbnError) as e:
+        sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, codes, s_w, 16, 2, 4, ydt=sbn.SBN_BF16, Y=Ybad)
+    assert e.value.status == DTYPE
+    Wt = torch.zeros((256, 16), dtype=torch.bfloat16).t()          # column stride 16
+    with pytest.raises(sbn.SbnError) as e:
+        sbn.sbn_mask_ternarize_pack(Wt, 2, 4)
+    assert e.value.status == SHAPE
+    dY = torch.zeros((4, 16), dtype=torch.float32)
+    with pytest.raises(sbn.SbnError) as e:
+        sbn.sbn_backward(dY, Xq, s_x, codes, codes, s_w, 2, 4)
+    assert e.value.status == DTYPE

@@ -1,9 +1,11 @@
 """GPU parity: the HIP library, called through its C ABI, against the CPU oracle.
 
 Bars (see gpu_util.py): meta, codes, s_w, Xq, s_x and int32 accumulators are
-compared bit for bit; float outputs within the stated tolerances.  Shapes
+compared bit for bit; float32 and bf16 outputs bit for bit against the
+oracle's rounding of the exact accumulator, and within the stated
+tolerances of the real value.  Shapes
 span several tiles with ragged tails in every dimension, the full workload
-sizes (sampled where the oracle would be slow), all supported N:M ratios,
+sizes (every output), all supported N:M ratios,
 and the degenerate cases (zero weights, zero tokens, ties, subnormals,
 magnitudes outside the fast summation window).
 """
@@ -215,14 +217,29 @@ def run_matmul(kind, Xq, s_x, codes, meta, s_w, R, n, m, ydt):
     return host(Y.contiguous())
 
 
+def assert_float_outputs(y32, yb, acc, sw, sx, what):
+    """f32 Y and bf16 Y: bit for bit the operator's rounding of the exact
+    accumulator (one float32 product with the token's float32 scale; bf16 its
+    nearest-even rounding), and within the stated tolerances of the real value."""
+    if y32 is not None:
+        ref32 = O.output_f32(acc, sw, sx)
+        bad = f32_bits(y32) != f32_bits(ref32)
+        assert not bad.any(), f"{what} f32 Y: {bad.sum()} differ, first at {np.argwhere(bad)[0].tolist()}"
+        assert_rel(y32, O.output(acc, sw, sx), 1e-3, f"{what} f32 Y")
+    if yb is not None:
+        refb = O.output_bf16(acc, sw, sx)
+        bad = yb != refb
+        assert not bad.any(), f"{what} bf16 Y: {bad.sum()} differ, first at {np.argwhere(bad)[0].tolist()}"
+        assert_rel(bf16_bits_to_f64(yb), O.output(acc, sw, sx), BF16_REL, f"{what} bf16 Y")
+
+
 def check_outputs(kind, f, Xq, s_x, codes, meta, s_w, R, n, m):
     acc = run_matmul(kind, Xq, s_x, codes, meta, s_w, R, n, m, sbn.SBN_I32_ACC)
     assert np.array_equal(acc.astype(np.int64), f["acc"]), \
         f"acc differ at {np.argwhere(acc != f['acc'])[:3].tolist()}"
     y32 = run_matmul(kind, Xq, s_x, codes, meta, s_w, R, n, m, sbn.SBN_F32)
-    assert_rel(y32, f["y"], 1e-3, f"{kind} f32 Y")
     yb = run_matmul(kind, Xq, s_x, codes, meta, s_w, R, n, m, sbn.SBN_BF16)
-    assert_rel(bf16_bits_to_f64(yb), f["y"], BF16_REL, f"{kind} bf16 Y")
+    assert_float_outputs(y32, yb, f["acc"], f["s_w"], f["s_x"], kind)
 
 
 def test_gemm_tiny_workload_fp32_output():
@@ -329,7 +346,7 @@ def test_gemv_batched_matches_oracle(n, m, K, count, R, T):
             if ydt == sbn.SBN_I32_ACC:
                 assert np.array_equal(got.astype(np.int64), acc), f"weight {b}"
             else:
-                assert_rel(got, O.output(acc, sw, s_x_h), 1e-3, f"weight {b} f32 Y")
+                assert_float_outputs(got, None, acc, sw, s_x_h, f"weight {b}")
 
 
 @pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
@@ -344,35 +361,29 @@ def test_gemv_decode_full_size(n, m):
         got = run_matmul("gemv", dev(Xq_h), dev(s_x_h), codes, meta, s_w, 4096, n, m, sbn.SBN_I32_ACC)
         assert np.array_equal(got.astype(np.int64), acc)
         yb = run_matmul("gemv", dev(Xq_h), dev(s_x_h), codes, meta, s_w, 4096, n, m, sbn.SBN_BF16)
-        assert_rel(bf16_bits_to_f64(yb), O.output(acc, sw, s_x_h), BF16_REL, "decode bf16 Y")
+        assert_float_outputs(None, yb, acc, sw, s_x_h, f"decode T={T}")
 
 
-def sampled_check(Xq_h, s_x_h, eff, sw, got_acc, got_bf16, nsamp=4096, seed=0):
-    rng = np.random.default_rng(seed)
-    T, R = got_acc.shape
-    ts = rng.integers(0, T, nsamp)
-    rs = rng.integers(0, R, nsamp)
-    ref = np.einsum("ik,ik->i", Xq_h[ts].astype(np.int64), eff[rs].astype(np.int64))
-    assert np.array_equal(got_acc[ts, rs].astype(np.int64), ref)
-    y = ref.astype(np.float64) * float(sw) * s_x_h[ts].astype(np.float64)
-    assert_rel(bf16_bits_to_f64(got_bf16[ts, rs]), y, BF16_REL, "sampled bf16 Y")
-    # every output: the bf16 result is the scaled int32 result
-    ysc = got_acc.astype(np.float64) * float(sw) * s_x_h.astype(np.float64)[:, None]
-    assert_rel(bf16_bits_to_f64(got_bf16), ysc, BF16_REL, "bf16 Y vs scaled acc")
-
-
-@pytest.mark.parametrize("name,n,m", [("prefill", 2, 4), ("sweep", 2, 4), ("sweep", 6, 8), ("sweep", 8, 8),
-                                      ("sweep", 4, 8), ("sweep", 2, 8), ("sweep", 1, 4)])
-def test_gemm_full_size_sampled(name, n, m):
+@pytest.mark.parametrize("name,n,m", [("prefill", 2, 4), ("train", 6, 8), ("sweep", 2, 4), ("sweep", 4, 8),
+                                      ("sweep", 6, 8), ("sweep", 2, 8), ("sweep", 1, 4), ("sweep", 8, 8)])
+def test_gemm_full_size_exact(name, n, m):
+    """Every output of the GEMM at the full prefill, train-step and sweep
+    shapes: the whole int32 accumulator equals the oracle's, and the bf16 Y
+    equals the oracle's rounding of it, element by element."""
     wl = WORKLOADS[name]
     W, eff, cp, mp, sw = full_ref(name, n, m)
     codes, meta, s_w = check_pack(W, n, m, ref=(cp, mp, sw))
     X = wl.activations(seed=0)
     Xq_h, s_x_h = O.act_quant(X)
     Xq, s_x = check_act_quant(X)
+    print(f"full-size GEMM {name} {n}:{m} T={wl.T} R={wl.R} K={wl.K}", flush=True)
     acc = run_matmul("gemm", Xq, s_x, codes, meta, s_w, wl.R, n, m, sbn.SBN_I32_ACC)
+    ref = O.accumulate(Xq_h, eff)
+    bad = acc.astype(np.int64) != ref
+    assert not bad.any(), f"acc: {bad.sum()} of {bad.size} differ, first at {np.argwhere(bad)[0].tolist()}"
+    del bad, acc
     yb = run_matmul("gemm", Xq, s_x, codes, meta, s_w, wl.R, n, m, sbn.SBN_BF16)
-    sampled_check(Xq_h, s_x_h, eff, sw, acc, yb)
+    assert_float_outputs(None, yb, ref, sw, s_x_h, f"{name} {n}:{m}")
 
 
 def test_gemm_deterministic_and_matches_gemv():
@@ -417,7 +428,9 @@ def test_backward_multi_tile_and_bf16_dx():
     check_backward(40, 64, 128, 6, 8, seed=4, dxdt=sbn.SBN_BF16)
 
 
-def test_backward_train_size_sampled():
+def test_backward_train_size_full():
+    """The train-step backward at full size (T=8192, R=11008, K=4096, 6:8):
+    every element of dX and dW against the oracle within the abs-product bound."""
     import torch
     wl = WORKLOADS["train"]
     n, m = wl.nm[0]
@@ -426,19 +439,16 @@ def test_backward_train_size_sampled():
     X = wl.activations(seed=0)
     dY = wl.upstream_grad(seed=0)
     Xq_h, s_x_h = O.act_quant(X)
+    print(f"full-size backward train {n}:{m}", flush=True)
     dX, dW = sbn.sbn_backward(dev_bf16(dY), dev(Xq_h), dev(s_x_h), codes, meta, s_w, n, m)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    dYf = bf16_bits_to_f64(dY)
-    ts = rng.choice(wl.T, 24, replace=False)
-    gX = dYf[ts] @ (float(sw) * eff.astype(np.float64))
-    bX = np.abs(dYf[ts]) @ (float(sw) * np.abs(eff.astype(np.float64)))
-    assert_abs_product(host(dX[torch.from_numpy(ts).cuda()]), gX, bX, "dX rows")
-    rs = rng.choice(wl.R, 24, replace=False)
-    Xh = s_x_h.astype(np.float64)[:, None] * Xq_h.astype(np.float64)
-    gW = dYf[:, rs].T @ Xh
-    bW = np.abs(dYf[:, rs]).T @ np.abs(Xh)
-    assert_abs_product(host(dW[torch.from_numpy(rs).cuda()]), gW, bW, "dW rows")
+    gX, gW = O.backward(dY, Xq_h, s_x_h, eff, sw)
+    dYa = np.abs(bf16_bits_to_f64(dY))
+    bX = dYa @ (float(sw) * np.abs(eff.astype(np.float64)))
+    assert_abs_product(host(dX), gX, bX, "dX")
+    del gX, bX, dX
+    bW = dYa.T @ (s_x_h.astype(np.float64)[:, None] * np.abs(Xq_h.astype(np.float64)))
+    assert_abs_product(host(dW), gW, bW, "dW")
 
 
 # ------------------------------------------------------------------ HIP graph replay

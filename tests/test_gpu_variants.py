@@ -191,14 +191,27 @@ def check_forward(T, R, K, n, m, flags=0, ldw=None, ldx=None, seed=0, ydt=None):
     assert np.array_equal(host(Xq), xq)
     assert np.array_equal(f32_bits(host(s_x)), f32_bits(sx))
     acc = O.accumulate(xq, eff)
+    check_forward_y(Y, ydt, acc, sw, sx)
+
+
+def check_forward_y(Y, ydt, acc, sw, sx):
+    """Y of the one-call forward: the int32 accumulator exactly; f32 / bf16 bit
+    for bit the oracle's rounding of it, and within the stated tolerances."""
+    got = host(Y)
     if ydt == sbn.SBN_I32_ACC:
-        assert np.array_equal(host(Y).astype(np.int64), acc)
+        bad = got.astype(np.int64) != acc
+        assert not bad.any(), f"acc: {bad.sum()} differ, first at {np.argwhere(bad)[0].tolist()}"
+        return
+    y = O.output(acc, sw, sx)
+    if ydt == sbn.SBN_BF16:
+        bad = got != O.output_bf16(acc, sw, sx)
+        got = bf16_bits_to_f64(got)
+        rel = 2.0 ** -8 + 2.0 ** -20
     else:
-        y = O.output(acc, sw, sx)
-        got = host(Y)
-        got = bf16_bits_to_f64(got) if ydt == sbn.SBN_BF16 else got
-        rel = 2.0 ** -8 + 2.0 ** -20 if ydt == sbn.SBN_BF16 else 1e-3
-        assert (np.abs(got - y) <= rel * np.abs(y)).all()
+        bad = f32_bits(got) != f32_bits(O.output_f32(acc, sw, sx))
+        rel = 1e-3
+    assert not bad.any(), f"Y: {bad.sum()} differ, first at {np.argwhere(bad)[0].tolist()}"
+    assert (np.abs(got - y) <= rel * np.abs(y)).all()
 
 
 @pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (1, 8), (8, 8)])
@@ -230,6 +243,25 @@ def test_forward_prefill_size_equals_separate_calls():
     torch.cuda.synchronize()
     for x, y in zip(a, (codes, meta, s_w, Xq, s_x, Y)):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["prefill", "train"])
+def test_forward_full_size_exact(name):
+    """The one-call forward exactly as the benchmark runs it (full prefill
+    shape at 2:4 and full train-step shape at 6:8, bf16 Y): planes, scales,
+    Xq, s_x and every bf16 output against the oracle."""
+    import torch
+    wl = WORKLOADS[name]
+    n, m = wl.nm[0]
+    W, X = wl.weights(0), wl.activations(0)
+    print(f"full-size forward {name} {n}:{m} T={wl.T} R={wl.R} K={wl.K}", flush=True)
+    codes, meta, s_w, Xq, s_x, Y = sbn.sbn_forward(dev_bf16(W), dev_bf16(X), n, m, ydt=sbn.SBN_BF16)
+    torch.cuda.synchronize()
+    eff, mask, sw = compare_planes(codes, meta, s_w, W, n, m, "master")
+    xq, sx = O.act_quant(X)
+    assert np.array_equal(host(Xq), xq)
+    assert np.array_equal(f32_bits(host(s_x)), f32_bits(sx))
+    check_forward_y(Y, sbn.SBN_BF16, O.accumulate(xq, eff), sw, sx)
 
 
 # ------------------------------------------------------------------ optional non-finite input check

@@ -129,7 +129,10 @@ def test_pack_mutants_are_caught(mutant):
     assert not (cp.tolist() == ecp.tolist() and mp.tolist() == emp.tolist())
 
 
-def _aq_reciprocal(X):
+def _aq_reading_reciprocal_multiply(X):
+    """The other reading of the activation rounding, q = rint(fl32(x * fl32(127/a))):
+    not the one the oracle takes (q = rint((127x)/a), one division), and the
+    exact-rational pin tells the two apart."""
     x = O.bf16_to_f32(X)
     a = np.maximum(np.abs(x).max(1), np.float32(1e-5))
     q = np.clip(np.rint(x * (np.float32(127) / a)[:, None]), -127, 127).astype(np.int8)
@@ -151,7 +154,7 @@ def _aq_scale_128(X):
     return q, (a / np.float32(128)).astype(np.float32)
 
 
-@pytest.mark.parametrize("mutant", [_aq_reciprocal, _aq_half_away, _aq_scale_128])
+@pytest.mark.parametrize("mutant", [_aq_reading_reciprocal_multiply, _aq_half_away, _aq_scale_128])
 def test_act_quant_mutants_are_caught(mutant):
     X = f32_to_bf16_bits(np.array([[3.0, 1.5, -1.5, 0.75, 2.0, -1.0, 0.5, 0.25],
                                    [8.0, 4.0, -4.0, 1.5, 3.0, 0.0, 1.0, 2.0],
@@ -301,3 +304,45 @@ def test_d2_mutants_are_caught(mutant):
     codes, _, _ = O.quant_then_mask(W, 6, 8)
     plane = mutant(codes)
     assert not (np.array_equal(plane, pins.d2_by_loops(codes)) and pins.d2_decode_matches(plane, codes))
+
+
+# ------------------------------------------------------------------ float outputs
+def _out_one_rounding(acc, s_w, s_x):
+    y = acc.astype(np.float64) * np.float64(s_w) * s_x.astype(np.float64)[:, None]
+    return y.astype(np.float32)
+
+
+def _out_scale_acc_first(acc, s_w, s_x):
+    y = (acc.astype(np.float32) * np.float32(s_w)).astype(np.float32)
+    return (y * s_x.astype(np.float32)[:, None]).astype(np.float32)
+
+
+def _out_bf16_truncated(acc, s_w, s_x):
+    return (O.output_f32(acc, s_w, s_x).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _out_bf16_half_up(acc, s_w, s_x):
+    u = O.output_f32(acc, s_w, s_x).view(np.uint32).astype(np.uint64)
+    return ((u + 0x8000) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("mutant", [_out_one_rounding, _out_scale_acc_first, _out_bf16_truncated,
+                                    _out_bf16_half_up])
+def test_output_mutants_are_caught(mutant):
+    rng = np.random.default_rng(5)
+    T, R = 24, 40
+    acc = rng.integers(-127 * 4096, 127 * 4096 + 1, size=(T, R))
+    acc[:, 0] = 1 << np.arange(T)                   # exact powers of two: bf16 ties of c itself
+    s_w = np.float32(1 / 3)
+    s_x = (np.float32(1.0) / np.arange(3, 3 + T, dtype=np.float32) / np.float32(127)).astype(np.float32)
+    f32_fn, bf16_fn = O.output_f32, O.output_bf16
+    if mutant in (_out_one_rounding, _out_scale_acc_first):
+        f32_fn = mutant
+        bf16_fn = lambda a, s, x: O.f32_to_bf16_rne(mutant(a, s, x))
+    else:
+        bf16_fn = mutant
+    # power-of-two scales: acc = 257, 259, 770, 774 lie exactly half-way between two bf16 values
+    acc2 = np.array([[257, 259, -257, 770, 774, 1, -3]])
+    p2 = (np.float32(0.5), np.array([2.0 ** -7], dtype=np.float32))
+    assert not (pins.output_matches_exact(f32_fn, bf16_fn, acc, s_w, s_x)
+                and pins.output_matches_exact(f32_fn, bf16_fn, acc2, *p2))

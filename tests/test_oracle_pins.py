@@ -47,6 +47,11 @@ def test_worked_example_1x8():
     assert f["Xq"].tolist() == [e["Xq"]]
     assert f32_bits(f["s_x"][0]) == int(e["s_x_bits"], 16)
     assert int(f["acc"][0, 0]) == e["acc"]
+    # the float outputs, derived by hand with the token scale rounded once
+    c = np.float32(f["s_w"]) * f["s_x"]
+    assert f32_bits(c[0]) == int(e["scale_bits"], 16)
+    assert f32_bits(O.output_f32(f["acc"], f["s_w"], f["s_x"])[0, 0]) == int(e["y_f32_bits"], 16)
+    assert int(O.output_bf16(f["acc"], f["s_w"], f["s_x"])[0, 0]) == int(e["y_bf16_bits"], 16)
     # exact real value -51/127; the oracle applies the fp32 s_x (8/127 rounded),
     # so the two differ by at most that one fp32 rounding
     exact = Fraction(e["y_num"], e["y_den"])
@@ -270,6 +275,37 @@ def test_output_scaling_exact_rational():
             exact = Fraction(int(f["acc"][t, r])) * Fraction(float(f["s_w"])) * Fraction(float(f["s_x"][t]))
             got = Fraction(float(f["y"][t, r]))
             assert abs(got - exact) <= abs(exact) * Fraction(1, 2 ** 50)
+
+
+def test_output_f32_and_bf16_match_exact_roundings():
+    """Float outputs against exact rational arithmetic: one float32 rounding
+    of s_w * s_x[t], one of acc times it, one bf16 rounding of that."""
+    rng = np.random.default_rng(12)
+    T, R = 24, 40
+    acc = rng.integers(-127 * 4096, 127 * 4096 + 1, size=(T, R))
+    acc[0, :4] = [0, 1, -1, 127 * 8192]
+    s_w = np.float32(rng.uniform(0.005, 0.03))
+    s_x = (rng.uniform(0.001, 0.2, size=T)).astype(np.float32)
+    assert pins.output_matches_exact(O.output_f32, O.output_bf16, acc, s_w, s_x)
+    # scales with many significant bits on both sides (products far from exact)
+    s_x2 = np.float32(1.0) / np.arange(3, 3 + T, dtype=np.float32) / np.float32(127)
+    assert pins.output_matches_exact(O.output_f32, O.output_bf16, acc, np.float32(1 / 3), s_x2)
+    # c = 2^-8: 257, 259, 770 and 774 land half-way between two bf16 values (hand-derived:
+    # 1 + 2^-8 -> 1, 1 + 3*2^-8 -> 1 + 2^-6, 3 + 2^-7 -> 3, 3 + 3*2^-7 -> 3 + 2^-5 ... ties to even)
+    acc2 = np.array([[257, 259, -257, 770, 774, 1, -3]])
+    assert pins.output_matches_exact(O.output_f32, O.output_bf16, acc2, np.float32(0.5),
+                                     np.array([2.0 ** -7], dtype=np.float32))
+    assert O.output_bf16(acc2, np.float32(0.5), np.array([2.0 ** -7], np.float32)).tolist() == \
+        [[0x3F80, 0x3F82, 0xBF80, 0x4040, 0x4042, 0x3B80, 0xBC40]]
+
+
+def test_output_f32_within_rel_bound_of_real_value():
+    """Two float32 roundings stay within 2^-23 relative of the real product."""
+    W = gaussian_bf16((16, 256), 0.02, seed=13, stream=0)
+    X = gaussian_bf16((8, 256), 1.0, seed=13, stream=1)
+    f = O.forward(W, X, 2, 4)
+    y32 = O.output_f32(f["acc"], f["s_w"], f["s_x"]).astype(np.float64)
+    assert np.all(np.abs(y32 - f["y"]) <= 2.0 ** -23 * np.abs(f["y"]))
 
 
 # ----------------------------------------------------------------- backward
