@@ -175,6 +175,21 @@ sbn_status sbn_mask_ternarize_pack_ex(const uint16_t* W, int64_t R, int64_t K, i
                                       float* s_w, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sbn_mask_ternarize_pack without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): same arguments and results bit for
+ * bit, no flags.  Its scratch is a fixed 528 KiB array inside the library, one
+ * per GPU, kept until the process ends; the call allocates and frees nothing.
+ * Limit: R*K <= 2^28 (larger weights return SBN_ERR_WORKSPACE and launch
+ * nothing; use sbn_mask_ternarize_pack with a workspace).  All calls on one GPU
+ * share that scratch: calls that overlap on one GPU (different streams, or
+ * threads, without ordering) race and are outside the contract; calls ordered
+ * on one stream are fine.  SBN_CHECK_FINITE is not applied.
+ */
+sbn_status sbn_mask_ternarize_pack_noalloc(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
+                                           uint8_t* codes, uint8_t* meta, float* s_w, void* stream);
+
+/*
  * One optimizer step on the BF16 master weights followed by the next
  * step's mask/ternarize/pack of the updated weights, in two passes over W.
  * The pages keep BF16 master weights that receive the gradients and

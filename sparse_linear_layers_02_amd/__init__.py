@@ -55,6 +55,7 @@ _SIGNATURES = {
     "sbn_mask_ternarize_pack_ex": ([_vp, _i64, _i64, _i64, _int, _int, _u32, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "sbn_sgd_update_pack": ([_vp, _i64, _i64, _i64, _vp, _i64, ctypes.c_float, _int, _int, _u32, _vp, _vp, _vp,
                              _vp, _sz, _vp], _int),
+    "sbn_mask_ternarize_pack_noalloc": ([_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp], _int),
     "sbn_act_quant": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], _int),
     "sbn_sparse_ternary_gemm": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _int, _int, _vp, _int, _i64,
                                  _vp, _sz, _vp], _int),
@@ -182,7 +183,7 @@ def _req(t, name: str, dt: str, contiguous: bool = False, fn: str = "sbn") -> No
         raise SbnError(fn, 2, f"{name} must have unit column stride (row-major)")
 
 
-def _pack_outputs(W, n: int, m: int, codes, meta, s_w, ws, stream=None):
+def _pack_outputs(W, n: int, m: int, codes, meta, s_w, ws, stream=None, want_ws=True):
     torch = _torch()
     R, K = W.shape
     _req(W, "W", "bf16")
@@ -197,9 +198,8 @@ def _pack_outputs(W, n: int, m: int, codes, meta, s_w, ws, stream=None):
         meta = torch.empty(mb, dtype=torch.uint8, device=dev)
     if s_w is None:
         s_w = torch.empty(1, dtype=torch.float32, device=dev)
-    need = sbn_workspace_bytes(SBN_OP_PACK, 0, R, K, n, m)
-    if ws is None:
-        ws = _workspace("pack", need, dev, stream)
+    if want_ws and ws is None:
+        ws = _workspace("pack", sbn_workspace_bytes(SBN_OP_PACK, 0, R, K, n, m), dev, stream)
     return codes, meta, s_w, ws
 
 
@@ -223,6 +223,17 @@ def sbn_mask_ternarize_pack_ex(W, n: int, m: int, flags: int, *, codes=None, met
            lib().sbn_mask_ternarize_pack_ex(_ptr(W), R, K, W.stride(0), n, m, flags, _ptr(codes), _ptr(meta),
                                             _ptr(s_w), _ptr(ws), ws.numel() if ws is not None else 0,
                                             _stream(stream)))
+    return codes, meta, s_w
+
+
+def sbn_mask_ternarize_pack_noalloc(W, n: int, m: int, *, codes=None, meta=None, s_w=None, stream=None):
+    """sbn_mask_ternarize_pack on the library's fixed scratch (no workspace; R*K <= 2^28).
+    Returns (codes, meta, s_w)."""
+    R, K = W.shape
+    codes, meta, s_w, _ = _pack_outputs(W, n, m, codes, meta, s_w, None, stream, want_ws=False)
+    _check("sbn_mask_ternarize_pack_noalloc",
+           lib().sbn_mask_ternarize_pack_noalloc(_ptr(W), R, K, W.stride(0), n, m, _ptr(codes), _ptr(meta),
+                                                 _ptr(s_w), _stream(stream)))
     return codes, meta, s_w
 
 
@@ -510,7 +521,7 @@ def sbn_profile_dump() -> dict:
 
 __all__ = [
     "lib", "header_symbols", "SbnError", "sbn_abi_version", "sbn_packed_bytes", "sbn_workspace_bytes",
-    "sbn_mask_ternarize_pack", "sbn_act_quant", "sbn_sparse_ternary_gemm", "sbn_sparse_ternary_gemv",
+    "sbn_mask_ternarize_pack", "sbn_mask_ternarize_pack_noalloc", "sbn_act_quant", "sbn_sparse_ternary_gemm", "sbn_sparse_ternary_gemv",
     "sbn_backward", "sbn_backward_ex", "sbn_mask_ternarize_pack_ex", "sbn_sgd_update_pack", "sbn_forward",
     "sbn_decode_plane_bytes", "sbn_repack_d2", "sbn_ternary_gemv_d2", "sbn_ternary_gemv_d2_batched",
     "sbn_gemm_weight_bytes", "sbn_prepare_gemm_weight", "sbn_sparse_ternary_gemm_prepared", "SBN_OP_GEMM_PREPARED",

@@ -414,6 +414,34 @@ sbn_status sbn_mask_ternarize_pack_ex(const uint16_t* W, int64_t R, int64_t K, i
                      nullptr, 0, 0.0f, stream);
 }
 
+sbn_status sbn_mask_ternarize_pack_noalloc(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
+                                           uint8_t* codes, uint8_t* meta, float* s_w, void* stream) {
+  const char* fn = "sbn_mask_ternarize_pack_noalloc";
+  SBN_NONNULL(W);
+  SBN_NONNULL(codes);
+  SBN_NONNULL(s_w);
+  SBN_TRY(check_nm(n, m));
+  if (n < m) SBN_NONNULL(meta);
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
+  SBN_TRY(check_ld("ldw", ldw, K, R));
+  SBN_ALIGNED(W);
+  SBN_ALIGNED(codes);
+  if (n < m) SBN_ALIGNED(meta);
+  const size_t need = pack_plan(R, K).bytes;
+  if (need > noalloc_scratch_bytes())
+    return fail(SBN_ERR_WORKSPACE,
+                "%s: R*K = %lld needs %zu bytes of scratch, above the library's fixed %zu (R*K up to 2^28); "
+                "use sbn_mask_ternarize_pack with a workspace",
+                fn, (long long)(R * K), need, noalloc_scratch_bytes());
+  void* scr = nullptr;
+  const hipError_t e = noalloc_scratch(&scr);
+  if (e != hipSuccess) return fail(SBN_ERR_HIP, "%s: scratch address: %s", fn, hipGetErrorString(e));
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_pack(W, R, K, ldw, n, m, codes, meta, s_w, scr, 0u, nullptr, 0, 0.0f, st), st, fn);
+}
+
 sbn_status sbn_sgd_update_pack(uint16_t* W, int64_t R, int64_t K, int64_t ldw, const float* G, int64_t ldg,
                                float lr, int n, int m, uint32_t flags, uint8_t* codes, uint8_t* meta,
                                float* s_w, void* ws, size_t ws_bytes, void* stream) {

@@ -38,6 +38,9 @@
 // fp32: a float64 estimate, and an exact comparison against the two
 // neighbouring midpoints whenever the estimate is too close to one of them
 // to decide.  The workspace needs no initialisation.
+#include <map>
+#include <mutex>
+
 #include "act_quant.h"
 
 namespace sbn {
@@ -761,6 +764,43 @@ hipError_t launch_pack_quant(const uint16_t* W, int64_t R, int64_t K, int64_t ld
   else SBN_MPQ(1);
 #undef SBN_MPQ
   return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- allocation-free pack
+// Workspace of sbn_mask_ternarize_pack_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  It takes the pack workspace
+// (per-block int64 partials, flags and exponent bins), which every call
+// writes in full before reading, so nothing in it has to be cleared; up to
+// 256 pass-1 blocks fit, i.e. every weight with R*K <= 2^28.  In host code the
+// array's name is not a device address: its address on the current device
+// comes from hipGetSymbolAddress, once per device, and only that address is
+// handed to the kernels.
+constexpr size_t NOALLOC_SCRATCH_BYTES = 528 * 1024;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+namespace {
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;   // device -> address of `scratch` there
+}  // namespace
+
+size_t noalloc_scratch_bytes() { return NOALLOC_SCRATCH_BYTES; }
+
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *ptr = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_ptr[dev] = p;
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace sbn

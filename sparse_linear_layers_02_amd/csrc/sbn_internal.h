@@ -71,6 +71,10 @@ struct PackPlan {
   size_t bytes;
 };
 PackPlan pack_plan(int64_t R, int64_t K);
+// The allocation-free pack's device scratch: its size, and its address on the
+// current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
 
 // Sparse (smfmac) expansion: values [RB][KB128][64][16 B] + idx [RB][KB128][64][4 B]
 // Dense expansion: [RB][KB64][64][16 B]; RB covers R rounded up to the GEMM row tile.

@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = sbn.header_symbols()
-    assert len(names) == 25
+    assert len(names) == 26
     for nm in names:
         assert hasattr(L, nm), nm
 
@@ -356,3 +356,18 @@ def test_binding_rejects_layouts_the_abi_cannot_see():
     with pytest.raises(sbn.SbnError) as e:
         sbn.sbn_backward(dY, Xq, s_x, codes, codes, s_w, 2, 4)
     assert e.value.status == DTYPE
+
+
+def test_noalloc_pack_validation(L):
+    """The allocation-free pack validates like the pack and refuses weights
+    beyond its fixed scratch (R*K above 2^28) before any launch."""
+    f = L.sbn_mask_ternarize_pack_noalloc
+    i64 = ctypes.c_int64
+    assert f(None, 16, 256, 256, 2, 4, P, P, P, None) == NULL
+    assert f(P, 16, 256, 256, 2, 4, P, None, P, None) == NULL
+    assert f(P, 16, 250, 256, 2, 4, P, P, P, None) == SHAPE
+    assert f(P, 16, 256, 260, 2, 4, P, P, P, None) == ALIGN
+    assert f(P, 16, 256, 256, 3, 6, P, P, P, None) == NM
+    assert f(P, i64(1 << 19), 1 << 10, 1 << 10, 2, 4, P, P, P, None) == WS       # R*K = 2^29
+    assert b"2^28" in L.sbn_last_error()
+    assert f(P, i64(1 << 50), 256, 256, 2, 4, P, P, P, None) == SHAPE
