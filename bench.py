@@ -264,7 +264,9 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
     from the library's events; (ii-a) the pool as separate calls, replayed as
     four HIP graphs on four streams so launch ramps overlap; (ii-b) the pool
     as batched calls of 64 weights that share the activations (one launch
-    each), replayed from a HIP graph.  GB/s = algorithmic bytes (packed W +
+    each), replayed from a HIP graph; (ii-c) the pool as one table call (its
+    weights listed once in a device table: one launch), replayed from a HIP
+    graph.  GB/s = algorithmic bytes (packed W +
     Xq + s_x + Y + s_w per weight) / time."""
     import torch
     import sparse_linear_layers_02_amd as sbn
@@ -334,6 +336,11 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
     gb = capture(lambda: [batched(b0) for b0 in range(0, P, B)])
     bt_ms = replay_ms([gb], [streams[0]], P)
     del gb
+    # (ii-c) the pool as one table call (one launch), one graph on one stream
+    tab = sbn.GemvTable(codes, metas, s_ws, wl.R, wl.K, n, m, T=T, Ys=Ys)
+    gt = capture(lambda: sbn.sbn_sparse_ternary_gemv_table(Xq, s_x, tab))
+    tb_ms = replay_ms([gt], [streams[0]], P)
+    del gt, tab
     frac = lambda ms_: round(algo / (ms_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
     gbps = lambda ms_: round(algo / (ms_ * 1e-3) / 1e9, 1)
     return {
@@ -344,6 +351,8 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
                                            "frac_hbm": frac(ss_ms)},
         f"steady_batched_{B}": {"us_per_weight": round(bt_ms * 1e3, 3), "GBps": gbps(bt_ms), "frac_hbm": frac(bt_ms),
                                 "launches_per_pool": P // B},
+        f"steady_table_{P}": {"us_per_weight": round(tb_ms * 1e3, 3), "GBps": gbps(tb_ms), "frac_hbm": frac(tb_ms),
+                              "launches_per_pool": 1},
     }
 
 
@@ -489,6 +498,10 @@ def speedup_tables(reps):
                     Xq, s_x, p["codes"][b:b + BATCH], p["metas"][b:b + BATCH], p["s_ws"][b:b + BATCH], R, n, m,
                     Ys=Ys[b:b + BATCH]) for b in range(0, P, BATCH)], reps)
                 row[f"sbn_{n}{m}_batched_us"] = round(ms * 1e3 / P, 3)
+                tab = sbn.GemvTable(p["codes"], p["metas"], p["s_ws"], R, K, n, m, T=T, Ys=Ys)
+                ms = graph_ms(lambda: sbn.sbn_sparse_ternary_gemv_table(Xq, s_x, tab), reps)
+                row[f"sbn_{n}{m}_table_us"] = round(ms * 1e3 / P, 3)
+                del tab
             if (n, m) == (6, 8):                       # the same weights as decode planes (2 bits per weight)
                 Pd = -(-2 * MALL_BYTES // (R * K // 4))
                 d2s = [sbn.sbn_repack_d2(p["codes"][i % P], p["metas"][i % P], R, K, n, m) for i in range(Pd)]
@@ -498,6 +511,10 @@ def speedup_tables(reps):
                     Xq, s_x, d2s[b:b + BATCH], sds[b:b + BATCH], R, Ys=Yd[b:b + BATCH])
                     for b in range(0, Pd, BATCH)], reps)
                 row["sbn_68_d2_batched_us"] = round(ms * 1e3 / Pd, 3)
+                tab = sbn.GemvTable.planes(d2s, sds, R, K, T=T, Ys=Yd)
+                ms = graph_ms(lambda: sbn.sbn_ternary_gemv_d2_table(Xq, s_x, tab), reps)
+                row["sbn_68_d2_table_us"] = round(ms * 1e3 / Pd, 3)
+                del tab
                 del d2s, sds, Yd
             del Ys, ws
         Yb = [torch.empty((T, R), dtype=torch.bfloat16, device="cuda") for _ in range(Pb)]
@@ -507,7 +524,8 @@ def speedup_tables(reps):
         ms, err = vendor(lambda: [torch._int_mm(Xq, Wi[i], out=Yi[i]) for i in range(Pi)])
         row["int8_us"], row["int8_error"] = (round(ms * 1e3 / Pi, 3) if ms else None), err
         del Yb, Yi
-        for key in ("sbn_24", "sbn_68", "sbn_24_batched", "sbn_68_batched", "sbn_68_d2_batched"):
+        for key in ("sbn_24", "sbn_68", "sbn_24_batched", "sbn_68_batched", "sbn_68_d2_batched", "sbn_24_table",
+                    "sbn_68_table", "sbn_68_d2_table"):
             t = row[key + "_us"]
             row[key + "_vs_dense_ternary"] = round(row["sbn_88_us"] / t, 3)
             row[key + "_vs_bf16"] = round(row["bf16_us"] / t, 3) if row["bf16_us"] else None
@@ -624,40 +642,36 @@ def cpu_baseline(wl, n, m, tokens, runs=3):
 
 
 # ---------------------------------------------------------------------- decode step
-POOL, BATCH = 128, 64
+POOL = 128                     # weights per pool (one table launch per pool)
+BATCH = 64                     # weights per by-value batched call (its maximum)
 
 
 def make_decode_step(T=1):
     """Decode step: every weight of two pools of POOL distinct R = K = 4096
     packed weights (2:4 and 6:8; 537 MB and 671 MB, each at least twice the
-    Infinity Cache) multiplied by the same T activations, as batched calls of
-    BATCH weights (one launch each).  Returns (step, bytes per step, per-launch
-    bytes by kernel name)."""
+    Infinity Cache) multiplied by the same T activations, one table GEMV per
+    pool (the pool's weights listed once in a device table: one launch each).
+    Returns (step, bytes per step, per-launch bytes by kernel name, workload)."""
     import torch
     import sparse_linear_layers_02_amd as sbn
     from workloads import WORKLOADS
     wl = WORKLOADS["decode"]
     W = bf16_dev(wl.weights(0))
     Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0, T=T)))
-    pools, total, per_launch = [], 0, {}
+    tables, total, per_launch = [], 0, {}
     for n, m in wl.nm:
         codes0, meta0, s_w0 = sbn.sbn_mask_ternarize_pack(W, n, m)
         cb, mb = sbn.sbn_packed_bytes(wl.R, wl.K, n, m)
         per = cb + mb + T * wl.K + 4 * T + 2 * T * wl.R + 4
-        pool = dict(n=n, m=m, codes=[codes0.clone() for _ in range(POOL)], metas=[meta0.clone() for _ in range(POOL)],
-                    s_ws=[s_w0.clone() for _ in range(POOL)],
-                    Ys=[torch.empty((T, wl.R), dtype=torch.bfloat16, device="cuda") for _ in range(POOL)])
-        pools.append(pool)
+        tables.append(sbn.GemvTable([codes0.clone() for _ in range(POOL)], [meta0.clone() for _ in range(POOL)],
+                                    [s_w0.clone() for _ in range(POOL)], wl.R, wl.K, n, m, T=T))
         total += POOL * per
-        per_launch[f"gemv_stream_{n}{m}"] = BATCH * per
+        per_launch[f"gemv_stream_{n}{m}"] = POOL * per
     del W
 
     def step():
-        for p in pools:
-            for b0 in range(0, POOL, BATCH):
-                sl = slice(b0, b0 + BATCH)
-                sbn.sbn_sparse_ternary_gemv_batched(Xq, s_x, p["codes"][sl], p["metas"][sl], p["s_ws"][sl], wl.R,
-                                                    p["n"], p["m"], Ys=p["Ys"][sl])
+        for tab in tables:
+            sbn.sbn_sparse_ternary_gemv_table(Xq, s_x, tab)
 
     return step, total, per_launch, wl
 
@@ -665,32 +679,30 @@ def make_decode_step(T=1):
 def make_decode_step_d2(T=1):
     """The decode step on decode planes: the same two pools (2:4 and 6:8 weights,
     POOL each) repacked once, outside the timed region, into the dense 2-bit
-    decode plane (4.19 MB per weight for both ratios), as batched calls of
-    BATCH planes.  Returns (step, bytes per step, bytes per launch)."""
+    decode plane (4.19 MB per weight for both ratios), one table GEMV per
+    pool.  Returns (step, bytes per step, bytes per launch)."""
     import torch
     import sparse_linear_layers_02_amd as sbn
     from workloads import WORKLOADS
     wl = WORKLOADS["decode"]
     W = bf16_dev(wl.weights(0))
     Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0, T=T)))
-    pools, total = [], 0
+    tables, total = [], 0
     per = wl.R * wl.K // 4 + T * wl.K + 4 * T + 2 * T * wl.R + 4
     for n, m in wl.nm:
         codes0, meta0, s_w0 = sbn.sbn_mask_ternarize_pack(W, n, m)
         d20 = sbn.sbn_repack_d2(codes0, meta0, wl.R, wl.K, n, m)
-        pools.append(dict(d2s=[d20.clone() for _ in range(POOL)], s_ws=[s_w0.clone() for _ in range(POOL)],
-                          Ys=[torch.empty((T, wl.R), dtype=torch.bfloat16, device="cuda") for _ in range(POOL)]))
+        tables.append(sbn.GemvTable.planes([d20.clone() for _ in range(POOL)], [s_w0.clone() for _ in range(POOL)],
+                                           wl.R, wl.K, T=T))
         total += POOL * per
         del codes0, meta0, d20
     del W
 
     def step():
-        for p in pools:
-            for b0 in range(0, POOL, BATCH):
-                sl = slice(b0, b0 + BATCH)
-                sbn.sbn_ternary_gemv_d2_batched(Xq, s_x, p["d2s"][sl], p["s_ws"][sl], wl.R, Ys=p["Ys"][sl])
+        for tab in tables:
+            sbn.sbn_ternary_gemv_d2_table(Xq, s_x, tab)
 
-    return step, total, BATCH * per
+    return step, total, POOL * per
 
 
 def measure_decode_step(a, with_d2=True):
@@ -704,8 +716,8 @@ def measure_decode_step(a, with_d2=True):
     out = {"GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms, 4), "wall_s": round(wall, 4),
            "launch": mode, "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
            "config": {"workload": "decode", "T": 1, "R": wl.R, "K": wl.K, "nm": "2:4+6:8",
-                      "pool_weights_per_ratio": POOL, "weights_per_launch": BATCH,
-                      "step": "batched decode GEMV over both pools", "y_dtype": "bf16", "seed": 0}}
+                      "pool_weights_per_ratio": POOL, "weights_per_launch": POOL,
+                      "step": "one table decode GEMV per pool (both pools)", "y_dtype": "bf16", "seed": 0}}
     for key, kname in (("roofline", "gemv_stream_24"), ("roofline_68", "gemv_stream_68")):
         k_ms, k_cnt = kernel_avg_ms(profile_pass(step, a.steps, kname), kname)
         ach = per_launch[kname] / (k_ms * 1e-3) / 1e9

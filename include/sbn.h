@@ -322,6 +322,51 @@ sbn_status sbn_sparse_ternary_gemv_batched(const int8_t* Xq, const float* s_x, i
                                            void* stream);
 
 /*
+ * One weight of a decode GEMV table: the device pointers of sbn_sparse_ternary_
+ * gemv's per-weight arguments (for a decode plane: codes = the plane, meta
+ * unused).  Four pointers, 32 bytes, 8-byte aligned.
+ */
+typedef struct sbn_gemv_entry {
+  const uint8_t* codes;
+  const uint8_t* meta;
+  const float* s_w;
+  void* Y;
+} sbn_gemv_entry;
+
+/*
+ * sbn_sparse_ternary_gemv over `count` weights sharing the activations, with
+ * the weights listed in a table in DEVICE memory, in one launch whatever the
+ * count (decode over a whole pool of weights: the launch's start-up and drain
+ * are paid once, and the caller builds the table once and reuses it across
+ * steps and graph replays):
+ *   Y_b = that call's result for (Xq, s_x, table[b].codes, table[b].meta,
+ *         table[b].s_w), written to table[b].Y, for b < count.
+ * Every weight is R x K at ratio n:m; every Y_b is [T x R] of dtype ydt with
+ * row stride ldy.  Covered shapes: 1 <= T <= 16, K a multiple of 1024 up to
+ * 4096, n:m 2:4 or 6:8; others return SBN_ERR_SHAPE / SBN_ERR_UNSUPPORTED_NM
+ * (use the batched call).  count * ceil(R / 16) <= 2^40.
+ * The table and every pointer in it are read by the kernel, not by the host:
+ * they must stay valid and unchanged until the launch completes, and the
+ * library cannot check them.  sbn_gemv_table_check checks a host copy of a
+ * table (each entry as sbn_sparse_ternary_gemv checks its arguments); an
+ * entry that would fail it gives undefined results (a misaligned or dangling
+ * pointer can fault the device).  Only `table` itself is checked here
+ * (non-NULL, 16-byte aligned).
+ */
+sbn_status sbn_sparse_ternary_gemv_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                         const sbn_gemv_entry* table, int64_t count, int64_t R, int n, int m,
+                                         sbn_dtype ydt, int64_t ldy, void* stream);
+
+/*
+ * Host-only check of a GEMV table before it is copied to the device: every
+ * entry of the HOST array `table` (count entries) against the arguments of a
+ * later sbn_sparse_ternary_gemv_table call (d2 = 0) or sbn_ternary_gemv_d2_table
+ * call (d2 = 1; n, m ignored).  Returns the first failure, naming the entry.
+ */
+sbn_status sbn_gemv_table_check(const sbn_gemv_entry* table, int64_t count, int64_t T, int64_t K, int64_t R,
+                                int n, int m, int d2, sbn_dtype ydt, int64_t ldy);
+
+/*
  * Decode plane: a byte-lean form of a packed weight for memory-bound decode
  * (not a format of the pages; at 6:8 the packed planes hold 2.5 bits per
  * weight, the decode plane 2).  It holds the effective ternary weights (pruned
@@ -349,6 +394,16 @@ sbn_status sbn_ternary_gemv_d2(const int8_t* Xq, const float* s_x, int64_t T, in
 sbn_status sbn_ternary_gemv_d2_batched(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                                        const uint8_t* const* d2, const float* const* s_w, int64_t R,
                                        void* const* Y, sbn_dtype ydt, int64_t ldy, int64_t count, void* stream);
+/*
+ * sbn_ternary_gemv_d2_table: sbn_ternary_gemv_d2 over a DEVICE table of
+ * `count` planes (table[b].codes = plane b; meta unused) sharing the
+ * activations, one launch, as sbn_sparse_ternary_gemv_table (K a multiple of
+ * 1024 up to 4096, 1 <= T <= 16, count * ceil(R / 16) <= 2^40; the entries
+ * are the caller's to keep valid and are not checked here).
+ */
+sbn_status sbn_ternary_gemv_d2_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                     const sbn_gemv_entry* table, int64_t count, int64_t R, sbn_dtype ydt,
+                                     int64_t ldy, void* stream);
 
 /*
  * Dual-STE backward of Sparse-BitLinear (ja §2.1, de §2 "Dual STE",

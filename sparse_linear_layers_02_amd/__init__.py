@@ -75,6 +75,9 @@ _SIGNATURES = {
     "sbn_sparse_ternary_gemv_batched": ([_vp, _vp, _i64, _i64, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                          ctypes.POINTER(_vp), _i64, _int, _int, ctypes.POINTER(_vp), _int,
                                          _i64, _i64, _vp], _int),
+    "sbn_sparse_ternary_gemv_table": ([_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _int, _int, _i64, _vp], _int),
+    "sbn_ternary_gemv_d2_table": ([_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _i64, _vp], _int),
+    "sbn_gemv_table_check": ([_vp, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _i64], _int),
     "sbn_backward": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _int, _int, _vp, _int, _vp, _vp,
                       _sz, _vp], _int),
     "sbn_backward_ex": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _int, _int, _vp, _int, _vp, _u32, _vp,
@@ -455,6 +458,91 @@ def sbn_sparse_ternary_gemv_batched(Xq, s_x, codes, metas, s_ws, R: int, n: int,
     return Ys
 
 
+class GemvTable:
+    """The weights of a table GEMV: per weight the device pointers of its
+    packed planes (or decode plane), scale and output, in a table in device
+    memory (sbn_gemv_entry: four pointers), built once and reused by every
+    sbn_sparse_ternary_gemv_table / sbn_ternary_gemv_d2_table call.  The
+    entries are checked on the host (sbn_gemv_table_check) before the copy;
+    the object holds a reference to every tensor the table points at, so they
+    stay alive as long as it does.  Ys: the outputs ([T, R] each, allocated
+    with the row stride rounded up to 8 when not given)."""
+
+    def __init__(self, codes, metas, s_ws, R: int, K: int, n: int, m: int, *, T: int = 1, ydt: int = SBN_BF16,
+                 Ys=None, d2: bool = False):
+        torch = _torch()
+        fn = "sbn_ternary_gemv_d2_table" if d2 else "sbn_sparse_ternary_gemv_table"
+        count = len(codes)
+        if count < 1:
+            raise SbnError(fn, 2, "a table needs at least one weight")
+        for b in range(count):
+            _req(codes[b], "d2" if d2 else "codes", "u8", True, fn)
+            _req(None if d2 or metas is None else metas[b], "meta", "u8", True, fn)
+            _req(s_ws[b], "s_w", "f32", True, fn)
+            if Ys is not None:
+                if ydt in _YD:
+                    _req(Ys[b], "Y", _YD[ydt], False, fn)
+                if tuple(Ys[b].shape) != (T, R) or Ys[b].stride(0) != Ys[0].stride(0):
+                    raise SbnError(fn, 2, f"every Y must be [{T}, {R}] with one row stride")
+        dev = codes[0].device
+        if Ys is None:
+            ld = (R + 7) // 8 * 8
+            Ys = [torch.empty((T, ld), dtype=getattr(torch, _YT[ydt]), device=dev)[:, :R] for _ in range(count)]
+        ldy = Ys[0].stride(0)
+        ptr = lambda t: 0 if t is None else t.data_ptr()
+        host = (_vp * (4 * count))()
+        for b in range(count):
+            mt = None if d2 or metas is None else metas[b]
+            host[4 * b: 4 * b + 4] = [ptr(codes[b]), ptr(mt), ptr(s_ws[b]), ptr(Ys[b])]
+        _check("sbn_gemv_table_check", lib().sbn_gemv_table_check(host, count, T, K, R, n, m, int(d2), ydt, ldy))
+        flat = torch.tensor([0 if v is None else v for v in host], dtype=torch.int64)
+        self.dev = flat.to(dev)                      # count x 4 pointers; 16-byte aligned (allocator)
+        self.codes, self.metas, self.s_ws, self.Ys = list(codes), None if metas is None else list(metas), list(s_ws), Ys
+        self.R, self.K, self.n, self.m, self.T, self.ydt, self.ldy = R, K, n, m, T, ydt, ldy
+        self.count, self.d2 = count, bool(d2)
+
+    @classmethod
+    def planes(cls, d2s, s_ws, R: int, K: int, *, T: int = 1, ydt: int = SBN_BF16, Ys=None):
+        """A table of decode planes (sbn_repack_d2 outputs)."""
+        return cls(d2s, None, s_ws, R, K, 0, 0, T=T, ydt=ydt, Ys=Ys, d2=True)
+
+
+def _table_call(fn, Xq, s_x, table):
+    T, K = Xq.shape
+    _req(Xq, "Xq", "i8", True, fn)
+    _req(s_x, "s_x", "f32", True, fn)
+    if not isinstance(table, GemvTable):
+        raise SbnError(fn, 2, "table must be a GemvTable")
+    if (T, K) != (table.T, table.K) or Xq.device != table.dev.device:
+        raise SbnError(fn, 2, f"Xq [{T}, {K}] on {Xq.device} does not match the table's T = {table.T}, "
+                              f"K = {table.K} on {table.dev.device}")
+    return T, K
+
+
+def sbn_sparse_ternary_gemv_table(Xq, s_x, table, *, stream=None):
+    """Decode GEMV of every weight of `table` (a GemvTable of packed weights)
+    against Xq, one launch.  Returns the table's list of Y."""
+    fn = "sbn_sparse_ternary_gemv_table"
+    T, K = _table_call(fn, Xq, s_x, table)
+    if table.d2:
+        raise SbnError(fn, 2, "the table holds decode planes: use sbn_ternary_gemv_d2_table")
+    _check(fn, lib().sbn_sparse_ternary_gemv_table(_ptr(Xq), _ptr(s_x), T, K, table.dev.data_ptr(), table.count,
+                                                   table.R, table.n, table.m, table.ydt, table.ldy, _stream(stream)))
+    return table.Ys
+
+
+def sbn_ternary_gemv_d2_table(Xq, s_x, table, *, stream=None):
+    """Decode GEMV of every plane of `table` (GemvTable.planes) against Xq,
+    one launch.  Returns the table's list of Y."""
+    fn = "sbn_ternary_gemv_d2_table"
+    T, K = _table_call(fn, Xq, s_x, table)
+    if not table.d2:
+        raise SbnError(fn, 2, "the table holds packed weights: use sbn_sparse_ternary_gemv_table")
+    _check(fn, lib().sbn_ternary_gemv_d2_table(_ptr(Xq), _ptr(s_x), T, K, table.dev.data_ptr(), table.count, table.R,
+                                               table.ydt, table.ldy, _stream(stream)))
+    return table.Ys
+
+
 def _backward(name, flags, dY, Xq, s_x, codes, meta, s_w, n, m, dxdt, want_dX, want_dW, dX, dW, ws, stream):
     torch = _torch()
     T, R = dY.shape
@@ -524,6 +612,7 @@ __all__ = [
     "sbn_mask_ternarize_pack", "sbn_mask_ternarize_pack_noalloc", "sbn_act_quant", "sbn_sparse_ternary_gemm", "sbn_sparse_ternary_gemv",
     "sbn_backward", "sbn_backward_ex", "sbn_mask_ternarize_pack_ex", "sbn_sgd_update_pack", "sbn_forward",
     "sbn_decode_plane_bytes", "sbn_repack_d2", "sbn_ternary_gemv_d2", "sbn_ternary_gemv_d2_batched",
+    "GemvTable", "sbn_sparse_ternary_gemv_table", "sbn_ternary_gemv_d2_table",
     "sbn_gemm_weight_bytes", "sbn_prepare_gemm_weight", "sbn_sparse_ternary_gemm_prepared", "SBN_OP_GEMM_PREPARED",
     "SBN_ERR_VALUE",
     "SBN_FLAGS_NONE", "SBN_MASK_FROM_TERNARY", "SBN_GRAD_W_MASKED",

@@ -735,6 +735,83 @@ sbn_status sbn_ternary_gemv_d2_batched(const int8_t* Xq, const float* s_x, int64
   return hip_result(launch_gemv_d2_batched(Xq, s_x, T, K, d2, s_w, R, Y, ydt, ldy, (int)count, st), st, fn);
 }
 
+// The arguments of a table GEMV call that the host can see (the entries live
+// in device memory): activations, shapes, output layout, the table pointer
+// and the count.
+static sbn_status check_table_call(const char* fn, const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                   const sbn_gemv_entry* table, int64_t count, int64_t R, sbn_dtype ydt,
+                                   int64_t ldy) {
+  SBN_NONNULL(Xq);
+  SBN_NONNULL(s_x);
+  SBN_NONNULL(table);
+  SBN_TRY(check_rows("T", T));
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
+  if (T > 16) return fail(SBN_ERR_SHAPE, "%s: T = %lld exceeds 16; use the GEMM", fn, (long long)T);
+  SBN_TRY(check_ld("ldy", ldy, R, T));
+  if (ydt != SBN_F32 && ydt != SBN_BF16 && ydt != SBN_I32_ACC)
+    return fail(SBN_ERR_DTYPE, "%s: unknown output dtype %d", fn, (int)ydt);
+  if (count < 1) return fail(SBN_ERR_SHAPE, "%s: count = %lld must be at least 1", fn, (long long)count);
+  if (!prod_below(count, (R + 15) / 16, (int64_t)1 << 40))
+    return fail(SBN_ERR_SHAPE, "%s: count * ceil(R / 16) reaches 2^40", fn);
+  SBN_ALIGNED(Xq);
+  SBN_ALIGNED(table);
+  return SBN_OK;
+}
+
+sbn_status sbn_sparse_ternary_gemv_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                         const sbn_gemv_entry* table, int64_t count, int64_t R, int n, int m,
+                                         sbn_dtype ydt, int64_t ldy, void* stream) {
+  const char* fn = "sbn_sparse_ternary_gemv_table";
+  SBN_TRY(check_nm(n, m));
+  SBN_TRY(check_table_call(fn, Xq, s_x, T, K, table, count, R, ydt, ldy));
+  if (!((n == 2 && m == 4) || (n == 6 && m == 8)))
+    return fail(SBN_ERR_UNSUPPORTED_NM, "%s: %d:%d has no table GEMV (2:4 and 6:8 only); use the batched call", fn,
+                n, m);
+  if (!gemv_table_shape_ok(K, n, m))
+    return fail(SBN_ERR_SHAPE, "%s: K = %lld must be a multiple of 1024 up to 4096; use the batched call", fn,
+                (long long)K);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_gemv_table(Xq, s_x, T, K, table, count, R, n, m, ydt, ldy, st), st, fn);
+}
+
+sbn_status sbn_ternary_gemv_d2_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                     const sbn_gemv_entry* table, int64_t count, int64_t R, sbn_dtype ydt,
+                                     int64_t ldy, void* stream) {
+  const char* fn = "sbn_ternary_gemv_d2_table";
+  SBN_TRY(check_table_call(fn, Xq, s_x, T, K, table, count, R, ydt, ldy));
+  if (!gemv_d2_table_shape_ok(K))
+    return fail(SBN_ERR_SHAPE, "%s: K = %lld must be a multiple of 1024 up to 4096; use the batched call", fn,
+                (long long)K);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_gemv_d2_table(Xq, s_x, T, K, table, count, R, ydt, ldy, st), st, fn);
+}
+
+sbn_status sbn_gemv_table_check(const sbn_gemv_entry* table, int64_t count, int64_t T, int64_t K, int64_t R,
+                                int n, int m, int d2, sbn_dtype ydt, int64_t ldy) {
+  const char* fn = "sbn_gemv_table_check";
+  SBN_NONNULL(table);
+  if (count < 1) return fail(SBN_ERR_SHAPE, "%s: count = %lld must be at least 1", fn, (long long)count);
+  // the activations are not part of the table: stand-ins that pass their checks
+  alignas(16) static const int8_t xq_ok[16] = {};
+  static const float sx_ok = 1.0f;
+  for (int64_t b = 0; b < count; ++b) {
+    const sbn_gemv_entry& e = table[b];
+    const sbn_status st_b =
+        d2 ? check_d2_args(fn, xq_ok, &sx_ok, T, K, e.codes, e.s_w, R, e.Y, ydt, ldy)
+           : check_matmul_args(fn, xq_ok, &sx_ok, T, K, e.codes, n < m ? e.meta : nullptr, e.s_w, R, n, m, e.Y, ydt,
+                               ldy);
+    if (st_b != SBN_OK) {
+      char msg[512];
+      snprintf(msg, sizeof(msg), "%s (entry %lld)", sbn_last_error(), (long long)b);
+      return fail(st_b, "%s", msg);
+    }
+  }
+  if (T > 16) return fail(SBN_ERR_SHAPE, "%s: T = %lld exceeds 16", fn, (long long)T);
+  return SBN_OK;
+}
+
 sbn_status sbn_backward_ex(const uint16_t* dY, int64_t T, int64_t R, const int8_t* Xq,
                            const float* s_x, int64_t K, const uint8_t* codes, const uint8_t* meta,
                            const float* s_w, int n, int m, void* dX, sbn_dtype dxdt, float* dW,

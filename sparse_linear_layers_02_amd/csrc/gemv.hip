@@ -201,22 +201,91 @@ constexpr int GV_RING = SBN_GV_RING;
 #define SBN_GV_STREAM 1
 #endif
 
-// The weights of one streamed launch (kernel argument, by value).
+// The weights of one streamed launch: either up to GV_MAX_BATCH entries by
+// value in the kernel argument, or a table of any length in device memory
+// that the caller fills once and reuses.  Both index as P.e[w]; the kernel
+// reads an entry with wave-uniform (scalar) loads.
+static_assert(sizeof(GvEntry) == 32 && alignof(GvEntry) == 8, "GvEntry: four device pointers");
 struct GemvBatch {
-  const uint8_t* codes[GV_MAX_BATCH];
-  const uint8_t* meta[GV_MAX_BATCH];
-  const float* s_w[GV_MAX_BATCH];
-  void* Y[GV_MAX_BATCH];
+  GvEntry e[GV_MAX_BATCH];
 };
+struct GemvTable {
+  const GvEntry* e;
+};
+// Entry w and a weight's scale, read through the constant address space: the
+// table and the scales stay unchanged while the kernel runs, so the loads are
+// scalar (the scalar cache; no wait on the ring's vector loads).
+typedef const __attribute__((address_space(4))) uint64_t* U64C;
+typedef const __attribute__((address_space(4))) float* FloatC;
+__device__ inline GvEntry gv_entry(const GemvBatch& P, int64_t w) { return P.e[w]; }
+__device__ inline GvEntry gv_entry(const GemvTable& P, int64_t w) {
+  const U64C q = (U64C)(P.e + w);
+  return GvEntry{(const uint8_t*)q[0], (const uint8_t*)q[1], (const float*)q[2], (void*)q[3]};
+}
+__device__ inline float gv_scale(const float* s_w) { return *(FloatC)s_w; }
+
+// Sum of the four 16-byte words at p, p + 1 KB, p + 2 KB and p + 3 KB of LDS,
+// read in one asm block that also waits for them.  Through the compiler's own
+// LDS reads, each sum waited for every direct global->LDS load in flight
+// (the compiler cannot tell the ring's loads from these reads), which drained
+// the ring once per row group.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ inline v4i lds_sum4_1k(const int* p) {
+  const uint32_t a = lds_addr(p);
+  v4i x0, x1, x2, x3;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+      : "v"(a)
+      : "memory");
+  return x0 + x1 + x2 + x3;
+}
+
+// A ring slot's words into registers, the same way: four or five 16-byte
+// reads at the given LDS addresses, waited for in the block, so the slot can
+// be refilled right after.
+__device__ inline void lds_read4(v4i& x0, v4i& x1, v4i& x2, v4i& x3, uint32_t a0, uint32_t a1, uint32_t a2,
+                                 uint32_t a3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+__device__ inline void lds_read5(v4i& x0, v4i& x1, v4i& x2, v4i& x3, v4i& x4, uint32_t a0, uint32_t a1,
+                                 uint32_t a2, uint32_t a3, uint32_t a4) {
+  asm volatile(
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %6\n\t"
+      "ds_read_b128 %2, %7\n\t"
+      "ds_read_b128 %3, %8\n\t"
+      "ds_read_b128 %4, %9\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(a4)
+      : "memory");
+}
 
 // Output side.  Row groups 4k .. 4k + 3 of a weight (64 rows) form one output
 // group.  Per row group the four waves' 16 x 16 partial sums go through red
 // (one of two buffers, alternating per row group, so one barrier per row group
-// suffices).  Lane (t = tid / 16, r = tid % 16) owns rows 4r .. 4r + 3 of its
-// output group for token t: it sums them (16 contiguous bytes of each wave's
-// partials) after row group r / 4 of the group and keeps them in registers;
-// once the group is complete they are stored together, so each token's 64
-// outputs leave as one contiguous 128- or 256-byte run.
+// suffices).  Thread (r = tid / 16, t = tid % 16) owns rows 4r .. 4r + 3 of
+// its output group for token t: it sums them (16 contiguous bytes of each
+// wave's partials) after row group r / 4 of the group and keeps them in
+// registers; once the group is complete they are stored together.  Row group
+// j of a group is summed by wave j (threads 64j .. 64j + 63), so the four
+// waves share the summing whatever the number of tokens, and each wave stores
+// one 32- or 64-byte run (16 rows) per token.
 template <int OUT>
 struct StreamOut {
   v4i v;                                               // this lane's four outputs (bf16: v[0..1] packed)
@@ -231,11 +300,11 @@ struct StreamOut {
                                    int64_t grp_row0, int64_t T, float swv, float sxv, void* Y) {
     *(v4i*)&red[wave][lane * 4] = acc;
     lds_barrier();
-    const int t = tid >> 4, r = tid & 15;
+    const int r = tid >> 4, t = tid & 15;
     if ((r >> 2) == j && t < T) {
       // rows 4 (r % 4) .. +3 of this row group: entries 64 (r % 4) + 4 t + 0..3 of every wave's partials
       const int e = 64 * (r & 3) + 4 * t;
-      const v4i a = *(const v4i*)&red[0][e] + *(const v4i*)&red[1][e] + *(const v4i*)&red[2][e] + *(const v4i*)&red[3][e];
+      const v4i a = lds_sum4_1k(&red[0][e]);
       const v4i sum = a >> 6;                          // exact: every partial is a multiple of 64
       if (OUT == 0) {
         v = sum;
@@ -257,23 +326,30 @@ struct StreamOut {
       pY = Y;
     }
   }
+  // Y through global-space pointers: a generic (flat) store would have to
+  // wait for the ring's in-flight loads into LDS, which it might alias.
+  typedef __attribute__((address_space(1))) uint16_t* GU16;
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(1))) v2u* GU2;
+  typedef __attribute__((address_space(1))) int* GI32;
+  typedef __attribute__((address_space(1))) v4i* GV4;
   __device__ inline void commit(int tid, int64_t R, int64_t ldy) {
     if (prow < 0) return;
-    const int64_t row = prow, t = tid >> 4;
+    const int64_t row = prow, t = tid & 15;
     prow = -1;
     if (OUT == 2) {
-      uint16_t* y = (uint16_t*)pY + t * ldy + row;
+      const GU16 y = (GU16)pY + t * ldy + row;
       if (row + 4 <= R) {
-        *(uint2*)y = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+        *(GU2)y = (v2u){(uint32_t)v[0], (uint32_t)v[1]};
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (row + q < R) y[q] = (uint16_t)((uint32_t)v[q >> 1] >> (16 * (q & 1)));
       }
     } else {
-      int* y = (int*)pY + t * ldy + row;
+      const GI32 y = (GI32)pY + t * ldy + row;
       if (row + 4 <= R) {
-        *(v4i*)y = v;
+        *(GV4)y = v;
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -327,11 +403,19 @@ struct Dec24 {
     for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(blo[s]), "v"(bhi[s]));
   }
   __device__ inline void build_lut(uint8_t*, int) {}
-  __device__ inline v4i compute(const uint8_t* slot, const uint8_t*, int rl, int g) {
-    const uint8_t* sl = slot + rl * 128;
-    const int c0 = (2 * g) ^ (rl & 7), c1 = (2 * g + 1) ^ (rl & 7);
-    const v4i m0 = *(const v4i*)(sl + 16 * c0), m1 = *(const v4i*)(sl + 16 * c1);
-    const v4i k0 = *(const v4i*)(sl + 2048 + 16 * c0), k1 = *(const v4i*)(sl + 2048 + 16 * c1);
+  struct Frag {
+    v4i m0, m1, k0, k1;
+  };
+  // this lane's words of the slot (row rl, lane group g) into registers
+  __device__ inline Frag read(const uint8_t* slot, int rl, int g) const {
+    const uint32_t sl = lds_addr(slot + rl * 128);
+    const uint32_t c0 = 16 * ((2 * g) ^ (rl & 7)), c1 = 16 * ((2 * g + 1) ^ (rl & 7));
+    Frag f;
+    lds_read4(f.m0, f.m1, f.k0, f.k1, sl + c0, sl + c1, sl + 2048 + c0, sl + 2048 + c1);
+    return f;
+  }
+  __device__ inline v4i compute(const Frag& f, const uint8_t*) const {
+    const v4i m0 = f.m0, m1 = f.m1, k0 = f.k0, k1 = f.k1;
     const uint32_t mw[8] = {(uint32_t)m0[0], (uint32_t)m0[1], (uint32_t)m0[2], (uint32_t)m0[3],
                             (uint32_t)m1[0], (uint32_t)m1[1], (uint32_t)m1[2], (uint32_t)m1[3]};
     const uint32_t cw[8] = {(uint32_t)k0[0], (uint32_t)k0[1], (uint32_t)k0[2], (uint32_t)k0[3],
@@ -363,16 +447,19 @@ struct Dec24 {
 // with a selector taken from a 256-entry table indexed by the group's meta
 // byte (0x0C selects a zero byte at a pruned position).
 __device__ inline v4i lut68_entry(uint32_t mb) {
-  // survivor rank -> byte of the permute window, per output word
-  constexpr uint32_t M0[6] = {0, 1, 4, 5, 2, 3};            // words 0, 1: window (lo A, hi B)
-  constexpr uint32_t M2[6] = {2, 3, 4, 5, 12, 12};          // word 2: window (lo B, hi C)
-  constexpr uint32_t M3[6] = {12, 12, 0, 1, 4, 5};          // word 3: window (lo C, hi D)
+  // survivor rank -> byte of the permute window, per output word, one nibble
+  // per rank (rank 0 lowest), so no table in memory is indexed:
+  //   words 0, 1: window (lo A, hi B): 0 1 4 5 2 3
+  //   word 2:     window (lo B, hi C): 2 3 4 5 12 12
+  //   word 3:     window (lo C, hi D): 12 12 0 1 4 5
+  constexpr uint32_t M0 = 0x325410u, M2 = 0xCC5432u, M3 = 0x5410CCu;
   uint32_t w[4] = {0, 0, 0, 0};
   uint32_t r = 0;
+#pragma unroll
   for (int p = 0; p < 8; ++p) {
     const bool on = (mb >> p) & 1u;
     const uint32_t rr = r < 6 ? r : 5;
-    const uint32_t a = on ? M0[rr] : 12u, b = on ? (p < 4 ? M2[rr] : M3[rr]) : 12u;
+    const uint32_t a = on ? (M0 >> (4 * rr)) & 15u : 12u, b = on ? ((p < 4 ? M2 : M3) >> (4 * rr)) & 15u : 12u;
     w[p >> 2] |= a << (8 * (p & 3));
     w[2 + (p >> 2)] |= b << (8 * (p & 3));
     r += on ? 1u : 0u;
@@ -418,16 +505,30 @@ struct Dec68 {
     for (int s = 0; s < 16; ++s) asm volatile("" ::"v"(bx[s]));
   }
   __device__ inline void build_lut(uint8_t* lut, int tid) { *(v4i*)(lut + 16 * tid) = lut68_entry((uint32_t)tid); }
-  __device__ inline v4i compute(const uint8_t* slot, const uint8_t* lut, int rl, int g) {
-    const uint8_t* sm = slot + rl * 128;
-    const uint8_t* sc = slot + 2048 + rl * 192;
+  struct Frag {
+    v4i m0, m1, c[3];
+  };
+  __device__ inline Frag read(const uint8_t* slot, int rl, int g) const {
+    const uint32_t sm = lds_addr(slot + rl * 128);
+    const uint32_t sc = lds_addr(slot + 2048 + rl * 192);
     const int r7 = rl & 7;
-    const v4i m0 = *(const v4i*)(sm + 16 * ((2 * g) ^ r7)), m1 = *(const v4i*)(sm + 16 * ((2 * g + 1) ^ r7));
-    uint32_t cw[12];
+    uint32_t ac[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int c = 3 * g + i + r7;
-      const v4i v = *(const v4i*)(sc + 16 * (c < 12 ? c : c - 12));
+      ac[i] = sc + 16 * (c < 12 ? c : c - 12);
+    }
+    Frag f;
+    lds_read5(f.m0, f.m1, f.c[0], f.c[1], f.c[2], sm + 16 * ((2 * g) ^ r7), sm + 16 * ((2 * g + 1) ^ r7), ac[0],
+              ac[1], ac[2]);
+    return f;
+  }
+  __device__ inline v4i compute(const Frag& f, const uint8_t* lut) const {
+    const v4i m0 = f.m0, m1 = f.m1;
+    uint32_t cw[12];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const v4i v = f.c[i];
       cw[4 * i] = (uint32_t)v[0]; cw[4 * i + 1] = (uint32_t)v[1]; cw[4 * i + 2] = (uint32_t)v[2]; cw[4 * i + 3] = (uint32_t)v[3];
     }
     const uint32_t mw[8] = {(uint32_t)m0[0], (uint32_t)m0[1], (uint32_t)m0[2], (uint32_t)m0[3],
@@ -496,12 +597,21 @@ struct Dec2 {
     for (int s = 0; s < 16; ++s) asm volatile("" ::"v"(bx[s]));
   }
   __device__ inline void build_lut(uint8_t*, int) {}
-  __device__ inline v4i compute(const uint8_t* slot, const uint8_t*, int rl, int g) {
-    const uint8_t* sr = slot + rl * 256;
+  struct Frag {
+    v4i w[4];
+  };
+  __device__ inline Frag read(const uint8_t* slot, int rl, int g) const {
+    const uint32_t sr = lds_addr(slot + rl * 256);
+    Frag f;
+    lds_read4(f.w[0], f.w[1], f.w[2], f.w[3], sr + 16 * ((4 * g) ^ rl), sr + 16 * ((4 * g + 1) ^ rl),
+              sr + 16 * ((4 * g + 2) ^ rl), sr + 16 * ((4 * g + 3) ^ rl));
+    return f;
+  }
+  __device__ inline v4i compute(const Frag& f, const uint8_t*) const {
     uint32_t w[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const v4i v = *(const v4i*)(sr + 16 * ((4 * g + i) ^ rl));
+      const v4i v = f.w[i];
       w[4 * i] = (uint32_t)v[0]; w[4 * i + 1] = (uint32_t)v[1]; w[4 * i + 2] = (uint32_t)v[2]; w[4 * i + 3] = (uint32_t)v[3];
     }
     constexpr uint32_t MK = 0xC0C0C0C0u;
@@ -515,43 +625,75 @@ struct Dec2 {
   }
 };
 
+// The row groups one block walks, in order: chunks of `chunk` consecutive
+// global row groups q = w * nrg + lr (over the count * nrg of the launch),
+// chunk b, b + G, b + 2G, ... for block b of G.  Small chunks keep the blocks
+// of the chip reading neighbouring addresses at any moment.
+struct RgWalk {
+  int64_t kc, q, qend, w, lr;
+  __device__ inline void seek(int64_t c, int64_t chunk, int64_t total, int64_t nrg) {
+    kc = c;
+    q = c * chunk;
+    qend = q + chunk < total ? q + chunk : total;
+    w = q / nrg;
+    lr = q - w * nrg;
+  }
+  __device__ inline bool last_in_chunk() const { return q + 1 == qend; }
+  __device__ inline void next(int64_t G, int64_t chunk, int64_t total, int64_t nrg) {
+    if (++q == qend) {
+      seek(kc + G, chunk, total, nrg);
+    } else if (++lr == nrg) {
+      lr = 0;
+      ++w;
+    }
+  }
+};
+
 // One launch over `count` weights of R rows each: global row group q = w * nrg + lr.
-template <int OUT, typename Dec>
+template <int OUT, typename Dec, typename Tab>
 __global__ __launch_bounds__(256, Dec::BPC) void gemv_stream_kernel(
-    const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K, const GemvBatch P,
-    int count, int64_t R, int64_t ldy) {
-  // one LDS array: [4 waves][GV_RING][SLOT] ring, the decode table, red[2][4][256]
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * GV_RING * Dec::SLOT + Dec::LUT + 2 * 4 * 256 * 4];
-  uint8_t* lut = lds + 4 * GV_RING * Dec::SLOT;
-  int (*red)[4][256] = (int (*)[4][256])(lut + Dec::LUT);
+    const int8_t* __restrict__ Xq, const float* __restrict__ s_x, int64_t T, int64_t K, const Tab P,
+    int64_t count, int64_t R, int64_t ldy, int64_t chunk) {
+  // LDS: the [4 waves][GV_RING][SLOT] ring, the decode table and red[2][4][256]
+  // as three objects (the table's reads then do not wait for the ring's
+  // in-flight loads)
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * GV_RING * Dec::SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t lut[Dec::LUT > 0 ? Dec::LUT : 16];
+  __shared__ __attribute__((aligned(16))) int red[2][4][256];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, rl = lane & 15;
   const int64_t nrg = cdiv(R, 16);
   const int64_t rowm = Dec::meta_row(K), rowc = Dec::code_row(K);      // plane bytes per row
   const bool has = wave < K / 1024;                    // wave-uniform
-  const int64_t tq = tid >> 4;                         // token of the outputs this thread writes
+  const int64_t tq = tid & 15;                         // token of the outputs this thread writes
   const float sxv = OUT != 0 ? s_x[tq < T ? tq : 0] : 0.0f;
   uint8_t* myring = lds + wave * GV_RING * Dec::SLOT;
   Dec dec;
   dec.init(wave, lane);
 
-  // this block's row groups: [q0, q0 + nit) of the count * nrg, consecutive
-  const int64_t total = nrg * count;
-  const int64_t q0 = (int64_t)blockIdx.x * total / gridDim.x;
-  const int nit = (int)(((int64_t)blockIdx.x + 1) * total / gridDim.x - q0);
-  // position (weight, row group) of the next row group to load
-  int iw = (int)(q0 / nrg);
-  int64_t ilr = q0 - (int64_t)iw * nrg;
+  // this block's chunks and its number of row groups
+  const int64_t total = nrg * count, G = gridDim.x, b = blockIdx.x;
+  const int64_t nch = cdiv(total, chunk);
+  const int64_t mine = (nch - 1 - b) / G + 1;          // chunks b, b + G, ... below nch (b < nch)
+  const bool has_tail = (nch - 1 - b) % G == 0;        // the last, possibly short, chunk is this block's
+  const int nit = (int)(mine * chunk - (has_tail ? nch * chunk - total : 0));
+  RgWalk iss, cur;                                     // next row group to load / to compute
+  iss.seek(b, chunk, total, nrg);
+  cur.seek(b, chunk, total, nrg);
   auto issue_next = [&](int slot) {
-    const int valid = (int)(R - ilr * 16 < 16 ? R - ilr * 16 : 16);
-    const uint8_t* mp = rowm ? P.meta[iw] + ilr * 16 * rowm : nullptr;
-    dec.issue(myring + slot * Dec::SLOT, mp, P.codes[iw] + ilr * 16 * rowc, valid, K);
-    if (++ilr == nrg) { ilr = 0; ++iw; }
+    const int valid = (int)(R - iss.lr * 16 < 16 ? R - iss.lr * 16 : 16);
+    const GvEntry ew = gv_entry(P, iss.w);
+    const uint8_t* mp = rowm ? ew.meta + iss.lr * 16 * rowm : nullptr;
+    dec.issue(myring + slot * Dec::SLOT, mp, ew.codes + iss.lr * 16 * rowc, valid, K);
+    iss.next(G, chunk, total, nrg);
   };
+  // GV_RING row groups in flight from the start: a slot is refilled as soon
+  // as its words are in registers, so every slot is loading while the wave
+  // computes
   if (has) {
 #pragma unroll
-    for (int i = 0; i < GV_RING - 1; ++i)
+    for (int i = 0; i < GV_RING; ++i)
       if (i < nit) issue_next(i);
   }
   dec.build_lut(lut, tid);
@@ -560,33 +702,40 @@ __global__ __launch_bounds__(256, Dec::BPC) void gemv_stream_kernel(
   lds_barrier();                                       // decode table complete
 
   StreamOut<OUT> out;
-  int cw = (int)(q0 / nrg);                            // position of the row group being computed
-  int64_t clr = q0 - (int64_t)cw * nrg;
-  int j0 = (int)(clr & 3);
+  int j0 = (int)(cur.lr & 3);
   int slot = 0, par = 0;
   for (int it = 0; it < nit; ++it) {
     v4i acc = (v4i){0, 0, 0, 0};
     float swv = 0.0f;
-    if (OUT != 0) swv = *P.s_w[cw];
+    const GvEntry ec = gv_entry(P, cur.w);
+    if (OUT != 0) swv = gv_scale(ec.s_w);
     if (has) {
-      if (it + GV_RING - 1 < nit) issue_next((slot + GV_RING - 1) % GV_RING);
-      // this slot's loads are done once at most NDMA per later row group remain
+      // row groups it + 1 .. it + GV_RING - 1 (those that exist) were issued
+      // after this one: its loads are done once at most NDMA per later row
+      // group remain (the stores committed since sit between them and are
+      // waited for too)
       const int later = nit - 1 - it;
       if (later >= GV_RING - 1) wait_vmcnt<Dec::NDMA * (GV_RING - 1)>();
       else if (GV_RING > 3 && later == 2) wait_vmcnt<Dec::NDMA * 2>();
       else if (later == 1) wait_vmcnt<Dec::NDMA>();
       else wait_vmcnt<0>();
       out.commit(tid, R, ldy);
-      acc = dec.compute(myring + slot * Dec::SLOT, lut, rl, g);
+      // the slot's words into registers (waited for in the read), then refill it
+      const typename Dec::Frag f = dec.read(myring + slot * Dec::SLOT, rl, g);
+      if (it + GV_RING < nit) issue_next(slot);
+      acc = dec.compute(f, lut);
       slot = slot + 1 == GV_RING ? 0 : slot + 1;
     }
-    const int j = (int)(clr & 3);
+    // output group of four row groups: this block fills places j0 .. j of it
+    const int j = (int)(cur.lr & 3);
     if (j == 0) j0 = 0;
-    const bool done = j == 3 || clr == nrg - 1 || it == nit - 1;
-    out.row_group(red[par], acc, tid, wave, lane, j, j0, done, (clr & ~(int64_t)3) * 16, T, swv, sxv, P.Y[cw]);
+    const bool done = j == 3 || cur.lr == nrg - 1 || cur.last_in_chunk();
+    out.row_group(red[par], acc, tid, wave, lane, j, j0, done, (cur.lr & ~(int64_t)3) * 16, T, swv, sxv, ec.Y);
     par ^= 1;
     if (!has) out.commit(tid, R, ldy);
-    if (++clr == nrg) { clr = 0; ++cw; }
+    const bool new_chunk = cur.last_in_chunk();
+    cur.next(G, chunk, total, nrg);
+    if (new_chunk) j0 = (int)(cur.lr & 3);
   }
   out.commit(tid, R, ldy);
 }
@@ -756,18 +905,31 @@ hipError_t launch_gemv_nm(const int8_t* Xq, const float* s_x, int64_t T, int64_t
   return hipGetLastError();
 }
 
-template <typename Dec>
+// Row groups per chunk: up to 8 (128 rows), fewer when the launch has fewer
+// row groups than 8 per resident block, so that small launches still spread
+// over the chip (measured on the 128-weight decode pools: chunks of 8 beat one
+// contiguous run per block by 1-4%, 6:8 the most).
+int64_t stream_chunk(int64_t total, int64_t blocks) {
+#ifdef SBN_GV_CHUNK
+  if (SBN_GV_CHUNK > 0) return SBN_GV_CHUNK;
+#endif
+  const int64_t even = cdiv(total, blocks);
+  return even < 8 ? even : 8;
+}
+
+template <typename Dec, typename Tab>
 hipError_t launch_stream(const char* name, const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
-                         const GemvBatch& P, int count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
+                         const Tab& P, int64_t count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
   const int64_t total = cdiv(R, 16) * count;
   const int64_t blocks = 256 * Dec::BPC;   // one wave of resident blocks over the 256 CUs
-  const dim3 grid((unsigned)(total < blocks ? total : blocks)), block(256);
+  const int64_t chunk = stream_chunk(total, blocks), nch = cdiv(total, chunk);
+  const dim3 grid((unsigned)(nch < blocks ? nch : blocks)), block(256);
   if (ydt == SBN_I32_ACC)
-    SBN_LAUNCH(name, (gemv_stream_kernel<0, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
+    SBN_LAUNCH(name, (gemv_stream_kernel<0, Dec, Tab>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy, chunk);
   else if (ydt == SBN_F32)
-    SBN_LAUNCH(name, (gemv_stream_kernel<1, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
+    SBN_LAUNCH(name, (gemv_stream_kernel<1, Dec, Tab>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy, chunk);
   else
-    SBN_LAUNCH(name, (gemv_stream_kernel<2, Dec>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy);
+    SBN_LAUNCH(name, (gemv_stream_kernel<2, Dec, Tab>), grid, block, 0, st, Xq, s_x, T, K, P, count, R, ldy, chunk);
   return hipGetLastError();
 }
 
@@ -792,18 +954,8 @@ hipError_t launch_gemv_batched(const int8_t* Xq, const float* s_x, int64_t T, in
   const bool stream_ok = SBN_GV_STREAM && K % 1024 == 0 && K <= 4096 && ((n == 2 && m == 4) || (n == 6 && m == 8));
   if (stream_ok) {
     GemvBatch P;
-    for (int b = 0; b < count; ++b) {
-      P.codes[b] = codes[b];
-      P.meta[b] = meta[b];
-      P.s_w[b] = s_w[b];
-      P.Y[b] = Y[b];
-    }
-    for (int b = count; b < GV_MAX_BATCH; ++b) {
-      P.codes[b] = nullptr;
-      P.meta[b] = nullptr;
-      P.s_w[b] = nullptr;
-      P.Y[b] = nullptr;
-    }
+    for (int b = 0; b < GV_MAX_BATCH; ++b)
+      P.e[b] = b < count ? GvEntry{codes[b], meta[b], s_w[b], Y[b]} : GvEntry{nullptr, nullptr, nullptr, nullptr};
     if (n == 2) return launch_stream<Dec24>("gemv_stream_24", Xq, s_x, T, K, P, count, R, ydt, ldy, st);
     return launch_stream<Dec68>("gemv_stream_68", Xq, s_x, T, K, P, count, R, ydt, ldy, st);
   }
@@ -813,6 +965,18 @@ hipError_t launch_gemv_batched(const int8_t* Xq, const float* s_x, int64_t T, in
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+bool gemv_table_shape_ok(int64_t K, int n, int m) {
+  return SBN_GV_STREAM && K % 1024 == 0 && K <= 4096 && ((n == 2 && m == 4) || (n == 6 && m == 8));
+}
+
+hipError_t launch_gemv_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const GvEntry* table,
+                             int64_t count, int64_t R, int n, int m, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
+  if (!gemv_table_shape_ok(K, n, m)) return hipErrorInvalidValue;
+  const GemvTable P{table};
+  if (n == 2) return launch_stream<Dec24>("gemv_stream_24", Xq, s_x, T, K, P, count, R, ydt, ldy, st);
+  return launch_stream<Dec68>("gemv_stream_68", Xq, s_x, T, K, P, count, R, ydt, ldy, st);
 }
 
 hipError_t launch_gemv(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
@@ -900,17 +1064,21 @@ hipError_t launch_repack_d2(const uint8_t* codes, const uint8_t* meta, int64_t R
   return hipGetLastError();
 }
 
+bool gemv_d2_table_shape_ok(int64_t K) { return SBN_GV_STREAM && K % 1024 == 0 && K <= 4096; }
+
+hipError_t launch_gemv_d2_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const GvEntry* table,
+                                int64_t count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
+  if (!gemv_d2_table_shape_ok(K)) return hipErrorInvalidValue;
+  return launch_stream<Dec2>("gemv_stream_d2", Xq, s_x, T, K, GemvTable{table}, count, R, ydt, ldy, st);
+}
+
 hipError_t launch_gemv_d2_batched(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                                   const uint8_t* const* d2, const float* const* s_w, int64_t R, void* const* Y,
                                   sbn_dtype ydt, int64_t ldy, int count, hipStream_t st) {
   if (SBN_GV_STREAM && K % 1024 == 0 && K <= 4096) {
     GemvBatch P;
-    for (int b = 0; b < GV_MAX_BATCH; ++b) {
-      P.codes[b] = b < count ? d2[b] : nullptr;
-      P.meta[b] = nullptr;
-      P.s_w[b] = b < count ? s_w[b] : nullptr;
-      P.Y[b] = b < count ? Y[b] : nullptr;
-    }
+    for (int b = 0; b < GV_MAX_BATCH; ++b)
+      P.e[b] = b < count ? GvEntry{d2[b], nullptr, s_w[b], Y[b]} : GvEntry{nullptr, nullptr, nullptr, nullptr};
     return launch_stream<Dec2>("gemv_stream_d2", Xq, s_x, T, K, P, count, R, ydt, ldy, st);
   }
   const dim3 grid((unsigned)cdiv(R, 16)), block(256);

@@ -143,6 +143,15 @@ hipError_t launch_gemv_batched(const int8_t* Xq, const float* s_x, int64_t T, in
                                const uint8_t* const* codes, const uint8_t* const* meta,
                                const float* const* s_w, int64_t R, int n, int m, void* const* Y,
                                sbn_dtype ydt, int64_t ldy, int count, hipStream_t st);
+// Decode GEMV over a table of `count` weights in device memory; one launch.  The shapes it covers (K a multiple of 1024 up
+// to 4096; 2:4 and 6:8 packed weights, or decode planes of any ratio):
+using GvEntry = sbn_gemv_entry;
+bool gemv_table_shape_ok(int64_t K, int n, int m);
+bool gemv_d2_table_shape_ok(int64_t K);
+hipError_t launch_gemv_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const GvEntry* table,
+                             int64_t count, int64_t R, int n, int m, sbn_dtype ydt, int64_t ldy, hipStream_t st);
+hipError_t launch_gemv_d2_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const GvEntry* table,
+                                int64_t count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st);
 // Decode plane: repack of the packed planes, and the GEMV over up to GV_MAX_BATCH planes.
 hipError_t launch_repack_d2(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, int n, int m,
                             uint8_t* d2, hipStream_t st);

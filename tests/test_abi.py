@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = sbn.header_symbols()
-    assert len(names) == 26
+    assert len(names) == 29
     for nm in names:
         assert hasattr(L, nm), nm
 
@@ -138,6 +138,74 @@ def test_gemv_batched_validation(L):
     assert call(n=5, m=4) == NM
     assert call(ydt=7) == DTYPE
     assert call(meta=arr(P, P, MIS)) == ALIGN and b"weight 2" in L.sbn_last_error()
+
+
+def test_gemv_table_validation(L):
+    """The table calls check what the host can see (the table's entries live in
+    device memory); sbn_gemv_table_check checks a host copy of the entries."""
+    f = L.sbn_sparse_ternary_gemv_table
+
+    def call(table=P, count=3, T=4, K=4096, R=256, n=2, m=4, ydt=1, ldy=256):
+        return f(P, P, T, K, table, count, R, n, m, ydt, ldy, None)
+
+    assert call(table=None) == NULL
+    assert f(None, P, 4, 4096, P, 3, 256, 2, 4, 1, 256, None) == NULL
+    assert call(table=MIS) == ALIGN
+    assert call(count=0) == SHAPE
+    assert call(count=1 << 40) == SHAPE                     # count * ceil(R / 16) reaches 2^40
+    assert call(T=17) == SHAPE
+    assert call(K=2560) == SHAPE                            # not a multiple of 1024
+    assert call(K=5120) == SHAPE                            # above 4096
+    assert call(n=4, m=8) == NM                             # no streamed decoder for 4:8
+    assert call(n=5, m=4) == NM
+    assert call(ydt=7) == DTYPE
+    assert call(ldy=250) == SHAPE
+    g = L.sbn_ternary_gemv_d2_table
+    assert g(P, P, 4, 4096, None, 3, 256, 1, 256, None) == NULL
+    assert g(P, P, 4, 3000, P, 3, 256, 1, 256, None) == SHAPE
+    assert g(P, P, 4, 4096, P, 0, 256, 1, 256, None) == SHAPE
+    assert g(P, P, 4, 4096, MIS, 3, 256, 1, 256, None) == ALIGN
+    c = L.sbn_gemv_table_check
+    tab = lambda *rows: (ctypes.c_void_p * (4 * len(rows)))(*[p for r in rows for p in r])
+    good = (P, P2, P, P2)
+    assert c(tab(good, good), 2, 4, 4096, 256, 2, 4, 0, 1, 256) == OK
+    assert c(tab(good, (None, P2, P, P2)), 2, 4, 4096, 256, 2, 4, 0, 1, 256) == NULL
+    assert b"entry 1" in L.sbn_last_error()
+    assert c(tab(good, (P, MIS, P, P2)), 2, 4, 4096, 256, 2, 4, 0, 1, 256) == ALIGN
+    assert c(tab(good, (P, None, P, P2)), 2, 4, 4096, 256, 2, 4, 0, 1, 256) == NULL     # meta below n == m
+    assert c(tab(good, (P, None, P, P2)), 2, 4, 4096, 256, 0, 0, 1, 1, 256) == OK       # planes: meta unused
+    assert c(tab(good, (P, P, P, MIS)), 2, 4, 4096, 256, 2, 4, 0, 1, 256) == ALIGN      # Y
+    assert c(tab(good), 1, 17, 4096, 256, 2, 4, 0, 1, 256) == SHAPE
+    assert c(None, 1, 4, 4096, 256, 2, 4, 0, 1, 256) == NULL
+
+
+def test_gemv_table_binding_checks_before_the_copy():
+    """GemvTable checks every entry on the host and refuses mismatched outputs;
+    the calls refuse activations whose shape is not the table's (CPU tensors:
+    nothing is launched)."""
+    import torch
+    codes = [torch.zeros(4096 * 256 // 4, dtype=torch.uint8) for _ in range(2)]
+    metas = [torch.zeros(4096 * 256 // 8, dtype=torch.uint8) for _ in range(2)]
+    s_ws = [torch.ones(1, dtype=torch.float32) for _ in range(2)]
+    tab = sbn.GemvTable(codes, metas, s_ws, 256, 4096, 2, 4, T=2)
+    assert tab.count == 2 and tab.dev.shape == (8,) and tab.ldy == 256 and len(tab.Ys) == 2
+    assert int(tab.dev[0]) == codes[0].data_ptr() and int(tab.dev[7]) == tab.Ys[1].data_ptr()
+    with pytest.raises(sbn.SbnError) as e:
+        sbn.sbn_sparse_ternary_gemv_table(torch.zeros((3, 4096), dtype=torch.int8), torch.ones(3), tab)
+    assert e.value.status == 2
+    with pytest.raises(sbn.SbnError) as e:
+        sbn.sbn_ternary_gemv_d2_table(torch.zeros((2, 4096), dtype=torch.int8), torch.ones(2), tab)
+    assert e.value.status == 2
+    with pytest.raises(sbn.SbnError) as e:            # one Y with another row stride
+        sbn.GemvTable(codes, metas, s_ws, 256, 4096, 2, 4, T=2,
+                      Ys=[torch.empty((2, 256), dtype=torch.bfloat16), torch.empty((2, 264), dtype=torch.bfloat16)[:, :256]])
+    assert e.value.status == 2
+    with pytest.raises(sbn.SbnError) as e:            # 6:8 without its meta planes
+        sbn.GemvTable(codes, None, s_ws, 256, 4096, 6, 8, T=2)
+    assert e.value.status == 1
+    with pytest.raises(sbn.SbnError) as e:
+        sbn.GemvTable([], [], [], 256, 4096, 2, 4)
+    assert e.value.status == 2
 
 
 def test_backward_validation(L):
