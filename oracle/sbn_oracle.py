@@ -39,6 +39,9 @@ readings below (each is repeated at the function that uses it):
     and grad_W blocked at pruned positions (grad_W * mask);
   * a decode plane (pack_d2, not on the pages): the effective ternary
     weights as one 2-bit code per position, for memory-bound decode;
+  * a joint 2:4 code (pack_j6, not on the pages): each group of four
+    effective 2:4 weights as one 6-bit code of its two (position, value)
+    slots, 1.5 bits per weight, for memory-bound decode;
   * the master-weight optimizer step ([ja] §2.1: BF16 master weights are
     kept and receive the gradients; no optimizer is named): plain SGD,
     w' = bf16(fl32(w - lr*g)) with fl32 one rounding of the exact value
@@ -71,6 +74,7 @@ __all__ = [
     "pack_sbn1", "act_quant", "accumulate", "output", "backward",
     "forward", "S_FLOOR", "QMAX", "nm_mask_ternary", "fma_f32", "f32_to_bf16_rne",
     "sgd_update", "pack_d2", "unpack_d2", "output_f32", "output_bf16",
+    "j6_group_code", "j6_group_weights", "pack_j6", "unpack_j6", "j6_bytes",
 ]
 
 
@@ -282,6 +286,118 @@ def unpack_d2(plane: np.ndarray, R: int, K: int) -> np.ndarray:
     c = (words >> shift.astype(np.uint32)) & 3
     w = np.where(c == 1, 1, np.where(c == 3, -1, 0)).astype(np.int8)
     return w.reshape(R, K)
+
+
+# --------------------------------------------------------------------------- joint 2:4 code
+# Not a format of the pages: a byte-lean form of a 2:4 weight for memory-bound
+# decode ([ja] §3.2 and [de] §4 "Geschwindigkeit" report decoding speed; a 2:4
+# group of ternary weights has at most two nonzeros, so it is fixed by two
+# (position, value) slots).  A group's code is 6 bits, c = nib | h << 4:
+#   nib = i1 | i2 << 2, the positions (0..3) of slot 1 and slot 2;
+#   if i1 != i2: slot values v1 = -1 if h & 1 else +1, v2 = -1 if h & 2 else +1;
+#   if i1 == i2: v1 = 0, +1, -1 for h = 0, 1, 3 (h = 2 is not a code), v2 = 0;
+# and the group's weights are v1 at i1 plus v2 at i2.  The canonical code of a
+# group (the one pack_j6 writes): two nonzeros at i < j -> nib = i | j << 2
+# with their signs in h; one nonzero at p -> nib = p | p << 2, h = 1 (+1) or
+# 3 (-1); no nonzero -> c = 0.  33 groups, 33 canonical codes.
+
+def j6_group_code(w4) -> int:
+    """Canonical 6-bit code of one group of four effective ternary weights
+    (at most two nonzeros)."""
+    nz = [p for p in range(4) if w4[p] != 0]
+    if len(nz) > 2:
+        raise ValueError(f"group {list(w4)} has more than two nonzeros")
+    if len(nz) == 2:
+        i, j = nz
+        h = (1 if w4[i] < 0 else 0) | (2 if w4[j] < 0 else 0)
+        return (i | j << 2) | h << 4
+    if len(nz) == 1:
+        p = nz[0]
+        return (p | p << 2) | (1 if w4[p] > 0 else 3) << 4
+    return 0
+
+
+def j6_group_weights(c: int) -> list:
+    """The four weights a 6-bit code stands for: v1 at i1 plus v2 at i2."""
+    nib, h = c & 15, c >> 4
+    i1, i2 = nib & 3, nib >> 2
+    w = [0, 0, 0, 0]
+    if i1 != i2:
+        w[i1] += -1 if h & 1 else 1
+        w[i2] += -1 if h & 2 else 1
+    else:
+        if h == 2:
+            raise ValueError(f"code {c:#x} is not a code (equal positions with h = 2)")
+        w[i1] += {0: 0, 1: 1, 3: -1}[h]
+    return w
+
+
+def _j6_tables():
+    # code of every ternary group (key sum (w_p + 1) * 3^p; -1 where > 2 nonzeros),
+    # and the weights of every 6-bit code (a row of 99 where c is not a code)
+    code = np.full(81, -1, dtype=np.int16)
+    for key in range(81):
+        w4 = [(key // 3 ** p) % 3 - 1 for p in range(4)]
+        if sum(1 for v in w4 if v) <= 2:
+            code[key] = j6_group_code(w4)
+    weights = np.full((64, 4), 99, dtype=np.int8)
+    for c in range(64):
+        try:
+            weights[c] = j6_group_weights(c)
+        except ValueError:
+            pass
+    return code, weights
+
+
+_J6_CODE, _J6_WEIGHTS = _j6_tables()
+
+
+def j6_bytes(R: int, K: int):
+    """(nibble-plane bytes, h-plane bytes) of an R x K weight: K/8 and K/16 per row."""
+    return R * K // 8, R * K // 16
+
+
+def pack_j6(codes: np.ndarray):
+    """Joint 2:4 code of an effective 2:4 ternary weight (int8 [R, K], K a
+    multiple of 64; every group of 4 with at most two nonzeros).
+
+    Two planes, each row-major with the row strides below:
+      nibble plane (K/8 bytes per row): the nib of group g in bits 4(g % 2)
+        .. +3 of byte g / 2 -- as 32-bit little-endian words, word v holds
+        groups 8v .. 8v + 7 at bits 4(g % 8), the index word of the 2:4
+        matrix instruction for those 32 positions;
+      h plane (K/16 bytes per row): word u (32-bit little-endian) holds the h
+        of groups 16u .. 16u + 15; group 16u + 8b + 2k + o (b, o in 0..1,
+        k in 0..3) in byte k at bits 2f, 2f + 1 with f = 2b + o.
+    Returns (nibble_plane uint8 [R, K/8], h_plane uint8 [R, K/16]).
+    """
+    R, K = codes.shape
+    assert K % 64 == 0
+    key = ((codes.astype(np.int16) + 1).reshape(R, K // 4, 4) * np.array([1, 3, 9, 27], dtype=np.int16)).sum(-1)
+    c = _J6_CODE[key]
+    if (c < 0).any():
+        raise ValueError("a group has more than two nonzeros")
+    nib = (c & 15).astype(np.uint8)
+    h = (c >> 4).astype(np.uint8)
+    nib_plane = nib[:, 0::2] | (nib[:, 1::2] << 4)
+    hh = h.reshape(R, K // 64, 2, 4, 2)                  # [r, u, b, k, o]
+    f = 2 * np.arange(2)[:, None, None] + np.arange(2)[None, None, :]      # [b, 1, o] -> f = 2b + o
+    byte = (hh.astype(np.uint32) << (2 * f)[None, None, :, :, :].astype(np.uint32)).sum(axis=(2, 4))   # [r, u, k]
+    h_plane = byte.astype(np.uint8).reshape(R, K // 16)
+    return nib_plane, h_plane
+
+
+def unpack_j6(nib_plane: np.ndarray, h_plane: np.ndarray, R: int, K: int) -> np.ndarray:
+    """Inverse of pack_j6 (any valid code, canonical or not): int8 [R, K]."""
+    nib = np.stack([nib_plane & 15, nib_plane >> 4], axis=-1).reshape(R, K // 4)
+    byte = h_plane.reshape(R, K // 64, 1, 4, 1).astype(np.uint32)          # [r, u, -, k, -]
+    f = 2 * np.arange(2)[:, None, None] + np.arange(2)[None, None, :]
+    h = (byte >> (2 * f)[None, None, :, :, :].astype(np.uint32)) & 3      # [r, u, b, k, o]
+    c = nib.astype(np.int32) | (h.reshape(R, K // 4).astype(np.int32) << 4)
+    w = _J6_WEIGHTS[c]
+    if (w == 99).any():
+        raise ValueError("not a code")
+    return w.reshape(R, K).astype(np.int8)
 
 
 # --------------------------------------------------------------------------- activations

@@ -335,3 +335,57 @@ def d2_decode_matches(plane, codes) -> bool:
                     if sv != 64 * int(codes[r, 16 * w + 4 * k + b]):
                         return False
     return True
+
+
+def j6_by_loops(eff):
+    """Bit-by-bit construction of the joint 2:4 code planes from the written
+    definition: per group the slots (i1, v1), (i2, v2) -- both nonzeros in
+    increasing position, or the one nonzero twice with a zero second value, or
+    position 0 with zeros -- then nib = i1 | i2 << 2 at bits 4(g % 2) of byte
+    g / 2, and h (slot signs, or the single value's 2-bit code) at bits
+    2(2b + o) of byte k of the 16-group word, group 16u + 8b + 2k + o."""
+    R, K = eff.shape
+    nib_plane = np.zeros((R, K // 8), dtype=np.uint8)
+    h_plane = np.zeros((R, K // 16), dtype=np.uint8)
+    for r in range(R):
+        for g in range(K // 4):
+            w = [int(v) for v in eff[r, 4 * g: 4 * g + 4]]
+            nz = [p for p in range(4) if w[p] != 0]
+            assert len(nz) <= 2
+            if len(nz) == 2:
+                i1, i2 = nz
+                h = (1 if w[i1] < 0 else 0) + (2 if w[i2] < 0 else 0)
+            elif len(nz) == 1:
+                i1 = i2 = nz[0]
+                h = 1 if w[i1] > 0 else 3
+            else:
+                i1 = i2 = 0
+                h = 0
+            nib_plane[r, g // 2] |= (i1 | (i2 << 2)) << (4 * (g % 2))
+            u, rem = divmod(g, 16)
+            b, rem = divmod(rem, 8)
+            k, o = divmod(rem, 2)
+            h_plane[r, 4 * u + k] |= h << (2 * (2 * b + o))
+    return nib_plane, h_plane
+
+
+def j6_slots_sum(nib_plane, h_plane, R, K):
+    """The decode the kernels use, slot by slot: value v1 at i1 plus v2 at i2
+    (i1 != i2: both +-1 from the sign bits; i1 == i2: v1 from the 2-bit code,
+    v2 = 0).  Returns int8 [R, K]."""
+    out = np.zeros((R, K), dtype=np.int8)
+    code = {0: 0, 1: 1, 3: -1}
+    for r in range(R):
+        for g in range(K // 4):
+            nib = (int(nib_plane[r, g // 2]) >> (4 * (g % 2))) & 15
+            u, rem = divmod(g, 16)
+            b, rem = divmod(rem, 8)
+            k, o = divmod(rem, 2)
+            h = (int(h_plane[r, 4 * u + k]) >> (2 * (2 * b + o))) & 3
+            i1, i2 = nib & 3, nib >> 2
+            if i1 != i2:
+                out[r, 4 * g + i1] += -1 if h & 1 else 1
+                out[r, 4 * g + i2] += -1 if h & 2 else 1
+            else:
+                out[r, 4 * g + i1] += code[h]
+    return out

@@ -346,3 +346,63 @@ def test_output_mutants_are_caught(mutant):
     p2 = (np.float32(0.5), np.array([2.0 ** -7], dtype=np.float32))
     assert not (pins.output_matches_exact(f32_fn, bf16_fn, acc, s_w, s_x)
                 and pins.output_matches_exact(f32_fn, bf16_fn, acc2, *p2))
+
+
+# ----------------------------------------------------------------- joint 2:4 code
+def _j6_h_fields_transposed(eff):
+    nib, h = O.pack_j6(eff)
+    R, K = eff.shape
+    # f = 2o + b instead of 2b + o
+    hh = np.zeros_like(h)
+    for f_old, f_new in ((0, 0), (1, 2), (2, 1), (3, 3)):
+        hh |= ((h >> (2 * f_old)) & 3) << (2 * f_new)
+    return nib, hh
+
+
+def _j6_nibbles_high_first(eff):
+    nib, h = O.pack_j6(eff)
+    return ((nib << 4) | (nib >> 4)).astype(np.uint8), h
+
+
+def _j6_pair_sign_bits_swapped(eff):
+    return O.pack_j6(_swap_pair_signs(eff))
+
+
+def _swap_pair_signs(eff):
+    # exchanges the two signs of every two-nonzero group (the slot-1 / slot-2 bits swapped)
+    out = eff.copy()
+    R, K = eff.shape
+    for r in range(R):
+        for g in range(K // 4):
+            w = out[r, 4 * g: 4 * g + 4]
+            nz = np.flatnonzero(w)
+            if len(nz) == 2:
+                w[nz[0]], w[nz[1]] = w[nz[1]], w[nz[0]]
+    return out
+
+
+def _j6_single_minus_as_2(eff):
+    nib, h = O.pack_j6(eff)
+    R, K = eff.shape
+    out = h.copy()
+    for g in range(K // 4):
+        u, rem = divmod(g, 16)
+        b, rem = divmod(rem, 8)
+        k, o = divmod(rem, 2)
+        f = 2 * b + o
+        for r in range(R):
+            w = eff[r, 4 * g: 4 * g + 4]
+            if np.count_nonzero(w) == 1 and w.min() < 0:
+                out[r, 4 * u + k] = (int(out[r, 4 * u + k]) & (0xFF ^ (3 << (2 * f)))) | (2 << (2 * f))
+    return nib, out
+
+
+@pytest.mark.parametrize("mutant", [_j6_h_fields_transposed, _j6_nibbles_high_first, _j6_pair_sign_bits_swapped,
+                                    _j6_single_minus_as_2])
+def test_j6_mutants_are_caught(mutant):
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "j6_row_k64.json")))
+    eff = np.array(g["rows"], dtype=np.int8)
+    nib, h = mutant(eff)
+    assert not (nib.tolist() == g["nib_plane"] and h.tolist() == g["h_plane"])

@@ -442,3 +442,77 @@ def test_d2_worked_word():
     # position 0 -> bits 6,7 of byte 0 (code 01 -> 0x40); position 5 -> bits 4,5 of byte 1
     # (code 11 -> 0x30); position 15 -> bits 0,1 of byte 3 (code 01 -> 0x01)
     assert O.pack_d2(codes).tolist() == [[0x40, 0x30, 0x00, 0x01]]
+
+
+# ----------------------------------------------------------------- joint 2:4 code
+def test_j6_worked_rows():
+    g = json.load(open(os.path.join(GOLDEN, "j6_row_k64.json")))
+    eff = np.array(g["rows"], dtype=np.int8)
+    nib, h = O.pack_j6(eff)
+    assert nib.tolist() == g["nib_plane"] and h.tolist() == g["h_plane"]
+    assert np.array_equal(O.unpack_j6(nib, h, 2, g["K"]), eff)
+
+
+def test_j6_groups_closed_form_count_and_round_trip():
+    # a 2:4 group of effective ternary weights has 0, 1 or 2 nonzeros:
+    # 1 + 4*2 + C(4,2)*4 = 33 groups, so 6 bits (64 >= 33 > 32) -- 1.5 bits per weight
+    groups = [w for w in itertools.product((-1, 0, 1), repeat=4) if sum(1 for v in w if v) <= 2]
+    assert len(groups) == 1 + 4 * 2 + math.comb(4, 2) * 4 == 33
+    codes = [O.j6_group_code(w) for w in groups]
+    assert len(set(codes)) == 33 and all(0 <= c < 64 for c in codes)
+    for w, c in zip(groups, codes):
+        assert O.j6_group_weights(c) == list(w)
+    for w in itertools.product((-1, 0, 1), repeat=4):
+        if sum(1 for v in w if v) > 2:
+            with pytest.raises(ValueError):
+                O.j6_group_code(w)
+
+
+def test_j6_every_code_is_two_slots():
+    # every 6-bit value is either not a code (equal positions with h = 2: four values)
+    # or stands for at most two nonzeros, at the positions its nibble names
+    bad = 0
+    for c in range(64):
+        i1, i2, h = c & 3, (c >> 2) & 3, c >> 4
+        if i1 == i2 and h == 2:
+            bad += 1
+            with pytest.raises(ValueError):
+                O.j6_group_weights(c)
+            continue
+        w = O.j6_group_weights(c)
+        support = {p for p in range(4) if w[p] != 0}
+        assert support <= {i1, i2} and len(support) <= 2
+        assert O.j6_group_weights(O.j6_group_code(w)) == w          # canonical form stands for the same group
+    assert bad == 4
+
+
+def test_j6_all_sbn1_24_states():
+    # every 2:4 packed state (two survivors, each code 0 / +1 / -1): 6 * 9 = 54 states,
+    # whose effective groups the joint code must reproduce
+    states = 0
+    for pos in itertools.combinations(range(4), 2):
+        for vals in itertools.product((0, 1, -1), repeat=2):
+            eff = np.zeros((1, 64), dtype=np.int8)
+            eff[0, list(pos)] = vals
+            nib, h = O.pack_j6(eff)
+            assert np.array_equal(O.unpack_j6(nib, h, 1, 64), eff)
+            assert np.array_equal(pins.j6_slots_sum(nib, h, 1, 64), eff)
+            states += 1
+    assert states == 54
+
+
+@pytest.mark.parametrize("R,K", [(3, 64), (5, 256), (2, 1024)])
+def test_j6_matches_bit_loops_on_real_weights(R, K):
+    W = gaussian_bf16((R, K), 0.02, seed=R + K, stream=0)
+    eff, mask, sw = O.quant_then_mask(W, 2, 4)
+    nib, h = O.pack_j6(eff)
+    ln, lh = pins.j6_by_loops(eff)
+    assert np.array_equal(nib, ln) and np.array_equal(h, lh)
+    assert np.array_equal(pins.j6_slots_sum(nib, h, R, K), eff)
+    assert np.array_equal(O.unpack_j6(nib, h, R, K), eff)
+    # 1.5 bits per weight: 3/4 of the 2:4 packed planes
+    cb, mb = O.packed_bytes(R, K, 2, 4)
+    assert O.j6_bytes(R, K) == (nib.size, h.size) and 4 * (nib.size + h.size) == 3 * (cb + mb)
+    # the GEMV through the code is the GEMV of the effective weights
+    Xq, _ = O.act_quant(gaussian_bf16((3, K), 1.0, seed=K, stream=1))
+    assert np.array_equal(O.accumulate(Xq, O.unpack_j6(nib, h, R, K)), O.accumulate(Xq, eff))
