@@ -705,6 +705,66 @@ def make_decode_step_d2(T=1):
     return step, total, POOL * per
 
 
+def make_decode_pool_24(form, T=1):
+    """The 2:4 pool of the decode step alone (POOL weights of R = K = 4096),
+    as packed planes (form "packed") or as joint 2:4 codes (form "j6",
+    repacked once outside the timed region), one table launch.  Returns
+    (step, bytes per step)."""
+    import sparse_linear_layers_02_amd as sbn
+    from workloads import WORKLOADS
+    wl = WORKLOADS["decode"]
+    W = bf16_dev(wl.weights(0))
+    Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0, T=T)))
+    codes0, meta0, s_w0 = sbn.sbn_mask_ternarize_pack(W, 2, 4)
+    del W
+    rest = T * wl.K + 4 * T + 2 * T * wl.R + 4
+    if form == "packed":
+        tab = sbn.GemvTable([codes0.clone() for _ in range(POOL)], [meta0.clone() for _ in range(POOL)],
+                            [s_w0.clone() for _ in range(POOL)], wl.R, wl.K, 2, 4, T=T)
+        per = sum(sbn.sbn_packed_bytes(wl.R, wl.K, 2, 4)) + rest
+
+        def step():
+            sbn.sbn_sparse_ternary_gemv_table(Xq, s_x, tab)
+    else:
+        nib0, h0 = sbn.sbn_repack_j6(codes0, meta0, wl.R, wl.K)
+        tab = sbn.GemvTable.joint([nib0.clone() for _ in range(POOL)], [h0.clone() for _ in range(POOL)],
+                                  [s_w0.clone() for _ in range(POOL)], wl.R, wl.K, T=T)
+        per = sum(sbn.sbn_j6_bytes(wl.R, wl.K)) + rest
+
+        def step():
+            sbn.sbn_ternary_gemv_j6_table(Xq, s_x, tab)
+    return step, POOL * per
+
+
+def measure_decode_j6(a):
+    """The 2:4 pool as joint 2:4 codes (1.5 bits per weight) against the same
+    pool as packed planes (2 bits per weight), each one table launch per step:
+    time per pool, GB/s of each form's own bytes, and the joint code's HBM
+    roofline (`gemv_stream_j6`)."""
+    import torch
+    res = {}
+    for form, kname in (("packed", "gemv_stream_24"), ("j6", "gemv_stream_j6")):
+        step, nbytes = make_decode_pool_24(form)
+        ms, _, _, mode = time_steps(step, a.steps, a.warmup, kernel=kname)
+        k_ms, k_cnt = kernel_avg_ms(profile_pass(step, a.steps, kname), kname)
+        ach = nbytes / (k_ms * 1e-3) / 1e9
+        res[form] = {"ms_per_pool": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "launch": mode,
+                     "bytes_per_pool": nbytes,
+                     "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                                  "traffic": traffic_from_profiles(kname, "decode"), "kernel_us": round(k_ms * 1e3, 3),
+                                  "launches": k_cnt, "bytes_per_launch": nbytes}}
+        del step
+        torch.cuda.empty_cache()
+    res["speedup_vs_packed"] = round(res["packed"]["ms_per_pool"] / res["j6"]["ms_per_pool"], 3)
+    res["weights_per_s"] = {f: round(POOL * 4096 * 4096 / (res[f]["ms_per_pool"] * 1e-3) / 1e12, 3)
+                            for f in ("packed", "j6")}
+    res["note"] = ("the 2:4 pool (128 weights of 4096 x 4096, T = 1, bf16 Y) as joint 2:4 codes, repacked once outside "
+                   "the timed region, against the same weights as packed planes; weights_per_s in 1e12 weights/s")
+    return res
+
+
 def measure_decode_step(a, with_d2=True):
     """The decode half of the metric as one step: batched decode GEMVs over
     both pools (make_decode_step), timed like every step, with the HBM
@@ -748,6 +808,7 @@ def measure_decode_step(a, with_d2=True):
                          "kernel_us": round(k_ms * 1e3, 3), "launches": k_cnt, "bytes_per_launch": per_launch2}}
         del step2
         torch.cuda.empty_cache()
+        out["decode_j6"] = measure_decode_j6(a)
     return out
 
 
@@ -905,6 +966,8 @@ def main():
                                                 "roofline_68")}
         torch.cuda.empty_cache()
         out["decode_gemv"] = [decode_gemv(2, 4, 1), decode_gemv(6, 8, 1)]
+        torch.cuda.empty_cache()
+        out["decode_j6"] = measure_decode_j6(a)
     if not a.no_extras and a.workload == "train":
         out["variants"] = variants_extras(WORKLOADS["train"])
 

@@ -360,11 +360,16 @@ sbn_status sbn_sparse_ternary_gemv_table(const int8_t* Xq, const float* s_x, int
 /*
  * Host-only check of a GEMV table before it is copied to the device: every
  * entry of the HOST array `table` (count entries) against the arguments of a
- * later sbn_sparse_ternary_gemv_table call (d2 = 0) or sbn_ternary_gemv_d2_table
- * call (d2 = 1; n, m ignored).  Returns the first failure, naming the entry.
+ * later table call of the given form: SBN_FORM_PACKED for
+ * sbn_sparse_ternary_gemv_table, SBN_FORM_D2 for sbn_ternary_gemv_d2_table,
+ * SBN_FORM_J6 for sbn_ternary_gemv_j6_table (n, m ignored for the last two).
+ * Returns the first failure, naming the entry; SBN_ERR_VALUE for an unknown form.
  */
+#define SBN_FORM_PACKED 0
+#define SBN_FORM_D2 1
+#define SBN_FORM_J6 2
 sbn_status sbn_gemv_table_check(const sbn_gemv_entry* table, int64_t count, int64_t T, int64_t K, int64_t R,
-                                int n, int m, int d2, sbn_dtype ydt, int64_t ldy);
+                                int n, int m, int form, sbn_dtype ydt, int64_t ldy);
 
 /*
  * Decode plane: a byte-lean form of a packed weight for memory-bound decode
@@ -402,6 +407,49 @@ sbn_status sbn_ternary_gemv_d2_batched(const int8_t* Xq, const float* s_x, int64
  * are the caller's to keep valid and are not checked here).
  */
 sbn_status sbn_ternary_gemv_d2_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                     const sbn_gemv_entry* table, int64_t count, int64_t R, sbn_dtype ydt,
+                                     int64_t ldy, void* stream);
+
+/*
+ * Joint 2:4 code: a byte-lean form of a 2:4 packed weight for memory-bound
+ * decode (not a format of the pages; the pages benchmark 2:4 decode,
+ * gist.science/ja 技術概要 §3.2, gist.science/de Technische Zusammenfassung §4).
+ * Each group of four effective ternary weights (at most two nonzeros) is one
+ * 6-bit code, 1.5 bits per weight against the packed planes' 2:
+ *   code = nib | h << 4, nib = i1 | i2 << 2 (positions of two slots);
+ *   i1 != i2: slot values v1 = h & 1 ? -1 : +1, v2 = h & 2 ? -1 : +1;
+ *   i1 == i2: v1 = 0, +1, -1 for h = 0, 1, 3, v2 = 0;
+ *   the group's weights are v1 at i1 plus v2 at i2.
+ * Canonical code (what sbn_repack_j6 writes): two nonzeros at i < j ->
+ * (i, j) with their signs; one nonzero at p -> (p, p) with its code; none -> 0.
+ * Two planes, row-major:
+ *   nibble plane, K/8 bytes per row: nib of group g in bits 4(g % 2) of byte
+ *     g / 2 (32-bit little-endian word v holds groups 8v .. 8v+7 at bits
+ *     4(g % 8): the 2:4 matrix instruction's index word for those positions);
+ *   h plane, K/16 bytes per row: 32-bit little-endian word u holds groups
+ *     16u .. 16u+15, group 16u + 8b + 2k + o (b, o in 0..1, k in 0..3) in
+ *     byte k at bits 2(2b + o) and 2(2b + o) + 1.
+ *
+ * sbn_j6_bytes: nibble- and h-plane bytes, R*K/8 and R*K/16 each rounded up
+ *   to 16 (host-only).  K a multiple of 64.
+ * sbn_repack_j6: 2:4 packed planes (codes, meta) -> the two planes.  K a
+ *   multiple of 64.  The inputs must be 2:4 planes as sbn_mask_ternarize_pack
+ *   writes them (two survivors per group).
+ * sbn_ternary_gemv_j6: the decode GEMV of sbn_sparse_ternary_gemv on the
+ *   joint code (same results bit for bit; s_w the weight's scale), 1 <= T <=
+ *   16, K a multiple of 1024 up to 4096 (else SBN_ERR_SHAPE).
+ * sbn_ternary_gemv_j6_table: the same over a DEVICE table of weights
+ *   (table[b].codes = nibble plane, table[b].meta = h plane), one launch, as
+ *   sbn_sparse_ternary_gemv_table.
+ * Errors: as the packed-weight calls.
+ */
+sbn_status sbn_j6_bytes(int64_t R, int64_t K, size_t* nib_bytes, size_t* h_bytes);
+sbn_status sbn_repack_j6(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, uint8_t* nib,
+                         uint8_t* hpl, void* stream);
+sbn_status sbn_ternary_gemv_j6(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const uint8_t* nib,
+                               const uint8_t* hpl, const float* s_w, int64_t R, void* Y, sbn_dtype ydt, int64_t ldy,
+                               void* stream);
+sbn_status sbn_ternary_gemv_j6_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                                      const sbn_gemv_entry* table, int64_t count, int64_t R, sbn_dtype ydt,
                                      int64_t ldy, void* stream);
 

@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libsbn.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "sbn.h")
 
 SBN_F32, SBN_BF16, SBN_I32_ACC = 0, 1, 2
+SBN_FORM_PACKED, SBN_FORM_D2, SBN_FORM_J6 = 0, 1, 2     # the weight forms a GEMV table can hold
 SBN_OP_PACK, SBN_OP_ACT_QUANT, SBN_OP_GEMM, SBN_OP_GEMV, SBN_OP_BACKWARD, SBN_OP_FORWARD = 0, 1, 2, 3, 4, 5
 SBN_OP_GEMM_PREPARED = 6
 SBN_FLAGS_NONE, SBN_MASK_FROM_TERNARY, SBN_GRAD_W_MASKED = 0, 1, 2
@@ -78,6 +79,10 @@ _SIGNATURES = {
     "sbn_sparse_ternary_gemv_table": ([_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _int, _int, _i64, _vp], _int),
     "sbn_ternary_gemv_d2_table": ([_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _i64, _vp], _int),
     "sbn_gemv_table_check": ([_vp, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _i64], _int),
+    "sbn_j6_bytes": ([_i64, _i64, ctypes.POINTER(_sz), ctypes.POINTER(_sz)], _int),
+    "sbn_repack_j6": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp], _int),
+    "sbn_ternary_gemv_j6": ([_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _vp, _int, _i64, _vp], _int),
+    "sbn_ternary_gemv_j6_table": ([_vp, _vp, _i64, _i64, _vp, _i64, _i64, _int, _i64, _vp], _int),
     "sbn_backward": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _int, _int, _vp, _int, _vp, _vp,
                       _sz, _vp], _int),
     "sbn_backward_ex": ([_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _int, _int, _vp, _int, _vp, _u32, _vp,
@@ -469,15 +474,18 @@ class GemvTable:
     with the row stride rounded up to 8 when not given)."""
 
     def __init__(self, codes, metas, s_ws, R: int, K: int, n: int, m: int, *, T: int = 1, ydt: int = SBN_BF16,
-                 Ys=None, d2: bool = False):
+                 Ys=None, d2: bool = False, form: int = None):
         torch = _torch()
-        fn = "sbn_ternary_gemv_d2_table" if d2 else "sbn_sparse_ternary_gemv_table"
+        if form is None:
+            form = SBN_FORM_D2 if d2 else SBN_FORM_PACKED
+        fn = {SBN_FORM_PACKED: "sbn_sparse_ternary_gemv_table", SBN_FORM_D2: "sbn_ternary_gemv_d2_table",
+              SBN_FORM_J6: "sbn_ternary_gemv_j6_table"}[form]
         count = len(codes)
         if count < 1:
             raise SbnError(fn, 2, "a table needs at least one weight")
         for b in range(count):
-            _req(codes[b], "d2" if d2 else "codes", "u8", True, fn)
-            _req(None if d2 or metas is None else metas[b], "meta", "u8", True, fn)
+            _req(codes[b], "codes", "u8", True, fn)
+            _req(None if form == SBN_FORM_D2 or metas is None else metas[b], "meta", "u8", True, fn)
             _req(s_ws[b], "s_w", "f32", True, fn)
             if Ys is not None:
                 if ydt in _YD:
@@ -492,19 +500,25 @@ class GemvTable:
         ptr = lambda t: 0 if t is None else t.data_ptr()
         host = (_vp * (4 * count))()
         for b in range(count):
-            mt = None if d2 or metas is None else metas[b]
+            mt = None if form == SBN_FORM_D2 or metas is None else metas[b]
             host[4 * b: 4 * b + 4] = [ptr(codes[b]), ptr(mt), ptr(s_ws[b]), ptr(Ys[b])]
-        _check("sbn_gemv_table_check", lib().sbn_gemv_table_check(host, count, T, K, R, n, m, int(d2), ydt, ldy))
+        _check("sbn_gemv_table_check", lib().sbn_gemv_table_check(host, count, T, K, R, n, m, form, ydt, ldy))
         flat = torch.tensor([0 if v is None else v for v in host], dtype=torch.int64)
         self.dev = flat.to(dev)                      # count x 4 pointers; 16-byte aligned (allocator)
         self.codes, self.metas, self.s_ws, self.Ys = list(codes), None if metas is None else list(metas), list(s_ws), Ys
         self.R, self.K, self.n, self.m, self.T, self.ydt, self.ldy = R, K, n, m, T, ydt, ldy
-        self.count, self.d2 = count, bool(d2)
+        self.count, self.form = count, form
+        self.d2 = form == SBN_FORM_D2
 
     @classmethod
     def planes(cls, d2s, s_ws, R: int, K: int, *, T: int = 1, ydt: int = SBN_BF16, Ys=None):
         """A table of decode planes (sbn_repack_d2 outputs)."""
-        return cls(d2s, None, s_ws, R, K, 0, 0, T=T, ydt=ydt, Ys=Ys, d2=True)
+        return cls(d2s, None, s_ws, R, K, 0, 0, T=T, ydt=ydt, Ys=Ys, form=SBN_FORM_D2)
+
+    @classmethod
+    def joint(cls, nibs, hs, s_ws, R: int, K: int, *, T: int = 1, ydt: int = SBN_BF16, Ys=None):
+        """A table of joint 2:4 codes (sbn_repack_j6 outputs: nibble and h planes)."""
+        return cls(nibs, hs, s_ws, R, K, 2, 4, T=T, ydt=ydt, Ys=Ys, form=SBN_FORM_J6)
 
 
 def _table_call(fn, Xq, s_x, table):
@@ -519,13 +533,59 @@ def _table_call(fn, Xq, s_x, table):
     return T, K
 
 
+def sbn_j6_bytes(R: int, K: int) -> tuple[int, int]:
+    nb, hb = _sz(), _sz()
+    _check("sbn_j6_bytes", lib().sbn_j6_bytes(R, K, ctypes.byref(nb), ctypes.byref(hb)))
+    return nb.value, hb.value
+
+
+def sbn_repack_j6(codes, meta, R: int, K: int, *, nib=None, hpl=None, stream=None):
+    """2:4 packed planes -> joint 2:4 code planes.  Returns (nib, hpl)."""
+    torch = _torch()
+    for t, name in ((codes, "codes"), (meta, "meta"), (nib, "nib"), (hpl, "hpl")):
+        _req(t, name, "u8", True, "sbn_repack_j6")
+    nb, hb = sbn_j6_bytes(R, K)
+    if nib is None:
+        nib = torch.empty(nb, dtype=torch.uint8, device=codes.device)
+    if hpl is None:
+        hpl = torch.empty(hb, dtype=torch.uint8, device=codes.device)
+    _check("sbn_repack_j6", lib().sbn_repack_j6(_ptr(codes), _ptr(meta), R, K, _ptr(nib), _ptr(hpl), _stream(stream)))
+    return nib, hpl
+
+
+def sbn_ternary_gemv_j6(Xq, s_x, nib, hpl, s_w, R: int, *, ydt: int = SBN_BF16, Y=None, stream=None):
+    """Decode GEMV (T <= 16) on a joint 2:4 code.  Returns Y [T, R]."""
+    torch = _torch()
+    T, K = Xq.shape
+    _req_matmul("sbn_ternary_gemv_j6", Xq, s_x, s_w, ydt, Y)
+    _req(nib, "nib", "u8", True, "sbn_ternary_gemv_j6")
+    _req(hpl, "hpl", "u8", True, "sbn_ternary_gemv_j6")
+    if Y is None:
+        Y = torch.empty((T, (R + 7) // 8 * 8), dtype=getattr(torch, _YT[ydt]), device=Xq.device)[:, :R]
+    _check("sbn_ternary_gemv_j6", lib().sbn_ternary_gemv_j6(_ptr(Xq), _ptr(s_x), T, K, _ptr(nib), _ptr(hpl), _ptr(s_w),
+                                                          R, _ptr(Y), ydt, Y.stride(0), _stream(stream)))
+    return Y
+
+
+def sbn_ternary_gemv_j6_table(Xq, s_x, table, *, stream=None):
+    """Decode GEMV of every weight of `table` (GemvTable.joint) against Xq, one
+    launch.  Returns the table's list of Y."""
+    fn = "sbn_ternary_gemv_j6_table"
+    T, K = _table_call(fn, Xq, s_x, table)
+    if table.form != SBN_FORM_J6:
+        raise SbnError(fn, 2, "the table does not hold joint codes")
+    _check(fn, lib().sbn_ternary_gemv_j6_table(_ptr(Xq), _ptr(s_x), T, K, table.dev.data_ptr(), table.count, table.R,
+                                               table.ydt, table.ldy, _stream(stream)))
+    return table.Ys
+
+
 def sbn_sparse_ternary_gemv_table(Xq, s_x, table, *, stream=None):
     """Decode GEMV of every weight of `table` (a GemvTable of packed weights)
     against Xq, one launch.  Returns the table's list of Y."""
     fn = "sbn_sparse_ternary_gemv_table"
     T, K = _table_call(fn, Xq, s_x, table)
-    if table.d2:
-        raise SbnError(fn, 2, "the table holds decode planes: use sbn_ternary_gemv_d2_table")
+    if table.form != SBN_FORM_PACKED:
+        raise SbnError(fn, 2, "the table does not hold packed weights")
     _check(fn, lib().sbn_sparse_ternary_gemv_table(_ptr(Xq), _ptr(s_x), T, K, table.dev.data_ptr(), table.count,
                                                    table.R, table.n, table.m, table.ydt, table.ldy, _stream(stream)))
     return table.Ys
@@ -536,8 +596,8 @@ def sbn_ternary_gemv_d2_table(Xq, s_x, table, *, stream=None):
     one launch.  Returns the table's list of Y."""
     fn = "sbn_ternary_gemv_d2_table"
     T, K = _table_call(fn, Xq, s_x, table)
-    if not table.d2:
-        raise SbnError(fn, 2, "the table holds packed weights: use sbn_sparse_ternary_gemv_table")
+    if table.form != SBN_FORM_D2:
+        raise SbnError(fn, 2, "the table does not hold decode planes")
     _check(fn, lib().sbn_ternary_gemv_d2_table(_ptr(Xq), _ptr(s_x), T, K, table.dev.data_ptr(), table.count, table.R,
                                                table.ydt, table.ldy, _stream(stream)))
     return table.Ys
@@ -612,7 +672,8 @@ __all__ = [
     "sbn_mask_ternarize_pack", "sbn_mask_ternarize_pack_noalloc", "sbn_act_quant", "sbn_sparse_ternary_gemm", "sbn_sparse_ternary_gemv",
     "sbn_backward", "sbn_backward_ex", "sbn_mask_ternarize_pack_ex", "sbn_sgd_update_pack", "sbn_forward",
     "sbn_decode_plane_bytes", "sbn_repack_d2", "sbn_ternary_gemv_d2", "sbn_ternary_gemv_d2_batched",
-    "GemvTable", "sbn_sparse_ternary_gemv_table", "sbn_ternary_gemv_d2_table",
+    "GemvTable", "sbn_sparse_ternary_gemv_table", "sbn_ternary_gemv_d2_table", "SBN_FORM_PACKED", "SBN_FORM_D2",
+    "SBN_FORM_J6", "sbn_j6_bytes", "sbn_repack_j6", "sbn_ternary_gemv_j6", "sbn_ternary_gemv_j6_table",
     "sbn_gemm_weight_bytes", "sbn_prepare_gemm_weight", "sbn_sparse_ternary_gemm_prepared", "SBN_OP_GEMM_PREPARED",
     "SBN_ERR_VALUE",
     "SBN_FLAGS_NONE", "SBN_MASK_FROM_TERNARY", "SBN_GRAD_W_MASKED",

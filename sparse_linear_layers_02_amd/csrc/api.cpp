@@ -684,6 +684,36 @@ sbn_status sbn_repack_d2(const uint8_t* codes, const uint8_t* meta, int64_t R, i
   return hip_result(launch_repack_d2(codes, n == m ? nullptr : meta, R, K, n, m, d2, st), st, fn);
 }
 
+sbn_status sbn_j6_bytes(int64_t R, int64_t K, size_t* nib_bytes, size_t* h_bytes) {
+  const char* fn = "sbn_j6_bytes";
+  SBN_NONNULL(nib_bytes);
+  SBN_NONNULL(h_bytes);
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
+  *nib_bytes = (size_t)round_up(R * K / 8, 16);
+  *h_bytes = (size_t)round_up(R * K / 16, 16);
+  return ok();
+}
+
+sbn_status sbn_repack_j6(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, uint8_t* nib,
+                         uint8_t* hpl, void* stream) {
+  const char* fn = "sbn_repack_j6";
+  SBN_NONNULL(codes);
+  SBN_NONNULL(meta);
+  SBN_NONNULL(nib);
+  SBN_NONNULL(hpl);
+  SBN_TRY(check_rows("R", R));
+  SBN_TRY(check_k(K));
+  SBN_TRY(check_numel(fn, "W (R*K)", R, K));
+  SBN_ALIGNED(codes);
+  SBN_ALIGNED(meta);
+  SBN_ALIGNED(nib);
+  SBN_ALIGNED(hpl);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_repack_j6(codes, meta, R, K, nib, hpl, st), st, fn);
+}
+
 static sbn_status check_d2_args(const char* fn, const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                                 const uint8_t* d2, const float* s_w, int64_t R, void* Y, sbn_dtype ydt,
                                 int64_t ldy) {
@@ -788,20 +818,51 @@ sbn_status sbn_ternary_gemv_d2_table(const int8_t* Xq, const float* s_x, int64_t
   return hip_result(launch_gemv_d2_table(Xq, s_x, T, K, table, count, R, ydt, ldy, st), st, fn);
 }
 
+sbn_status sbn_ternary_gemv_j6(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const uint8_t* nib,
+                               const uint8_t* hpl, const float* s_w, int64_t R, void* Y, sbn_dtype ydt, int64_t ldy,
+                               void* stream) {
+  const char* fn = "sbn_ternary_gemv_j6";
+  SBN_TRY(check_d2_args(fn, Xq, s_x, T, K, nib, s_w, R, Y, ydt, ldy));
+  SBN_NONNULL(hpl);
+  SBN_ALIGNED(hpl);
+  if (!gemv_d2_table_shape_ok(K))
+    return fail(SBN_ERR_SHAPE, "%s: K = %lld must be a multiple of 1024 up to 4096", fn, (long long)K);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_gemv_j6(Xq, s_x, T, K, nib, hpl, s_w, R, Y, ydt, ldy, st), st, fn);
+}
+
+sbn_status sbn_ternary_gemv_j6_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
+                                     const sbn_gemv_entry* table, int64_t count, int64_t R, sbn_dtype ydt,
+                                     int64_t ldy, void* stream) {
+  const char* fn = "sbn_ternary_gemv_j6_table";
+  SBN_TRY(check_table_call(fn, Xq, s_x, T, K, table, count, R, ydt, ldy));
+  if (!gemv_d2_table_shape_ok(K))
+    return fail(SBN_ERR_SHAPE, "%s: K = %lld must be a multiple of 1024 up to 4096", fn, (long long)K);
+  hipStream_t st = (hipStream_t)stream;
+  return hip_result(launch_gemv_j6_table(Xq, s_x, T, K, table, count, R, ydt, ldy, st), st, fn);
+}
+
 sbn_status sbn_gemv_table_check(const sbn_gemv_entry* table, int64_t count, int64_t T, int64_t K, int64_t R,
-                                int n, int m, int d2, sbn_dtype ydt, int64_t ldy) {
+                                int n, int m, int form, sbn_dtype ydt, int64_t ldy) {
   const char* fn = "sbn_gemv_table_check";
   SBN_NONNULL(table);
   if (count < 1) return fail(SBN_ERR_SHAPE, "%s: count = %lld must be at least 1", fn, (long long)count);
+  if (form != SBN_FORM_PACKED && form != SBN_FORM_D2 && form != SBN_FORM_J6)
+    return fail(SBN_ERR_VALUE, "%s: unknown form %d", fn, form);
   // the activations are not part of the table: stand-ins that pass their checks
   alignas(16) static const int8_t xq_ok[16] = {};
   static const float sx_ok = 1.0f;
   for (int64_t b = 0; b < count; ++b) {
     const sbn_gemv_entry& e = table[b];
-    const sbn_status st_b =
-        d2 ? check_d2_args(fn, xq_ok, &sx_ok, T, K, e.codes, e.s_w, R, e.Y, ydt, ldy)
-           : check_matmul_args(fn, xq_ok, &sx_ok, T, K, e.codes, n < m ? e.meta : nullptr, e.s_w, R, n, m, e.Y, ydt,
-                               ldy);
+    sbn_status st_b =
+        form != SBN_FORM_PACKED
+            ? check_d2_args(fn, xq_ok, &sx_ok, T, K, e.codes, e.s_w, R, e.Y, ydt, ldy)
+            : check_matmul_args(fn, xq_ok, &sx_ok, T, K, e.codes, n < m ? e.meta : nullptr, e.s_w, R, n, m, e.Y, ydt,
+                                ldy);
+    if (st_b == SBN_OK && form == SBN_FORM_J6) {       // the h plane travels in meta
+      if (!e.meta) st_b = fail(SBN_ERR_NULL, "%s: argument 'meta' (the h plane) is NULL", fn);
+      else if (!aligned16(e.meta)) st_b = fail(SBN_ERR_ALIGN, "%s: 'meta' (the h plane) is not 16-byte aligned", fn);
+    }
     if (st_b != SBN_OK) {
       char msg[512];
       snprintf(msg, sizeof(msg), "%s (entry %lld)", sbn_last_error(), (long long)b);

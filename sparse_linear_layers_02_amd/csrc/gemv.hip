@@ -262,6 +262,16 @@ __device__ inline void lds_read4(v4i& x0, v4i& x1, v4i& x2, v4i& x3, uint32_t a0
       : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
       : "memory");
 }
+__device__ inline void lds_read3(v4i& x0, v4i& x1, v4i& x2, uint32_t a0, uint32_t a1, uint32_t a2) {
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_b128 %2, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2)
+      : "v"(a0), "v"(a1), "v"(a2)
+      : "memory");
+}
 __device__ inline void lds_read5(v4i& x0, v4i& x1, v4i& x2, v4i& x3, v4i& x4, uint32_t a0, uint32_t a1,
                                  uint32_t a2, uint32_t a3, uint32_t a4) {
   asm volatile(
@@ -620,6 +630,107 @@ struct Dec2 {
     for (int s = 0; s < 16; ++s) {
       const v4i a = (v4i){(int)(w[s] & MK), (int)((w[s] << 2) & MK), (int)((w[s] << 4) & MK), (int)((w[s] << 6) & MK)};
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bx[s], acc, 0, 0, 0);
+    }
+    return acc;
+  }
+};
+
+// Joint 2:4 code decoder, v_smfmac_i32_16x16x128_i8 with the lane mapping of
+// Dec24 (step s, lane group g: groups 64g + 8s .. 64g + 8s + 7 of the range,
+// 32 positions).  A group's 6-bit code is its nibble nib = i1 | i2 << 2 (the
+// positions of its two slots) and a 2-bit h; the nibble plane's 32-bit word
+// for those 8 groups is the instruction's index word as it stands, and the
+// slot values come from a 64-entry table of byte pairs (v1, v2 as 64 * w)
+// indexed by h | nib << 2, built in LDS by each block.  The table indices of
+// four groups are formed at once, one per byte, twice the index (the byte
+// offset of a 2-byte entry): h to bits 1-2, nib to bits 3-6.
+// Ring slot: 16 rows x 128 B of nibbles (chunk c of row r at c ^ (r & 7)),
+// then 16 rows x 64 B of h (chunk c of row r at c ^ ((r >> 2) & 3)); the h
+// word u of a row range holds groups 16u .. 16u + 15, group 16u + 8b + 2k + o
+// in byte k at bits 2(2b + o).
+struct Dec24j {
+  static constexpr int SLOT = 3072, NDMA = 3, LUT = 128, BPC = 4;   // 32.1 KB LDS per block
+  __host__ __device__ static int64_t meta_row(int64_t K) { return K / 16; }   // h plane (entry.meta)
+  __host__ __device__ static int64_t code_row(int64_t K) { return K / 8; }    // nibble plane (entry.codes)
+  int rowq[3], colq[3];
+  v4i blo[8], bhi[8];
+  __device__ inline void init(int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {                        // nibbles: chunk positions 64q + lane
+      const int sp = 64 * q + lane, rr = sp >> 3;
+      rowq[q] = rr;
+      colq[q] = 128 * wave + 16 * ((sp & 7) ^ (rr & 7));
+    }
+    const int rr = lane >> 2;                            // h: chunk positions lane
+    rowq[2] = rr;
+    colq[2] = 64 * wave + 16 * ((lane & 3) ^ ((rr >> 2) & 3));
+  }
+  __device__ inline void issue(uint8_t* dst, const uint8_t* hp, const uint8_t* np, int valid, int64_t K) {
+    const int rown = (int)(K / 8), rowh = (int)(K / 16);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = rowq[q] < valid ? rowq[q] : valid - 1;
+      g2lds16(np + r * rown + colq[q], dst + 1024 * q);
+    }
+    const int r = rowq[2] < valid ? rowq[2] : valid - 1;
+    g2lds16(hp + r * rowh + colq[2], dst + 2048);
+  }
+  __device__ inline void load_x(const int8_t* xrow, bool ok, int wave, int g) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int64_t lo = 1024 * wave + 256 * (g >> 1) + 32 * s + 16 * (g & 1);
+      blo[s] = ok ? *(const v4i*)(xrow + lo) : (v4i){0, 0, 0, 0};
+      bhi[s] = ok ? *(const v4i*)(xrow + lo + 512) : (v4i){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(blo[s]), "v"(bhi[s]));
+  }
+  // entry e = h | nib << 2: (v1, v2) as 64 * w; i1 != i2: the signs in h; i1 == i2:
+  // v1 = 0, +1, -1 for h = 0, 1, 3 and v2 = 0 (h = 2 is not a code: zeros)
+  __device__ inline void build_lut(uint8_t* lut, int tid) {
+    if (tid < 64) {
+      const uint32_t h = tid & 3, i1 = (tid >> 2) & 3, i2 = tid >> 4;
+      uint32_t v1, v2;
+      if (i1 != i2) {
+        v1 = (h & 1) ? 0xC0u : 0x40u;
+        v2 = (h & 2) ? 0xC0u : 0x40u;
+      } else {
+        v1 = h == 1 ? 0x40u : (h == 3 ? 0xC0u : 0u);
+        v2 = 0u;
+      }
+      *(uint16_t*)(lut + 2 * tid) = (uint16_t)(v1 | v2 << 8);
+    }
+  }
+  struct Frag {
+    v4i n0, n1, h;
+  };
+  __device__ inline Frag read(const uint8_t* slot, int rl, int g) const {
+    const uint32_t sn = lds_addr(slot + rl * 128);
+    const uint32_t sh = lds_addr(slot + 2048 + rl * 64) + 16 * (g ^ ((rl >> 2) & 3));
+    Frag f;
+    lds_read3(f.n0, f.n1, f.h, sn + 16 * ((2 * g) ^ (rl & 7)), sn + 16 * ((2 * g + 1) ^ (rl & 7)), sh);
+    return f;
+  }
+  __device__ inline v4i compute(const Frag& f, const uint8_t* lut) const {
+    const uint32_t nw[8] = {(uint32_t)f.n0[0], (uint32_t)f.n0[1], (uint32_t)f.n0[2], (uint32_t)f.n0[3],
+                            (uint32_t)f.n1[0], (uint32_t)f.n1[1], (uint32_t)f.n1[2], (uint32_t)f.n1[3]};
+    v4i acc = (v4i){0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t N = nw[s], Hw = (uint32_t)f.h[s >> 1];
+      const int fe = 2 * (s & 1);                      // h field of the even groups; fe + 1 of the odd ones
+      const uint32_t he = fe == 0 ? Hw << 1 : Hw >> 3, ho = fe == 0 ? Hw >> 1 : Hw >> 5;
+      const uint32_t E0 = ((N << 3) & 0x78787878u) | (he & 0x06060606u);   // groups 0, 2, 4, 6
+      const uint32_t E1 = ((N >> 1) & 0x78787878u) | (ho & 0x06060606u);   // groups 1, 3, 5, 7
+      v4i a;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = *(const uint16_t*)(lut + ((E0 >> (8 * k)) & 0xFFu));
+        const uint32_t hi = *(const uint16_t*)(lut + ((E1 >> (8 * k)) & 0xFFu));
+        a[k] = (int)(lo | hi << 16);
+      }
+      const v8i b = (v8i){blo[s][0], blo[s][1], blo[s][2], blo[s][3], bhi[s][0], bhi[s][1], bhi[s][2], bhi[s][3]};
+      acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, acc, (int)N, 0, 0);
     }
     return acc;
   }
@@ -1062,6 +1173,69 @@ hipError_t launch_repack_d2(const uint8_t* codes, const uint8_t* meta, int64_t R
     SBN_LAUNCH("repack_d2", repack_d2_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, st, codes, mp, R, K, n, cplane,
                (uint32_t*)d2);
   return hipGetLastError();
+}
+
+namespace {
+
+// 2:4 packed planes -> joint code planes: one thread per 16 groups (64
+// positions: 8 meta bytes, 8 code bytes -> 8 nibble bytes, one h word).
+__global__ __launch_bounds__(256) void repack_j6_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ meta, int64_t R, int64_t K,
+                                                        uint8_t* __restrict__ nib, uint8_t* __restrict__ hpl) {
+  const int64_t wpr = K / 64, total = R * wpr;
+  for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < total; gid += (int64_t)gridDim.x * 256) {
+    const int64_t r = gid / wpr, u = gid - r * wpr;
+    const uint64_t mw = *(const uint64_t*)(meta + r * (K / 8) + 8 * u);    // group g: bits 4g .. 4g + 3
+    const uint64_t cw = *(const uint64_t*)(codes + r * (K / 8) + 8 * u);   // group g: survivors at bits 4g, 4g + 2
+    uint64_t nibs = 0;
+    uint32_t hw = 0;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const uint32_t m4 = (uint32_t)(mw >> (4 * g)) & 15u;
+      const uint32_t c0 = (uint32_t)(cw >> (4 * g)) & 3u, c1 = (uint32_t)(cw >> (4 * g + 2)) & 3u;
+      const uint32_t p0 = m4 ? (uint32_t)__builtin_ctz(m4) : 0u, p1 = m4 ? 31u - (uint32_t)__builtin_clz(m4) : 0u;
+      uint32_t i1 = 0, i2 = 0, h = 0;
+      if (c0 && c1) {                                  // two nonzeros: their positions and signs
+        i1 = p0;
+        i2 = p1;
+        h = (c0 == 3u ? 1u : 0u) | (c1 == 3u ? 2u : 0u);
+      } else if (c0 || c1) {                           // one nonzero: its position twice, its code
+        i1 = i2 = c0 ? p0 : p1;
+        h = c0 ? c0 : c1;
+      }
+      nibs |= (uint64_t)(i1 | i2 << 2) << (4 * g);
+      const int b = g >> 3, k = (g & 7) >> 1, o = g & 1;
+      hw |= h << (8 * k + 2 * (2 * b + o));
+    }
+    *(uint64_t*)(nib + r * (K / 8) + 8 * u) = nibs;
+    *(uint32_t*)(hpl + r * (K / 16) + 4 * u) = hw;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_repack_j6(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, uint8_t* nib,
+                            uint8_t* hpl, hipStream_t st) {
+  const int64_t total = R * (K / 64);
+  const int64_t blocks = cdiv(total, 256) < 4096 ? cdiv(total, 256) : 4096;
+  SBN_LAUNCH("repack_j6", repack_j6_kernel, dim3((unsigned)blocks), dim3(256), 0, st, codes, meta, R, K, nib, hpl);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_j6_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const GvEntry* table,
+                                int64_t count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
+  if (!gemv_d2_table_shape_ok(K)) return hipErrorInvalidValue;
+  return launch_stream<Dec24j>("gemv_stream_j6", Xq, s_x, T, K, GemvTable{table}, count, R, ydt, ldy, st);
+}
+
+hipError_t launch_gemv_j6(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const uint8_t* nib,
+                          const uint8_t* hpl, const float* s_w, int64_t R, void* Y, sbn_dtype ydt, int64_t ldy,
+                          hipStream_t st) {
+  if (!gemv_d2_table_shape_ok(K)) return hipErrorInvalidValue;
+  GemvBatch P;
+  for (int b = 0; b < GV_MAX_BATCH; ++b)
+    P.e[b] = b == 0 ? GvEntry{nib, hpl, s_w, Y} : GvEntry{nullptr, nullptr, nullptr, nullptr};
+  return launch_stream<Dec24j>("gemv_stream_j6", Xq, s_x, T, K, P, 1, R, ydt, ldy, st);
 }
 
 bool gemv_d2_table_shape_ok(int64_t K) { return SBN_GV_STREAM && K % 1024 == 0 && K <= 4096; }

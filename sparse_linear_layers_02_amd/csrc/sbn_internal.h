@@ -152,6 +152,16 @@ hipError_t launch_gemv_table(const int8_t* Xq, const float* s_x, int64_t T, int6
                              int64_t count, int64_t R, int n, int m, sbn_dtype ydt, int64_t ldy, hipStream_t st);
 hipError_t launch_gemv_d2_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const GvEntry* table,
                                 int64_t count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st);
+// Joint 2:4 code: repack of 2:4 packed planes (K a multiple of 64), and the
+// streamed GEMV on it (one weight, or a device table: codes = nibble plane,
+// meta = h plane; K a multiple of 1024 up to 4096).
+hipError_t launch_repack_j6(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, uint8_t* nib,
+                            uint8_t* hpl, hipStream_t st);
+hipError_t launch_gemv_j6(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const uint8_t* nib,
+                          const uint8_t* hpl, const float* s_w, int64_t R, void* Y, sbn_dtype ydt, int64_t ldy,
+                          hipStream_t st);
+hipError_t launch_gemv_j6_table(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const GvEntry* table,
+                                int64_t count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st);
 // Decode plane: repack of the packed planes, and the GEMV over up to GV_MAX_BATCH planes.
 hipError_t launch_repack_d2(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, int n, int m,
                             uint8_t* d2, hipStream_t st);

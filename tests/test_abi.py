@@ -22,7 +22,7 @@ def L():
 
 def test_exports_every_header_symbol(L):
     names = sbn.header_symbols()
-    assert len(names) == 29
+    assert len(names) == 33
     for nm in names:
         assert hasattr(L, nm), nm
 
@@ -177,6 +177,35 @@ def test_gemv_table_validation(L):
     assert c(tab(good, (P, P, P, MIS)), 2, 4, 4096, 256, 2, 4, 0, 1, 256) == ALIGN      # Y
     assert c(tab(good), 1, 17, 4096, 256, 2, 4, 0, 1, 256) == SHAPE
     assert c(None, 1, 4, 4096, 256, 2, 4, 0, 1, 256) == NULL
+
+
+def test_joint_code_validation(L):
+    nb, hb = sbn.sbn_j6_bytes(4096, 4096)
+    assert (nb, hb) == (4096 * 4096 // 8, 4096 * 4096 // 16)
+    assert sbn.sbn_j6_bytes(3, 64) == (32, 16)                         # 24 and 12 rounded up to 16
+    with pytest.raises(sbn.SbnError):
+        sbn.sbn_j6_bytes(4, 100)
+    f = L.sbn_repack_j6
+    assert f(P, None, 16, 256, P2, P2, None) == NULL                   # meta is required (2:4 planes)
+    assert f(P, P, 16, 250, P2, P2, None) == SHAPE
+    assert f(P, P, 16, 256, P2, MIS, None) == ALIGN
+    g = L.sbn_ternary_gemv_j6
+    assert g(P, P, 17, 4096, P, P, P, 64, P, 1, 64, None) == SHAPE     # T > 16
+    assert g(P, P, 4, 2560, P, P, P, 64, P, 1, 64, None) == SHAPE      # K not a multiple of 1024
+    assert g(P, P, 4, 4096, P, None, P, 64, P, 1, 64, None) == NULL    # h plane
+    assert g(P, P, 4, 4096, P, MIS, P, 64, P, 1, 64, None) == ALIGN
+    assert g(P, P, 4, 4096, P, P, P, 64, P, 7, 64, None) == DTYPE
+    t = L.sbn_ternary_gemv_j6_table
+    assert t(P, P, 4, 4096, None, 3, 256, 1, 256, None) == NULL
+    assert t(P, P, 4, 5120, P, 3, 256, 1, 256, None) == SHAPE
+    assert t(P, P, 4, 4096, P, 0, 256, 1, 256, None) == SHAPE
+    c = L.sbn_gemv_table_check
+    tab = lambda *rows: (ctypes.c_void_p * (4 * len(rows)))(*[p for r in rows for p in r])
+    good = (P, P2, P, P2)
+    assert c(tab(good), 1, 4, 4096, 256, 2, 4, sbn.SBN_FORM_J6, 1, 256) == OK
+    assert c(tab(good, (P, None, P, P2)), 2, 4, 4096, 256, 2, 4, sbn.SBN_FORM_J6, 1, 256) == NULL   # no h plane
+    assert c(tab(good, (P, MIS, P, P2)), 2, 4, 4096, 256, 2, 4, sbn.SBN_FORM_J6, 1, 256) == ALIGN
+    assert c(tab(good), 1, 4, 4096, 256, 2, 4, 7, 1, 256) == VALUE                                  # unknown form
 
 
 def test_gemv_table_binding_checks_before_the_copy():
