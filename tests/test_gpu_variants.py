@@ -227,6 +227,7 @@ def test_forward_token_lengths(K):
 
 def test_forward_leading_dims_flags_and_outputs():
     check_forward(21, 96, 256, 6, 8, ldw=264, ldx=272, seed=3)
+    check_forward(19, 100, 192, 2, 4, ldw=200, ldx=208, seed=7)     # 2:4 with ragged rows, a 64-K tail step
     check_forward(21, 96, 256, 2, 4, flags=sbn.SBN_MASK_FROM_TERNARY, seed=4)
     check_forward(50, 520, 576, 2, 4, seed=5, ydt=sbn.SBN_BF16)
     check_forward(50, 520, 576, 6, 8, seed=6, ydt=sbn.SBN_F32)
