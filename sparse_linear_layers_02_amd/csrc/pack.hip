@@ -460,12 +460,13 @@ __device__ inline void mask_pack_body(
         code[p] = nz | ((nz & (w >> 15)) << 1);          // 00 = 0, 01 = +1, 11 = -1
       }
       // Survivors: the n largest of M distinct keys.  n = 1, 2, M - 2, M - 1 take
-      // a threshold from a min/max network (the largest two or the smallest two:
-      // from sorted pairs, the two extremes of a union of two sorted pairs are
-      // min(x1, y1) and min(max(x1, y1), min(x2, y2)), and likewise with max);
-      // other n count each key's rank.
+      // the one or two extreme keys from a min/max network (the largest two or
+      // the smallest two: from sorted pairs, the two extremes of a union of two
+      // sorted pairs are min(x1, y1) and min(max(x1, y1), min(x2, y2)), and
+      // likewise with max), which name the kept or dropped positions; other n
+      // count each key's rank.
       constexpr int mode = (n == 1 || n == 2) ? 1 : (n == M - 1 || n == M - 2) ? 2 : 0;
-      uint32_t thk = 0;
+      uint32_t e1x = 0, e2x = 0;
       if (mode != 0) {
         const bool big = mode == 1;                      // keep the largest (else drop the smallest)
         const bool two = big ? n == 2 : n == M - 2;
@@ -485,26 +486,44 @@ __device__ inline void mask_pack_body(
             e2[i] = big ? max(min(x1, y1), max(x2, y2)) : min(max(x1, y1), min(x2, y2));
           }
         }
-        thk = two ? e2[0] : e1[0];                       // n-th largest (big) / (M-n)-th smallest
+        e1x = e1[0];                                     // the largest (big) / smallest key
+        e2x = e2[0];                                     // the second largest / second smallest
       }
-      int slot = 0;
+      if (mode != 0) {
+        // the network's extreme keys name the positions directly (key & 7 = 7 - p):
+        // mode 1 keeps those positions, mode 2 drops them; the survivors' codes
+        // are the group's code word with the dropped 2-bit fields cut out (mode 2)
+        // or the kept fields picked (mode 1)
+        const bool two = mode == 1 ? n == 2 : n == M - 2;
+        const uint32_t pa = 7u - (e1x & 7u), pb = two ? 7u - (e2x & 7u) : pa;
+        const uint32_t lo = pa < pb ? pa : pb, hi = pa < pb ? pb : pa;
+        const uint32_t sel = (1u << pa) | (1u << pb);
+        uint32_t cg = 0;
 #pragma unroll
-      for (int p = 0; p < M; ++p) {
-        bool kp;
+        for (int p = 0; p < M; ++p) cg |= code[p] << (2 * p);
+        uint32_t packed;
         if (mode == 1) {
-          kp = key[p] >= thk;
-        } else if (mode == 2) {
-          kp = key[p] > thk;
+          packed = two ? ((cg >> (2 * lo)) & 3u) | (((cg >> (2 * hi)) & 3u) << 2) : (cg >> (2 * lo)) & 3u;
         } else {
+          packed = (cg & ((1u << (2 * hi)) - 1u)) | ((cg >> (2 * hi + 2)) << (2 * hi));    // cut field hi
+          if (two) packed = (packed & ((1u << (2 * lo)) - 1u)) | ((packed >> (2 * lo + 2)) << (2 * lo));   // then lo
+        }
+        const uint32_t keepg = mode == 1 ? sel : (((1u << M) - 1u) ^ sel);
+        keep |= keepg << (g * M);
+        cw |= (unsigned long long)packed << (2 * n * g);
+      } else {
+        int slot = 0;
+#pragma unroll
+        for (int p = 0; p < M; ++p) {
           int rank = 0;
 #pragma unroll
           for (int q = 0; q < M; ++q)
             if (q != p) rank += key[q] > key[p] ? 1 : 0;
-          kp = rank < n;
+          const bool kp = rank < n;
+          keep |= (kp ? 1u : 0u) << (g * M + p);
+          cw |= (unsigned long long)(kp ? code[p] : 0u) << (2 * (n * g + slot));
+          slot += kp ? 1 : 0;
         }
-        keep |= (kp ? 1u : 0u) << (g * M + p);
-        cw |= (unsigned long long)(kp ? code[p] : 0u) << (2 * (n * g + slot));
-        slot += kp ? 1 : 0;
       }
     }
     if (meta) *(uint32_t*)(meta + r * (K / 8) + ch * 4) = keep;
