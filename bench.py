@@ -264,9 +264,11 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
     from the library's events; (ii-a) the pool as separate calls, replayed as
     four HIP graphs on four streams so launch ramps overlap; (ii-b) the pool
     as batched calls of 64 weights that share the activations (one launch
-    each), replayed from a HIP graph; (ii-c) the pool as one table call (its
-    weights listed once in a device table: one launch), replayed from a HIP
-    graph.  GB/s = algorithmic bytes (packed W +
+    each), replayed from a HIP graph of PASSES passes over the pool; (ii-c)
+    the pool as one table call (its weights listed once in a device table:
+    one launch), replayed from a HIP graph of PASSES passes.  Every steady
+    mode replays its graphs untimed for 30 ms first (the clocks settle under
+    load) and times at least 10 ms.  GB/s = algorithmic bytes (packed W +
     Xq + s_x + Y + s_w per weight) / time."""
     import torch
     import sparse_linear_layers_02_amd as sbn
@@ -302,13 +304,24 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def replay_ms(graphs, streams, calls):
-        for g in graphs:
-            g.replay()
+        # untimed replays for at least 30 ms (clocks settle under load), then
+        # enough timed replays for at least 10 ms
+        t_warm = time.perf_counter()
+        n_warm = 0
+        while (time.perf_counter() - t_warm) * 1e3 < 30.0 or n_warm < 2:
+            for g, s_ in zip(graphs, streams):
+                with torch.cuda.stream(s_):
+                    g.replay()
+            for s_ in streams:
+                s_.synchronize()
+            n_warm += 1
+        per = (time.perf_counter() - t_warm) * 1e3 / n_warm
+        nrep = max(reps, int(10.0 / max(per, 1e-3)) + 1)
         torch.cuda.synchronize()
         e0.record()
         for s_ in streams:
             s_.wait_event(e0)
-        for _ in range(reps):
+        for _ in range(nrep):
             for g, s_ in zip(graphs, streams):
                 with torch.cuda.stream(s_):
                     g.replay()
@@ -316,7 +329,7 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
             torch.cuda.current_stream().wait_stream(s_)
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * calls)
+        return e0.elapsed_time(e1) / (nrep * calls)
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
@@ -332,14 +345,14 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
     graphs = [capture(lambda b=b: [call(i) for i in range(b, P, 4)]) for b in range(4)]
     ss_ms = replay_ms(graphs, streams, P)
     del graphs
-    # (ii-b) batched calls of B weights, one graph on one stream
-    gb = capture(lambda: [batched(b0) for b0 in range(0, P, B)])
-    bt_ms = replay_ms([gb], [streams[0]], P)
+    # (ii-b) batched calls of B weights, one graph of PASSES passes over the pool on one stream
+    gb = capture(lambda: [batched(b0) for _ in range(PASSES) for b0 in range(0, P, B)])
+    bt_ms = replay_ms([gb], [streams[0]], P * PASSES)
     del gb
-    # (ii-c) the pool as one table call (one launch), one graph on one stream
+    # (ii-c) the pool as one table call (one launch), one graph of PASSES passes on one stream
     tab = sbn.GemvTable(codes, metas, s_ws, wl.R, wl.K, n, m, T=T, Ys=Ys)
-    gt = capture(lambda: sbn.sbn_sparse_ternary_gemv_table(Xq, s_x, tab))
-    tb_ms = replay_ms([gt], [streams[0]], P)
+    gt = capture(lambda: [sbn.sbn_sparse_ternary_gemv_table(Xq, s_x, tab) for _ in range(PASSES)])
+    tb_ms = replay_ms([gt], [streams[0]], P * PASSES)
     del gt, tab
     frac = lambda ms_: round(algo / (ms_ * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
     gbps = lambda ms_: round(algo / (ms_ * 1e-3) / 1e9, 1)
@@ -350,9 +363,9 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
         "steady_separate_calls_4streams": {"us_per_weight": round(ss_ms * 1e3, 3), "GBps": gbps(ss_ms),
                                            "frac_hbm": frac(ss_ms)},
         f"steady_batched_{B}": {"us_per_weight": round(bt_ms * 1e3, 3), "GBps": gbps(bt_ms), "frac_hbm": frac(bt_ms),
-                                "launches_per_pool": P // B},
+                                "launches_per_pool": P // B, "pool_passes_per_graph": PASSES},
         f"steady_table_{P}": {"us_per_weight": round(tb_ms * 1e3, 3), "GBps": gbps(tb_ms), "frac_hbm": frac(tb_ms),
-                              "launches_per_pool": 1},
+                              "launches_per_pool": 1, "pool_passes_per_graph": PASSES},
     }
 
 
@@ -644,6 +657,7 @@ def cpu_baseline(wl, n, m, tokens, runs=3):
 # ---------------------------------------------------------------------- decode step
 POOL = 128                     # weights per pool (one table launch per pool)
 BATCH = 64                     # weights per by-value batched call (its maximum)
+PASSES = 4                     # passes over a pool per replayed graph in decode_gemv's steady modes
 
 
 def make_decode_step(T=1):
