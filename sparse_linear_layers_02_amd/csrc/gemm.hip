@@ -42,12 +42,18 @@
 //                 32*(l/16) + 4*(j/2) + idx_j (idx_j = bits 2j..2j+1 of the index
 //                 register); B lane l -> col l%16, bytes 0..15 = K[16*(l/16)..),
 //                 bytes 16..31 = K[64 + 16*(l/16)..); C as above.
+#include <cstdlib>
+#include <cstring>
+
 #include "sbn_decode.h"
 
 namespace sbn {
 namespace {
 
 constexpr int GT = 256;
+
+// row fragments of the expanded W: R rounded up to the square tile's 256 rows
+inline int64_t gemm_rb_dev(int64_t R) { return round_up(R, GEMM_TILE_R) / 16; }
 
 __device__ inline int8_t code_to_i8(uint32_t c) { return c == 1u ? (int8_t)1 : c == 3u ? (int8_t)-1 : (int8_t)0; }
 
@@ -539,6 +545,229 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------- GEMM, wide sparse tile
+// One block per compute unit, one wave per SIMD: block tile MI row fragments
+// (16*MI rows) x 256 tokens; wave w owns tokens 64w..64w+63 of it against all
+// MI row fragments (MI x 4 accumulator tiles: 4*MI accumulator registers per
+// lane).  A compute unit streams operands from L2 into LDS at about 23 bytes
+// per clock whatever the grid (measured; the 256 x 256 kernel's main loop runs
+// at exactly that rate with its matrix cores half idle), so this tile is
+// shaped for the fewest operand bytes per output: a K step of 16*MI x 256
+// outputs loads MI + NG + 32 KB (W fragments, their index blocks, X), against
+// 52 KB for 256 x 256 outputs.  It pays where the 256 x 256 grid ends in a
+// partial round: 6912 rows x 4096 tokens is 432 square tiles on 256 compute
+// units but 256 tiles of 432 x 256.  Two LDS stages of one K step: the next
+// step's loads fly while a step's matrix work runs.
+// A raw buffer resource over `bytes` bytes at `base` (reads past the end
+// return zero), and a 16-byte-per-lane load through it into LDS at `lds`
+// (wave-uniform) + 16 * lane: vector offset `voff`, uniform offset `soff`.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+template <int OUT, int MI>
+__global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
+    const uint8_t* __restrict__ Aw, const uint8_t* __restrict__ Ai, const uint8_t* __restrict__ Xt,
+    const float* __restrict__ s_x, const float* __restrict__ s_w, int64_t T, int64_t R, int64_t RB,
+    int64_t nks, int64_t KC, void* __restrict__ Y, int64_t ldy) {
+  static_assert(MI % 4 == 0, "tiles start on an index block");
+  constexpr int NG = MI / 4;                         // index blocks of the tile's row fragments
+  constexpr int NB = MI + NG + 32;                   // 1 KB blocks per K step: W, index words, X (16 x lo/hi)
+  constexpr int STAGE = NB * 1024;
+  static_assert(2 * STAGE + 1024 <= 160 * 1024, "LDS");
+  // two stage buffers as separate objects, each step's reads and fills naming
+  // them statically: the compiler then knows a step's LDS reads do not touch
+  // the buffer its global->LDS loads are filling, and does not wait for them
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm1[STAGE];
+  __shared__ float sxs[256];                         // the tile's activation scales
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  int64_t rtile, ttile;
+  tile_of_block(blockIdx.x, cdiv(RB, MI), cdiv(T, 256), rtile, ttile);
+  const int64_t rb0 = rtile * MI, tb0 = ttile * 16, tile_t = ttile * 256;
+  const int64_t g0 = rb0 / 4;                        // row fragment rb0 + i: index block g0 + i / 4, word i % 4
+  if (OUT != 0) sxs[tid] = tile_t + tid < T ? s_x[tile_t + tid] : 0.0f;
+
+  // Loads of one K step: wave w takes W fragments w, w+4, .. (MI / 4 slots),
+  // index blocks w and w+4 (the last wave's second slot loads block NG - 1
+  // again: same bytes to the same place) and X blocks w, w+4, .. (8 slots).
+  // The expanded W holds whole wide tiles of row fragments (the rows past R
+  // are never stored).  Buffer loads: one resource per operand, the slot's
+  // offset uniform, the lane's 16 bytes as the vector offset (every operand is
+  // below 2^31 bytes: the launcher checks).  Slot offsets are walked with
+  // opaque adds so the compiler keeps two registers per operand, not one per slot.
+  const uint32_t fa = (uint32_t)nks * 1024u;          // bytes per row fragment (and per index block) over all K steps
+  const int64_t RBw = round_up(RB, MI);               // row fragments of the expanded W
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(Aw, (uint32_t)(RBw * fa));
+  const __amdgpu_buffer_rsrc_t rI = make_rsrc(Ai, (uint32_t)((RBw / 4) * fa));
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(Xt, (uint32_t)(cdiv(T, 256) * 16 * KC * 1024));
+  const uint32_t voff = (uint32_t)lane * 16u;
+  const uint32_t offa0 = (uint32_t)(rb0 + wave) * fa, stepa = 4u * fa;
+  const int bi1 = wave + 4 < NG ? wave + 4 : NG - 1;
+  const uint32_t offi0 = (uint32_t)(g0 + wave) * fa, offi1 = (uint32_t)(g0 + bi1) * fa;
+  const uint32_t offx0 = (uint32_t)(((tb0 + wave / 2) * KC + wave % 2) * 1024), stepx = (uint32_t)(2 * KC * 1024);
+  auto load_stage = [&](uint8_t* d, int ks) {
+    const uint32_t k1 = (uint32_t)ks * 1024u;
+    uint32_t so = offa0 + k1;
+#pragma unroll
+    for (int q = 0; q < MI / 4; ++q) {
+      buf2lds16(rA, voff, so, d + (wave + 4 * q) * 1024);
+      so += stepa;
+      asm volatile("" : "+s"(so));
+    }
+    buf2lds16(rI, voff, offi0 + k1, d + (MI + wave) * 1024);
+    buf2lds16(rI, voff, offi1 + k1, d + (MI + bi1) * 1024);
+    so = offx0 + 2 * k1;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      buf2lds16(rX, voff, so, d + (MI + NG + wave + 4 * q) * 1024);
+      so += stepx;
+      asm volatile("" : "+s"(so));
+    }
+  };
+
+  v4i acc[MI][4];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+
+  // One K step from buffer buf: the wave's four X fragments, then the W
+  // fragments and index words two row fragments ahead of the matrix
+  // instructions that use them; the loads of K step `next` (if any) are
+  // issued after the first reads.
+  auto step = [&](const uint8_t* st, uint8_t* nst, int next) {
+    const uint8_t* xb = st + (MI + NG + 8 * wave) * 1024 + lane * 16;
+    const uint8_t* ab = st + lane * 16;
+    const uint8_t* ib = st + MI * 1024 + lane * 16;
+    v8i b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4i lo = *(const v4i*)(xb + (2 * j) * 1024), hi = *(const v4i*)(xb + (2 * j + 1) * 1024);
+      b[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    v4i a[MI], ixg[NG];                              // ixg[g]: index words of row fragments 4g .. 4g+3
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = *(const v4i*)(ab + i * 1024);
+    ixg[0] = *(const v4i*)ib;
+    sched_fence();
+    if (next >= 0) load_stage(nst, next);
+    sched_fence();
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      // W fragment i + 2 and, two fragments before a group starts, that group's index words
+      const bool ra2 = i + 2 < MI, rg = (i + 2) % 4 == 0 && i + 2 < MI;
+      if (ra2) a[i + 2] = *(const v4i*)(ab + (i + 2) * 1024);
+      if (rg) ixg[(i + 2) / 4] = *(const v4i*)(ib + ((i + 2) / 4) * 1024);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a[i], b[j], acc[i][j], ixg[i / 4][i % 4], 0, 0);
+      if (rg) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // the LDS reads above
+      else if (ra2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                // then fragment i's matrix instructions
+    }
+    sched_fence();
+  };
+
+  // stage s lives in buffer s % 2; step s loads stage s + 1 into the other
+  // buffer (freed by the barrier after step s - 1)
+  auto finish = [&]() {
+    wait_vmem();                                     // this wave's loads of the next stage have landed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    pp_barrier();                                    // every wave is done with this buffer; the next stage is whole
+  };
+  load_stage(sm0, 0);
+  wait_vmem();
+  pp_barrier();
+  const int ns = (int)nks;                           // 32-bit step counts keep the loop control scalar
+  int s = 0;
+  for (; s + 1 < ns; s += 2) {
+    step(sm0, sm1, s + 1);
+    finish();
+    step(sm1, sm0, s + 2 < ns ? s + 2 : -1);
+    finish();
+  }
+  if (s < ns) {
+    step(sm0, sm1, -1);
+    finish();
+  }
+
+  const float sw = OUT != 0 ? *s_w : 0.0f;
+  if constexpr (OUT == 2) {
+    // bf16: a wave's 64 tokens x 16*MI rows, 32 tokens at a time, through LDS
+    // as [token][row] (the stage buffers are free: every wave passed the last
+    // barrier), then stored as whole token rows of 32*MI contiguous bytes,
+    // 16 per lane, non-temporal so the output streams past L2
+    constexpr int PITCH = MI * 32 + 16;              // bytes per staged token row (16 bytes of padding)
+    constexpr int NV = MI * 2;                       // 16-byte pieces per token row
+    static_assert(2 * 32 * PITCH <= STAGE, "epilogue staging fits");
+    uint8_t* stg = (wave < 2 ? sm0 : sm1) + (wave & 1) * 32 * PITCH;
+    const int64_t r0 = rb0 * 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * h + jj;
+        const float sc = sw * sxs[16 * (4 * wave + j) + (lane & 15)];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const v4i c = acc[i][j];
+          uint2 v;
+          v.x = (uint32_t)f32_to_bf16_rne((float)c[0] * sc) | ((uint32_t)f32_to_bf16_rne((float)c[1] * sc) << 16);
+          v.y = (uint32_t)f32_to_bf16_rne((float)c[2] * sc) | ((uint32_t)f32_to_bf16_rne((float)c[3] * sc) << 16);
+          *(uint2*)(stg + (16 * jj + (lane & 15)) * PITCH + (16 * i + 4 * (lane >> 4)) * 2) = v;
+        }
+      }
+      const int64_t t0 = tile_t + 16 * (4 * wave + 2 * h);
+#pragma unroll 4
+      for (int k = 0; k < 32 * NV / 64; ++k) {
+        const int p = lane + 64 * k, tl = p / NV, pc = p - tl * NV;
+        const v4i v = *(const v4i*)(stg + tl * PITCH + pc * 16);
+        const int64_t t = t0 + tl, r = r0 + 8 * pc;
+        if (t >= T || r >= R) continue;
+        uint16_t* y = (uint16_t*)Y + t * ldy + r;
+        if (r + 7 < R) {
+          __builtin_nontemporal_store(v, (v4i*)y);
+        } else {
+          const uint32_t w[4] = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+          for (int e = 0; e < 8 && r + e < R; ++e) y[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this half's reads are done before the next half's writes
+    }
+    return;
+  }
+  // int32 / float32: lane holds rows r..r+3 of token t of each accumulator tile, 16 bytes
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tl = 16 * (4 * wave + j) + (lane & 15);
+    const int64_t t = tile_t + tl;
+    if (t >= T) continue;
+    const float sc = OUT != 0 ? sw * sxs[tl] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int64_t r = (rb0 + i) * 16 + 4 * (lane >> 4);
+      if (r >= R) continue;
+      const v4i c = acc[i][j];
+      if (OUT == 0) {
+        int* y = (int*)Y + t * ldy + r;
+        if (r + 3 < R) *(v4i*)y = c;
+        else for (int v = 0; v < 4 && r + v < R; ++v) y[v] = c[v];
+      } else {
+        float* y = (float*)Y + t * ldy + r;
+        const v4f o = (v4f){(float)c[0] * sc, (float)c[1] * sc, (float)c[2] * sc, (float)c[3] * sc};
+        if (r + 3 < R) *(v4f*)y = o;
+        else for (int v = 0; v < 4 && r + v < R; ++v) y[v] = o[v];
+      }
+    }
+  }
+}
+
 template <bool SPARSE, int MJ, bool DX>
 hipError_t launch_gemm_mj(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
                           const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y,
@@ -582,10 +811,57 @@ int gemm_mj(bool sparse, int64_t T, int64_t R) {
   return best;
 }
 
+constexpr int WIDE_MI = 28;                          // 448-row tiles
+
+template <int MI>
+hipError_t launch_gemm_wide(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
+                            const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y, sbn_dtype ydt,
+                            int64_t ldy, hipStream_t st) {
+  const int64_t RB = gemm_rb_dev(R);
+  const dim3 grid((unsigned)(cdiv(RB, MI) * cdiv(T, 256))), block(256);
+  const int64_t KC = 2 * KBn;
+  if (ydt == SBN_I32_ACC)
+    SBN_LAUNCH("gemm_smfmac_wide", (gemm_wide_kernel<0, MI>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, RB, KBn,
+               KC, Y, ldy);
+  else if (ydt == SBN_F32)
+    SBN_LAUNCH("gemm_smfmac_wide", (gemm_wide_kernel<1, MI>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, RB, KBn,
+               KC, Y, ldy);
+  else
+    SBN_LAUNCH("gemm_smfmac_wide", (gemm_wide_kernel<2, MI>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, RB, KBn,
+               KC, Y, ldy);
+  return hipGetLastError();
+}
+
+// The wide tile where its grid finishes first: both kernels' main loops run
+// at the compute unit's operand streaming rate, so a grid costs its rounds
+// of 256 tiles times the bytes one tile loads per K step (KB: 256 x 256: 52,
+// 256 x 128: 36, 256 x 64: 28; wide: MI + NG + 32).  SBN_GEMM_TILE=wide or
+// =square in the environment overrides the choice (read per call; operands
+// of 2^31 bytes or more always take the square tiles).
+bool gemm_use_wide(int64_t T, int64_t R, int64_t KBn) {
+  // the wide kernel addresses each operand with 32-bit offsets
+  const int64_t lim = (int64_t)1 << 31;
+  if (round_up(gemm_rb_dev(R), WIDE_MI) * KBn * 1024 >= lim || cdiv(T, 256) * 16 * KBn * 2048 >= lim) return false;
+  if (const char* e = getenv("SBN_GEMM_TILE")) {
+    if (!strcmp(e, "wide")) return true;
+    if (!strcmp(e, "square")) return false;
+  }
+  const int mj = gemm_mj(true, T, R);
+  const double sq_bytes = mj == 4 ? 52.0 : mj == 2 ? 36.0 : 28.0;
+  const double sq = (double)cdiv(cdiv(T, 64 * mj) * cdiv(R, GEMM_TILE_R), 256) * sq_bytes;
+  const double wide_bytes = WIDE_MI + WIDE_MI / 4 + 32;
+  const double wd = (double)cdiv(cdiv(gemm_rb_dev(R), WIDE_MI) * cdiv(T, 256), 256) * wide_bytes;
+  return wd < 0.9 * sq;
+}
+
 template <bool SPARSE, bool DX>
 hipError_t launch_gemm_t(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
                          const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y,
                          sbn_dtype ydt, int64_t ldy, hipStream_t st) {
+  if constexpr (SPARSE && !DX) {
+    if (gemm_use_wide(T, R, KBn))
+      return launch_gemm_wide<WIDE_MI>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+  }
   const int mj = gemm_mj(SPARSE, T, R);
   if (mj == 4) return launch_gemm_mj<SPARSE, 4, DX>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
   if (mj == 2) return launch_gemm_mj<SPARSE, 2, DX>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
@@ -610,8 +886,11 @@ static GemmWs gemm_ws(int64_t T, int64_t R, int64_t K, int n, int m) {
   GemmWs g;
   g.w_bytes = align256((size_t)(RB * KBn * 2048));                 // sparse: vals use the first half
   if (gemm_uses_smfmac(n, m)) {
-    g.w_bytes = align256((size_t)(RB * KBn * 1024));
-    g.i_bytes = align256((size_t)(RB * KBn * 256));
+    // whole wide tiles of row fragments (the wide kernel reads them; the
+    // expansion writes the first RB)
+    const int64_t RBw = round_up(RB, WIDE_MI);
+    g.w_bytes = align256((size_t)(RBw * KBn * 1024));
+    g.i_bytes = align256((size_t)(RBw * KBn * 256));
   } else {
     g.i_bytes = 0;
   }
