@@ -123,6 +123,18 @@ def traffic_from_profiles(kernel, workload):
     return float(m.group(1))
 
 
+GEMM_KERNELS = ("gemm_smfmac_wide", "gemm_smfmac", "gemm_mfma")
+
+
+def gemm_name_in(prof, default="gemm_smfmac"):
+    """The forward GEMM kernel a profile saw (the library picks the wide or the
+    square sparse tiles, or the dense kernel, by shape)."""
+    for nm in GEMM_KERNELS:
+        if nm in prof:
+            return nm
+    return default
+
+
 def gemm_roofline(gname, T, R, K, n, m, k_ms, launches, traffic):
     """Roofline of the forward GEMM: `achieved` counts the products the method
     performs, 2*T*R*K*n/m int8 ops (pruned positions are not work), against
@@ -891,8 +903,8 @@ def main():
         wl = WORKLOADS[a.workload]
         n, m = wl.nm[0]
         step = make_forward_step(wl, n, m, with_backward=(a.workload == "train"))
-        gname = "gemm_smfmac" if (n <= 2) else "gemm_mfma"
         ms, wall, prof, mode = time_steps(step, a.steps, a.warmup)          # every stage, for stages_us
+        gname = gemm_name_in(prof, "gemm_smfmac" if n <= 2 else "gemm_mfma")
         prof_g = profile_pass(step, a.steps, gname)                          # the roofline kernel alone
         nprod = 3 if a.workload == "train" else 1
         ops = 2 * wl.T * wl.R * wl.K * nprod
@@ -944,10 +956,9 @@ def main():
             codes, meta, s_w = sbn.sbn_mask_ternarize_pack(W, n, m)
             Xq, s_x = sbn.sbn_act_quant(bf16_dev(wl.activations(0)))
             Y = torch.empty((wl.T, wl.R), dtype=torch.bfloat16, device="cuda")
-            gname = "gemm_smfmac" if sbn_uses_smfmac(n, m) else "gemm_mfma"
             ms, wall, prof, mode = time_steps(
-                lambda: sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, wl.R, n, m, Y=Y), a.steps, a.warmup,
-                kernel=gname)
+                lambda: sbn.sbn_sparse_ternary_gemm(Xq, s_x, codes, meta, s_w, wl.R, n, m, Y=Y), a.steps, a.warmup)
+            gname = gemm_name_in(prof, "gemm_smfmac" if sbn_uses_smfmac(n, m) else "gemm_mfma")
             g_ms, g_cnt = kernel_avg_ms(prof, gname)
             ops = 2 * wl.T * wl.R * wl.K
             ws_p = torch.empty(max(sbn.sbn_workspace_bytes(sbn.SBN_OP_PACK, 0, wl.R, wl.K, n, m), 256),

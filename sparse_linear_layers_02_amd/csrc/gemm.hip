@@ -498,8 +498,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(
       for (int i = 0; i < MI; ++i) {
         const v4i c = acc[i][j];
         uint2 v;
-        v.x = (uint32_t)f32_to_bf16_rne((float)c[0] * sc) | ((uint32_t)f32_to_bf16_rne((float)c[1] * sc) << 16);
-        v.y = (uint32_t)f32_to_bf16_rne((float)c[2] * sc) | ((uint32_t)f32_to_bf16_rne((float)c[3] * sc) << 16);
+        v.x = pack_bf16x2((float)c[0] * sc, (float)c[1] * sc);
+        v.y = pack_bf16x2((float)c[2] * sc, (float)c[3] * sc);
         *(uint2*)(st + (16 * j + (lane & 15)) * PITCH + (16 * i + 4 * (lane >> 4)) * 2) = v;
       }
     }
@@ -718,8 +718,8 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
         for (int i = 0; i < MI; ++i) {
           const v4i c = acc[i][j];
           uint2 v;
-          v.x = (uint32_t)f32_to_bf16_rne((float)c[0] * sc) | ((uint32_t)f32_to_bf16_rne((float)c[1] * sc) << 16);
-          v.y = (uint32_t)f32_to_bf16_rne((float)c[2] * sc) | ((uint32_t)f32_to_bf16_rne((float)c[3] * sc) << 16);
+          v.x = pack_bf16x2((float)c[0] * sc, (float)c[1] * sc);
+          v.y = pack_bf16x2((float)c[2] * sc, (float)c[3] * sc);
           *(uint2*)(stg + (16 * jj + (lane & 15)) * PITCH + (16 * i + 4 * (lane >> 4)) * 2) = v;
         }
       }

@@ -27,6 +27,14 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 __device__ inline float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+// two float32 -> packed bf16 bits (a in the low half), rounded to nearest even
+// by the conversion instruction (one instruction per pair; equal to
+// f32_to_bf16_rne on finite inputs)
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t h = (bf16x2_t){(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
 
 // Write-once global stores through the vector path.
 __device__ inline void store_u16x4(uint16_t* p, uint16_t a, uint16_t b, uint16_t c, uint16_t d) {
