@@ -552,8 +552,29 @@ __device__ inline void mask_pack_body(
 // stores) with U loads in flight.  Per group the second-largest of four
 // distinct keys (|w| << 2 | 3 - p) is the threshold; the two keys at or above
 // it survive and their codes are picked with find-first-bit.
-__device__ inline void group24(uint32_t w01, uint32_t w23, uint32_t thr, int tmask, uint32_t& keep4,
-                               uint32_t& code4) {
+template <bool TMASK>
+__device__ inline void group24(uint32_t w01, uint32_t w23, uint32_t thr, uint32_t& keep4, uint32_t& code4) {
+  if constexpr (!TMASK) {
+    // keys |w| << 2 | (3 - p), built in place from the two words (distinct; a
+    // tie in |w| goes to the lower position); the largest and second largest
+    // key name the survivors through their low two bits
+    const uint32_t k0 = ((w01 << 2) & 0x1FFFCu) | 3u, k1 = ((w01 >> 14) & 0x1FFFCu) | 2u;
+    const uint32_t k2 = ((w23 << 2) & 0x1FFFCu) | 1u, k3 = (w23 >> 14) & 0x1FFFCu;
+    const uint32_t hi01 = max(k0, k1), lo01 = min(k0, k1), hi23 = max(k2, k3), lo23 = min(k2, k3);
+    const uint32_t ka = max(hi01, hi23), kb = max(min(hi01, hi23), max(lo01, lo23));
+    const uint32_t ta = ka & 3u, tb = kb & 3u;                 // 3 - position
+    keep4 = (8u >> ta) | (8u >> tb);
+    // a survivor's code: nonzero where |w| > thr, i.e. key > thr << 2 | 3; its
+    // sign is bit 8p + 7 of the four high bytes gathered by one permute
+    const uint32_t thr4 = (thr << 2) | 3u;
+    const uint32_t sg = __builtin_amdgcn_perm(w23, w01, 0x07050301u);
+    const uint32_t na = ka > thr4 ? 1u : 0u, nb = kb > thr4 ? 1u : 0u;
+    const uint32_t sa = (sg << (8u * ta)) >> 31, sb = (sg << (8u * tb)) >> 31;
+    const uint32_t ca = na | ((na & sa) << 1), cb = nb | ((nb & sb) << 1);
+    code4 = ta > tb ? (ca | (cb << 2)) : (cb | (ca << 2));   // the lower position first
+    return;
+  }
+  constexpr int tmask = 1;                       // keys from the ternary magnitude (|q| in {0, 1})
   const uint32_t w[4] = {w01 & 0xFFFFu, w01 >> 16, w23 & 0xFFFFu, w23 >> 16};
   uint32_t k[4], code8 = 0;
 #pragma unroll
@@ -572,22 +593,13 @@ __device__ inline void group24(uint32_t w01, uint32_t w23, uint32_t thr, int tma
   code4 = ((code8 >> (2 * p0)) & 3u) | (((code8 >> (2 * p1)) & 3u) << 2);
 }
 
-template <bool FLAT>
-__device__ inline void mask_pack24_body(
-    int64_t blk, int64_t nblk, const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ meta, float* __restrict__ s_w_ptr,
-    const unsigned char* __restrict__ ws, int64_t nb, int tmask) {
-  const int64_t kc = K / 8, total = R * kc;
+template <bool FLAT, bool TMASK>
+__device__ inline void mask_pack24_loop(int64_t blk, int64_t nblk, const uint16_t* __restrict__ W, int64_t K,
+                                        int64_t ldw, int64_t total, uint8_t* __restrict__ codes,
+                                        uint8_t* __restrict__ meta, uint32_t thr, int64_t base, uint4 (&v)[U]) {
+  const int64_t kc = K / 8;
   const int64_t step = nblk * PT * U;
-  int64_t base = blk * PT * U + threadIdx.x;
-  uint4 v[U], nx[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {                  // first loads fly while the scale is formed
-    const int64_t c = base + (int64_t)u * PT;
-    v[u] = c < total ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
-  }
-  const float h = 0.5f * scale_from_partials(ws, nb, R * K, s_w_ptr, blk == 0);
-  const uint32_t thr = __float_as_uint(h) >> 16;
+  uint4 nx[U];
   for (; base < total; base += step) {
     if (base + step < total) {                   // next chunks load while these are packed
 #pragma unroll
@@ -601,8 +613,8 @@ __device__ inline void mask_pack24_body(
       const int64_t c = base + (int64_t)u * PT;
       if (c < total) {
         uint32_t k0, c0, k1, c1;
-        group24(v[u].x, v[u].y, thr, tmask, k0, c0);
-        group24(v[u].z, v[u].w, thr, tmask, k1, c1);
+        group24<TMASK>(v[u].x, v[u].y, thr, k0, c0);
+        group24<TMASK>(v[u].z, v[u].w, thr, k1, c1);
         meta[c] = (uint8_t)(k0 | (k1 << 4));
         codes[c] = (uint8_t)(c0 | (c1 << 4));
       }
@@ -610,6 +622,25 @@ __device__ inline void mask_pack24_body(
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = nx[u];
   }
+}
+
+template <bool FLAT>
+__device__ inline void mask_pack24_body(
+    int64_t blk, int64_t nblk, const uint16_t* __restrict__ W, int64_t R, int64_t K, int64_t ldw,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ meta, float* __restrict__ s_w_ptr,
+    const unsigned char* __restrict__ ws, int64_t nb, int tmask) {
+  const int64_t kc = K / 8, total = R * kc;
+  const int64_t base = blk * PT * U + threadIdx.x;
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {                  // first loads fly while the scale is formed
+    const int64_t c = base + (int64_t)u * PT;
+    v[u] = c < total ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
+  }
+  const float h = 0.5f * scale_from_partials(ws, nb, R * K, s_w_ptr, blk == 0);
+  const uint32_t thr = __float_as_uint(h) >> 16;
+  if (tmask) mask_pack24_loop<FLAT, true>(blk, nblk, W, K, ldw, total, codes, meta, thr, base, v);
+  else mask_pack24_loop<FLAT, false>(blk, nblk, W, K, ldw, total, codes, meta, thr, base, v);
 }
 
 struct MaskPackArgs {
