@@ -274,29 +274,27 @@ __device__ inline void abs_sum_body(int64_t blk, int64_t nb, const uint16_t* __r
   constexpr int64_t STEP = (int64_t)PT1 * U1;
   uint4 v[U1], nx[U1];
   float4 g[U1][2], ng[U1][2];
-  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  // Every load is issued (past the block's end it rereads the block's last
+  // chunk, and that copy is zeroed before use): with no load under a divergent
+  // branch the wait before the sums covers only the chunks being summed, not
+  // the next ones in flight.
   int64_t base = c0 + tid;
 #pragma unroll
   for (int u = 0; u < U1; ++u) {
-    const int64_t c = base + (int64_t)u * PT1;
-    v[u] = c < c1 ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
-    if (UPD) {
-      g[u][0] = g[u][1] = z4;
-      if (c < c1) grad_at<FLAT>(G, c, kc, ldg, g[u][0], g[u][1]);
-    }
+    const int64_t c = min(base + (int64_t)u * PT1, c1 - 1);
+    v[u] = chunk_at<FLAT>(W, c, kc, ldw);
+    if (UPD) grad_at<FLAT>(G, c, kc, ldg, g[u][0], g[u][1]);
   }
   for (; base < c1; base += STEP) {
-    if (base + STEP < c1) {                      // next chunks load while these are summed
 #pragma unroll
-      for (int u = 0; u < U1; ++u) {
-        const int64_t c = base + STEP + (int64_t)u * PT1;
-        nx[u] = c < c1 ? chunk_at<FLAT>(W, c, kc, ldw) : make_uint4(0, 0, 0, 0);
-        if (UPD) {
-          ng[u][0] = ng[u][1] = z4;
-          if (c < c1) grad_at<FLAT>(G, c, kc, ldg, ng[u][0], ng[u][1]);
-        }
-      }
+    for (int u = 0; u < U1; ++u) {               // next chunks load while these are summed
+      const int64_t c = min(base + STEP + (int64_t)u * PT1, c1 - 1);
+      nx[u] = chunk_at<FLAT>(W, c, kc, ldw);
+      if (UPD) grad_at<FLAT>(G, c, kc, ldg, ng[u][0], ng[u][1]);
     }
+#pragma unroll
+    for (int u = 0; u < U1; ++u)
+      if (base + (int64_t)u * PT1 >= c1) v[u] = make_uint4(0, 0, 0, 0);
     if (UPD) {
 #pragma unroll
       for (int u = 0; u < U1; ++u) {
@@ -311,18 +309,39 @@ __device__ inline void abs_sum_body(int64_t blk, int64_t nb, const uint16_t* __r
             dst = (uint16_t*)W + r * ldw + (c - r * kc) * 8;
           }
           *(uint4*)dst = v[u];
-        } else {
-          v[u] = make_uint4(0, 0, 0, 0);
         }
       }
     }
+    // Fast path: every magnitude is summed, and one max and one min over the
+    // step tell whether any nonzero one lies outside the window (m - 1 wraps
+    // zero to the top, so zeros never count as too small); if one does, the
+    // step is summed again with the out-of-window values left to the bins
+    // (rare).
+    // The two bf16 magnitudes of a word are tested side by side as 16-bit lanes.
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     double acc = 0.0;
-    bool ok = true;
+    u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+    const u16x2 one = {1, 1};
 #pragma unroll
-    for (int u = 0; u < U1; ++u)
-      acc += pair_abs(v[u].x, ok) + pair_abs(v[u].y, ok) + pair_abs(v[u].z, ok) + pair_abs(v[u].w, ok);
-    if (!ok) {
+    for (int u = 0; u < U1; ++u) {
+      const uint32_t q[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t m = q[j] & 0x7FFF7FFFu;
+        const u16x2 m2 = __builtin_bit_cast(u16x2, m);
+        mx = __builtin_elementwise_max(mx, m2);
+        mn = __builtin_elementwise_min(mn, m2 - one);
+        acc += (double)__uint_as_float(m << 16) + (double)__uint_as_float(m & 0xFFFF0000u);
+      }
+    }
+    const uint32_t mxs = max((uint32_t)mx.x, (uint32_t)mx.y), mns = min((uint32_t)mn.x, (uint32_t)mn.y);
+    if (mxs >= (E_HI << 7) || mns < (E_LO << 7) - 1u) {
       any_slow = 1;
+      bool ok = true;
+      acc = 0.0;
+#pragma unroll
+      for (int u = 0; u < U1; ++u)
+        acc += pair_abs(v[u].x, ok) + pair_abs(v[u].y, ok) + pair_abs(v[u].z, ok) + pair_abs(v[u].w, ok);
 #pragma unroll
       for (int u = 0; u < U1; ++u) {
         pair_slow(v[u].x, bins);
