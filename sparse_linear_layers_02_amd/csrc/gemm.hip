@@ -568,11 +568,23 @@ __device__ inline void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
-template <int OUT, int MI>
+// DX: X straight from row-major Xq [T][K] (K a multiple of 64) instead of the
+// tiled copy.  A K step of one token is then one 128-byte line, and the stage
+// holds the tile's 256 lines as [token][8 x 16 bytes], the 16-byte pieces of
+// token t's line permuted by xswz(t % 16): a load instruction fetches eight
+// whole lines (lane l: line l/8, slot l%8 takes piece (l%8) ^ xswz), and the
+// fragment reads (lane: token n of 16, pieces g and g+4) fall on distinct
+// banks in every group of 8 and of 16 lanes.  Tokens past T and the bytes
+// past the end of Xq read as zero through the buffer resource's bound (the
+// whole offset travels in the vector operand, which the bound checks); a last
+// half step's upper pieces read the next row, against zero weights.
+__device__ inline uint32_t xswz(uint32_t n) { return (n ^ (n >> 3)) & 7u; }
+
+template <int OUT, int MI, bool DX>
 __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     const uint8_t* __restrict__ Aw, const uint8_t* __restrict__ Ai, const uint8_t* __restrict__ Xt,
     const float* __restrict__ s_x, const float* __restrict__ s_w, int64_t T, int64_t R, int64_t RB,
-    int64_t nks, int64_t KC, void* __restrict__ Y, int64_t ldy) {
+    int64_t nks, int64_t KC, int64_t K, void* __restrict__ Y, int64_t ldy) {
   static_assert(MI % 4 == 0, "tiles start on an index block");
   constexpr int NG = MI / 4;                         // index blocks of the tile's row fragments
   constexpr int NB = MI + NG + 32;                   // 1 KB blocks per K step: W, index words, X (16 x lo/hi)
@@ -605,12 +617,21 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
   const int64_t RBw = round_up(RB, MI);               // row fragments of the expanded W
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(Aw, (uint32_t)(RBw * fa));
   const __amdgpu_buffer_rsrc_t rI = make_rsrc(Ai, (uint32_t)((RBw / 4) * fa));
-  const __amdgpu_buffer_rsrc_t rX = make_rsrc(Xt, (uint32_t)(cdiv(T, 256) * 16 * KC * 1024));
+  const __amdgpu_buffer_rsrc_t rX =
+      make_rsrc(Xt, DX ? (uint32_t)(T * K) : (uint32_t)(cdiv(T, 256) * 16 * KC * 1024));
   const uint32_t voff = (uint32_t)lane * 16u;
+  // DX: lane's line (token tile_t + 8 * wave + lane / 8 in slot 0; each later
+  // slot 32 tokens on) and its piece
+  const uint32_t xl = (uint32_t)(8 * wave + (lane >> 3));
+  const uint32_t voffx = DX ? (uint32_t)((tile_t + xl) * K) + 16u * ((uint32_t)(lane & 7) ^ xswz(xl & 15u)) : voff;
+  // DX: the lane's fragment-read offset in the stage's X lines (token 64 * wave + lane % 16, piece lane / 16)
+  const uint32_t xlane = (uint32_t)((64 * wave + (lane & 15)) * 128) +
+                         16u * ((uint32_t)(lane >> 4) ^ xswz((uint32_t)(lane & 15)));
   const uint32_t offa0 = (uint32_t)(rb0 + wave) * fa, stepa = 4u * fa;
   const int bi1 = wave + 4 < NG ? wave + 4 : NG - 1;
   const uint32_t offi0 = (uint32_t)(g0 + wave) * fa, offi1 = (uint32_t)(g0 + bi1) * fa;
-  const uint32_t offx0 = (uint32_t)(((tb0 + wave / 2) * KC + wave % 2) * 1024), stepx = (uint32_t)(2 * KC * 1024);
+  const uint32_t offx0 = DX ? 0u : (uint32_t)(((tb0 + wave / 2) * KC + wave % 2) * 1024);
+  const uint32_t stepx = DX ? (uint32_t)(32 * K) : (uint32_t)(2 * KC * 1024);
   auto load_stage = [&](uint8_t* d, int ks) {
     const uint32_t k1 = (uint32_t)ks * 1024u;
     uint32_t so = offa0 + k1;
@@ -622,12 +643,22 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
     }
     buf2lds16(rI, voff, offi0 + k1, d + (MI + wave) * 1024);
     buf2lds16(rI, voff, offi1 + k1, d + (MI + bi1) * 1024);
-    so = offx0 + 2 * k1;
+    if constexpr (DX) {
+      // the whole offset in the vector operand, so the resource's bound checks all of it
+      uint32_t vo = voffx + (uint32_t)ks * 128u;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      buf2lds16(rX, voff, so, d + (MI + NG + wave + 4 * q) * 1024);
-      so += stepx;
-      asm volatile("" : "+s"(so));
+      for (int q = 0; q < 8; ++q) {
+        buf2lds16(rX, vo, 0u, d + (MI + NG + wave + 4 * q) * 1024);
+        vo += stepx;
+      }
+    } else {
+      so = offx0 + 2 * k1;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        buf2lds16(rX, voff, so, d + (MI + NG + wave + 4 * q) * 1024);
+        so += stepx;
+        asm volatile("" : "+s"(so));
+      }
     }
   };
 
@@ -642,14 +673,31 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
   // instructions that use them; the loads of K step `next` (if any) are
   // issued after the first reads.
   auto step = [&](const uint8_t* st, uint8_t* nst, int next) {
-    const uint8_t* xb = st + (MI + NG + 8 * wave) * 1024 + lane * 16;
     const uint8_t* ab = st + lane * 16;
     const uint8_t* ib = st + MI * 1024 + lane * 16;
     v8i b[4];
+    if constexpr (DX) {
+      // token 64 * wave + 16 * j + n (n = lane % 16): pieces g and g + 4 (g =
+      // lane / 16); lines start on 128 bytes, so piece g + 4's slot is piece
+      // g's with bit 6 flipped.  The lane's offset is rebuilt every step (an
+      // opaque copy) rather than kept per stage buffer and half.
+      uint32_t xo = xlane;
+      asm volatile("" : "+v"(xo));
+      const uint8_t* xr = st + (MI + NG) * 1024;
+      const uint8_t* xlo = xr + xo;
+      const uint8_t* xhi = xr + (xo ^ 64u);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4i lo = *(const v4i*)(xb + (2 * j) * 1024), hi = *(const v4i*)(xb + (2 * j + 1) * 1024);
-      b[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      for (int j = 0; j < 4; ++j) {
+        const v4i lo = *(const v4i*)(xlo + j * 2048), hi = *(const v4i*)(xhi + j * 2048);
+        b[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    } else {
+      const uint8_t* xb = st + (MI + NG + 8 * wave) * 1024 + lane * 16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v4i lo = *(const v4i*)(xb + (2 * j) * 1024), hi = *(const v4i*)(xb + (2 * j + 1) * 1024);
+        b[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
     }
     v4i a[MI], ixg[NG];                              // ixg[g]: index words of row fragments 4g .. 4g+3
 #pragma unroll
@@ -813,7 +861,7 @@ int gemm_mj(bool sparse, int64_t T, int64_t R) {
 
 constexpr int WIDE_MI = 28;                          // 448-row tiles
 
-template <int MI>
+template <int MI, bool DX>
 hipError_t launch_gemm_wide(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
                             const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y, sbn_dtype ydt,
                             int64_t ldy, hipStream_t st) {
@@ -821,14 +869,14 @@ hipError_t launch_gemm_wide(const uint8_t* Aw, const uint8_t* Ai, const uint8_t*
   const dim3 grid((unsigned)(cdiv(RB, MI) * cdiv(T, 256))), block(256);
   const int64_t KC = 2 * KBn;
   if (ydt == SBN_I32_ACC)
-    SBN_LAUNCH("gemm_smfmac_wide", (gemm_wide_kernel<0, MI>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, RB, KBn,
-               KC, Y, ldy);
+    SBN_LAUNCH("gemm_smfmac_wide", (gemm_wide_kernel<0, MI, DX>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, RB,
+               KBn, KC, K, Y, ldy);
   else if (ydt == SBN_F32)
-    SBN_LAUNCH("gemm_smfmac_wide", (gemm_wide_kernel<1, MI>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, RB, KBn,
-               KC, Y, ldy);
+    SBN_LAUNCH("gemm_smfmac_wide", (gemm_wide_kernel<1, MI, DX>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, RB,
+               KBn, KC, K, Y, ldy);
   else
-    SBN_LAUNCH("gemm_smfmac_wide", (gemm_wide_kernel<2, MI>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, RB, KBn,
-               KC, Y, ldy);
+    SBN_LAUNCH("gemm_smfmac_wide", (gemm_wide_kernel<2, MI, DX>), grid, block, 0, st, Aw, Ai, Xt, s_x, s_w, T, R, RB,
+               KBn, KC, K, Y, ldy);
   return hipGetLastError();
 }
 
@@ -858,9 +906,9 @@ template <bool SPARSE, bool DX>
 hipError_t launch_gemm_t(const uint8_t* Aw, const uint8_t* Ai, const uint8_t* Xt, const float* s_x,
                          const float* s_w, int64_t T, int64_t K, int64_t R, int64_t KBn, void* Y,
                          sbn_dtype ydt, int64_t ldy, hipStream_t st) {
-  if constexpr (SPARSE && !DX) {
+  if constexpr (SPARSE) {
     if (gemm_use_wide(T, R, KBn))
-      return launch_gemm_wide<WIDE_MI>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
+      return launch_gemm_wide<WIDE_MI, DX>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
   }
   const int mj = gemm_mj(SPARSE, T, R);
   if (mj == 4) return launch_gemm_mj<SPARSE, 4, DX>(Aw, Ai, Xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
@@ -906,8 +954,9 @@ size_t gemm_ws_bytes(int64_t T, int64_t R, int64_t K, int n, int m) {
 // The GEMM call in parts: the layout launch expands W into `w` (expand_w),
 // beside it tiles X into `xt` when the GEMM follows (run_gemm); without the
 // expansion (a prepared weight in `w`) the GEMM reads X straight from Xq: no
-// layout launch runs then, while the main loop is 5-10% faster on the tiled
-// copy, which otherwise rides beside the expansion almost for free.
+// layout launch runs then, while the main loop is faster on the tiled copy
+// (about 4% for the wide tile, 5-10% for the square ones), which otherwise
+// rides beside the expansion for about 1.4 us at the prefill shape.
 static hipError_t gemm_parts(const int8_t* Xq, const float* s_x, int64_t T, int64_t K, const uint8_t* codes,
                              const uint8_t* meta, const float* s_w, int64_t R, int n, int m, void* Y, sbn_dtype ydt,
                              int64_t ldy, uint8_t* w, uint8_t* xt, bool expand_w, bool run_gemm, hipStream_t st) {
