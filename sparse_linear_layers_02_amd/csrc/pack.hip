@@ -251,6 +251,49 @@ __device__ inline void grad_at(const float* __restrict__ G, int64_t c, int64_t k
   g1 = p[1];
 }
 
+// The exact sum of the magnitudes of one step's chunks in units of 2^-39.
+// Fast path: every magnitude is summed, and one max and one min over the
+// step tell whether any nonzero one lies outside the window (m - 1 wraps
+// zero to the top, so zeros never count as too small); if one does, the step
+// is summed again with the out-of-window values left to the bins (rare).  The
+// two bf16 magnitudes of a word are tested side by side as 16-bit lanes.
+template <int N>
+__device__ inline unsigned long long step_abs_sum(const uint4 (&cv)[N], unsigned long long* bins, int* any_slow) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  double acc = 0.0;
+  u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+  const u16x2 one = {1, 1};
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const uint32_t q[4] = {cv[u].x, cv[u].y, cv[u].z, cv[u].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t m = q[j] & 0x7FFF7FFFu;
+      const u16x2 m2 = __builtin_bit_cast(u16x2, m);
+      mx = __builtin_elementwise_max(mx, m2);
+      mn = __builtin_elementwise_min(mn, m2 - one);
+      acc += (double)__uint_as_float(m << 16) + (double)__uint_as_float(m & 0xFFFF0000u);
+    }
+  }
+  const uint32_t mxs = max((uint32_t)mx.x, (uint32_t)mx.y), mns = min((uint32_t)mn.x, (uint32_t)mn.y);
+  if (mxs >= (E_HI << 7) || mns < (E_LO << 7) - 1u) {
+    *any_slow = 1;
+    bool ok = true;
+    acc = 0.0;
+#pragma unroll
+    for (int u = 0; u < N; ++u)
+      acc += pair_abs(cv[u].x, ok) + pair_abs(cv[u].y, ok) + pair_abs(cv[u].z, ok) + pair_abs(cv[u].w, ok);
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      pair_slow(cv[u].x, bins);
+      pair_slow(cv[u].y, bins);
+      pair_slow(cv[u].z, bins);
+      pair_slow(cv[u].w, bins);
+    }
+  }
+  return (unsigned long long)(acc * FAST_SCALE);   // exact integer < 2^53
+}
+
 // UPD: the optimizer step -- chunk c of W is first updated in place with the
 // gradient chunk of G (row stride ldg), nlr = -lr; the sum is of the new values.
 // Pass 1 as block `blk` of `nb` (the body of abs_sum_kernel and of the fused
@@ -312,45 +355,7 @@ __device__ inline void abs_sum_body(int64_t blk, int64_t nb, const uint16_t* __r
         }
       }
     }
-    // Fast path: every magnitude is summed, and one max and one min over the
-    // step tell whether any nonzero one lies outside the window (m - 1 wraps
-    // zero to the top, so zeros never count as too small); if one does, the
-    // step is summed again with the out-of-window values left to the bins
-    // (rare).
-    // The two bf16 magnitudes of a word are tested side by side as 16-bit lanes.
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    double acc = 0.0;
-    u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
-    const u16x2 one = {1, 1};
-#pragma unroll
-    for (int u = 0; u < U1; ++u) {
-      const uint32_t q[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t m = q[j] & 0x7FFF7FFFu;
-        const u16x2 m2 = __builtin_bit_cast(u16x2, m);
-        mx = __builtin_elementwise_max(mx, m2);
-        mn = __builtin_elementwise_min(mn, m2 - one);
-        acc += (double)__uint_as_float(m << 16) + (double)__uint_as_float(m & 0xFFFF0000u);
-      }
-    }
-    const uint32_t mxs = max((uint32_t)mx.x, (uint32_t)mx.y), mns = min((uint32_t)mn.x, (uint32_t)mn.y);
-    if (mxs >= (E_HI << 7) || mns < (E_LO << 7) - 1u) {
-      any_slow = 1;
-      bool ok = true;
-      acc = 0.0;
-#pragma unroll
-      for (int u = 0; u < U1; ++u)
-        acc += pair_abs(v[u].x, ok) + pair_abs(v[u].y, ok) + pair_abs(v[u].z, ok) + pair_abs(v[u].w, ok);
-#pragma unroll
-      for (int u = 0; u < U1; ++u) {
-        pair_slow(v[u].x, bins);
-        pair_slow(v[u].y, bins);
-        pair_slow(v[u].z, bins);
-        pair_slow(v[u].w, bins);
-      }
-    }
-    acc_i += (unsigned long long)(acc * FAST_SCALE);   // exact integer < 2^53
+    acc_i += step_abs_sum(v, bins, &any_slow);
 #pragma unroll
     for (int u = 0; u < U1; ++u) {
       v[u] = nx[u];
