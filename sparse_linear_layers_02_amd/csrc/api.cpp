@@ -559,9 +559,19 @@ sbn_status sbn_forward(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, con
   SBN_TRY(check_finite(fn, "W", W, R, K, ldw, 2, st));
   SBN_TRY(check_finite(fn, "X", X, T, K, ldx, 2, st));
   uint8_t* mp = n == m ? nullptr : meta;
-  hipError_t e = launch_pack_quant(W, R, K, ldw, n, m, codes, mp, s_w, ws, flags, X, T, ldx, Xq, s_x, st);
-  if (e == hipSuccess)
-    e = launch_gemm(Xq, s_x, T, K, codes, mp, s_w, R, n, m, Y, ydt, ldy, (uint8_t*)ws + pack_b, st);
+  hipError_t e;
+  if (forward_writes_operand(T, R, K, n, m, flags)) {
+    // three launches: pass 2 also writes the GEMM's weight operand (into the
+    // GEMM part of ws, laid out as a prepared weight), and the GEMM reads it
+    uint8_t* op = (uint8_t*)ws + pack_b;
+    e = launch_pack_quant_operand(W, R, K, ldw, codes, mp, s_w, ws, X, T, ldx, Xq, s_x, op,
+                                  (uint32_t*)(op + gemm_operand_idx_offset(R, K, n, m)), st);
+    if (e == hipSuccess) e = launch_gemm_prepared(Xq, s_x, T, K, op, s_w, R, n, m, Y, ydt, ldy, nullptr, st);
+  } else {
+    e = launch_pack_quant(W, R, K, ldw, n, m, codes, mp, s_w, ws, flags, X, T, ldx, Xq, s_x, st);
+    if (e == hipSuccess)
+      e = launch_gemm(Xq, s_x, T, K, codes, mp, s_w, R, n, m, Y, ydt, ldy, (uint8_t*)ws + pack_b, st);
+  }
   return hip_result(e, st, fn);
 }
 

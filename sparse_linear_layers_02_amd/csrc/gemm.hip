@@ -1005,6 +1005,15 @@ static hipError_t gemm_parts(const int8_t* Xq, const float* s_x, int64_t T, int6
             : launch_gemm_t<false, false>(w, nullptr, xt, s_x, s_w, T, K, R, KBn, Y, ydt, ldy, st);
 }
 
+// The one-call forward writes the GEMM's weight operand from pass 2 of the pack
+// (and skips the layout launch) where the GEMM then runs on the wide tiles:
+// 2:4 without flags; the wide kernel reads the activations in place.
+bool forward_writes_operand(int64_t T, int64_t R, int64_t K, int n, int m, uint32_t flags) {
+  return n == 2 && m == 4 && flags == 0 && gemm_use_wide(T, R, cdiv(K, (int64_t)128));
+}
+
+size_t gemm_operand_idx_offset(int64_t R, int64_t K, int n, int m) { return gemm_ws(1, R, K, n, m).w_bytes; }
+
 size_t gemm_weight_bytes(int64_t R, int64_t K, int n, int m) {
   const GemmWs g = gemm_ws(1, R, K, n, m);
   return g.w_bytes + g.i_bytes;

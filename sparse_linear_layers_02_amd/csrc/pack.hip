@@ -42,6 +42,7 @@
 #include <mutex>
 
 #include "act_quant.h"
+#include "sbn_decode.h"
 
 namespace sbn {
 namespace {
@@ -718,6 +719,83 @@ __global__ __launch_bounds__(PT) void mask_pack_quant_kernel(const MaskPackArgs 
   }
 }
 
+// Pass 2 at 2:4 for the one-call forward whose GEMM reads a prepared weight
+// operand: besides the planes it writes the structured-sparse operand of the
+// matrix instruction (16 int8 values and one word of 2-bit indices per lane
+// and 128-K step), decoded from the planes' words by the same routine as the
+// layout launch's expansion, so that launch does not run.  Block (g, kq): the
+// 64 rows of index block g (row fragments 4g .. 4g+3, one per wave) over the
+// K steps [OP_KQ kq, OP_KQ kq + OP_KQ); lane l of wave q owns row
+// 16 (4g + q) + l % 16 and positions 32 (l / 16) .. +32 of each step, i.e.
+// its own lane of the operand fragment: a wave stores one whole 1 KB fragment
+// per step, and the four waves fill each 16-byte unit of the index block.
+constexpr int OP_KQ = 5;                             // K steps per block
+struct OperandArgs {
+  uint8_t* vals;                                     // [RB][KBn][64][16 B]
+  uint32_t* idx;                                     // [RB/4][KBn][64][4]
+  int64_t RB, KBn, nkq;
+};
+
+__device__ inline void mask_pack24_operand_body(int64_t blk, const MaskPackArgs& a, const OperandArgs& o) {
+  const int64_t g = blk / o.nkq, kq = blk - g * o.nkq;
+  const int q = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t rb = 4 * g + q, r = rb * 16 + (l & 15);
+  const int64_t K = a.K, rowb = K / 8;
+  const int64_t kb0 = kq * OP_KQ, kb1 = min(kb0 + (int64_t)OP_KQ, o.KBn);
+  const bool rowin = r < a.R;
+  const uint16_t* wrow = a.W + (rowin ? r : 0) * a.ldw;
+  // The 64 bytes of W of step kb (always loaded: a row past R or positions past
+  // K read the row's start instead, and that copy is not used).
+  auto load = [&](int64_t kb, uint4 (&d)[4]) {
+    const int64_t k0 = kb * 128 + 32 * (l >> 4);
+    const uint4* src = (const uint4*)(wrow + (rowin && k0 < K ? k0 : 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = src[i];
+  };
+  uint4 v[4], nv[4];
+  load(kb0, v);                                      // the first loads fly while the scale is formed
+  const float h = 0.5f * scale_from_partials(a.ws, a.nb, a.R * K, a.s_w, blk == 0);
+  const uint32_t thr = __float_as_uint(h) >> 16;
+  for (int64_t kb = kb0; kb < kb1; ++kb) {
+    load(kb + 1 < kb1 ? kb + 1 : kb, nv);
+    const int64_t k0 = kb * 128 + 32 * (l >> 4);
+    const bool in = rowin && k0 < K;
+    uint32_t mb = 0, cb = 0;                         // the planes' words of these 32 positions
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {                    // chunk c: positions 8c .. 8c+7, two groups
+      uint32_t k0c, c0c, k1c, c1c;
+      group24<false>(v[c].x, v[c].y, thr, k0c, c0c);
+      group24<false>(v[c].z, v[c].w, thr, k1c, c1c);
+      mb |= (k0c | (k1c << 4)) << (8 * c);
+      cb |= (c0c | (c1c << 4)) << (8 * c);
+    }
+    v4i av = (v4i){0, 0, 0, 0};
+    int ix = 0x44444444;                             // (0,1) in every half: harmless with zero values
+    if (in) {
+      *(uint32_t*)(a.meta + r * rowb + k0 / 8) = mb;
+      *(uint32_t*)(a.codes + r * rowb + k0 / 8) = cb;
+      decode24(mb, cb, av, ix);
+    }
+    *(v4i*)(o.vals + ((rb * o.KBn + kb) * 64 + l) * 16) = av;
+    o.idx[((g * o.KBn + kb) * 64 + l) * 4 + q] = (uint32_t)ix;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = nv[i];
+  }
+}
+
+// Blocks [0, nop) pack W and write the operand, blocks [nop, nop + T) quantize one token each.
+template <int CH>
+__global__ __launch_bounds__(PT) void mask_pack_quant_operand_kernel(const MaskPackArgs a, const OperandArgs o,
+                                                                     int64_t nop, const QuantArgs qa) {
+  const int64_t b = blockIdx.x;
+  if (b < nop) {
+    mask_pack24_operand_body(b, a, o);
+  } else {
+    __shared__ uint32_t qred[PT / 64];
+    act_quant_token<CH>(true, b - nop, threadIdx.x, qred, qa.X, qa.K, qa.ldx, qa.Xq, qa.s_x);
+  }
+}
+
 }  // namespace
 
 PackPlan pack_plan(int64_t R, int64_t K) {
@@ -837,6 +915,40 @@ hipError_t launch_pack_quant(const uint16_t* W, int64_t R, int64_t K, int64_t ld
   if (kind == 0) SBN_MPQ(0);
   else SBN_MPQ(1);
 #undef SBN_MPQ
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_quant_operand(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, uint8_t* codes,
+                                     uint8_t* meta, float* s_w, void* ws, const uint16_t* X, int64_t T, int64_t ldx,
+                                     int8_t* Xq, float* s_x, uint8_t* vals, uint32_t* idx, hipStream_t st) {
+  const PackPlan p = pack_plan(R, K);
+  if (ldw == K)
+    SBN_LAUNCH("abs_sum", (abs_sum_kernel<true, false>), dim3((unsigned)p.nblocks), dim3(PT1), 0, st, W, R, K, ldw,
+               p.chunks_per_block, (unsigned char*)ws, nullptr, 0, 0.0f);
+  else
+    SBN_LAUNCH("abs_sum", (abs_sum_kernel<false, false>), dim3((unsigned)p.nblocks), dim3(PT1), 0, st, W, R, K, ldw,
+               p.chunks_per_block, (unsigned char*)ws, nullptr, 0, 0.0f);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MaskPackArgs a = {};
+  a.W = W; a.R = R; a.K = K; a.ldw = ldw; a.n = 2;
+  a.codes = codes; a.meta = meta; a.s_w = s_w;
+  a.ws = (const unsigned char*)ws; a.nb = p.nblocks;
+  a.tmask = 0;
+  OperandArgs o;
+  o.vals = vals;
+  o.idx = idx;
+  o.RB = round_up(R, (int64_t)GEMM_TILE_R) / 16;
+  o.KBn = cdiv(K, (int64_t)128);
+  o.nkq = cdiv(o.KBn, (int64_t)OP_KQ);
+  const int64_t nop = (o.RB / 4) * o.nkq;
+  const QuantArgs q{X, T, K, ldx, Xq, s_x};
+  const dim3 grid((unsigned)(nop + T)), block(PT);
+  const int ch = act_quant_ch(K);
+  if (ch == 1) SBN_LAUNCH("mask_pack_quant", mask_pack_quant_operand_kernel<1>, grid, block, 0, st, a, o, nop, q);
+  else if (ch == 2) SBN_LAUNCH("mask_pack_quant", mask_pack_quant_operand_kernel<2>, grid, block, 0, st, a, o, nop, q);
+  else if (ch == 4) SBN_LAUNCH("mask_pack_quant", mask_pack_quant_operand_kernel<4>, grid, block, 0, st, a, o, nop, q);
+  else SBN_LAUNCH("mask_pack_quant", mask_pack_quant_operand_kernel<0>, grid, block, 0, st, a, o, nop, q);
   return hipGetLastError();
 }
 

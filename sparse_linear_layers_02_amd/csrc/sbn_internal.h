@@ -135,6 +135,15 @@ hipError_t launch_act_quant(const uint16_t* X, int64_t T, int64_t K, int64_t ldx
 hipError_t launch_pack_quant(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, int n, int m,
                              uint8_t* codes, uint8_t* meta, float* s_w, void* ws, uint32_t flags,
                              const uint16_t* X, int64_t T, int64_t ldx, int8_t* Xq, float* s_x, hipStream_t st);
+// The one-call forward at 2:4 on the wide GEMM tiles: pass 2 of the pack also
+// writes the GEMM's weight operand in the prepared-weight layout (values, then
+// the index words at gemm_operand_idx_offset), and the GEMM on it reads the
+// activations in place, so no layout launch runs.
+bool forward_writes_operand(int64_t T, int64_t R, int64_t K, int n, int m, uint32_t flags);
+size_t gemm_operand_idx_offset(int64_t R, int64_t K, int n, int m);
+hipError_t launch_pack_quant_operand(const uint16_t* W, int64_t R, int64_t K, int64_t ldw, uint8_t* codes,
+                                     uint8_t* meta, float* s_w, void* ws, const uint16_t* X, int64_t T, int64_t ldx,
+                                     int8_t* Xq, float* s_x, uint8_t* vals, uint32_t* idx, hipStream_t st);
 // The weight operand of the GEMM expanded once (for weights used by many calls),
 // and the GEMM on it (the activations are tiled into ws, gemm_x_bytes).
 hipError_t launch_prepare_gemm_weight(const uint8_t* codes, const uint8_t* meta, int64_t R, int64_t K, int n, int m,

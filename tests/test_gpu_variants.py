@@ -233,6 +233,40 @@ def test_forward_leading_dims_flags_and_outputs():
     check_forward(50, 520, 576, 6, 8, seed=6, ydt=sbn.SBN_F32)
 
 
+@pytest.mark.parametrize("ydt", [sbn.SBN_I32_ACC, sbn.SBN_BF16])
+@pytest.mark.parametrize("T,R,K,ldw,ldx", [(300, 520, 576, None, None), (17, 33, 128, None, None),
+                                           (40, 100, 64, None, None), (257, 1000, 1152, 1160, 1168),
+                                           (64, 7000, 384, None, None)])
+def test_forward_wide_writes_operand(monkeypatch, T, R, K, ldw, ldx, ydt):
+    """2:4 one-call forward with the wide GEMM tiles forced on: the pack's second
+    pass writes the GEMM's weight operand and the GEMM reads the activations in
+    place (no layout launch); planes, scales, Xq, s_x and Y against the oracle
+    on ragged rows and tokens, a 64-position K tail, K = 64 and padded rows."""
+    monkeypatch.setenv("SBN_GEMM_TILE", "wide")
+    print(f"forward, operand from pass 2: T={T} R={R} K={K} ldw={ldw} ldx={ldx} ydt={ydt}", flush=True)
+    check_forward(T, R, K, 2, 4, ldw=ldw, ldx=ldx, seed=T + K, ydt=ydt)
+
+
+def test_forward_launches_at_prefill_size():
+    """The prefill-shape forward runs three kernels (pass 1, pass 2 with the
+    quantizer and the weight operand, the wide GEMM); a 6:8 forward keeps the
+    layout launch."""
+    import torch
+    wl = WORKLOADS["prefill"]
+    W, X = dev_bf16(wl.weights(0)), dev_bf16(wl.activations(0))
+    sbn.sbn_forward(W, X, 2, 4)
+    torch.cuda.synchronize()
+    for nm, want in (((2, 4), {"abs_sum", "mask_pack_quant", "gemm_smfmac_wide"}),
+                     ((6, 8), {"abs_sum", "mask_pack", "act_quant", "layout_dense", "gemm_mfma"})):
+        sbn.sbn_profile_reset()
+        sbn.sbn_profile_enable(True)
+        sbn.sbn_forward(W, X, *nm)
+        torch.cuda.synchronize()
+        sbn.sbn_profile_enable(False)
+        got = set(sbn.sbn_profile_dump())
+        assert got == want, f"{nm}: kernels {sorted(got)}"
+
+
 def test_forward_prefill_size_equals_separate_calls():
     import torch
     wl = WORKLOADS["prefill"]
