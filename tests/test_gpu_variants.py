@@ -236,12 +236,13 @@ def test_forward_leading_dims_flags_and_outputs():
 @pytest.mark.parametrize("ydt", [sbn.SBN_I32_ACC, sbn.SBN_BF16])
 @pytest.mark.parametrize("T,R,K,ldw,ldx", [(300, 520, 576, None, None), (17, 33, 128, None, None),
                                            (40, 100, 64, None, None), (257, 1000, 1152, 1160, 1168),
-                                           (64, 7000, 384, None, None)])
+                                           (64, 7000, 384, None, None), (33, 264, 1664, None, None)])
 def test_forward_wide_writes_operand(monkeypatch, T, R, K, ldw, ldx, ydt):
     """2:4 one-call forward with the wide GEMM tiles forced on: the pack's second
     pass writes the GEMM's weight operand and the GEMM reads the activations in
     place (no layout launch); planes, scales, Xq, s_x and Y against the oracle
-    on ragged rows and tokens, a 64-position K tail, K = 64 and padded rows."""
+    on ragged rows and tokens, a 64-position K tail, K = 64, padded rows and
+    13 K steps split unevenly over two blocks."""
     monkeypatch.setenv("SBN_GEMM_TILE", "wide")
     print(f"forward, operand from pass 2: T={T} R={R} K={K} ldw={ldw} ldx={ldx} ydt={ydt}", flush=True)
     check_forward(T, R, K, 2, 4, ldw=ldw, ldx=ldx, seed=T + K, ydt=ydt)
