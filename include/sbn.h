@@ -275,7 +275,10 @@ sbn_status sbn_sparse_ternary_gemm_prepared(const int8_t* Xq, const float* s_x, 
  * with the same results, bit for bit.  The activation quantizer does not
  * depend on the weight pack; at 2:4 it runs in the same launch as the pack's
  * second pass, side by side, which saves a launch and overlaps their memory
- * traffic.
+ * traffic.  At 2:4 with flags 0, where the GEMM takes its wide tiles, that
+ * second pass also writes the GEMM's weight operand into ws and the GEMM
+ * reads it and Xq in place (three launches, no layout launch); ws keeps the
+ * same size either way.
  *
  *   W      [R x K] bf16, row stride ldw >= K                    (in)
  *   X      [T x K] bf16, row stride ldx >= K                    (in)
