@@ -747,33 +747,30 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
 
   const float sw = OUT != 0 ? *s_w : 0.0f;
   if constexpr (OUT == 2) {
-    // bf16: a wave's 64 tokens x 16*MI rows, 32 tokens at a time, through LDS
-    // as [token][row] (the stage buffers are free: every wave passed the last
-    // barrier), then stored as whole token rows of 32*MI contiguous bytes,
-    // 16 per lane, non-temporal so the output streams past L2
+    // bf16: a wave's 64 tokens x 16*MI rows, one 16-token fragment at a time,
+    // through LDS as [token][row] (the stage buffers are free: every wave
+    // passed the last barrier), then stored as whole token rows of 32*MI
+    // contiguous bytes, 16 per lane, non-temporal so the output streams past
+    // L2; the stores of one fragment fly while the next is converted
     constexpr int PITCH = MI * 32 + 16;              // bytes per staged token row (16 bytes of padding)
     constexpr int NV = MI * 2;                       // 16-byte pieces per token row
     static_assert(2 * 32 * PITCH <= STAGE, "epilogue staging fits");
     uint8_t* stg = (wave < 2 ? sm0 : sm1) + (wave & 1) * 32 * PITCH;
     const int64_t r0 = rb0 * 16;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int j = 0; j < 4; ++j) {
+      const float sc = sw * sxs[16 * (4 * wave + j) + (lane & 15)];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int j = 2 * h + jj;
-        const float sc = sw * sxs[16 * (4 * wave + j) + (lane & 15)];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const v4i c = acc[i][j];
-          uint2 v;
-          v.x = pack_bf16x2((float)c[0] * sc, (float)c[1] * sc);
-          v.y = pack_bf16x2((float)c[2] * sc, (float)c[3] * sc);
-          *(uint2*)(stg + (16 * jj + (lane & 15)) * PITCH + (16 * i + 4 * (lane >> 4)) * 2) = v;
-        }
+      for (int i = 0; i < MI; ++i) {
+        const v4i c = acc[i][j];
+        uint2 v;
+        v.x = pack_bf16x2((float)c[0] * sc, (float)c[1] * sc);
+        v.y = pack_bf16x2((float)c[2] * sc, (float)c[3] * sc);
+        *(uint2*)(stg + (lane & 15) * PITCH + (16 * i + 4 * (lane >> 4)) * 2) = v;
       }
-      const int64_t t0 = tile_t + 16 * (4 * wave + 2 * h);
-#pragma unroll 4
-      for (int k = 0; k < 32 * NV / 64; ++k) {
+      const int64_t t0 = tile_t + 16 * (4 * wave + j);
+#pragma unroll 2
+      for (int k = 0; k < 16 * NV / 64; ++k) {
         const int p = lane + 64 * k, tl = p / NV, pc = p - tl * NV;
         const v4i v = *(const v4i*)(stg + tl * PITCH + pc * 16);
         const int64_t t = t0 + tl, r = r0 + 8 * pc;
@@ -786,7 +783,7 @@ __global__ __launch_bounds__(256, 1) void gemm_wide_kernel(
           for (int e = 0; e < 8 && r + e < R; ++e) y[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
         }
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this half's reads are done before the next half's writes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this fragment's reads are done before the next one's writes
     }
     return;
   }
