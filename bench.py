@@ -1,6 +1,6 @@
 """Throughput of the Sparse-BitLinear hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--min-warmup-ms MS]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--min-warmup-ms MS] [--steps-per-graph S]
                     [--workload prefill|train|sweep|decode|speedup]
 
 A step is one pass of the hot path over one batch of synthetic input already
@@ -28,8 +28,10 @@ resident in HBM:
                      Cache); `value` is the 2:4 call's TOPS at T=4096.
 `value` is dense-equivalent int8 TOPS of the whole step (2*T*R*K per
 forward product; the train step counts its three products), timed over
---steps replays of the step captured as a HIP graph (the library only
-enqueues kernels on the caller's stream), after --warmup steps and untimed
+--steps steps replayed from HIP graphs of --steps-per-graph (4) steps each,
+the remainder as one-step replays (the library only enqueues kernels on the
+caller's stream, so a step captures cleanly; one replay's host cost then
+falls once per four steps), after --warmup steps and untimed
 replays up to --min-warmup-ms (100 ms) from the start of the warmup, so the
 part's clocks have settled.  One JSON line is printed.  The
 same line carries:
@@ -87,6 +89,8 @@ def parse():
                     help="after the warmup steps, replay the step untimed until this much time has passed "
                          "(the part's clocks need tens of ms under load to settle)")
     ap.add_argument("--workload", default="prefill", choices=["prefill", "train", "sweep", "decode", "speedup"])
+    ap.add_argument("--steps-per-graph", type=int, default=4,
+                    help="prefill/train: steps captured back to back in one replayed HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode GEMV measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -215,15 +219,18 @@ def capture_graph(step):
 MIN_WARMUP_MS = 100.0
 
 
-def time_steps(step, steps, warmup, kernel=None, use_graph=True):
+def time_steps(step, steps, warmup, kernel=None, use_graph=True, per_graph=1):
     """Timed region: `steps` steps between two synchronisations, replayed from
-    a HIP graph when possible, after `warmup` steps and untimed replays until
-    MIN_WARMUP_MS have passed (measured on this part: the decode step takes
-    290-320 us per step in its first 10 ms from idle and 262 us from about 25
-    ms on; the prefill step 100 us, then 95 us).  Then the same number of
-    eager steps with the library's HIP events around `kernel` (all kernels if
-    None) give its average launch duration.  Returns (ms_per_step, wall_s,
-    prof, mode)."""
+    HIP graphs when possible -- graphs of `per_graph` steps back to back (the
+    host's cost of one replay, a few us, then falls once per `per_graph`
+    steps, as it does for the layers of a model captured together), and the
+    last steps % per_graph as one-step replays, so exactly `steps` steps run --
+    after `warmup` steps and untimed replays until MIN_WARMUP_MS have passed
+    (measured on this part: the decode step takes 290-320 us per step in its
+    first 10 ms from idle and 262 us from about 25 ms on; the prefill step 100
+    us, then 95 us).  Then the same number of eager steps with the library's
+    HIP events around `kernel` (all kernels if None) give its average launch
+    duration.  Returns (ms_per_step, wall_s, prof, mode)."""
     import torch
     import sparse_linear_layers_02_amd as sbn
     t_warm = time.perf_counter()
@@ -232,8 +239,13 @@ def time_steps(step, steps, warmup, kernel=None, use_graph=True):
     torch.cuda.synchronize()
     g = capture_graph(step) if use_graph else None
     run = g.replay if g is not None else step
+    gm = None
+    if g is not None and per_graph > 1:
+        gm = capture_graph(lambda: [step() for _ in range(per_graph)])
     for _ in range(2):
         run()
+        if gm is not None:
+            gm.replay()
     torch.cuda.synchronize()
     while (time.perf_counter() - t_warm) * 1e3 < MIN_WARMUP_MS:
         for _ in range(4):
@@ -243,8 +255,14 @@ def time_steps(step, steps, warmup, kernel=None, use_graph=True):
     torch.cuda.synchronize()                     # barrier (one rank) + sync on both sides
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(steps):
-        run()
+    if gm is not None:
+        for _ in range(steps // per_graph):
+            gm.replay()
+        for _ in range(steps % per_graph):
+            run()
+    else:
+        for _ in range(steps):
+            run()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -903,13 +921,14 @@ def main():
         wl = WORKLOADS[a.workload]
         n, m = wl.nm[0]
         step = make_forward_step(wl, n, m, with_backward=(a.workload == "train"))
-        ms, wall, prof, mode = time_steps(step, a.steps, a.warmup)          # every stage, for stages_us
+        ms, wall, prof, mode = time_steps(step, a.steps, a.warmup,          # every stage, for stages_us
+                                          per_graph=a.steps_per_graph)
         gname = gemm_name_in(prof, "gemm_smfmac" if n <= 2 else "gemm_mfma")
         prof_g = profile_pass(step, a.steps, gname)                          # the roofline kernel alone
         nprod = 3 if a.workload == "train" else 1
         ops = 2 * wl.T * wl.R * wl.K * nprod
         out.update(value=round(ops / (ms * 1e-3) / 1e12, 3), unit="TOPS", ms_per_step=round(ms, 4),
-                   wall_s=round(wall, 4), launch=mode)
+                   wall_s=round(wall, 4), launch=mode, steps_per_graph=a.steps_per_graph if mode == "graph" else 1)
         out["config"] = {"workload": a.workload, "T": wl.T, "R": wl.R, "K": wl.K, "nm": f"{n}:{m}",
                          "step": "pack+act_quant+gemm" + ("+backward" if nprod == 3 else ""),
                          "y_dtype": "bf16", "seed": 0}
