@@ -57,7 +57,7 @@ same line carries:
                 at pruned positions), per kernel;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload, with
                 all of its BLAS threads and with one (median of 3 each).
-Multi-GPU runs are not part of this build: --gpus above 1 exits.
+Runs on more than one GPU are not supported: --gpus above 1 exits.
 """
 from __future__ import annotations
 
