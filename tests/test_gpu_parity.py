@@ -428,6 +428,13 @@ def test_backward_multi_tile_and_bf16_dx():
     check_backward(40, 64, 128, 6, 8, seed=4, dxdt=sbn.SBN_BF16)
 
 
+def test_backward_short_contraction():
+    """One contraction step in both GEMMs (T <= 32 for dW, R <= 32 for dX), and
+    two for dX (R = 56): fewer steps than the kernels' LDS stages."""
+    check_backward(17, 24, 64, 2, 4, seed=5)
+    check_backward(33, 56, 128, 6, 8, seed=6, dxdt=sbn.SBN_BF16)
+
+
 def test_backward_train_size_full():
     """The train-step backward at full size (T=8192, R=11008, K=4096, 6:8):
     every element of dX and dW against the oracle within the abs-product bound."""
