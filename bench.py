@@ -109,6 +109,16 @@ def kernel_avg_ms(prof, name):
     return (ms / cnt if cnt else float("nan")), cnt
 
 
+def gemv_kernel_name(step, n, m):
+    """The name the decode GEMV launches of `step` carry: at 2:4 the library
+    launches the one-token kernel (gemv_tok1_24) when T = 1 and the streamed
+    kernel (gemv_stream_24) otherwise; 6:8 is always gemv_stream_68."""
+    if (n, m) != (2, 4):
+        return f"gemv_stream_{n}{m}"
+    prof = profile_pass(step, 1)
+    return "gemv_tok1_24" if "gemv_tok1_24" in prof else "gemv_stream_24"
+
+
 def traffic_from_profiles(kernel, workload):
     """HBM bytes per launch from the committed PMC summary, if it was taken on
     the current kernel source (the summary records the source hash)."""
@@ -328,7 +338,7 @@ def decode_gemv(n=2, m=4, T=1, reps=5):
     for i in range(P):
         call(i)
     # (i) cold single calls: kernel time from the library's events (gemv only)
-    kname = f"gemv_stream_{n}{m}"
+    kname = gemv_kernel_name(lambda: call(0), n, m)
     prof = profile_pass(lambda: [call(i) for i in range(P)], 1, kname)
     kern_ms, kcnt = kernel_avg_ms(prof, kname)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -787,8 +797,9 @@ def measure_decode_j6(a):
     roofline (`gemv_stream_j6`)."""
     import torch
     res = {}
-    for form, kname in (("packed", "gemv_stream_24"), ("j6", "gemv_stream_j6")):
+    for form in ("packed", "j6"):
         step, nbytes = make_decode_pool_24(form)
+        kname = gemv_kernel_name(step, 2, 4) if form == "packed" else "gemv_stream_j6"
         ms, _, _, mode = time_steps(step, a.steps, a.warmup, kernel=kname)
         k_ms, k_cnt = kernel_avg_ms(profile_pass(step, a.steps, kname), kname)
         ach = nbytes / (k_ms * 1e-3) / 1e9
@@ -822,13 +833,14 @@ def measure_decode_step(a, with_d2=True):
            "config": {"workload": "decode", "T": 1, "R": wl.R, "K": wl.K, "nm": "2:4+6:8",
                       "pool_weights_per_ratio": POOL, "weights_per_launch": POOL,
                       "step": "one table decode GEMV per pool (both pools)", "y_dtype": "bf16", "seed": 0}}
-    for key, kname in (("roofline", "gemv_stream_24"), ("roofline_68", "gemv_stream_68")):
+    for key, (n, m) in (("roofline", (2, 4)), ("roofline_68", (6, 8))):
+        kname = gemv_kernel_name(step, n, m)
         k_ms, k_cnt = kernel_avg_ms(profile_pass(step, a.steps, kname), kname)
-        ach = per_launch[kname] / (k_ms * 1e-3) / 1e9
+        ach = per_launch[f"gemv_stream_{n}{m}"] / (k_ms * 1e-3) / 1e9
         out[key] = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                     "traffic": traffic_from_profiles(kname, "decode"), "kernel_us": round(k_ms * 1e3, 3),
-                    "launches": k_cnt, "bytes_per_launch": per_launch[kname],
+                    "launches": k_cnt, "bytes_per_launch": per_launch[f"gemv_stream_{n}{m}"],
                     "note": "algorithmic bytes: packed planes + activations + scales + bf16 outputs of the "
                             "weights of one launch"}
     out["stages_us"] = {k: round(v[1] / v[0] * 1e3, 3) for k, v in sorted(prof.items()) if v[0]}

@@ -27,6 +27,7 @@
 //         LDS that maps (4 meta bits, the next 8 code bits) to the four weights
 //         of those positions (unused code bits are ignored); each block
 //         computes the table while its first loads are in flight.
+#include <type_traits>
 #include "sbn_decode.h"
 
 namespace sbn {
@@ -851,6 +852,172 @@ __global__ __launch_bounds__(256, Dec::BPC) void gemv_stream_kernel(
   out.commit(tid, R, ldy);
 }
 
+// ----------------------------------------------------------------------------- one-token streamed decode (2:4)
+// For one token the activations are at most 4 KB: they sit in LDS, and each
+// wave takes whole row groups over the full contraction (the K / 1024 ranges
+// of the 2:4 decoder in turn), so no partial sums cross waves and, after the
+// activations are in place, no barrier is needed.  A wave's packed words
+// stream through its own ring of NS range slots (direct global->LDS loads,
+// as in gemv_stream_kernel); the activations of a range are read from LDS
+// into the B fragments of the token's lanes (the other lanes hold zeros).
+// Wave gw of the grid's GW waves takes row groups gw, gw + GW, ...
+#ifndef SBN_GV_TOK1
+#define SBN_GV_TOK1 1
+#endif
+#ifndef SBN_T1_NS
+#define SBN_T1_NS 3
+#define SBN_T1_BPC 3
+#endif
+constexpr int T1_NS = SBN_T1_NS, T1_BPC = SBN_T1_BPC;    // ring slots per wave, resident blocks per CU (52 KB LDS each)
+
+// Wait until the ring slot of this iteration is loaded: at most NDMA loads per
+// later range in flight (up to NS - 1 of them) remain, plus the store issued
+// after the latest refill (vmcnt counts loads and stores in issue order; a
+// ragged group's stores may take more than one instruction, and counting one
+// for them only waits for the rest too).
+template <int NDMA, int NS>
+__device__ inline void wait_ring(int later, bool kst) {
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  if (NS > 3 && later >= 3) {
+    if (kst) wait_vmcnt<NDMA * 3 + 1>();
+    else wait_vmcnt<NDMA * 3>();
+  } else if (NS > 2 && later >= 2) {
+    if (kst) wait_vmcnt<NDMA * 2 + 1>();
+    else wait_vmcnt<NDMA * 2>();
+  } else if (later >= 1) {
+    if (kst) wait_vmcnt<NDMA + 1>();
+    else wait_vmcnt<NDMA>();
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+template <int OUT, typename Tab, int NS, int BPC>
+__global__ __launch_bounds__(256, BPC) void gemv_tok1_kernel(const int8_t* __restrict__ Xq,
+                                                             const float* __restrict__ s_x, int64_t K,
+                                                             const Tab P, int64_t count, int64_t R) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * NS * Dec24::SLOT];
+  __shared__ __attribute__((aligned(16))) int8_t xs[4096];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int g = lane >> 4, rl = lane & 15;
+  const int nr = (int)(K >> 10);                       // ranges of 1024 positions per row
+  const int64_t nrg = cdiv(R, 16), total = nrg * count;
+  const int64_t rowb = K / 8;                          // bytes per row of either plane
+  for (int64_t i = tid * 16; i < K; i += 256 * 16) *(v4i*)(xs + i) = *(const v4i*)(Xq + i);
+  __syncthreads();
+  const int64_t GW = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wave;
+  if (gw >= total) return;                             // wave-uniform; no barrier follows
+  const float sxv = OUT != 0 ? s_x[0] : 0.0f;
+  uint8_t* myring = lds + wave * NS * Dec24::SLOT;
+  const int nit = (int)(((total - 1 - gw) / GW + 1) * nr);
+  Dec24 dec;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) dec.blo[s] = dec.bhi[s] = (v4i){0, 0, 0, 0};
+
+  int64_t iq = gw;                                     // next range to load: range ir of row group iq
+  int ir = 0;
+  auto issue_next = [&](int slot) {
+    const int64_t w = iq / nrg, lr = iq - w * nrg;
+    const int valid = (int)(R - lr * 16 < 16 ? R - lr * 16 : 16);
+    const GvEntry e = gv_entry(P, w);
+    dec.init(ir, lane);                                // the range takes the place of the wave
+    dec.issue(myring + slot * Dec24::SLOT, e.meta + lr * 16 * rowb, e.codes + lr * 16 * rowb, valid, K);
+    if (++ir == nr) {
+      ir = 0;
+      iq += GW;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < NS; ++i)
+    if (i < nit) issue_next(i);
+
+  typedef __attribute__((address_space(1))) uint16_t* GU16;
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(1))) v2u* GU2;
+  typedef __attribute__((address_space(1))) int* GI32;
+  typedef __attribute__((address_space(1))) v4i* GV4;
+  v4i tot = (v4i){0, 0, 0, 0}, pv = (v4i){0, 0, 0, 0};
+  int64_t cq = gw, prow = 0;                           // row group being computed; first row of the pending store
+  void* pY = nullptr;
+  bool pend = false, kst = false;                      // a store is pending / was issued after the latest refill
+  // lanes of token 0 (rl == 0) store rows prow .. prow + 3 of the pending group
+  auto store = [&]() {
+    if (rl == 0) {
+      if (OUT == 2) {
+        const GU16 y = (GU16)pY + prow;
+        if (prow + 4 <= R) {
+          *(GU2)y = (v2u){(uint32_t)pv[0], (uint32_t)pv[1]};
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (prow + q < R) y[q] = (uint16_t)((uint32_t)pv[q >> 1] >> (16 * (q & 1)));
+        }
+      } else {
+        const GI32 y = (GI32)pY + prow;
+        if (prow + 4 <= R) {
+          *(GV4)y = pv;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (prow + q < R) y[q] = pv[q];
+        }
+      }
+    }
+  };
+  int slot = 0, cr = 0;
+  for (int it = 0; it < nit; ++it) {
+    // the range's activations (token 0's lanes), read while the ring loads land
+    if (rl == 0) {
+      const int8_t* xr = xs + 1024 * cr + 256 * (g >> 1) + 16 * (g & 1);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        dec.blo[s] = *(const v4i*)(xr + 32 * s);
+        dec.bhi[s] = *(const v4i*)(xr + 32 * s + 512);
+      }
+    }
+    wait_ring<Dec24::NDMA, NS>(nit - 1 - it, kst);
+    // the slot's words into registers (waited for in the read), refill it,
+    // then the previous group's store
+    const Dec24::Frag f = dec.read(myring + slot * Dec24::SLOT, rl, g);
+    if (it + NS < nit) issue_next(slot);
+    kst = pend;
+    if (pend) {
+      store();
+      pend = false;
+    }
+    tot += dec.compute(f, nullptr);
+    if (++cr == nr) {
+      const int64_t w = cq / nrg, lr = cq - w * nrg;
+      const GvEntry e = gv_entry(P, w);
+      const v4i sum = tot >> 6;                        // exact: every partial is a multiple of 64
+      if (OUT == 0) {
+        pv = sum;
+      } else {
+        const float sc = gv_scale(e.s_w) * sxv;
+        float y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y[q] = (float)sum[q] * sc;
+        if (OUT == 1) {
+          pv = (v4i){(int)__float_as_uint(y[0]), (int)__float_as_uint(y[1]), (int)__float_as_uint(y[2]),
+                     (int)__float_as_uint(y[3])};
+        } else {
+          pv[0] = (int)((uint32_t)f32_to_bf16_rne(y[0]) | ((uint32_t)f32_to_bf16_rne(y[1]) << 16));
+          pv[1] = (int)((uint32_t)f32_to_bf16_rne(y[2]) | ((uint32_t)f32_to_bf16_rne(y[3]) << 16));
+        }
+      }
+      prow = lr * 16 + 4 * g;
+      pY = e.Y;
+      pend = true;
+      tot = (v4i){0, 0, 0, 0};
+      cr = 0;
+      cq += GW;
+    }
+    slot = slot + 1 == NS ? 0 : slot + 1;
+  }
+  if (pend) store();
+}
+
 // ----------------------------------------------------------------------------- table path
 // Range of 64*S positions (S <= SMAX steps); lane group g's run is positions
 // p0 = kbeg + 16*S*g + [0, 16*S); step j takes positions p0 + 16*j .. +16 as
@@ -1028,10 +1195,29 @@ int64_t stream_chunk(int64_t total, int64_t blocks) {
   return even < 8 ? even : 8;
 }
 
+template <typename Tab>
+hipError_t launch_tok1(const int8_t* Xq, const float* s_x, int64_t K, const Tab& P, int64_t count, int64_t R,
+                       sbn_dtype ydt, hipStream_t st) {
+  const int64_t waves = cdiv(R, 16) * count, blocks = 256 * T1_BPC;
+  const int64_t nb = cdiv(waves, 4);
+  const dim3 grid((unsigned)(nb < blocks ? nb : blocks)), block(256);
+  if (ydt == SBN_I32_ACC)
+    SBN_LAUNCH("gemv_tok1_24", (gemv_tok1_kernel<0, Tab, T1_NS, T1_BPC>), grid, block, 0, st, Xq, s_x, K, P, count, R);
+  else if (ydt == SBN_F32)
+    SBN_LAUNCH("gemv_tok1_24", (gemv_tok1_kernel<1, Tab, T1_NS, T1_BPC>), grid, block, 0, st, Xq, s_x, K, P, count, R);
+  else
+    SBN_LAUNCH("gemv_tok1_24", (gemv_tok1_kernel<2, Tab, T1_NS, T1_BPC>), grid, block, 0, st, Xq, s_x, K, P, count, R);
+  return hipGetLastError();
+}
+
 template <typename Dec, typename Tab>
 hipError_t launch_stream(const char* name, const int8_t* Xq, const float* s_x, int64_t T, int64_t K,
                          const Tab& P, int64_t count, int64_t R, sbn_dtype ydt, int64_t ldy, hipStream_t st) {
   const int64_t total = cdiv(R, 16) * count;
+  // one token with at least a row group for every resident wave of the
+  // one-token kernel; fewer row groups keep four waves on each (K split)
+  if (SBN_GV_TOK1 && std::is_same<Dec, Dec24>::value && T == 1 && total >= 256 * T1_BPC * 4)
+    return launch_tok1(Xq, s_x, K, P, count, R, ydt, st);
   const int64_t blocks = 256 * Dec::BPC;   // one wave of resident blocks over the 256 CUs
   const int64_t chunk = stream_chunk(total, blocks), nch = cdiv(total, chunk);
   const dim3 grid((unsigned)(nch < blocks ? nch : blocks)), block(256);

@@ -42,8 +42,8 @@ def test_committed_profiles_match_the_sources():
     has changed since they were taken the bench reports null, and this test
     says so (skip) rather than failing the suite."""
     stale = []
-    for kern, wl in (("gemm_smfmac_wide", "prefill"), ("gemv_stream_24", "decode"), ("gemv_stream_68", "decode"),
-                     ("gemv_stream_d2", "decode")):
+    for kern, wl in (("gemm_smfmac_wide", "prefill"), ("gemv_tok1_24", "decode"), ("gemv_stream_68", "decode"),
+                     ("gemv_stream_d2", "decode"), ("gemv_stream_j6", "decode")):
         assert os.path.exists(os.path.join(ROOT, "profiles", f"pmc_{kern}_{wl}.md")), (kern, wl)
         if bench.traffic_from_profiles(kern, wl) is None:
             stale.append(f"{kern}/{wl}")

@@ -97,6 +97,42 @@ def test_gemv_table_matches_oracle(n, m, d2, count, R, K, T):
                 assert bool((fulls[b][:, R:] == 77).all()), f"weight {b}: write past R"
 
 
+@pytest.mark.parametrize("K", [1024, 3072, 4096])
+def test_gemv_table_one_token_kernel(K):
+    """One token over 240 weights of R = 203 rows (3120 row groups, at least
+    one for each of the 3072 resident waves of the one-token 2:4 kernel, which
+    then takes the launch): every output in every dtype against the oracle,
+    ragged last row group included, and the padding columns untouched.  Eight
+    distinct weights, each listed 30 times with its own output."""
+    import torch
+    R, T, n, m, count = 203, 1, 2, 4, 240
+    Wd = weights(8, R, K, seed=7000 + K // 1024)
+    Ws = [Wd[b % 8] for b in range(count)]
+    X = gaussian_bf16((T, K), 1.0, seed=K + 11, stream=1)
+    xq, sx = O.act_quant(X)
+    Xq, s_x = dev(xq), dev(sx)
+    refs = []
+    for W in Wd:
+        eff, _, sw = O.quant_then_mask(W, n, m)
+        refs.append((O.accumulate(xq, eff), sw))
+    for ydt in YDTS:
+        tab, fulls = build_table(Ws, R, K, n, m, T, ydt, False)
+        print(f"one-token table gemv K={K} ydt={ydt}", flush=True)
+        torch.cuda.synchronize()
+        sbn.sbn_profile_reset()
+        sbn.sbn_profile_enable(True, None)
+        run_table(Xq, s_x, tab)
+        sbn.sbn_profile_enable(False)
+        assert "gemv_tok1_24" in sbn.sbn_profile_dump(), "the one-token kernel did not run"
+        for b in range(count):
+            acc, sw = refs[b % 8]
+            got = got_bits(tab.Ys[b], ydt)
+            want = expect(acc, sw, sx, ydt)
+            bad = got != want
+            assert not bad.any(), f"weight {b} ydt {ydt}: {bad.sum()} differ, first at {np.argwhere(bad)[0].tolist()}"
+            assert bool((fulls[b][:, R:] == 77).all()), f"weight {b}: write past R"
+
+
 def test_gemv_table_reused_with_new_activations():
     """A table is built once and called again with other activations: the
     second call's outputs are the oracle's for the new activations."""
