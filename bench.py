@@ -111,12 +111,15 @@ def kernel_avg_ms(prof, name):
 
 def gemv_kernel_name(step, n, m):
     """The name the decode GEMV launches of `step` carry: at 2:4 the library
-    launches the one-token kernel (gemv_tok1_24) when T = 1 and the streamed
-    kernel (gemv_stream_24) otherwise; 6:8 is always gemv_stream_68."""
-    if (n, m) != (2, 4):
+    launches the one-token kernel (gemv_tok1_24) for one token over a large
+    launch and the streamed kernel (gemv_stream_24) otherwise, and the same
+    for the joint 2:4 code (n, m = "j", 6: gemv_tok1_j6 / gemv_stream_j6);
+    6:8 is always gemv_stream_68."""
+    if (n, m) not in ((2, 4), ("j", 6)):
         return f"gemv_stream_{n}{m}"
     prof = profile_pass(step, 1)
-    return "gemv_tok1_24" if "gemv_tok1_24" in prof else "gemv_stream_24"
+    tag = f"{n}{m}"
+    return f"gemv_tok1_{tag}" if f"gemv_tok1_{tag}" in prof else f"gemv_stream_{tag}"
 
 
 def traffic_from_profiles(kernel, workload):
@@ -799,7 +802,7 @@ def measure_decode_j6(a):
     res = {}
     for form in ("packed", "j6"):
         step, nbytes = make_decode_pool_24(form)
-        kname = gemv_kernel_name(step, 2, 4) if form == "packed" else "gemv_stream_j6"
+        kname = gemv_kernel_name(step, 2, 4) if form == "packed" else gemv_kernel_name(step, "j", 6)
         ms, _, _, mode = time_steps(step, a.steps, a.warmup, kernel=kname)
         k_ms, k_cnt = kernel_avg_ms(profile_pass(step, a.steps, kname), kname)
         ach = nbytes / (k_ms * 1e-3) / 1e9

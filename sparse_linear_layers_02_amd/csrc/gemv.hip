@@ -892,26 +892,28 @@ __device__ inline void wait_ring(int later, bool kst) {
   }
 }
 
-template <int OUT, typename Tab, int NS, int BPC>
+template <int OUT, typename Dec, typename Tab, int NS, int BPC>
 __global__ __launch_bounds__(256, BPC) void gemv_tok1_kernel(const int8_t* __restrict__ Xq,
                                                              const float* __restrict__ s_x, int64_t K,
                                                              const Tab P, int64_t count, int64_t R) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * NS * Dec24::SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * NS * Dec::SLOT];
   __shared__ __attribute__((aligned(16))) int8_t xs[4096];
+  __shared__ __attribute__((aligned(16))) uint8_t lut[Dec::LUT > 0 ? Dec::LUT : 16];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int g = lane >> 4, rl = lane & 15;
   const int nr = (int)(K >> 10);                       // ranges of 1024 positions per row
   const int64_t nrg = cdiv(R, 16), total = nrg * count;
-  const int64_t rowb = K / 8;                          // bytes per row of either plane
+  const int64_t rowm = Dec::meta_row(K), rowc = Dec::code_row(K);      // plane bytes per row
+  Dec dec;
   for (int64_t i = tid * 16; i < K; i += 256 * 16) *(v4i*)(xs + i) = *(const v4i*)(Xq + i);
+  dec.build_lut(lut, tid);
   __syncthreads();
   const int64_t GW = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wave;
   if (gw >= total) return;                             // wave-uniform; no barrier follows
   const float sxv = OUT != 0 ? s_x[0] : 0.0f;
-  uint8_t* myring = lds + wave * NS * Dec24::SLOT;
+  uint8_t* myring = lds + wave * NS * Dec::SLOT;
   const int nit = (int)(((total - 1 - gw) / GW + 1) * nr);
-  Dec24 dec;
 #pragma unroll
   for (int s = 0; s < 8; ++s) dec.blo[s] = dec.bhi[s] = (v4i){0, 0, 0, 0};
 
@@ -922,7 +924,7 @@ __global__ __launch_bounds__(256, BPC) void gemv_tok1_kernel(const int8_t* __res
     const int valid = (int)(R - lr * 16 < 16 ? R - lr * 16 : 16);
     const GvEntry e = gv_entry(P, w);
     dec.init(ir, lane);                                // the range takes the place of the wave
-    dec.issue(myring + slot * Dec24::SLOT, e.meta + lr * 16 * rowb, e.codes + lr * 16 * rowb, valid, K);
+    dec.issue(myring + slot * Dec::SLOT, e.meta + lr * 16 * rowm, e.codes + lr * 16 * rowc, valid, K);
     if (++ir == nr) {
       ir = 0;
       iq += GW;
@@ -976,17 +978,17 @@ __global__ __launch_bounds__(256, BPC) void gemv_tok1_kernel(const int8_t* __res
         dec.bhi[s] = *(const v4i*)(xr + 32 * s + 512);
       }
     }
-    wait_ring<Dec24::NDMA, NS>(nit - 1 - it, kst);
+    wait_ring<Dec::NDMA, NS>(nit - 1 - it, kst);
     // the slot's words into registers (waited for in the read), refill it,
     // then the previous group's store
-    const Dec24::Frag f = dec.read(myring + slot * Dec24::SLOT, rl, g);
+    const typename Dec::Frag f = dec.read(myring + slot * Dec::SLOT, rl, g);
     if (it + NS < nit) issue_next(slot);
     kst = pend;
     if (pend) {
       store();
       pend = false;
     }
-    tot += dec.compute(f, nullptr);
+    tot += dec.compute(f, lut);
     if (++cr == nr) {
       const int64_t w = cq / nrg, lr = cq - w * nrg;
       const GvEntry e = gv_entry(P, w);
@@ -1195,18 +1197,18 @@ int64_t stream_chunk(int64_t total, int64_t blocks) {
   return even < 8 ? even : 8;
 }
 
-template <typename Tab>
-hipError_t launch_tok1(const int8_t* Xq, const float* s_x, int64_t K, const Tab& P, int64_t count, int64_t R,
-                       sbn_dtype ydt, hipStream_t st) {
+template <typename Dec, typename Tab>
+hipError_t launch_tok1(const char* name, const int8_t* Xq, const float* s_x, int64_t K, const Tab& P, int64_t count,
+                       int64_t R, sbn_dtype ydt, hipStream_t st) {
   const int64_t waves = cdiv(R, 16) * count, blocks = 256 * T1_BPC;
   const int64_t nb = cdiv(waves, 4);
   const dim3 grid((unsigned)(nb < blocks ? nb : blocks)), block(256);
   if (ydt == SBN_I32_ACC)
-    SBN_LAUNCH("gemv_tok1_24", (gemv_tok1_kernel<0, Tab, T1_NS, T1_BPC>), grid, block, 0, st, Xq, s_x, K, P, count, R);
+    SBN_LAUNCH(name, (gemv_tok1_kernel<0, Dec, Tab, T1_NS, T1_BPC>), grid, block, 0, st, Xq, s_x, K, P, count, R);
   else if (ydt == SBN_F32)
-    SBN_LAUNCH("gemv_tok1_24", (gemv_tok1_kernel<1, Tab, T1_NS, T1_BPC>), grid, block, 0, st, Xq, s_x, K, P, count, R);
+    SBN_LAUNCH(name, (gemv_tok1_kernel<1, Dec, Tab, T1_NS, T1_BPC>), grid, block, 0, st, Xq, s_x, K, P, count, R);
   else
-    SBN_LAUNCH("gemv_tok1_24", (gemv_tok1_kernel<2, Tab, T1_NS, T1_BPC>), grid, block, 0, st, Xq, s_x, K, P, count, R);
+    SBN_LAUNCH(name, (gemv_tok1_kernel<2, Dec, Tab, T1_NS, T1_BPC>), grid, block, 0, st, Xq, s_x, K, P, count, R);
   return hipGetLastError();
 }
 
@@ -1216,8 +1218,11 @@ hipError_t launch_stream(const char* name, const int8_t* Xq, const float* s_x, i
   const int64_t total = cdiv(R, 16) * count;
   // one token with at least a row group for every resident wave of the
   // one-token kernel; fewer row groups keep four waves on each (K split)
-  if (SBN_GV_TOK1 && std::is_same<Dec, Dec24>::value && T == 1 && total >= 256 * T1_BPC * 4)
-    return launch_tok1(Xq, s_x, K, P, count, R, ydt, st);
+  // (the joint 2:4 code on the one-token kernel measured slower than K-split:
+  // 94.1-94.3 against 92.1-92.7 us on the 128-weight pool)
+  if constexpr (std::is_same<Dec, Dec24>::value)
+    if (SBN_GV_TOK1 && T == 1 && total >= 256 * T1_BPC * 4)
+      return launch_tok1<Dec>("gemv_tok1_24", Xq, s_x, K, P, count, R, ydt, st);
   const int64_t blocks = 256 * Dec::BPC;   // one wave of resident blocks over the 256 CUs
   const int64_t chunk = stream_chunk(total, blocks), nch = cdiv(total, chunk);
   const dim3 grid((unsigned)(nch < blocks ? nch : blocks)), block(256);
